@@ -1,0 +1,155 @@
+/*
+ * bakron.h -- C ABI of libbakron, a gfx950 (MI355X) implementation of BaKron:
+ * two-sided adaptive rounding of a weight matrix under a Kronecker-factored
+ * Hessian H_O (x) H_I.
+ *
+ * Sources (web pages, cited by title and section):
+ *   "BaKron: Efficient Quantization with Kronecker-Factored Hessians"
+ *       (insight.aitobox.com), Abstract: the solver schedules the two-sided
+ *       rounding rule with anti-diagonal parallelism and a recursive
+ *       divide-and-conquer so that it takes O(m+n) sequential steps and
+ *       O(mn(m+n)) work, and is modular in the base quantiser and in the
+ *       Hessian estimator.
+ *   YAQA article (news.43b.com.cn/a/479517), section 4: the rounding rule
+ *       W_ij = Q(W*_ij + a_i^T D[:i,:j] b_j + a_i^T D[:i,j] + D[i,:j] b_j)
+ *       with a_i, b_j columns of the strictly upper L_O, L_I and D = W* - W;
+ *       the factorisation H = (L + I) D (L + I)^T; the error bound.
+ *   YAQA article, section 3, and the K-FAC tutorial (www.mlqm.cn), section 5:
+ *       the factor estimates H_I = E[x^T x], H_O = E[g^T g] and damping.
+ *
+ * Conventions for every entry point:
+ *   - All matrix and vector pointers are DEVICE pointers (memory of the
+ *     current HIP device) unless a parameter says "host". Matrices are
+ *     row-major with a leading dimension (ld, in elements) >= the number of
+ *     columns. No alignment is required.
+ *   - The caller owns every buffer, including the workspace; the library
+ *     never allocates, frees or retains memory and keeps no state between
+ *     calls. Calls on different streams may run concurrently.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream). Only bakron_ldl waits for its work to finish.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid argument returns BAKRON_E_INVALID_ARG and enqueues nothing.
+ *     A failed launch returns BAKRON_E_DEVICE. No C++ exception crosses the
+ *     ABI.
+ */
+#ifndef BAKRON_H
+#define BAKRON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BAKRON_ABI_VERSION 1
+
+enum {
+    BAKRON_OK = 0,
+    BAKRON_E_INVALID_ARG = 1, /* bad pointer, size, leading dimension or option */
+    BAKRON_E_NOT_SPD = 2,     /* bakron_ldl: a pivot was not positive (or not finite) */
+    BAKRON_E_WORKSPACE = 3,   /* workspace pointer NULL or smaller than required */
+    BAKRON_E_DEVICE = 4       /* a HIP call or kernel launch failed */
+};
+
+enum { BAKRON_ROUND_NEAREST = 0, BAKRON_ROUND_STOCHASTIC = 1 };
+
+/*
+ * Base quantiser Q (the solver is modular in it: BaKron Abstract; YAQA
+ * section 4 names nearest and stochastic rounding).
+ *   Grid of row i: s_i * (c - Lq/2), c in {0, ..., Lq}, Lq = 2^bits - 1.
+ *   y = t / s_i + Lq/2 is the pre-rounding value t in grid steps.
+ *   NEAREST:    c = clamp(floor(y + 1/2), 0, Lq)
+ *   STOCHASTIC: c = clamp(floor(y + u_ij), 0, Lq), u_ij = (z >> 40) * 2^-24 with
+ *               z = SplitMix64 output number i*n + j + 1 of a stream seeded
+ *               with `seed` (independent of the order entries are visited).
+ *   row_scale:  device [m] fp32 scales, all finite and > 0; NULL means
+ *               s_i = fp32(2 * max_j |W*_ij|) / fp32(Lq), computed in fp32.
+ */
+typedef struct {
+    int32_t bits;          /* 1..8 */
+    int32_t rounding;      /* BAKRON_ROUND_NEAREST or BAKRON_ROUND_STOCHASTIC */
+    uint64_t seed;         /* stochastic rounding only */
+    const float* row_scale;/* device, [m], or NULL */
+} bakron_quantizer;
+
+/* Returns BAKRON_ABI_VERSION of the built library. */
+int bakron_abi_version(void);
+
+/* Static string describing a status code (never NULL). */
+const char* bakron_status_str(int status);
+
+/*
+ * Hessian factor accumulation (YAQA section 3: H_I = E[x^T x]; the same form
+ * gives H_O from output gradients):  H <- beta * H + alpha * X^T X.
+ *   X: T x d fp32, leading dimension ldx >= d (rows are tokens).
+ *   H: d x d fp32, ldh >= d. The full symmetric matrix is written (both
+ *      triangles, bit-identical mirror). With beta == 0, H is not read.
+ *   For H = X^T X / T pass alpha = 1/T, beta = 0; to accumulate over token
+ *   chunks call again with beta = 1 and alpha = 1/T_total.
+ *   T == 0 scales H by beta. Workspace: none (ws may be NULL, ws_bytes 0).
+ * Errors: INVALID_ARG for NULL X (T > 0) or H, d <= 0, T < 0, bad ld.
+ */
+size_t bakron_hessian_accum_workspace_bytes(int64_t T, int64_t d);
+int bakron_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, float alpha,
+                         float beta, float* H, int64_t ldh, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/*
+ * Damped LDL factorisation (YAQA section 4): with lambda = damp_rel * mean(diag H)
+ * (the mean of the undamped diagonal, in fp64), factor
+ *     H + lambda I = (L + I) diag(D) (L + I)^T,  L strictly UPPER triangular,
+ * i.e. a Cholesky factorisation taken from the last index to the first. The
+ * work is done in fp64 on the device; results are rounded to fp32.
+ *   H: d x d fp32, ldh >= d; only the upper triangle (with the diagonal) is
+ *      read. On return H holds L in its strict upper triangle, D on its
+ *      diagonal and zeros in its strict lower triangle.
+ *   D: device [d] fp32 copy of D, or NULL.
+ *   damp_rel: finite, >= 0 (fp64).
+ *   bad_pivot: HOST pointer or NULL; receives -1, or on BAKRON_E_NOT_SPD the
+ *      index j of the first pivot (taken from the last index down) that was
+ *      not positive and finite. H is then unspecified.
+ *   ws: device workspace of at least bakron_ldl_workspace_bytes(d) bytes.
+ * This call waits for the stream so that NOT_SPD can be reported.
+ */
+size_t bakron_ldl_workspace_bytes(int64_t d);
+int bakron_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, int64_t* bad_pivot,
+               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * BaKron solve: round W* (m x n) under H_O (x) H_I given the strict upper LDL
+ * factors, entry (i, j) receiving the feedback
+ *     a_i^T D[:i,:j] b_j + a_i^T D[:i,j] + D[i,:j] b_j
+ * from the error D = W* - W already committed (YAQA section 4), scheduled as
+ * a wavefront over 64x64 leaves (anti-diagonal parallelism, BaKron Abstract)
+ * whose far-field feedback is formed by MFMA GEMMs.
+ *   W:     m x n fp32, ldw >= n.
+ *   L_O:   m x m fp32 (ldlo >= m); only the strict upper triangle is read.
+ *          NULL means H_O = I up to scale (one-sided LDLQ / GPTQ).
+ *   L_I:   n x n fp32 (ldli >= n); strict upper triangle read; NULL means a
+ *          diagonal H_I.
+ *   q:     quantiser descriptor (host pointer), see above.
+ *   codes: m x n uint8 codes c_ij, ldc >= n.
+ *   scales_out: [m] fp32, receives the scales used.
+ *   delta_out:  optional m x n fp32 (ldd >= n), receives D = W* - s (c - Lq/2).
+ *   D_O, D_I, loss_out: if loss_out (device, 1 double) is not NULL it receives
+ *          the proxy loss sum_ij D_O,i D_I,j eta_ij^2 with eta = t - q, which
+ *          equals tr(D H_I D^T H_O) for the damped factors; D_I [n] is then
+ *          required and D_O [m] may be NULL only if L_O is NULL (D_O = 1).
+ *   clamped_out: optional device int64 count of entries whose code was clamped.
+ *   info:  optional device int32; 0, or i+1 for the first row i whose scale is
+ *          not finite and positive (then the outputs are unspecified).
+ *   ws:    device workspace of at least bakron_solve_workspace_bytes(m, n).
+ */
+size_t bakron_solve_workspace_bytes(int64_t m, int64_t n);
+int bakron_solve(const float* W, int64_t m, int64_t n, int64_t ldw, const float* L_O, int64_t ldlo,
+                 const float* L_I, int64_t ldli, const bakron_quantizer* q, uint8_t* codes,
+                 int64_t ldc, float* scales_out, float* delta_out, int64_t ldd, const float* D_O,
+                 const float* D_I, double* loss_out, int64_t* clamped_out, int32_t* info,
+                 void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BAKRON_H */

@@ -1,0 +1,16 @@
+"""MI355X-native BaKron: two-sided adaptive rounding under a Kronecker-factored Hessian.
+
+The computation runs in libbakron (HIP kernels for gfx950, C ABI in
+include/bakron.h); this package is a thin ctypes binding that takes PyTorch
+tensors for device memory and uses the current stream.
+
+  hessian_accum(X)            H <- beta H + alpha X^T X            (fp32 MFMA)
+  ldl(H, damp_rel)            H + lambda I = (L + I) D (L + I)^T   (fp64, L strictly upper)
+  solve(W, L_O, L_I, bits)    BaKron rounding: codes, scales, error, proxy loss
+  quantize_layer(W, X, G, b)  the whole per-layer path
+"""
+from ._binding import (  # noqa: F401
+    BAKRON_E_DEVICE, BAKRON_E_INVALID_ARG, BAKRON_E_NOT_SPD, BAKRON_E_WORKSPACE, BAKRON_OK,
+    EXPORTS, LIB, LIB_PATH, BakronError, SolveResult, abi_version, hessian_accum, ldl,
+    quantize_layer, release_workspace, solve,
+)

@@ -1,0 +1,244 @@
+"""ctypes binding of libbakron (include/bakron.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libbakron. Tensors must be CUDA (ROCm) tensors on the current
+device, row-major with unit column stride; PyTorch supplies device memory and
+the current stream. If the built library is missing this module raises
+ImportError: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch  # loads the HIP runtime first; libbakron binds to the same one
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "_build", "libbakron.so")
+
+BAKRON_OK = 0
+BAKRON_E_INVALID_ARG = 1
+BAKRON_E_NOT_SPD = 2
+BAKRON_E_WORKSPACE = 3
+BAKRON_E_DEVICE = 4
+ROUNDING = {"nearest": 0, "stochastic": 1}
+
+
+class BakronError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__("%s failed: %s (status %d)" % (fn, msg, status))
+        self.status = status
+
+
+class _Quantizer(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("rounding", ctypes.c_int32),
+                ("seed", ctypes.c_uint64), ("row_scale", ctypes.c_void_p)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libbakron.so is not built (%s); run "
+                          "`python -m kronecker_hessian_rounding_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    f32 = ctypes.c_float
+    lib.bakron_abi_version.restype = ctypes.c_int
+    lib.bakron_abi_version.argtypes = []
+    lib.bakron_status_str.restype = ctypes.c_char_p
+    lib.bakron_status_str.argtypes = [ctypes.c_int]
+    lib.bakron_hessian_accum_workspace_bytes.restype = sz
+    lib.bakron_hessian_accum_workspace_bytes.argtypes = [i64, i64]
+    lib.bakron_hessian_accum.restype = ctypes.c_int
+    lib.bakron_hessian_accum.argtypes = [vp, i64, i64, i64, f32, f32, vp, i64, vp, sz, vp]
+    lib.bakron_ldl_workspace_bytes.restype = sz
+    lib.bakron_ldl_workspace_bytes.argtypes = [i64]
+    lib.bakron_ldl.restype = ctypes.c_int
+    lib.bakron_ldl.argtypes = [vp, i64, i64, ctypes.c_double, vp, ctypes.POINTER(i64), vp, sz, vp]
+    lib.bakron_solve_workspace_bytes.restype = sz
+    lib.bakron_solve_workspace_bytes.argtypes = [i64, i64]
+    lib.bakron_solve.restype = ctypes.c_int
+    lib.bakron_solve.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, ctypes.POINTER(_Quantizer),
+                                 vp, i64, vp, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    return lib
+
+
+LIB = _load()
+
+EXPORTS = ("bakron_abi_version", "bakron_status_str", "bakron_hessian_accum_workspace_bytes",
+           "bakron_hessian_accum", "bakron_ldl_workspace_bytes", "bakron_ldl",
+           "bakron_solve_workspace_bytes", "bakron_solve")
+
+
+def abi_version() -> int:
+    return int(LIB.bakron_abi_version())
+
+
+def _check(fn: str, status: int):
+    if status != BAKRON_OK:
+        raise BakronError(fn, status, LIB.bakron_status_str(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _mat(t: torch.Tensor, name: str, dtype=torch.float32) -> int:
+    """Validate a row-major device matrix; returns its leading dimension."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a CUDA/ROCm tensor" % name)
+    if t.dtype != dtype or t.dim() != 2:
+        raise ValueError("%s must be a 2-D %s tensor" % (name, dtype))
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("%s must have unit column stride" % name)
+    return max(int(t.stride(0)), int(t.shape[1]))
+
+
+def _vec(t: Optional[torch.Tensor], name: str, n: int, dtype=torch.float32):
+    if t is None:
+        return None
+    if not t.is_cuda or t.dtype != dtype or t.numel() != n or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous CUDA %s vector of length %d" % (name, dtype, n))
+    return t
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    key = (str(device), "ws")
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def release_workspace():
+    _ws_cache.clear()
+
+
+# --------------------------------------------------------------------------
+def hessian_accum(X: torch.Tensor, H: Optional[torch.Tensor] = None, alpha: Optional[float] = None,
+                  beta: float = 0.0) -> torch.Tensor:
+    """H <- beta H + alpha X^T X (default alpha = 1/T), fp32 MFMA on the device."""
+    ldx = _mat(X, "X")
+    T, d = X.shape
+    if H is None:
+        H = torch.empty((d, d), dtype=torch.float32, device=X.device)
+    ldh = _mat(H, "H")
+    if tuple(H.shape) != (d, d):
+        raise ValueError("H must be %d x %d" % (d, d))
+    if alpha is None:
+        alpha = 1.0 / max(T, 1)
+    nb = LIB.bakron_hessian_accum_workspace_bytes(T, d)
+    ws = _workspace(nb, X.device)
+    _check("bakron_hessian_accum",
+           LIB.bakron_hessian_accum(_ptr(X), T, d, ldx, alpha, beta, _ptr(H), ldh, _ptr(ws), nb,
+                                    _stream()))
+    return H
+
+
+def ldl(H: torch.Tensor, damp_rel: float = 0.01, D: Optional[torch.Tensor] = None):
+    """In place: H + damp_rel*mean(diag H)*I = (L + I) diag(D) (L + I)^T, L strictly upper.
+
+    Returns (H, D): H holds L above its diagonal, D on it and zeros below.
+    Raises BakronError(status=BAKRON_E_NOT_SPD) with .bad_pivot on failure.
+    """
+    ldh = _mat(H, "H")
+    d = H.shape[0]
+    if H.shape[1] != d:
+        raise ValueError("H must be square")
+    if D is None:
+        D = torch.empty(d, dtype=torch.float32, device=H.device)
+    _vec(D, "D", d)
+    nb = LIB.bakron_ldl_workspace_bytes(d)
+    ws = _workspace(nb, H.device)
+    bad = ctypes.c_int64(-1)
+    st = LIB.bakron_ldl(_ptr(H), d, ldh, damp_rel, _ptr(D), ctypes.byref(bad), _ptr(ws), nb,
+                        _stream())
+    if st != BAKRON_OK:
+        err = BakronError("bakron_ldl", st, LIB.bakron_status_str(st).decode())
+        err.bad_pivot = int(bad.value)
+        raise err
+    return H, D
+
+
+@dataclass
+class SolveResult:
+    codes: torch.Tensor
+    scales: torch.Tensor
+    delta: Optional[torch.Tensor]
+    loss: Optional[torch.Tensor]      # device double [1]
+    clamped: torch.Tensor             # device int64 [1]
+    info: torch.Tensor                # device int32 [1]
+
+
+def solve(W: torch.Tensor, L_O: Optional[torch.Tensor], L_I: Optional[torch.Tensor], bits: int,
+          rounding: str = "nearest", seed: int = 0, row_scale: Optional[torch.Tensor] = None,
+          D_O: Optional[torch.Tensor] = None, D_I: Optional[torch.Tensor] = None,
+          want_delta: bool = False, want_loss: bool = False,
+          out: Optional[SolveResult] = None) -> SolveResult:
+    """BaKron two-sided rounding of W (m x n) given strict-upper LDL factors L_O, L_I."""
+    ldw = _mat(W, "W")
+    m, n = W.shape
+    ldlo = ldli = 0
+    if L_O is not None:
+        ldlo = _mat(L_O, "L_O")
+        if tuple(L_O.shape) != (m, m):
+            raise ValueError("L_O must be %d x %d" % (m, m))
+    if L_I is not None:
+        ldli = _mat(L_I, "L_I")
+        if tuple(L_I.shape) != (n, n):
+            raise ValueError("L_I must be %d x %d" % (n, n))
+    _vec(row_scale, "row_scale", m)
+    _vec(D_O, "D_O", m)
+    _vec(D_I, "D_I", n)
+    dev = W.device
+    if out is None:
+        out = SolveResult(
+            codes=torch.empty((m, n), dtype=torch.uint8, device=dev),
+            scales=torch.empty(m, dtype=torch.float32, device=dev),
+            delta=torch.empty((m, n), dtype=torch.float32, device=dev) if want_delta else None,
+            loss=torch.empty(1, dtype=torch.float64, device=dev) if want_loss else None,
+            clamped=torch.empty(1, dtype=torch.int64, device=dev),
+            info=torch.empty(1, dtype=torch.int32, device=dev))
+    q = _Quantizer(int(bits), ROUNDING[rounding], int(seed) & (2**64 - 1),
+                   None if row_scale is None else row_scale.data_ptr())
+    nb = LIB.bakron_solve_workspace_bytes(m, n)
+    ws = _workspace(nb, dev)
+    ldd = n if out.delta is None else _mat(out.delta, "delta")
+    st = LIB.bakron_solve(_ptr(W), m, n, ldw, _ptr(L_O), ldlo, _ptr(L_I), ldli, ctypes.byref(q),
+                          _ptr(out.codes), _mat(out.codes, "codes", torch.uint8), _ptr(out.scales),
+                          _ptr(out.delta), ldd, _ptr(D_O), _ptr(D_I), _ptr(out.loss),
+                          _ptr(out.clamped), _ptr(out.info), _ptr(ws), nb, _stream())
+    _check("bakron_solve", st)
+    return out
+
+
+def quantize_layer(W: torch.Tensor, X: torch.Tensor, G: Optional[torch.Tensor], bits: int,
+                   rounding: str = "nearest", seed: int = 0, damp_rel: float = 0.01,
+                   want_delta: bool = False, want_loss: bool = True, workspace=None):
+    """The whole per-layer path on the device: H_I from X, H_O from G (or H_O = I when
+    G is None), damping + LDL of both, scales, and the BaKron solve."""
+    m, n = W.shape
+    if workspace is None:
+        workspace = {}
+    HI = hessian_accum(X, workspace.get("HI"))
+    HI, DI = ldl(HI, damp_rel, workspace.get("DI"))
+    if G is not None:
+        HO = hessian_accum(G, workspace.get("HO"))
+        HO, DO = ldl(HO, damp_rel, workspace.get("DO"))
+        LO = HO
+    else:
+        LO, DO = None, None
+    res = solve(W, LO, HI, bits, rounding, seed, D_O=DO, D_I=DI, want_delta=want_delta,
+                want_loss=want_loss, out=workspace.get("out"))
+    return res, (LO, DO, HI, DI)

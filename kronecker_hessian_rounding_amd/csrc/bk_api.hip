@@ -1,0 +1,104 @@
+// bk_api.hip -- the extern "C" entry points of libbakron: argument validation on
+// the host, workspace checks, then dispatch to the kernel drivers. Every check
+// happens before anything is enqueued, so an invalid call enqueues no work.
+#include "bk_internal.hpp"
+
+namespace {
+
+bool bad_ld(int64_t ld, int64_t cols) { return ld < cols || ld <= 0; }
+
+}  // namespace
+
+extern "C" {
+
+int bakron_abi_version(void) { return BAKRON_ABI_VERSION; }
+
+const char* bakron_status_str(int status) {
+    switch (status) {
+        case BAKRON_OK: return "ok";
+        case BAKRON_E_INVALID_ARG: return "invalid argument";
+        case BAKRON_E_NOT_SPD: return "matrix is not positive definite";
+        case BAKRON_E_WORKSPACE: return "workspace missing or too small";
+        case BAKRON_E_DEVICE: return "HIP runtime or kernel launch failure";
+        default: return "unknown status";
+    }
+}
+
+size_t bakron_hessian_accum_workspace_bytes(int64_t T, int64_t d) {
+    (void)T;
+    (void)d;
+    return 0;
+}
+
+int bakron_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, float alpha,
+                         float beta, float* H, int64_t ldh, void* ws, size_t ws_bytes,
+                         void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    if (!H || d <= 0 || T < 0 || bad_ld(ldh, d)) return BAKRON_E_INVALID_ARG;
+    if (T > 0 && (!X || bad_ld(ldx, d))) return BAKRON_E_INVALID_ARG;
+    return bk::launch_hessian_accum(X, T, d, ldx, alpha, beta, H, ldh, (hipStream_t)stream);
+}
+
+size_t bakron_ldl_workspace_bytes(int64_t d) {
+    if (d <= 0) return 0;
+    return bk::ldl_workspace_bytes(d);
+}
+
+int bakron_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, int64_t* bad_pivot,
+               void* ws, size_t ws_bytes, void* stream) {
+    if (bad_pivot) *bad_pivot = -1;
+    if (!H || d <= 0 || bad_ld(ldh, d)) return BAKRON_E_INVALID_ARG;
+    if (!(damp_rel >= 0.0) || !(damp_rel < INFINITY)) return BAKRON_E_INVALID_ARG;
+    if (!ws || ws_bytes < bk::ldl_workspace_bytes(d)) return BAKRON_E_WORKSPACE;
+    return bk::run_ldl(H, d, ldh, damp_rel, D, bad_pivot, ws, (hipStream_t)stream);
+}
+
+size_t bakron_solve_workspace_bytes(int64_t m, int64_t n) {
+    if (m <= 0 || n <= 0) return 0;
+    return bk::solve_workspace_bytes(m, n);
+}
+
+int bakron_solve(const float* W, int64_t m, int64_t n, int64_t ldw, const float* L_O, int64_t ldlo,
+                 const float* L_I, int64_t ldli, const bakron_quantizer* q, uint8_t* codes,
+                 int64_t ldc, float* scales_out, float* delta_out, int64_t ldd, const float* D_O,
+                 const float* D_I, double* loss_out, int64_t* clamped_out, int32_t* info,
+                 void* ws, size_t ws_bytes, void* stream) {
+    if (!W || !q || !codes || !scales_out) return BAKRON_E_INVALID_ARG;
+    if (m <= 0 || n <= 0 || bad_ld(ldw, n) || bad_ld(ldc, n)) return BAKRON_E_INVALID_ARG;
+    if (m > (int64_t)1 << 30 || n > (int64_t)1 << 30) return BAKRON_E_INVALID_ARG;
+    if (L_O && bad_ld(ldlo, m)) return BAKRON_E_INVALID_ARG;
+    if (L_I && bad_ld(ldli, n)) return BAKRON_E_INVALID_ARG;
+    if (delta_out && bad_ld(ldd, n)) return BAKRON_E_INVALID_ARG;
+    if (q->bits < 1 || q->bits > 8) return BAKRON_E_INVALID_ARG;
+    if (q->rounding != BAKRON_ROUND_NEAREST && q->rounding != BAKRON_ROUND_STOCHASTIC)
+        return BAKRON_E_INVALID_ARG;
+    if (loss_out && (!D_I || (!D_O && L_O))) return BAKRON_E_INVALID_ARG;
+    if (!ws || ws_bytes < bk::solve_workspace_bytes(m, n)) return BAKRON_E_WORKSPACE;
+    bk::SolveArgs a;
+    a.W = W;
+    a.m = m;
+    a.n = n;
+    a.ldw = ldw;
+    a.LO = L_O;
+    a.ldlo = ldlo;
+    a.LI = L_I;
+    a.ldli = ldli;
+    a.bits = q->bits;
+    a.stochastic = q->rounding == BAKRON_ROUND_STOCHASTIC;
+    a.seed = q->seed;
+    a.row_scale = q->row_scale;
+    a.codes = codes;
+    a.ldc = ldc;
+    a.scales = scales_out;
+    a.delta = delta_out;
+    a.ldd = ldd;
+    a.DO = D_O;
+    a.DI = D_I;
+    a.loss = loss_out;
+    a.clamped = clamped_out;
+    a.info = info;
+    return bk::run_solve(a, ws, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// bk_internal.hpp -- host-side interfaces between the C ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/bakron.h"
+
+namespace bk {
+
+// Round a byte count up to a 256-byte boundary (workspace carving).
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// --- Hessian factor accumulation (bk_accum.hip) ---
+int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, float alpha,
+                         float beta, float* H, int64_t ldh, hipStream_t stream);
+
+// --- LDL factorisation (bk_ldl.hip) ---
+size_t ldl_workspace_bytes(int64_t d);
+int run_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, int64_t* bad_pivot,
+            void* ws, hipStream_t stream);
+
+// --- rounding solve (bk_solve.hip) ---
+struct SolveArgs {
+    const float* W;
+    int64_t m, n, ldw;
+    const float* LO;
+    int64_t ldlo;
+    const float* LI;
+    int64_t ldli;
+    int bits;
+    int stochastic;
+    uint64_t seed;
+    const float* row_scale;
+    uint8_t* codes;
+    int64_t ldc;
+    float* scales;
+    float* delta;
+    int64_t ldd;
+    const float* DO;
+    const float* DI;
+    double* loss;
+    int64_t* clamped;
+    int32_t* info;
+};
+size_t solve_workspace_bytes(int64_t m, int64_t n);
+int run_solve(const SolveArgs& a, void* ws, hipStream_t stream);
+
+}  // namespace bk

@@ -1,0 +1,111 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol that
+include/bakron.h declares, and rejects invalid arguments on the host before
+enqueueing any work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bakron.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import kronecker_hessian_rounding_amd as bk
+    return bk.LIB
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bakron_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("bakron_hessian_accum", "bakron_ldl", "bakron_solve"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import kronecker_hessian_rounding_amd as bk
+    names = declared_functions()
+    assert set(names) == set(bk.EXPORTS)
+    for n in names:
+        assert getattr(lib, n) is not None
+    # and through the dynamic symbol table
+    out = os.popen("nm -D --defined-only %s" % bk.LIB_PATH).read()
+    for n in names:
+        assert re.search(r"\bT %s\b" % n, out), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.bakron_abi_version() == 1
+    for s in range(5):
+        assert lib.bakron_status_str(s)
+    assert lib.bakron_status_str(99) == b"unknown status"
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def test_hessian_accum_rejects_bad_arguments(lib):
+    f = lib.bakron_hessian_accum
+    assert f(FAKE, 10, 0, 4, 1.0, 0.0, FAKE, 4, None, 0, None) == 1     # d <= 0
+    assert f(FAKE, -1, 4, 4, 1.0, 0.0, FAKE, 4, None, 0, None) == 1     # T < 0
+    assert f(None, 10, 4, 4, 1.0, 0.0, FAKE, 4, None, 0, None) == 1     # X NULL
+    assert f(FAKE, 10, 4, 3, 1.0, 0.0, FAKE, 4, None, 0, None) == 1     # ldx < d
+    assert f(FAKE, 10, 4, 4, 1.0, 0.0, FAKE, 3, None, 0, None) == 1     # ldh < d
+    assert f(FAKE, 10, 4, 4, 1.0, 0.0, None, 4, None, 0, None) == 1     # H NULL
+    assert lib.bakron_hessian_accum_workspace_bytes(10, 4) == 0
+
+
+def test_ldl_rejects_bad_arguments(lib):
+    f = lib.bakron_ldl
+    bad = ctypes.c_int64(7)
+    ws_need = lib.bakron_ldl_workspace_bytes(100)
+    assert ws_need >= 100 * 100 * 8
+    assert f(None, 100, 100, 0.01, None, ctypes.byref(bad), FAKE, ws_need, None) == 1
+    assert bad.value == -1
+    assert f(FAKE, 0, 100, 0.01, None, None, FAKE, ws_need, None) == 1
+    assert f(FAKE, 100, 99, 0.01, None, None, FAKE, ws_need, None) == 1
+    assert f(FAKE, 100, 100, -0.5, None, None, FAKE, ws_need, None) == 1
+    assert f(FAKE, 100, 100, float("nan"), None, None, FAKE, ws_need, None) == 1
+    assert f(FAKE, 100, 100, 0.01, None, None, None, ws_need, None) == 3
+    assert f(FAKE, 100, 100, 0.01, None, None, FAKE, ws_need - 1, None) == 3
+
+
+def test_solve_rejects_bad_arguments(lib):
+    import kronecker_hessian_rounding_amd._binding as b
+    f = lib.bakron_solve
+    q = b._Quantizer(2, 0, 0, None)
+    m, n = 70, 50
+    need = lib.bakron_solve_workspace_bytes(m, n)
+    assert need >= 2 * m * n * 4
+
+    def call(W=FAKE, m=m, n=n, ldw=n, LO=FAKE, ldlo=m, LI=FAKE, ldli=n, qq=q, codes=FAKE, ldc=n,
+             scales=FAKE, delta=None, ldd=n, DO=None, DI=None, loss=None, ws=FAKE, nb=need):
+        return f(W, m, n, ldw, LO, ldlo, LI, ldli, ctypes.byref(qq) if qq is not None else None,
+                 codes, ldc, scales, delta, ldd, DO, DI, loss, None, None, ws, nb, None)
+
+    assert call(W=None) == 1
+    assert call(m=0) == 1
+    assert call(n=-3) == 1
+    assert call(ldw=n - 1) == 1
+    assert call(ldc=n - 1) == 1
+    assert call(ldlo=m - 1) == 1
+    assert call(ldli=n - 1) == 1
+    assert call(codes=None) == 1
+    assert call(scales=None) == 1
+    assert call(qq=None) == 1
+    assert call(delta=FAKE, ldd=n - 1) == 1
+    assert call(qq=b._Quantizer(0, 0, 0, None)) == 1
+    assert call(qq=b._Quantizer(9, 0, 0, None)) == 1
+    assert call(qq=b._Quantizer(2, 2, 0, None)) == 1
+    assert call(loss=FAKE) == 1                       # D_I missing
+    assert call(loss=FAKE, DI=FAKE) == 1              # D_O missing with L_O given
+    assert call(ws=None) == 3
+    assert call(nb=need - 1) == 3
+    assert lib.bakron_solve_workspace_bytes(0, 5) == 0

@@ -1,0 +1,264 @@
+"""GPU parity of the HIP path against the CPU oracle (element by element).
+
+Acceptance (from the method's definition; see the oracle's replay()):
+  * codes: identical to the oracle's rounding of the pre-rounding value that the
+    rule gives with the device's own committed error, except counted flips whose
+    value lies within 1e-4 grid steps of the boundary between the two codes;
+  * scales: bit-identical (both sides compute them in fp32);
+  * proxy loss: within 1e-4 relative of the oracle's;
+  * Hessian accumulation: |H^ - H| <= 4 u sqrt(max(T, 64)) (|X|^T |X| / T)
+    entrywise (fp32 accumulation over T terms, u = 2^-24);
+  * LDL: fp64 on the device, so L^ and D^ agree with the fp64 oracle to a
+    couple of fp32 ulps; backward error ||H - (L^+I)D^(L^+I)^T|| / ||H|| <= 1e-6.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+U32 = 2.0 ** -24
+
+
+def note(msg):
+    print("[gpu-case] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def bk():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kronecker_hessian_rounding_amd as m
+    return m
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def factors(m, n, T=None, name="tiny", one_sided=False):
+    """Damped fp64 oracle factors for scaled workloads; returned as fp32 (shared inputs)."""
+    T = T or max(4 * max(m, n), 256)
+    w, x, g = workloads.make_inputs(name, m=m, n=n, T=T)
+    HI = oracle.damp(oracle.hessian(x))
+    LI, DI = oracle.udu(HI)
+    if one_sided:
+        LO, DO = None, np.full(m, 1.0)
+    else:
+        HO = oracle.damp(oracle.hessian(g))
+        LO, DO = oracle.udu(HO)
+    f32 = lambda a: None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+    return w, f32(LO), f32(LI), f32(DO), f32(DI)
+
+
+def check_solve(bk, w, LO, LI, DO, DI, bits, rounding="nearest", seed=0, row_scale=None,
+                free_run=True, label=""):
+    m, n = w.shape
+    note("solve %s m=%d n=%d bits=%d %s seed=%d" % (label, m, n, bits, rounding, seed))
+    d = dev()
+    T = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(d)
+    res = bk.solve(T(w), T(LO), T(LI), bits, rounding, seed,
+                   row_scale=T(row_scale), D_O=T(DO) if LO is not None else None, D_I=T(DI),
+                   want_delta=True, want_loss=True)
+    torch.cuda.synchronize()
+    assert int(res.info.item()) == 0
+    codes = res.codes.cpu().numpy()
+    scales = res.scales.cpu().numpy()
+    if row_scale is None:
+        assert np.array_equal(scales, oracle.row_scales(w, bits))
+    else:
+        assert np.array_equal(scales, row_scale)
+    lo64 = None if LO is None else LO.astype(np.float64)
+    rp = oracle.replay(w, lo64, LI.astype(np.float64), scales, bits, codes, rounding, seed,
+                       DO=DO.astype(np.float64), DI=DI.astype(np.float64))
+    assert rp["bad"] == 0, ("mismatches outside the 1e-4 band", rp["bad"], rp["bad_index"])
+    assert rp["max_flip_margin"] < 1e-4
+    # the device's committed error is W* - s (c - Lq/2)
+    Lq = 2**bits - 1
+    dl = res.delta.cpu().numpy().astype(np.float64)
+    exact = w.astype(np.float64) - scales[:, None].astype(np.float64) * (codes - Lq / 2.0)
+    assert np.max(np.abs(dl - exact)) <= 2 * U32 * np.max(np.abs(exact)) + 1e-30
+    loss = float(res.loss.item())
+    # 1e-4 relative, with a floor for degenerate near-zero losses (every value on the grid):
+    # 1e-7 of the size of the loss bound sum_i D_O,i s_i^2/4 tr(D_I)
+    floor = 1e-7 * oracle.bound_terms(scales, DO, DI)[0]
+    tol = lambda ref: 1e-4 * abs(ref) + floor
+    assert abs(loss - rp["loss"]) <= tol(rp["loss"]), (loss, rp["loss"])
+    assert int(res.clamped.item()) >= 0
+    out = dict(flips=rp["flips"], loss=loss, codes=codes)
+    if free_run:
+        fr = oracle.sweep(w, lo64, LI.astype(np.float64), scales, bits, rounding, seed)
+        mism = int((fr["codes"] != codes).sum())
+        fl = oracle.loss_identity(fr["eta"], DO.astype(np.float64), DI.astype(np.float64))
+        out.update(free_mismatch=mism, free_loss=fl)
+        note("  flips=%d free-run mismatches=%d loss=%.8g free=%.8g clamped=%d/%d" % (
+            rp["flips"], mism, loss, fl, int(res.clamped.item()), fr["clamped"]))
+        if mism == 0:
+            assert int(res.clamped.item()) == fr["clamped"]
+        assert abs(loss - fl) <= tol(fl)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Hessian factor accumulation
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("T,d", [(1024, 64), (333, 100), (8192, 512), (1, 5), (2000, 129), (0, 7)])
+def test_hessian_accum_matches_oracle(bk, T, d):
+    note("hessian T=%d d=%d" % (T, d))
+    x = workloads.make_x(max(T, 1), d, 99 + d, "gauss", 2 if d > 2 else 0)[:T]
+    X = torch.from_numpy(np.ascontiguousarray(x)).to(dev())
+    if T == 0:
+        H = torch.full((d, d), 3.0, device=dev())
+        bk.hessian_accum(X, H, alpha=1.0, beta=0.5)
+        assert torch.all(H.cpu() == 1.5)
+        return
+    H = bk.hessian_accum(X).cpu().numpy()
+    assert np.array_equal(H, H.T)
+    ref = oracle.hessian(x)
+    ax = np.abs(x.astype(np.float64))
+    bound = 4 * U32 * np.sqrt(max(T, 64)) * (ax.T @ ax) / T + 1e-30
+    assert np.all(np.abs(H - ref) <= bound), np.max(np.abs(H - ref) / bound)
+
+
+def test_hessian_accum_chunks_and_strides(bk):
+    note("hessian chunked + strided")
+    x = workloads.make_x(3000, 96, 5, "gauss", 2)
+    big = np.zeros((3000, 128), dtype=np.float32)
+    big[:, :96] = x
+    Xb = torch.from_numpy(big).to(dev())
+    Xv = Xb[:, :96]  # leading dimension 128
+    H = torch.empty((96, 96), device=dev())
+    bk.hessian_accum(Xv[:1000], H, alpha=1.0 / 3000, beta=0.0)
+    bk.hessian_accum(Xv[1000:], H, alpha=1.0 / 3000, beta=1.0)
+    ref = oracle.hessian(x)
+    ax = np.abs(x.astype(np.float64))
+    bound = 8 * U32 * np.sqrt(3000) * (ax.T @ ax) / 3000
+    assert np.all(np.abs(H.cpu().numpy() - ref) <= bound)
+
+
+# ----------------------------------------------------------------------------
+# damped LDL
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("d", [1, 5, 64, 100, 257, 512, 1000])
+def test_ldl_matches_oracle(bk, d):
+    note("ldl d=%d" % d)
+    x = workloads.make_x(max(2 * d, 64), d, 7 + d, "gauss", min(2, d))
+    H32 = oracle.hessian(x).astype(np.float32)
+    ref_H = oracle.damp(H32.astype(np.float64), 0.01)
+    L, D = oracle.udu(ref_H)
+    Ht = torch.from_numpy(H32.copy()).to(dev())
+    Hg, Dg = bk.ldl(Ht, 0.01)
+    Hc = Hg.cpu().numpy()
+    Lg = np.triu(Hc, 1).astype(np.float64)
+    Dv = Dg.cpu().numpy().astype(np.float64)
+    assert np.all(np.tril(Hc, -1) == 0)
+    assert np.array_equal(np.diag(Hc), Dg.cpu().numpy())
+    assert np.all(np.abs(Lg - L) <= 4 * U32 * np.abs(L) + 1e-6 * U32 * max(1.0, np.abs(L).max()))
+    assert np.all(np.abs(Dv - D) <= 4 * U32 * D)
+    A = Lg + np.eye(d)
+    rec = A @ np.diag(Dv) @ A.T
+    assert np.linalg.norm(rec - ref_H) / np.linalg.norm(ref_H) < 1e-6
+
+
+def test_ldl_reports_first_bad_pivot(bk):
+    note("ldl not-SPD")
+    x = workloads.make_x(256, 130, 3, "gauss", 2)
+    H = oracle.hessian(x).astype(np.float32)
+    H[77, 77] = -5.0
+    H[120, 120] = -5.0
+    with pytest.raises(ValueError, match="pivot 120"):
+        oracle.udu(oracle.damp(H.astype(np.float64)))
+    with pytest.raises(bk.BakronError) as ei:
+        bk.ldl(torch.from_numpy(H).to(dev()), 0.01)
+    assert ei.value.status == bk.BAKRON_E_NOT_SPD
+    assert ei.value.bad_pivot == 120
+
+
+# ----------------------------------------------------------------------------
+# the BaKron solve
+# ----------------------------------------------------------------------------
+def test_solve_tiny_config_nearest(bk):
+    w, x, g = workloads.make_inputs("tiny")
+    HI, HO = oracle.damp(oracle.hessian(x)), oracle.damp(oracle.hessian(g))
+    (LI, DI), (LO, DO) = oracle.udu(HI), oracle.udu(HO)
+    f = lambda a: a.astype(np.float32)
+    out = check_solve(bk, w, f(LO), f(LI), f(DO), f(DI), 2, label="tiny")
+    assert out["free_mismatch"] == 0
+
+
+def test_solve_tiny_config_stochastic(bk):
+    w, LO, LI, DO, DI = factors(64, 64, 1024)
+    check_solve(bk, w, LO, LI, DO, DI, 2, "stochastic", seed=4000, label="tiny-stoch")
+
+
+@pytest.mark.parametrize("m,n", [(1, 1), (1, 64), (64, 1), (3, 200), (65, 129), (100, 70),
+                                 (130, 66), (128, 128), (200, 333)])
+def test_solve_ragged_shapes(bk, m, n):
+    w, LO, LI, DO, DI = factors(m, n)
+    check_solve(bk, w, LO, LI, DO, DI, 2, label="ragged")
+
+
+@pytest.mark.parametrize("bits", [1, 3, 4, 8])
+def test_solve_bit_widths(bk, bits):
+    w, LO, LI, DO, DI = factors(96, 160)
+    check_solve(bk, w, LO, LI, DO, DI, bits, label="bits")
+
+
+def test_solve_one_sided_is_ldlq(bk):
+    w, LO, LI, DO, DI = factors(150, 200, one_sided=True)
+    out = check_solve(bk, w, None, LI, DO, DI, 3, label="one-sided")
+    # H_O = I: the rows are independent one-sided LDLQ problems
+    assert out["free_mismatch"] == 0
+
+
+def test_solve_diagonal_factors_is_rtn(bk):
+    w, _, _, _, _ = factors(70, 90)
+    d = dev()
+    res = bk.solve(torch.from_numpy(w).to(d), None, None, 3)
+    s = oracle.row_scales(w, 3)
+    rtn = np.clip(np.floor(w.astype(np.float64) / s[:, None].astype(np.float64) + 3.5 + 0.5), 0, 7)
+    got = res.codes.cpu().numpy()
+    y = w.astype(np.float64) / s[:, None].astype(np.float64) + 3.5
+    tie = np.abs((y - np.floor(y)) - 0.5) < 1e-5
+    assert np.all((got == rtn) | tie)
+
+
+def test_solve_user_scales(bk):
+    w, LO, LI, DO, DI = factors(80, 100)
+    rs = (1.7 * np.max(np.abs(w), axis=1) / 7.0).astype(np.float32)
+    check_solve(bk, w, LO, LI, DO, DI, 3, row_scale=rs, label="user-scales")
+
+
+def test_solve_reports_zero_row(bk):
+    w, LO, LI, DO, DI = factors(70, 40)
+    w[33] = 0.0
+    d = dev()
+    res = bk.solve(torch.from_numpy(w).to(d), torch.from_numpy(LO).to(d),
+                   torch.from_numpy(LI).to(d), 2)
+    assert int(res.info.item()) == 34
+
+
+def test_solve_small_config(bk):
+    w, x, g = workloads.make_inputs("small")
+    HI, HO = oracle.damp(oracle.hessian(x)), oracle.damp(oracle.hessian(g))
+    (LI, DI), (LO, DO) = oracle.udu(HI), oracle.udu(HO)
+    f = lambda a: a.astype(np.float32)
+    check_solve(bk, w, f(LO), f(LI), f(DO), f(DI), 3, label="small")
+    check_solve(bk, w, None, f(LI), np.full(512, 1.0, np.float32), f(DI), 3, label="small-H_O=I")
+
+
+def test_solve_is_deterministic(bk):
+    w, LO, LI, DO, DI = factors(300, 260)
+    d = dev()
+    T = lambda a: torch.from_numpy(a).to(d)
+    a = bk.solve(T(w), T(LO), T(LI), 2, D_O=T(DO), D_I=T(DI), want_loss=True, want_delta=True)
+    a_codes, a_delta, a_loss = a.codes.clone(), a.delta.clone(), a.loss.clone()
+    b = bk.solve(T(w), T(LO), T(LI), 2, D_O=T(DO), D_I=T(DI), want_loss=True, want_delta=True)
+    assert torch.equal(a_codes, b.codes) and torch.equal(a_delta, b.delta)
+    assert torch.equal(a_loss, b.loss)
