@@ -102,6 +102,100 @@ __device__ __forceinline__ void tile_gemm_f32(const float* __restrict__ A, int64
     }
 }
 
+// ---------------------------------------------------------------------------
+// fp32 64x64 tile, 32-deep k-slices. The slices are stored transposed in LDS
+// ([r][k], row stride 36 floats) so that each lane fetches the 16 k-values it
+// feeds to 16 consecutive MFMAs with four ds_read_b128: in MFMA m, lanes of
+// half h (lane / 32) supply k = 16 h + m, so MFMA m accumulates
+// k in {m, 16 + m} and the 16 MFMAs cover the whole slice.
+// ---------------------------------------------------------------------------
+constexpr int kKT32 = 32;
+constexpr int kLdT = kKT32 + 4;
+struct GemmSmemT {
+    float a[2][kTile][kLdT];
+    float b[2][kTile][kLdT];
+};
+
+// Thread t loads rows k0 + (t >> 4) and k0 + 16 + (t >> 4), columns
+// 4 (t & 15) .. +3, of a K-major operand; zeros outside [0, K) x [0, R).
+__device__ __forceinline__ void slice_load32(const float* __restrict__ A, int64_t lda, int R,
+                                             int64_t K, int64_t k0, bool fast, f32x4 (&v)[2]) {
+    const int t = threadIdx.x;
+    const int c4 = (t & 15) << 2;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t k = k0 + (t >> 4) + 16 * h;
+        const float* p = A + k * lda + c4;
+        if (fast) {
+            v[h] = *reinterpret_cast<const f32x4*>(p);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[h][e] = (k < K && c4 + e < R) ? p[e] : 0.0f;
+        }
+    }
+}
+
+__device__ __forceinline__ void slice_store32(float (&dst)[kTile][kLdT], const f32x4 (&v)[2]) {
+    const int t = threadIdx.x;
+    const int c4 = (t & 15) << 2;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[c4 + e][(t >> 4) + 16 * h] = v[h][e];
+}
+
+// acc += A^T B over K for the 64x64 tile (same operand convention as
+// tile_gemm_f32). All 256 threads of the workgroup must call it.
+__device__ __forceinline__ void tile_gemm32_f32(const float* __restrict__ A, int64_t lda, int R,
+                                                const float* __restrict__ B, int64_t ldb, int Cn,
+                                                int64_t K, f32x16& acc, GemmSmemT& sm) {
+    if (K <= 0) return;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int ra = (w >> 1) * 32 + (lane & 31);
+    const int rb = (w & 1) * 32 + (lane & 31);
+    const int kh = (lane >> 5) * 16;
+    // full, aligned slices take unchecked vector loads
+    const bool aligned = R == kTile && Cn == kTile && (lda & 3) == 0 && (ldb & 3) == 0 &&
+                         ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
+    const int64_t nk = (K + kKT32 - 1) / kKT32;
+    f32x4 va[2], vb[2];
+    {
+        const bool fast = aligned && kKT32 <= K;
+        slice_load32(A, lda, R, K, 0, fast, va);
+        slice_load32(B, ldb, Cn, K, 0, fast, vb);
+        slice_store32(sm.a[0], va);
+        slice_store32(sm.b[0], vb);
+    }
+    __syncthreads();
+    for (int64_t it = 0; it < nk; ++it) {
+        const int cur = (int)(it & 1);
+        const bool more = it + 1 < nk;
+        if (more) {
+            const int64_t k0 = (it + 1) * kKT32;
+            const bool fast = aligned && k0 + kKT32 <= K;
+            slice_load32(A, lda, R, K, k0, fast, va);
+            slice_load32(B, ldb, Cn, K, k0, fast, vb);
+        }
+        f32x4 fa[4], fb[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            fa[q] = *reinterpret_cast<const f32x4*>(&sm.a[cur][ra][kh + 4 * q]);
+            fb[q] = *reinterpret_cast<const f32x4*>(&sm.b[cur][rb][kh + 4 * q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[q][e], fb[q][e], acc, 0, 0, 0);
+        if (more) {
+            slice_store32(sm.a[cur ^ 1], va);
+            slice_store32(sm.b[cur ^ 1], vb);
+        }
+        __syncthreads();
+    }
+}
+
 // Position (row, col) inside the 64x64 tile of element v (0..15) of this
 // lane's fp32 accumulator (32x32x2 output layout: col = lane % 32,
 // row = 8*(v/4) + 4*(lane/32) + v%4 within the wave's quadrant).

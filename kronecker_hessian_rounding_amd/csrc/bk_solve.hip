@@ -31,10 +31,8 @@
 namespace bk {
 
 constexpr int kB = kTile;  // leaf edge
-constexpr int kNch = 16;   // maximum K-chunks per far-field product
-constexpr int kDs = 72;    // LDS row stride of the D tile (8 mod 32: conflict-free column walks)
-constexpr int kGs = 68;    // LDS row stride of the C tile (4 mod 32)
-constexpr int kLs = 72;    // LDS row stride of the L_I diagonal block
+constexpr int kNch = 8;    // maximum K-chunks per far-field product
+constexpr int kTargetWg = 1024;  // far-field workgroups aimed for per launch
 
 struct SolveParams {
     const float* W;
@@ -123,265 +121,298 @@ __global__ void k_solve_init(unsigned* counters, int ncounters, int* info) {
 }
 
 // ---------------------------------------------------------------------------
-// far-field GEMM role: one K-chunk of p (kind 0) or o^T (kind 1) of one leaf
-// of diagonal d1, from blocks at least two leaves away
+// far field of diagonal d: chunk c (of nch) of p (kind 0) or o^T (kind 1) of
+// one leaf, over every block above (p) or to the left (o) of the leaf. Each
+// chunk writes its own 64x64 partial; the leaf adds the partials in chunk
+// order, so the result does not depend on scheduling.
 // ---------------------------------------------------------------------------
-struct FarSmem {
-    GemmSmem<float> g;
-    int last;
-};
+__device__ __forceinline__ void chunk_range(int kblk, int nch, int c, int& b0, int& b1) {
+    const int len = (kblk + nch - 1) / nch;
+    b0 = min(c * len, kblk);
+    b1 = min(b0 + len, kblk);
+}
 
-__device__ void far_chunk(const SolveParams& p, int d1, int task, FarSmem& sm) {
-    const int slot = task / (2 * kNch);
-    const int kind = (task / kNch) & 1;
-    const int c = task % kNch;
-    const int I = leaf_lo(p, d1) + slot;
-    const int J = d1 - I;
-    if (I > leaf_hi(p, d1)) return;
-    const int kblk = (kind == 0) ? I - 1 : J - 1;
+__global__ __launch_bounds__(kThreads) void k_far(SolveParams p, int d, int nch) {
+    if (*p.info != INT_MAX) return;  // a row scale was invalid
+    __shared__ GemmSmemT sm;
+    const int task = blockIdx.x;
+    const int slot = task / (2 * nch);
+    const int kind = (task / nch) & 1;
+    const int c = task % nch;
+    const int I = leaf_lo(p, d) + slot;
+    const int J = d - I;
     if ((kind == 0 && !p.LO) || (kind == 1 && !p.LI)) return;
-    const int nv = nchunks(kblk, p.cbk);
-    if (c >= nv) return;
-    const int kb0 = c * p.cbk, kb1 = min(kb0 + p.cbk, kblk);
+    int kb0, kb1;
+    chunk_range(kind == 0 ? I : J, nch, c, kb0, kb1);
+    if (kb1 <= kb0) return;
     const int64_t i0 = (int64_t)I * kB, j0 = (int64_t)J * kB;
     const int R = (int)min<int64_t>(kB, p.m - i0), Cc = (int)min<int64_t>(kB, p.n - j0);
     const int64_t k0 = (int64_t)kb0 * kB, K = (int64_t)(kb1 - kb0) * kB;
     f32x16 acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-    int rows, cols;
-    if (kind == 0) {  // p[ii][jj] = sum_k L_O[k][i0+ii] D[k][j0+jj]
-        tile_gemm_f32(p.LO + k0 * p.ldlo + i0, p.ldlo, R, p.delta + k0 * p.ldd + j0, p.ldd, Cc, K,
-                      acc, sm.g);
-        rows = R;
-        cols = Cc;
-    } else {  // o^T[jj][ii] = sum_l L_I[l][j0+jj] C^T[l][i0+ii]
-        tile_gemm_f32(p.LI + k0 * p.ldli + j0, p.ldli, Cc, p.ct + k0 * p.m + i0, p.m, R, K, acc,
-                      sm.g);
-        rows = Cc;
-        cols = R;
-    }
-    (void)rows;
-    (void)cols;
-    const int par = d1 & 1;
-    float* part = part_ptr(p, par, slot, kind, c);
+    if (kind == 0)  // p[ii][jj] = sum_k L_O[k][i0+ii] D[k][j0+jj]
+        tile_gemm32_f32(p.LO + k0 * p.ldlo + i0, p.ldlo, R, p.delta + k0 * p.ldd + j0, p.ldd, Cc,
+                        K, acc, sm);
+    else  // o^T[jj][ii] = sum_l L_I[l][j0+jj] C^T[l][i0+ii]
+        tile_gemm32_f32(p.LI + k0 * p.ldli + j0, p.ldli, Cc, p.ct + k0 * p.m + i0, p.m, R, K, acc,
+                        sm);
+    float* part = part_ptr(p, 0, slot, kind, c);
     const int cc = acc32_col();
 #pragma unroll
     for (int v = 0; v < 16; ++v) part[acc32_row(v) * kB + cc] = acc[v];
-    // deterministic reduction by the last chunk to finish
-    __threadfence();
-    __syncthreads();
-    unsigned* ctr = p.counters + ((size_t)(par * p.maxleaf + slot) * 2 + kind);
-    if (threadIdx.x == 0) sm.last = (atomicAdd(ctr, 1u) == (unsigned)(nv - 1));
-    __syncthreads();
-    if (!sm.last) return;
-    __threadfence();
-    float* out = offs_ptr(p, par, slot, kind);
-    for (int e = threadIdx.x; e < kB * kB; e += kThreads) {
-        float s = 0.0f;
-        for (int q = 0; q < nv; ++q) s += part_ptr(p, par, slot, kind, q)[e];
-        out[e] = s;
-    }
-    if (threadIdx.x == 0) *ctr = 0u;
 }
 
 // ---------------------------------------------------------------------------
-// leaf role: solve the 64x64 leaf (I, J) of diagonal d
+// leaf solve: the 64x64 leaf (I, J) of diagonal d, given its far fields.
+//
+// Entry (i, j) is finalised at step i + j. Its in-leaf sums
+//   pn = sum_{k<i} L_O[k][i] D[k][j],   rn = sum_{l<j} g[i][l] L_I[l][j]
+// (g = C, the column feedback plus error of the row) are split into a bulk,
+// which only uses entries finalised two or more steps earlier, and the newest
+// term (k = i-1, l = j-1). Waves 0-3 compute the bulk of step st+1 while wave
+// 4 finalises step st, so the dependent chain per step is short and the bulk
+// LDS traffic overlaps it. The finaliser takes D[i-1][j] from the lane above
+// (it was that lane's result one step earlier) and g[i][j-1] from its own
+// previous step, so only the two bulk sums cross LDS on the chain.
+//
+// Bulk lanes are (row i, quarter q) with lane = 4 i + q; quarter q owns the
+// k / l chunks [8q, 8q+8) and [32+8q, 32+8q+8). With 68-float rows (16 bytes
+// of bank offset per row) the four b128 reads of a row pair hit eight
+// distinct bank groups.
 // ---------------------------------------------------------------------------
+constexpr int kLeafThreads = 5 * 64;
+constexpr int kTs = 68;  // row stride of the k/l-indexed tiles
+constexpr int kPs = 66;  // row stride of the per-entry inputs: anti-diagonal walks hit distinct banks
+
 struct LeafSmem {
-    union {
-        GemmSmem<float> g;  // prologue GEMMs
-        struct {
-            float Ds[kB][kDs];  // D of the leaf (0 where not yet known)
-            float Gs[kB][kGs];  // C of the leaf
-        } w;
-    } u;
-    float LIs[kB][kLs];      // L_I diagonal block, strictly upper (0 elsewhere)
-    float base[kB][kB + 1];  // W* + o
-    float pin[kB][kB + 1];   // p
-    float wst[kB][kB + 1];   // W*
-    uint8_t code[kB][kB];
+    float DT[kB][kTs];     // D transposed: DT[j][k] = D[k][j] (0 until known)
+    float Gs[kB][kTs];     // g = C of the leaf, row-major (0 until known)
+    float LIT[kB][kTs];    // L_I diagonal block transposed: LIT[j][l] = L_I[l][j], l < j
+    float base[kB][kPs];   // W* + o
+    float pin[kB][kPs];    // p
+    float wst[kB][kPs];    // W*
+    float pnb[2][kB];      // bulk sums, double buffered by step parity
+    float rnb[2][kB];
+    uint8_t code[kB][kB + 4];
     float DI[kB];
-    double red[kThreads];
-    int red_i[kThreads];
+    double red[kLeafThreads];
+    int red_i[kLeafThreads];
 };
 
-__device__ void leaf_solve(const SolveParams& p, int d, int slot, LeafSmem& sm) {
+__device__ __forceinline__ float lane_above(float x) {
+    // wave_shr:1 -- lane i receives lane i-1's value, lane 0 receives 0
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x138,
+                                                                  0xF, 0xF, false));
+}
+
+__global__ __launch_bounds__(kLeafThreads) void k_leaf(SolveParams p, int d, int nch) {
+    if (*p.info != INT_MAX) return;
+    __shared__ LeafSmem sm;
+    const int slot = blockIdx.x;
     const int I = leaf_lo(p, d) + slot;
     const int J = d - I;
     const int64_t i0 = (int64_t)I * kB, j0 = (int64_t)J * kB;
     const int R = (int)min<int64_t>(kB, p.m - i0), Cc = (int)min<int64_t>(kB, p.n - j0);
     const int t = threadIdx.x;
-    const int par = d & 1;
-    const int cc = acc32_col();
+    const int np = (p.LO && I > 0) ? nch : 0;  // partials of p and o^T to add
+    const int no = (p.LI && J > 0) ? nch : 0;
 
-    // ---- p: far part (precomputed) + adjacent block I-1 ----
-    {
-        f32x16 acc;
+    // ---- LDS set-up: far fields (sum of the K-chunk partials, in chunk order) ----
+    for (int g4 = t; g4 < kB * kB / 4; g4 += kLeafThreads) {
+        const int e = 4 * g4;
+        f32x4 pv = {0.f, 0.f, 0.f, 0.f}, ov = {0.f, 0.f, 0.f, 0.f};
+        f32x4 xp[kNch], xo[kNch];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-        if (p.LO && I >= 1) {
-            const int64_t k0 = i0 - kB;
-            tile_gemm_f32(p.LO + k0 * p.ldlo + i0, p.ldlo, R, p.delta + k0 * p.ldd + j0, p.ldd, Cc,
-                          kB, acc, sm.u.g);
+        for (int c = 0; c < kNch; ++c) {
+            int b0, b1;
+            chunk_range(I, nch, c, b0, b1);
+            xp[c] = (c < np && b1 > b0) ? *reinterpret_cast<const f32x4*>(part_ptr(p, 0, slot, 0, c) + e)
+                                        : f32x4{0.f, 0.f, 0.f, 0.f};
+            chunk_range(J, nch, c, b0, b1);
+            xo[c] = (c < no && b1 > b0) ? *reinterpret_cast<const f32x4*>(part_ptr(p, 0, slot, 1, c) + e)
+                                        : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        const bool far = p.LO && nchunks(I - 1, p.cbk) > 0;
-        const float* off = offs_ptr(p, par, slot, 0);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int r = acc32_row(v);
-            float x = acc[v];
-            if (far) x += off[r * kB + cc];
-            sm.pin[r][cc] = x;
+        for (int c = 0; c < kNch; ++c) {
+            pv += xp[c];
+            ov += xo[c];
         }
-    }
-    __syncthreads();
-    // ---- o^T: far part + adjacent block J-1; base = W* + o ----
-    {
-        f32x16 acc;
+        const int r = e / kB, c0 = e % kB;  // p: row r, cols c0..c0+3; o^T: row (= leaf col) r, leaf rows c0..
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-        if (p.LI && J >= 1) {
-            const int64_t l0 = j0 - kB;
-            tile_gemm_f32(p.LI + l0 * p.ldli + j0, p.ldli, Cc, p.ct + l0 * p.m + i0, p.m, R, kB,
-                          acc, sm.u.g);
-        }
-        const bool far = p.LI && nchunks(J - 1, p.cbk) > 0;
-        const float* off = offs_ptr(p, par, slot, 1);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int jj = acc32_row(v);  // o^T row = column of the leaf
-            float x = acc[v];
-            if (far) x += off[jj * kB + cc];
-            sm.base[cc][jj] = x;  // cc = leaf row
+        for (int k = 0; k < 4; ++k) {
+            sm.pin[r][c0 + k] = pv[k];
+            sm.base[c0 + k][r] = ov[k];
         }
     }
     __syncthreads();
-    // ---- LDS set-up for the wavefront ----
-    for (int e = t; e < kB * kB; e += kThreads) {
+    for (int e = t; e < kB * kB; e += kLeafThreads) {
         const int i = e / kB, j = e % kB;
-        float wv = 0.0f;
-        if (i < R && j < Cc) wv = p.W[(i0 + i) * p.ldw + j0 + j];
-        sm.base[i][j] += wv;
+        const float wv = (i < R && j < Cc) ? p.W[(i0 + i) * p.ldw + j0 + j] : 0.0f;
+        // L_I[l][jj] stored at LIT[jj][l] (here l = i, jj = j)
+        const float lv = (p.LI && i < j && j < Cc) ? p.LI[(j0 + i) * p.ldli + j0 + j] : 0.0f;
         sm.wst[i][j] = wv;
-        sm.u.w.Ds[i][j] = 0.0f;
-        sm.u.w.Gs[i][j] = 0.0f;
-        float l = 0.0f;
-        if (p.LI && i < j && j < Cc) l = p.LI[(j0 + i) * p.ldli + j0 + j];
-        sm.LIs[i][j] = l;
+        sm.base[i][j] += wv;
+        sm.LIT[j][i] = lv;
+        sm.DT[i][j] = 0.0f;
+        sm.Gs[i][j] = 0.0f;
         sm.code[i][j] = 0;
     }
-    if (t < kB) sm.DI[t] = (p.want_loss && t < Cc) ? p.DI[j0 + t] : 0.0f;
-
-    const int i = t >> 2;  // leaf row of this thread
-    const int q = t & 3;   // quarter of the in-leaf sums
-    float lo_reg[16];      // L_O[i0 + 4r + q][i0 + i], strictly above the diagonal
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int k = 4 * r + q;
-        lo_reg[r] = (p.LO && k < i && i < R) ? p.LO[(i0 + k) * p.ldlo + i0 + i] : 0.0f;
+    if (t < kB) {
+        sm.DI[t] = (p.want_loss && t < Cc) ? p.DI[j0 + t] : 0.0f;
+        sm.pnb[0][t] = sm.pnb[1][t] = 0.0f;
+        sm.rnb[0][t] = sm.rnb[1][t] = 0.0f;
     }
-    const int Lq = (1 << p.bits) - 1;
-    const float half = 0.5f * (float)Lq;
-    const float s = (i < R) ? p.scales[i0 + i] : 1.0f;
-    const float dO = (p.want_loss && i < R) ? (p.DO ? p.DO[i0 + i] : 1.0f) : 0.0f;
+
+    const int w = t >> 6;
     double loss = 0.0;
     int nclamp = 0;
-    __syncthreads();
-
-    // ---- in-leaf anti-diagonal wavefront: 2*64-1 dependent steps ----
-    for (int st = 0; st < 2 * kB - 1; ++st) {
-        const int j = st - i;
-        const bool act = (j >= 0) && (j < kB);
-        float pn = 0.0f, rn = 0.0f;
-        if (act) {
+    if (w < 4) {
+        // ---------------- bulk waves ----------------
+        const int i = t >> 2;
+        const int q = t & 3;
+        const int ka = 8 * q, kb = 32 + 8 * q;  // the quarter's two 8-wide chunks
+        float lo_a[8], lo_b[8];                 // L_O[i0 + k][i0 + i] for k <= i - 2
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int k = 4 * r + q;
-                pn = fmaf(lo_reg[r], sm.u.w.Ds[k][j], pn);
-                rn = fmaf(sm.u.w.Gs[i][k], sm.LIs[k][j], rn);
-            }
+        for (int e = 0; e < 8; ++e) {
+            lo_a[e] = (p.LO && ka + e <= i - 2 && i < R) ? p.LO[(i0 + ka + e) * p.ldlo + i0 + i] : 0.0f;
+            lo_b[e] = (p.LO && kb + e <= i - 2 && i < R) ? p.LO[(i0 + kb + e) * p.ldlo + i0 + i] : 0.0f;
         }
-        pn = quad_sum(pn);
-        rn = quad_sum(rn);
-        if (act && i < R && j < Cc) {
-            const float P = sm.pin[i][j] + pn;
-            const float tv = sm.base[i][j] + P + rn;
-            const float y = tv / s + half;
-            float cf;
-            if (p.stochastic) {
-                const float u = uniform24(p.seed, (uint64_t)(i0 + i) * (uint64_t)p.n + (uint64_t)(j0 + j));
-                cf = floorf(y + u);
-            } else {
-                cf = floorf(y + 0.5f);
-            }
-            const bool clamp = (cf < 0.0f) || (cf > (float)Lq);
-            cf = fminf(fmaxf(cf, 0.0f), (float)Lq);
-            const float wv = sm.wst[i][j];
-            const float dl = fmaf(-s, cf - half, wv);  // D = W* - s (c - Lq/2), one rounding
-            if (q == 0) {
-                sm.u.w.Ds[i][j] = dl;
-                sm.u.w.Gs[i][j] = P + dl;
-                sm.code[i][j] = (uint8_t)cf;
-                const float eta = tv - s * (cf - half);
-                loss += (double)dO * (double)sm.DI[j] * (double)eta * (double)eta;
-                nclamp += clamp ? 1 : 0;
-            }
-        }
+        const bool pa = p.LO && ka <= i - 2, pbl = p.LO && kb <= i - 2;
         __syncthreads();
+        for (int st = 0; st < 2 * kB - 1; ++st) {
+            const int jn = st + 1 - i;  // entry (i, jn) is finalised at the next step
+            float pn = 0.0f, rn = 0.0f;
+            if (jn >= 0 && jn < kB) {
+                const float* dcol = &sm.DT[jn][0];
+                if (pa) {
+                    const f32x4 d0 = *reinterpret_cast<const f32x4*>(dcol + ka);
+                    const f32x4 d1 = *reinterpret_cast<const f32x4*>(dcol + ka + 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        pn = fmaf(lo_a[e], d0[e], pn);
+                        pn = fmaf(lo_a[4 + e], d1[e], pn);
+                    }
+                }
+                if (pbl) {
+                    const f32x4 d0 = *reinterpret_cast<const f32x4*>(dcol + kb);
+                    const f32x4 d1 = *reinterpret_cast<const f32x4*>(dcol + kb + 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        pn = fmaf(lo_b[e], d0[e], pn);
+                        pn = fmaf(lo_b[4 + e], d1[e], pn);
+                    }
+                }
+                // rn bulk: l <= jn - 2 (l = jn - 1 is the newest term, masked below)
+                const float* grow = &sm.Gs[i][0];
+                const float* lcol = &sm.LIT[jn][0];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int kc = h ? kb : ka;
+                    if (kc <= jn - 2) {
+                        const f32x4 g0 = *reinterpret_cast<const f32x4*>(grow + kc);
+                        const f32x4 g1 = *reinterpret_cast<const f32x4*>(grow + kc + 4);
+                        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lcol + kc);
+                        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lcol + kc + 4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            rn = fmaf(g0[e], (kc + e == jn - 1) ? 0.0f : l0[e], rn);
+                            rn = fmaf(g1[e], (kc + 4 + e == jn - 1) ? 0.0f : l1[e], rn);
+                        }
+                    }
+                }
+            }
+            pn = quad_sum(pn);
+            rn = quad_sum(rn);
+            if (q == 0 && jn >= 0 && jn < kB) {
+                sm.pnb[(st + 1) & 1][i] = pn;
+                sm.rnb[(st + 1) & 1][i] = rn;
+            }
+            __syncthreads();
+        }
+    } else {
+        // ---------------- finaliser wave: lane i owns row i ----------------
+        const int i = t & 63;
+        const float lo_last = (p.LO && i >= 1 && i < R) ? p.LO[(i0 + i - 1) * p.ldlo + i0 + i] : 0.0f;
+        const int Lq = (1 << p.bits) - 1;
+        const float half = 0.5f * (float)Lq;
+        const float s = (i < R) ? p.scales[i0 + i] : 1.0f;
+        const float rs = 1.0f / s;
+        const float dO = (p.want_loss && i < R) ? (p.DO ? p.DO[i0 + i] : 1.0f) : 0.0f;
+        float d_last = 0.0f;  // D of this row's previous entry (read by the lane below)
+        float g_last = 0.0f;  // g of this row's previous entry
+        __syncthreads();
+        // static inputs of the first entry of the row (j = 0) are read at step i
+        float x_pin = 0.f, x_base = 0.f, x_w = 0.f, x_l = 0.f, x_di = 0.f;
+        for (int st = 0; st < 2 * kB - 1; ++st) {
+            const int j = st - i;
+            const float dprev = lane_above(d_last);
+            if (j >= 0 && j < kB) {
+                x_pin = sm.pin[i][j];
+                x_base = sm.base[i][j];
+                x_w = sm.wst[i][j];
+                x_l = (j >= 1) ? sm.LIT[j][j - 1] : 0.0f;
+                x_di = sm.DI[j];
+            }
+            if (j >= 0 && j < Cc && i < R) {
+                float u = 0.5f;
+                if (p.stochastic)
+                    u = uniform24(p.seed, (uint64_t)(i0 + i) * (uint64_t)p.n + (uint64_t)(j0 + j));
+                const float P = x_pin + (sm.pnb[st & 1][i] + lo_last * dprev);
+                const float Rr = sm.rnb[st & 1][i] + g_last * x_l;
+                const float tv = x_base + P + Rr;
+                const float y = fmaf(tv, rs, half);
+                float cf = floorf(y + u);
+                nclamp += (cf < 0.0f || cf > (float)Lq) ? 1 : 0;
+                cf = fminf(fmaxf(cf, 0.0f), (float)Lq);
+                const float dl = fmaf(-s, cf - half, x_w);  // D = W* - s (c - Lq/2)
+                const float g = P + dl;
+                sm.DT[j][i] = dl;
+                sm.Gs[i][j] = g;
+                sm.code[i][j] = (uint8_t)cf;
+                d_last = dl;
+                g_last = g;
+                const float eta = fmaf(-s, cf - half, tv);
+                loss += (double)(dO * x_di) * (double)eta * (double)eta;
+            }
+            __syncthreads();
+        }
     }
 
     // ---- outputs ----
-    for (int e = t; e < kB * kB; e += kThreads) {
+    for (int e = t; e < kB * kB; e += kLeafThreads) {
         const int ii = e / kB, jj = e % kB;
         if (ii < R && jj < Cc) {
             p.codes[(i0 + ii) * p.ldc + j0 + jj] = sm.code[ii][jj];
-            p.delta[(i0 + ii) * p.ldd + j0 + jj] = sm.u.w.Ds[ii][jj];
+            p.delta[(i0 + ii) * p.ldd + j0 + jj] = sm.DT[jj][ii];
         }
         const int ci = e % kB, cj = e / kB;  // C^T written along the leaf's rows
-        if (ci < R && cj < Cc) p.ct[(j0 + cj) * p.m + i0 + ci] = sm.u.w.Gs[ci][cj];
+        if (ci < R && cj < Cc) p.ct[(j0 + cj) * p.m + i0 + ci] = sm.Gs[ci][cj];
     }
-    if (p.want_loss) {
-        sm.red[t] = loss;
-        sm.red_i[t] = nclamp;
-        __syncthreads();
-        for (int o = kThreads / 2; o > 0; o >>= 1) {
-            if (t < o) {
-                sm.red[t] += sm.red[t + o];
-                sm.red_i[t] += sm.red_i[t + o];
-            }
-            __syncthreads();
+    sm.red[t] = loss;
+    sm.red_i[t] = nclamp;
+    __syncthreads();
+    if (t < 64) {
+        double a = 0.0;
+        int b = 0;
+        for (int k = t; k < kLeafThreads; k += 64) {
+            a += sm.red[k];
+            b += sm.red_i[k];
         }
-        if (t == 0) {
-            p.leaf_loss[(size_t)I * p.N + J] = sm.red[0];
-            p.leaf_clamp[(size_t)I * p.N + J] = sm.red_i[0];
-        }
-    } else {
-        sm.red_i[t] = nclamp;
-        __syncthreads();
-        for (int o = kThreads / 2; o > 0; o >>= 1) {
-            if (t < o) sm.red_i[t] += sm.red_i[t + o];
-            __syncthreads();
-        }
-        if (t == 0) {
-            p.leaf_loss[(size_t)I * p.N + J] = 0.0;
-            p.leaf_clamp[(size_t)I * p.N + J] = sm.red_i[0];
-        }
+        sm.red[t] = a;
+        sm.red_i[t] = b;
     }
-}
-
-// One launch per leaf-diagonal d: workgroups [0, nleaf(d)) solve the leaves of
-// d; the rest form the far-field chunks of diagonal d + 1.
-__global__ __launch_bounds__(kThreads) void k_diag(SolveParams p, int d, int nleaf) {
-    if (*p.info != INT_MAX) return;  // a row scale was invalid
-    __shared__ union {
-        LeafSmem leaf;
-        FarSmem far;
-    } sm;
-    if ((int)blockIdx.x < nleaf) {
-        leaf_solve(p, d, blockIdx.x, sm.leaf);
-    } else {
-        far_chunk(p, d + 1, blockIdx.x - nleaf, sm.far);
+    __syncthreads();
+    for (int o = 32; o > 0; o >>= 1) {
+        if (t < o) {
+            sm.red[t] += sm.red[t + o];
+            sm.red_i[t] += sm.red_i[t + o];
+        }
+        __syncthreads();
+    }
+    if (t == 0) {
+        p.leaf_loss[(size_t)I * p.N + J] = sm.red[0];
+        p.leaf_clamp[(size_t)I * p.N + J] = sm.red_i[0];
     }
 }
 
@@ -429,7 +460,7 @@ Layout layout(int64_t m, int64_t n) {
     L.M = (int)((m + kB - 1) / kB);
     L.N = (int)((n + kB - 1) / kB);
     L.maxleaf = std::min(L.M, L.N);
-    const int kmax = std::max(L.M, L.N) - 2;
+    const int kmax = std::max(L.M, L.N) - 1;
     L.cbk = std::max(1, (kmax + kNch - 1) / kNch);
     size_t o = 0;
     L.ct = o;
@@ -437,11 +468,11 @@ Layout layout(int64_t m, int64_t n) {
     L.delta = o;
     o += align256(sizeof(float) * (size_t)m * (size_t)n);
     L.offs = o;
-    o += align256(sizeof(float) * 2 * (size_t)L.maxleaf * 2 * kB * kB);
+    o += align256(sizeof(float) * (size_t)L.maxleaf * 2 * kB * kB);
     L.parts = o;
-    o += align256(sizeof(float) * 2 * (size_t)L.maxleaf * 2 * kNch * kB * kB);
+    o += align256(sizeof(float) * (size_t)L.maxleaf * 2 * kNch * kB * kB);
     L.counters = o;
-    o += align256(sizeof(unsigned) * 2 * (size_t)L.maxleaf * 2);
+    o += align256(sizeof(unsigned) * (size_t)L.maxleaf * 2);
     L.leaf_loss = o;
     o += align256(sizeof(double) * (size_t)L.M * L.N);
     L.leaf_clamp = o;
@@ -490,7 +521,7 @@ int run_solve(const SolveArgs& a, void* ws, hipStream_t stream) {
     p.maxleaf = L.maxleaf;
     p.cbk = L.cbk;
 
-    const int ncnt = 2 * L.maxleaf * 2;
+    const int ncnt = L.maxleaf * 2;
     hipLaunchKernelGGL(k_solve_init, dim3((ncnt + 255) / 256), dim3(256), 0, stream, p.counters,
                        ncnt, p.info);
     hipLaunchKernelGGL(k_scales, dim3((unsigned)a.m), dim3(kThreads), 0, stream, a.W, a.n, a.ldw,
@@ -499,13 +530,18 @@ int run_solve(const SolveArgs& a, void* ws, hipStream_t stream) {
     for (int d = 0; d < ndiag; ++d) {
         const int lo = std::max(0, d - (L.N - 1)), hi = std::min(d, L.M - 1);
         const int nleaf = hi - lo + 1;
-        int nfar = 0;
-        if (d + 1 < ndiag) {
-            const int lo1 = std::max(0, d + 1 - (L.N - 1)), hi1 = std::min(d + 1, L.M - 1);
-            nfar = (hi1 - lo1 + 1) * 2 * kNch;
+        // K-chunks per far-field product: enough workgroups to fill the chip,
+        // chunks of at least 4 blocks (256)
+        const int kmax = std::max(hi, d - lo);
+        int nch = std::max(1, (kTargetWg + 2 * nleaf - 1) / (2 * nleaf));
+        nch = std::min(nch, std::max(1, kmax / 4));
+        nch = std::min(nch, kNch);
+        if (d > 0) {  // far fields of diagonal d (every leaf of d - 1 is done)
+            hipLaunchKernelGGL(k_far, dim3((unsigned)(nleaf * 2 * nch)), dim3(kThreads), 0, stream,
+                               p, d, nch);
         }
-        hipLaunchKernelGGL(k_diag, dim3((unsigned)(nleaf + nfar)), dim3(kThreads), 0, stream, p, d,
-                           nleaf);
+        hipLaunchKernelGGL(k_leaf, dim3((unsigned)nleaf), dim3(kLeafThreads), 0, stream, p, d,
+                           nch);
     }
     hipLaunchKernelGGL(k_solve_finish, dim3(1), dim3(kThreads), 0, stream, p.leaf_loss,
                        p.leaf_clamp, L.M * L.N, a.loss, a.clamped, p.info, a.info);
