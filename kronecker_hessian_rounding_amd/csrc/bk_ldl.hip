@@ -5,17 +5,17 @@
 //
 // With J the index reversal, J H J = C' C'^T (lower Cholesky) gives H = C C^T
 // with C = J C' J upper triangular; then L + I = C diag(C)^-1 and D = diag(C)^2.
-// C is computed by a right-looking blocked Cholesky that runs from the LAST
-// index block to the first, in fp64 on the device:
-//   for each 64-wide block [k0, k1), last first:
-//     diag   : C22 = reverse Cholesky of A[k0:k1, k0:k1] (one workgroup, LDS),
-//              plus C22^-1 for the panel solve
-//     panel  : C12 = A[0:k0, k0:k1] C22^-T  (rows independent)
-//     update : A[0:k0, s0:k0] -= C12 C12[s0:k0]^T inside the current 256-wide
-//              super-panel [s0, s1) (fp64 MFMA tiles)
-//   and after each super-panel one trailing update of A[0:s0, 0:s0] with
-//   K = s1 - s0 (fp64 MFMA tiles, upper triangle only).
-// Only the upper triangle of the working copy is ever read or written.
+// C is computed in fp64 by a right-looking blocked Cholesky that runs from the
+// LAST 64-wide index block to the first. The working copy A holds the lower
+// triangle (A[r][c] = H[r][c], r >= c), so a factored block column of C is
+// stored as a block ROW of A (C^T), contiguous along the long index. Every
+// contraction then has the "TN" form of bk_common.hpp (both operands K-major):
+//   diag  : C22 = reverse Cholesky of the 64x64 diagonal block, and C22^-1
+//   panel : C12^T = C22^-1 A[k0:k1, 0:k0]           (MFMA, in place)
+//   inner : A[s0:k0, 0:k0] -= C12 C12^T restricted to the current 256-wide
+//           super-panel's rows                        (MFMA, lower part)
+//   outer : after each super-panel, A[0:s0, 0:s0] -= C_S C_S^T with
+//           K = the super-panel width                 (MFMA, lower part)
 #include <algorithm>
 
 #include "bk_common.hpp"
@@ -26,9 +26,8 @@ namespace bk {
 constexpr int kSuper = 256;  // super-panel width (K of the big trailing updates)
 
 struct LdlWs {
-    double* A;     // d x d working copy (upper triangle used), ld = d
-    double* CT;    // kSuper x d: CT[q][r] = C[r][s0 + q] of the current super-panel
-    double* Cinv;  // 64 x 64 inverse of the current diagonal block's C22
+    double* A;     // d x d working copy, lower triangle used, ld = d
+    double* Wt;    // 64 x 64: Wt[q][p] = (C22^-1)[p][q] of the current diagonal block
     double* lam;   // damping lambda
     int64_t* info; // -1, or the first failing pivot index
 };
@@ -38,9 +37,7 @@ static LdlWs carve(void* ws, int64_t d) {
     LdlWs w;
     w.A = (double*)p;
     p += align256(sizeof(double) * (size_t)d * (size_t)d);
-    w.CT = (double*)p;
-    p += align256(sizeof(double) * (size_t)kSuper * (size_t)d);
-    w.Cinv = (double*)p;
+    w.Wt = (double*)p;
     p += align256(sizeof(double) * 64 * 64);
     w.lam = (double*)p;
     p += 256;
@@ -49,8 +46,7 @@ static LdlWs carve(void* ws, int64_t d) {
 }
 
 size_t ldl_workspace_bytes(int64_t d) {
-    return align256(sizeof(double) * (size_t)d * (size_t)d) +
-           align256(sizeof(double) * (size_t)kSuper * (size_t)d) + align256(sizeof(double) * 4096) +
+    return align256(sizeof(double) * (size_t)d * (size_t)d) + align256(sizeof(double) * 4096) +
            256 + 256;
 }
 
@@ -72,123 +68,208 @@ __global__ __launch_bounds__(kThreads) void k_ldl_init(const float* __restrict__
     }
 }
 
-// A = upper triangle of H (fp64) + lambda on the diagonal.
+// A[r][c] = H[c][r] (upper triangle of H read, lower triangle of A written),
+// plus lambda on the diagonal; 64x64 tiles transposed through LDS.
 __global__ __launch_bounds__(kThreads) void k_ldl_load(const float* __restrict__ H, int64_t d,
                                                        int64_t ldh, LdlWs w) {
-    const int64_t rt = blockIdx.y, ct = blockIdx.x;
-    if (rt > ct) return;
+    const int64_t rt = blockIdx.y, ct = blockIdx.x;  // tile of A: rows rt, cols ct, rt >= ct
+    if (ct > rt) return;
+    __shared__ float tile[kTile][kTile + 1];
+    const int64_t r0 = rt * kTile, c0 = ct * kTile;
+    for (int e = threadIdx.x; e < kTile * kTile; e += kThreads) {
+        const int a = e / kTile, b = e % kTile;  // H row c0 + a, col r0 + b
+        const int64_t hr = c0 + a, hc = r0 + b;
+        tile[a][b] = (hr < d && hc < d && hr <= hc) ? H[hr * ldh + hc] : 0.0f;
+    }
+    __syncthreads();
     const double lam = *w.lam;
     for (int e = threadIdx.x; e < kTile * kTile; e += kThreads) {
-        const int64_t i = rt * kTile + e / kTile, j = ct * kTile + e % kTile;
-        if (i >= d || j >= d || i > j) continue;
-        double v = (double)H[i * ldh + j];
-        if (i == j) v += lam;
-        w.A[i * d + j] = v;
+        const int a = e / kTile, b = e % kTile;  // A row r0 + a, col c0 + b
+        const int64_t r = r0 + a, c = c0 + b;
+        if (r >= d || c > r) continue;
+        double v = (double)tile[b][a];
+        if (r == c) v += lam;
+        w.A[r * d + c] = v;
     }
 }
 
-// Reverse Cholesky of the diagonal block A[k0:k0+nb, k0:k0+nb] (upper) in LDS,
-// written back as C22, and C22^-1 into w.Cinv.
+// Reverse Cholesky of the diagonal block and the inverse of its factor.
+// The block is held as the upper matrix a[i][j] = A[k0 + j][k0 + i] (i <= j),
+// padded with the identity beyond nb. Thread t owns rows ti + 16 x and columns
+// tj + 16 y (x, y = 0..3) in registers, with tj = t / 16 and ti = t % 16, so
+// the 16 owners of a column (and its pivot) sit in one wave: the pivot is
+// broadcast with readlane and each column costs one workgroup barrier.
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const long long b = __builtin_bit_cast(long long, v);
+    const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffll), lane);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
+    return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
+}
+
 __global__ __launch_bounds__(kThreads) void k_ldl_diag(int64_t d, int64_t k0, int nb, LdlWs w) {
     if (*w.info >= 0) return;
-    __shared__ double a[64][65];
-    __shared__ double inv[64][65];
+    __shared__ double col[2][64];   // scaled column jj of C (rows < jj)
+    __shared__ double cst[64][65];  // C, column-major: cst[j][i] = C[i][j]
+    __shared__ double rcd[64];      // 1 / C[j][j]
+    __shared__ double xrow[2][64];  // row m of X = C^-1
+    __shared__ int bad;
     const int t = threadIdx.x;
-    for (int e = t; e < 64 * 64; e += kThreads) {
-        const int i = e / 64, j = e % 64;
-        a[i][j] = (i <= j && j < nb) ? w.A[(k0 + i) * d + k0 + j] : 0.0;
-        inv[i][j] = 0.0;
-    }
+    const int tj = t >> 4, ti = t & 15;
+    const int wv = t >> 6;
+    double a[4][4];
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int i = ti + 16 * x, j = tj + 16 * y;
+            double v = 0.0;
+            if (i <= j) {
+                if (j < nb) v = w.A[(k0 + j) * d + k0 + i];
+                else if (i == j) v = 1.0;
+            }
+            a[x][y] = v;
+        }
+    if (t == 0) bad = 0;
     __syncthreads();
-    for (int jj = nb - 1; jj >= 0; --jj) {
-        const double piv = a[jj][jj];
-        if (!(piv > 0.0) || !(piv < INFINITY)) {  // uniform: every thread read the same value
-            if (t == 0) *w.info = k0 + jj;
-            return;
+
+    // columns jj = 16 yj + bj from the last; yj is a compile-time index into a[][]
+#pragma unroll
+    for (int yj = 3; yj >= 0; --yj) {
+        for (int bj = 15; bj >= 0; --bj) {
+            const int jj = 16 * yj + bj;
+            if (wv == (bj >> 2)) {  // the wave holding column jj
+                const double pv = readlane_f64(a[yj][yj], (16 * bj + bj) & 63);
+                if (!(pv > 0.0) || !(pv < INFINITY)) {
+                    if ((t & 63) == 0) bad = 1;
+                } else if (tj == bj) {  // its 16 owners scale the column
+                    const double rc = rsqrt(pv);
+                    const double c = pv * rc;
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const int i = ti + 16 * x;
+                        if (i < jj) {
+                            a[x][yj] *= rc;
+                            col[jj & 1][i] = a[x][yj];
+                            cst[jj][i] = a[x][yj];
+                        } else if (i == jj) {
+                            a[x][yj] = c;
+                            cst[jj][i] = c;
+                            rcd[jj] = rc;
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            if (bad) {  // uniform after the barrier
+                if (t == 0 && jj < nb) *w.info = k0 + jj;
+                return;
+            }
+            // a[i][k] -= C[i][jj] C[k][jj] for i <= k < jj
+            double ci[4], ck[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) ci[x] = col[jj & 1][ti + 16 * x];
+#pragma unroll
+            for (int y = 0; y < 4; ++y) ck[y] = col[jj & 1][tj + 16 * y];
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int y = 0; y <= yj; ++y) {
+                    const int i = ti + 16 * x, k = tj + 16 * y;
+                    if (i <= k && k < jj) a[x][y] = fma(-ci[x], ck[y], a[x][y]);
+                }
         }
-        const double c = sqrt(piv);
-        __syncthreads();
-        if (t < jj) a[t][jj] /= c;
-        if (t == 0) a[jj][jj] = c;
-        __syncthreads();
-        // a[ii][kk] -= a[ii][jj] * a[kk][jj] for ii <= kk < jj
-        for (int e = t; e < jj * jj; e += kThreads) {
-            const int ii = e / jj, kk = e % jj;
-            if (ii <= kk) a[ii][kk] -= a[ii][jj] * a[kk][jj];
-        }
-        __syncthreads();
     }
-    // inverse of the upper triangular C22, one column per thread
-    if (t < nb) {
-        const int j = t;
-        inv[j][j] = 1.0 / a[j][j];
-        for (int p = j - 1; p >= 0; --p) {
-            double s = 0.0;
-            for (int qq = p + 1; qq <= j; ++qq) s += a[p][qq] * inv[qq][j];
-            inv[p][j] = -s / a[p][p];
+    // C22 back into A (lower storage: A[k0 + j][k0 + i] = C[i][j])
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int i = ti + 16 * x, j = tj + 16 * y;
+            if (i <= j && j < nb) w.A[(k0 + j) * d + k0 + i] = a[x][y];
         }
-    }
-    __syncthreads();
-    for (int e = t; e < 64 * 64; e += kThreads) {
-        const int i = e / 64, j = e % 64;
-        if (i <= j && j < nb) w.A[(k0 + i) * d + k0 + j] = a[i][j];
-        w.Cinv[e] = inv[i][j];
+    // X = C^-1 (upper), right-looking from the last row: s[i][k] accumulates
+    // sum_{m > current} C[i][m] X[m][k]; row m is final once every m' > m is in.
+    double s[4][4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) s[x][y] = 0.0;
+#pragma unroll
+    for (int xm = 3; xm >= 0; --xm) {
+        for (int bm = 15; bm >= 0; --bm) {
+            const int m = 16 * xm + bm;
+            if (ti == bm) {  // owners of row m finish it
+                const double inv = rcd[m];
+#pragma unroll
+                for (int y = 0; y < 4; ++y) {
+                    const int k = tj + 16 * y;
+                    double v = 0.0;
+                    if (k >= m) v = ((k == m ? 1.0 : 0.0) - s[xm][y]) * inv;
+                    xrow[m & 1][k] = v;
+                    w.Wt[k * 64 + m] = v;  // Wt[q][p] = X[p][q]
+                }
+            }
+            __syncthreads();
+            double cm[4], xk[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) cm[x] = cst[m][ti + 16 * x];  // C[i][m]
+#pragma unroll
+            for (int y = 0; y < 4; ++y) xk[y] = xrow[m & 1][tj + 16 * y];
+#pragma unroll
+            for (int x = 0; x <= xm; ++x)
+#pragma unroll
+                for (int y = 0; y < 4; ++y) {
+                    const int i = ti + 16 * x, k = tj + 16 * y;
+                    if (i < m && k >= m) s[x][y] = fma(cm[x], xk[y], s[x][y]);
+                }
+        }
     }
 }
 
-// C12 = A[r0:r0+64, k0:k0+nb] C22^-T for rows r < k0; written back into A and,
-// transposed, into CT rows (k0 - s0) .. (k0 - s0 + nb).
-__global__ __launch_bounds__(kThreads) void k_ldl_panel(int64_t d, int64_t k0, int nb,
-                                                        int64_t s0, LdlWs w) {
+// C12^T[p][r] = sum_q (C22^-1)[p][q] A[k0 + q][r] for r in this workgroup's 64
+// columns (r < k0), written back in place into A[k0 + p][r].
+__global__ __launch_bounds__(kThreads) void k_ldl_panel(int64_t d, int64_t k0, int nb, LdlWs w) {
     if (*w.info >= 0) return;
-    __shared__ double a[64][65];
-    __shared__ double ci[64][65];
-    __shared__ double out[64][65];
-    const int t = threadIdx.x;
-    const int64_t r0 = (int64_t)blockIdx.x * 64;
-    const int rows = (int)min<int64_t>(64, k0 - r0);
-    for (int e = t; e < 64 * 64; e += kThreads) {
-        const int i = e / 64, j = e % 64;
-        a[i][j] = (i < rows && j < nb) ? w.A[(r0 + i) * d + k0 + j] : 0.0;
-        ci[i][j] = w.Cinv[e];
-    }
-    __syncthreads();
-    {
-        const int rr = t >> 2;
-        for (int p = t & 3; p < 64; p += 4) {
-            double s = 0.0;
-            for (int qq = p; qq < nb; ++qq) s += a[rr][qq] * ci[p][qq];
-            out[rr][p] = s;
-        }
-    }
-    __syncthreads();
-    for (int e = t; e < 64 * 64; e += kThreads) {
-        const int i = e / 64, j = e % 64;  // row-major write into A
-        if (i < rows && j < nb) w.A[(r0 + i) * d + k0 + j] = out[i][j];
-        const int p = e / 64, rr = e % 64;  // transposed write into CT
-        if (rr < rows && p < nb) w.CT[(k0 - s0 + p) * d + r0 + rr] = out[rr][p];
-    }
+    __shared__ GemmSmem<double> sm;
+    const int64_t r0 = (int64_t)blockIdx.x * kTile;
+    const int Cn = (int)min<int64_t>(kTile, k0 - r0);
+    f64x4 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+    tile_gemm_f64(w.Wt, 64, nb, w.A + k0 * d + r0, d, Cn, nb, acc, sm);
+    // every read of this workgroup's columns is complete (the tile loop ends in a barrier)
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int pr = acc64_row(bi, r), rc = acc64_col(bj);
+                if (pr < nb && rc < Cn) w.A[(k0 + pr) * d + r0 + rc] = acc[bi][bj][r];
+            }
 }
 
-// A[r][c] -= sum_q CT[q0 + q][r] CT[q0 + q][c], q < K, over rows [0, rmax) and
-// columns [c_lo, c_hi), upper triangle only (r <= c).
-__global__ __launch_bounds__(kThreads) void k_ldl_update(int64_t d, int64_t rmax, int64_t c_lo,
+// A[r][c] -= sum_{q < K} A[q0 + q][r] A[q0 + q][c] over rows [r_lo, r_hi),
+// columns [0, c_hi), lower triangle only (c <= r).
+__global__ __launch_bounds__(kThreads) void k_ldl_update(int64_t d, int64_t r_lo, int64_t r_hi,
                                                          int64_t c_hi, int64_t q0, int64_t K,
                                                          LdlWs w) {
     if (*w.info >= 0) return;
-    const int64_t r0 = (int64_t)blockIdx.y * kTile;
-    const int64_t c0 = c_lo + (int64_t)blockIdx.x * kTile;
-    if (r0 > c0 + kTile - 1) return;  // tile entirely below the diagonal
+    const int64_t r0 = r_lo + (int64_t)blockIdx.y * kTile;
+    const int64_t c0 = (int64_t)blockIdx.x * kTile;
+    if (c0 > r0 + kTile - 1) return;  // tile entirely above the diagonal
     __shared__ GemmSmem<double> sm;
-    const int R = (int)min<int64_t>(kTile, rmax - r0);
+    const int R = (int)min<int64_t>(kTile, r_hi - r0);
     const int Cn = (int)min<int64_t>(kTile, c_hi - c0);
     f64x4 acc[2][2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
-    const double* CT = w.CT + q0 * d;
-    tile_gemm_f64(CT + r0, d, R, CT + c0, d, Cn, K, acc, sm);
+    const double* P = w.A + q0 * d;
+    tile_gemm_f64(P + r0, d, R, P + c0, d, Cn, K, acc, sm);
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
@@ -197,27 +278,41 @@ __global__ __launch_bounds__(kThreads) void k_ldl_update(int64_t d, int64_t rmax
             for (int r = 0; r < 4; ++r) {
                 const int lr = acc64_row(bi, r), lc = acc64_col(bj);
                 const int64_t gi = r0 + lr, gj = c0 + lc;
-                if (lr < R && lc < Cn && gi <= gj) w.A[gi * d + gj] -= acc[bi][bj][r];
+                if (lr < R && lc < Cn && gj <= gi) w.A[gi * d + gj] -= acc[bi][bj][r];
             }
 }
 
-// H <- L (strict upper, fp32), D on the diagonal, 0 below; D[] if requested.
+// H[i][j] = C[i][j] / C[j][j] (i < j), C[j][j]^2 (i = j), 0 (i > j), with
+// C[i][j] = A[j][i]; D[j] = C[j][j]^2 if requested.
 __global__ __launch_bounds__(kThreads) void k_ldl_store(float* __restrict__ H, int64_t d,
                                                         int64_t ldh, float* __restrict__ D,
                                                         LdlWs w) {
-    const int64_t rt = blockIdx.y, ct = blockIdx.x;
+    const int64_t rt = blockIdx.y, ct = blockIdx.x;  // tile of H: rows rt, cols ct
+    __shared__ float tile[kTile][kTile + 1];
+    __shared__ double dj[kTile];
+    const int64_t i0 = rt * kTile, j0 = ct * kTile;
+    if (threadIdx.x < kTile) {
+        const int64_t j = j0 + threadIdx.x;
+        dj[threadIdx.x] = (j < d) ? w.A[j * d + j] : 1.0;
+    }
+    __syncthreads();
     for (int e = threadIdx.x; e < kTile * kTile; e += kThreads) {
-        const int64_t i = rt * kTile + e / kTile, j = ct * kTile + e % kTile;
-        if (i >= d || j >= d) continue;
+        const int b = e / kTile, a = e % kTile;  // A row j0 + b, col i0 + a
+        const int64_t j = j0 + b, i = i0 + a;
         float v = 0.0f;
-        if (i < j) {
-            v = (float)(w.A[i * d + j] / w.A[j * d + j]);
-        } else if (i == j) {
-            const double c = w.A[j * d + j];
-            v = (float)(c * c);
-            if (D) D[j] = v;
+        if (i < d && j < d) {
+            if (i < j) v = (float)(w.A[j * d + i] / dj[b]);
+            else if (i == j) v = (float)(dj[b] * dj[b]);
         }
-        H[i * ldh + j] = v;
+        tile[a][b] = v;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < kTile * kTile; e += kThreads) {
+        const int a = e / kTile, b = e % kTile;  // H row i0 + a, col j0 + b
+        const int64_t i = i0 + a, j = j0 + b;
+        if (i >= d || j >= d) continue;
+        H[i * ldh + j] = tile[a][b];
+        if (D && i == j) D[j] = tile[a][b];
     }
 }
 
@@ -237,18 +332,18 @@ int run_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, int64_t
             hipLaunchKernelGGL(k_ldl_diag, dim3(1), dim3(kThreads), 0, stream, d, k0, nb, w);
             if (k0 > 0) {
                 hipLaunchKernelGGL(k_ldl_panel, dim3((unsigned)((k0 + 63) / 64)), dim3(kThreads),
-                                   0, stream, d, k0, nb, s0, w);
+                                   0, stream, d, k0, nb, w);
             }
-            if (k0 > s0) {
-                const int64_t ct = (k0 - s0 + kTile - 1) / kTile, rt = (k0 + kTile - 1) / kTile;
+            if (k0 > s0) {  // rows [s0, k0) of the super-panel, every column < k0
+                const int64_t rt = (k0 - s0 + kTile - 1) / kTile, ct = (k0 + kTile - 1) / kTile;
                 hipLaunchKernelGGL(k_ldl_update, dim3((unsigned)ct, (unsigned)rt), dim3(kThreads),
-                                   0, stream, d, k0, s0, k0, k0 - s0, (int64_t)nb, w);
+                                   0, stream, d, s0, k0, k0, k0, (int64_t)nb, w);
             }
         }
         if (s0 > 0) {
             const int64_t tt = (s0 + kTile - 1) / kTile;
             hipLaunchKernelGGL(k_ldl_update, dim3((unsigned)tt, (unsigned)tt), dim3(kThreads), 0,
-                               stream, d, s0, (int64_t)0, s0, (int64_t)0, s1 - s0, w);
+                               stream, d, (int64_t)0, s0, s0, s0, s1 - s0, w);
         }
     }
     hipLaunchKernelGGL(k_ldl_store, dim3((unsigned)nbt, (unsigned)nbt), dim3(kThreads), 0, stream,
