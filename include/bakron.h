@@ -87,7 +87,11 @@ const char* bakron_status_str(int status);
  *      triangles, bit-identical mirror). With beta == 0, H is not read.
  *   For H = X^T X / T pass alpha = 1/T, beta = 0; to accumulate over token
  *   chunks call again with beta = 1 and alpha = 1/T_total.
- *   T == 0 scales H by beta. Workspace: none (ws may be NULL, ws_bytes 0).
+ *   T == 0 scales H by beta.
+ *   ws: optional device workspace of bakron_hessian_accum_workspace_bytes(T, d)
+ *      bytes, used to split the last round of output tiles over T so the GPU
+ *      stays busy; with ws == NULL (or too small) the call is still correct,
+ *      only that split is skipped. The result does not depend on it.
  * Errors: INVALID_ARG for NULL X (T > 0) or H, d <= 0, T < 0, bad ld.
  */
 size_t bakron_hessian_accum_workspace_bytes(int64_t T, int64_t d);

@@ -4,59 +4,297 @@
 // layer inputs and H_O = E[g^T g] of the output gradients (YAQA article,
 // section 3; K-FAC tutorial on mlqm.cn, section 5). With X stored as T x d
 // (one token per row), X^T X is a contraction over T whose operands are both
-// K-major, so each 64x64 tile of H is one TN tile GEMM. Only tiles on or above
-// the diagonal are computed; each writes its tile and the mirrored tile, and a
-// diagonal tile writes its upper half and mirrors it, so H is exactly
-// symmetric.
+// K-major, so each 128x128 tile of H is one TN tile GEMM. Only tiles on or
+// above the diagonal are computed; each writes its tile and the mirrored
+// tile, and a diagonal tile writes its upper half and mirrors it, so H is
+// exactly symmetric.
+//
+// Work balance: with P workgroups resident at once (two per CU), whole rounds
+// of P tiles run over the full K; the tiles left over after the last whole
+// round (or all tiles, when there are fewer than P) are split over K into
+// partials that a second kernel adds in a fixed order, so the result does not
+// depend on scheduling.
+#include <algorithm>
+
 #include "bk_common.hpp"
 #include "bk_internal.hpp"
 
 namespace bk {
 
-__global__ __launch_bounds__(kThreads) void k_syrk(const float* __restrict__ X, int64_t T,
-                                                   int64_t d, int64_t ldx, float alpha,
-                                                   float beta, float* __restrict__ H,
-                                                   int64_t ldh, int64_t nb) {
-    __shared__ GemmSmem<float> sm;
-    // tile id -> (bi, bj), bi <= bj, row-major over the upper triangle
-    const int64_t id = blockIdx.x;
+constexpr int kT128 = 128;
+constexpr int kSyKT = 32;
+
+// k-slices stored as loaded ([k][column]): 16-byte stores of consecutive columns
+// and, for each MFMA, 32 consecutive columns of one k-row per half-wave, both
+// free of bank conflicts
+struct SyrkSmem {
+    float a[2][kSyKT][kT128];
+    float b[2][kSyKT][kT128];
+};
+
+// tile id -> (bi, bj), bi <= bj, row-major over the upper triangle of nb x nb tiles
+__device__ __forceinline__ void upper_tile(int64_t id, int64_t nb, int64_t& bi, int64_t& bj) {
     auto start = [nb](int64_t b) { return b * (2 * nb - b + 1) / 2; };
     const double q = (double)(2 * nb + 1);
-    int64_t bi = (int64_t)((q - sqrt(q * q - 8.0 * (double)id)) * 0.5);
+    bi = (int64_t)((q - sqrt(q * q - 8.0 * (double)id)) * 0.5);
     if (bi < 0) bi = 0;
     while (bi + 1 < nb && start(bi + 1) <= id) ++bi;
     while (bi > 0 && start(bi) > id) --bi;
-    const int64_t bj = bi + (id - start(bi));
+    bj = bi + (id - start(bi));
+}
 
-    const int64_t r0 = bi * kTile, c0 = bj * kTile;
-    const int R = (int)min<int64_t>(kTile, d - r0);
-    const int Cn = (int)min<int64_t>(kTile, d - c0);
-    f32x16 acc;
+// Thread t loads rows k0 + (t >> 5) + 8 h (h = 0..3), columns 4 (t & 31)..+3
+// of the 128 columns starting at X + c0; zeros outside [0, K) x [0, ncol).
+__device__ __forceinline__ void syrk_load(const float* __restrict__ X, int64_t ldx, int ncol,
+                                          int64_t K, int64_t k0, bool fast, f32x4 (&v)[4]) {
+    const int t = threadIdx.x;
+    const int c4 = (t & 31) << 2;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-    tile_gemm_f32(X + r0, ldx, R, X + c0, ldx, Cn, T, acc, sm);
+    for (int h = 0; h < 4; ++h) {
+        const int64_t k = k0 + (t >> 5) + 8 * h;
+        const float* p = X + k * ldx + c4;
+        if (fast) {
+            v[h] = *reinterpret_cast<const f32x4*>(p);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[h][e] = (k < K && c4 + e < ncol) ? p[e] : 0.0f;
+        }
+    }
+}
 
-    const int c = acc32_col();
+__device__ __forceinline__ void syrk_store(float (&dst)[kSyKT][kT128], const f32x4 (&v)[4]) {
+    const int t = threadIdx.x;
+    const int c4 = (t & 31) << 2;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int r = acc32_row(v);
-        if (r >= R || c >= Cn) continue;
+    for (int h = 0; h < 4; ++h) *reinterpret_cast<f32x4*>(&dst[(t >> 5) + 8 * h][c4]) = v[h];
+}
+
+// acc[rb][cb] (32x32 blocks of this wave's 64x64 quadrant) += sum_{k in [kb, ke)}
+// X[k][r0 + r] X[k][c0 + c].
+__device__ __forceinline__ void syrk_tile(const float* __restrict__ X, int64_t ldx, int64_t r0,
+                                          int R, int64_t c0, int Cn, int64_t kb, int64_t ke,
+                                          f32x16 (&acc)[2][2], SyrkSmem& sm) {
+    const int64_t K = ke;
+    if (ke <= kb) return;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int wr = (w >> 1) * 64, wc = (w & 1) * 64;
+    const int kh = lane >> 5;
+    const float* A = X + r0;
+    const float* B = X + c0;
+    const bool aligned = R == kT128 && Cn == kT128 && (ldx & 3) == 0 &&
+                         ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
+    const int64_t nk = (ke - kb + kSyKT - 1) / kSyKT;
+    f32x4 va[4], vb[4];
+    {
+        const bool fast = aligned && kb + kSyKT <= K;
+        syrk_load(A, ldx, R, K, kb, fast, va);
+        syrk_load(B, ldx, Cn, K, kb, fast, vb);
+        syrk_store(sm.a[0], va);
+        syrk_store(sm.b[0], vb);
+    }
+    __syncthreads();
+    for (int64_t it = 0; it < nk; ++it) {
+        const int cur = (int)(it & 1);
+        const bool more = it + 1 < nk;
+        if (more) {
+            const int64_t k0 = kb + (it + 1) * kSyKT;
+            const bool fast = aligned && k0 + kSyKT <= K;
+            syrk_load(A, ldx, R, K, k0, fast, va);
+            syrk_load(B, ldx, Cn, K, k0, fast, vb);
+        }
+#pragma unroll
+        for (int kk = 0; kk < kSyKT; kk += 2) {
+            float fa[2], fb[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                fa[h] = sm.a[cur][kk + kh][wr + 32 * h + (lane & 31)];
+                fb[h] = sm.b[cur][kk + kh][wc + 32 * h + (lane & 31)];
+            }
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[rb], fb[cb], acc[rb][cb], 0, 0, 0);
+        }
+        if (more) {
+            syrk_store(sm.a[cur ^ 1], va);
+            syrk_store(sm.b[cur ^ 1], vb);
+        }
+        __syncthreads();
+    }
+}
+
+// row / column inside the 128x128 tile of element v of block (rb, cb)
+__device__ __forceinline__ int syrk_row(int rb, int v) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    return (w >> 1) * 64 + 32 * rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+}
+__device__ __forceinline__ int syrk_col(int cb) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    return (w & 1) * 64 + 32 * cb + (lane & 31);
+}
+
+// Write alpha * acc (+ beta H) into tile (bi, bj) of H and its mirror.
+__device__ __forceinline__ void syrk_write(float* __restrict__ H, int64_t ldh, int64_t d,
+                                           int64_t bi, int64_t bj, float alpha, float beta,
+                                           const f32x16 (&acc)[2][2]) {
+    const int64_t r0 = bi * kT128, c0 = bj * kT128;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            const int c = syrk_col(cb);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = syrk_row(rb, v);
+                const int64_t gi = r0 + r, gj = c0 + c;
+                if (gi >= d || gj >= d) continue;
+                if (bi == bj && r > c) continue;
+                float val = alpha * acc[rb][cb][v];
+                if (beta != 0.0f) val = fmaf(beta, H[gi * ldh + gj], val);
+                H[gi * ldh + gj] = val;
+                if (gi != gj) H[gj * ldh + gi] = val;
+            }
+        }
+}
+
+// Whole tiles [tile_beg, tile_beg + gridDim.x) over the full K.
+__global__ __launch_bounds__(kThreads) void k_syrk_full(const float* __restrict__ X, int64_t T,
+                                                        int64_t d, int64_t ldx, float alpha,
+                                                        float beta, float* __restrict__ H,
+                                                        int64_t ldh, int64_t nb, int64_t tile_beg) {
+    __shared__ SyrkSmem sm;
+    int64_t bi, bj;
+    upper_tile(tile_beg + blockIdx.x, nb, bi, bj);
+    const int R = (int)min<int64_t>(kT128, d - bi * kT128);
+    const int Cn = (int)min<int64_t>(kT128, d - bj * kT128);
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+    syrk_tile(X, ldx, bi * kT128, R, bj * kT128, Cn, 0, T, acc, sm);
+    syrk_write(H, ldh, d, bi, bj, alpha, beta, acc);
+}
+
+// Tiles [tile_beg, tile_beg + ntiles), each split into nsplit K-ranges; block
+// (tile u, split s) writes its raw 128x128 partial to part[(u * nsplit + s)].
+__global__ __launch_bounds__(kThreads) void k_syrk_split(const float* __restrict__ X, int64_t T,
+                                                         int64_t d, int64_t ldx, int64_t nb,
+                                                         int64_t tile_beg, int nsplit,
+                                                         float* __restrict__ part) {
+    __shared__ SyrkSmem sm;
+    const int u = blockIdx.x / nsplit, sp = blockIdx.x % nsplit;
+    int64_t bi, bj;
+    upper_tile(tile_beg + u, nb, bi, bj);
+    const int R = (int)min<int64_t>(kT128, d - bi * kT128);
+    const int Cn = (int)min<int64_t>(kT128, d - bj * kT128);
+    // K-ranges in whole slices
+    const int64_t nsl = (T + kSyKT - 1) / kSyKT;
+    const int64_t per = (nsl + nsplit - 1) / nsplit;
+    const int64_t kb = std::min<int64_t>(T, (int64_t)sp * per * kSyKT);
+    const int64_t ke = std::min<int64_t>(T, kb + per * kSyKT);
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+    syrk_tile(X, ldx, bi * kT128, R, bj * kT128, Cn, kb, ke, acc, sm);
+    float* out = part + (size_t)blockIdx.x * kT128 * kT128;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            const int c = syrk_col(cb);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) out[syrk_row(rb, v) * kT128 + c] = acc[rb][cb][v];
+        }
+}
+
+// Sum the nsplit partials of each split tile in order and write H; block
+// (u, g) handles rows 8 g .. 8 g + 7 of tile u.
+__global__ __launch_bounds__(kThreads) void k_syrk_reduce(int64_t d, float alpha, float beta,
+                                                          float* __restrict__ H, int64_t ldh,
+                                                          int64_t nb, int64_t tile_beg, int nsplit,
+                                                          const float* __restrict__ part) {
+    const int u = blockIdx.x;
+    int64_t bi, bj;
+    upper_tile(tile_beg + u, nb, bi, bj);
+    const float* base = part + (size_t)u * nsplit * kT128 * kT128;
+    const int e = blockIdx.y * 8 * kT128 + threadIdx.x * 4;
+    f32x4 s = *reinterpret_cast<const f32x4*>(base + e);
+    for (int q = 1; q < nsplit; ++q) s += *reinterpret_cast<const f32x4*>(base + (size_t)q * kT128 * kT128 + e);
+    const int r = e / kT128, c0 = e % kT128;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int c = c0 + k;
+        const int64_t gi = bi * kT128 + r, gj = bj * kT128 + c;
+        if (gi >= d || gj >= d) continue;
         if (bi == bj && r > c) continue;
-        const int64_t gi = r0 + r, gj = c0 + c;
-        float val = alpha * acc[v];
+        float val = alpha * s[k];
         if (beta != 0.0f) val = fmaf(beta, H[gi * ldh + gj], val);
         H[gi * ldh + gj] = val;
         if (gi != gj) H[gj * ldh + gi] = val;
     }
 }
 
+namespace {
+int resident_slots() {
+    static int slots = 0;
+    if (slots == 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        slots = 2 * cus;  // two 74 KB-LDS workgroups per CU
+    }
+    return slots;
+}
+}  // namespace
+
+size_t hessian_workspace_bytes(int64_t T, int64_t d) {
+    (void)T;
+    (void)d;
+    return sizeof(float) * (size_t)resident_slots() * kT128 * kT128;
+}
+
 int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, float alpha,
-                         float beta, float* H, int64_t ldh, hipStream_t stream) {
-    const int64_t nb = (d + kTile - 1) / kTile;
+                         float beta, float* H, int64_t ldh, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+    const int64_t nb = (d + kT128 - 1) / kT128;
     const int64_t tiles = nb * (nb + 1) / 2;
     if (tiles > 0x7fffffff) return BAKRON_E_INVALID_ARG;
-    hipLaunchKernelGGL(k_syrk, dim3((unsigned)tiles), dim3(kThreads), 0, stream, X, T, d, ldx,
-                       alpha, beta, H, ldh, nb);
+    const int64_t P = resident_slots();
+    int64_t full = (tiles / P) * P;  // whole rounds over the full K
+    int64_t rem = tiles - full;
+    if (rem > P / 2) {  // a well-filled last round: run it whole too
+        full = tiles;
+        rem = 0;
+    }
+    const int64_t nsl = (T + kSyKT - 1) / kSyKT;
+    int nsplit = rem > 0 ? (int)std::min<int64_t>(P / rem, nsl / 8) : 1;
+    const size_t need = sizeof(float) * (size_t)rem * (size_t)std::max(nsplit, 1) * kT128 * kT128;
+    if (rem > 0 && (nsplit < 2 || ws == nullptr || ws_bytes < need)) {  // no split possible
+        full = tiles;
+        rem = 0;
+    }
+    if (full > 0) {
+        hipLaunchKernelGGL(k_syrk_full, dim3((unsigned)full), dim3(kThreads), 0, stream, X, T, d,
+                           ldx, alpha, beta, H, ldh, nb, (int64_t)0);
+    }
+    if (rem > 0) {
+        float* part = (float*)ws;
+        hipLaunchKernelGGL(k_syrk_split, dim3((unsigned)(rem * nsplit)), dim3(kThreads), 0, stream,
+                           X, T, d, ldx, nb, full, nsplit, part);
+        hipLaunchKernelGGL(k_syrk_reduce, dim3((unsigned)rem, kT128 / 8), dim3(kThreads), 0, stream, d, alpha,
+                           beta, H, ldh, nb, full, nsplit, (const float*)part);
+    }
     return hipGetLastError() == hipSuccess ? BAKRON_OK : BAKRON_E_DEVICE;
 }
 

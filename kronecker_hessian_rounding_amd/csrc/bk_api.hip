@@ -25,19 +25,17 @@ const char* bakron_status_str(int status) {
 }
 
 size_t bakron_hessian_accum_workspace_bytes(int64_t T, int64_t d) {
-    (void)T;
-    (void)d;
-    return 0;
+    if (d <= 0 || T < 0) return 0;
+    return bk::hessian_workspace_bytes(T, d);
 }
 
 int bakron_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, float alpha,
                          float beta, float* H, int64_t ldh, void* ws, size_t ws_bytes,
                          void* stream) {
-    (void)ws;
-    (void)ws_bytes;
     if (!H || d <= 0 || T < 0 || bad_ld(ldh, d)) return BAKRON_E_INVALID_ARG;
     if (T > 0 && (!X || bad_ld(ldx, d))) return BAKRON_E_INVALID_ARG;
-    return bk::launch_hessian_accum(X, T, d, ldx, alpha, beta, H, ldh, (hipStream_t)stream);
+    return bk::launch_hessian_accum(X, T, d, ldx, alpha, beta, H, ldh, ws, ws_bytes,
+                                    (hipStream_t)stream);
 }
 
 size_t bakron_ldl_workspace_bytes(int64_t d) {

@@ -103,17 +103,15 @@ __device__ __forceinline__ void tile_gemm_f32(const float* __restrict__ A, int64
 }
 
 // ---------------------------------------------------------------------------
-// fp32 64x64 tile, 32-deep k-slices. The slices are stored transposed in LDS
-// ([r][k], row stride 36 floats) so that each lane fetches the 16 k-values it
-// feeds to 16 consecutive MFMAs with four ds_read_b128: in MFMA m, lanes of
-// half h (lane / 32) supply k = 16 h + m, so MFMA m accumulates
-// k in {m, 16 + m} and the 16 MFMAs cover the whole slice.
+// fp32 64x64 tile, 32-deep k-slices kept in LDS as loaded ([k][column]):
+// 16-byte stores of consecutive columns, and per MFMA each half-wave reads 32
+// consecutive columns of one k-row, so neither side has bank conflicts. The
+// next slice is fetched into registers while the current one feeds the MFMAs.
 // ---------------------------------------------------------------------------
 constexpr int kKT32 = 32;
-constexpr int kLdT = kKT32 + 4;
 struct GemmSmemT {
-    float a[2][kTile][kLdT];
-    float b[2][kTile][kLdT];
+    float a[2][kKT32][kTile];
+    float b[2][kKT32][kTile];
 };
 
 // Thread t loads rows k0 + (t >> 4) and k0 + 16 + (t >> 4), columns
@@ -135,13 +133,11 @@ __device__ __forceinline__ void slice_load32(const float* __restrict__ A, int64_
     }
 }
 
-__device__ __forceinline__ void slice_store32(float (&dst)[kTile][kLdT], const f32x4 (&v)[2]) {
+__device__ __forceinline__ void slice_store32(float (&dst)[kKT32][kTile], const f32x4 (&v)[2]) {
     const int t = threadIdx.x;
     const int c4 = (t & 15) << 2;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[c4 + e][(t >> 4) + 16 * h] = v[h][e];
+    for (int h = 0; h < 2; ++h) *reinterpret_cast<f32x4*>(&dst[(t >> 4) + 16 * h][c4]) = v[h];
 }
 
 // acc += A^T B over K for the 64x64 tile (same operand convention as
@@ -154,7 +150,7 @@ __device__ __forceinline__ void tile_gemm32_f32(const float* __restrict__ A, int
     const int w = threadIdx.x >> 6;
     const int ra = (w >> 1) * 32 + (lane & 31);
     const int rb = (w & 1) * 32 + (lane & 31);
-    const int kh = (lane >> 5) * 16;
+    const int kh = lane >> 5;
     // full, aligned slices take unchecked vector loads
     const bool aligned = R == kTile && Cn == kTile && (lda & 3) == 0 && (ldb & 3) == 0 &&
                          ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
@@ -177,17 +173,10 @@ __device__ __forceinline__ void tile_gemm32_f32(const float* __restrict__ A, int
             slice_load32(A, lda, R, K, k0, fast, va);
             slice_load32(B, ldb, Cn, K, k0, fast, vb);
         }
-        f32x4 fa[4], fb[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            fa[q] = *reinterpret_cast<const f32x4*>(&sm.a[cur][ra][kh + 4 * q]);
-            fb[q] = *reinterpret_cast<const f32x4*>(&sm.b[cur][rb][kh + 4 * q]);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[q][e], fb[q][e], acc, 0, 0, 0);
+        for (int kk = 0; kk < kKT32; kk += 2)
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sm.a[cur][kk + kh][ra], sm.b[cur][kk + kh][rb],
+                                                       acc, 0, 0, 0);
         if (more) {
             slice_store32(sm.a[cur ^ 1], va);
             slice_store32(sm.b[cur ^ 1], vb);

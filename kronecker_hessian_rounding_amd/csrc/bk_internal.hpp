@@ -13,8 +13,10 @@ namespace bk {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // --- Hessian factor accumulation (bk_accum.hip) ---
+size_t hessian_workspace_bytes(int64_t T, int64_t d);
 int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, float alpha,
-                         float beta, float* H, int64_t ldh, hipStream_t stream);
+                         float beta, float* H, int64_t ldh, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
 
 // --- LDL factorisation (bk_ldl.hip) ---
 size_t ldl_workspace_bytes(int64_t d);
