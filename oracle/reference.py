@@ -262,23 +262,31 @@ def replay(W, LO, LI, scales, bits, codes, rounding="nearest", seed=0, u=None, b
 
 
 def replay_rows(W, LO, LI, scales, bits, codes, rows, rounding="nearest", seed=0, band=1e-4):
-    """replay() restricted to selected full rows (cheap at very large sizes)."""
+    """replay() restricted to selected full rows (cheap at very large sizes).
+
+    For row i: t^_i = W*_i + (a_i^T D^[:i+1]) A_I - D^_i with a_i column i of A_O
+    restricted to rows 0..i, evaluated with the candidate's committed error D^.
+    """
     w = np.asarray(W, dtype=np.float32)
     m, n = w.shape
     Lq = 2**bits - 1
     rows = np.asarray(rows, dtype=np.int64)
+    top = int(rows.max()) + 1
     s_all = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    # D^ = W* - s (c^ - Lq/2) for every row up to the last sampled one, formed once
+    dh = np.empty((top, n), dtype=np.float64)
+    for r0 in range(0, top, 1024):
+        r1 = min(top, r0 + 1024)
+        dh[r0:r1] = w[r0:r1].astype(np.float64) - s_all[r0:r1, None] * (
+            np.asarray(codes[r0:r1]).astype(np.float64) - Lq / 2.0)
     li = None if LI is None else np.asarray(LI)
     out_y, out_t, out_q = [], [], []
     for i in rows:
-        c_hat = np.asarray(codes[: i + 1]).astype(np.int64)
-        q = s_all[: i + 1, None] * (c_hat - Lq / 2.0)
-        dh = w[: i + 1].astype(np.float64) - q
         a = np.zeros(i + 1)
         a[i] = 1.0
         if LO is not None:
             a[:i] = np.asarray(LO[:i, i], dtype=np.float64)
-        v = a @ dh                                   # (A_O^T D^)_{i,:}
+        v = a @ dh[: i + 1]                          # (A_O^T D^)_{i,:}
         if li is not None:
             # v A_I = v + v L_I, evaluated without forming an n x n fp64 copy
             vl = np.zeros(n)
@@ -288,15 +296,15 @@ def replay_rows(W, LO, LI, scales, bits, codes, rows, rounding="nearest", seed=0
             e = v + vl
         else:
             e = v
+        q = w[i].astype(np.float64) - dh[i]
         t = w[i].astype(np.float64) + (e - dh[i])
         out_t.append(t)
-        out_q.append(q[i])
+        out_q.append(q)
         out_y.append(t / s_all[i] + Lq / 2.0)
     y = np.array(out_y)
     uu = None
     if rounding == "stochastic":
-        uu = np.stack([uniform_matrix(seed, m, n)[i] for i in rows]) if m * n <= 2**26 else \
-            np.stack([_uniform_row(seed, i, n) for i in rows])
+        uu = np.stack([_uniform_row(seed, i, n) for i in rows])
     return _classify(y, Lq, uu, np.asarray(codes)[rows].astype(np.int64), band,
                      np.array(out_t), np.array(out_q), s_all[rows][:, None], None, None)
 
