@@ -25,6 +25,33 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_FP64_MFMA_TFLOPS = 78.6
+CAL_BYTES = 256 << 20
+
+# HBM traffic of one hessian_accum call at the attn workload, from two
+# rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per
+# dispatch, summed over the call's k_syrk_full, k_syrk_split and
+# k_syrk_reduce). The counters are scaled by what they read for the
+# calibration copy above: FETCH_SIZE 131088.9 KiB and WRITE_SIZE 262144.0 KiB
+# for 262144 KiB moved each way. Valid only for the kernel source it was
+# measured on (hash of bk_accum.hip + bk_common.hpp); otherwise reported null.
+SYRK_COUNTERS = {
+    ("attn", "9d3d92a54b2f654a", "e3ba0e5947ae25fa"): {"fetch_kib": 3688401.3,
+                                                        "write_kib": 99611.4},
+}
+CAL_FETCH_KIB, CAL_WRITE_KIB = 131088.9, 262144.0
+
+
+def syrk_traffic_bytes(workload):
+    """Calibrated HBM bytes per hessian_accum call, or None if not measured for this source."""
+    import hashlib
+    csrc = os.path.join(ROOT, "kronecker_hessian_rounding_amd", "csrc")
+    key = (workload,) + tuple(hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest()[:16]
+                              for f in ("bk_accum.hip", "bk_common.hpp"))
+    c = SYRK_COUNTERS.get(key)
+    if c is None:
+        return None
+    cal_kib = CAL_BYTES / 1024.0
+    return 1024.0 * (c["fetch_kib"] * cal_kib / CAL_FETCH_KIB + c["write_kib"] * cal_kib / CAL_WRITE_KIB)
 
 WORKLOAD_LABEL = {
     "tiny": "tiny 64x64, T=1024",
@@ -44,15 +71,15 @@ def parse():
     ap.add_argument("--bits", type=int, default=2)
     ap.add_argument("--rounding", default="nearest", choices=["nearest", "stochastic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=96, help="rows of the CPU sweep sample")
+    ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the CPU sweep sample")
     return ap.parse_args()
 
 
 def cpu_baseline(w, LO, LI, x, bits, rounding, seed, rows):
     """The oracle as it stands, on a bounded sample of the same layer, extrapolated.
 
-    Phases: fp64 X^T X on 2048 tokens (scaled by T/2048, twice: H_I and H_O of
-    the same size class), the plain O(d^3) LDL at d=1024 (scaled by (d/1024)^3
+    Phases: fp64 X^T X on 8192 tokens (scaled by T/8192, twice: H_I and H_O of
+    the same size class), the plain O(d^3) LDL at d=2048 (scaled by (d/2048)^3
     per factor) and the row-major accumulator sweep on the first `rows` rows
     with the device's factors (scaled by the sweep's cost model
     (m^2 n + m n^2) / (r^2 n + r n^2)).
@@ -64,11 +91,11 @@ def cpu_baseline(w, LO, LI, x, bits, rounding, seed, rows):
     m, n = w.shape
     T = x.shape[0]
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    ts = min(T, 2048)
+    ts = min(T, 8192)
     t0 = time.perf_counter()
     oracle.hessian(x[:ts])
     t_h = (time.perf_counter() - t0) * (T / ts)
-    ds = min(1024, n)
+    ds = min(2048, n)
     Hs = oracle.damp(oracle.hessian(x[: 4 * ds, :ds]))
     t0 = time.perf_counter()
     oracle.udu(Hs)
@@ -81,7 +108,7 @@ def cpu_baseline(w, LO, LI, x, bits, rounding, seed, rows):
     oracle.sweep(w[:r], lo, LI, s, bits, rounding, seed)
     t_s = time.perf_counter() - t0
     t_sweep = t_s * (m * m * n + m * n * n) / (r * r * n + r * n * n)
-    t_layer = 2 * t_h * (1.0 if m == n else 1.0) + t_ldl + t_sweep
+    t_layer = t_h * (1.0 + (m / n) ** 2) + t_ldl + t_sweep  # H_I (T n^2) and H_O (T m^2)
     return {
         "value": m * n / t_layer,
         "unit": "weights/s",
@@ -130,6 +157,14 @@ def main():
                          clamped=torch.empty(1, dtype=torch.int64, device=dev),
                          info=torch.empty(1, dtype=torch.int32, device=dev))
     seed = wl.seed_round
+    # A plain device copy of known size (256 MiB read + 256 MiB written) runs once
+    # before the warm-up: under a counter profiler its FETCH_SIZE / WRITE_SIZE
+    # readings calibrate the counters that price the Hessian kernel's traffic.
+    cal = torch.empty(CAL_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    cal_out = torch.empty_like(cal)
+    cal_out.copy_(cal)
+    torch.cuda.synchronize()
+    del cal, cal_out
     phases = ("hess_I", "ldl_I", "hess_O", "ldl_O", "solve")
     ev = {k: [] for k in phases}
 
@@ -177,18 +212,24 @@ def main():
     loss = float(out.loss.item())
     clamped = int(out.clamped.item())
 
-    # roofline of the dominant kernel: the Hessian SYRK (one launch per factor)
+    # Roofline of the dominant kernel, the Hessian SYRK. Timed per hessian_accum
+    # call (events on the stream the kernels run on); one call is k_syrk_full
+    # plus, when the tile count is not a whole number of rounds, the split-K
+    # pair k_syrk_split + k_syrk_reduce for the leftover tiles.
     syrk_ms = float(np.mean(ev["hess_I"] + ev["hess_O"]))
-    syrk_flops = float(T) * (n * n + m * m) / 2.0  # T d^2 per factor (upper half, 2 flops/FMA)
+    # algorithmic flops per call, averaged over the two calls: T d^2 per factor
+    # (the upper half, T d^2 / 2 FMAs at 2 flops each)
+    syrk_flops = float(T) * (n * n + m * m) / 2.0
     solve_flops = float(m) * n * (m + n)            # far-field feedback, minimal
     dominant = max(ph, key=ph.get)
     roof = {
-        "kernel": "k_syrk (Hessian factor X^T X, fp32 MFMA)",
+        "kernel": "hessian_accum: k_syrk_full (+ k_syrk_split, k_syrk_reduce), fp32 MFMA",
         "bound": "mfma",
         "achieved": syrk_flops / (syrk_ms * 1e-3) / 1e12,
         "peak": PEAK_FP32_MFMA_TFLOPS,
         "unit": "TFLOP/s",
-        "traffic": None,
+        "traffic": syrk_traffic_bytes(args.workload),
+        "flops_per_call": syrk_flops,
     }
     roof["frac"] = roof["achieved"] / roof["peak"]
 
