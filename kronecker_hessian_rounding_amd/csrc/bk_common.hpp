@@ -55,53 +55,6 @@ __device__ __forceinline__ void gemm_load_slice(const T* __restrict__ A, int64_t
     }
 }
 
-// fp32: acc += A^T B over K for the 64x64 tile; A element (k, r) at A[k*lda + r]
-// with r < R valid (others read as 0), B (k, c) at B[k*ldb + c] with c < Cn.
-// Must be called by all 256 threads of the workgroup.
-__device__ __forceinline__ void tile_gemm_f32(const float* __restrict__ A, int64_t lda, int R,
-                                              const float* __restrict__ B, int64_t ldb, int Cn,
-                                              int64_t K, f32x16& acc, GemmSmem<float>& sm) {
-    if (K <= 0) return;
-    const int t = threadIdx.x;
-    const int lk = t >> 4;
-    const int lc = (t & 15) << 2;
-    const int lane = t & 63;
-    const int w = t >> 6;
-    const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
-    float ra[4], rb[4];
-    const int64_t nk = (K + kKT - 1) / kKT;
-    gemm_load_slice<float>(A, lda, R, K, 0, lk, lc, ra);
-    gemm_load_slice<float>(B, ldb, Cn, K, 0, lk, lc, rb);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        sm.a[0][lk][lc + e] = ra[e];
-        sm.b[0][lk][lc + e] = rb[e];
-    }
-    __syncthreads();
-    for (int64_t it = 0; it < nk; ++it) {
-        const int cur = (int)(it & 1);
-        const bool more = (it + 1 < nk);
-        if (more) {
-            gemm_load_slice<float>(A, lda, R, K, (it + 1) * kKT, lk, lc, ra);
-            gemm_load_slice<float>(B, ldb, Cn, K, (it + 1) * kKT, lk, lc, rb);
-        }
-#pragma unroll
-        for (int kk = 0; kk < kKT; kk += 2) {
-            const float a = sm.a[cur][kk + (lane >> 5)][wr + (lane & 31)];
-            const float b = sm.b[cur][kk + (lane >> 5)][wc + (lane & 31)];
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
-        }
-        if (more) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sm.a[cur ^ 1][lk][lc + e] = ra[e];
-                sm.b[cur ^ 1][lk][lc + e] = rb[e];
-            }
-        }
-        __syncthreads();
-    }
-}
-
 // ---------------------------------------------------------------------------
 // fp32 64x64 tile, 32-deep k-slices kept in LDS as loaded ([k][column]):
 // 16-byte stores of consecutive columns, and per MFMA each half-wave reads 32
@@ -141,7 +94,7 @@ __device__ __forceinline__ void slice_store32(float (&dst)[kKT32][kTile], const 
 }
 
 // acc += A^T B over K for the 64x64 tile (same operand convention as
-// tile_gemm_f32). All 256 threads of the workgroup must call it.
+// the fp32 tile). All 256 threads of the workgroup must call it.
 __device__ __forceinline__ void tile_gemm32_f32(const float* __restrict__ A, int64_t lda, int R,
                                                 const float* __restrict__ B, int64_t ldb, int Cn,
                                                 int64_t K, f32x16& acc, GemmSmemT& sm) {

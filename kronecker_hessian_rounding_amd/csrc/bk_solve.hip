@@ -14,13 +14,12 @@
 //   p  = sum_{I'<I} L_O[R_I', R_I]^T D[R_I', S_J]   (column far field)
 //   o  = sum_{J'<J} C[R_I, S_J'] L_I[S_J', S_J]      (row far field)
 // plus the in-leaf sums, which the leaf workgroup runs as a 127-step
-// anti-diagonal wavefront. The far fields are MFMA GEMMs; all of them except
-// the contribution of the two adjacent leaves of diagonal d-1 are formed one
-// launch early by extra workgroups of the previous launch (split over K, with
-// a deterministic last-block reduction), so they overlap the leaf solves; the
-// adjacent contributions (K = 64) are added by the leaf workgroup itself.
-// Total far-field work is mn(m+n) flops, the O(mn(m+n)) of the BaKron
-// Abstract; the wavefront takes 2(m+n)/64 - 1 leaf launches, O(m+n).
+// anti-diagonal wavefront. For each leaf-diagonal d, k_far(d) forms both far
+// fields of every leaf of d as MFMA GEMMs over all earlier blocks (split over
+// K into partials, added by the leaf in chunk order, so the result does not
+// depend on scheduling), then k_leaf(d) solves the leaves. Total far-field
+// work is mn(m+n) flops, the O(mn(m+n)) of the BaKron Abstract; the wavefront
+// takes 2(m+n)/64 - 1 leaf launches, O(m+n).
 #include <limits.h>
 
 #include <algorithm>
@@ -51,9 +50,7 @@ struct SolveParams {
     float* delta;
     int64_t ldd;
     float* ct;  // n x m, C^T, ld = m
-    float* offs;
     float* parts;
-    unsigned* counters;
     double* leaf_loss;
     int* leaf_clamp;
     const float* DO;
@@ -61,21 +58,15 @@ struct SolveParams {
     int want_loss;
     int* info;
     int maxleaf;
-    int cbk;  // K-chunk length in 64-blocks
 };
 
 __device__ __forceinline__ int leaf_lo(const SolveParams& p, int d) { return max(0, d - (p.N - 1)); }
 __device__ __forceinline__ int leaf_hi(const SolveParams& p, int d) { return min(d, p.M - 1); }
 
-// offs / parts / counters indexing: parity of the diagonal, leaf slot, kind (0: p, 1: o)
-__device__ __forceinline__ float* offs_ptr(const SolveParams& p, int par, int slot, int kind) {
-    return p.offs + ((size_t)(par * p.maxleaf + slot) * 2 + kind) * (kB * kB);
+// far-field partials: leaf slot on the diagonal, kind (0: p, 1: o^T), K-chunk
+__device__ __forceinline__ float* part_ptr(const SolveParams& p, int slot, int kind, int c) {
+    return p.parts + (((size_t)slot * 2 + kind) * kNch + c) * (kB * kB);
 }
-__device__ __forceinline__ float* part_ptr(const SolveParams& p, int par, int slot, int kind,
-                                           int c) {
-    return p.parts + (((size_t)(par * p.maxleaf + slot) * 2 + kind) * kNch + c) * (kB * kB);
-}
-__device__ __forceinline__ int nchunks(int kblk, int cbk) { return kblk <= 0 ? 0 : (kblk + cbk - 1) / cbk; }
 
 // ---------------------------------------------------------------------------
 // scales: s_i = fp32(2 max_j |W*_ij|) / fp32(Lq), or the caller's scale
@@ -114,9 +105,7 @@ __global__ __launch_bounds__(kThreads) void k_scales(const float* __restrict__ W
     }
 }
 
-__global__ void k_solve_init(unsigned* counters, int ncounters, int* info) {
-    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < ncounters; e += gridDim.x * blockDim.x)
-        counters[e] = 0u;
+__global__ void k_solve_init(int* info) {
     if (blockIdx.x == 0 && threadIdx.x == 0) *info = INT_MAX;
 }
 
@@ -157,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void k_far(SolveParams p, int d, int nch)
     else  // o^T[jj][ii] = sum_l L_I[l][j0+jj] C^T[l][i0+ii]
         tile_gemm32_f32(p.LI + k0 * p.ldli + j0, p.ldli, Cc, p.ct + k0 * p.m + i0, p.m, R, K, acc,
                         sm);
-    float* part = part_ptr(p, 0, slot, kind, c);
+    float* part = part_ptr(p, slot, kind, c);
     const int cc = acc32_col();
 #pragma unroll
     for (int v = 0; v < 16; ++v) part[acc32_row(v) * kB + cc] = acc[v];
@@ -227,10 +216,10 @@ __global__ __launch_bounds__(kLeafThreads) void k_leaf(SolveParams p, int d, int
         for (int c = 0; c < kNch; ++c) {
             int b0, b1;
             chunk_range(I, nch, c, b0, b1);
-            xp[c] = (c < np && b1 > b0) ? *reinterpret_cast<const f32x4*>(part_ptr(p, 0, slot, 0, c) + e)
+            xp[c] = (c < np && b1 > b0) ? *reinterpret_cast<const f32x4*>(part_ptr(p, slot, 0, c) + e)
                                         : f32x4{0.f, 0.f, 0.f, 0.f};
             chunk_range(J, nch, c, b0, b1);
-            xo[c] = (c < no && b1 > b0) ? *reinterpret_cast<const f32x4*>(part_ptr(p, 0, slot, 1, c) + e)
+            xo[c] = (c < no && b1 > b0) ? *reinterpret_cast<const f32x4*>(part_ptr(p, slot, 1, c) + e)
                                         : f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
@@ -451,8 +440,8 @@ __global__ __launch_bounds__(kThreads) void k_solve_finish(const double* leaf_lo
 // ---------------------------------------------------------------------------
 namespace {
 struct Layout {
-    int M, N, maxleaf, cbk;
-    size_t ct, delta, offs, parts, counters, leaf_loss, leaf_clamp, info, total;
+    int M, N, maxleaf;
+    size_t ct, delta, parts, leaf_loss, leaf_clamp, info, total;
 };
 
 Layout layout(int64_t m, int64_t n) {
@@ -460,19 +449,13 @@ Layout layout(int64_t m, int64_t n) {
     L.M = (int)((m + kB - 1) / kB);
     L.N = (int)((n + kB - 1) / kB);
     L.maxleaf = std::min(L.M, L.N);
-    const int kmax = std::max(L.M, L.N) - 1;
-    L.cbk = std::max(1, (kmax + kNch - 1) / kNch);
     size_t o = 0;
     L.ct = o;
     o += align256(sizeof(float) * (size_t)m * (size_t)n);
     L.delta = o;
     o += align256(sizeof(float) * (size_t)m * (size_t)n);
-    L.offs = o;
-    o += align256(sizeof(float) * (size_t)L.maxleaf * 2 * kB * kB);
     L.parts = o;
     o += align256(sizeof(float) * (size_t)L.maxleaf * 2 * kNch * kB * kB);
-    L.counters = o;
-    o += align256(sizeof(unsigned) * (size_t)L.maxleaf * 2);
     L.leaf_loss = o;
     o += align256(sizeof(double) * (size_t)L.M * L.N);
     L.leaf_clamp = o;
@@ -509,9 +492,7 @@ int run_solve(const SolveArgs& a, void* ws, hipStream_t stream) {
     p.delta = a.delta ? a.delta : (float*)(base + L.delta);
     p.ldd = a.delta ? a.ldd : a.n;
     p.ct = (float*)(base + L.ct);
-    p.offs = (float*)(base + L.offs);
     p.parts = (float*)(base + L.parts);
-    p.counters = (unsigned*)(base + L.counters);
     p.leaf_loss = (double*)(base + L.leaf_loss);
     p.leaf_clamp = (int*)(base + L.leaf_clamp);
     p.DO = a.DO;
@@ -519,11 +500,8 @@ int run_solve(const SolveArgs& a, void* ws, hipStream_t stream) {
     p.want_loss = a.loss != nullptr;
     p.info = (int*)(base + L.info);
     p.maxleaf = L.maxleaf;
-    p.cbk = L.cbk;
 
-    const int ncnt = L.maxleaf * 2;
-    hipLaunchKernelGGL(k_solve_init, dim3((ncnt + 255) / 256), dim3(256), 0, stream, p.counters,
-                       ncnt, p.info);
+    hipLaunchKernelGGL(k_solve_init, dim3(1), dim3(64), 0, stream, p.info);
     hipLaunchKernelGGL(k_scales, dim3((unsigned)a.m), dim3(kThreads), 0, stream, a.W, a.n, a.ldw,
                        a.bits, a.row_scale, a.scales, p.info);
     const int ndiag = L.M + L.N - 1;
