@@ -94,11 +94,16 @@ __global__ __launch_bounds__(kThreads) void k_ldl_load(const float* __restrict__
 }
 
 // Reverse Cholesky of the diagonal block and the inverse of its factor.
-// The block is held as the upper matrix a[i][j] = A[k0 + j][k0 + i] (i <= j),
-// padded with the identity beyond nb. Thread t owns rows ti + 16 x and columns
-// tj + 16 y (x, y = 0..3) in registers, with tj = t / 16 and ti = t % 16, so
-// the 16 owners of a column (and its pivot) sit in one wave: the pivot is
-// broadcast with readlane and each column costs one workgroup barrier.
+// The block is held in LDS as the upper matrix u[i][j] = A[k0 + j][k0 + i]
+// (i <= j), padded with the identity beyond nb, and factored in 16-wide block
+// columns from the last. Wave 0 factors a block column with one lane per row:
+// the pivot and the scaled column entries move between lanes by readlane, so
+// the 16 columns of a block need no barrier. The four waves then apply the
+// rank-16 update to the block columns on its left with f64 MFMA. The inverse
+// X = C^-1 is formed blockwise: the four 16x16 diagonal blocks by back
+// substitution (one wave each), then
+//   X[I][J] = -X[I][I] sum_{I<Q<=J} C[I][Q] X[Q][J]
+// for block rows I = 2, 1, 0 (MFMA, one wave per block).
 __device__ __forceinline__ double readlane_f64(double v, int lane) {
     const long long b = __builtin_bit_cast(long long, v);
     const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffll), lane);
@@ -106,123 +111,131 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
     return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
 }
 
+constexpr int kUs = 65;  // LDS row stride (doubles) of the diagonal-block tiles
+
 __global__ __launch_bounds__(kThreads) void k_ldl_diag(int64_t d, int64_t k0, int nb, LdlWs w) {
     if (*w.info >= 0) return;
-    __shared__ double col[2][64];   // scaled column jj of C (rows < jj)
-    __shared__ double cst[64][65];  // C, column-major: cst[j][i] = C[i][j]
+    __shared__ double u[64][kUs];   // C, upper part
+    __shared__ double xs[64][kUs];  // X = C^-1, upper part
     __shared__ double rcd[64];      // 1 / C[j][j]
-    __shared__ double xrow[2][64];  // row m of X = C^-1
-    __shared__ int bad;
+    __shared__ int badj;
     const int t = threadIdx.x;
-    const int tj = t >> 4, ti = t & 15;
+    const int lane = t & 63;
     const int wv = t >> 6;
-    double a[4][4];
-#pragma unroll
-    for (int y = 0; y < 4; ++y)
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int i = ti + 16 * x, j = tj + 16 * y;
-            double v = 0.0;
-            if (i <= j) {
-                if (j < nb) v = w.A[(k0 + j) * d + k0 + i];
-                else if (i == j) v = 1.0;
-            }
-            a[x][y] = v;
+    for (int e = t; e < 64 * 64; e += kThreads) {
+        const int i = e & 63, j = e >> 6;
+        double v = 0.0;
+        if (i <= j) {
+            if (j < nb) v = w.A[(k0 + j) * d + k0 + i];
+            else if (i == j) v = 1.0;
         }
-    if (t == 0) bad = 0;
+        u[i][j] = v;
+    }
     __syncthreads();
 
-    // columns jj = 16 yj + bj from the last; yj is a compile-time index into a[][]
+    int bad = -1;  // wave 0: the first failing pivot, in factorisation order
 #pragma unroll
-    for (int yj = 3; yj >= 0; --yj) {
-        for (int bj = 15; bj >= 0; --bj) {
-            const int jj = 16 * yj + bj;
-            if (wv == (bj >> 2)) {  // the wave holding column jj
-                const double pv = readlane_f64(a[yj][yj], (16 * bj + bj) & 63);
-                if (!(pv > 0.0) || !(pv < INFINITY)) {
-                    if ((t & 63) == 0) bad = 1;
-                } else if (tj == bj) {  // its 16 owners scale the column
-                    const double rc = rsqrt(pv);
-                    const double c = pv * rc;
+    for (int b = 3; b >= 0; --b) {
+        if (wv == 0) {
+            double r[16];  // row `lane` of block column b
 #pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        const int i = ti + 16 * x;
-                        if (i < jj) {
-                            a[x][yj] *= rc;
-                            col[jj & 1][i] = a[x][yj];
-                            cst[jj][i] = a[x][yj];
-                        } else if (i == jj) {
-                            a[x][yj] = c;
-                            cst[jj][i] = c;
-                            rcd[jj] = rc;
-                        }
-                    }
+            for (int q = 0; q < 16; ++q) r[q] = u[lane][16 * b + q];
+#pragma unroll
+            for (int jl = 15; jl >= 0; --jl) {
+                const int jj = 16 * b + jl;
+                const double piv = readlane_f64(r[jl], jj);
+                if (bad < 0 && !(piv > 0.0 && piv < INFINITY)) bad = jj;
+                const double rc = rsqrt(piv);
+                const double v = lane < jj ? r[jl] * rc : (lane == jj ? piv * rc : 0.0);
+                r[jl] = v;
+                if (lane == jj) rcd[jj] = rc;
+                // columns q < jj of the block: r[q] -= C[lane][jj] C[q][jj]
+#pragma unroll
+                for (int q = jl - 1; q >= 0; --q) r[q] = fma(-v, readlane_f64(v, 16 * b + q), r[q]);
+            }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) u[lane][16 * b + q] = r[q];
+        }
+        __syncthreads();
+        if (b > 0) {
+            // u[0:16b, 0:16b] -= P P^T with P = u[0:16b, 16b:16b+16], 16x16 tiles (I, K), I <= K
+            for (int tile = wv; tile < b * (b + 1) / 2; tile += 4) {
+                int I = 0, K = tile;
+                while (K >= b - I) {
+                    K -= b - I;
+                    ++I;
                 }
+                K += I;
+                f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int kq = 16 * b + 4 * kk + (lane >> 4);
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(u[16 * I + (lane & 15)][kq],
+                                                               u[16 * K + (lane & 15)][kq], acc, 0, 0, 0);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) u[16 * I + (lane >> 4) + 4 * r][16 * K + (lane & 15)] -= acc[r];
             }
             __syncthreads();
-            if (bad) {  // uniform after the barrier
-                if (t == 0 && jj < nb) *w.info = k0 + jj;
-                return;
-            }
-            // a[i][k] -= C[i][jj] C[k][jj] for i <= k < jj
-            double ci[4], ck[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) ci[x] = col[jj & 1][ti + 16 * x];
-#pragma unroll
-            for (int y = 0; y < 4; ++y) ck[y] = col[jj & 1][tj + 16 * y];
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-#pragma unroll
-                for (int y = 0; y <= yj; ++y) {
-                    const int i = ti + 16 * x, k = tj + 16 * y;
-                    if (i <= k && k < jj) a[x][y] = fma(-ci[x], ck[y], a[x][y]);
-                }
         }
     }
-    // C22 back into A (lower storage: A[k0 + j][k0 + i] = C[i][j])
+    if (t == 0) badj = bad;
+    __syncthreads();
+    if (badj >= 0) {  // uniform after the barrier
+        if (t == 0 && badj < nb) *w.info = k0 + badj;
+        return;
+    }
+
+    // diagonal blocks of X: wave wv, lane k < 16 solves column k of block wv
+    {
+        const int B0 = 16 * wv;
+        const int k = lane & 15;
+        double xl[16];
 #pragma unroll
-    for (int y = 0; y < 4; ++y)
+        for (int m = 15; m >= 0; --m) {
+            double sacc = (m == k) ? 1.0 : 0.0;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int i = ti + 16 * x, j = tj + 16 * y;
-            if (i <= j && j < nb) w.A[(k0 + j) * d + k0 + i] = a[x][y];
+            for (int q = m + 1; q < 16; ++q) sacc = fma(-u[B0 + m][B0 + q], xl[q], sacc);
+            xl[m] = sacc * rcd[B0 + m];
         }
-    // X = C^-1 (upper), right-looking from the last row: s[i][k] accumulates
-    // sum_{m > current} C[i][m] X[m][k]; row m is final once every m' > m is in.
-    double s[4][4];
+        if (lane < 16) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+            for (int m = 0; m < 16; ++m) xs[B0 + m][B0 + k] = xl[m];
+        }
+    }
+    __syncthreads();
+    // off-diagonal blocks of X, block row I = 2, 1, 0; wave wv takes J = I + 1 + wv
 #pragma unroll
-        for (int y = 0; y < 4; ++y) s[x][y] = 0.0;
+    for (int I = 2; I >= 0; --I) {
+        const int J = I + 1 + wv;
+        if (J <= 3) {
+            f64x4 tacc = {0.0, 0.0, 0.0, 0.0};  // T = sum_Q C[I][Q] X[Q][J]
+            for (int Q = I + 1; Q <= J; ++Q) {
 #pragma unroll
-    for (int xm = 3; xm >= 0; --xm) {
-        for (int bm = 15; bm >= 0; --bm) {
-            const int m = 16 * xm + bm;
-            if (ti == bm) {  // owners of row m finish it
-                const double inv = rcd[m];
-#pragma unroll
-                for (int y = 0; y < 4; ++y) {
-                    const int k = tj + 16 * y;
-                    double v = 0.0;
-                    if (k >= m) v = ((k == m ? 1.0 : 0.0) - s[xm][y]) * inv;
-                    xrow[m & 1][k] = v;
-                    w.Wt[k * 64 + m] = v;  // Wt[q][p] = X[p][q]
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int kq = 4 * kk + (lane >> 4);
+                    tacc = __builtin_amdgcn_mfma_f64_16x16x4f64(u[16 * I + (lane & 15)][16 * Q + kq],
+                                                                xs[16 * Q + kq][16 * J + (lane & 15)],
+                                                                tacc, 0, 0, 0);
                 }
             }
-            __syncthreads();
-            double cm[4], xk[4];
+            // tacc[kk] holds T[4 kk + lane / 16][lane % 16]: the B operand of k-step kk
+            f64x4 xacc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-            for (int x = 0; x < 4; ++x) cm[x] = cst[m][ti + 16 * x];  // C[i][m]
+            for (int kk = 0; kk < 4; ++kk)
+                xacc = __builtin_amdgcn_mfma_f64_16x16x4f64(
+                    xs[16 * I + (lane & 15)][16 * I + 4 * kk + (lane >> 4)], tacc[kk], xacc, 0, 0, 0);
 #pragma unroll
-            for (int y = 0; y < 4; ++y) xk[y] = xrow[m & 1][tj + 16 * y];
-#pragma unroll
-            for (int x = 0; x <= xm; ++x)
-#pragma unroll
-                for (int y = 0; y < 4; ++y) {
-                    const int i = ti + 16 * x, k = tj + 16 * y;
-                    if (i < m && k >= m) s[x][y] = fma(cm[x], xk[y], s[x][y]);
-                }
+            for (int r = 0; r < 4; ++r) xs[16 * I + (lane >> 4) + 4 * r][16 * J + (lane & 15)] = -xacc[r];
         }
+        __syncthreads();
+    }
+
+    // C22 back into A (lower storage: A[k0 + j][k0 + i] = C[i][j]); Wt[j][i] = X[i][j]
+    for (int e = t; e < 64 * 64; e += kThreads) {
+        const int i = e & 63, j = e >> 6;
+        if (i <= j && j < nb) w.A[(k0 + j) * d + k0 + i] = u[i][j];
+        w.Wt[e] = (i <= j) ? xs[i][j] : 0.0;
     }
 }
 
