@@ -95,9 +95,12 @@ __device__ __forceinline__ void slice_store32(float (&dst)[kKT32][kTile], const 
 
 // acc += A^T B over K for the 64x64 tile (same operand convention as
 // the fp32 tile). All 256 threads of the workgroup must call it.
+// Threads 0..255 compute; with active = false a thread (of a larger
+// workgroup) only takes part in the barriers.
 __device__ __forceinline__ void tile_gemm32_f32(const float* __restrict__ A, int64_t lda, int R,
                                                 const float* __restrict__ B, int64_t ldb, int Cn,
-                                                int64_t K, f32x16& acc, GemmSmemT& sm) {
+                                                int64_t K, f32x16& acc, GemmSmemT& sm,
+                                                bool active = true) {
     if (K <= 0) return;
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
@@ -109,7 +112,7 @@ __device__ __forceinline__ void tile_gemm32_f32(const float* __restrict__ A, int
                          ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
     const int64_t nk = (K + kKT32 - 1) / kKT32;
     f32x4 va[2], vb[2];
-    {
+    if (active) {
         const bool fast = aligned && kKT32 <= K;
         slice_load32(A, lda, R, K, 0, fast, va);
         slice_load32(B, ldb, Cn, K, 0, fast, vb);
@@ -119,7 +122,11 @@ __device__ __forceinline__ void tile_gemm32_f32(const float* __restrict__ A, int
     __syncthreads();
     for (int64_t it = 0; it < nk; ++it) {
         const int cur = (int)(it & 1);
-        const bool more = it + 1 < nk;
+        const bool more = active && it + 1 < nk;
+        if (!active) {
+            __syncthreads();
+            continue;
+        }
         if (more) {
             const int64_t k0 = (it + 1) * kKT32;
             const bool fast = aligned && k0 + kKT32 <= K;

@@ -14,12 +14,15 @@
 //   p  = sum_{I'<I} L_O[R_I', R_I]^T D[R_I', S_J]   (column far field)
 //   o  = sum_{J'<J} C[R_I, S_J'] L_I[S_J', S_J]      (row far field)
 // plus the in-leaf sums, which the leaf workgroup runs as a 127-step
-// anti-diagonal wavefront. For each leaf-diagonal d, k_far(d) forms both far
-// fields of every leaf of d as MFMA GEMMs over all earlier blocks (split over
-// K into partials, added by the leaf in chunk order, so the result does not
-// depend on scheduling), then k_leaf(d) solves the leaves. Total far-field
-// work is mn(m+n) flops, the O(mn(m+n)) of the BaKron Abstract; the wavefront
-// takes 2(m+n)/64 - 1 leaf launches, O(m+n).
+// anti-diagonal wavefront. The far fields are MFMA GEMMs. Their contributions
+// from blocks on leaf-diagonals d-2 and earlier (split over K into partials)
+// need only the leaves of d-2, so they are formed by extra workgroups of the
+// launch that solves the leaves of d-1, on the CUs those leaves leave free.
+// The two blocks adjacent to the leaf (on diagonal d-1, K = 64) are
+// multiplied by the leaf workgroup itself. The leaf adds the partials in chunk order and then the adjacent
+// products, so the result does not depend on scheduling. Total far-field work
+// is mn(m+n) flops, the O(mn(m+n)) of the BaKron Abstract; the wavefront takes
+// 2(m+n)/64 - 1 leaf launches, O(m+n).
 #include <limits.h>
 
 #include <algorithm>
@@ -63,9 +66,9 @@ struct SolveParams {
 __device__ __forceinline__ int leaf_lo(const SolveParams& p, int d) { return max(0, d - (p.N - 1)); }
 __device__ __forceinline__ int leaf_hi(const SolveParams& p, int d) { return min(d, p.M - 1); }
 
-// far-field partials: leaf slot on the diagonal, kind (0: p, 1: o^T), K-chunk
-__device__ __forceinline__ float* part_ptr(const SolveParams& p, int slot, int kind, int c) {
-    return p.parts + (((size_t)slot * 2 + kind) * kNch + c) * (kB * kB);
+// far-field partials: parity of the diagonal, leaf slot on it, kind (0: p, 1: o^T), K-chunk
+__device__ __forceinline__ float* part_ptr(const SolveParams& p, int par, int slot, int kind, int c) {
+    return p.parts + ((((size_t)par * p.maxleaf + slot) * 2 + kind) * kNch + c) * (kB * kB);
 }
 
 // ---------------------------------------------------------------------------
@@ -111,9 +114,9 @@ __global__ void k_solve_init(int* info) {
 
 // ---------------------------------------------------------------------------
 // far field of diagonal d: chunk c (of nch) of p (kind 0) or o^T (kind 1) of
-// one leaf, over every block above (p) or to the left (o) of the leaf. Each
-// chunk writes its own 64x64 partial; the leaf adds the partials in chunk
-// order, so the result does not depend on scheduling.
+// one leaf, over the blocks above (p) or to the left (o) of the leaf except
+// the adjacent one, i.e. blocks on diagonals d-2 and earlier. Each chunk
+// writes its own 64x64 partial; the leaf adds the partials in chunk order.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void chunk_range(int kblk, int nch, int c, int& b0, int& b1) {
     const int len = (kblk + nch - 1) / nch;
@@ -121,18 +124,18 @@ __device__ __forceinline__ void chunk_range(int kblk, int nch, int c, int& b0, i
     b1 = min(b0 + len, kblk);
 }
 
-__global__ __launch_bounds__(kThreads) void k_far(SolveParams p, int d, int nch) {
+__device__ __forceinline__ void far_body(const SolveParams& p, int d, int nch, int task, GemmSmemT& sm) {
     if (*p.info != INT_MAX) return;  // a row scale was invalid
-    __shared__ GemmSmemT sm;
-    const int task = blockIdx.x;
     const int slot = task / (2 * nch);
     const int kind = (task / nch) & 1;
     const int c = task % nch;
     const int I = leaf_lo(p, d) + slot;
     const int J = d - I;
     if ((kind == 0 && !p.LO) || (kind == 1 && !p.LI)) return;
+    const int kblk = (kind == 0 ? I : J) - 1;
+    if (kblk <= 0) return;
     int kb0, kb1;
-    chunk_range(kind == 0 ? I : J, nch, c, kb0, kb1);
+    chunk_range(kblk, nch, c, kb0, kb1);
     if (kb1 <= kb0) return;
     const int64_t i0 = (int64_t)I * kB, j0 = (int64_t)J * kB;
     const int R = (int)min<int64_t>(kB, p.m - i0), Cc = (int)min<int64_t>(kB, p.n - j0);
@@ -140,13 +143,15 @@ __global__ __launch_bounds__(kThreads) void k_far(SolveParams p, int d, int nch)
     f32x16 acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+    const bool active = threadIdx.x < kThreads;  // the fifth wave only joins the barriers
     if (kind == 0)  // p[ii][jj] = sum_k L_O[k][i0+ii] D[k][j0+jj]
         tile_gemm32_f32(p.LO + k0 * p.ldlo + i0, p.ldlo, R, p.delta + k0 * p.ldd + j0, p.ldd, Cc,
-                        K, acc, sm);
+                        K, acc, sm, active);
     else  // o^T[jj][ii] = sum_l L_I[l][j0+jj] C^T[l][i0+ii]
         tile_gemm32_f32(p.LI + k0 * p.ldli + j0, p.ldli, Cc, p.ct + k0 * p.m + i0, p.m, R, K, acc,
-                        sm);
-    float* part = part_ptr(p, slot, kind, c);
+                        sm, active);
+    if (!active) return;
+    float* part = part_ptr(p, d & 1, slot, kind, c);
     const int cc = acc32_col();
 #pragma unroll
     for (int v = 0; v < 16; ++v) part[acc32_row(v) * kB + cc] = acc[v];
@@ -189,25 +194,79 @@ struct LeafSmem {
     int red_i[kLeafThreads];
 };
 
+// acc += X^T Y over k = 0..63 for the 64x64 tile, X[k][r] at x[k * sx + r] and
+// Y[k][c] at y[k * sy + c] in LDS; waves 0-3 each own a 32x32 quadrant
+// (32x32x2 f32 MFMA operand and output layout of bk_common.hpp).
+__device__ __forceinline__ void adj_gemm(const float* x, int sx, const float* y, int sy, f32x16& acc) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
+#pragma unroll
+    for (int k = 0; k < kB; k += 2) {
+        const int kr = k + (lane >> 5);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x[kr * sx + wr + (lane & 31)], y[kr * sy + wc + (lane & 31)],
+                                                   acc, 0, 0, 0);
+    }
+}
+
 __device__ __forceinline__ float lane_above(float x) {
     // wave_shr:1 -- lane i receives lane i-1's value, lane 0 receives 0
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x138,
                                                                   0xF, 0xF, false));
 }
 
-__global__ __launch_bounds__(kLeafThreads) void k_leaf(SolveParams p, int d, int nch) {
+__device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, int slot, LeafSmem& sm) {
     if (*p.info != INT_MAX) return;
-    __shared__ LeafSmem sm;
-    const int slot = blockIdx.x;
     const int I = leaf_lo(p, d) + slot;
     const int J = d - I;
     const int64_t i0 = (int64_t)I * kB, j0 = (int64_t)J * kB;
     const int R = (int)min<int64_t>(kB, p.m - i0), Cc = (int)min<int64_t>(kB, p.n - j0);
     const int t = threadIdx.x;
-    const int np = (p.LO && I > 0) ? nch : 0;  // partials of p and o^T to add
-    const int no = (p.LI && J > 0) ? nch : 0;
+    const int par = d & 1;
+    const int np = (p.LO && I > 1) ? nch : 0;  // partials of p and o^T to add
+    const int no = (p.LI && J > 1) ? nch : 0;
+    const bool adj_p = p.LO && I > 0, adj_o = p.LI && J > 0;
+    const int w = t >> 6;
 
-    // ---- LDS set-up: far fields (sum of the K-chunk partials, in chunk order) ----
+    // ---- adjacent blocks (K = 64), staged in LDS regions that are set up later:
+    //   p  += L_O[i0-64+k][i0+ii] D[i0-64+k][j0+jj]
+    //   o^T += L_I[j0-64+l][j0+jj] C^T[j0-64+l][i0+ii]
+    {
+        // every load of the thread is issued before the first LDS store
+        constexpr int kPer = (kB * kB + kLeafThreads - 1) / kLeafThreads;
+        float v1[kPer], v2[kPer], v3[kPer], v4[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int e = t + u * kLeafThreads;
+            const int k = e >> 6, c = e & 63;
+            const bool in = e < kB * kB;
+            const int64_t ik = i0 - kB + k, jk = j0 - kB + k;
+            v1[u] = (in && adj_p && c < R) ? p.LO[ik * p.ldlo + i0 + c] : 0.0f;
+            v2[u] = (in && adj_p && c < Cc) ? p.delta[ik * p.ldd + j0 + c] : 0.0f;
+            v3[u] = (in && adj_o && c < Cc) ? p.LI[jk * p.ldli + j0 + c] : 0.0f;
+            v4[u] = (in && adj_o && c < R) ? p.ct[jk * p.m + i0 + c] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int e = t + u * kLeafThreads;
+            if (e < kB * kB) {
+                const int k = e >> 6, c = e & 63;
+                sm.DT[k][c] = v1[u];
+                sm.Gs[k][c] = v2[u];
+                sm.LIT[k][c] = v3[u];
+                sm.wst[k][c] = v4[u];
+            }
+        }
+    }
+    __syncthreads();
+    f32x16 ap, ao;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) ap[v] = ao[v] = 0.0f;
+    if (w < 4) {
+        if (adj_p) adj_gemm(&sm.DT[0][0], kTs, &sm.Gs[0][0], kTs, ap);
+        if (adj_o) adj_gemm(&sm.LIT[0][0], kTs, &sm.wst[0][0], kPs, ao);
+    }
+
+    // ---- far fields from diagonals d-2 and earlier (sum of the K-chunk partials, in chunk order) ----
     for (int g4 = t; g4 < kB * kB / 4; g4 += kLeafThreads) {
         const int e = 4 * g4;
         f32x4 pv = {0.f, 0.f, 0.f, 0.f}, ov = {0.f, 0.f, 0.f, 0.f};
@@ -215,11 +274,11 @@ __global__ __launch_bounds__(kLeafThreads) void k_leaf(SolveParams p, int d, int
 #pragma unroll
         for (int c = 0; c < kNch; ++c) {
             int b0, b1;
-            chunk_range(I, nch, c, b0, b1);
-            xp[c] = (c < np && b1 > b0) ? *reinterpret_cast<const f32x4*>(part_ptr(p, slot, 0, c) + e)
+            chunk_range(I - 1, nch, c, b0, b1);
+            xp[c] = (c < np && b1 > b0) ? *reinterpret_cast<const f32x4*>(part_ptr(p, par, slot, 0, c) + e)
                                         : f32x4{0.f, 0.f, 0.f, 0.f};
-            chunk_range(J, nch, c, b0, b1);
-            xo[c] = (c < no && b1 > b0) ? *reinterpret_cast<const f32x4*>(part_ptr(p, slot, 1, c) + e)
+            chunk_range(J - 1, nch, c, b0, b1);
+            xo[c] = (c < no && b1 > b0) ? *reinterpret_cast<const f32x4*>(part_ptr(p, par, slot, 1, c) + e)
                                         : f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
@@ -232,6 +291,15 @@ __global__ __launch_bounds__(kLeafThreads) void k_leaf(SolveParams p, int d, int
         for (int k = 0; k < 4; ++k) {
             sm.pin[r][c0 + k] = pv[k];
             sm.base[c0 + k][r] = ov[k];
+        }
+    }
+    __syncthreads();
+    if (w < 4) {  // then the adjacent products
+        const int cc = acc32_col();
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            sm.pin[acc32_row(v)][cc] += ap[v];
+            sm.base[cc][acc32_row(v)] += ao[v];
         }
     }
     __syncthreads();
@@ -253,7 +321,6 @@ __global__ __launch_bounds__(kLeafThreads) void k_leaf(SolveParams p, int d, int
         sm.rnb[0][t] = sm.rnb[1][t] = 0.0f;
     }
 
-    const int w = t >> 6;
     double loss = 0.0;
     int nclamp = 0;
     if (w < 4) {
@@ -405,6 +472,22 @@ __global__ __launch_bounds__(kLeafThreads) void k_leaf(SolveParams p, int d, int
     }
 }
 
+// One launch per leaf-diagonal d: workgroups 0..nleaf-1 solve the leaves of
+// d (dispatched first), the others form the far fields of d + 1 (their inputs
+// are the leaves of d - 1 and earlier, finished by the previous launch) on
+// the CUs the leaves leave free.
+union StepSmem {
+    LeafSmem leaf;
+    GemmSmemT far;
+};
+
+__global__ __launch_bounds__(kLeafThreads) void k_step(SolveParams p, int d, int nch, int nleaf,
+                                                       int nch_next) {
+    __shared__ StepSmem sm;
+    if ((int)blockIdx.x < nleaf) leaf_body(p, d, nch, blockIdx.x, sm.leaf);
+    else far_body(p, d + 1, nch_next, blockIdx.x - nleaf, sm.far);
+}
+
 // loss = sum of leaf partials in a fixed order; clamped count; info.
 __global__ __launch_bounds__(kThreads) void k_solve_finish(const double* leaf_loss,
                                                            const int* leaf_clamp, int nleaves,
@@ -454,8 +537,8 @@ Layout layout(int64_t m, int64_t n) {
     o += align256(sizeof(float) * (size_t)m * (size_t)n);
     L.delta = o;
     o += align256(sizeof(float) * (size_t)m * (size_t)n);
-    L.parts = o;
-    o += align256(sizeof(float) * (size_t)L.maxleaf * 2 * kNch * kB * kB);
+    L.parts = o;  // two diagonals in flight (parity)
+    o += align256(sizeof(float) * 2 * (size_t)L.maxleaf * 2 * kNch * kB * kB);
     L.leaf_loss = o;
     o += align256(sizeof(double) * (size_t)L.M * L.N);
     L.leaf_clamp = o;
@@ -505,21 +588,23 @@ int run_solve(const SolveArgs& a, void* ws, hipStream_t stream) {
     hipLaunchKernelGGL(k_scales, dim3((unsigned)a.m), dim3(kThreads), 0, stream, a.W, a.n, a.ldw,
                        a.bits, a.row_scale, a.scales, p.info);
     const int ndiag = L.M + L.N - 1;
-    for (int d = 0; d < ndiag; ++d) {
+    // per diagonal: leaf count and K-chunks per far-field product (enough
+    // workgroups to fill the chip, chunks of at least 4 blocks)
+    auto diag_shape = [&](int d, int& nleaf, int& nch, int& nfar) {
         const int lo = std::max(0, d - (L.N - 1)), hi = std::min(d, L.M - 1);
-        const int nleaf = hi - lo + 1;
-        // K-chunks per far-field product: enough workgroups to fill the chip,
-        // chunks of at least 4 blocks (256)
-        const int kmax = std::max(hi, d - lo);
-        int nch = std::max(1, (kTargetWg + 2 * nleaf - 1) / (2 * nleaf));
+        nleaf = hi - lo + 1;
+        const int kmax = std::max(hi, d - lo) - 1;  // blocks before the adjacent one
+        nch = std::max(1, (kTargetWg + 2 * nleaf - 1) / (2 * nleaf));
         nch = std::min(nch, std::max(1, kmax / 4));
         nch = std::min(nch, kNch);
-        if (d > 0) {  // far fields of diagonal d (every leaf of d - 1 is done)
-            hipLaunchKernelGGL(k_far, dim3((unsigned)(nleaf * 2 * nch)), dim3(kThreads), 0, stream,
-                               p, d, nch);
-        }
-        hipLaunchKernelGGL(k_leaf, dim3((unsigned)nleaf), dim3(kLeafThreads), 0, stream, p, d,
-                           nch);
+        nfar = kmax > 0 ? nleaf * 2 * nch : 0;
+    };
+    for (int d = 0; d < ndiag; ++d) {
+        int nleaf, nch, nfar, nl1 = 0, nch1 = 1, nfar1 = 0;  // this diagonal, the next one
+        diag_shape(d, nleaf, nch, nfar);
+        if (d + 1 < ndiag) diag_shape(d + 1, nl1, nch1, nfar1);
+        hipLaunchKernelGGL(k_step, dim3((unsigned)(nleaf + nfar1)), dim3(kLeafThreads), 0, stream, p,
+                           d, nch, nleaf, nch1);
     }
     hipLaunchKernelGGL(k_solve_finish, dim3(1), dim3(kThreads), 0, stream, p.leaf_loss,
                        p.leaf_clamp, L.M * L.N, a.loss, a.clamped, p.info, a.info);
