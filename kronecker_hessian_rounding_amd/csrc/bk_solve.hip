@@ -135,8 +135,7 @@ __device__ __forceinline__ void far_body(const SolveParams& p, int d, int nch, i
     const int kblk = (kind == 0 ? I : J) - 1;
     if (kblk <= 0) return;
     int kb0, kb1;
-    chunk_range(kblk, nch, c, kb0, kb1);
-    if (kb1 <= kb0) return;
+    chunk_range(kblk, nch, c, kb0, kb1);  // an empty chunk writes a zero partial
     const int64_t i0 = (int64_t)I * kB, j0 = (int64_t)J * kB;
     const int R = (int)min<int64_t>(kB, p.m - i0), Cc = (int)min<int64_t>(kB, p.n - j0);
     const int64_t k0 = (int64_t)kb0 * kB, K = (int64_t)(kb1 - kb0) * kB;
@@ -163,17 +162,18 @@ __device__ __forceinline__ void far_body(const SolveParams& p, int d, int nch, i
 // Entry (i, j) is finalised at step i + j. Its in-leaf sums
 //   pn = sum_{k<i} L_O[k][i] D[k][j],   rn = sum_{l<j} g[i][l] L_I[l][j]
 // (g = C, the column feedback plus error of the row) are split into a bulk,
-// which only uses entries finalised two or more steps earlier, and the newest
-// term (k = i-1, l = j-1). Waves 0-3 compute the bulk of step st+1 while wave
-// 4 finalises step st, so the dependent chain per step is short and the bulk
-// LDS traffic overlaps it. The finaliser takes D[i-1][j] from the lane above
-// (it was that lane's result one step earlier) and g[i][j-1] from its own
-// previous step, so only the two bulk sums cross LDS on the chain.
+// which only uses entries finalised three or more steps earlier, and the two
+// newest terms of each (k = i-1, i-2 and l = j-1, j-2). Waves 0-3 compute the
+// bulk of step st + 2 while wave 4 finalises step st, so the dependent chain
+// of a step holds no LDS read: the finaliser takes D[i-1][j] and D[i-2][j]
+// from the lanes above by DPP, g[i][j-1] and g[i][j-2] from its own previous
+// steps, and the bulk sums and static inputs were read one step ahead.
 //
 // Bulk lanes are (row i, quarter q) with lane = 4 i + q; quarter q owns the
-// k / l chunks [8q, 8q+8) and [32+8q, 32+8q+8). With 68-float rows (16 bytes
-// of bank offset per row) the four b128 reads of a row pair hit eight
-// distinct bank groups.
+// k / l range [16q, 16q + 16), read as four adjacent 16-byte words (68-float
+// rows spread a row group over the banks); a range without a useful term
+// reads a zero row instead, which keeps the LDS traffic near the triangular
+// work without a branch.
 // ---------------------------------------------------------------------------
 constexpr int kLeafThreads = 5 * 64;
 constexpr int kTs = 68;  // row stride of the k/l-indexed tiles
@@ -182,12 +182,15 @@ constexpr int kPs = 66;  // row stride of the per-entry inputs: anti-diagonal wa
 struct LeafSmem {
     float DT[kB][kTs];     // D transposed: DT[j][k] = D[k][j] (0 until known)
     float Gs[kB][kTs];     // g = C of the leaf, row-major (0 until known)
-    float LIT[kB][kTs];    // L_I diagonal block transposed: LIT[j][l] = L_I[l][j], l < j
+    float LIT[kB][kTs];    // L_I diagonal block transposed: LIT[j][l] = L_I[l][j], l < j - 2 (else 0)
     float base[kB][kPs];   // W* + o
     float pin[kB][kPs];    // p
-    float wst[kB][kPs];    // W*
-    float pnb[2][kB];      // bulk sums, double buffered by step parity
-    float rnb[2][kB];
+    float wst[kB][kPs];    // W*, overwritten by eta = t - q once the entry is final
+    float pnb[3][kB];      // bulk sums, by step modulo 3 (written two steps ahead)
+    float rnb[3][kB];
+    float zrow[16];        // zeros: read by bulk lanes whose chunk holds no useful term
+    float li1[kB];         // L_I[j-1][j] and L_I[j-2][j]: the finaliser's copies of the two
+    float li2[kB];         // superdiagonals, which are zero in LIT
     uint8_t code[kB][kB + 4];
     float DI[kB];
     double red[kLeafThreads];
@@ -214,6 +217,8 @@ __device__ __forceinline__ float lane_above(float x) {
                                                                   0xF, 0xF, false));
 }
 
+__device__ __forceinline__ f32x4 lds4(const float* q) { return *reinterpret_cast<const f32x4*>(q); }
+
 __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, int slot, LeafSmem& sm) {
     if (*p.info != INT_MAX) return;
     const int I = leaf_lo(p, d) + slot;
@@ -221,19 +226,23 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
     const int64_t i0 = (int64_t)I * kB, j0 = (int64_t)J * kB;
     const int R = (int)min<int64_t>(kB, p.m - i0), Cc = (int)min<int64_t>(kB, p.n - j0);
     const int t = threadIdx.x;
-    const int par = d & 1;
-    const int np = (p.LO && I > 1) ? nch : 0;  // partials of p and o^T to add
-    const int no = (p.LI && J > 1) ? nch : 0;
-    const bool adj_p = p.LO && I > 0, adj_o = p.LI && J > 0;
     const int w = t >> 6;
+    const int par = d & 1;
+    const bool far_p = p.LO && I > 1, far_o = p.LI && J > 1;  // all nch partials were written
+    const bool adj_p = p.LO && I > 0, adj_o = p.LI && J > 0;
 
-    // ---- adjacent blocks (K = 64), staged in LDS regions that are set up later:
-    //   p  += L_O[i0-64+k][i0+ii] D[i0-64+k][j0+jj]
-    //   o^T += L_I[j0-64+l][j0+jj] C^T[j0-64+l][i0+ii]
+    if (t < 16) sm.zrow[t] = 0.0f;
+    if (t < 2) {
+        sm.li2[t] = 0.0f;  // no L_I[j-2][j] for j < 2, no L_I[j-1][j] for j = 0
+        if (t == 0) sm.li1[0] = 0.0f;
+    }
+    // ---- A: every tile load of the thread in flight at once, then LDS
+    //   DT  <- L_O[i0-64+k][i0+c]   Gs   <- D[i0-64+k][j0+c]      (block above: staging)
+    //   pin <- L_I[j0-64+k][j0+c]   base <- C^T[j0-64+k][i0+c]    (block to the left: staging)
+    //   wst <- W*[i0+k][j0+c]       LIT[c][k] <- L_I[j0+k][j0+c], k < c
     {
-        // every load of the thread is issued before the first LDS store
         constexpr int kPer = (kB * kB + kLeafThreads - 1) / kLeafThreads;
-        float v1[kPer], v2[kPer], v3[kPer], v4[kPer];
+        float v1[kPer], v2[kPer], v3[kPer], v4[kPer], v5[kPer], v6[kPer];
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
             const int e = t + u * kLeafThreads;
@@ -244,6 +253,8 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
             v2[u] = (in && adj_p && c < Cc) ? p.delta[ik * p.ldd + j0 + c] : 0.0f;
             v3[u] = (in && adj_o && c < Cc) ? p.LI[jk * p.ldli + j0 + c] : 0.0f;
             v4[u] = (in && adj_o && c < R) ? p.ct[jk * p.m + i0 + c] : 0.0f;
+            v5[u] = (in && k < R && c < Cc) ? p.W[(i0 + k) * p.ldw + j0 + c] : 0.0f;
+            v6[u] = (in && p.LI && k < c && c < Cc) ? p.LI[(j0 + k) * p.ldli + j0 + c] : 0.0f;
         }
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
@@ -252,39 +263,55 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
                 const int k = e >> 6, c = e & 63;
                 sm.DT[k][c] = v1[u];
                 sm.Gs[k][c] = v2[u];
-                sm.LIT[k][c] = v3[u];
-                sm.wst[k][c] = v4[u];
+                sm.pin[k][c] = v3[u];
+                sm.base[k][c] = v4[u];
+                sm.wst[k][c] = v5[u];
+                sm.LIT[c][k] = (c - k <= 2) ? 0.0f : v6[u];
+                if (c - k == 1) sm.li1[c] = v6[u];
+                if (c - k == 2) sm.li2[c] = v6[u];
             }
         }
     }
     __syncthreads();
-    f32x16 ap, ao;
+    f32x16 ap, ao;  // adjacent products (K = 64): p += L_O^T D, o^T += L_I^T C^T
 #pragma unroll
     for (int v = 0; v < 16; ++v) ap[v] = ao[v] = 0.0f;
     if (w < 4) {
         if (adj_p) adj_gemm(&sm.DT[0][0], kTs, &sm.Gs[0][0], kTs, ap);
-        if (adj_o) adj_gemm(&sm.LIT[0][0], kTs, &sm.wst[0][0], kPs, ao);
+        if (adj_o) adj_gemm(&sm.pin[0][0], kPs, &sm.base[0][0], kPs, ao);
     }
+    __syncthreads();
 
-    // ---- far fields from diagonals d-2 and earlier (sum of the K-chunk partials, in chunk order) ----
+    // ---- B: far fields from diagonals d-2 and earlier: the K-chunk partials
+    // summed in chunk order (all loads issued first; absent chunks read a
+    // valid address and are replaced by zero)
     for (int g4 = t; g4 < kB * kB / 4; g4 += kLeafThreads) {
         const int e = 4 * g4;
-        f32x4 pv = {0.f, 0.f, 0.f, 0.f}, ov = {0.f, 0.f, 0.f, 0.f};
+        if (!far_p && !far_o) {  // uniform: nothing to read
+            const int r = e / kB, c0 = e % kB;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                sm.pin[r][c0 + k] = 0.0f;
+                sm.base[c0 + k][r] = 0.0f;
+            }
+            continue;
+        }
         f32x4 xp[kNch], xo[kNch];
 #pragma unroll
         for (int c = 0; c < kNch; ++c) {
-            int b0, b1;
-            chunk_range(I - 1, nch, c, b0, b1);
-            xp[c] = (c < np && b1 > b0) ? *reinterpret_cast<const f32x4*>(part_ptr(p, par, slot, 0, c) + e)
-                                        : f32x4{0.f, 0.f, 0.f, 0.f};
-            chunk_range(J - 1, nch, c, b0, b1);
-            xo[c] = (c < no && b1 > b0) ? *reinterpret_cast<const f32x4*>(part_ptr(p, par, slot, 1, c) + e)
-                                        : f32x4{0.f, 0.f, 0.f, 0.f};
+            const int cc = min(c, nch - 1);
+            xp[c] = *reinterpret_cast<const f32x4*>(part_ptr(p, par, slot, 0, cc) + e);
+            xo[c] = *reinterpret_cast<const f32x4*>(part_ptr(p, par, slot, 1, cc) + e);
         }
+        f32x4 pv = {0.f, 0.f, 0.f, 0.f}, ov = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < kNch; ++c) {
-            pv += xp[c];
-            ov += xo[c];
+            const bool up = far_p && c < nch, uo = far_o && c < nch;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                pv[k] += up ? xp[c][k] : 0.0f;
+                ov[k] += uo ? xo[c][k] : 0.0f;
+            }
         }
         const int r = e / kB, c0 = e % kB;  // p: row r, cols c0..c0+3; o^T: row (= leaf col) r, leaf rows c0..
 #pragma unroll
@@ -294,7 +321,8 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
         }
     }
     __syncthreads();
-    if (w < 4) {  // then the adjacent products
+    // ---- C: then the adjacent products, then W*; clear D, g and the codes
+    if (w < 4) {
         const int cc = acc32_col();
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -305,117 +333,123 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
     __syncthreads();
     for (int e = t; e < kB * kB; e += kLeafThreads) {
         const int i = e / kB, j = e % kB;
-        const float wv = (i < R && j < Cc) ? p.W[(i0 + i) * p.ldw + j0 + j] : 0.0f;
-        // L_I[l][jj] stored at LIT[jj][l] (here l = i, jj = j)
-        const float lv = (p.LI && i < j && j < Cc) ? p.LI[(j0 + i) * p.ldli + j0 + j] : 0.0f;
-        sm.wst[i][j] = wv;
-        sm.base[i][j] += wv;
-        sm.LIT[j][i] = lv;
+        sm.base[i][j] += sm.wst[i][j];
         sm.DT[i][j] = 0.0f;
         sm.Gs[i][j] = 0.0f;
         sm.code[i][j] = 0;
     }
     if (t < kB) {
         sm.DI[t] = (p.want_loss && t < Cc) ? p.DI[j0 + t] : 0.0f;
-        sm.pnb[0][t] = sm.pnb[1][t] = 0.0f;
-        sm.rnb[0][t] = sm.rnb[1][t] = 0.0f;
+        sm.pnb[0][t] = sm.pnb[1][t] = sm.pnb[2][t] = 0.0f;
+        sm.rnb[0][t] = sm.rnb[1][t] = sm.rnb[2][t] = 0.0f;
     }
 
     double loss = 0.0;
     int nclamp = 0;
     if (w < 4) {
         // ---------------- bulk waves ----------------
+        // lane (row i, quarter q) sums the k / l range [16q, 16q + 16)
         const int i = t >> 2;
         const int q = t & 3;
-        const int ka = 8 * q, kb = 32 + 8 * q;  // the quarter's two 8-wide chunks
-        float lo_a[8], lo_b[8];                 // L_O[i0 + k][i0 + i] for k <= i - 2
+        const int k0 = 16 * q;
+        float lo[16];  // L_O[i0 + k][i0 + i] for k <= i - 3, else 0
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            lo_a[e] = (p.LO && ka + e <= i - 2 && i < R) ? p.LO[(i0 + ka + e) * p.ldlo + i0 + i] : 0.0f;
-            lo_b[e] = (p.LO && kb + e <= i - 2 && i < R) ? p.LO[(i0 + kb + e) * p.ldlo + i0 + i] : 0.0f;
-        }
-        const bool pa = p.LO && ka <= i - 2, pbl = p.LO && kb <= i - 2;
+        for (int e = 0; e < 16; ++e)
+            lo[e] = (p.LO && k0 + e <= i - 3 && i < R) ? p.LO[(i0 + k0 + e) * p.ldlo + i0 + i] : 0.0f;
+        const bool pn_any = p.LO && k0 <= i - 3 && i < R;  // this lane's chunk of L_O has a term
         __syncthreads();
+        int slot3 = 2;  // (st + 2) mod 3
         for (int st = 0; st < 2 * kB - 1; ++st) {
-            const int jn = st + 1 - i;  // entry (i, jn) is finalised at the next step
-            float pn = 0.0f, rn = 0.0f;
-            if (jn >= 0 && jn < kB) {
-                const float* dcol = &sm.DT[jn][0];
-                if (pa) {
-                    const f32x4 d0 = *reinterpret_cast<const f32x4*>(dcol + ka);
-                    const f32x4 d1 = *reinterpret_cast<const f32x4*>(dcol + ka + 4);
+            // entry (i, jn) is finalised two steps later; its bulk takes k <= i-3 and
+            // l <= jn-3. D[k][jn] and g[i][l] in that range are final; L_O is zero
+            // beyond i-3 and LIT holds zeros for l >= jn-2 (the superdiagonals are
+            // the finaliser's), so the entries being written in this step meet a zero
+            // factor. A chunk without a useful term reads the zero row instead.
+            const int jn = st + 2 - i;
+            const bool live = jn >= 0 && jn < kB;
+            const int jc = min(max(jn, 0), kB - 1);
+            const bool rn_any = live && k0 <= jn - 3;
+            const float* dp = (live && pn_any) ? &sm.DT[jc][k0] : sm.zrow;
+            const float* gp = rn_any ? &sm.Gs[i][k0] : sm.zrow;
+            const float* lp = rn_any ? &sm.LIT[jc][k0] : sm.zrow;
+            const f32x4 d0 = lds4(dp), d1 = lds4(dp + 4), d2 = lds4(dp + 8), d3 = lds4(dp + 12);
+            const f32x4 g0 = lds4(gp), g1 = lds4(gp + 4), g2 = lds4(gp + 8), g3 = lds4(gp + 12);
+            const f32x4 l0 = lds4(lp), l1 = lds4(lp + 4), l2 = lds4(lp + 8), l3 = lds4(lp + 12);
+            __builtin_amdgcn_sched_barrier(0);  // the twelve reads go out together
+            float p0 = 0.0f, p1 = 0.0f, r0 = 0.0f, r1 = 0.0f;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        pn = fmaf(lo_a[e], d0[e], pn);
-                        pn = fmaf(lo_a[4 + e], d1[e], pn);
-                    }
-                }
-                if (pbl) {
-                    const f32x4 d0 = *reinterpret_cast<const f32x4*>(dcol + kb);
-                    const f32x4 d1 = *reinterpret_cast<const f32x4*>(dcol + kb + 4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        pn = fmaf(lo_b[e], d0[e], pn);
-                        pn = fmaf(lo_b[4 + e], d1[e], pn);
-                    }
-                }
-                // rn bulk: l <= jn - 2 (l = jn - 1 is the newest term, masked below)
-                const float* grow = &sm.Gs[i][0];
-                const float* lcol = &sm.LIT[jn][0];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int kc = h ? kb : ka;
-                    if (kc <= jn - 2) {
-                        const f32x4 g0 = *reinterpret_cast<const f32x4*>(grow + kc);
-                        const f32x4 g1 = *reinterpret_cast<const f32x4*>(grow + kc + 4);
-                        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lcol + kc);
-                        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lcol + kc + 4);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            rn = fmaf(g0[e], (kc + e == jn - 1) ? 0.0f : l0[e], rn);
-                            rn = fmaf(g1[e], (kc + 4 + e == jn - 1) ? 0.0f : l1[e], rn);
-                        }
-                    }
-                }
+            for (int e = 0; e < 4; ++e) {
+                p0 = fmaf(lo[e], d0[e], p0);
+                p1 = fmaf(lo[4 + e], d1[e], p1);
+                r0 = fmaf(g0[e], l0[e], r0);
+                r1 = fmaf(g1[e], l1[e], r1);
             }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                p0 = fmaf(lo[8 + e], d2[e], p0);
+                p1 = fmaf(lo[12 + e], d3[e], p1);
+                r0 = fmaf(g2[e], l2[e], r0);
+                r1 = fmaf(g3[e], l3[e], r1);
+            }
+            float pn = live ? p0 + p1 : 0.0f;
+            float rn = live ? r0 + r1 : 0.0f;
             pn = quad_sum(pn);
             rn = quad_sum(rn);
-            if (q == 0 && jn >= 0 && jn < kB) {
-                sm.pnb[(st + 1) & 1][i] = pn;
-                sm.rnb[(st + 1) & 1][i] = rn;
+            if (q == 0 && live) {
+                sm.pnb[slot3][i] = pn;
+                sm.rnb[slot3][i] = rn;
             }
+            slot3 = slot3 == 2 ? 0 : slot3 + 1;
             __syncthreads();
         }
     } else {
         // ---------------- finaliser wave: lane i owns row i ----------------
+        // adds the two newest terms of each sum: D[i-1][j], D[i-2][j] (from the
+        // lanes above, by DPP) and g[i][j-1], g[i][j-2] (its own previous results);
+        // eta = t - q goes into W*'s slot (consumed one step earlier) for the loss
         const int i = t & 63;
-        const float lo_last = (p.LO && i >= 1 && i < R) ? p.LO[(i0 + i - 1) * p.ldlo + i0 + i] : 0.0f;
+        const float lo1 = (p.LO && i >= 1 && i < R) ? p.LO[(i0 + i - 1) * p.ldlo + i0 + i] : 0.0f;
+        const float lo2 = (p.LO && i >= 2 && i < R) ? p.LO[(i0 + i - 2) * p.ldlo + i0 + i] : 0.0f;
         const int Lq = (1 << p.bits) - 1;
         const float half = 0.5f * (float)Lq;
         const float s = (i < R) ? p.scales[i0 + i] : 1.0f;
         const float rs = 1.0f / s;
-        const float dO = (p.want_loss && i < R) ? (p.DO ? p.DO[i0 + i] : 1.0f) : 0.0f;
-        float d_last = 0.0f;  // D of this row's previous entry (read by the lane below)
-        float g_last = 0.0f;  // g of this row's previous entry
+        float d_last = 0.0f;   // D of this row's previous entry (read by the lane below)
+        float dp1_last = 0.0f; // D[i-1][j] of the previous step (read by the lane below)
+        float g_last = 0.0f, g_last2 = 0.0f;  // g of this row's previous two entries
         __syncthreads();
-        // static inputs of the first entry of the row (j = 0) are read at step i
-        float x_pin = 0.f, x_base = 0.f, x_w = 0.f, x_l = 0.f, x_di = 0.f;
+        // inputs of the next entry, read one step ahead: bulk sums and static data
+        float n_pb = sm.pnb[0][i], n_rb = sm.rnb[0][i];
+        float n_pin = 0.f, n_base = 0.f, n_w = 0.f, n_l1 = 0.f, n_l2 = 0.f;
+        if (i == 0) {
+            n_pin = sm.pin[0][0];
+            n_base = sm.base[0][0];
+            n_w = sm.wst[0][0];
+        }
+        int slot3n = 1;  // (st + 1) mod 3
         for (int st = 0; st < 2 * kB - 1; ++st) {
             const int j = st - i;
-            const float dprev = lane_above(d_last);
-            if (j >= 0 && j < kB) {
-                x_pin = sm.pin[i][j];
-                x_base = sm.base[i][j];
-                x_w = sm.wst[i][j];
-                x_l = (j >= 1) ? sm.LIT[j][j - 1] : 0.0f;
-                x_di = sm.DI[j];
+            const float dprev1 = lane_above(d_last);    // D[i-1][j]
+            const float dprev2 = lane_above(dp1_last);  // D[i-2][j]
+            const float pb = n_pb, rb = n_rb;
+            const float x_pin = n_pin, x_base = n_base, x_w = n_w, x_l1 = n_l1, x_l2 = n_l2;
+            n_pb = sm.pnb[slot3n][i];
+            n_rb = sm.rnb[slot3n][i];
+            slot3n = slot3n == 2 ? 0 : slot3n + 1;
+            const int jn = j + 1;
+            if (jn >= 0 && jn < kB) {
+                n_pin = sm.pin[i][jn];
+                n_base = sm.base[i][jn];
+                n_w = sm.wst[i][jn];
+                n_l1 = sm.li1[jn];
+                n_l2 = sm.li2[jn];
             }
             if (j >= 0 && j < Cc && i < R) {
                 float u = 0.5f;
                 if (p.stochastic)
                     u = uniform24(p.seed, (uint64_t)(i0 + i) * (uint64_t)p.n + (uint64_t)(j0 + j));
-                const float P = x_pin + (sm.pnb[st & 1][i] + lo_last * dprev);
-                const float Rr = sm.rnb[st & 1][i] + g_last * x_l;
+                const float P = x_pin + ((pb + lo2 * dprev2) + lo1 * dprev1);
+                const float Rr = (rb + g_last2 * x_l2) + g_last * x_l1;
                 const float tv = x_base + P + Rr;
                 const float y = fmaf(tv, rs, half);
                 float cf = floorf(y + u);
@@ -426,12 +460,24 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
                 sm.DT[j][i] = dl;
                 sm.Gs[i][j] = g;
                 sm.code[i][j] = (uint8_t)cf;
+                sm.wst[i][j] = fmaf(-s, cf - half, tv);  // eta
                 d_last = dl;
+                g_last2 = g_last;
                 g_last = g;
-                const float eta = fmaf(-s, cf - half, tv);
-                loss += (double)(dO * x_di) * (double)eta * (double)eta;
             }
+            dp1_last = dprev1;
             __syncthreads();
+        }
+    }
+    // loss partial: sum of D_O,i D_I,j eta_ij^2 over the leaf, in fp64
+    if (p.want_loss) {
+        for (int e = t; e < kB * kB; e += kLeafThreads) {
+            const int i = e / kB, j = e % kB;
+            if (i < R && j < Cc) {
+                const float dO = p.DO ? p.DO[i0 + i] : 1.0f;
+                const double eta = (double)sm.wst[i][j];
+                loss += (double)(dO * sm.DI[j]) * eta * eta;
+            }
         }
     }
 
@@ -481,7 +527,7 @@ union StepSmem {
     GemmSmemT far;
 };
 
-__global__ __launch_bounds__(kLeafThreads) void k_step(SolveParams p, int d, int nch, int nleaf,
+__global__ __launch_bounds__(kLeafThreads, 1) void k_step(SolveParams p, int d, int nch, int nleaf,
                                                        int nch_next) {
     __shared__ StepSmem sm;
     if ((int)blockIdx.x < nleaf) leaf_body(p, d, nch, blockIdx.x, sm.leaf);
