@@ -45,17 +45,21 @@ __device__ __forceinline__ void upper_tile(int64_t id, int64_t nb, int64_t& bi, 
 
 // Thread t loads rows k0 + (t >> 5) + 8 h (h = 0..3), columns 4 (t & 31)..+3
 // of the 128 columns starting at X + c0; zeros outside [0, K) x [0, ncol).
+// kFull: the tile is 128 columns wide and 16-byte aligned, so each row is one
+// vector load (rows past K are clamped to K - 1 and replaced by zero).
+template <bool kFull>
 __device__ __forceinline__ void syrk_load(const float* __restrict__ X, int64_t ldx, int ncol,
-                                          int64_t K, int64_t k0, bool fast, f32x4 (&v)[4]) {
+                                          int64_t K, int64_t k0, f32x4 (&v)[4]) {
     const int t = threadIdx.x;
     const int c4 = (t & 31) << 2;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
         const int64_t k = k0 + (t >> 5) + 8 * h;
-        const float* p = X + k * ldx + c4;
-        if (fast) {
-            v[h] = *reinterpret_cast<const f32x4*>(p);
+        if (kFull) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(X + min(k, K - 1) * ldx + c4);
+            v[h] = k < K ? x : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         } else {
+            const float* p = X + k * ldx + c4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[h][e] = (k < K && c4 + e < ncol) ? p[e] : 0.0f;
         }
@@ -69,60 +73,80 @@ __device__ __forceinline__ void syrk_store(float (&dst)[kSyKT][kT128], const f32
     for (int h = 0; h < 4; ++h) *reinterpret_cast<f32x4*>(&dst[(t >> 5) + 8 * h][c4]) = v[h];
 }
 
-// acc[rb][cb] (32x32 blocks of this wave's 64x64 quadrant) += sum_{k in [kb, ke)}
-// X[k][r0 + r] X[k][c0 + c].
-__device__ __forceinline__ void syrk_tile(const float* __restrict__ X, int64_t ldx, int64_t r0,
-                                          int R, int64_t c0, int Cn, int64_t kb, int64_t ke,
-                                          f32x16 (&acc)[2][2], SyrkSmem& sm) {
-    const int64_t K = ke;
-    if (ke <= kb) return;
+// The MFMAs of one 32-deep slice: wave quadrant rows wr.., columns wc..; the
+// operands of k-step s + 1 are read from LDS before the MFMAs of step s issue.
+__device__ __forceinline__ void syrk_slice(const float (&a)[kSyKT][kT128], const float (&b)[kSyKT][kT128],
+                                           int wr, int wc, f32x16 (&acc)[2][2]) {
     const int lane = threadIdx.x & 63;
+    const int kh = lane >> 5, l31 = lane & 31;
+    float fa[2][2], fb[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        fa[0][h] = a[kh][wr + 32 * h + l31];
+        fb[0][h] = b[kh][wc + 32 * h + l31];
+    }
+#pragma unroll
+    for (int s = 0; s < kSyKT / 2; ++s) {
+        const int cur = s & 1;
+        if (s + 1 < kSyKT / 2) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                fa[cur ^ 1][h] = a[2 * (s + 1) + kh][wr + 32 * h + l31];
+                fb[cur ^ 1][h] = b[2 * (s + 1) + kh][wc + 32 * h + l31];
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of this step's MFMAs
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+                acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[cur][rb], fb[cur][cb], acc[rb][cb], 0, 0, 0);
+    }
+}
+
+// acc[rb][cb] (32x32 blocks of this wave's 64x64 quadrant) += sum_{k in [kb, ke)}
+// X[k][r0 + r] X[k][c0 + c]; the next slice is loaded into registers while the
+// current one feeds the MFMAs.
+template <bool kFull>
+__device__ __forceinline__ void syrk_tile_impl(const float* __restrict__ A, const float* __restrict__ B,
+                                               int64_t ldx, int R, int Cn, int64_t kb, int64_t ke,
+                                               f32x16 (&acc)[2][2], SyrkSmem& sm) {
     const int w = threadIdx.x >> 6;
     const int wr = (w >> 1) * 64, wc = (w & 1) * 64;
-    const int kh = lane >> 5;
-    const float* A = X + r0;
-    const float* B = X + c0;
-    const bool aligned = R == kT128 && Cn == kT128 && (ldx & 3) == 0 &&
-                         ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
     const int64_t nk = (ke - kb + kSyKT - 1) / kSyKT;
     f32x4 va[4], vb[4];
-    {
-        const bool fast = aligned && kb + kSyKT <= K;
-        syrk_load(A, ldx, R, K, kb, fast, va);
-        syrk_load(B, ldx, Cn, K, kb, fast, vb);
-        syrk_store(sm.a[0], va);
-        syrk_store(sm.b[0], vb);
-    }
+    syrk_load<kFull>(A, ldx, R, ke, kb, va);
+    syrk_load<kFull>(B, ldx, Cn, ke, kb, vb);
+    syrk_store(sm.a[0], va);
+    syrk_store(sm.b[0], vb);
     __syncthreads();
     for (int64_t it = 0; it < nk; ++it) {
         const int cur = (int)(it & 1);
         const bool more = it + 1 < nk;
         if (more) {
             const int64_t k0 = kb + (it + 1) * kSyKT;
-            const bool fast = aligned && k0 + kSyKT <= K;
-            syrk_load(A, ldx, R, K, k0, fast, va);
-            syrk_load(B, ldx, Cn, K, k0, fast, vb);
+            syrk_load<kFull>(A, ldx, R, ke, k0, va);
+            syrk_load<kFull>(B, ldx, Cn, ke, k0, vb);
         }
-#pragma unroll
-        for (int kk = 0; kk < kSyKT; kk += 2) {
-            float fa[2], fb[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                fa[h] = sm.a[cur][kk + kh][wr + 32 * h + (lane & 31)];
-                fb[h] = sm.b[cur][kk + kh][wc + 32 * h + (lane & 31)];
-            }
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb)
-                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[rb], fb[cb], acc[rb][cb], 0, 0, 0);
-        }
+        syrk_slice(sm.a[cur], sm.b[cur], wr, wc, acc);
         if (more) {
             syrk_store(sm.a[cur ^ 1], va);
             syrk_store(sm.b[cur ^ 1], vb);
         }
         __syncthreads();
     }
+}
+
+__device__ __forceinline__ void syrk_tile(const float* __restrict__ X, int64_t ldx, int64_t r0,
+                                          int R, int64_t c0, int Cn, int64_t kb, int64_t ke,
+                                          f32x16 (&acc)[2][2], SyrkSmem& sm) {
+    if (ke <= kb) return;
+    const float* A = X + r0;
+    const float* B = X + c0;
+    const bool full = R == kT128 && Cn == kT128 && (ldx & 3) == 0 &&
+                      ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
+    if (full) syrk_tile_impl<true>(A, B, ldx, R, Cn, kb, ke, acc, sm);
+    else syrk_tile_impl<false>(A, B, ldx, R, Cn, kb, ke, acc, sm);
 }
 
 // row / column inside the 128x128 tile of element v of block (rb, cb)
