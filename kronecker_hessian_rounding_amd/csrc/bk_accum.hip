@@ -46,7 +46,8 @@ __device__ __forceinline__ void upper_tile(int64_t id, int64_t nb, int64_t& bi, 
 // Thread t loads rows k0 + (t >> 5) + 8 h (h = 0..3), columns 4 (t & 31)..+3
 // of the 128 columns starting at X + c0; zeros outside [0, K) x [0, ncol).
 // kFull: the tile is 128 columns wide and 16-byte aligned, so each row is one
-// vector load (rows past K are clamped to K - 1 and replaced by zero).
+// vector load (rows past K are clamped to K - 1 here and zeroed by the store,
+// which keeps the loads in flight).
 template <bool kFull>
 __device__ __forceinline__ void syrk_load(const float* __restrict__ X, int64_t ldx, int ncol,
                                           int64_t K, int64_t k0, f32x4 (&v)[4]) {
@@ -56,8 +57,7 @@ __device__ __forceinline__ void syrk_load(const float* __restrict__ X, int64_t l
     for (int h = 0; h < 4; ++h) {
         const int64_t k = k0 + (t >> 5) + 8 * h;
         if (kFull) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(X + min(k, K - 1) * ldx + c4);
-            v[h] = k < K ? x : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            v[h] = *reinterpret_cast<const f32x4*>(X + min(k, K - 1) * ldx + c4);
         } else {
             const float* p = X + k * ldx + c4;
 #pragma unroll
@@ -66,11 +66,16 @@ __device__ __forceinline__ void syrk_load(const float* __restrict__ X, int64_t l
     }
 }
 
-__device__ __forceinline__ void syrk_store(float (&dst)[kSyKT][kT128], const f32x4 (&v)[4]) {
+// stores a loaded slice; rows k0 + r >= K are written as zeros
+__device__ __forceinline__ void syrk_store(float (&dst)[kSyKT][kT128], const f32x4 (&v)[4], int64_t K,
+                                           int64_t k0) {
     const int t = threadIdx.x;
     const int c4 = (t & 31) << 2;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) *reinterpret_cast<f32x4*>(&dst[(t >> 5) + 8 * h][c4]) = v[h];
+    for (int h = 0; h < 4; ++h) {
+        const int r = (t >> 5) + 8 * h;
+        *reinterpret_cast<f32x4*>(&dst[r][c4]) = k0 + r < K ? v[h] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
 }
 
 // The MFMAs of one 32-deep slice: wave quadrant rows wr.., columns wc..; the
@@ -117,8 +122,8 @@ __device__ __forceinline__ void syrk_tile_impl(const float* __restrict__ A, cons
     f32x4 va[4], vb[4];
     syrk_load<kFull>(A, ldx, R, ke, kb, va);
     syrk_load<kFull>(B, ldx, Cn, ke, kb, vb);
-    syrk_store(sm.a[0], va);
-    syrk_store(sm.b[0], vb);
+    syrk_store(sm.a[0], va, ke, kb);
+    syrk_store(sm.b[0], vb, ke, kb);
     __syncthreads();
     for (int64_t it = 0; it < nk; ++it) {
         const int cur = (int)(it & 1);
@@ -130,8 +135,8 @@ __device__ __forceinline__ void syrk_tile_impl(const float* __restrict__ A, cons
         }
         syrk_slice(sm.a[cur], sm.b[cur], wr, wc, acc);
         if (more) {
-            syrk_store(sm.a[cur ^ 1], va);
-            syrk_store(sm.b[cur ^ 1], vb);
+            syrk_store(sm.a[cur ^ 1], va, ke, kb + (it + 1) * kSyKT);
+            syrk_store(sm.b[cur ^ 1], vb, ke, kb + (it + 1) * kSyKT);
         }
         __syncthreads();
     }

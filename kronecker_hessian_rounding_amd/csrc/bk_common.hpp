@@ -56,68 +56,70 @@ __device__ __forceinline__ void gemm_load_slice(const T* __restrict__ A, int64_t
 }
 
 // ---------------------------------------------------------------------------
-// fp32 64x64 tile, 32-deep k-slices kept in LDS as loaded ([k][column]):
+// fp32 64x64 tile over KT-deep k-slices kept in LDS as loaded ([k][column]):
 // 16-byte stores of consecutive columns, and per MFMA each half-wave reads 32
 // consecutive columns of one k-row, so neither side has bank conflicts. The
-// next slice is fetched into registers while the current one feeds the MFMAs.
+// next slice is fetched into registers while the current one feeds the MFMAs,
+// and the MFMA operands are read from LDS two k-steps ahead.
 // ---------------------------------------------------------------------------
-constexpr int kKT32 = 32;
-struct GemmSmemT {
-    float a[2][kKT32][kTile];
-    float b[2][kKT32][kTile];
+template <int KT>
+struct GemmSmemF32 {
+    float a[2][KT][kTile];
+    float b[2][KT][kTile];
 };
 
-// Thread t loads rows k0 + (t >> 4) and k0 + 16 + (t >> 4), columns
-// 4 (t & 15) .. +3, of a K-major operand; zeros outside [0, K) x [0, R).
-__device__ __forceinline__ void slice_load32(const float* __restrict__ A, int64_t lda, int R,
-                                             int64_t K, int64_t k0, bool fast, f32x4 (&v)[2]) {
+// Thread t loads rows k0 + (t >> 4) + 16 h (h < KT / 16), columns 4 (t & 15)..+3,
+// of a K-major operand; zeros outside [0, K) x [0, R). fast: the tile is 64
+// columns wide and 16-byte aligned, so each row is one vector load (rows past
+// K are clamped here and zeroed by the store, which keeps the loads in flight).
+template <int KT, bool kFast>
+__device__ __forceinline__ void slice_load_f32(const float* __restrict__ A, int64_t lda, int R,
+                                               int64_t K, int64_t k0, f32x4 (&v)[KT / 16]) {
     const int t = threadIdx.x;
     const int c4 = (t & 15) << 2;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < KT / 16; ++h) {
         const int64_t k = k0 + (t >> 4) + 16 * h;
-        const float* p = A + k * lda + c4;
-        if (fast) {
-            v[h] = *reinterpret_cast<const f32x4*>(p);
+        if (kFast) {
+            v[h] = *reinterpret_cast<const f32x4*>(A + min(k, K - 1) * lda + c4);
         } else {
+            const float* p = A + k * lda + c4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[h][e] = (k < K && c4 + e < R) ? p[e] : 0.0f;
         }
     }
 }
 
-__device__ __forceinline__ void slice_store32(float (&dst)[kKT32][kTile], const f32x4 (&v)[2]) {
+// stores a loaded slice; rows k0 + r >= K are written as zeros
+template <int KT>
+__device__ __forceinline__ void slice_store_f32(float (&dst)[KT][kTile], const f32x4 (&v)[KT / 16],
+                                                int64_t K, int64_t k0) {
     const int t = threadIdx.x;
     const int c4 = (t & 15) << 2;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) *reinterpret_cast<f32x4*>(&dst[(t >> 4) + 16 * h][c4]) = v[h];
+    for (int h = 0; h < KT / 16; ++h) {
+        const int r = (t >> 4) + 16 * h;
+        *reinterpret_cast<f32x4*>(&dst[r][c4]) = k0 + r < K ? v[h] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
 }
 
-// acc += A^T B over K for the 64x64 tile (same operand convention as
-// the fp32 tile). All 256 threads of the workgroup must call it.
-// Threads 0..255 compute; with active = false a thread (of a larger
-// workgroup) only takes part in the barriers.
-__device__ __forceinline__ void tile_gemm32_f32(const float* __restrict__ A, int64_t lda, int R,
-                                                const float* __restrict__ B, int64_t ldb, int Cn,
-                                                int64_t K, f32x16& acc, GemmSmemT& sm,
-                                                bool active = true) {
-    if (K <= 0) return;
+template <int KT, bool kFast>
+__device__ __forceinline__ void tile_gemm_f32_impl(const float* __restrict__ A, int64_t lda, int R,
+                                                   const float* __restrict__ B, int64_t ldb, int Cn,
+                                                   int64_t K, f32x16& acc, GemmSmemF32<KT>& sm,
+                                                   bool active) {
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int ra = (w >> 1) * 32 + (lane & 31);
     const int rb = (w & 1) * 32 + (lane & 31);
     const int kh = lane >> 5;
-    // full, aligned slices take unchecked vector loads
-    const bool aligned = R == kTile && Cn == kTile && (lda & 3) == 0 && (ldb & 3) == 0 &&
-                         ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
-    const int64_t nk = (K + kKT32 - 1) / kKT32;
-    f32x4 va[2], vb[2];
+    const int64_t nk = (K + KT - 1) / KT;
+    f32x4 va[KT / 16], vb[KT / 16];
     if (active) {
-        const bool fast = aligned && kKT32 <= K;
-        slice_load32(A, lda, R, K, 0, fast, va);
-        slice_load32(B, ldb, Cn, K, 0, fast, vb);
-        slice_store32(sm.a[0], va);
-        slice_store32(sm.b[0], vb);
+        slice_load_f32<KT, kFast>(A, lda, R, K, 0, va);
+        slice_load_f32<KT, kFast>(B, ldb, Cn, K, 0, vb);
+        slice_store_f32<KT>(sm.a[0], va, K, 0);
+        slice_store_f32<KT>(sm.b[0], vb, K, 0);
     }
     __syncthreads();
     for (int64_t it = 0; it < nk; ++it) {
@@ -128,21 +130,46 @@ __device__ __forceinline__ void tile_gemm32_f32(const float* __restrict__ A, int
             continue;
         }
         if (more) {
-            const int64_t k0 = (it + 1) * kKT32;
-            const bool fast = aligned && k0 + kKT32 <= K;
-            slice_load32(A, lda, R, K, k0, fast, va);
-            slice_load32(B, ldb, Cn, K, k0, fast, vb);
+            slice_load_f32<KT, kFast>(A, lda, R, K, (it + 1) * KT, va);
+            slice_load_f32<KT, kFast>(B, ldb, Cn, K, (it + 1) * KT, vb);
         }
+        float fa[3], fb[3];
+        fa[0] = sm.a[cur][kh][ra];
+        fb[0] = sm.b[cur][kh][rb];
+        fa[1] = sm.a[cur][2 + kh][ra];
+        fb[1] = sm.b[cur][2 + kh][rb];
 #pragma unroll
-        for (int kk = 0; kk < kKT32; kk += 2)
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sm.a[cur][kk + kh][ra], sm.b[cur][kk + kh][rb],
-                                                       acc, 0, 0, 0);
+        for (int s = 0; s < KT / 2; ++s) {
+            if (s + 2 < KT / 2) {
+                fa[(s + 2) % 3] = sm.a[cur][2 * (s + 2) + kh][ra];
+                fb[(s + 2) % 3] = sm.b[cur][2 * (s + 2) + kh][rb];
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep the reads two steps ahead of the MFMAs
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[s % 3], fb[s % 3], acc, 0, 0, 0);
+        }
         if (more) {
-            slice_store32(sm.a[cur ^ 1], va);
-            slice_store32(sm.b[cur ^ 1], vb);
+            slice_store_f32<KT>(sm.a[cur ^ 1], va, K, (it + 1) * KT);
+            slice_store_f32<KT>(sm.b[cur ^ 1], vb, K, (it + 1) * KT);
         }
         __syncthreads();
     }
+}
+
+// acc += A^T B over K for the 64x64 tile: A element (k, r) at A[k*lda + r]
+// with r < R valid (others read as 0), B (k, c) at B[k*ldb + c] with c < Cn;
+// wave w owns the 32x32 quadrant (w / 2, w % 2). Threads 0..255 compute; with
+// active = false a thread (of a larger workgroup) only takes part in the
+// barriers. Every thread of the workgroup must call it.
+template <int KT>
+__device__ __forceinline__ void tile_gemm_f32(const float* __restrict__ A, int64_t lda, int R,
+                                              const float* __restrict__ B, int64_t ldb, int Cn,
+                                              int64_t K, f32x16& acc, GemmSmemF32<KT>& sm,
+                                              bool active = true) {
+    if (K <= 0) return;
+    const bool fast = R == kTile && Cn == kTile && (lda & 3) == 0 && (ldb & 3) == 0 &&
+                      ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
+    if (fast) tile_gemm_f32_impl<KT, true>(A, lda, R, B, ldb, Cn, K, acc, sm, active);
+    else tile_gemm_f32_impl<KT, false>(A, lda, R, B, ldb, Cn, K, acc, sm, active);
 }
 
 // Position (row, col) inside the 64x64 tile of element v (0..15) of this

@@ -35,6 +35,7 @@ namespace bk {
 constexpr int kB = kTile;  // leaf edge
 constexpr int kNch = 8;    // maximum K-chunks per far-field product
 constexpr int kTargetWg = 1024;  // far-field workgroups aimed for per launch
+constexpr int kFarKT = 64;       // k-slice depth of the far-field GEMMs
 
 struct SolveParams {
     const float* W;
@@ -124,7 +125,7 @@ __device__ __forceinline__ void chunk_range(int kblk, int nch, int c, int& b0, i
     b1 = min(b0 + len, kblk);
 }
 
-__device__ __forceinline__ void far_body(const SolveParams& p, int d, int nch, int task, GemmSmemT& sm) {
+__device__ __forceinline__ void far_body(const SolveParams& p, int d, int nch, int task, GemmSmemF32<kFarKT>& sm) {
     if (*p.info != INT_MAX) return;  // a row scale was invalid
     const int slot = task / (2 * nch);
     const int kind = (task / nch) & 1;
@@ -144,10 +145,10 @@ __device__ __forceinline__ void far_body(const SolveParams& p, int d, int nch, i
     for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
     const bool active = threadIdx.x < kThreads;  // the fifth wave only joins the barriers
     if (kind == 0)  // p[ii][jj] = sum_k L_O[k][i0+ii] D[k][j0+jj]
-        tile_gemm32_f32(p.LO + k0 * p.ldlo + i0, p.ldlo, R, p.delta + k0 * p.ldd + j0, p.ldd, Cc,
+        tile_gemm_f32<kFarKT>(p.LO + k0 * p.ldlo + i0, p.ldlo, R, p.delta + k0 * p.ldd + j0, p.ldd, Cc,
                         K, acc, sm, active);
     else  // o^T[jj][ii] = sum_l L_I[l][j0+jj] C^T[l][i0+ii]
-        tile_gemm32_f32(p.LI + k0 * p.ldli + j0, p.ldli, Cc, p.ct + k0 * p.m + i0, p.m, R, K, acc,
+        tile_gemm_f32<kFarKT>(p.LI + k0 * p.ldli + j0, p.ldli, Cc, p.ct + k0 * p.m + i0, p.m, R, K, acc,
                         sm, active);
     if (!active) return;
     float* part = part_ptr(p, d & 1, slot, kind, c);
@@ -524,7 +525,7 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
 // the CUs the leaves leave free.
 union StepSmem {
     LeafSmem leaf;
-    GemmSmemT far;
+    GemmSmemF32<kFarKT> far;
 };
 
 __global__ __launch_bounds__(kLeafThreads, 1) void k_step(SolveParams p, int d, int nch, int nleaf,
