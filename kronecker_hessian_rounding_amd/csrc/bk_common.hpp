@@ -19,41 +19,11 @@ namespace bk {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 64;      // output tile edge (also the rounding leaf edge)
 constexpr int kThreads = 256;  // threads per workgroup for tile kernels
-constexpr int kKT = 16;        // k-slice staged in LDS per step
-
-// ---------------------------------------------------------------------------
-// LDS staging for a tile GEMM (double buffered k-slices of A and B)
-// ---------------------------------------------------------------------------
-template <typename T>
-struct GemmSmem {
-    T a[2][kKT][kTile];
-    T b[2][kKT][kTile];
-};
-
-// Load one k-slice element set for this thread: rows k0 + lk, 4 consecutive
-// output columns lc..lc+3 (fp32) or 2 sets of 2 (fp64 uses 4 scalars too).
-template <typename T>
-__device__ __forceinline__ void gemm_load_slice(const T* __restrict__ A, int64_t lda, int R,
-                                                int64_t K, int64_t k0, int lk, int lc, T (&ra)[4]) {
-    const int64_t k = k0 + lk;
-    if (k < K) {
-        const T* p = A + k * lda + lc;
-        if (lc + 3 < R) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ra[e] = p[e];
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ra[e] = (lc + e < R) ? p[e] : T(0);
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ra[e] = T(0);
-    }
-}
 
 // ---------------------------------------------------------------------------
 // fp32 64x64 tile over KT-deep k-slices kept in LDS as loaded ([k][column]):
@@ -184,55 +154,115 @@ __device__ __forceinline__ int acc32_col() {
     return (w & 1) * 32 + (lane & 31);
 }
 
-// fp64: acc[4] (2x2 blocks of 16x16 per wave quadrant) += A^T B over K.
-__device__ __forceinline__ void tile_gemm_f64(const double* __restrict__ A, int64_t lda, int R,
-                                              const double* __restrict__ B, int64_t ldb, int Cn,
-                                              int64_t K, f64x4 (&acc)[2][2], GemmSmem<double>& sm) {
-    if (K <= 0) return;
+// ---------------------------------------------------------------------------
+// fp64 64x64 tile over KT-deep k-slices (double buffered, [k][column] as
+// loaded); same structure as the fp32 tile: loads of the next slice in
+// flight during the MFMAs, MFMA operands read one k-step ahead.
+// ---------------------------------------------------------------------------
+template <int KT>
+struct GemmSmemF64 {
+    double a[2][KT][kTile];
+    double b[2][KT][kTile];
+};
+
+// Thread t loads 16-byte pairs: rows k0 + (t >> 5) + 8 u (u < KT / 8), columns
+// 2 (t & 31), +1; zeros outside [0, K) x [0, R). kFast: 64 columns, 16-byte
+// aligned rows (rows past K clamped here, zeroed by the store).
+template <int KT, bool kFast>
+__device__ __forceinline__ void slice_load_f64(const double* __restrict__ A, int64_t lda, int R,
+                                               int64_t K, int64_t k0, f64x2 (&v)[KT / 8]) {
     const int t = threadIdx.x;
-    const int lk = t >> 4;
-    const int lc = (t & 15) << 2;
-    const int lane = t & 63;
-    const int w = t >> 6;
-    const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
-    double ra[4], rb[4];
-    const int64_t nk = (K + kKT - 1) / kKT;
-    gemm_load_slice<double>(A, lda, R, K, 0, lk, lc, ra);
-    gemm_load_slice<double>(B, ldb, Cn, K, 0, lk, lc, rb);
+    const int c2 = (t & 31) << 1;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        sm.a[0][lk][lc + e] = ra[e];
-        sm.b[0][lk][lc + e] = rb[e];
+    for (int u = 0; u < KT / 8; ++u) {
+        const int64_t k = k0 + (t >> 5) + 8 * u;
+        if (kFast) {
+            v[u] = *reinterpret_cast<const f64x2*>(A + min(k, K - 1) * lda + c2);
+        } else {
+            const double* p = A + k * lda + c2;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) v[u][e] = (k < K && c2 + e < R) ? p[e] : 0.0;
+        }
     }
+}
+
+template <int KT>
+__device__ __forceinline__ void slice_store_f64(double (&dst)[KT][kTile], const f64x2 (&v)[KT / 8],
+                                                int64_t K, int64_t k0) {
+    const int t = threadIdx.x;
+    const int c2 = (t & 31) << 1;
+#pragma unroll
+    for (int u = 0; u < KT / 8; ++u) {
+        const int r = (t >> 5) + 8 * u;
+        *reinterpret_cast<f64x2*>(&dst[r][c2]) = k0 + r < K ? v[u] : f64x2{0.0, 0.0};
+    }
+}
+
+template <int KT, bool kFast>
+__device__ __forceinline__ void tile_gemm_f64_impl(const double* __restrict__ A, int64_t lda, int R,
+                                                   const double* __restrict__ B, int64_t ldb, int Cn,
+                                                   int64_t K, f64x4 (&acc)[2][2], GemmSmemF64<KT>& sm) {
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int ra = (w >> 1) * 32 + (lane & 15);
+    const int rb = (w & 1) * 32 + (lane & 15);
+    const int kq = lane >> 4;
+    const int64_t nk = (K + KT - 1) / KT;
+    f64x2 va[KT / 8], vb[KT / 8];
+    slice_load_f64<KT, kFast>(A, lda, R, K, 0, va);
+    slice_load_f64<KT, kFast>(B, ldb, Cn, K, 0, vb);
+    slice_store_f64<KT>(sm.a[0], va, K, 0);
+    slice_store_f64<KT>(sm.b[0], vb, K, 0);
     __syncthreads();
     for (int64_t it = 0; it < nk; ++it) {
         const int cur = (int)(it & 1);
-        const bool more = (it + 1 < nk);
+        const bool more = it + 1 < nk;
         if (more) {
-            gemm_load_slice<double>(A, lda, R, K, (it + 1) * kKT, lk, lc, ra);
-            gemm_load_slice<double>(B, ldb, Cn, K, (it + 1) * kKT, lk, lc, rb);
+            slice_load_f64<KT, kFast>(A, lda, R, K, (it + 1) * KT, va);
+            slice_load_f64<KT, kFast>(B, ldb, Cn, K, (it + 1) * KT, vb);
         }
+        double fa[2][2], fb[2][2];
+        fa[0][0] = sm.a[cur][kq][ra];
+        fa[0][1] = sm.a[cur][kq][ra + 16];
+        fb[0][0] = sm.b[cur][kq][rb];
+        fb[0][1] = sm.b[cur][kq][rb + 16];
 #pragma unroll
-        for (int kk = 0; kk < kKT; kk += 4) {
-            const int kr = kk + (lane >> 4);
-            const double a0 = sm.a[cur][kr][wr + (lane & 15)];
-            const double a1 = sm.a[cur][kr][wr + 16 + (lane & 15)];
-            const double b0 = sm.b[cur][kr][wc + (lane & 15)];
-            const double b1 = sm.b[cur][kr][wc + 16 + (lane & 15)];
-            acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
-            acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
-            acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
-            acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
-        }
-        if (more) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sm.a[cur ^ 1][lk][lc + e] = ra[e];
-                sm.b[cur ^ 1][lk][lc + e] = rb[e];
+        for (int s = 0; s < KT / 4; ++s) {
+            const int c = s & 1;
+            if (s + 1 < KT / 4) {
+                const int kr = 4 * (s + 1) + kq;
+                fa[c ^ 1][0] = sm.a[cur][kr][ra];
+                fa[c ^ 1][1] = sm.a[cur][kr][ra + 16];
+                fb[c ^ 1][0] = sm.b[cur][kr][rb];
+                fb[c ^ 1][1] = sm.b[cur][kr][rb + 16];
             }
+            __builtin_amdgcn_sched_barrier(0);  // keep the reads one step ahead of the MFMAs
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < 2; ++bj)
+                    acc[bi][bj] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[c][bi], fb[c][bj], acc[bi][bj], 0, 0, 0);
+        }
+        if (more) {
+            slice_store_f64<KT>(sm.a[cur ^ 1], va, K, (it + 1) * KT);
+            slice_store_f64<KT>(sm.b[cur ^ 1], vb, K, (it + 1) * KT);
         }
         __syncthreads();
     }
+}
+
+// fp64: acc[bi][bj] (2x2 blocks of 16x16 per wave quadrant) += A^T B over K,
+// A element (k, r) at A[k*lda + r] (r < R), B (k, c) at B[k*ldb + c] (c < Cn).
+// All 256 threads of the workgroup must call it.
+template <int KT>
+__device__ __forceinline__ void tile_gemm_f64(const double* __restrict__ A, int64_t lda, int R,
+                                              const double* __restrict__ B, int64_t ldb, int Cn,
+                                              int64_t K, f64x4 (&acc)[2][2], GemmSmemF64<KT>& sm) {
+    if (K <= 0) return;
+    const bool fast = R == kTile && Cn == kTile && (lda & 1) == 0 && (ldb & 1) == 0 &&
+                      ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
+    if (fast) tile_gemm_f64_impl<KT, true>(A, lda, R, B, ldb, Cn, K, acc, sm);
+    else tile_gemm_f64_impl<KT, false>(A, lda, R, B, ldb, Cn, K, acc, sm);
 }
 
 // Position of element r (0..3) of block (bi, bj) of this lane's fp64 accumulator

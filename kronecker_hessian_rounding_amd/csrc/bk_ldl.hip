@@ -24,6 +24,8 @@
 namespace bk {
 
 constexpr int kSuper = 256;  // super-panel width (K of the big trailing updates)
+constexpr int kLdlKT = 32;   // k-slice depth of the fp64 panel / inner-update GEMMs (K = 64);
+                             // the wide outer updates use 16 (half the LDS, more workgroups per CU)
 
 struct LdlWs {
     double* A;     // d x d working copy, lower triangle used, ld = d
@@ -122,14 +124,20 @@ __global__ __launch_bounds__(kThreads) void k_ldl_diag(int64_t d, int64_t k0, in
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wv = t >> 6;
-    for (int e = t; e < 64 * 64; e += kThreads) {
-        const int i = e & 63, j = e >> 6;
-        double v = 0.0;
-        if (i <= j) {
-            if (j < nb) v = w.A[(k0 + j) * d + k0 + i];
-            else if (i == j) v = 1.0;
+    {
+        // every load of the thread in flight before the LDS stores
+        double v[64 * 64 / kThreads];
+#pragma unroll
+        for (int r = 0; r < 64 * 64 / kThreads; ++r) {
+            const int e = t + r * kThreads;
+            const int i = e & 63, j = e >> 6;
+            v[r] = (i <= j && j < nb) ? w.A[(k0 + j) * d + k0 + i] : (i == j ? 1.0 : 0.0);
         }
-        u[i][j] = v;
+#pragma unroll
+        for (int r = 0; r < 64 * 64 / kThreads; ++r) {
+            const int e = t + r * kThreads;
+            u[e & 63][e >> 6] = v[r];
+        }
     }
     __syncthreads();
 
@@ -243,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void k_ldl_diag(int64_t d, int64_t k0, in
 // columns (r < k0), written back in place into A[k0 + p][r].
 __global__ __launch_bounds__(kThreads) void k_ldl_panel(int64_t d, int64_t k0, int nb, LdlWs w) {
     if (*w.info >= 0) return;
-    __shared__ GemmSmem<double> sm;
+    __shared__ GemmSmemF64<kLdlKT> sm;
     const int64_t r0 = (int64_t)blockIdx.x * kTile;
     const int Cn = (int)min<int64_t>(kTile, k0 - r0);
     f64x4 acc[2][2];
@@ -251,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void k_ldl_panel(int64_t d, int64_t k0, i
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
-    tile_gemm_f64(w.Wt, 64, nb, w.A + k0 * d + r0, d, Cn, nb, acc, sm);
+    tile_gemm_f64<kLdlKT>(w.Wt, 64, nb, w.A + k0 * d + r0, d, Cn, nb, acc, sm);
     // every read of this workgroup's columns is complete (the tile loop ends in a barrier)
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi)
@@ -266,6 +274,7 @@ __global__ __launch_bounds__(kThreads) void k_ldl_panel(int64_t d, int64_t k0, i
 
 // A[r][c] -= sum_{q < K} A[q0 + q][r] A[q0 + q][c] over rows [r_lo, r_hi),
 // columns [0, c_hi), lower triangle only (c <= r).
+template <int KT>
 __global__ __launch_bounds__(kThreads) void k_ldl_update(int64_t d, int64_t r_lo, int64_t r_hi,
                                                          int64_t c_hi, int64_t q0, int64_t K,
                                                          LdlWs w) {
@@ -273,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void k_ldl_update(int64_t d, int64_t r_lo
     const int64_t r0 = r_lo + (int64_t)blockIdx.y * kTile;
     const int64_t c0 = (int64_t)blockIdx.x * kTile;
     if (c0 > r0 + kTile - 1) return;  // tile entirely above the diagonal
-    __shared__ GemmSmem<double> sm;
+    __shared__ GemmSmemF64<KT> sm;
     const int R = (int)min<int64_t>(kTile, r_hi - r0);
     const int Cn = (int)min<int64_t>(kTile, c_hi - c0);
     f64x4 acc[2][2];
@@ -282,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void k_ldl_update(int64_t d, int64_t r_lo
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
     const double* P = w.A + q0 * d;
-    tile_gemm_f64(P + r0, d, R, P + c0, d, Cn, K, acc, sm);
+    tile_gemm_f64<KT>(P + r0, d, R, P + c0, d, Cn, K, acc, sm);
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
@@ -349,13 +358,13 @@ int run_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, int64_t
             }
             if (k0 > s0) {  // rows [s0, k0) of the super-panel, every column < k0
                 const int64_t rt = (k0 - s0 + kTile - 1) / kTile, ct = (k0 + kTile - 1) / kTile;
-                hipLaunchKernelGGL(k_ldl_update, dim3((unsigned)ct, (unsigned)rt), dim3(kThreads),
+                hipLaunchKernelGGL(k_ldl_update<kLdlKT>, dim3((unsigned)ct, (unsigned)rt), dim3(kThreads),
                                    0, stream, d, s0, k0, k0, k0, (int64_t)nb, w);
             }
         }
         if (s0 > 0) {
             const int64_t tt = (s0 + kTile - 1) / kTile;
-            hipLaunchKernelGGL(k_ldl_update, dim3((unsigned)tt, (unsigned)tt), dim3(kThreads), 0,
+            hipLaunchKernelGGL(k_ldl_update<16>, dim3((unsigned)tt, (unsigned)tt), dim3(kThreads), 0,
                                stream, d, (int64_t)0, s0, s0, s0, s1 - s0, w);
         }
     }
