@@ -33,7 +33,7 @@
 namespace bk {
 
 constexpr int kB = kTile;  // leaf edge
-constexpr int kNch = 8;    // maximum K-chunks per far-field product
+constexpr int kNch = 4;    // maximum K-chunks per far-field product
 constexpr int kTargetWg = 1024;  // far-field workgroups aimed for per launch
 constexpr int kFarKT = 64;       // k-slice depth of the far-field GEMMs
 
