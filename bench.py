@@ -33,10 +33,10 @@ CAL_BYTES = 256 << 20
 # k_syrk_reduce). The counters are scaled by what they read for the
 # calibration copy above: FETCH_SIZE 131088.9 KiB and WRITE_SIZE 262144.0 KiB
 # for 262144 KiB moved each way. Valid only for the kernel source it was
-# measured on (hash of bk_accum.hip + bk_common.hpp); otherwise reported null.
+# measured on (hash of bk_accum.hip, which holds the SYRK kernels); otherwise
+# reported null.
 SYRK_COUNTERS = {
-    ("attn", "9d3d92a54b2f654a", "e3ba0e5947ae25fa"): {"fetch_kib": 3688401.3,
-                                                        "write_kib": 99611.4},
+    ("attn", "13d48bf759322dd1"): {"fetch_kib": 3678291.6, "write_kib": 101190.6},
 }
 CAL_FETCH_KIB, CAL_WRITE_KIB = 131088.9, 262144.0
 
@@ -45,8 +45,7 @@ def syrk_traffic_bytes(workload):
     """Calibrated HBM bytes per hessian_accum call, or None if not measured for this source."""
     import hashlib
     csrc = os.path.join(ROOT, "kronecker_hessian_rounding_amd", "csrc")
-    key = (workload,) + tuple(hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest()[:16]
-                              for f in ("bk_accum.hip", "bk_common.hpp"))
+    key = (workload, hashlib.sha256(open(os.path.join(csrc, "bk_accum.hip"), "rb").read()).hexdigest()[:16])
     c = SYRK_COUNTERS.get(key)
     if c is None:
         return None
