@@ -204,6 +204,18 @@ def test_solve_ragged_shapes(bk, m, n):
     check_solve(bk, w, LO, LI, DO, DI, 2, label="ragged")
 
 
+@pytest.mark.parametrize("m,n,bits,rounding,recipe", [
+    (700, 1500, 2, "nearest", "tiny"),
+    (1500, 700, 3, "stochastic", "tiny"),
+    (1000, 1000, 4, "nearest", "mlp_down"),
+])
+def test_solve_many_leaf_diagonals(bk, m, n, bits, rounding, recipe):
+    # dozens of leaf-diagonals: split-K far fields, the adjacent-block products of
+    # the leaf, ragged last leaves, every entry replayed against the oracle
+    w, LO, LI, DO, DI = factors(m, n, name=recipe)
+    check_solve(bk, w, LO, LI, DO, DI, bits, rounding, seed=4002, label="many-diagonals")
+
+
 @pytest.mark.parametrize("bits", [1, 3, 4, 8])
 def test_solve_bit_widths(bk, bits):
     w, LO, LI, DO, DI = factors(96, 160)
