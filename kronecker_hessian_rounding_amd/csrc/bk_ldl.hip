@@ -100,12 +100,19 @@ __global__ __launch_bounds__(kThreads) void k_ldl_load(const float* __restrict__
 // (i <= j), padded with the identity beyond nb, and factored in 16-wide block
 // columns from the last. Wave 0 factors a block column with one lane per row:
 // the pivot and the scaled column entries move between lanes by readlane, so
-// the 16 columns of a block need no barrier. The four waves then apply the
-// rank-16 update to the block columns on its left with f64 MFMA. The inverse
-// X = C^-1 is formed blockwise: the four 16x16 diagonal blocks by back
-// substitution (one wave each), then
-//   X[I][J] = -X[I][I] sum_{I<Q<=J} C[I][Q] X[Q][J]
-// for block rows I = 2, 1, 0 (MFMA, one wave per block).
+// the 16 columns of a block need no barrier. Each column first updates the
+// next column and starts that pivot's reciprocal square root, then applies the
+// rest of its rank-1 update, so the pivot chain overlaps the bulk of the work.
+// All four waves then apply the rank-16 update to the block columns on its
+// left with f64 MFMA. The inverse X = C^-1 is formed blockwise by waves 1-3
+// while wave 0 factors the next block column, each block as soon as what it
+// reads is final:
+//   X[B][B]: back substitution on the 16x16 diagonal block (one wave),
+//   X[I][J] = -X[I][I] sum_{I<Q<=J} C[I][Q] X[Q][J], J > I (MFMA, one wave).
+// A pivot that is not positive and finite gives a reciprocal square root that
+// is not positive and finite, and turns every later pivot into NaN, so the
+// first failing pivot in factorisation order is the highest index whose
+// 1 / C[j][j] is bad.
 __device__ __forceinline__ double readlane_f64(double v, int lane) {
     const long long b = __builtin_bit_cast(long long, v);
     const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffll), lane);
@@ -113,19 +120,121 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
     return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
 }
 
+// 1 / sqrt(x): the hardware estimate y, then y (1 + e/2 + 3 e^2 / 8) with e = 1 - x y^2,
+// which leaves a relative error of order e^3 (below double rounding)
+__device__ __forceinline__ double rsqrt_f64(double x) {
+    const double y = __builtin_amdgcn_rsq(x);
+    const double e = fma(-x * y, y, 1.0);
+    return fma(y * e, fma(e, 0.375, 0.5), y);
+}
+
 constexpr int kUs = 65;  // LDS row stride (doubles) of the diagonal-block tiles
 
+struct DiagSmem {
+    double u[64][kUs];   // C, upper part
+    double xs[64][kUs];  // X = C^-1, upper part
+    double rcd[64];      // 1 / C[j][j]
+    int badj;
+};
+
+// wave 0: factor block column b (columns 16b .. 16b+15), lane = row
+template <int b>
+__device__ __forceinline__ void ldl_factor_bcol(DiagSmem& s, int lane) {
+    double r[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) r[q] = s.u[lane][16 * b + q];
+    double rcs[16];
+    double rc = rsqrt_f64(readlane_f64(r[15], 16 * b + 15));
+#pragma unroll
+    for (int jl = 15; jl >= 0; --jl) {
+        const int jj = 16 * b + jl;
+        rcs[jl] = rc;
+        const double v = lane <= jj ? r[jl] * rc : 0.0;  // C[lane][jj]
+        r[jl] = v;
+        if (jl > 0) {  // the next column first: its pivot starts the next step's chain
+            r[jl - 1] = fma(-v, readlane_f64(v, jj - 1), r[jl - 1]);
+            rc = rsqrt_f64(readlane_f64(r[jl - 1], jj - 1));
+        }
+#pragma unroll
+        for (int q = jl - 2; q >= 0; --q) r[q] = fma(-v, readlane_f64(v, 16 * b + q), r[q]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) s.u[lane][16 * b + q] = r[q];
+    if (lane == 0) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) s.rcd[16 * b + q] = rcs[q];
+    }
+}
+
+// u[0:16b, 0:16b] -= P P^T with P = u[0:16b, 16b:16b+16], 16x16 tiles (I, K), I <= K
+__device__ __forceinline__ void ldl_trailing(DiagSmem& s, int b, int wv, int lane) {
+    for (int tile = wv; tile < b * (b + 1) / 2; tile += 4) {
+        int I = 0, K = tile;
+        while (K >= b - I) {
+            K -= b - I;
+            ++I;
+        }
+        K += I;
+        f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int kq = 16 * b + 4 * kk + (lane >> 4);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(s.u[16 * I + (lane & 15)][kq],
+                                                       s.u[16 * K + (lane & 15)][kq], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s.u[16 * I + (lane >> 4) + 4 * r][16 * K + (lane & 15)] -= acc[r];
+    }
+}
+
+// X[B][B]: lane k (mod 16) solves column k of the inverse of the 16x16 diagonal block
+__device__ __forceinline__ void ldl_inv_diag(DiagSmem& s, int B, int lane) {
+    const int B0 = 16 * B;
+    const int k = lane & 15;
+    double xl[16];
+#pragma unroll
+    for (int m = 15; m >= 0; --m) {
+        double sacc = (m == k) ? 1.0 : 0.0;
+#pragma unroll
+        for (int q = m + 1; q < 16; ++q) sacc = fma(-s.u[B0 + m][B0 + q], xl[q], sacc);
+        xl[m] = sacc * s.rcd[B0 + m];
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int m = 0; m < 16; ++m) s.xs[B0 + m][B0 + k] = xl[m];
+    }
+}
+
+// X[I][J] = -X[I][I] T, T = sum_{I<Q<=J} C[I][Q] X[Q][J]
+__device__ __forceinline__ void ldl_inv_off(DiagSmem& s, int I, int J, int lane) {
+    f64x4 tacc = {0.0, 0.0, 0.0, 0.0};
+    for (int Q = I + 1; Q <= J; ++Q) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int kq = 4 * kk + (lane >> 4);
+            tacc = __builtin_amdgcn_mfma_f64_16x16x4f64(s.u[16 * I + (lane & 15)][16 * Q + kq],
+                                                        s.xs[16 * Q + kq][16 * J + (lane & 15)], tacc,
+                                                        0, 0, 0);
+        }
+    }
+    // tacc[kk] holds T[4 kk + lane / 16][lane % 16]: the B operand of k-step kk
+    f64x4 xacc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        xacc = __builtin_amdgcn_mfma_f64_16x16x4f64(s.xs[16 * I + (lane & 15)][16 * I + 4 * kk + (lane >> 4)],
+                                                    tacc[kk], xacc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s.xs[16 * I + (lane >> 4) + 4 * r][16 * J + (lane & 15)] = -xacc[r];
+}
+
 __global__ __launch_bounds__(kThreads) void k_ldl_diag(int64_t d, int64_t k0, int nb, LdlWs w) {
-    if (*w.info >= 0) return;
-    __shared__ double u[64][kUs];   // C, upper part
-    __shared__ double xs[64][kUs];  // X = C^-1, upper part
-    __shared__ double rcd[64];      // 1 / C[j][j]
-    __shared__ int badj;
+    __shared__ DiagSmem s;
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wv = t >> 6;
     {
-        // every load of the thread in flight before the LDS stores
+        // the block and the status word in flight together
         double v[64 * 64 / kThreads];
 #pragma unroll
         for (int r = 0; r < 64 * 64 / kThreads; ++r) {
@@ -133,117 +242,63 @@ __global__ __launch_bounds__(kThreads) void k_ldl_diag(int64_t d, int64_t k0, in
             const int i = e & 63, j = e >> 6;
             v[r] = (i <= j && j < nb) ? w.A[(k0 + j) * d + k0 + i] : (i == j ? 1.0 : 0.0);
         }
+        if (*w.info >= 0) return;  // an earlier block failed
 #pragma unroll
         for (int r = 0; r < 64 * 64 / kThreads; ++r) {
             const int e = t + r * kThreads;
-            u[e & 63][e >> 6] = v[r];
+            s.u[e & 63][e >> 6] = v[r];
         }
     }
     __syncthreads();
 
-    int bad = -1;  // wave 0: the first failing pivot, in factorisation order
-#pragma unroll
-    for (int b = 3; b >= 0; --b) {
-        if (wv == 0) {
-            double r[16];  // row `lane` of block column b
-#pragma unroll
-            for (int q = 0; q < 16; ++q) r[q] = u[lane][16 * b + q];
-#pragma unroll
-            for (int jl = 15; jl >= 0; --jl) {
-                const int jj = 16 * b + jl;
-                const double piv = readlane_f64(r[jl], jj);
-                if (bad < 0 && !(piv > 0.0 && piv < INFINITY)) bad = jj;
-                const double rc = rsqrt(piv);
-                const double v = lane < jj ? r[jl] * rc : (lane == jj ? piv * rc : 0.0);
-                r[jl] = v;
-                if (lane == jj) rcd[jj] = rc;
-                // columns q < jj of the block: r[q] -= C[lane][jj] C[q][jj]
-#pragma unroll
-                for (int q = jl - 1; q >= 0; --q) r[q] = fma(-v, readlane_f64(v, 16 * b + q), r[q]);
-            }
-#pragma unroll
-            for (int q = 0; q < 16; ++q) u[lane][16 * b + q] = r[q];
-        }
-        __syncthreads();
-        if (b > 0) {
-            // u[0:16b, 0:16b] -= P P^T with P = u[0:16b, 16b:16b+16], 16x16 tiles (I, K), I <= K
-            for (int tile = wv; tile < b * (b + 1) / 2; tile += 4) {
-                int I = 0, K = tile;
-                while (K >= b - I) {
-                    K -= b - I;
-                    ++I;
-                }
-                K += I;
-                f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int kq = 16 * b + 4 * kk + (lane >> 4);
-                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(u[16 * I + (lane & 15)][kq],
-                                                               u[16 * K + (lane & 15)][kq], acc, 0, 0, 0);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) u[16 * I + (lane >> 4) + 4 * r][16 * K + (lane & 15)] -= acc[r];
-            }
-            __syncthreads();
-        }
-    }
-    if (t == 0) badj = bad;
+    // block column 3
+    if (wv == 0) ldl_factor_bcol<3>(s, lane);
     __syncthreads();
-    if (badj >= 0) {  // uniform after the barrier
-        if (t == 0 && badj < nb) *w.info = k0 + badj;
+    ldl_trailing(s, 3, wv, lane);
+    __syncthreads();
+    // block column 2; X[3][3] alongside
+    if (wv == 0) ldl_factor_bcol<2>(s, lane);
+    else if (wv == 1) ldl_inv_diag(s, 3, lane);
+    __syncthreads();
+    ldl_trailing(s, 2, wv, lane);
+    __syncthreads();
+    // block column 1; X[2][2] alongside
+    if (wv == 0) ldl_factor_bcol<1>(s, lane);
+    else if (wv == 1) ldl_inv_diag(s, 2, lane);
+    __syncthreads();
+    ldl_trailing(s, 1, wv, lane);
+    __syncthreads();
+    // block column 0; X[1][1] and X[2][3] alongside
+    if (wv == 0) ldl_factor_bcol<0>(s, lane);
+    else if (wv == 1) ldl_inv_diag(s, 1, lane);
+    else if (wv == 2) ldl_inv_off(s, 2, 3, lane);
+    __syncthreads();
+    // X[0][0], X[1][2], X[1][3]; wave 0 looks for a failed pivot
+    if (wv == 0) {
+        const bool bad = lane < nb && !(s.rcd[lane] > 0.0 && s.rcd[lane] < INFINITY);
+        const unsigned long long m = __ballot(bad);
+        if (lane == 0) s.badj = m ? 63 - __clzll((long long)m) : -1;
+    } else if (wv == 1) {
+        ldl_inv_diag(s, 0, lane);
+    } else if (wv == 2) {
+        ldl_inv_off(s, 1, 2, lane);
+    } else {
+        ldl_inv_off(s, 1, 3, lane);
+    }
+    __syncthreads();
+    if (s.badj >= 0) {  // uniform after the barrier
+        if (t == 0) *w.info = k0 + s.badj;
         return;
     }
-
-    // diagonal blocks of X: wave wv, lane k < 16 solves column k of block wv
-    {
-        const int B0 = 16 * wv;
-        const int k = lane & 15;
-        double xl[16];
-#pragma unroll
-        for (int m = 15; m >= 0; --m) {
-            double sacc = (m == k) ? 1.0 : 0.0;
-#pragma unroll
-            for (int q = m + 1; q < 16; ++q) sacc = fma(-u[B0 + m][B0 + q], xl[q], sacc);
-            xl[m] = sacc * rcd[B0 + m];
-        }
-        if (lane < 16) {
-#pragma unroll
-            for (int m = 0; m < 16; ++m) xs[B0 + m][B0 + k] = xl[m];
-        }
-    }
+    // X[0][1], X[0][2], X[0][3]
+    if (wv > 0) ldl_inv_off(s, 0, wv, lane);
     __syncthreads();
-    // off-diagonal blocks of X, block row I = 2, 1, 0; wave wv takes J = I + 1 + wv
-#pragma unroll
-    for (int I = 2; I >= 0; --I) {
-        const int J = I + 1 + wv;
-        if (J <= 3) {
-            f64x4 tacc = {0.0, 0.0, 0.0, 0.0};  // T = sum_Q C[I][Q] X[Q][J]
-            for (int Q = I + 1; Q <= J; ++Q) {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int kq = 4 * kk + (lane >> 4);
-                    tacc = __builtin_amdgcn_mfma_f64_16x16x4f64(u[16 * I + (lane & 15)][16 * Q + kq],
-                                                                xs[16 * Q + kq][16 * J + (lane & 15)],
-                                                                tacc, 0, 0, 0);
-                }
-            }
-            // tacc[kk] holds T[4 kk + lane / 16][lane % 16]: the B operand of k-step kk
-            f64x4 xacc = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                xacc = __builtin_amdgcn_mfma_f64_16x16x4f64(
-                    xs[16 * I + (lane & 15)][16 * I + 4 * kk + (lane >> 4)], tacc[kk], xacc, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) xs[16 * I + (lane >> 4) + 4 * r][16 * J + (lane & 15)] = -xacc[r];
-        }
-        __syncthreads();
-    }
 
     // C22 back into A (lower storage: A[k0 + j][k0 + i] = C[i][j]); Wt[j][i] = X[i][j]
     for (int e = t; e < 64 * 64; e += kThreads) {
         const int i = e & 63, j = e >> 6;
-        if (i <= j && j < nb) w.A[(k0 + j) * d + k0 + i] = u[i][j];
-        w.Wt[e] = (i <= j) ? xs[i][j] : 0.0;
+        if (i <= j && j < nb) w.A[(k0 + j) * d + k0 + i] = s.u[i][j];
+        w.Wt[e] = (i <= j) ? s.xs[i][j] : 0.0;
     }
 }
 
