@@ -183,15 +183,16 @@ constexpr int kPs = 66;  // row stride of the per-entry inputs: anti-diagonal wa
 struct LeafSmem {
     float DT[kB][kTs];     // D transposed: DT[j][k] = D[k][j] (0 until known)
     float Gs[kB][kTs];     // g = C of the leaf, row-major (0 until known)
-    float LIT[kB][kTs];    // L_I diagonal block transposed: LIT[j][l] = L_I[l][j], l < j - 2 (else 0)
+    float LIT[kB][kTs];    // L_I diagonal block transposed: LIT[j][l] = L_I[l][j], l < j - 3 (else 0)
     float base[kB][kPs];   // W* + o
     float pin[kB][kPs];    // p
     float wst[kB][kPs];    // W*, overwritten by eta = t - q once the entry is final
     float pnb[3][kB];      // bulk sums, by step modulo 3 (written two steps ahead)
     float rnb[3][kB];
     float zrow[16];        // zeros: read by bulk lanes whose chunk holds no useful term
-    float li1[kB];         // L_I[j-1][j] and L_I[j-2][j]: the finaliser's copies of the two
-    float li2[kB];         // superdiagonals, which are zero in LIT
+    float li1[kB];         // L_I[j-1][j], L_I[j-2][j], L_I[j-3][j]: the three superdiagonals,
+    float li2[kB];         // which are zero in LIT (the first two are the finaliser's terms,
+    float li3[kB];         // the third the bulk's newest term)
     uint8_t code[kB][kB + 4];
     float DI[kB];
     double red[kLeafThreads];
@@ -211,6 +212,13 @@ __device__ __forceinline__ void adj_gemm(const float* x, int sx, const float* y,
                                                    acc, 0, 0, 0);
     }
 }
+
+// A step ends with lds_wait_all() (the step's LDS stores are complete), the reads
+// for the next step, then barrier_no_wait(): the reads stay in flight across the
+// barrier, which needs only the stores. The memory clobbers keep the compiler from
+// moving memory operations across either point.
+__device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void barrier_no_wait() { asm volatile("s_barrier" ::: "memory"); }
 
 __device__ __forceinline__ float lane_above(float x) {
     // wave_shr:1 -- lane i receives lane i-1's value, lane 0 receives 0
@@ -233,9 +241,10 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
     const bool adj_p = p.LO && I > 0, adj_o = p.LI && J > 0;
 
     if (t < 16) sm.zrow[t] = 0.0f;
-    if (t < 2) {
-        sm.li2[t] = 0.0f;  // no L_I[j-2][j] for j < 2, no L_I[j-1][j] for j = 0
-        if (t == 0) sm.li1[0] = 0.0f;
+    if (t < 3) {  // no L_I[j-d][j] for j < d
+        sm.li3[t] = 0.0f;
+        if (t < 2) sm.li2[t] = 0.0f;
+        if (t < 1) sm.li1[t] = 0.0f;
     }
     // ---- A: every tile load of the thread in flight at once, then LDS
     //   DT  <- L_O[i0-64+k][i0+c]   Gs   <- D[i0-64+k][j0+c]      (block above: staging)
@@ -267,9 +276,10 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
                 sm.pin[k][c] = v3[u];
                 sm.base[k][c] = v4[u];
                 sm.wst[k][c] = v5[u];
-                sm.LIT[c][k] = (c - k <= 2) ? 0.0f : v6[u];
+                sm.LIT[c][k] = (c - k <= 3) ? 0.0f : v6[u];
                 if (c - k == 1) sm.li1[c] = v6[u];
                 if (c - k == 2) sm.li2[c] = v6[u];
+                if (c - k == 3) sm.li3[c] = v6[u];
             }
         }
     }
@@ -349,48 +359,60 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
     int nclamp = 0;
     if (w < 4) {
         // ---------------- bulk waves ----------------
-        // lane (row i, quarter q) sums the k / l range [16q, 16q + 16)
+        // lane (row i, quarter q) sums the k / l range [16q, 16q + 16). The bulk of
+        // entry (i, jn), finalised two steps later, is k <= i-3 and l <= jn-3: the
+        // newest of those (k = i-3, l = jn-3, finalised in the previous step) are read
+        // on their own at the start of the step, the rest (final one step earlier)
+        // were read at the end of the previous step, so the LDS latency of the
+        // twelve 16-byte chunk reads overlaps the barrier and the finaliser's work.
         const int i = t >> 2;
         const int q = t & 3;
         const int k0 = 16 * q;
-        float lo[16];  // L_O[i0 + k][i0 + i] for k <= i - 3, else 0
+        float lo[16];  // L_O[i0 + k][i0 + i] for k <= i - 4, else 0
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-            lo[e] = (p.LO && k0 + e <= i - 3 && i < R) ? p.LO[(i0 + k0 + e) * p.ldlo + i0 + i] : 0.0f;
-        const bool pn_any = p.LO && k0 <= i - 3 && i < R;  // this lane's chunk of L_O has a term
-        __syncthreads();
+            lo[e] = (p.LO && k0 + e <= i - 4 && i < R) ? p.LO[(i0 + k0 + e) * p.ldlo + i0 + i] : 0.0f;
+        // L_O[i-3][i], added by quarter 0 with the newest D
+        const float lo3 = (p.LO && q == 0 && i >= 3 && i < R) ? p.LO[(i0 + i - 3) * p.ldlo + i0 + i] : 0.0f;
+        const float gq = q == 0 ? 1.0f : 0.0f;  // quarter 0 adds the newest g term
+        // chunks of the step's operands: D column jn (k0..), g row i (k0..), L_I column jn (k0..).
+        // An entry written in the step the chunk is read meets a zero factor: L_O is
+        // zero beyond i-4 and LIT beyond jn-4.
+        auto fetch = [&](int st, f32x4 (&c)[12]) {
+            const int jc = min(max(st + 2 - i, 0), kB - 1);
+            const float* dp = &sm.DT[jc][k0];
+            const float* gp = &sm.Gs[i][k0];
+            const float* lp = &sm.LIT[jc][k0];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                c[h] = lds4(dp + 4 * h);
+                c[4 + h] = lds4(gp + 4 * h);
+                c[8 + h] = lds4(lp + 4 * h);
+            }
+        };
         int slot3 = 2;  // (st + 2) mod 3
-        for (int st = 0; st < 2 * kB - 1; ++st) {
-            // entry (i, jn) is finalised two steps later; its bulk takes k <= i-3 and
-            // l <= jn-3. D[k][jn] and g[i][l] in that range are final; L_O is zero
-            // beyond i-3 and LIT holds zeros for l >= jn-2 (the superdiagonals are
-            // the finaliser's), so the entries being written in this step meet a zero
-            // factor. A chunk without a useful term reads the zero row instead.
+        auto step = [&](int st, const f32x4 (&cur)[12], f32x4 (&nxt)[12]) {
             const int jn = st + 2 - i;
             const bool live = jn >= 0 && jn < kB;
             const int jc = min(max(jn, 0), kB - 1);
-            const bool rn_any = live && k0 <= jn - 3;
-            const float* dp = (live && pn_any) ? &sm.DT[jc][k0] : sm.zrow;
-            const float* gp = rn_any ? &sm.Gs[i][k0] : sm.zrow;
-            const float* lp = rn_any ? &sm.LIT[jc][k0] : sm.zrow;
-            const f32x4 d0 = lds4(dp), d1 = lds4(dp + 4), d2 = lds4(dp + 8), d3 = lds4(dp + 12);
-            const f32x4 g0 = lds4(gp), g1 = lds4(gp + 4), g2 = lds4(gp + 8), g3 = lds4(gp + 12);
-            const f32x4 l0 = lds4(lp), l1 = lds4(lp + 4), l2 = lds4(lp + 8), l3 = lds4(lp + 12);
-            __builtin_amdgcn_sched_barrier(0);  // the twelve reads go out together
-            float p0 = 0.0f, p1 = 0.0f, r0 = 0.0f, r1 = 0.0f;
+            // the newest terms, read behind the chunks fetched in the previous step
+            const float dnew = sm.DT[jc][max(i - 3, 0)];             // D[i-3][jn]
+            const float gnew = sm.Gs[i][min(max(jn - 3, 0), kB - 1)];  // g[i][jn-3]
+            const float lnew = sm.li3[jc];                            // L_I[jn-3][jn]
+            float p0 = lo3 * dnew, p1 = 0.0f, r0 = gq * gnew * lnew, r1 = 0.0f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                p0 = fmaf(lo[e], d0[e], p0);
-                p1 = fmaf(lo[4 + e], d1[e], p1);
-                r0 = fmaf(g0[e], l0[e], r0);
-                r1 = fmaf(g1[e], l1[e], r1);
+                p0 = fmaf(lo[e], cur[0][e], p0);
+                p1 = fmaf(lo[4 + e], cur[1][e], p1);
+                r0 = fmaf(cur[4][e], cur[8][e], r0);
+                r1 = fmaf(cur[5][e], cur[9][e], r1);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                p0 = fmaf(lo[8 + e], d2[e], p0);
-                p1 = fmaf(lo[12 + e], d3[e], p1);
-                r0 = fmaf(g2[e], l2[e], r0);
-                r1 = fmaf(g3[e], l3[e], r1);
+                p0 = fmaf(lo[8 + e], cur[2][e], p0);
+                p1 = fmaf(lo[12 + e], cur[3][e], p1);
+                r0 = fmaf(cur[6][e], cur[10][e], r0);
+                r1 = fmaf(cur[7][e], cur[11][e], r1);
             }
             float pn = live ? p0 + p1 : 0.0f;
             float rn = live ? r0 + r1 : 0.0f;
@@ -401,8 +423,24 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
                 sm.rnb[slot3][i] = rn;
             }
             slot3 = slot3 == 2 ? 0 : slot3 + 1;
-            __syncthreads();
+            // the next step's chunks go out after the stores and stay in flight across
+            // the barrier: every entry they read with a nonzero factor was final a step
+            // earlier, so later writes into the chunks meet a zero factor
+            lds_wait_all();
+            __builtin_amdgcn_sched_barrier(0);
+            fetch(st + 1, nxt);
+            __builtin_amdgcn_sched_barrier(0);
+            barrier_no_wait();
+        };
+        f32x4 ca[12], cb[12];
+        __syncthreads();
+        fetch(0, ca);
+        int st = 0;
+        for (; st + 1 < 2 * kB - 1; st += 2) {
+            step(st, ca, cb);
+            step(st + 1, cb, ca);
         }
+        step(st, ca, cb);  // 127 steps: the last one
     } else {
         // ---------------- finaliser wave: lane i owns row i ----------------
         // adds the two newest terms of each sum: D[i-1][j], D[i-2][j] (from the
@@ -434,17 +472,6 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
             const float dprev2 = lane_above(dp1_last);  // D[i-2][j]
             const float pb = n_pb, rb = n_rb;
             const float x_pin = n_pin, x_base = n_base, x_w = n_w, x_l1 = n_l1, x_l2 = n_l2;
-            n_pb = sm.pnb[slot3n][i];
-            n_rb = sm.rnb[slot3n][i];
-            slot3n = slot3n == 2 ? 0 : slot3n + 1;
-            const int jn = j + 1;
-            if (jn >= 0 && jn < kB) {
-                n_pin = sm.pin[i][jn];
-                n_base = sm.base[i][jn];
-                n_w = sm.wst[i][jn];
-                n_l1 = sm.li1[jn];
-                n_l2 = sm.li2[jn];
-            }
             if (j >= 0 && j < Cc && i < R) {
                 float u = 0.5f;
                 if (p.stochastic)
@@ -467,7 +494,22 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
                 g_last = g;
             }
             dp1_last = dprev1;
-            __syncthreads();
+            // inputs of the next entry (the bulk sums written in the previous step, static
+            // data, this lane's own W* slot), read after the stores and left in flight
+            // across the barrier; nothing writes them in the next step
+            lds_wait_all();
+            __builtin_amdgcn_sched_barrier(0);
+            const int jn = min(max(j + 1, 0), kB - 1);
+            n_pb = sm.pnb[slot3n][i];
+            n_rb = sm.rnb[slot3n][i];
+            n_pin = sm.pin[i][jn];
+            n_base = sm.base[i][jn];
+            n_w = sm.wst[i][jn];
+            n_l1 = sm.li1[jn];
+            n_l2 = sm.li2[jn];
+            slot3n = slot3n == 2 ? 0 : slot3n + 1;
+            __builtin_amdgcn_sched_barrier(0);
+            barrier_no_wait();
         }
     }
     // loss partial: sum of D_O,i D_I,j eta_ij^2 over the leaf, in fp64
