@@ -188,17 +188,28 @@ __device__ __forceinline__ void ldl_trailing(DiagSmem& s, int b, int wv, int lan
     }
 }
 
-// X[B][B]: lane k (mod 16) solves column k of the inverse of the 16x16 diagonal block
+// X[B][B]: lane k (mod 16) solves column k of the inverse of the 16x16 diagonal block by
+// column-oriented back substitution: once x[m] is known it is removed from every
+// equation above it, so the dependent chain is two operations per row
 __device__ __forceinline__ void ldl_inv_diag(DiagSmem& s, int B, int lane) {
     const int B0 = 16 * B;
     const int k = lane & 15;
-    double xl[16];
+    double cu[16][16];  // C[B0 + q][B0 + m], q < m (upper part of the block)
+#pragma unroll
+    for (int m = 1; m < 16; ++m)
+#pragma unroll
+        for (int q = 0; q < m; ++q) cu[q][m] = s.u[B0 + q][B0 + m];
+    double rc[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) rc[m] = s.rcd[B0 + m];
+    double rhs[16], xl[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) rhs[m] = (m == k) ? 1.0 : 0.0;
 #pragma unroll
     for (int m = 15; m >= 0; --m) {
-        double sacc = (m == k) ? 1.0 : 0.0;
+        xl[m] = rhs[m] * rc[m];
 #pragma unroll
-        for (int q = m + 1; q < 16; ++q) sacc = fma(-s.u[B0 + m][B0 + q], xl[q], sacc);
-        xl[m] = sacc * s.rcd[B0 + m];
+        for (int q = m - 1; q >= 0; --q) rhs[q] = fma(-cu[q][m], xl[m], rhs[q]);
     }
     if (lane < 16) {
 #pragma unroll
@@ -228,28 +239,68 @@ __device__ __forceinline__ void ldl_inv_off(DiagSmem& s, int I, int J, int lane)
     for (int r = 0; r < 4; ++r) s.xs[16 * I + (lane >> 4) + 4 * r][16 * J + (lane & 15)] = -xacc[r];
 }
 
-__global__ __launch_bounds__(kThreads) void k_ldl_diag(int64_t d, int64_t k0, int nb, LdlWs w) {
-    __shared__ DiagSmem s;
+// With pn, the block first takes the update of the panel block just formed below it:
+// u[i][j] -= sum_{p < np} pn[p d + i] pn[p d + j] (np rows of C12^T, the block's 64 columns).
+__device__ __forceinline__ void diag_body(int64_t d, int64_t k0, int nb, const LdlWs& w, DiagSmem& s,
+                                          const double* pn = nullptr, int np = 0) {
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wv = t >> 6;
     {
-        // the block and the status word in flight together
-        double v[64 * 64 / kThreads];
+        // the block, the panel rows and the status word in flight together
+        constexpr int kPer = 64 * 64 / kThreads;
+        double v[kPer], pv[kPer];
 #pragma unroll
-        for (int r = 0; r < 64 * 64 / kThreads; ++r) {
+        for (int r = 0; r < kPer; ++r) {
             const int e = t + r * kThreads;
             const int i = e & 63, j = e >> 6;
             v[r] = (i <= j && j < nb) ? w.A[(k0 + j) * d + k0 + i] : (i == j ? 1.0 : 0.0);
+            pv[r] = (pn && j < np) ? pn[j * d + i] : 0.0;  // row j of the panel, column i
         }
         if (*w.info >= 0) return;  // an earlier block failed
 #pragma unroll
-        for (int r = 0; r < 64 * 64 / kThreads; ++r) {
+        for (int r = 0; r < kPer; ++r) {
             const int e = t + r * kThreads;
             s.u[e & 63][e >> 6] = v[r];
+            s.xs[e >> 6][e & 63] = pv[r];  // xs is free until the inverse
         }
     }
     __syncthreads();
+    if (pn) {
+        // 32x32 quadrants on or above the diagonal, one wave each, K = 64 panel rows
+        const int qi = wv >> 1, qj = wv & 1;
+        if (qi <= qj) {
+            const int ra = 32 * qi + (lane & 15), rb = 32 * qj + (lane & 15);
+            const int kq = lane >> 4;
+            f64x4 acc[2][2];
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+            for (int kk = 0; kk < 16; ++kk) {
+                const int p = 4 * kk + kq;
+                const double fa0 = s.xs[p][ra], fa1 = s.xs[p][ra + 16];
+                const double fb0 = s.xs[p][rb], fb1 = s.xs[p][rb + 16];
+                acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa0, fb0, acc[0][0], 0, 0, 0);
+                acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa0, fb1, acc[0][1], 0, 0, 0);
+                acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa1, fb0, acc[1][0], 0, 0, 0);
+                acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa1, fb1, acc[1][1], 0, 0, 0);
+            }
+            // output layout: row = 16 bi + lane / 16 + 4 r, column = 16 bj + lane % 16
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 32 * qi + 16 * bi + (lane >> 4) + 4 * r;
+                        const int j = 32 * qj + 16 * bj + (lane & 15);
+                        if (i <= j) s.u[i][j] -= acc[bi][bj][r];
+                    }
+        }
+        __syncthreads();
+    }
 
     // block column 3
     if (wv == 0) ldl_factor_bcol<3>(s, lane);
@@ -294,12 +345,29 @@ __global__ __launch_bounds__(kThreads) void k_ldl_diag(int64_t d, int64_t k0, in
     if (wv > 0) ldl_inv_off(s, 0, wv, lane);
     __syncthreads();
 
-    // C22 back into A (lower storage: A[k0 + j][k0 + i] = C[i][j]); Wt[j][i] = X[i][j]
-    for (int e = t; e < 64 * 64; e += kThreads) {
+    // C22 back into A (lower storage: A[k0 + j][k0 + i] = C[i][j]); Wt[j][i] = X[i][j].
+    // Every LDS read of the thread first, then the stores.
+    constexpr int kPer = 64 * 64 / kThreads;
+    double cv[kPer], xv[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const int e = t + r * kThreads;
         const int i = e & 63, j = e >> 6;
-        if (i <= j && j < nb) w.A[(k0 + j) * d + k0 + i] = s.u[i][j];
-        w.Wt[e] = (i <= j) ? s.xs[i][j] : 0.0;
+        cv[r] = s.u[i][j];
+        xv[r] = (i <= j) ? s.xs[i][j] : 0.0;
     }
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const int e = t + r * kThreads;
+        const int i = e & 63, j = e >> 6;
+        if (i <= j && j < nb) w.A[(k0 + j) * d + k0 + i] = cv[r];
+        w.Wt[e] = xv[r];
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_ldl_diag(int64_t d, int64_t k0, int nb, LdlWs w) {
+    __shared__ DiagSmem s;
+    diag_body(d, k0, nb, w, s);
 }
 
 // C12^T[p][r] = sum_q (C22^-1)[p][q] A[k0 + q][r] for r in this workgroup's 64
@@ -327,17 +395,12 @@ __global__ __launch_bounds__(kThreads) void k_ldl_panel(int64_t d, int64_t k0, i
             }
 }
 
-// A[r][c] -= sum_{q < K} A[q0 + q][r] A[q0 + q][c] over rows [r_lo, r_hi),
-// columns [0, c_hi), lower triangle only (c <= r).
+// One 64x64 tile (rows r0.., columns c0..) of A[r][c] -= sum_{q < K} A[q0 + q][r] A[q0 + q][c],
+// rows below r_hi, columns below c_hi, lower triangle only (c <= r).
 template <int KT>
-__global__ __launch_bounds__(kThreads) void k_ldl_update(int64_t d, int64_t r_lo, int64_t r_hi,
-                                                         int64_t c_hi, int64_t q0, int64_t K,
-                                                         LdlWs w) {
-    if (*w.info >= 0) return;
-    const int64_t r0 = r_lo + (int64_t)blockIdx.y * kTile;
-    const int64_t c0 = (int64_t)blockIdx.x * kTile;
-    if (c0 > r0 + kTile - 1) return;  // tile entirely above the diagonal
-    __shared__ GemmSmemF64<KT> sm;
+__device__ __forceinline__ void update_tile(int64_t d, int64_t r0, int64_t r_hi, int64_t c0,
+                                            int64_t c_hi, int64_t q0, int64_t K, const LdlWs& w,
+                                            GemmSmemF64<KT>& sm) {
     const int R = (int)min<int64_t>(kTile, r_hi - r0);
     const int Cn = (int)min<int64_t>(kTile, c_hi - c0);
     f64x4 acc[2][2];
@@ -357,6 +420,46 @@ __global__ __launch_bounds__(kThreads) void k_ldl_update(int64_t d, int64_t r_lo
                 const int64_t gi = r0 + lr, gj = c0 + lc;
                 if (lr < R && lc < Cn && gj <= gi) w.A[gi * d + gj] -= acc[bi][bj][r];
             }
+}
+
+// A[r][c] -= sum_{q < K} A[q0 + q][r] A[q0 + q][c] over rows [r_lo, r_hi),
+// columns [0, c_hi), lower triangle only (c <= r).
+template <int KT>
+__global__ __launch_bounds__(kThreads) void k_ldl_update(int64_t d, int64_t r_lo, int64_t r_hi,
+                                                         int64_t c_hi, int64_t q0, int64_t K,
+                                                         LdlWs w) {
+    if (*w.info >= 0) return;
+    const int64_t r0 = r_lo + (int64_t)blockIdx.y * kTile;
+    const int64_t c0 = (int64_t)blockIdx.x * kTile;
+    if (c0 > r0 + kTile - 1) return;  // tile entirely above the diagonal
+    __shared__ GemmSmemF64<KT> sm;
+    update_tile<KT>(d, r0, r_hi, c0, c_hi, q0, K, w, sm);
+}
+
+// Workgroup 0 applies the update of the block just panelled (K rows at q0) to the
+// diagonal block at kn (64 wide) and factors it; the others apply the same block's
+// inner update to rows [r_lo, r_hi) x columns [0, c_hi), in a ct-wide grid of
+// tiles, all but the tile (kn, kn). The two parts touch disjoint parts of A.
+__global__ __launch_bounds__(kThreads) void k_ldl_diag_update(int64_t d, int64_t kn, int64_t r_lo,
+                                                              int64_t r_hi, int64_t c_hi, int64_t q0,
+                                                              int64_t K, int ct, LdlWs w) {
+    __shared__ union {
+        DiagSmem diag;
+        GemmSmemF64<kLdlKT> g;
+    } sm;
+    if (blockIdx.x == 0) {
+        // the block was last updated by the super-panel's earlier blocks; the panel
+        // block at q0 (K rows) is applied here
+        diag_body(d, kn, kTile, w, sm.diag, w.A + q0 * d + kn, (int)K);
+        return;
+    }
+    if (*w.info >= 0) return;
+    const int tile = (int)blockIdx.x - 1;
+    const int64_t r0 = r_lo + (int64_t)(tile / ct) * kTile;
+    const int64_t c0 = (int64_t)(tile % ct) * kTile;
+    if (c0 > r0 + kTile - 1) return;     // entirely above the diagonal
+    if (r0 == kn && c0 == kn) return;    // the next diagonal block
+    update_tile<kLdlKT>(d, r0, r_hi, c0, c_hi, q0, K, w, sm.g);
 }
 
 // H[i][j] = C[i][j] / C[j][j] (i < j), C[j][j]^2 (i = j), 0 (i > j), with
@@ -401,20 +504,29 @@ int run_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, int64_t
     hipLaunchKernelGGL(k_ldl_init, dim3(1), dim3(kThreads), 0, stream, H, d, ldh, damp_rel, w);
     hipLaunchKernelGGL(k_ldl_load, dim3((unsigned)nbt, (unsigned)nbt), dim3(kThreads), 0, stream,
                        H, d, ldh, w);
+    // Per 64-wide block k0 (last to first) of each 256-wide super-panel [s0, s1):
+    //   panel(k0)
+    //   diag(k0 - 64) + inner(k0)      -- one launch: the next diagonal block takes this
+    //                                     block's update and is factored beside the rest
+    //                                     of this block's inner update
+    // and after the super-panel the outer update, then the next super-panel's first
+    // diagonal block on its own.
     const int64_t nsuper = (d + kSuper - 1) / kSuper;
     for (int64_t s = nsuper - 1; s >= 0; --s) {
         const int64_t s0 = s * kSuper, s1 = std::min<int64_t>(s0 + kSuper, d);
-        for (int64_t k0 = ((s1 - 1) / 64) * 64; k0 >= s0; k0 -= 64) {
+        const int64_t top = ((s1 - 1) / 64) * 64;
+        hipLaunchKernelGGL(k_ldl_diag, dim3(1), dim3(kThreads), 0, stream, d, top,
+                           (int)std::min<int64_t>(64, d - top), w);
+        for (int64_t k0 = top; k0 >= s0; k0 -= 64) {
             const int nb = (int)std::min<int64_t>(64, d - k0);
-            hipLaunchKernelGGL(k_ldl_diag, dim3(1), dim3(kThreads), 0, stream, d, k0, nb, w);
             if (k0 > 0) {
                 hipLaunchKernelGGL(k_ldl_panel, dim3((unsigned)((k0 + 63) / 64)), dim3(kThreads),
                                    0, stream, d, k0, nb, w);
             }
             if (k0 > s0) {  // rows [s0, k0) of the super-panel, every column < k0
                 const int64_t rt = (k0 - s0 + kTile - 1) / kTile, ct = (k0 + kTile - 1) / kTile;
-                hipLaunchKernelGGL(k_ldl_update<kLdlKT>, dim3((unsigned)ct, (unsigned)rt), dim3(kThreads),
-                                   0, stream, d, s0, k0, k0, k0, (int64_t)nb, w);
+                hipLaunchKernelGGL(k_ldl_diag_update, dim3((unsigned)(1 + rt * ct)), dim3(kThreads),
+                                   0, stream, d, k0 - 64, s0, k0, k0, k0, (int64_t)nb, (int)ct, w);
             }
         }
         if (s0 > 0) {
