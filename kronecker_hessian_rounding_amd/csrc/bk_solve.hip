@@ -183,16 +183,13 @@ constexpr int kPs = 66;  // row stride of the per-entry inputs: anti-diagonal wa
 struct LeafSmem {
     float DT[kB][kTs];     // D transposed: DT[j][k] = D[k][j] (0 until known)
     float Gs[kB][kTs];     // g = C of the leaf, row-major (0 until known)
-    float LIT[kB][kTs];    // L_I diagonal block transposed: LIT[j][l] = L_I[l][j], l < j - 3 (else 0)
     float base[kB][kPs];   // W* + o
     float pin[kB][kPs];    // p
     float wst[kB][kPs];    // W*, overwritten by eta = t - q once the entry is final
     float pnb[3][kB];      // bulk sums, by step modulo 3 (written two steps ahead)
     float rnb[3][kB];
-    float zrow[16];        // zeros: read by bulk lanes whose chunk holds no useful term
-    float li1[kB];         // L_I[j-1][j], L_I[j-2][j], L_I[j-3][j]: the three superdiagonals,
-    float li2[kB];         // which are zero in LIT (the first two are the finaliser's terms,
-    float li3[kB];         // the third the bulk's newest term)
+    float li1[kB];         // L_I[j-1][j], L_I[j-2][j]: the finaliser's terms
+    float li2[kB];
     uint8_t code[kB][kB + 4];
     float DI[kB];
     double red[kLeafThreads];
@@ -240,16 +237,14 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
     const bool far_p = p.LO && I > 1, far_o = p.LI && J > 1;  // all nch partials were written
     const bool adj_p = p.LO && I > 0, adj_o = p.LI && J > 0;
 
-    if (t < 16) sm.zrow[t] = 0.0f;
-    if (t < 3) {  // no L_I[j-d][j] for j < d
-        sm.li3[t] = 0.0f;
-        if (t < 2) sm.li2[t] = 0.0f;
+    if (t < 2) {  // no L_I[j-d][j] for j < d
+        sm.li2[t] = 0.0f;
         if (t < 1) sm.li1[t] = 0.0f;
     }
     // ---- A: every tile load of the thread in flight at once, then LDS
     //   DT  <- L_O[i0-64+k][i0+c]   Gs   <- D[i0-64+k][j0+c]      (block above: staging)
     //   pin <- L_I[j0-64+k][j0+c]   base <- C^T[j0-64+k][i0+c]    (block to the left: staging)
-    //   wst <- W*[i0+k][j0+c]       LIT[c][k] <- L_I[j0+k][j0+c], k < c
+    //   wst <- W*[i0+k][j0+c]       li1, li2 <- the first two superdiagonals of L_I
     {
         constexpr int kPer = (kB * kB + kLeafThreads - 1) / kLeafThreads;
         float v1[kPer], v2[kPer], v3[kPer], v4[kPer], v5[kPer], v6[kPer];
@@ -264,7 +259,7 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
             v3[u] = (in && adj_o && c < Cc) ? p.LI[jk * p.ldli + j0 + c] : 0.0f;
             v4[u] = (in && adj_o && c < R) ? p.ct[jk * p.m + i0 + c] : 0.0f;
             v5[u] = (in && k < R && c < Cc) ? p.W[(i0 + k) * p.ldw + j0 + c] : 0.0f;
-            v6[u] = (in && p.LI && k < c && c < Cc) ? p.LI[(j0 + k) * p.ldli + j0 + c] : 0.0f;
+            v6[u] = (in && p.LI && (c - k == 1 || c - k == 2) && c < Cc) ? p.LI[(j0 + k) * p.ldli + j0 + c] : 0.0f;
         }
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
@@ -276,10 +271,8 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
                 sm.pin[k][c] = v3[u];
                 sm.base[k][c] = v4[u];
                 sm.wst[k][c] = v5[u];
-                sm.LIT[c][k] = (c - k <= 3) ? 0.0f : v6[u];
                 if (c - k == 1) sm.li1[c] = v6[u];
                 if (c - k == 2) sm.li2[c] = v6[u];
-                if (c - k == 3) sm.li3[c] = v6[u];
             }
         }
     }
@@ -359,68 +352,72 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
     int nclamp = 0;
     if (w < 4) {
         // ---------------- bulk waves ----------------
-        // lane (row i, quarter q) sums the k / l range [16q, 16q + 16). The bulk of
-        // entry (i, jn), finalised two steps later, is k <= i-3 and l <= jn-3: the
-        // newest of those (k = i-3, l = jn-3, finalised in the previous step) are read
-        // on their own at the start of the step, the rest (final one step earlier)
-        // were read at the end of the previous step, so the LDS latency of the
-        // twelve 16-byte chunk reads overlaps the barrier and the finaliser's work.
-        const int i = t >> 2;
+        // Lane (a, quarter q) sums the k / l range [16q, 16q + 16) of two bulk sums of
+        // the entries finalised two steps later (x = st + 2 - a):
+        //   P of entry (a, x): sum_k L_O[k][a] D[k][x],  k <= a - 3 (row a)
+        //   R of entry (x, a): sum_l g[x][l] L_I[l][a],  l <= a - 3 (column a)
+        // so both triangular factors stay in registers (row a of L_O^T, column a of
+        // L_I) and a step reads two 16-float chunks per lane: column x of D and row x
+        // of g. The newest terms (k, l = a - 3, final in the previous step) are read
+        // on their own at the start of the step; the chunks (entries final a step
+        // earlier) were read at the end of the previous step, so their LDS latency
+        // overlaps the barrier and the finaliser's work.
+        const int a = t >> 2;
         const int q = t & 3;
         const int k0 = 16 * q;
-        float lo[16];  // L_O[i0 + k][i0 + i] for k <= i - 4, else 0
+        float lo[16];  // L_O[i0 + k][i0 + a] for k <= a - 4, else 0
+        float li[16];  // L_I[j0 + l][j0 + a] for l <= a - 4, else 0
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            lo[e] = (p.LO && k0 + e <= i - 4 && i < R) ? p.LO[(i0 + k0 + e) * p.ldlo + i0 + i] : 0.0f;
-        // L_O[i-3][i], added by quarter 0 with the newest D
-        const float lo3 = (p.LO && q == 0 && i >= 3 && i < R) ? p.LO[(i0 + i - 3) * p.ldlo + i0 + i] : 0.0f;
-        const float gq = q == 0 ? 1.0f : 0.0f;  // quarter 0 adds the newest g term
-        // chunks of the step's operands: D column jn (k0..), g row i (k0..), L_I column jn (k0..).
-        // An entry written in the step the chunk is read meets a zero factor: L_O is
-        // zero beyond i-4 and LIT beyond jn-4.
-        auto fetch = [&](int st, f32x4 (&c)[12]) {
-            const int jc = min(max(st + 2 - i, 0), kB - 1);
-            const float* dp = &sm.DT[jc][k0];
-            const float* gp = &sm.Gs[i][k0];
-            const float* lp = &sm.LIT[jc][k0];
+        for (int e = 0; e < 16; ++e) {
+            lo[e] = (p.LO && k0 + e <= a - 4 && a < R) ? p.LO[(i0 + k0 + e) * p.ldlo + i0 + a] : 0.0f;
+            li[e] = (p.LI && k0 + e <= a - 4 && a < Cc) ? p.LI[(j0 + k0 + e) * p.ldli + j0 + a] : 0.0f;
+        }
+        // L_O[a-3][a] and L_I[a-3][a], added by quarter 0 with the newest D and g
+        const float lo3 = (p.LO && q == 0 && a >= 3 && a < R) ? p.LO[(i0 + a - 3) * p.ldlo + i0 + a] : 0.0f;
+        const float li3 = (p.LI && q == 0 && a >= 3 && a < Cc) ? p.LI[(j0 + a - 3) * p.ldli + j0 + a] : 0.0f;
+        // An entry written in the step the chunk is read meets a zero factor: L_O and
+        // L_I are zero beyond a - 4.
+        auto fetch = [&](int st, f32x4 (&c)[8]) {
+            const int xc = min(max(st + 2 - a, 0), kB - 1);
+            const float* dp = &sm.DT[xc][k0];
+            const float* gp = &sm.Gs[xc][k0];
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
                 c[h] = lds4(dp + 4 * h);
                 c[4 + h] = lds4(gp + 4 * h);
-                c[8 + h] = lds4(lp + 4 * h);
             }
         };
         int slot3 = 2;  // (st + 2) mod 3
-        auto step = [&](int st, const f32x4 (&cur)[12], f32x4 (&nxt)[12]) {
-            const int jn = st + 2 - i;
-            const bool live = jn >= 0 && jn < kB;
-            const int jc = min(max(jn, 0), kB - 1);
+        auto step = [&](int st, const f32x4 (&cur)[8], f32x4 (&nxt)[8]) {
+            const int x = st + 2 - a;
+            const bool live = x >= 0 && x < kB;
+            const int xc = min(max(x, 0), kB - 1);
             // the newest terms, read behind the chunks fetched in the previous step
-            const float dnew = sm.DT[jc][max(i - 3, 0)];             // D[i-3][jn]
-            const float gnew = sm.Gs[i][min(max(jn - 3, 0), kB - 1)];  // g[i][jn-3]
-            const float lnew = sm.li3[jc];                            // L_I[jn-3][jn]
-            float p0 = lo3 * dnew, p1 = 0.0f, r0 = gq * gnew * lnew, r1 = 0.0f;
+            const int a3 = max(a - 3, 0);
+            const float dnew = sm.DT[xc][a3];  // D[a-3][x]
+            const float gnew = sm.Gs[xc][a3];  // g[x][a-3]
+            float p0 = lo3 * dnew, p1 = 0.0f, r0 = li3 * gnew, r1 = 0.0f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 p0 = fmaf(lo[e], cur[0][e], p0);
                 p1 = fmaf(lo[4 + e], cur[1][e], p1);
-                r0 = fmaf(cur[4][e], cur[8][e], r0);
-                r1 = fmaf(cur[5][e], cur[9][e], r1);
+                r0 = fmaf(li[e], cur[4][e], r0);
+                r1 = fmaf(li[4 + e], cur[5][e], r1);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 p0 = fmaf(lo[8 + e], cur[2][e], p0);
                 p1 = fmaf(lo[12 + e], cur[3][e], p1);
-                r0 = fmaf(cur[6][e], cur[10][e], r0);
-                r1 = fmaf(cur[7][e], cur[11][e], r1);
+                r0 = fmaf(li[8 + e], cur[6][e], r0);
+                r1 = fmaf(li[12 + e], cur[7][e], r1);
             }
             float pn = live ? p0 + p1 : 0.0f;
             float rn = live ? r0 + r1 : 0.0f;
             pn = quad_sum(pn);
             rn = quad_sum(rn);
             if (q == 0 && live) {
-                sm.pnb[slot3][i] = pn;
-                sm.rnb[slot3][i] = rn;
+                sm.pnb[slot3][a] = pn;  // entry (a, x)
+                sm.rnb[slot3][x] = rn;  // entry (x, a)
             }
             slot3 = slot3 == 2 ? 0 : slot3 + 1;
             // the next step's chunks go out after the stores and stay in flight across
@@ -432,7 +429,7 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
             __builtin_amdgcn_sched_barrier(0);
             barrier_no_wait();
         };
-        f32x4 ca[12], cb[12];
+        f32x4 ca[8], cb[8];
         __syncthreads();
         fetch(0, ca);
         int st = 0;
