@@ -14,6 +14,10 @@
 // round (or all tiles, when there are fewer than P) are split over K into
 // partials that a second kernel adds in a fixed order, so the result does not
 // depend on scheduling.
+//
+// Whole 128x128 tiles stream their 32-deep k-slices straight from global memory
+// into LDS (direct-to-LDS loads, one slice ahead); ragged tiles go through
+// registers with zero fill.
 #include <algorithm>
 
 #include "bk_common.hpp"
@@ -22,7 +26,11 @@
 namespace bk {
 
 constexpr int kT128 = 128;
-constexpr int kSyKT = 32;
+constexpr int kSyKT = 32;   // k-slice depth of the register-staged path (ragged tiles)
+constexpr int kRingKT = 32; // k-slice depth of the direct-to-LDS ring (whole 128x128 tiles)
+constexpr int kRingNS = 2;  // slices in the ring: loads run kRingNS - 1 slices ahead
+                            // (measured against 16 x 3, 16 x 4, 24 x 2, 40 x 2 and the deeper
+                            // one-workgroup-per-CU rings; 32 x 2 keeps two workgroups per CU)
 
 // k-slices stored as loaded ([k][column]): 16-byte stores of consecutive columns
 // and, for each MFMA, 32 consecutive columns of one k-row per half-wave, both
@@ -30,6 +38,18 @@ constexpr int kSyKT = 32;
 struct SyrkSmem {
     float a[2][kSyKT][kT128];
     float b[2][kSyKT][kT128];
+};
+
+// Whole tiles: a ring of kRingNS slices, each filled by direct global-to-LDS loads
+// (global_load_lds_dwordx4: a wave's 64 lanes write two consecutive 128-float rows).
+struct SyrkRing {
+    float a[kRingNS][kRingKT][kT128];
+    float b[kRingNS][kRingKT][kT128];
+};
+
+union SyrkShared {
+    SyrkSmem staged;
+    SyrkRing ring;
 };
 
 // tile id -> (bi, bj), bi <= bj, row-major over the upper triangle of nb x nb tiles
@@ -44,11 +64,7 @@ __device__ __forceinline__ void upper_tile(int64_t id, int64_t nb, int64_t& bi, 
 }
 
 // Thread t loads rows k0 + (t >> 5) + 8 h (h = 0..3), columns 4 (t & 31)..+3
-// of the 128 columns starting at X + c0; zeros outside [0, K) x [0, ncol).
-// kFull: the tile is 128 columns wide and 16-byte aligned, so each row is one
-// vector load (rows past K are clamped to K - 1 here and zeroed by the store,
-// which keeps the loads in flight).
-template <bool kFull>
+// of the ncol columns starting at X + c0; zeros outside [0, K) x [0, ncol).
 __device__ __forceinline__ void syrk_load(const float* __restrict__ X, int64_t ldx, int ncol,
                                           int64_t K, int64_t k0, f32x4 (&v)[4]) {
     const int t = threadIdx.x;
@@ -56,13 +72,9 @@ __device__ __forceinline__ void syrk_load(const float* __restrict__ X, int64_t l
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
         const int64_t k = k0 + (t >> 5) + 8 * h;
-        if (kFull) {
-            v[h] = *reinterpret_cast<const f32x4*>(X + min(k, K - 1) * ldx + c4);
-        } else {
-            const float* p = X + k * ldx + c4;
+        const float* p = X + k * ldx + c4;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[h][e] = (k < K && c4 + e < ncol) ? p[e] : 0.0f;
-        }
+        for (int e = 0; e < 4; ++e) v[h][e] = (k < K && c4 + e < ncol) ? p[e] : 0.0f;
     }
 }
 
@@ -80,7 +92,8 @@ __device__ __forceinline__ void syrk_store(float (&dst)[kSyKT][kT128], const f32
 
 // The MFMAs of one 32-deep slice: wave quadrant rows wr.., columns wc..; the
 // operands of k-step s + 1 are read from LDS before the MFMAs of step s issue.
-__device__ __forceinline__ void syrk_slice(const float (&a)[kSyKT][kT128], const float (&b)[kSyKT][kT128],
+template <int KT>
+__device__ __forceinline__ void syrk_slice(const float (&a)[KT][kT128], const float (&b)[KT][kT128],
                                            int wr, int wc, f32x16 (&acc)[2][2]) {
     const int lane = threadIdx.x & 63;
     const int kh = lane >> 5, l31 = lane & 31;
@@ -91,9 +104,9 @@ __device__ __forceinline__ void syrk_slice(const float (&a)[kSyKT][kT128], const
         fb[0][h] = b[kh][wc + 32 * h + l31];
     }
 #pragma unroll
-    for (int s = 0; s < kSyKT / 2; ++s) {
+    for (int s = 0; s < KT / 2; ++s) {
         const int cur = s & 1;
-        if (s + 1 < kSyKT / 2) {
+        if (s + 1 < KT / 2) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 fa[cur ^ 1][h] = a[2 * (s + 1) + kh][wr + 32 * h + l31];
@@ -110,18 +123,17 @@ __device__ __forceinline__ void syrk_slice(const float (&a)[kSyKT][kT128], const
 }
 
 // acc[rb][cb] (32x32 blocks of this wave's 64x64 quadrant) += sum_{k in [kb, ke)}
-// X[k][r0 + r] X[k][c0 + c]; the next slice is loaded into registers while the
-// current one feeds the MFMAs.
-template <bool kFull>
-__device__ __forceinline__ void syrk_tile_impl(const float* __restrict__ A, const float* __restrict__ B,
+// X[k][r0 + r] X[k][c0 + c] for a ragged tile; the next slice is loaded into
+// registers while the current one feeds the MFMAs.
+__device__ __forceinline__ void syrk_tile_staged(const float* __restrict__ A, const float* __restrict__ B,
                                                int64_t ldx, int R, int Cn, int64_t kb, int64_t ke,
                                                f32x16 (&acc)[2][2], SyrkSmem& sm) {
     const int w = threadIdx.x >> 6;
     const int wr = (w >> 1) * 64, wc = (w & 1) * 64;
     const int64_t nk = (ke - kb + kSyKT - 1) / kSyKT;
     f32x4 va[4], vb[4];
-    syrk_load<kFull>(A, ldx, R, ke, kb, va);
-    syrk_load<kFull>(B, ldx, Cn, ke, kb, vb);
+    syrk_load(A, ldx, R, ke, kb, va);
+    syrk_load(B, ldx, Cn, ke, kb, vb);
     syrk_store(sm.a[0], va, ke, kb);
     syrk_store(sm.b[0], vb, ke, kb);
     __syncthreads();
@@ -130,10 +142,10 @@ __device__ __forceinline__ void syrk_tile_impl(const float* __restrict__ A, cons
         const bool more = it + 1 < nk;
         if (more) {
             const int64_t k0 = kb + (it + 1) * kSyKT;
-            syrk_load<kFull>(A, ldx, R, ke, k0, va);
-            syrk_load<kFull>(B, ldx, Cn, ke, k0, vb);
+            syrk_load(A, ldx, R, ke, k0, va);
+            syrk_load(B, ldx, Cn, ke, k0, vb);
         }
-        syrk_slice(sm.a[cur], sm.b[cur], wr, wc, acc);
+        syrk_slice<kSyKT>(sm.a[cur], sm.b[cur], wr, wc, acc);
         if (more) {
             syrk_store(sm.a[cur ^ 1], va, ke, kb + (it + 1) * kSyKT);
             syrk_store(sm.b[cur ^ 1], vb, ke, kb + (it + 1) * kSyKT);
@@ -142,16 +154,83 @@ __device__ __forceinline__ void syrk_tile_impl(const float* __restrict__ A, cons
     }
 }
 
+// Wait until at most N of this wave's vector-memory operations are outstanding, then
+// meet the other waves. Direct-to-LDS loads complete in issue order with the wave's
+// other vector loads, so with N = the loads issued after slice s, slice s is in LDS
+// once every wave has passed. No compiler fence is involved: the ring's later loads
+// stay in flight across the barrier.
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// The whole-tile case (128 x 128, 16-byte aligned rows): slice s of the K-range goes to
+// ring slot s mod kRingNS; at the top of slice s the loads of slice s + kRingNS - 1 go
+// out into the slot every wave finished reading in slice s - 1. A K-range that is not
+// a whole number of slices ends with one register-staged, zero-filled slice.
+__device__ __forceinline__ void syrk_tile_ring(const float* __restrict__ A, const float* __restrict__ B,
+                                               int64_t ldx, int64_t kb, int64_t ke,
+                                               f32x16 (&acc)[2][2], SyrkRing& sm) {
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = (w >> 1) * 64, wc = (w & 1) * 64;
+    const int c4 = (lane & 31) << 2;
+    constexpr int kLoads = 2 * (kRingKT / 8);  // direct loads per wave per slice
+    const int64_t nf = (ke - kb) / kRingKT;    // whole slices
+    auto issue = [&](int64_t s) {
+        const int slot = (int)(s % kRingNS);
+        const int64_t k0 = kb + s * kRingKT;
+#pragma unroll
+        for (int h = 0; h < kRingKT / 8; ++h) {
+            const int r = 2 * w + 8 * h;  // this wave's two rows
+            const int64_t k = k0 + r + (lane >> 5);
+            __builtin_amdgcn_global_load_lds(A + k * ldx + c4, &sm.a[slot][r][0], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(B + k * ldx + c4, &sm.b[slot][r][0], 16, 0, 0);
+        }
+    };
+    for (int s = 0; s < kRingNS - 1; ++s)
+        if (s < nf) issue(s);
+    for (int64_t it = 0; it < nf; ++it) {
+        if (it + kRingNS - 2 < nf) vm_wait_barrier<(kRingNS - 2) * kLoads>();
+        else vm_wait_barrier<0>();
+        if (it + kRingNS - 1 < nf) issue(it + kRingNS - 1);
+        const int slot = (int)(it % kRingNS);
+        syrk_slice<kRingKT>(sm.a[slot], sm.b[slot], wr, wc, acc);
+    }
+    const int64_t kt = kb + nf * kRingKT;
+    if (kt < ke) {
+        __syncthreads();  // every wave is done with the ring
+        const int t = threadIdx.x;
+        f32x4 va[kRingKT / 8], vb[kRingKT / 8];
+#pragma unroll
+        for (int h = 0; h < kRingKT / 8; ++h) {
+            const int64_t k = kt + (t >> 5) + 8 * h;
+            const int64_t kc = min(k, ke - 1);
+            va[h] = *reinterpret_cast<const f32x4*>(A + kc * ldx + c4);
+            vb[h] = *reinterpret_cast<const f32x4*>(B + kc * ldx + c4);
+        }
+#pragma unroll
+        for (int h = 0; h < kRingKT / 8; ++h) {
+            const int r = (t >> 5) + 8 * h;
+            const bool in = kt + r < ke;
+            *reinterpret_cast<f32x4*>(&sm.a[0][r][c4]) = in ? va[h] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            *reinterpret_cast<f32x4*>(&sm.b[0][r][c4]) = in ? vb[h] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        __syncthreads();
+        syrk_slice<kRingKT>(sm.a[0], sm.b[0], wr, wc, acc);
+    }
+}
+
 __device__ __forceinline__ void syrk_tile(const float* __restrict__ X, int64_t ldx, int64_t r0,
                                           int R, int64_t c0, int Cn, int64_t kb, int64_t ke,
-                                          f32x16 (&acc)[2][2], SyrkSmem& sm) {
+                                          f32x16 (&acc)[2][2], SyrkShared& sm) {
     if (ke <= kb) return;
     const float* A = X + r0;
     const float* B = X + c0;
     const bool full = R == kT128 && Cn == kT128 && (ldx & 3) == 0 &&
                       ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
-    if (full) syrk_tile_impl<true>(A, B, ldx, R, Cn, kb, ke, acc, sm);
-    else syrk_tile_impl<false>(A, B, ldx, R, Cn, kb, ke, acc, sm);
+    if (full) syrk_tile_ring(A, B, ldx, kb, ke, acc, sm.ring);
+    else syrk_tile_staged(A, B, ldx, R, Cn, kb, ke, acc, sm.staged);
 }
 
 // row / column inside the 128x128 tile of element v of block (rb, cb)
@@ -193,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void k_syrk_full(const float* __restrict_
                                                         int64_t d, int64_t ldx, float alpha,
                                                         float beta, float* __restrict__ H,
                                                         int64_t ldh, int64_t nb, int64_t tile_beg) {
-    __shared__ SyrkSmem sm;
+    __shared__ SyrkShared sm;
     int64_t bi, bj;
     upper_tile(tile_beg + blockIdx.x, nb, bi, bj);
     const int R = (int)min<int64_t>(kT128, d - bi * kT128);
@@ -215,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void k_syrk_split(const float* __restrict
                                                          int64_t d, int64_t ldx, int64_t nb,
                                                          int64_t tile_beg, int nsplit,
                                                          float* __restrict__ part) {
-    __shared__ SyrkSmem sm;
+    __shared__ SyrkShared sm;
     const int u = blockIdx.x / nsplit, sp = blockIdx.x % nsplit;
     int64_t bi, bj;
     upper_tile(tile_beg + u, nb, bi, bj);
@@ -281,7 +360,7 @@ int resident_slots() {
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             cus <= 0)
             cus = 256;
-        slots = 2 * cus;  // two 74 KB-LDS workgroups per CU
+        slots = 2 * cus;  // two 64 KB-LDS workgroups per CU
     }
     return slots;
 }

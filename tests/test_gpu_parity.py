@@ -142,6 +142,25 @@ def test_hessian_accum_chunks_and_strides(bk):
     assert np.all(np.abs(H.cpu().numpy() - ref) <= bound)
 
 
+@pytest.mark.parametrize("off", [4, 1])
+def test_hessian_accum_strided_whole_tiles(bk, off):
+    # a 256-column view of a wider buffer: at a 16-byte offset the whole 128x128 tiles
+    # stream their k-slices straight into LDS; at a 4-byte offset they take the
+    # register path. T is odd, so the last k-slice is partial either way.
+    note("hessian strided whole tiles, column offset %d" % off)
+    T, d = 4133, 256
+    x = workloads.make_x(T, d, 17 + off, "gauss", 2)
+    big = np.zeros((T, d + 8), dtype=np.float32)
+    big[:, off:off + d] = x
+    Xb = torch.from_numpy(big).to(dev())
+    H = bk.hessian_accum(Xb[:, off:off + d]).cpu().numpy()
+    assert np.array_equal(H, H.T)
+    ref = oracle.hessian(x)
+    ax = np.abs(x.astype(np.float64))
+    bound = 4 * U32 * np.sqrt(T) * (ax.T @ ax) / T
+    assert np.all(np.abs(H - ref) <= bound), np.max(np.abs(H - ref) / bound)
+
+
 # ----------------------------------------------------------------------------
 # damped LDL
 # ----------------------------------------------------------------------------
