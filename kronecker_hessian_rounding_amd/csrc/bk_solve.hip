@@ -192,8 +192,8 @@ struct LeafSmem {
     float li2[kB];
     uint8_t code[kB][kB + 4];
     float DI[kB];
-    double red[kLeafThreads];
-    int red_i[kLeafThreads];
+    double red[kLeafThreads / 64];
+    int red_i[kLeafThreads / 64];
 };
 
 // acc += X^T Y over k = 0..63 for the 64x64 tile, X[k][r] at x[k * sx + r] and
@@ -287,45 +287,78 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
     __syncthreads();
 
     // ---- B: far fields from diagonals d-2 and earlier: the K-chunk partials
-    // summed in chunk order (all loads issued first; absent chunks read a
-    // valid address and are replaced by zero)
-    for (int g4 = t; g4 < kB * kB / 4; g4 += kLeafThreads) {
-        const int e = 4 * g4;
-        if (!far_p && !far_o) {  // uniform: nothing to read
-            const int r = e / kB, c0 = e % kB;
+    // summed in chunk order (every load issued first; absent chunks read a valid
+    // address and are replaced by zero). D, g and the codes are cleared while the
+    // loads are in flight (the staging in DT and Gs is consumed).
+    {
+        constexpr int kG = (kB * kB / 4 + kLeafThreads - 1) / kLeafThreads;
+        const bool any = far_p || far_o;
+        f32x4 xp[kG][kNch], xo[kG][kNch];
+        if (any) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                sm.pin[r][c0 + k] = 0.0f;
-                sm.base[c0 + k][r] = 0.0f;
-            }
-            continue;
-        }
-        f32x4 xp[kNch], xo[kNch];
+            for (int u = 0; u < 2; ++u) {
+                const int g = min(t + u * kLeafThreads, kB * kB / 4 - 1);
 #pragma unroll
-        for (int c = 0; c < kNch; ++c) {
-            const int cc = min(c, nch - 1);
-            xp[c] = *reinterpret_cast<const f32x4*>(part_ptr(p, par, slot, 0, cc) + e);
-            xo[c] = *reinterpret_cast<const f32x4*>(part_ptr(p, par, slot, 1, cc) + e);
-        }
-        f32x4 pv = {0.f, 0.f, 0.f, 0.f}, ov = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < kNch; ++c) {
-            const bool up = far_p && c < nch, uo = far_o && c < nch;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                pv[k] += up ? xp[c][k] : 0.0f;
-                ov[k] += uo ? xo[c][k] : 0.0f;
+                for (int c = 0; c < kNch; ++c) {
+                    const int cc = min(c, nch - 1);
+                    xp[u][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, par, slot, 0, cc) + 4 * g);
+                    xo[u][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, par, slot, 1, cc) + 4 * g);
+                }
             }
         }
-        const int r = e / kB, c0 = e % kB;  // p: row r, cols c0..c0+3; o^T: row (= leaf col) r, leaf rows c0..
+        const f32x4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (any) {
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            sm.pin[r][c0 + k] = pv[k];
-            sm.base[c0 + k][r] = ov[k];
+        for (int u = 0; u < kG; ++u) {
+            const int g = t + u * kLeafThreads;
+            if (g < kB * kB / 4) {
+                const int k = g >> 4, c4 = (g & 15) << 2;
+                *reinterpret_cast<f32x4*>(&sm.DT[k][c4]) = z4;
+                *reinterpret_cast<f32x4*>(&sm.Gs[k][c4]) = z4;
+                *reinterpret_cast<uint32_t*>(&sm.code[k][c4]) = 0u;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kG; ++u) {
+            if (u == 2 && any) {
+#pragma unroll
+                for (int uu = 2; uu < kG; ++uu) {
+                    const int gg = min(t + uu * kLeafThreads, kB * kB / 4 - 1);
+#pragma unroll
+                    for (int c = 0; c < kNch; ++c) {
+                        const int cc = min(c, nch - 1);
+                        xp[uu][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, par, slot, 0, cc) + 4 * gg);
+                        xo[uu][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, par, slot, 1, cc) + 4 * gg);
+                    }
+                }
+            }
+            const int g = t + u * kLeafThreads;
+            if (g >= kB * kB / 4) continue;
+            f32x4 pv = z4, ov = z4;
+            if (any) {
+#pragma unroll
+                for (int c = 0; c < kNch; ++c) {
+                    const bool up = far_p && c < nch, uo = far_o && c < nch;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        pv[k] += up ? xp[u][c][k] : 0.0f;
+                        ov[k] += uo ? xo[u][c][k] : 0.0f;
+                    }
+                }
+            }
+            const int e = 4 * g;
+            const int r = e / kB, c0 = e % kB;  // p: row r, cols c0..c0+3; o^T: row (= leaf col) r, leaf rows c0..
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                sm.pin[r][c0 + k] = pv[k];
+                sm.base[c0 + k][r] = ov[k];
+            }
         }
     }
     __syncthreads();
-    // ---- C: then the adjacent products, then W*; clear D, g and the codes
+    // ---- C: then the adjacent products, then W*
     if (w < 4) {
         const int cc = acc32_col();
 #pragma unroll
@@ -338,9 +371,6 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
     for (int e = t; e < kB * kB; e += kLeafThreads) {
         const int i = e / kB, j = e % kB;
         sm.base[i][j] += sm.wst[i][j];
-        sm.DT[i][j] = 0.0f;
-        sm.Gs[i][j] = 0.0f;
-        sm.code[i][j] = 0;
     }
     if (t < kB) {
         sm.DI[t] = (p.want_loss && t < Cc) ? p.DI[j0 + t] : 0.0f;
@@ -521,40 +551,78 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
         }
     }
 
-    // ---- outputs ----
-    for (int e = t; e < kB * kB; e += kLeafThreads) {
-        const int ii = e / kB, jj = e % kB;
-        if (ii < R && jj < Cc) {
-            p.codes[(i0 + ii) * p.ldc + j0 + jj] = sm.code[ii][jj];
-            p.delta[(i0 + ii) * p.ldd + j0 + jj] = sm.DT[jj][ii];
+    // ---- outputs: codes and D along the leaf's rows, C^T along its columns; every LDS
+    // read of the thread first, then the stores (four columns per store where aligned)
+    {
+        constexpr int kG = (kB * kB / 4 + kLeafThreads - 1) / kLeafThreads;
+        const bool ovec = ((reinterpret_cast<uintptr_t>(p.delta) | reinterpret_cast<uintptr_t>(p.ct)) & 15) == 0 &&
+                          (reinterpret_cast<uintptr_t>(p.codes) & 3) == 0 && ((p.ldd | p.m | p.ldc) & 3) == 0;
+        uint32_t cv[kG];
+        f32x4 dv[kG], gv[kG];
+#pragma unroll
+        for (int u = 0; u < kG; ++u) {
+            const int g = min(t + u * kLeafThreads, kB * kB / 4 - 1);
+            const int r = g >> 4, c4 = (g & 15) << 2;
+            cv[u] = *reinterpret_cast<const uint32_t*>(&sm.code[r][c4]);  // code[r][c4..]
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dv[u][e] = sm.DT[c4 + e][r];  // D[r][c4 + e]
+                gv[u][e] = sm.Gs[c4 + e][r];  // C[c4 + e][r], row r of C^T
+            }
         }
-        const int ci = e % kB, cj = e / kB;  // C^T written along the leaf's rows
-        if (ci < R && cj < Cc) p.ct[(j0 + cj) * p.m + i0 + ci] = sm.Gs[ci][cj];
-    }
-    sm.red[t] = loss;
-    sm.red_i[t] = nclamp;
-    __syncthreads();
-    if (t < 64) {
-        double a = 0.0;
-        int b = 0;
-        for (int k = t; k < kLeafThreads; k += 64) {
-            a += sm.red[k];
-            b += sm.red_i[k];
+#pragma unroll
+        for (int u = 0; u < kG; ++u) {
+            const int g = t + u * kLeafThreads;
+            if (g >= kB * kB / 4) continue;
+            const int r = g >> 4, c4 = (g & 15) << 2;
+            if (r < R) {  // row i0 + r of the codes and of D, columns j0 + c4..
+                uint8_t* cp = p.codes + (i0 + r) * p.ldc + j0 + c4;
+                float* dp = p.delta + (i0 + r) * p.ldd + j0 + c4;
+                if (ovec && c4 + 3 < Cc) {
+                    *reinterpret_cast<uint32_t*>(cp) = cv[u];
+                    *reinterpret_cast<f32x4*>(dp) = dv[u];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (c4 + e < Cc) {
+                            cp[e] = (uint8_t)(cv[u] >> (8 * e));
+                            dp[e] = dv[u][e];
+                        }
+                }
+            }
+            if (r < Cc) {  // row j0 + r of C^T, columns i0 + c4..
+                float* gp = p.ct + (j0 + r) * p.m + i0 + c4;
+                if (ovec && c4 + 3 < R) {
+                    *reinterpret_cast<f32x4*>(gp) = gv[u];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (c4 + e < R) gp[e] = gv[u][e];
+                }
+            }
         }
-        sm.red[t] = a;
-        sm.red_i[t] = b;
     }
-    __syncthreads();
+    // the leaf's loss and clamp count: within each wave by shuffles, then over the waves
+#pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-        if (t < o) {
-            sm.red[t] += sm.red[t + o];
-            sm.red_i[t] += sm.red_i[t + o];
-        }
-        __syncthreads();
+        loss += __shfl_xor(loss, o);
+        nclamp += __shfl_xor(nclamp, o);
     }
+    if ((t & 63) == 0) {
+        sm.red[w] = loss;
+        sm.red_i[w] = nclamp;
+    }
+    __syncthreads();
     if (t == 0) {
-        p.leaf_loss[(size_t)I * p.N + J] = sm.red[0];
-        p.leaf_clamp[(size_t)I * p.N + J] = sm.red_i[0];
+        double lsum = 0.0;
+        int csum = 0;
+#pragma unroll
+        for (int k = 0; k < kLeafThreads / 64; ++k) {
+            lsum += sm.red[k];
+            csum += sm.red_i[k];
+        }
+        p.leaf_loss[(size_t)I * p.N + J] = lsum;
+        p.leaf_clamp[(size_t)I * p.N + J] = csum;
     }
 }
 
