@@ -170,11 +170,12 @@ __device__ __forceinline__ void far_body(const SolveParams& p, int d, int nch, i
 // from the lanes above by DPP, g[i][j-1] and g[i][j-2] from its own previous
 // steps, and the bulk sums and static inputs were read one step ahead.
 //
-// Bulk lanes are (row i, quarter q) with lane = 4 i + q; quarter q owns the
-// k / l range [16q, 16q + 16), read as four adjacent 16-byte words (68-float
-// rows spread a row group over the banks); a range without a useful term
-// reads a zero row instead, which keeps the LDS traffic near the triangular
-// work without a branch.
+// Bulk lanes are (a, quarter q) with lane = 4 a + q; quarter q owns the k / l
+// range [16q, 16q + 16). Lane a sums P along row a of L_O^T and R along column
+// a of L_I, both held in registers, against 16-float chunks of D and g read as
+// four adjacent 16-byte words (68-float rows spread a row group over the
+// banks); the factors are zero beyond the bulk's range, so no term needs a
+// per-step mask.
 // ---------------------------------------------------------------------------
 constexpr int kLeafThreads = 5 * 64;
 constexpr int kTs = 68;  // row stride of the k/l-indexed tiles
