@@ -26,7 +26,8 @@
  *     never allocates, frees or retains memory and keeps no state between
  *     calls. Calls on different streams may run concurrently.
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
- *     stream). Only bakron_ldl waits for its work to finish.
+ *     stream). Only bakron_ldl waits for its work to finish (bakron_ldl_async
+ *     does not).
  *   - Arguments are validated on the host before anything is enqueued; an
  *     invalid argument returns BAKRON_E_INVALID_ARG and enqueues nothing.
  *     A failed launch returns BAKRON_E_DEVICE. No C++ exception crosses the
@@ -119,6 +120,21 @@ int bakron_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, floa
 size_t bakron_ldl_workspace_bytes(int64_t d);
 int bakron_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, int64_t* bad_pivot,
                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The same factorisation, enqueued on `stream` without waiting (the damped LDL
+ * of YAQA section 4, as above). Independent factorisations, such as H_I and H_O
+ * of one layer, can then run side by side on two streams: each is a chain of
+ * small launches that leaves most of the GPU idle.
+ *   bad_pivot_dev: DEVICE int64 (required); when the stream reaches it, it holds
+ *      -1, or the index of the first pivot that was not positive and finite (H is
+ *      then unspecified). The return value reports only argument, workspace and
+ *      launch errors.
+ *   ws: as for bakron_ldl; it and H, D stay in use until the stream has passed
+ *      the call.
+ */
+int bakron_ldl_async(float* H, int64_t d, int64_t ldh, double damp_rel, float* D,
+                     int64_t* bad_pivot_dev, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * BaKron solve: round W* (m x n) under H_O (x) H_I given the strict upper LDL

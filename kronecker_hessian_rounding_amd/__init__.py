@@ -6,11 +6,12 @@ tensors for device memory and uses the current stream.
 
   hessian_accum(X)            H <- beta H + alpha X^T X            (fp32 MFMA)
   ldl(H, damp_rel)            H + lambda I = (L + I) D (L + I)^T   (fp64, L strictly upper)
+  ldl_pair(HA, HB, damp_rel)  two independent factorisations side by side on two streams
   solve(W, L_O, L_I, bits)    BaKron rounding: codes, scales, error, proxy loss
   quantize_layer(W, X, G, b)  the whole per-layer path
 """
 from ._binding import (  # noqa: F401
     BAKRON_E_DEVICE, BAKRON_E_INVALID_ARG, BAKRON_E_NOT_SPD, BAKRON_E_WORKSPACE, BAKRON_OK,
-    EXPORTS, LIB, LIB_PATH, BakronError, SolveResult, abi_version, hessian_accum, ldl,
+    EXPORTS, LIB, LIB_PATH, BakronError, SolveResult, abi_version, hessian_accum, ldl, ldl_pair,
     quantize_layer, release_workspace, solve,
 )

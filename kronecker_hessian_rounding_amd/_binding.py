@@ -56,6 +56,8 @@ def _load() -> ctypes.CDLL:
     lib.bakron_ldl_workspace_bytes.argtypes = [i64]
     lib.bakron_ldl.restype = ctypes.c_int
     lib.bakron_ldl.argtypes = [vp, i64, i64, ctypes.c_double, vp, ctypes.POINTER(i64), vp, sz, vp]
+    lib.bakron_ldl_async.restype = ctypes.c_int
+    lib.bakron_ldl_async.argtypes = [vp, i64, i64, ctypes.c_double, vp, vp, vp, sz, vp]
     lib.bakron_solve_workspace_bytes.restype = sz
     lib.bakron_solve_workspace_bytes.argtypes = [i64, i64]
     lib.bakron_solve.restype = ctypes.c_int
@@ -67,7 +69,7 @@ def _load() -> ctypes.CDLL:
 LIB = _load()
 
 EXPORTS = ("bakron_abi_version", "bakron_status_str", "bakron_hessian_accum_workspace_bytes",
-           "bakron_hessian_accum", "bakron_ldl_workspace_bytes", "bakron_ldl",
+           "bakron_hessian_accum", "bakron_ldl_workspace_bytes", "bakron_ldl", "bakron_ldl_async",
            "bakron_solve_workspace_bytes", "bakron_solve")
 
 
@@ -110,10 +112,10 @@ def _stream():
 _ws_cache: dict = {}
 
 
-def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+def _workspace(nbytes: int, device, slot: int = 0) -> Optional[torch.Tensor]:
     if nbytes == 0:
         return None
-    key = (str(device), "ws")
+    key = (str(device), "ws", slot)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -123,6 +125,19 @@ def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 
 def release_workspace():
     _ws_cache.clear()
+
+
+_aux_streams: dict = {}
+
+
+def _aux_stream(device) -> torch.cuda.Stream:
+    """A second stream per device (default priority) for work beside the current stream."""
+    key = str(device)
+    s = _aux_streams.get(key)
+    if s is None:
+        s = torch.cuda.Stream(device=device)
+        _aux_streams[key] = s
+    return s
 
 
 # --------------------------------------------------------------------------
@@ -169,6 +184,54 @@ def ldl(H: torch.Tensor, damp_rel: float = 0.01, D: Optional[torch.Tensor] = Non
         err.bad_pivot = int(bad.value)
         raise err
     return H, D
+
+
+def ldl_pair(HA: torch.Tensor, HB: torch.Tensor, damp_rel: float = 0.01,
+             DA: Optional[torch.Tensor] = None, DB: Optional[torch.Tensor] = None):
+    """Two independent damped LDL factorisations at once (H_I and H_O of one layer).
+
+    HA is factored on the current stream and HB on a second stream that starts after
+    the current stream's earlier work; the current stream then waits for it, and the
+    call waits for both to report their pivots. Returns ((HA, DA), (HB, DB)); raises
+    BakronError(status=BAKRON_E_NOT_SPD) with .bad_pivot and .which (0 for HA, 1 for HB).
+    """
+    mats = []
+    for H, D, name in ((HA, DA, "HA"), (HB, DB, "HB")):
+        ldh = _mat(H, name)
+        d = H.shape[0]
+        if H.shape[1] != d:
+            raise ValueError("%s must be square" % name)
+        if D is None:
+            D = torch.empty(d, dtype=torch.float32, device=H.device)
+        _vec(D, "D" + name[1], d)
+        mats.append((H, D, d, ldh))
+    dev = HA.device
+    cur = torch.cuda.current_stream(dev)
+    aux = _aux_stream(dev)
+    info = torch.full((2,), -1, dtype=torch.int64, device=dev)
+    start = torch.cuda.Event()
+    start.record(cur)
+    aux.wait_event(start)
+    status = []
+    for k, ((H, D, d, ldh), s) in enumerate(zip(mats, (cur, aux))):
+        nb = LIB.bakron_ldl_workspace_bytes(d)
+        ws = _workspace(nb, dev, slot=k)
+        status.append(LIB.bakron_ldl_async(_ptr(H), d, ldh, damp_rel, _ptr(D),
+                                           ctypes.c_void_p(info.data_ptr() + 8 * k), _ptr(ws), nb,
+                                           ctypes.c_void_p(s.cuda_stream)))
+    done = torch.cuda.Event()
+    done.record(aux)
+    cur.wait_event(done)
+    bad = info.cpu().tolist()  # waits for both factorisations
+    for k in range(2):
+        _check("bakron_ldl_async", status[k])
+        if bad[k] >= 0:
+            err = BakronError("bakron_ldl_async", BAKRON_E_NOT_SPD,
+                              LIB.bakron_status_str(BAKRON_E_NOT_SPD).decode())
+            err.bad_pivot = int(bad[k])
+            err.which = k
+            raise err
+    return (mats[0][0], mats[0][1]), (mats[1][0], mats[1][1])
 
 
 @dataclass
@@ -232,12 +295,13 @@ def quantize_layer(W: torch.Tensor, X: torch.Tensor, G: Optional[torch.Tensor], 
     if workspace is None:
         workspace = {}
     HI = hessian_accum(X, workspace.get("HI"))
-    HI, DI = ldl(HI, damp_rel, workspace.get("DI"))
     if G is not None:
         HO = hessian_accum(G, workspace.get("HO"))
-        HO, DO = ldl(HO, damp_rel, workspace.get("DO"))
+        # the two factorisations are independent: run them side by side
+        (HI, DI), (HO, DO) = ldl_pair(HI, HO, damp_rel, workspace.get("DI"), workspace.get("DO"))
         LO = HO
     else:
+        HI, DI = ldl(HI, damp_rel, workspace.get("DI"))
         LO, DO = None, None
     res = solve(W, LO, HI, bits, rounding, seed, D_O=DO, D_I=DI, want_delta=want_delta,
                 want_loss=want_loss, out=workspace.get("out"))

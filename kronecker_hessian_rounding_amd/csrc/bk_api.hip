@@ -52,6 +52,14 @@ int bakron_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, int6
     return bk::run_ldl(H, d, ldh, damp_rel, D, bad_pivot, ws, (hipStream_t)stream);
 }
 
+int bakron_ldl_async(float* H, int64_t d, int64_t ldh, double damp_rel, float* D,
+                     int64_t* bad_pivot_dev, void* ws, size_t ws_bytes, void* stream) {
+    if (!H || !bad_pivot_dev || d <= 0 || bad_ld(ldh, d)) return BAKRON_E_INVALID_ARG;
+    if (!(damp_rel >= 0.0) || !(damp_rel < INFINITY)) return BAKRON_E_INVALID_ARG;
+    if (!ws || ws_bytes < bk::ldl_workspace_bytes(d)) return BAKRON_E_WORKSPACE;
+    return bk::enqueue_ldl(H, d, ldh, damp_rel, D, ws, (hipStream_t)stream, bad_pivot_dev);
+}
+
 size_t bakron_solve_workspace_bytes(int64_t m, int64_t n) {
     if (m <= 0 || n <= 0) return 0;
     return bk::solve_workspace_bytes(m, n);

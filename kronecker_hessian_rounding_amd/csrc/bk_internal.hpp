@@ -20,6 +20,10 @@ int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, floa
 
 // --- LDL factorisation (bk_ldl.hip) ---
 size_t ldl_workspace_bytes(int64_t d);
+// Enqueues the whole factorisation on `stream` without waiting; with info_dev
+// (device int64) non-null, the status (-1 or the first failing pivot) lands there.
+int enqueue_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, void* ws,
+                hipStream_t stream, int64_t* info_dev);
 int run_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, int64_t* bad_pivot,
             void* ws, hipStream_t stream);
 

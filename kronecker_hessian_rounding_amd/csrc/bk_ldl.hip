@@ -496,8 +496,11 @@ __global__ __launch_bounds__(kThreads) void k_ldl_store(float* __restrict__ H, i
     }
 }
 
-int run_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, int64_t* bad_pivot,
-            void* ws, hipStream_t stream) {
+// status word out: -1, or the first failing pivot
+__global__ void k_ldl_info_out(LdlWs w, int64_t* out) { *out = *w.info; }
+
+int enqueue_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, void* ws,
+                hipStream_t stream, int64_t* info_dev) {
     LdlWs w = carve(ws, d);
     const int64_t nbt = (d + kTile - 1) / kTile;
     if (nbt > 65535) return BAKRON_E_INVALID_ARG;
@@ -537,7 +540,15 @@ int run_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, int64_t
     }
     hipLaunchKernelGGL(k_ldl_store, dim3((unsigned)nbt, (unsigned)nbt), dim3(kThreads), 0, stream,
                        H, d, ldh, D, w);
-    if (hipGetLastError() != hipSuccess) return BAKRON_E_DEVICE;
+    if (info_dev) hipLaunchKernelGGL(k_ldl_info_out, dim3(1), dim3(1), 0, stream, w, info_dev);
+    return hipGetLastError() == hipSuccess ? BAKRON_OK : BAKRON_E_DEVICE;
+}
+
+int run_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, int64_t* bad_pivot,
+            void* ws, hipStream_t stream) {
+    const int st = enqueue_ldl(H, d, ldh, damp_rel, D, ws, stream, nullptr);
+    if (st != BAKRON_OK) return st;
+    const LdlWs w = carve(ws, d);
     int64_t info = -1;
     if (hipMemcpyAsync(&info, w.info, sizeof(int64_t), hipMemcpyDeviceToHost, stream) !=
         hipSuccess)

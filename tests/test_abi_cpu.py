@@ -78,6 +78,18 @@ def test_ldl_rejects_bad_arguments(lib):
     assert f(FAKE, 100, 100, 0.01, None, None, FAKE, ws_need - 1, None) == 3
 
 
+def test_ldl_async_rejects_bad_arguments(lib):
+    f = lib.bakron_ldl_async
+    ws_need = lib.bakron_ldl_workspace_bytes(100)
+    assert f(FAKE, 100, 100, 0.01, None, None, FAKE, ws_need, None) == 1   # status pointer NULL
+    assert f(None, 100, 100, 0.01, None, FAKE, FAKE, ws_need, None) == 1   # H NULL
+    assert f(FAKE, 0, 100, 0.01, None, FAKE, FAKE, ws_need, None) == 1     # d <= 0
+    assert f(FAKE, 100, 99, 0.01, None, FAKE, FAKE, ws_need, None) == 1    # ldh < d
+    assert f(FAKE, 100, 100, -0.5, None, FAKE, FAKE, ws_need, None) == 1   # damping < 0
+    assert f(FAKE, 100, 100, 0.01, None, FAKE, None, ws_need, None) == 3   # no workspace
+    assert f(FAKE, 100, 100, 0.01, None, FAKE, FAKE, ws_need - 1, None) == 3
+
+
 def test_solve_rejects_bad_arguments(lib):
     import kronecker_hessian_rounding_amd._binding as b
     f = lib.bakron_solve

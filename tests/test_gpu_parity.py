@@ -199,6 +199,36 @@ def test_ldl_reports_first_bad_pivot(bk):
     assert ei.value.bad_pivot == 120
 
 
+def test_ldl_pair_matches_single_calls(bk):
+    # the two factorisations run side by side on two streams; each must equal the
+    # single-call result exactly (same kernels, same inputs)
+    note("ldl pair d=300 and d=700")
+    HA = oracle.hessian(workloads.make_x(700, 300, 21, "gauss", 2)).astype(np.float32)
+    HB = oracle.hessian(workloads.make_x(1500, 700, 22, "gauss", 2)).astype(np.float32)
+    ga, gb = torch.from_numpy(HA).to(dev()), torch.from_numpy(HB).to(dev())
+    (pa, da), (pb, db) = bk.ldl_pair(ga.clone(), gb.clone(), 0.01)
+    sa, ea = bk.ldl(ga.clone(), 0.01)
+    sb, eb = bk.ldl(gb.clone(), 0.01)
+    assert torch.equal(pa, sa) and torch.equal(da, ea)
+    assert torch.equal(pb, sb) and torch.equal(db, eb)
+
+
+@pytest.mark.parametrize("which", [0, 1])
+def test_ldl_pair_reports_which_failed(bk, which):
+    note("ldl pair not-SPD in matrix %d" % which)
+    good = oracle.hessian(workloads.make_x(300, 90, 5, "gauss", 2)).astype(np.float32)
+    bad = oracle.hessian(workloads.make_x(400, 130, 3, "gauss", 2)).astype(np.float32)
+    bad[120, 120] = -5.0
+    mats = [torch.from_numpy(good).to(dev()), torch.from_numpy(bad).to(dev())]
+    if which == 0:
+        mats.reverse()
+    with pytest.raises(bk.BakronError) as ei:
+        bk.ldl_pair(mats[0], mats[1], 0.01)
+    assert ei.value.status == bk.BAKRON_E_NOT_SPD
+    assert ei.value.which == which
+    assert ei.value.bad_pivot == 120
+
+
 # ----------------------------------------------------------------------------
 # the BaKron solve
 # ----------------------------------------------------------------------------
