@@ -158,7 +158,9 @@ int bakron_ldl_async(float* H, int64_t d, int64_t ldh, double damp_rel, float* D
  *          required and D_O [m] may be NULL only if L_O is NULL (D_O = 1).
  *   clamped_out: optional device int64 count of entries whose code was clamped.
  *   info:  optional device int32; 0, or i+1 for the first row i whose scale is
- *          not finite and positive (then the outputs are unspecified).
+ *          not finite and positive, or -1 if one of the solve's internal waits
+ *          between workgroups ran past its limit (10 s of wall clock); in both
+ *          cases the outputs are unspecified.
  *   ws:    device workspace of at least bakron_solve_workspace_bytes(m, n).
  */
 size_t bakron_solve_workspace_bytes(int64_t m, int64_t n);

@@ -44,8 +44,7 @@ struct GemmSmemF32 {
 // K are clamped here and zeroed by the store, which keeps the loads in flight).
 template <int KT, bool kFast>
 __device__ __forceinline__ void slice_load_f32(const float* __restrict__ A, int64_t lda, int R,
-                                               int64_t K, int64_t k0, f32x4 (&v)[KT / 16]) {
-    const int t = threadIdx.x;
+                                               int64_t K, int64_t k0, f32x4 (&v)[KT / 16], int t) {
     const int c4 = (t & 15) << 2;
 #pragma unroll
     for (int h = 0; h < KT / 16; ++h) {
@@ -63,8 +62,7 @@ __device__ __forceinline__ void slice_load_f32(const float* __restrict__ A, int6
 // stores a loaded slice; rows k0 + r >= K are written as zeros
 template <int KT>
 __device__ __forceinline__ void slice_store_f32(float (&dst)[KT][kTile], const f32x4 (&v)[KT / 16],
-                                                int64_t K, int64_t k0) {
-    const int t = threadIdx.x;
+                                                int64_t K, int64_t k0, int t) {
     const int c4 = (t & 15) << 2;
 #pragma unroll
     for (int h = 0; h < KT / 16; ++h) {
@@ -77,19 +75,19 @@ template <int KT, bool kFast>
 __device__ __forceinline__ void tile_gemm_f32_impl(const float* __restrict__ A, int64_t lda, int R,
                                                    const float* __restrict__ B, int64_t ldb, int Cn,
                                                    int64_t K, f32x16& acc, GemmSmemF32<KT>& sm,
-                                                   bool active) {
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+                                                   bool active, int tid) {
+    const int lane = tid & 63;
+    const int w = tid >> 6;
     const int ra = (w >> 1) * 32 + (lane & 31);
     const int rb = (w & 1) * 32 + (lane & 31);
     const int kh = lane >> 5;
     const int64_t nk = (K + KT - 1) / KT;
     f32x4 va[KT / 16], vb[KT / 16];
     if (active) {
-        slice_load_f32<KT, kFast>(A, lda, R, K, 0, va);
-        slice_load_f32<KT, kFast>(B, ldb, Cn, K, 0, vb);
-        slice_store_f32<KT>(sm.a[0], va, K, 0);
-        slice_store_f32<KT>(sm.b[0], vb, K, 0);
+        slice_load_f32<KT, kFast>(A, lda, R, K, 0, va, tid);
+        slice_load_f32<KT, kFast>(B, ldb, Cn, K, 0, vb, tid);
+        slice_store_f32<KT>(sm.a[0], va, K, 0, tid);
+        slice_store_f32<KT>(sm.b[0], vb, K, 0, tid);
     }
     __syncthreads();
     for (int64_t it = 0; it < nk; ++it) {
@@ -100,8 +98,8 @@ __device__ __forceinline__ void tile_gemm_f32_impl(const float* __restrict__ A, 
             continue;
         }
         if (more) {
-            slice_load_f32<KT, kFast>(A, lda, R, K, (it + 1) * KT, va);
-            slice_load_f32<KT, kFast>(B, ldb, Cn, K, (it + 1) * KT, vb);
+            slice_load_f32<KT, kFast>(A, lda, R, K, (it + 1) * KT, va, tid);
+            slice_load_f32<KT, kFast>(B, ldb, Cn, K, (it + 1) * KT, vb, tid);
         }
         float fa[3], fb[3];
         fa[0] = sm.a[cur][kh][ra];
@@ -118,8 +116,8 @@ __device__ __forceinline__ void tile_gemm_f32_impl(const float* __restrict__ A, 
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[s % 3], fb[s % 3], acc, 0, 0, 0);
         }
         if (more) {
-            slice_store_f32<KT>(sm.a[cur ^ 1], va, K, (it + 1) * KT);
-            slice_store_f32<KT>(sm.b[cur ^ 1], vb, K, (it + 1) * KT);
+            slice_store_f32<KT>(sm.a[cur ^ 1], va, K, (it + 1) * KT, tid);
+            slice_store_f32<KT>(sm.b[cur ^ 1], vb, K, (it + 1) * KT, tid);
         }
         __syncthreads();
     }
@@ -129,28 +127,30 @@ __device__ __forceinline__ void tile_gemm_f32_impl(const float* __restrict__ A, 
 // with r < R valid (others read as 0), B (k, c) at B[k*ldb + c] with c < Cn;
 // wave w owns the 32x32 quadrant (w / 2, w % 2). Threads 0..255 compute; with
 // active = false a thread (of a larger workgroup) only takes part in the
-// barriers. Every thread of the workgroup must call it.
+// barriers. Every thread of the workgroup must call it; tid is its thread
+// index (passed in so that a caller looping over tasks can keep the index
+// arithmetic inside the loop).
 template <int KT>
 __device__ __forceinline__ void tile_gemm_f32(const float* __restrict__ A, int64_t lda, int R,
                                               const float* __restrict__ B, int64_t ldb, int Cn,
                                               int64_t K, f32x16& acc, GemmSmemF32<KT>& sm,
-                                              bool active = true) {
+                                              bool active, int tid) {
     if (K <= 0) return;
     const bool fast = R == kTile && Cn == kTile && (lda & 3) == 0 && (ldb & 3) == 0 &&
                       ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
-    if (fast) tile_gemm_f32_impl<KT, true>(A, lda, R, B, ldb, Cn, K, acc, sm, active);
-    else tile_gemm_f32_impl<KT, false>(A, lda, R, B, ldb, Cn, K, acc, sm, active);
+    if (fast) tile_gemm_f32_impl<KT, true>(A, lda, R, B, ldb, Cn, K, acc, sm, active, tid);
+    else tile_gemm_f32_impl<KT, false>(A, lda, R, B, ldb, Cn, K, acc, sm, active, tid);
 }
 
 // Position (row, col) inside the 64x64 tile of element v (0..15) of this
 // lane's fp32 accumulator (32x32x2 output layout: col = lane % 32,
 // row = 8*(v/4) + 4*(lane/32) + v%4 within the wave's quadrant).
-__device__ __forceinline__ int acc32_row(int v) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+__device__ __forceinline__ int acc32_row(int v, int tid) {
+    const int lane = tid & 63, w = tid >> 6;
     return (w >> 1) * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
 }
-__device__ __forceinline__ int acc32_col() {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+__device__ __forceinline__ int acc32_col(int tid) {
+    const int lane = tid & 63, w = tid >> 6;
     return (w & 1) * 32 + (lane & 31);
 }
 

@@ -8,21 +8,28 @@
 //   t_ij = W*_ij + P_ij + sum_{l<j} C_il L_I[l,j].
 // Entry (i, j) depends on every (k, l) with k <= i, l <= j, so all entries of
 // one anti-diagonal are independent (BaKron Abstract, anti-diagonal
-// parallelism). The schedule here is a wavefront over 64x64 leaves: the leaves
-// of leaf-diagonal d = I + J are solved together, one workgroup each. For
-// leaf (I, J) with row block R_I and column block S_J the feedback splits into
-//   p  = sum_{I'<I} L_O[R_I', R_I]^T D[R_I', S_J]   (column far field)
-//   o  = sum_{J'<J} C[R_I, S_J'] L_I[S_J', S_J]      (row far field)
-// plus the in-leaf sums, which the leaf workgroup runs as a 127-step
-// anti-diagonal wavefront. The far fields are MFMA GEMMs. Their contributions
-// from blocks on leaf-diagonals d-2 and earlier (split over K into partials)
-// need only the leaves of d-2, so they are formed by extra workgroups of the
-// launch that solves the leaves of d-1, on the CUs those leaves leave free.
-// The two blocks adjacent to the leaf (on diagonal d-1, K = 64) are
-// multiplied by the leaf workgroup itself. The leaf adds the partials in chunk order and then the adjacent
-// products, so the result does not depend on scheduling. Total far-field work
-// is mn(m+n) flops, the O(mn(m+n)) of the BaKron Abstract; the wavefront takes
-// 2(m+n)/64 - 1 leaf launches, O(m+n).
+// parallelism). The work is cut into 64x64 leaves; leaf (I, J), with row block
+// R_I and column block S_J, sits on leaf-diagonal d = I + J. Its feedback
+//   p = sum_{I'<I} L_O[R_I', R_I]^T D[R_I', S_J]   (column far field)
+//   o = sum_{J'<J} C[R_I, S_J'] L_I[S_J', S_J]      (row far field)
+// is split by how far back the source block lies:
+//  * three or more blocks back: MFMA GEMMs over K, split into partials, run by
+//    other workgroups once those leaves are done (O(mn(m+n)) flops in all, the
+//    bound of the BaKron Abstract);
+//  * two blocks back: multiplied by the leaf's own workgroup before its sweep;
+//  * the adjacent block: handed over 16 columns (rows) at a time while the
+//    neighbour is still sweeping, and multiplied as it arrives.
+// The leaf then runs its in-leaf sums as a 127-step anti-diagonal wavefront.
+// Column x of a leaf's D and row x of its C are final 63 + x steps into that
+// sweep, so a leaf can start about 64 steps (plus the hand-over latency) after
+// its neighbours rather than a whole sweep after them.
+//
+// Everything runs in one persistent launch. Workgroups take tasks in a fixed
+// order: the leaves of diagonal k, then the far fields of diagonal k + 1. A
+// task waits only on tasks earlier in that order, so the earliest unfinished
+// task can always proceed. Progress counters in global memory carry the
+// hand-overs; every wait is bounded in time, and an expired wait stops the
+// solve and is reported.
 #include <limits.h>
 
 #include <algorithm>
@@ -32,10 +39,14 @@
 
 namespace bk {
 
-constexpr int kB = kTile;  // leaf edge
-constexpr int kNch = 4;    // maximum K-chunks per far-field product
-constexpr int kTargetWg = 1024;  // far-field workgroups aimed for per launch
+constexpr int kB = kTile;        // leaf edge
+constexpr int kNch = 4;          // maximum K-chunks per far-field product
+constexpr int kRing = 4;         // diagonals whose far-field partials are held at once
+constexpr int kTargetWg = 1024;  // far-field tasks aimed for per diagonal
 constexpr int kFarKT = 64;       // k-slice depth of the far-field GEMMs
+constexpr int kSweep = 2 * kB - 1;  // steps of one leaf's wavefront
+constexpr int kStrip = 16;       // columns (rows) per hand-over
+constexpr int kStrips = kB / kStrip;
 
 struct SolveParams {
     const float* W;
@@ -62,14 +73,93 @@ struct SolveParams {
     int want_loss;
     int* info;
     int maxleaf;
+    // schedule
+    int* ticket;     // next task to take
+    int* abort;      // set once a wait has expired
+    int* prog_d;     // per leaf: strips of D published (0..4)
+    int* prog_c;     // per leaf: strips of C published (0..4)
+    int* setup;      // per leaf: 1 once its far-field partials are consumed
+    int* fardone;    // per leaf: far-field tasks finished
+    int* seg;        // first task of each group k (ND + 1 entries)
+    int* nchd;       // K-chunks of the far-field products, per diagonal
+    int ND;          // leaf-diagonals
+    int ntask;
+    uint64_t spin_limit;  // wall-clock ticks a single wait may take
 };
 
-__device__ __forceinline__ int leaf_lo(const SolveParams& p, int d) { return max(0, d - (p.N - 1)); }
-__device__ __forceinline__ int leaf_hi(const SolveParams& p, int d) { return min(d, p.M - 1); }
+__host__ __device__ __forceinline__ int diag_lo(int N, int d) { return d - (N - 1) > 0 ? d - (N - 1) : 0; }
+__host__ __device__ __forceinline__ int diag_hi(int M, int d) { return d < M - 1 ? d : M - 1; }
+__host__ __device__ __forceinline__ int diag_leaves(int M, int N, int d) {
+    return diag_hi(M, d) - diag_lo(N, d) + 1;
+}
+// K-chunks per far-field product on diagonal d: enough tasks to fill the chip,
+// chunks of at least 4 blocks
+__host__ __device__ __forceinline__ int diag_nch(int M, int N, int d) {
+    const int lo = diag_lo(N, d), hi = diag_hi(M, d), nl = hi - lo + 1;
+    const int kmax = (hi > d - lo ? hi : d - lo) - 2;  // blocks three or more back
+    int nch = (kTargetWg + 2 * nl - 1) / (2 * nl);
+    const int cap = kmax / 4 > 1 ? kmax / 4 : 1;
+    nch = nch < cap ? nch : cap;
+    nch = nch < kNch ? nch : kNch;
+    return nch > 1 ? nch : 1;
+}
+// tasks of group k: the leaves of diagonal k, then the far fields of diagonal k + 1
+// (those exist from diagonal 3 on: they need blocks three or more back). A far
+// task reads leaves two or more groups back, so it rarely waits; the leaves of
+// its diagonal come right after it in the order.
+__host__ __device__ __forceinline__ int group_far(int ND, int k) { return (k + 1 >= 3 && k + 1 < ND) ? k + 1 : -1; }
+__host__ __device__ __forceinline__ int group_tasks(int M, int N, int ND, int k) {
+    int s = diag_leaves(M, N, k);
+    const int df = group_far(ND, k);
+    if (df >= 0) s += diag_leaves(M, N, df) * 2 * diag_nch(M, N, df);
+    return s;
+}
 
-// far-field partials: parity of the diagonal, leaf slot on it, kind (0: p, 1: o^T), K-chunk
-__device__ __forceinline__ float* part_ptr(const SolveParams& p, int par, int slot, int kind, int c) {
-    return p.parts + ((((size_t)par * p.maxleaf + slot) * 2 + kind) * kNch + c) * (kB * kB);
+__device__ __forceinline__ int leaf_lo(const SolveParams& p, int d) { return diag_lo(p.N, d); }
+
+// far-field partials: ring slot of the diagonal, leaf slot on it, kind (0: p, 1: o^T), K-chunk
+__device__ __forceinline__ float* part_ptr(const SolveParams& p, int d, int slot, int kind, int c) {
+    return p.parts + ((((size_t)(d % kRing) * p.maxleaf + slot) * 2 + kind) * kNch + c) * (kB * kB);
+}
+
+// ---------------------------------------------------------------------------
+// hand-over primitives. Each XCD has its own L2, so data passed between
+// workgroups is written with device-coherent (agent-scope) stores, which go
+// through to memory, and a producer raises its counter (also agent scope)
+// only once those stores have completed (s_waitcnt vmcnt(0)): no cache-wide
+// write-back is needed. A consumer that then reads through the caches first
+// invalidates them (acquire fence at agent scope); the hand-overs inside a
+// leaf's sweep read with device-coherent loads instead, so the sweep never
+// waits on cache maintenance.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int ld_flag(const int* f) {
+    return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_flag(int* f, int v) {
+    __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent(float* q, float v) {
+    __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+// keeps the compiler from moving the data loads above the counter check
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+// the wave's own memory operations, cache maintenance included, have completed
+__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Waits until *f >= v. Returns false if this wait ran past the time limit (it
+// then stops every other wait of the solve) or another one already did.
+__device__ __forceinline__ bool wait_flag(const SolveParams& p, const int* f, int v) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (;;) {
+        if (ld_flag(f) >= v) return true;
+        if (ld_flag(p.abort)) return false;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > p.spin_limit) {
+            st_flag(p.abort, 1);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -109,15 +199,38 @@ __global__ __launch_bounds__(kThreads) void k_scales(const float* __restrict__ W
     }
 }
 
-__global__ void k_solve_init(int* info) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) *info = INT_MAX;
+
+// Clears the schedule state and builds the task table (one thread walks the
+// diagonals; the counters are cleared by the whole grid).
+__global__ __launch_bounds__(kThreads) void k_solve_init(SolveParams p) {
+    const int64_t nl = (int64_t)p.M * p.N;
+    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < nl; e += (int64_t)gridDim.x * kThreads) {
+        p.prog_d[e] = 0;
+        p.prog_c[e] = 0;
+        p.setup[e] = 0;
+        p.fardone[e] = 0;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *p.info = INT_MAX;
+        *p.ticket = 0;
+        *p.abort = 0;
+        int s = 0;
+        for (int k = 0; k < p.ND; ++k) {
+            p.nchd[k] = diag_nch(p.M, p.N, k);
+            p.seg[k] = s;
+            s += group_tasks(p.M, p.N, p.ND, k);
+        }
+        p.seg[p.ND] = s;
+    }
 }
 
 // ---------------------------------------------------------------------------
 // far field of diagonal d: chunk c (of nch) of p (kind 0) or o^T (kind 1) of
-// one leaf, over the blocks above (p) or to the left (o) of the leaf except
-// the adjacent one, i.e. blocks on diagonals d-2 and earlier. Each chunk
-// writes its own 64x64 partial; the leaf adds the partials in chunk order.
+// one leaf, over the blocks three or more above (p) or to the left (o) of the
+// leaf. It starts once the last leaf of its K range has published all of its
+// D (C); the leaves before it in that column (row) finished earlier, since
+// each waited on its predecessor. Each chunk writes its own 64x64 partial (an
+// empty chunk writes zeros); the leaf adds them in chunk order.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void chunk_range(int kblk, int nch, int c, int& b0, int& b1) {
     const int len = (kblk + nch - 1) / nch;
@@ -125,40 +238,63 @@ __device__ __forceinline__ void chunk_range(int kblk, int nch, int c, int& b0, i
     b1 = min(b0 + len, kblk);
 }
 
-__device__ __forceinline__ void far_body(const SolveParams& p, int d, int nch, int task, GemmSmemF32<kFarKT>& sm) {
-    if (*p.info != INT_MAX) return;  // a row scale was invalid
+__device__ __forceinline__ void far_task(const SolveParams& p, int d, int task, GemmSmemF32<kFarKT>& sm,
+                                         int tid) {
+    const int nch = p.nchd[d];
     const int slot = task / (2 * nch);
     const int kind = (task / nch) & 1;
     const int c = task % nch;
     const int I = leaf_lo(p, d) + slot;
     const int J = d - I;
-    if ((kind == 0 && !p.LO) || (kind == 1 && !p.LI)) return;
-    const int kblk = (kind == 0 ? I : J) - 1;
-    if (kblk <= 0) return;
-    int kb0, kb1;
-    chunk_range(kblk, nch, c, kb0, kb1);  // an empty chunk writes a zero partial
-    const int64_t i0 = (int64_t)I * kB, j0 = (int64_t)J * kB;
-    const int R = (int)min<int64_t>(kB, p.m - i0), Cc = (int)min<int64_t>(kB, p.n - j0);
-    const int64_t k0 = (int64_t)kb0 * kB, K = (int64_t)(kb1 - kb0) * kB;
-    f32x16 acc;
+    const bool has = kind == 0 ? (p.LO != nullptr && I > 2) : (p.LI != nullptr && J > 2);
+    if (has) {
+        int kb0, kb1;
+        chunk_range((kind == 0 ? I : J) - 2, nch, c, kb0, kb1);
+        if (tid == 0) {
+            if (kb1 > kb0) {
+                if (kind == 0) wait_flag(p, &p.prog_d[(int64_t)(kb1 - 1) * p.N + J], kStrips);
+                else wait_flag(p, &p.prog_c[(int64_t)I * p.N + kb1 - 1], kStrips);
+            }
+            if (d >= kRing) {  // the leaf that last used this ring slot has read it
+                const int dp = d - kRing;
+                if (slot < diag_leaves(p.M, p.N, dp)) {
+                    const int Ip = leaf_lo(p, dp) + slot;
+                    wait_flag(p, &p.setup[(int64_t)Ip * p.N + (dp - Ip)], 1);
+                }
+            }
+            acquire_agent();
+            vm_wait_all();
+        }
+        __syncthreads();
+        const int64_t i0 = (int64_t)I * kB, j0 = (int64_t)J * kB;
+        const int R = (int)min<int64_t>(kB, p.m - i0), Cc = (int)min<int64_t>(kB, p.n - j0);
+        const int64_t k0 = (int64_t)kb0 * kB, K = (int64_t)(kb1 - kb0) * kB;
+        f32x16 acc;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-    const bool active = threadIdx.x < kThreads;  // the fifth wave only joins the barriers
-    if (kind == 0)  // p[ii][jj] = sum_k L_O[k][i0+ii] D[k][j0+jj]
-        tile_gemm_f32<kFarKT>(p.LO + k0 * p.ldlo + i0, p.ldlo, R, p.delta + k0 * p.ldd + j0, p.ldd, Cc,
-                        K, acc, sm, active);
-    else  // o^T[jj][ii] = sum_l L_I[l][j0+jj] C^T[l][i0+ii]
-        tile_gemm_f32<kFarKT>(p.LI + k0 * p.ldli + j0, p.ldli, Cc, p.ct + k0 * p.m + i0, p.m, R, K, acc,
-                        sm, active);
-    if (!active) return;
-    float* part = part_ptr(p, d & 1, slot, kind, c);
-    const int cc = acc32_col();
+        for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+        const bool active = tid < kThreads;  // the other waves only join the barriers
+        if (kind == 0)  // p[ii][jj] = sum_k L_O[k][i0+ii] D[k][j0+jj]
+            tile_gemm_f32<kFarKT>(p.LO + k0 * p.ldlo + i0, p.ldlo, R, p.delta + k0 * p.ldd + j0, p.ldd, Cc, K,
+                                  acc, sm, active, tid);
+        else  // o^T[jj][ii] = sum_l L_I[l][j0+jj] C^T[l][i0+ii]
+            tile_gemm_f32<kFarKT>(p.LI + k0 * p.ldli + j0, p.ldli, Cc, p.ct + k0 * p.m + i0, p.m, R, K, acc,
+                                  sm, active, tid);
+        if (active) {
+            float* part = part_ptr(p, d, slot, kind, c);
+            const int cc = acc32_col(tid);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) part[acc32_row(v) * kB + cc] = acc[v];
+            for (int v = 0; v < 16; ++v) st_coherent(&part[acc32_row(v, tid) * kB + cc], acc[v]);
+        }
+        vm_wait_all();  // every wave's device-coherent partial stores have completed
+        __syncthreads();
+    }
+    if (tid == 0) {
+        __hip_atomic_fetch_add(&p.fardone[(int64_t)I * p.N + J], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // ---------------------------------------------------------------------------
-// leaf solve: the 64x64 leaf (I, J) of diagonal d, given its far fields.
+// leaf solve: the 64x64 leaf (I, J) of diagonal d.
 //
 // Entry (i, j) is finalised at step i + j. Its in-leaf sums
 //   pn = sum_{k<i} L_O[k][i] D[k][j],   rn = sum_{l<j} g[i][l] L_I[l][j]
@@ -176,8 +312,22 @@ __device__ __forceinline__ void far_body(const SolveParams& p, int d, int nch, i
 // four adjacent 16-byte words (68-float rows spread a row group over the
 // banks); the factors are zero beyond the bulk's range, so no term needs a
 // per-step mask.
+//
+// Waves 5 and 6 do the hand-overs, column-wise (5: D to the leaf below, and
+// L_O[above, this]^T D[above, strip] into p) and row-wise (6: C to the leaf on
+// the right, and C[strip, left] L_I[left, this] into o). Strip c (columns or
+// rows 16c..16c+15) of this leaf is final after step 78 + 16c; it is stored a
+// step later and its counter raised four steps after that, when the stores
+// have landed. The neighbour's strip c (c >= 1) is taken in a window ending at
+// step 16c - 2: counter read at 16c - 12, checked (and waited for, if late)
+// at 16c - 9 and the strip loaded (device-coherent loads, which go to memory),
+// multiplied with v_mfma_f32_16x16x4_f32 over steps 16c - 5 .. 16c - 3 (the
+// loads have four steps to land) and added to p (o) before the finaliser reads
+// columns (rows) 16c.., at the end of step 16c - 1. Strip 0 is taken before
+// the sweep.
 // ---------------------------------------------------------------------------
-constexpr int kLeafThreads = 5 * 64;
+constexpr int kLeafWaves = 7;
+constexpr int kLeafThreads = kLeafWaves * 64;
 constexpr int kTs = 68;  // row stride of the k/l-indexed tiles
 constexpr int kPs = 66;  // row stride of the per-entry inputs: anti-diagonal walks hit distinct banks
 
@@ -193,15 +343,15 @@ struct LeafSmem {
     float li2[kB];
     uint8_t code[kB][kB + 4];
     float DI[kB];
-    double red[kLeafThreads / 64];
-    int red_i[kLeafThreads / 64];
+    double red[kLeafWaves];
+    int red_i[kLeafWaves];
 };
 
 // acc += X^T Y over k = 0..63 for the 64x64 tile, X[k][r] at x[k * sx + r] and
 // Y[k][c] at y[k * sy + c] in LDS; waves 0-3 each own a 32x32 quadrant
 // (32x32x2 f32 MFMA operand and output layout of bk_common.hpp).
-__device__ __forceinline__ void adj_gemm(const float* x, int sx, const float* y, int sy, f32x16& acc) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+__device__ __forceinline__ void adj_gemm(const float* x, int sx, const float* y, int sy, f32x16& acc, int tid) {
+    const int lane = tid & 63, w = tid >> 6;
     const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
 #pragma unroll
     for (int k = 0; k < kB; k += 2) {
@@ -226,39 +376,130 @@ __device__ __forceinline__ float lane_above(float x) {
 
 __device__ __forceinline__ f32x4 lds4(const float* q) { return *reinterpret_cast<const f32x4*>(q); }
 
-__device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, int slot, LeafSmem& sm) {
-    if (*p.info != INT_MAX) return;
+// ---- hand-overs (waves 5 and 6). Operand kk of lane l is row 4 kk + l / 16,
+// column l % 16 of the neighbour's strip: D[i0-64+k][j0+16c+x] (column-wise) or
+// C^T[j0-64+l][i0+16c+r] (row-wise). The product tile is 64 x 16 (16 x 64),
+// four 16x16 blocks; element q of block t sits at row 4 (l / 16) + q, column
+// l % 16 of the block (v_mfma_f32_16x16x4_f32 output layout).
+struct Handover {
+    float fa[64];  // the static factor block in operand order: element 4 kk + t is
+                   // row 4 kk + l / 16, column 16 t + l % 16 of L_O[above, this] (L_I[left, this])
+    float bv[16];
+    f32x4 acc[4];
+};
+
+__device__ __forceinline__ void handover_factor(const SolveParams& p, bool col, int64_t i0, int64_t j0, int R,
+                                                int Cc, Handover& h, int lane) {
+    const float* src = col ? p.LO + (i0 - kB) * p.ldlo + i0 : p.LI + (j0 - kB) * p.ldli + j0;
+    const int64_t ld = col ? p.ldlo : p.ldli;
+    const int lim = col ? R : Cc;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+        const int64_t k = 4 * kk + (lane >> 4);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int c = 16 * t + (lane & 15);
+            h.fa[4 * kk + t] = c < lim ? src[k * ld + c] : 0.0f;
+        }
+    }
+}
+
+__device__ __forceinline__ void handover_load(const SolveParams& p, bool col, int c, int64_t i0, int64_t j0,
+                                              int R, int Cc, Handover& h, int lane) {
+    const int s = kStrip * c + (lane & 15);
+    // a wave-uniform base and stride, and a 32-bit lane offset
+    const float* src = col ? p.delta + (i0 - kB) * p.ldd + j0 : p.ct + (j0 - kB) * p.m + i0;
+    const int64_t ld = col ? p.ldd : p.m;
+    const bool ok = s < (col ? Cc : R);
+    const int64_t off = (lane >> 4) * ld + s;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+        const float* row = src + (int64_t)(4 * kk) * ld;
+        h.bv[kk] = ok ? __hip_atomic_load(row + off, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) h.acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+template <int KK0, int KK1>
+__device__ __forceinline__ void handover_mma(bool col, Handover& h) {
+#pragma unroll
+    for (int kk = KK0; kk < KK1; ++kk) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (col)  // p[a][x] += sum_k L_O[above k][a] D[above k][x]
+                h.acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(h.fa[4 * kk + t], h.bv[kk], h.acc[t], 0, 0, 0);
+            else  // o[r][j] += sum_l C[r][left l] L_I[left l][j]
+                h.acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(h.bv[kk], h.fa[4 * kk + t], h.acc[t], 0, 0, 0);
+        }
+    }
+}
+
+__device__ __forceinline__ void handover_add(LeafSmem& sm, bool col, int c, const Handover& h, int lane) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = 4 * (lane >> 4) + q, cc = lane & 15;
+            if (col) sm.pin[16 * t + r][kStrip * c + cc] += h.acc[t][q];
+            else sm.base[kStrip * c + r][16 * t + cc] += h.acc[t][q];
+        }
+}
+
+// stores strip c of this leaf's D (column-wise) or C^T (row-wise), device-coherent
+__device__ __forceinline__ void handover_publish(const SolveParams& p, const LeafSmem& sm, bool col, int c,
+                                                 int64_t i0, int64_t j0, int R, int Cc, int lane) {
+    const int s = kStrip * c + (lane & 15);
+    float* dst = col ? p.delta + i0 * p.ldd + j0 : p.ct + j0 * p.m + i0;
+    const int64_t ld = col ? p.ldd : p.m;
+    const int klim = col ? R : Cc, slim = col ? Cc : R;
+    const int64_t off = (lane >> 4) * ld + s;
+    const float* rowp = col ? &sm.DT[s][0] : &sm.Gs[s][0];  // D[k][s] = DT[s][k]; C[s][k] = Gs[s][k]
+    float v[16];
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) v[kk] = rowp[4 * kk + (lane >> 4)];  // every read first
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+        const int k = 4 * kk + (lane >> 4);
+        if (k < klim && s < slim) st_coherent(dst + (int64_t)(4 * kk) * ld + off, v[kk]);
+    }
+}
+
+__device__ __forceinline__ void handover_flag(const SolveParams& p, bool col, int64_t leaf, int v, int lane) {
+    vm_wait_all();  // the strip's device-coherent stores have completed
+    if (lane == 0) st_flag(col ? &p.prog_d[leaf] : &p.prog_c[leaf], v);
+}
+
+__device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot, LeafSmem& sm, int tid) {
     const int I = leaf_lo(p, d) + slot;
     const int J = d - I;
     const int64_t i0 = (int64_t)I * kB, j0 = (int64_t)J * kB;
     const int R = (int)min<int64_t>(kB, p.m - i0), Cc = (int)min<int64_t>(kB, p.n - j0);
-    const int t = threadIdx.x;
-    const int w = t >> 6;
-    const int par = d & 1;
-    const bool far_p = p.LO && I > 1, far_o = p.LI && J > 1;  // all nch partials were written
-    const bool adj_p = p.LO && I > 0, adj_o = p.LI && J > 0;
-
+    const int t = tid;
+    const int lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int64_t leaf = (int64_t)I * p.N + J;
+    const int nch = p.nchd[d];
+    const bool far_p = p.LO && I > 2, far_o = p.LI && J > 2;  // far-field partials (blocks <= I-3, J-3)
+    const bool two_p = p.LO && I > 1, two_o = p.LI && J > 1;  // the blocks two back
+    const bool adj_p = p.LO && I > 0, adj_o = p.LI && J > 0;  // the adjacent blocks (handed over)
     if (t < 2) {  // no L_I[j-d][j] for j < d
         sm.li2[t] = 0.0f;
         if (t < 1) sm.li1[t] = 0.0f;
     }
-    // ---- A: every tile load of the thread in flight at once, then LDS
-    //   DT  <- L_O[i0-64+k][i0+c]   Gs   <- D[i0-64+k][j0+c]      (block above: staging)
-    //   pin <- L_I[j0-64+k][j0+c]   base <- C^T[j0-64+k][i0+c]    (block to the left: staging)
+    constexpr int kPer = (kB * kB + kLeafThreads - 1) / kLeafThreads;
+    // ---- A: static inputs, every load of the thread in flight at once
+    //   DT  <- L_O[i0-128+k][i0+c]  pin <- L_I[j0-128+k][j0+c]   (blocks two back: staging)
     //   wst <- W*[i0+k][j0+c]       li1, li2 <- the first two superdiagonals of L_I
     {
-        constexpr int kPer = (kB * kB + kLeafThreads - 1) / kLeafThreads;
-        float v1[kPer], v2[kPer], v3[kPer], v4[kPer], v5[kPer], v6[kPer];
+        float v1[kPer], v3[kPer], v5[kPer], v6[kPer];
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
             const int e = t + u * kLeafThreads;
             const int k = e >> 6, c = e & 63;
             const bool in = e < kB * kB;
-            const int64_t ik = i0 - kB + k, jk = j0 - kB + k;
-            v1[u] = (in && adj_p && c < R) ? p.LO[ik * p.ldlo + i0 + c] : 0.0f;
-            v2[u] = (in && adj_p && c < Cc) ? p.delta[ik * p.ldd + j0 + c] : 0.0f;
-            v3[u] = (in && adj_o && c < Cc) ? p.LI[jk * p.ldli + j0 + c] : 0.0f;
-            v4[u] = (in && adj_o && c < R) ? p.ct[jk * p.m + i0 + c] : 0.0f;
+            v1[u] = (in && two_p && c < R) ? p.LO[(i0 - 2 * kB + k) * p.ldlo + i0 + c] : 0.0f;
+            v3[u] = (in && two_o && c < Cc) ? p.LI[(j0 - 2 * kB + k) * p.ldli + j0 + c] : 0.0f;
             v5[u] = (in && k < R && c < Cc) ? p.W[(i0 + k) * p.ldw + j0 + c] : 0.0f;
             v6[u] = (in && p.LI && (c - k == 1 || c - k == 2) && c < Cc) ? p.LI[(j0 + k) * p.ldli + j0 + c] : 0.0f;
         }
@@ -268,31 +509,26 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
             if (e < kB * kB) {
                 const int k = e >> 6, c = e & 63;
                 sm.DT[k][c] = v1[u];
-                sm.Gs[k][c] = v2[u];
                 sm.pin[k][c] = v3[u];
-                sm.base[k][c] = v4[u];
                 sm.wst[k][c] = v5[u];
                 if (c - k == 1) sm.li1[c] = v6[u];
                 if (c - k == 2) sm.li2[c] = v6[u];
             }
         }
     }
-    __syncthreads();
-    f32x16 ap, ao;  // adjacent products (K = 64): p += L_O^T D, o^T += L_I^T C^T
-#pragma unroll
-    for (int v = 0; v < 16; ++v) ap[v] = ao[v] = 0.0f;
-    if (w < 4) {
-        if (adj_p) adj_gemm(&sm.DT[0][0], kTs, &sm.Gs[0][0], kTs, ap);
-        if (adj_o) adj_gemm(&sm.pin[0][0], kPs, &sm.base[0][0], kPs, ao);
+    // ---- B: far fields from three or more blocks back: once their tasks are done,
+    // the K-chunk partials are summed in chunk order into registers (every load
+    // issued first; absent chunks read a valid address and are replaced by zero)
+    if (t == 0) {
+        if (d >= 3) wait_flag(p, &p.fardone[leaf], 2 * nch);
+        acquire_agent();
+        vm_wait_all();
     }
     __syncthreads();
-
-    // ---- B: far fields from diagonals d-2 and earlier: the K-chunk partials
-    // summed in chunk order (every load issued first; absent chunks read a valid
-    // address and are replaced by zero). D, g and the codes are cleared while the
-    // loads are in flight (the staging in DT and Gs is consumed).
+    constexpr int kG = (kB * kB / 4 + kLeafThreads - 1) / kLeafThreads;
+    const f32x4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 pvs[kG], ovs[kG];  // p and o^T, four consecutive entries per group
     {
-        constexpr int kG = (kB * kB / 4 + kLeafThreads - 1) / kLeafThreads;
         const bool any = far_p || far_o;
         f32x4 xp[kG][kNch], xo[kG][kNch];
         if (any) {
@@ -302,23 +538,9 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
 #pragma unroll
                 for (int c = 0; c < kNch; ++c) {
                     const int cc = min(c, nch - 1);
-                    xp[u][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, par, slot, 0, cc) + 4 * g);
-                    xo[u][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, par, slot, 1, cc) + 4 * g);
+                    xp[u][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, d, slot, 0, cc) + 4 * g);
+                    xo[u][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, d, slot, 1, cc) + 4 * g);
                 }
-            }
-        }
-        const f32x4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (any) {
-            __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int u = 0; u < kG; ++u) {
-            const int g = t + u * kLeafThreads;
-            if (g < kB * kB / 4) {
-                const int k = g >> 4, c4 = (g & 15) << 2;
-                *reinterpret_cast<f32x4*>(&sm.DT[k][c4]) = z4;
-                *reinterpret_cast<f32x4*>(&sm.Gs[k][c4]) = z4;
-                *reinterpret_cast<uint32_t*>(&sm.code[k][c4]) = 0u;
             }
         }
 #pragma unroll
@@ -330,13 +552,11 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
 #pragma unroll
                     for (int c = 0; c < kNch; ++c) {
                         const int cc = min(c, nch - 1);
-                        xp[uu][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, par, slot, 0, cc) + 4 * gg);
-                        xo[uu][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, par, slot, 1, cc) + 4 * gg);
+                        xp[uu][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, d, slot, 0, cc) + 4 * gg);
+                        xo[uu][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, d, slot, 1, cc) + 4 * gg);
                     }
                 }
             }
-            const int g = t + u * kLeafThreads;
-            if (g >= kB * kB / 4) continue;
             f32x4 pv = z4, ov = z4;
             if (any) {
 #pragma unroll
@@ -349,23 +569,75 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
                     }
                 }
             }
-            const int e = 4 * g;
-            const int r = e / kB, c0 = e % kB;  // p: row r, cols c0..c0+3; o^T: row (= leaf col) r, leaf rows c0..
+            pvs[u] = pv;
+            ovs[u] = ov;
+        }
+    }
+    // ---- the leaves two blocks up and to the left: once they are done, their
+    // blocks are multiplied (K = 64)
+    if (t == 0) {
+        if (two_p) wait_flag(p, &p.prog_d[leaf - 2 * (int64_t)p.N], kStrips);
+        if (two_o) wait_flag(p, &p.prog_c[leaf - 2], kStrips);
+        acquire_agent();
+        vm_wait_all();
+    }
+    __syncthreads();
+    //   Gs <- D[i0-128+k][j0+c]     base <- C^T[j0-128+k][i0+c]   (staging)
+    {
+        float v2[kPer], v4[kPer];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                sm.pin[r][c0 + k] = pv[k];
-                sm.base[c0 + k][r] = ov[k];
+        for (int u = 0; u < kPer; ++u) {
+            const int e = t + u * kLeafThreads;
+            const int k = e >> 6, c = e & 63;
+            const bool in = e < kB * kB;
+            v2[u] = (in && two_p && c < Cc) ? p.delta[(i0 - 2 * kB + k) * p.ldd + j0 + c] : 0.0f;
+            v4[u] = (in && two_o && c < R) ? p.ct[(j0 - 2 * kB + k) * p.m + i0 + c] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int e = t + u * kLeafThreads;
+            if (e < kB * kB) {
+                const int k = e >> 6, c = e & 63;
+                sm.Gs[k][c] = v2[u];
+                sm.base[k][c] = v4[u];
             }
         }
     }
     __syncthreads();
-    // ---- C: then the adjacent products, then W*
+    f32x16 ap, ao;  // products with the blocks two back: p += L_O^T D, o^T += L_I^T C^T
+#pragma unroll
+    for (int v = 0; v < 16; ++v) ap[v] = ao[v] = 0.0f;
     if (w < 4) {
-        const int cc = acc32_col();
+        if (two_p) adj_gemm(&sm.DT[0][0], kTs, &sm.Gs[0][0], kTs, ap, t);
+        if (two_o) adj_gemm(&sm.pin[0][0], kPs, &sm.base[0][0], kPs, ao, t);
+    }
+    __syncthreads();
+    // ---- C: p = partials + ap, o = partials + ao, then W* added to o; D, g and
+    // the codes cleared (the staging is consumed)
+#pragma unroll
+    for (int u = 0; u < kG; ++u) {
+        const int g = t + u * kLeafThreads;
+        if (g < kB * kB / 4) {
+            const int k = g >> 4, c4 = (g & 15) << 2;
+            *reinterpret_cast<f32x4*>(&sm.DT[k][c4]) = z4;
+            *reinterpret_cast<f32x4*>(&sm.Gs[k][c4]) = z4;
+            *reinterpret_cast<uint32_t*>(&sm.code[k][c4]) = 0u;
+            const int e = 4 * g;
+            const int r = e / kB, c0 = e % kB;  // p: row r, cols c0..c0+3; o^T: row (= leaf col) r, leaf rows c0..
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                sm.pin[r][c0 + q] = pvs[u][q];
+                sm.base[c0 + q][r] = ovs[u][q];
+            }
+        }
+    }
+    __syncthreads();
+    if (w < 4) {
+        const int cc = acc32_col(t);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            sm.pin[acc32_row(v)][cc] += ap[v];
-            sm.base[cc][acc32_row(v)] += ao[v];
+            sm.pin[acc32_row(v, t)][cc] += ap[v];
+            sm.base[cc][acc32_row(v, t)] += ao[v];
         }
     }
     __syncthreads();
@@ -377,6 +649,22 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
         sm.DI[t] = (p.want_loss && t < Cc) ? p.DI[j0 + t] : 0.0f;
         sm.pnb[0][t] = sm.pnb[1][t] = sm.pnb[2][t] = 0.0f;
         sm.rnb[0][t] = sm.rnb[1][t] = sm.rnb[2][t] = 0.0f;
+    }
+    __syncthreads();
+    // ---- D: the partials are consumed (their ring slot may be reused); the
+    // neighbours' first strips are taken before the sweep
+    if (t == 0) st_flag(&p.setup[leaf], 1);
+    const bool hcol = w == 5;
+    const bool hown = hcol ? adj_p : adj_o;  // this hand-over wave has a neighbour to take from
+    const int* hflag = !hown ? p.prog_d : hcol ? p.prog_d + (leaf - p.N) : p.prog_c + (leaf - 1);
+    Handover h;  // the factor block stays in registers for the whole sweep
+    if (w >= 5 && hown) {
+        handover_factor(p, hcol, i0, j0, R, Cc, h, lane);
+        wait_flag(p, hflag, 1);
+        compiler_fence();
+        handover_load(p, hcol, 0, i0, j0, R, Cc, h, lane);
+        handover_mma<0, 16>(hcol, h);
+        handover_add(sm, hcol, 0, h, lane);
     }
 
     double loss = 0.0;
@@ -469,7 +757,7 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
             step(st + 1, cb, ca);
         }
         step(st, ca, cb);  // 127 steps: the last one
-    } else {
+    } else if (w == 4) {
         // ---------------- finaliser wave: lane i owns row i ----------------
         // adds the two newest terms of each sum: D[i-1][j], D[i-2][j] (from the
         // lanes above, by DPP) and g[i][j-1], g[i][j-2] (its own previous results);
@@ -539,6 +827,51 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
             __builtin_amdgcn_sched_barrier(0);
             barrier_no_wait();
         }
+    } else {
+        // ---------------- hand-over waves (5: column-wise, 6: row-wise) ----------------
+        int seen = 0;  // neighbour's counter, read three steps before it is looked at
+        __syncthreads();
+#pragma nounroll
+        for (int st = 0; st < kSweep; ++st) {
+            // the lane index, opaque per step, so that the address arithmetic of the
+            // loads and stores below is not hoisted out of the sweep and held across it
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            // the neighbour's strip c >= 1: window st = 16c - 12 .. 16c - 2
+            const int cw = (st + 12) >> 4, ph = (st + 12) & 15;
+            if (hown && cw >= 1 && cw < kStrips) {
+                if (ph == 0) {
+                    seen = ld_flag(hflag);
+                } else if (ph == 3) {
+                    if (seen < cw + 1) wait_flag(p, hflag, cw + 1);
+                    compiler_fence();
+                    handover_load(p, hcol, cw, i0, j0, R, Cc, h, ln);
+                } else if (ph == 7) {
+                    handover_mma<0, 6>(hcol, h);
+                } else if (ph == 8) {
+                    handover_mma<6, 11>(hcol, h);
+                } else if (ph == 9) {
+                    handover_mma<11, 16>(hcol, h);
+                } else if (ph == 10) {
+                    handover_add(sm, hcol, cw, h, ln);
+                }
+            }
+            // this leaf's strip c <= 2: stored at st = 79 + 16c, counter raised 4 steps later
+            if (st >= kB + kStrip - 1) {
+                const int cp = (st - (kB + kStrip - 1)) >> 4, pp = (st - (kB + kStrip - 1)) & 15;
+                if (cp < kStrips - 1) {
+                    if (pp == 0) handover_publish(p, sm, hcol, cp, i0, j0, R, Cc, ln);
+                    else if (pp == 4) handover_flag(p, hcol, leaf, cp + 1, ln);
+                }
+            }
+            lds_wait_all();
+            barrier_no_wait();
+        }
+    }
+    // the last strips
+    if (w >= 5) {
+        handover_publish(p, sm, hcol, kStrips - 1, i0, j0, R, Cc, lane);
+        handover_flag(p, hcol, leaf, kStrips, lane);
     }
     // loss partial: sum of D_O,i D_I,j eta_ij^2 over the leaf, in fp64
     if (p.want_loss) {
@@ -551,55 +884,21 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
             }
         }
     }
-
-    // ---- outputs: codes and D along the leaf's rows, C^T along its columns; every LDS
-    // read of the thread first, then the stores (four columns per store where aligned)
+    // ---- codes, along the leaf's rows (four per store where aligned); D and C^T
+    // went out with the hand-overs
     {
-        constexpr int kG = (kB * kB / 4 + kLeafThreads - 1) / kLeafThreads;
-        const bool ovec = ((reinterpret_cast<uintptr_t>(p.delta) | reinterpret_cast<uintptr_t>(p.ct)) & 15) == 0 &&
-                          (reinterpret_cast<uintptr_t>(p.codes) & 3) == 0 && ((p.ldd | p.m | p.ldc) & 3) == 0;
-        uint32_t cv[kG];
-        f32x4 dv[kG], gv[kG];
-#pragma unroll
-        for (int u = 0; u < kG; ++u) {
-            const int g = min(t + u * kLeafThreads, kB * kB / 4 - 1);
+        const bool ovec = (reinterpret_cast<uintptr_t>(p.codes) & 3) == 0 && (p.ldc & 3) == 0;
+        for (int g = t; g < kB * kB / 4; g += kLeafThreads) {
             const int r = g >> 4, c4 = (g & 15) << 2;
-            cv[u] = *reinterpret_cast<const uint32_t*>(&sm.code[r][c4]);  // code[r][c4..]
+            if (r >= R) continue;
+            const uint32_t cv = *reinterpret_cast<const uint32_t*>(&sm.code[r][c4]);
+            uint8_t* cp = p.codes + (i0 + r) * p.ldc + j0 + c4;
+            if (ovec && c4 + 3 < Cc) {
+                *reinterpret_cast<uint32_t*>(cp) = cv;
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                dv[u][e] = sm.DT[c4 + e][r];  // D[r][c4 + e]
-                gv[u][e] = sm.Gs[c4 + e][r];  // C[c4 + e][r], row r of C^T
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kG; ++u) {
-            const int g = t + u * kLeafThreads;
-            if (g >= kB * kB / 4) continue;
-            const int r = g >> 4, c4 = (g & 15) << 2;
-            if (r < R) {  // row i0 + r of the codes and of D, columns j0 + c4..
-                uint8_t* cp = p.codes + (i0 + r) * p.ldc + j0 + c4;
-                float* dp = p.delta + (i0 + r) * p.ldd + j0 + c4;
-                if (ovec && c4 + 3 < Cc) {
-                    *reinterpret_cast<uint32_t*>(cp) = cv[u];
-                    *reinterpret_cast<f32x4*>(dp) = dv[u];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (c4 + e < Cc) {
-                            cp[e] = (uint8_t)(cv[u] >> (8 * e));
-                            dp[e] = dv[u][e];
-                        }
-                }
-            }
-            if (r < Cc) {  // row j0 + r of C^T, columns i0 + c4..
-                float* gp = p.ct + (j0 + r) * p.m + i0 + c4;
-                if (ovec && c4 + 3 < R) {
-                    *reinterpret_cast<f32x4*>(gp) = gv[u];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (c4 + e < R) gp[e] = gv[u][e];
-                }
+                for (int e = 0; e < 4; ++e)
+                    if (c4 + e < Cc) cp[e] = (uint8_t)(cv >> (8 * e));
             }
         }
     }
@@ -618,41 +917,61 @@ __device__ __forceinline__ void leaf_body(const SolveParams& p, int d, int nch, 
         double lsum = 0.0;
         int csum = 0;
 #pragma unroll
-        for (int k = 0; k < kLeafThreads / 64; ++k) {
+        for (int k = 0; k < kLeafWaves; ++k) {
             lsum += sm.red[k];
             csum += sm.red_i[k];
         }
-        p.leaf_loss[(size_t)I * p.N + J] = lsum;
-        p.leaf_clamp[(size_t)I * p.N + J] = csum;
+        p.leaf_loss[leaf] = lsum;
+        p.leaf_clamp[leaf] = csum;
     }
 }
 
-// One launch per leaf-diagonal d: workgroups 0..nleaf-1 solve the leaves of
-// d (dispatched first), the others form the far fields of d + 1 (their inputs
-// are the leaves of d - 1 and earlier, finished by the previous launch) on
-// the CUs the leaves leave free.
-union StepSmem {
+// The whole solve: each workgroup takes the next task until none is left.
+// Group k of the task order holds the leaves of diagonal k, then the far
+// fields of diagonal k + 1.
+union SolveSmem {
     LeafSmem leaf;
     GemmSmemF32<kFarKT> far;
 };
 
-__global__ __launch_bounds__(kLeafThreads, 1) void k_step(SolveParams p, int d, int nch, int nleaf,
-                                                       int nch_next) {
-    __shared__ StepSmem sm;
-    if ((int)blockIdx.x < nleaf) leaf_body(p, d, nch, blockIdx.x, sm.leaf);
-    else far_body(p, d + 1, nch_next, blockIdx.x - nleaf, sm.far);
+__global__ __launch_bounds__(kLeafThreads, 1) void k_solve_run(SolveParams p) {
+    __shared__ SolveSmem sm;
+    __shared__ int s_task;
+    if (*p.info != INT_MAX) return;  // a row scale was invalid
+    for (;;) {
+        // the thread index, opaque to the compiler once per task, so that index
+        // arithmetic is not hoisted out of the loop and held across it
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        if (tid == 0) s_task = atomicAdd(p.ticket, 1);
+        __syncthreads();
+        const int tk = __builtin_amdgcn_readfirstlane(s_task);  // uniform: keeps the task's indices scalar
+        if (tk >= p.ntask) break;
+        int lo = 0, hi = p.ND - 1;  // the last group starting at or before tk
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.seg[mid] <= tk) lo = mid;
+            else hi = mid - 1;
+        }
+        const int r = tk - p.seg[lo];
+        const int nl = diag_leaves(p.M, p.N, lo);
+        if (r < nl) leaf_task(p, lo, r, sm.leaf, tid);
+        else far_task(p, lo + 1, r - nl, sm.far, tid);
+        __syncthreads();  // the next task reuses the shared memory
+    }
 }
 
 // loss = sum of leaf partials in a fixed order; clamped count; info.
 __global__ __launch_bounds__(kThreads) void k_solve_finish(const double* leaf_loss,
-                                                           const int* leaf_clamp, int nleaves,
+                                                           const int* leaf_clamp, int64_t nleaves,
                                                            double* loss, int64_t* clamped,
-                                                           const int* info_ws, int32_t* info) {
+                                                           const int* info_ws, const int* abort,
+                                                           int32_t* info) {
     __shared__ double rl[kThreads];
     __shared__ long long rc[kThreads];
     double s = 0.0;
     long long c = 0;
-    for (int e = threadIdx.x; e < nleaves; e += kThreads) {
+    for (int64_t e = threadIdx.x; e < nleaves; e += kThreads) {
         s += leaf_loss[e];
         c += leaf_clamp[e];
     }
@@ -669,7 +988,7 @@ __global__ __launch_bounds__(kThreads) void k_solve_finish(const double* leaf_lo
     if (threadIdx.x == 0) {
         if (loss) *loss = rl[0];
         if (clamped) *clamped = (int64_t)rc[0];
-        if (info) *info = (*info_ws == INT_MAX) ? 0 : *info_ws;
+        if (info) *info = (*info_ws != INT_MAX) ? *info_ws : (*abort ? -1 : 0);
     }
 }
 
@@ -678,8 +997,8 @@ __global__ __launch_bounds__(kThreads) void k_solve_finish(const double* leaf_lo
 // ---------------------------------------------------------------------------
 namespace {
 struct Layout {
-    int M, N, maxleaf;
-    size_t ct, delta, parts, leaf_loss, leaf_clamp, info, total;
+    int M, N, maxleaf, ND;
+    size_t ct, delta, parts, leaf_loss, leaf_clamp, info, sched, flags, seg, nchd, total;
 };
 
 Layout layout(int64_t m, int64_t n) {
@@ -687,21 +1006,53 @@ Layout layout(int64_t m, int64_t n) {
     L.M = (int)((m + kB - 1) / kB);
     L.N = (int)((n + kB - 1) / kB);
     L.maxleaf = std::min(L.M, L.N);
+    L.ND = L.M + L.N - 1;
+    const size_t nl = (size_t)L.M * L.N;
     size_t o = 0;
     L.ct = o;
     o += align256(sizeof(float) * (size_t)m * (size_t)n);
     L.delta = o;
     o += align256(sizeof(float) * (size_t)m * (size_t)n);
-    L.parts = o;  // two diagonals in flight (parity)
-    o += align256(sizeof(float) * 2 * (size_t)L.maxleaf * 2 * kNch * kB * kB);
+    L.parts = o;  // kRing diagonals in flight
+    o += align256(sizeof(float) * kRing * (size_t)L.maxleaf * 2 * kNch * kB * kB);
     L.leaf_loss = o;
-    o += align256(sizeof(double) * (size_t)L.M * L.N);
+    o += align256(sizeof(double) * nl);
     L.leaf_clamp = o;
-    o += align256(sizeof(int) * (size_t)L.M * L.N);
+    o += align256(sizeof(int) * nl);
     L.info = o;
     o += 256;
+    L.sched = o;  // ticket, abort
+    o += 256;
+    L.flags = o;  // prog_d, prog_c, setup, fardone
+    o += align256(sizeof(int) * 4 * nl);
+    L.seg = o;
+    o += align256(sizeof(int) * ((size_t)L.ND + 1));
+    L.nchd = o;
+    o += align256(sizeof(int) * (size_t)L.ND);
     L.total = o;
     return L;
+}
+
+struct DeviceInfo {
+    int cus = 0;
+    int clock_khz = 0;  // wall clock of s_memrealtime
+};
+
+DeviceInfo device_info() {
+    static DeviceInfo cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    DeviceInfo& di = cache[dev];
+    if (di.cus == 0) {
+        int cus = 0, khz = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+            khz = 100000;
+        di.clock_khz = khz;
+        di.cus = cus;
+    }
+    return di;
 }
 }  // namespace
 
@@ -709,6 +1060,10 @@ size_t solve_workspace_bytes(int64_t m, int64_t n) { return layout(m, n).total; 
 
 int run_solve(const SolveArgs& a, void* ws, hipStream_t stream) {
     const Layout L = layout(a.m, a.n);
+    int64_t ntask = 0;
+    for (int k = 0; k < L.ND; ++k) ntask += group_tasks(L.M, L.N, L.ND, k);
+    if (ntask >= INT_MAX / 2) return BAKRON_E_INVALID_ARG;
+    const DeviceInfo di = device_info();
     char* base = (char*)ws;
     SolveParams p;
     p.W = a.W;
@@ -738,31 +1093,27 @@ int run_solve(const SolveArgs& a, void* ws, hipStream_t stream) {
     p.want_loss = a.loss != nullptr;
     p.info = (int*)(base + L.info);
     p.maxleaf = L.maxleaf;
+    const size_t nl = (size_t)L.M * L.N;
+    p.ticket = (int*)(base + L.sched);
+    p.abort = p.ticket + 1;
+    p.prog_d = (int*)(base + L.flags);
+    p.prog_c = p.prog_d + nl;
+    p.setup = p.prog_c + nl;
+    p.fardone = p.setup + nl;
+    p.seg = (int*)(base + L.seg);
+    p.nchd = (int*)(base + L.nchd);
+    p.ND = L.ND;
+    p.ntask = (int)ntask;
+    p.spin_limit = (uint64_t)di.clock_khz * 1000ull * 10ull;  // 10 s
 
-    hipLaunchKernelGGL(k_solve_init, dim3(1), dim3(64), 0, stream, p.info);
+    const int init_blocks = (int)std::min<size_t>(1024, std::max<size_t>(1, (nl + kThreads - 1) / kThreads));
+    hipLaunchKernelGGL(k_solve_init, dim3((unsigned)init_blocks), dim3(kThreads), 0, stream, p);
     hipLaunchKernelGGL(k_scales, dim3((unsigned)a.m), dim3(kThreads), 0, stream, a.W, a.n, a.ldw,
                        a.bits, a.row_scale, a.scales, p.info);
-    const int ndiag = L.M + L.N - 1;
-    // per diagonal: leaf count and K-chunks per far-field product (enough
-    // workgroups to fill the chip, chunks of at least 4 blocks)
-    auto diag_shape = [&](int d, int& nleaf, int& nch, int& nfar) {
-        const int lo = std::max(0, d - (L.N - 1)), hi = std::min(d, L.M - 1);
-        nleaf = hi - lo + 1;
-        const int kmax = std::max(hi, d - lo) - 1;  // blocks before the adjacent one
-        nch = std::max(1, (kTargetWg + 2 * nleaf - 1) / (2 * nleaf));
-        nch = std::min(nch, std::max(1, kmax / 4));
-        nch = std::min(nch, kNch);
-        nfar = kmax > 0 ? nleaf * 2 * nch : 0;
-    };
-    for (int d = 0; d < ndiag; ++d) {
-        int nleaf, nch, nfar, nl1 = 0, nch1 = 1, nfar1 = 0;  // this diagonal, the next one
-        diag_shape(d, nleaf, nch, nfar);
-        if (d + 1 < ndiag) diag_shape(d + 1, nl1, nch1, nfar1);
-        hipLaunchKernelGGL(k_step, dim3((unsigned)(nleaf + nfar1)), dim3(kLeafThreads), 0, stream, p,
-                           d, nch, nleaf, nch1);
-    }
+    const int grid = (int)std::min<int64_t>(di.cus, ntask);
+    hipLaunchKernelGGL(k_solve_run, dim3((unsigned)grid), dim3(kLeafThreads), 0, stream, p);
     hipLaunchKernelGGL(k_solve_finish, dim3(1), dim3(kThreads), 0, stream, p.leaf_loss,
-                       p.leaf_clamp, L.M * L.N, a.loss, a.clamped, p.info, a.info);
+                       p.leaf_clamp, (int64_t)nl, a.loss, a.clamped, p.info, p.abort, a.info);
     return hipGetLastError() == hipSuccess ? BAKRON_OK : BAKRON_E_DEVICE;
 }
 
