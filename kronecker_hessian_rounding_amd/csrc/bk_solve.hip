@@ -238,8 +238,85 @@ __device__ __forceinline__ void chunk_range(int kblk, int nch, int c, int& b0, i
     b1 = min(b0 + len, kblk);
 }
 
-__device__ __forceinline__ void far_task(const SolveParams& p, int d, int task, GemmSmemF32<kFarKT>& sm,
-                                         int tid) {
+// Whole 64x64 far-field tiles with 16-byte aligned rows: k-slices of kFarRingKT
+// rows fill a ring of kFarRingNS slots in LDS by direct global-to-LDS loads
+// (global_load_lds_dwordx4: one instruction of a wave fills four 64-float rows),
+// kFarRingNS - 1 slices ahead of the MFMAs, so several slices of loads are in
+// flight while the tile is computed. Waves 0-3 load and compute (32x32 quadrant
+// each); the others only join the barriers.
+constexpr int kFarRingKT = 32;
+constexpr int kFarRingNS = 4;
+struct FarRing {
+    float a[kFarRingNS][kFarRingKT][kB];
+    float b[kFarRingNS][kFarRingKT][kB];
+};
+
+// Wait until at most N of this wave's vector-memory operations are outstanding, then
+// meet the other waves. Direct-to-LDS loads complete in issue order, so with N = the
+// loads issued after slice s, slice s is in LDS once every wave has passed; the later
+// loads stay in flight across the barrier.
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// acc += A^T B over K (a multiple of kFarRingKT) for a whole 64x64 tile: A (k, r) at
+// A[k*lda + r], B (k, c) at B[k*ldb + c]; every thread of the workgroup calls it.
+__device__ __forceinline__ void far_gemm_ring(const float* __restrict__ A, int64_t lda,
+                                              const float* __restrict__ B, int64_t ldb, int64_t K,
+                                              f32x16& acc, FarRing& sm, int tid) {
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool active = w < 4;
+    const int ra = (w >> 1) * 32 + (lane & 31);
+    const int rb = (w & 1) * 32 + (lane & 31);
+    const int kh = lane >> 5;
+    const int c4 = (lane & 15) << 2;
+    constexpr int kLoads = 2 * (kFarRingKT / 16);  // direct loads per active wave per slice
+    const int64_t ns = K / kFarRingKT;
+    auto issue = [&](int64_t s) {
+        const int slot = (int)(s % kFarRingNS);
+        const int64_t k0 = s * kFarRingKT;
+#pragma unroll
+        for (int h = 0; h < kFarRingKT / 16; ++h) {
+            const int r = 4 * (2 * w + h);  // rows r .. r+3 of the slice
+            const int64_t k = k0 + r + (lane >> 4);
+            __builtin_amdgcn_global_load_lds(A + k * lda + c4, &sm.a[slot][r][0], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(B + k * ldb + c4, &sm.b[slot][r][0], 16, 0, 0);
+        }
+    };
+    if (active)
+        for (int s = 0; s < kFarRingNS - 1; ++s)
+            if (s < ns) issue(s);
+    for (int64_t it = 0; it < ns; ++it) {
+        if (it + kFarRingNS - 2 < ns) vm_wait_barrier<(kFarRingNS - 2) * kLoads>();
+        else vm_wait_barrier<0>();
+        if (!active) continue;
+        if (it + kFarRingNS - 1 < ns) issue(it + kFarRingNS - 1);
+        const int slot = (int)(it % kFarRingNS);
+        float fa[3], fb[3];
+        fa[0] = sm.a[slot][kh][ra];
+        fb[0] = sm.b[slot][kh][rb];
+        fa[1] = sm.a[slot][2 + kh][ra];
+        fb[1] = sm.b[slot][2 + kh][rb];
+#pragma unroll
+        for (int s = 0; s < kFarRingKT / 2; ++s) {
+            if (s + 2 < kFarRingKT / 2) {
+                fa[(s + 2) % 3] = sm.a[slot][2 * (s + 2) + kh][ra];
+                fb[(s + 2) % 3] = sm.b[slot][2 * (s + 2) + kh][rb];
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep the reads two steps ahead of the MFMAs
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[s % 3], fb[s % 3], acc, 0, 0, 0);
+        }
+    }
+}
+
+union FarSmem {
+    GemmSmemF32<kFarKT> staged;  // ragged tiles
+    FarRing ring;
+};
+
+__device__ __forceinline__ void far_task(const SolveParams& p, int d, int task, FarSmem& sm, int tid) {
     const int nch = p.nchd[d];
     const int slot = task / (2 * nch);
     const int kind = (task / nch) & 1;
@@ -273,12 +350,15 @@ __device__ __forceinline__ void far_task(const SolveParams& p, int d, int task, 
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
         const bool active = tid < kThreads;  // the other waves only join the barriers
-        if (kind == 0)  // p[ii][jj] = sum_k L_O[k][i0+ii] D[k][j0+jj]
-            tile_gemm_f32<kFarKT>(p.LO + k0 * p.ldlo + i0, p.ldlo, R, p.delta + k0 * p.ldd + j0, p.ldd, Cc, K,
-                                  acc, sm, active, tid);
-        else  // o^T[jj][ii] = sum_l L_I[l][j0+jj] C^T[l][i0+ii]
-            tile_gemm_f32<kFarKT>(p.LI + k0 * p.ldli + j0, p.ldli, Cc, p.ct + k0 * p.m + i0, p.m, R, K, acc,
-                                  sm, active, tid);
+        // p[ii][jj] = sum_k L_O[k][i0+ii] D[k][j0+jj];  o^T[jj][ii] = sum_l L_I[l][j0+jj] C^T[l][i0+ii]
+        const float* A = kind == 0 ? p.LO + k0 * p.ldlo + i0 : p.LI + k0 * p.ldli + j0;
+        const float* Bm = kind == 0 ? p.delta + k0 * p.ldd + j0 : p.ct + k0 * p.m + i0;
+        const int64_t lda = kind == 0 ? p.ldlo : p.ldli, ldb = kind == 0 ? p.ldd : p.m;
+        const int ra_lim = kind == 0 ? R : Cc, cb_lim = kind == 0 ? Cc : R;
+        const bool whole = R == kB && Cc == kB && ((lda | ldb) & 3) == 0 &&
+                           ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(Bm)) & 15) == 0;
+        if (whole) far_gemm_ring(A, lda, Bm, ldb, K, acc, sm.ring, tid);
+        else tile_gemm_f32<kFarKT>(A, lda, ra_lim, Bm, ldb, cb_lim, K, acc, sm.staged, active, tid);
         if (active) {
             float* part = part_ptr(p, d, slot, kind, c);
             const int cc = acc32_col(tid);
@@ -300,8 +380,8 @@ __device__ __forceinline__ void far_task(const SolveParams& p, int d, int task, 
 //   pn = sum_{k<i} L_O[k][i] D[k][j],   rn = sum_{l<j} g[i][l] L_I[l][j]
 // (g = C, the column feedback plus error of the row) are split into a bulk,
 // which only uses entries finalised three or more steps earlier, and the two
-// newest terms of each (k = i-1, i-2 and l = j-1, j-2). Waves 0-3 compute the
-// bulk of step st + 2 while wave 4 finalises step st, so the dependent chain
+// newest terms of each (k = i-1, i-2 and l = j-1, j-2). Four bulk waves compute
+// the bulk of step st + 2 while the finaliser wave finalises step st, so the dependent chain
 // of a step holds no LDS read: the finaliser takes D[i-1][j] and D[i-2][j]
 // from the lanes above by DPP, g[i][j-1] and g[i][j-2] from its own previous
 // steps, and the bulk sums and static inputs were read one step ahead.
@@ -317,17 +397,25 @@ __device__ __forceinline__ void far_task(const SolveParams& p, int d, int task, 
 // L_O[above, this]^T D[above, strip] into p) and row-wise (6: C to the leaf on
 // the right, and C[strip, left] L_I[left, this] into o). Strip c (columns or
 // rows 16c..16c+15) of this leaf is final after step 78 + 16c; it is stored a
-// step later and its counter raised four steps after that, when the stores
+// step later and its counter raised three steps after that, when the stores
 // have landed. The neighbour's strip c (c >= 1) is taken in a window ending at
 // step 16c - 2: counter read at 16c - 12, checked (and waited for, if late)
-// at 16c - 9 and the strip loaded (device-coherent loads, which go to memory),
-// multiplied with v_mfma_f32_16x16x4_f32 over steps 16c - 5 .. 16c - 3 (the
-// loads have four steps to land) and added to p (o) before the finaliser reads
-// columns (rows) 16c.., at the end of step 16c - 1. Strip 0 is taken before
-// the sweep.
+// at 16c - 10 and the strip loaded (device-coherent loads, which go to memory),
+// multiplied with v_mfma_f32_16x16x4_f32 over steps 16c - 7 .. 16c - 3 (a
+// dozen MFMAs a step, within what the other waves take for a step) and added
+// to p (o) before the finaliser reads columns (rows) 16c.., at the end of step
+// 16c - 1. Strip 0 is taken before the sweep.
 // ---------------------------------------------------------------------------
 constexpr int kLeafWaves = 7;
 constexpr int kLeafThreads = kLeafWaves * 64;
+// Roles in the sweep by wave index. Waves are spread over the four SIMDs by
+// index (SIMD w mod 4): the finaliser, whose chain sets the pace, has SIMD 3 to
+// itself (sharing it with a bulk wave cost a fifth of the sweep's speed); bulk
+// waves 0, 1, 2 and 4 and hand-over waves 5 and 6 fill SIMDs 0-2. Putting both
+// hand-over waves on one SIMD measured slower.
+constexpr int kFinWave = 3;
+constexpr int kColWave = 5;  // hand-over of columns of D (to the leaf below)
+constexpr int kRowWave = 6;  // hand-over of rows of C (to the leaf on the right)
 constexpr int kTs = 68;  // row stride of the k/l-indexed tiles
 constexpr int kPs = 66;  // row stride of the per-entry inputs: anti-diagonal walks hit distinct banks
 
@@ -573,6 +661,9 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
             ovs[u] = ov;
         }
     }
+    // the partials are read (their ring slot may be reused)
+    __syncthreads();
+    if (t == 0) st_flag(&p.setup[leaf], 1);
     // ---- the leaves two blocks up and to the left: once they are done, their
     // blocks are multiplied (K = 64)
     if (t == 0) {
@@ -651,14 +742,13 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
         sm.rnb[0][t] = sm.rnb[1][t] = sm.rnb[2][t] = 0.0f;
     }
     __syncthreads();
-    // ---- D: the partials are consumed (their ring slot may be reused); the
-    // neighbours' first strips are taken before the sweep
-    if (t == 0) st_flag(&p.setup[leaf], 1);
-    const bool hcol = w == 5;
+    // ---- D: the neighbours' first strips are taken before the sweep
+    const bool hwave = w == kColWave || w == kRowWave;
+    const bool hcol = w == kColWave;
     const bool hown = hcol ? adj_p : adj_o;  // this hand-over wave has a neighbour to take from
     const int* hflag = !hown ? p.prog_d : hcol ? p.prog_d + (leaf - p.N) : p.prog_c + (leaf - 1);
     Handover h;  // the factor block stays in registers for the whole sweep
-    if (w >= 5 && hown) {
+    if (hwave && hown) {
         handover_factor(p, hcol, i0, j0, R, Cc, h, lane);
         wait_flag(p, hflag, 1);
         compiler_fence();
@@ -669,7 +759,8 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
 
     double loss = 0.0;
     int nclamp = 0;
-    if (w < 4) {
+    const bool bulk = w != kFinWave && w != kColWave && w != kRowWave;
+    if (bulk) {
         // ---------------- bulk waves ----------------
         // Lane (a, quarter q) sums the k / l range [16q, 16q + 16) of two bulk sums of
         // the entries finalised two steps later (x = st + 2 - a):
@@ -681,8 +772,9 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
         // on their own at the start of the step; the chunks (entries final a step
         // earlier) were read at the end of the previous step, so their LDS latency
         // overlaps the barrier and the finaliser's work.
-        const int a = t >> 2;
-        const int q = t & 3;
+        const int bt = (w == 4 ? kFinWave : w) * 64 + lane;  // bulk thread 0..255 (waves 0, 1, 2, 4)
+        const int a = bt >> 2;
+        const int q = bt & 3;
         const int k0 = 16 * q;
         float lo[16];  // L_O[i0 + k][i0 + a] for k <= a - 4, else 0
         float li[16];  // L_I[j0 + l][j0 + a] for l <= a - 4, else 0
@@ -757,7 +849,7 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
             step(st + 1, cb, ca);
         }
         step(st, ca, cb);  // 127 steps: the last one
-    } else if (w == 4) {
+    } else if (w == kFinWave) {
         // ---------------- finaliser wave: lane i owns row i ----------------
         // adds the two newest terms of each sum: D[i-1][j], D[i-2][j] (from the
         // lanes above, by DPP) and g[i][j-1], g[i][j-2] (its own previous results);
@@ -828,7 +920,7 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
             barrier_no_wait();
         }
     } else {
-        // ---------------- hand-over waves (5: column-wise, 6: row-wise) ----------------
+        // ---------------- hand-over waves (column-wise, row-wise) ----------------
         int seen = 0;  // neighbour's counter, read three steps before it is looked at
         __syncthreads();
 #pragma nounroll
@@ -842,26 +934,30 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
             if (hown && cw >= 1 && cw < kStrips) {
                 if (ph == 0) {
                     seen = ld_flag(hflag);
-                } else if (ph == 3) {
+                } else if (ph == 2) {
                     if (seen < cw + 1) wait_flag(p, hflag, cw + 1);
                     compiler_fence();
                     handover_load(p, hcol, cw, i0, j0, R, Cc, h, ln);
+                } else if (ph == 5) {
+                    handover_mma<0, 3>(hcol, h);
+                } else if (ph == 6) {
+                    handover_mma<3, 6>(hcol, h);
                 } else if (ph == 7) {
-                    handover_mma<0, 6>(hcol, h);
+                    handover_mma<6, 9>(hcol, h);
                 } else if (ph == 8) {
-                    handover_mma<6, 11>(hcol, h);
+                    handover_mma<9, 12>(hcol, h);
                 } else if (ph == 9) {
-                    handover_mma<11, 16>(hcol, h);
+                    handover_mma<12, 16>(hcol, h);
                 } else if (ph == 10) {
                     handover_add(sm, hcol, cw, h, ln);
                 }
             }
-            // this leaf's strip c <= 2: stored at st = 79 + 16c, counter raised 4 steps later
+            // this leaf's strip c <= 2: stored at st = 79 + 16c, counter raised 3 steps later
             if (st >= kB + kStrip - 1) {
                 const int cp = (st - (kB + kStrip - 1)) >> 4, pp = (st - (kB + kStrip - 1)) & 15;
                 if (cp < kStrips - 1) {
                     if (pp == 0) handover_publish(p, sm, hcol, cp, i0, j0, R, Cc, ln);
-                    else if (pp == 4) handover_flag(p, hcol, leaf, cp + 1, ln);
+                    else if (pp == 3) handover_flag(p, hcol, leaf, cp + 1, ln);
                 }
             }
             lds_wait_all();
@@ -869,7 +965,7 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
         }
     }
     // the last strips
-    if (w >= 5) {
+    if (hwave) {
         handover_publish(p, sm, hcol, kStrips - 1, i0, j0, R, Cc, lane);
         handover_flag(p, hcol, leaf, kStrips, lane);
     }
@@ -931,7 +1027,7 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
 // fields of diagonal k + 1.
 union SolveSmem {
     LeafSmem leaf;
-    GemmSmemF32<kFarKT> far;
+    FarSmem far;
 };
 
 __global__ __launch_bounds__(kLeafThreads, 1) void k_solve_run(SolveParams p) {
