@@ -397,8 +397,9 @@ __device__ __forceinline__ void far_task(const SolveParams& p, int d, int task, 
 // L_O[above, this]^T D[above, strip] into p) and row-wise (6: C to the leaf on
 // the right, and C[strip, left] L_I[left, this] into o). Strip c (columns or
 // rows 16c..16c+15) of this leaf is final after step 78 + 16c; it is stored a
-// step later and its counter raised three steps after that, when the stores
-// have landed. The neighbour's strip c (c >= 1) is taken in a window ending at
+// step later (storing each column as it became final, 64 scattered rows a
+// store, measured slower) and its counter raised three steps after that, when
+// the stores have landed. The neighbour's strip c (c >= 1) is taken in a window ending at
 // step 16c - 2: counter read at 16c - 12, checked (and waited for, if late)
 // at 16c - 10 and the strip loaded (device-coherent loads, which go to memory),
 // multiplied with v_mfma_f32_16x16x4_f32 over steps 16c - 7 .. 16c - 3 (a
@@ -416,14 +417,14 @@ constexpr int kLeafThreads = kLeafWaves * 64;
 constexpr int kFinWave = 3;
 constexpr int kColWave = 5;  // hand-over of columns of D (to the leaf below)
 constexpr int kRowWave = 6;  // hand-over of rows of C (to the leaf on the right)
-constexpr int kTs = 68;  // row stride of the k/l-indexed tiles
+constexpr int kTs = 68;  // row stride of the 64x64 tiles: 16-byte aligned rows, 4 banks apart
 constexpr int kPs = 66;  // row stride of the per-entry inputs: anti-diagonal walks hit distinct banks
 
 struct LeafSmem {
     float DT[kB][kTs];     // D transposed: DT[j][k] = D[k][j] (0 until known)
     float Gs[kB][kTs];     // g = C of the leaf, row-major (0 until known)
-    float base[kB][kPs];   // W* + o
-    float pin[kB][kPs];    // p
+    float bt[kB][kTs];     // W* + o, transposed: bt[j][i] for entry (i, j)
+    float pt[kB][kTs];     // p, transposed: pt[j][i]
     float wst[kB][kPs];    // W*, overwritten by eta = t - q once the entry is final
     float pnb[3][kB];      // bulk sums, by step modulo 3 (written two steps ahead)
     float rnb[3][kB];
@@ -523,15 +524,17 @@ __device__ __forceinline__ void handover_mma(bool col, Handover& h) {
     }
 }
 
+// the four elements of a lane's block t are consecutive in the transposed p and
+// o: one 16-byte read-modify-write each
 __device__ __forceinline__ void handover_add(LeafSmem& sm, bool col, int c, const Handover& h, int lane) {
+    const int r0 = 4 * (lane >> 4), cc = lane & 15;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = 4 * (lane >> 4) + q, cc = lane & 15;
-            if (col) sm.pin[16 * t + r][kStrip * c + cc] += h.acc[t][q];
-            else sm.base[kStrip * c + r][16 * t + cc] += h.acc[t][q];
-        }
+    for (int t = 0; t < 4; ++t) {
+        // column-wise: entries (16t + r0 + q, 16c + cc); row-wise: (16c + r0 + q, 16t + cc)
+        f32x4* q4 = col ? reinterpret_cast<f32x4*>(&sm.pt[kStrip * c + cc][16 * t + r0])
+                        : reinterpret_cast<f32x4*>(&sm.bt[16 * t + cc][kStrip * c + r0]);
+        *q4 += h.acc[t];
+    }
 }
 
 // stores strip c of this leaf's D (column-wise) or C^T (row-wise), device-coherent
@@ -577,7 +580,7 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
     }
     constexpr int kPer = (kB * kB + kLeafThreads - 1) / kLeafThreads;
     // ---- A: static inputs, every load of the thread in flight at once
-    //   DT  <- L_O[i0-128+k][i0+c]  pin <- L_I[j0-128+k][j0+c]   (blocks two back: staging)
+    //   DT  <- L_O[i0-128+k][i0+c]  pt <- L_I[j0-128+k][j0+c]    (blocks two back: staging)
     //   wst <- W*[i0+k][j0+c]       li1, li2 <- the first two superdiagonals of L_I
     {
         float v1[kPer], v3[kPer], v5[kPer], v6[kPer];
@@ -597,7 +600,7 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
             if (e < kB * kB) {
                 const int k = e >> 6, c = e & 63;
                 sm.DT[k][c] = v1[u];
-                sm.pin[k][c] = v3[u];
+                sm.pt[k][c] = v3[u];
                 sm.wst[k][c] = v5[u];
                 if (c - k == 1) sm.li1[c] = v6[u];
                 if (c - k == 2) sm.li2[c] = v6[u];
@@ -673,7 +676,7 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
         vm_wait_all();
     }
     __syncthreads();
-    //   Gs <- D[i0-128+k][j0+c]     base <- C^T[j0-128+k][i0+c]   (staging)
+    //   Gs <- D[i0-128+k][j0+c]     bt <- C^T[j0-128+k][i0+c]     (staging)
     {
         float v2[kPer], v4[kPer];
 #pragma unroll
@@ -690,7 +693,7 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
             if (e < kB * kB) {
                 const int k = e >> 6, c = e & 63;
                 sm.Gs[k][c] = v2[u];
-                sm.base[k][c] = v4[u];
+                sm.bt[k][c] = v4[u];
             }
         }
     }
@@ -700,7 +703,7 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
     for (int v = 0; v < 16; ++v) ap[v] = ao[v] = 0.0f;
     if (w < 4) {
         if (two_p) adj_gemm(&sm.DT[0][0], kTs, &sm.Gs[0][0], kTs, ap, t);
-        if (two_o) adj_gemm(&sm.pin[0][0], kPs, &sm.base[0][0], kPs, ao, t);
+        if (two_o) adj_gemm(&sm.pt[0][0], kTs, &sm.bt[0][0], kTs, ao, t);
     }
     __syncthreads();
     // ---- C: p = partials + ap, o = partials + ao, then W* added to o; D, g and
@@ -716,10 +719,8 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
             const int e = 4 * g;
             const int r = e / kB, c0 = e % kB;  // p: row r, cols c0..c0+3; o^T: row (= leaf col) r, leaf rows c0..
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                sm.pin[r][c0 + q] = pvs[u][q];
-                sm.base[c0 + q][r] = ovs[u][q];
-            }
+            for (int q = 0; q < 4; ++q) sm.pt[c0 + q][r] = pvs[u][q];
+            *reinterpret_cast<f32x4*>(&sm.bt[r][c0]) = ovs[u];
         }
     }
     __syncthreads();
@@ -727,14 +728,14 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
         const int cc = acc32_col(t);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            sm.pin[acc32_row(v, t)][cc] += ap[v];
-            sm.base[cc][acc32_row(v, t)] += ao[v];
+            sm.pt[cc][acc32_row(v, t)] += ap[v];  // entry (row, cc)
+            sm.bt[acc32_row(v, t)][cc] += ao[v];  // entry (cc, row)
         }
     }
     __syncthreads();
     for (int e = t; e < kB * kB; e += kLeafThreads) {
-        const int i = e / kB, j = e % kB;
-        sm.base[i][j] += sm.wst[i][j];
+        const int j = e / kB, i = e % kB;
+        sm.bt[j][i] += sm.wst[i][j];
     }
     if (t < kB) {
         sm.DI[t] = (p.want_loss && t < Cc) ? p.DI[j0 + t] : 0.0f;
@@ -869,8 +870,8 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
         float n_pb = sm.pnb[0][i], n_rb = sm.rnb[0][i];
         float n_pin = 0.f, n_base = 0.f, n_w = 0.f, n_l1 = 0.f, n_l2 = 0.f;
         if (i == 0) {
-            n_pin = sm.pin[0][0];
-            n_base = sm.base[0][0];
+            n_pin = sm.pt[0][0];
+            n_base = sm.bt[0][0];
             n_w = sm.wst[0][0];
         }
         int slot3n = 1;  // (st + 1) mod 3
@@ -910,8 +911,8 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
             const int jn = min(max(j + 1, 0), kB - 1);
             n_pb = sm.pnb[slot3n][i];
             n_rb = sm.rnb[slot3n][i];
-            n_pin = sm.pin[i][jn];
-            n_base = sm.base[i][jn];
+            n_pin = sm.pt[jn][i];
+            n_base = sm.bt[jn][i];
             n_w = sm.wst[i][jn];
             n_l1 = sm.li1[jn];
             n_l2 = sm.li2[jn];
