@@ -159,8 +159,10 @@ int bakron_ldl_async(float* H, int64_t d, int64_t ldh, double damp_rel, float* D
  *   clamped_out: optional device int64 count of entries whose code was clamped.
  *   info:  optional device int32; 0, or i+1 for the first row i whose scale is
  *          not finite and positive, or -1 if one of the solve's internal waits
- *          between workgroups ran past its limit (10 s of wall clock); in both
- *          cases the outputs are unspecified.
+ *          between workgroups ran past its limit (10 s of wall clock; the
+ *          environment variable BAKRON_SOLVE_WAIT_LIMIT_US, read at each call,
+ *          lowers it so that tests can reach this path); in both cases the
+ *          outputs are unspecified.
  *   ws:    device workspace of at least bakron_solve_workspace_bytes(m, n).
  */
 size_t bakron_solve_workspace_bytes(int64_t m, int64_t n);

@@ -33,6 +33,7 @@
 #include <limits.h>
 
 #include <algorithm>
+#include <cstdlib>
 
 #include "bk_common.hpp"
 #include "bk_internal.hpp"
@@ -200,8 +201,9 @@ __global__ __launch_bounds__(kThreads) void k_scales(const float* __restrict__ W
 }
 
 
-// Clears the schedule state and builds the task table (one thread walks the
-// diagonals; the counters are cleared by the whole grid).
+// Clears the schedule state and builds the task table: workgroup 0 scans the
+// per-group task counts 256 diagonals at a time; the counters are cleared by the
+// whole grid.
 __global__ __launch_bounds__(kThreads) void k_solve_init(SolveParams p) {
     const int64_t nl = (int64_t)p.M * p.N;
     for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < nl; e += (int64_t)gridDim.x * kThreads) {
@@ -210,17 +212,34 @@ __global__ __launch_bounds__(kThreads) void k_solve_init(SolveParams p) {
         p.setup[e] = 0;
         p.fardone[e] = 0;
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (blockIdx.x != 0) return;
+    __shared__ int sc[kThreads];
+    const int t = threadIdx.x;
+    int carry = 0;
+    for (int base = 0; base < p.ND; base += kThreads) {
+        const int k = base + t;
+        int v = 0;
+        if (k < p.ND) {
+            p.nchd[k] = diag_nch(p.M, p.N, k);
+            v = group_tasks(p.M, p.N, p.ND, k);
+        }
+        sc[t] = v;
+        __syncthreads();
+        for (int o = 1; o < kThreads; o <<= 1) {  // inclusive scan
+            const int x = t >= o ? sc[t - o] : 0;
+            __syncthreads();
+            sc[t] += x;
+            __syncthreads();
+        }
+        if (k < p.ND) p.seg[k] = carry + sc[t] - v;
+        carry += sc[kThreads - 1];
+        __syncthreads();
+    }
+    if (t == 0) {
+        p.seg[p.ND] = carry;
         *p.info = INT_MAX;
         *p.ticket = 0;
         *p.abort = 0;
-        int s = 0;
-        for (int k = 0; k < p.ND; ++k) {
-            p.nchd[k] = diag_nch(p.M, p.N, k);
-            p.seg[k] = s;
-            s += group_tasks(p.M, p.N, p.ND, k);
-        }
-        p.seg[p.ND] = s;
     }
 }
 
@@ -1201,7 +1220,13 @@ int run_solve(const SolveArgs& a, void* ws, hipStream_t stream) {
     p.nchd = (int*)(base + L.nchd);
     p.ND = L.ND;
     p.ntask = (int)ntask;
-    p.spin_limit = (uint64_t)di.clock_khz * 1000ull * 10ull;  // 10 s
+    // 10 s, or BAKRON_SOLVE_WAIT_LIMIT_US (a test hook that makes the waits expire)
+    uint64_t limit_us = 10ull * 1000 * 1000;
+    if (const char* e = std::getenv("BAKRON_SOLVE_WAIT_LIMIT_US")) {
+        const long long v = std::atoll(e);
+        if (v > 0) limit_us = (uint64_t)v;
+    }
+    p.spin_limit = (uint64_t)di.clock_khz * limit_us / 1000ull;
 
     const int init_blocks = (int)std::min<size_t>(1024, std::max<size_t>(1, (nl + kThreads - 1) / kThreads));
     hipLaunchKernelGGL(k_solve_init, dim3((unsigned)init_blocks), dim3(kThreads), 0, stream, p);

@@ -305,6 +305,22 @@ def test_solve_reports_zero_row(bk):
     assert int(res.info.item()) == 34
 
 
+def test_solve_expired_wait_is_reported(bk, monkeypatch):
+    # The solve's workgroups wait on each other's progress counters, each wait bounded
+    # in time. A 1 us limit, set from the host, makes them expire: the solve must stop
+    # (every kernel still ends) and report info = -1; the next call runs normally.
+    note("solve with a 1 us wait limit")
+    w, LO, LI, DO, DI = factors(300, 260)
+    d = dev()
+    T = lambda a: torch.from_numpy(a).to(d)
+    monkeypatch.setenv("BAKRON_SOLVE_WAIT_LIMIT_US", "1")
+    res = bk.solve(T(w), T(LO), T(LI), 2)
+    assert int(res.info.item()) == -1
+    monkeypatch.delenv("BAKRON_SOLVE_WAIT_LIMIT_US")
+    res = bk.solve(T(w), T(LO), T(LI), 2)
+    assert int(res.info.item()) == 0
+
+
 def test_solve_small_config(bk):
     w, x, g = workloads.make_inputs("small")
     HI, HO = oracle.damp(oracle.hessian(x)), oracle.damp(oracle.hessian(g))
