@@ -556,22 +556,24 @@ __device__ __forceinline__ void handover_add(LeafSmem& sm, bool col, int c, cons
     }
 }
 
-// stores strip c of this leaf's D (column-wise) or C^T (row-wise), device-coherent
+// stores strip c of this leaf's D (column-wise) or C^T (row-wise), device-coherent.
+// Lane (s, quarter) reads 16 consecutive k of row s of DT (Gs) as four 16-byte words;
+// each store then covers 16 consecutive columns (strip entries s) of four rows k.
 __device__ __forceinline__ void handover_publish(const SolveParams& p, const LeafSmem& sm, bool col, int c,
                                                  int64_t i0, int64_t j0, int R, int Cc, int lane) {
-    const int s = kStrip * c + (lane & 15);
-    float* dst = col ? p.delta + i0 * p.ldd + j0 : p.ct + j0 * p.m + i0;
+    const int si = lane & 15, qk = lane >> 4;  // strip entry, quarter of k
+    const int s = kStrip * c + si;
+    float* dst = col ? p.delta + i0 * p.ldd + j0 + s : p.ct + j0 * p.m + i0 + s;
     const int64_t ld = col ? p.ldd : p.m;
     const int klim = col ? R : Cc, slim = col ? Cc : R;
-    const int64_t off = (lane >> 4) * ld + s;
-    const float* rowp = col ? &sm.DT[s][0] : &sm.Gs[s][0];  // D[k][s] = DT[s][k]; C[s][k] = Gs[s][k]
-    float v[16];
+    const float* rowp = col ? &sm.DT[s][16 * qk] : &sm.Gs[s][16 * qk];  // D[k][s] = DT[s][k]; C[s][k] = Gs[s][k]
+    f32x4 v[4];
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) v[kk] = rowp[4 * kk + (lane >> 4)];  // every read first
+    for (int h = 0; h < 4; ++h) v[h] = lds4(rowp + 4 * h);  // every read first
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-        const int k = 4 * kk + (lane >> 4);
-        if (k < klim && s < slim) st_coherent(dst + (int64_t)(4 * kk) * ld + off, v[kk]);
+    for (int e = 0; e < 16; ++e) {
+        const int k = 16 * qk + e;
+        if (k < klim && s < slim) st_coherent(dst + (int64_t)k * ld, v[e >> 2][e & 3]);
     }
 }
 
