@@ -75,7 +75,8 @@ def check_solve(bk, w, LO, LI, DO, DI, bits, rounding="nearest", seed=0, row_sca
     else:
         assert np.array_equal(scales, row_scale)
     lo64 = None if LO is None else LO.astype(np.float64)
-    rp = oracle.replay(w, lo64, LI.astype(np.float64), scales, bits, codes, rounding, seed,
+    li64 = None if LI is None else LI.astype(np.float64)
+    rp = oracle.replay(w, lo64, li64, scales, bits, codes, rounding, seed,
                        DO=DO.astype(np.float64), DI=DI.astype(np.float64))
     assert rp["bad"] == 0, ("mismatches outside the 1e-4 band", rp["bad"], rp["bad_index"])
     assert rp["max_flip_margin"] < 1e-4
@@ -93,7 +94,7 @@ def check_solve(bk, w, LO, LI, DO, DI, bits, rounding="nearest", seed=0, row_sca
     assert int(res.clamped.item()) >= 0
     out = dict(flips=rp["flips"], loss=loss, codes=codes)
     if free_run:
-        fr = oracle.sweep(w, lo64, LI.astype(np.float64), scales, bits, rounding, seed)
+        fr = oracle.sweep(w, lo64, li64, scales, bits, rounding, seed)
         mism = int((fr["codes"] != codes).sum())
         fl = oracle.loss_identity(fr["eta"], DO.astype(np.float64), DI.astype(np.float64))
         out.update(free_mismatch=mism, free_loss=fl)
@@ -276,6 +277,53 @@ def test_solve_one_sided_is_ldlq(bk):
     out = check_solve(bk, w, None, LI, DO, DI, 3, label="one-sided")
     # H_O = I: the rows are independent one-sided LDLQ problems
     assert out["free_mismatch"] == 0
+
+
+def test_solve_row_factor_only(bk):
+    # L_I absent (H_I diagonal): only the column feedback through L_O remains, so the
+    # column of leaves below a leaf hands over D while nothing passes along a row
+    w, LO, LI, DO, DI = factors(260, 150)
+    check_solve(bk, w, LO, None, DO, DI, 2, label="L_I absent")
+
+
+def test_solve_strided_operands(bk):
+    # every matrix a view with an odd leading dimension: the far-field GEMMs take the
+    # register-staged path, the strip hand-overs and the outputs use the strides
+    m, n, bits = 200, 330, 2
+    w, LO, LI, DO, DI = factors(m, n)
+    note("solve strided m=%d n=%d" % (m, n))
+    d = dev()
+
+    def strided(a, extra, dtype=torch.float32):
+        buf = torch.full((a.shape[0], a.shape[1] + extra), float("nan"), dtype=dtype, device=d)
+        v = buf[:, : a.shape[1]]
+        v.copy_(torch.from_numpy(np.ascontiguousarray(a)).to(d))
+        return v
+
+    Wv, LOv, LIv = strided(w, 3), strided(LO, 5), strided(LI, 1)
+    codes_buf = torch.zeros((m, n + 7), dtype=torch.uint8, device=d)
+    delta_buf = torch.full((m, n + 2), float("nan"), dtype=torch.float32, device=d)
+    out = bk.SolveResult(codes=codes_buf[:, :n], scales=torch.empty(m, dtype=torch.float32, device=d),
+                         delta=delta_buf[:, :n], loss=torch.empty(1, dtype=torch.float64, device=d),
+                         clamped=torch.empty(1, dtype=torch.int64, device=d),
+                         info=torch.empty(1, dtype=torch.int32, device=d))
+    res = bk.solve(Wv, LOv, LIv, bits, D_O=torch.from_numpy(DO).to(d), D_I=torch.from_numpy(DI).to(d),
+                   want_loss=True, out=out)
+    torch.cuda.synchronize()
+    assert int(res.info.item()) == 0
+    codes = res.codes.cpu().numpy()
+    scales = res.scales.cpu().numpy()
+    assert np.array_equal(scales, oracle.row_scales(w, bits))
+    rp = oracle.replay(w, LO.astype(np.float64), LI.astype(np.float64), scales, bits, codes,
+                       DO=DO.astype(np.float64), DI=DI.astype(np.float64))
+    assert rp["bad"] == 0 and rp["max_flip_margin"] < 1e-4
+    Lq = 2**bits - 1
+    exact = w.astype(np.float64) - scales[:, None].astype(np.float64) * (codes - Lq / 2.0)
+    assert np.max(np.abs(res.delta.cpu().numpy() - exact)) <= 2 * U32 * np.max(np.abs(exact))
+    floor = 1e-7 * oracle.bound_terms(scales, DO, DI)[0]
+    assert abs(float(res.loss.item()) - rp["loss"]) <= 1e-4 * abs(rp["loss"]) + floor
+    # nothing outside the views was written
+    assert torch.all(codes_buf[:, n:] == 0) and torch.all(torch.isnan(delta_buf[:, n:]))
 
 
 def test_solve_diagonal_factors_is_rtn(bk):
