@@ -1,7 +1,8 @@
 """Benchmark of the BaKron per-layer hot path on one MI355X.
 
 One step = the whole path for one layer on synthetic inputs already resident
-in HBM: H_I = X^T X / T and H_O = G^T G / T (fp32 MFMA), damping + LDL of
+in HBM: H_I = X^T X / T and H_O = G^T G / T (fp32 products formed from three
+bf16 pieces per operand on the bf16 matrix cores), damping + LDL of
 both (fp64), fp32 per-row scales, and the BaKron rounding solve with its proxy
 loss. Default workload: the attention-projection shape, W* 4096 x 4096,
 T = 32768 tokens, 2-bit nearest rounding.
@@ -24,19 +25,20 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_BF16_MFMA_TFLOPS = 2500.0
+PIECE_PRODUCTS = 6  # bf16 piece products per fp32 product in the Hessian
 PEAK_FP64_MFMA_TFLOPS = 78.6
 CAL_BYTES = 256 << 20
 
 # HBM traffic of one hessian_accum call at the attn workload, from two
 # rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per
-# dispatch, summed over the call's k_syrk_full, k_syrk_split and
+# dispatch, summed over the call's k_split3, k_syrk3_full, k_syrk3_split and
 # k_syrk_reduce). The counters are scaled by what they read for the
 # calibration copy above: FETCH_SIZE 131089.0 KiB and WRITE_SIZE 262144.0 KiB
 # for 262144 KiB moved each way. Valid only for the kernel source it was
 # measured on (hash of bk_accum.hip, which holds the SYRK kernels); otherwise
 # reported null.
 SYRK_COUNTERS = {
-    ("attn", "e599211bc58dd313"): {"fetch_kib": 6345559.8, "write_kib": 171207.3},
 }
 CAL_FETCH_KIB, CAL_WRITE_KIB = 131089.0, 262144.0
 
@@ -211,24 +213,30 @@ def main():
     loss = float(out.loss.item())
     clamped = int(out.clamped.item())
 
-    # Roofline of the dominant kernel, the Hessian SYRK. Timed per hessian_accum
-    # call (events on the stream the kernels run on); one call is k_syrk_full
-    # plus, when the tile count is not a whole number of rounds, the split-K
-    # pair k_syrk_split + k_syrk_reduce for the leftover tiles.
+    # Roofline of the kernel with the most time per step, the Hessian SYRK (two
+    # calls per step). Timed per hessian_accum call (events on the stream the
+    # kernels run on); one call is the k_split3 pre-pass, k_syrk3_full and, when
+    # the tile count is not a whole number of rounds, the split-K pair
+    # k_syrk3_split + k_syrk_reduce for the leftover tiles.
     syrk_ms = float(np.mean(ev["hess_I"] + ev["hess_O"]))
-    # algorithmic flops per call, averaged over the two calls: T d^2 per factor
-    # (the upper half, T d^2 / 2 FMAs at 2 flops each)
+    # algorithmic fp32 flops per call, averaged over the two calls: T d^2 per
+    # factor (the upper half, T d^2 / 2 FMAs at 2 flops each); the matrix cores
+    # run six bf16 piece products for each
     syrk_flops = float(T) * (n * n + m * m) / 2.0
     solve_flops = float(m) * n * (m + n)            # far-field feedback, minimal
     dominant = max(ph, key=ph.get)
+    fp32_equiv = syrk_flops / (syrk_ms * 1e-3) / 1e12
     roof = {
-        "kernel": "hessian_accum: k_syrk_full (+ k_syrk_split, k_syrk_reduce), fp32 MFMA",
+        "kernel": "hessian_accum: k_split3 + k_syrk3_full (+ k_syrk3_split, k_syrk_reduce), "
+                  "bf16 MFMA, six piece products per fp32 product",
         "bound": "mfma",
-        "achieved": syrk_flops / (syrk_ms * 1e-3) / 1e12,
-        "peak": PEAK_FP32_MFMA_TFLOPS,
+        "achieved": PIECE_PRODUCTS * fp32_equiv,
+        "peak": PEAK_BF16_MFMA_TFLOPS,
         "unit": "TFLOP/s",
         "traffic": syrk_traffic_bytes(args.workload),
-        "flops_per_call": syrk_flops,
+        "flops_per_call": PIECE_PRODUCTS * syrk_flops,
+        "fp32_equiv_tflops": fp32_equiv,
+        "fp32_equiv_frac_of_fp32_peak": fp32_equiv / PEAK_FP32_MFMA_TFLOPS,
     }
     roof["frac"] = roof["achieved"] / roof["peak"]
 
@@ -244,6 +252,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "dtype_detail": "Hessian: fp32 products as six bf16 piece products, fp32 accumulate; "
+                        "LDL: fp64; solve: fp32",
         "data": "synthetic",
         "config": {"workload": "%s, %d-bit %s" % (WORKLOAD_LABEL[args.workload], args.bits,
                                                   args.rounding),

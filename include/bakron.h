@@ -89,10 +89,23 @@ const char* bakron_status_str(int status);
  *   For H = X^T X / T pass alpha = 1/T, beta = 0; to accumulate over token
  *   chunks call again with beta = 1 and alpha = 1/T_total.
  *   T == 0 scales H by beta.
- *   ws: optional device workspace of bakron_hessian_accum_workspace_bytes(T, d)
- *      bytes, used to split the last round of output tiles over T so the GPU
- *      stays busy; with ws == NULL (or too small) the call is still correct,
- *      only that split is skipped. The result does not depend on it.
+ *   ws: optional device workspace; its size picks the arithmetic.
+ *      - At least bakron_hessian_accum_workspace_bytes(T, d) bytes: the
+ *        product runs on the bf16 matrix cores. X is first cut into three
+ *        bf16 pieces per element (x = h + m + l to within 2^-24 |x|), stored
+ *        in ws: 6 bytes per element of X, with T padded to a multiple of 32
+ *        and d to a multiple of 128. Each product is then the sum of six
+ *        piece products (hh, hm, mh, hl, lh, mm), accumulated in fp32. The
+ *        terms left out are below 2^-23 |x y|, so the error is of the order
+ *        of an fp32 product's. The remainder of ws (after the pieces,
+ *        256-byte aligned) holds the split-K partials of a short last round
+ *        of output tiles.
+ *      - NULL or smaller: the product runs on the fp32 matrix cores (about
+ *        2.5x slower at d = 4096). A workspace too small for the pieces is
+ *        still used for those split-K partials if it is large enough.
+ *      Both paths are within fp32 rounding of X^T X, but their results are
+ *      not bit-identical. For a given device, T, d and path the result is
+ *      deterministic.
  * Errors: INVALID_ARG for NULL X (T > 0) or H, d <= 0, T < 0, bad ld.
  */
 size_t bakron_hessian_accum_workspace_bytes(int64_t T, int64_t d);

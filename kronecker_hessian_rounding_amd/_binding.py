@@ -142,8 +142,13 @@ def _aux_stream(device) -> torch.cuda.Stream:
 
 # --------------------------------------------------------------------------
 def hessian_accum(X: torch.Tensor, H: Optional[torch.Tensor] = None, alpha: Optional[float] = None,
-                  beta: float = 0.0) -> torch.Tensor:
-    """H <- beta H + alpha X^T X (default alpha = 1/T), fp32 MFMA on the device."""
+                  beta: float = 0.0, pieces: bool = True) -> torch.Tensor:
+    """H <- beta H + alpha X^T X (default alpha = 1/T) on the device.
+
+    pieces=True passes the full workspace: each fp32 product is formed from three
+    bf16 pieces per operand on the bf16 matrix cores. pieces=False passes none,
+    which selects the fp32 matrix-core path.
+    """
     ldx = _mat(X, "X")
     T, d = X.shape
     if H is None:
@@ -153,7 +158,7 @@ def hessian_accum(X: torch.Tensor, H: Optional[torch.Tensor] = None, alpha: Opti
         raise ValueError("H must be %d x %d" % (d, d))
     if alpha is None:
         alpha = 1.0 / max(T, 1)
-    nb = LIB.bakron_hessian_accum_workspace_bytes(T, d)
+    nb = LIB.bakron_hessian_accum_workspace_bytes(T, d) if pieces else 0
     ws = _workspace(nb, X.device)
     _check("bakron_hessian_accum",
            LIB.bakron_hessian_accum(_ptr(X), T, d, ldx, alpha, beta, _ptr(H), ldh, _ptr(ws), nb,

@@ -52,15 +52,60 @@ union SyrkShared {
     SyrkRing ring;
 };
 
-// tile id -> (bi, bj), bi <= bj, row-major over the upper triangle of nb x nb tiles
+// Tile order. The upper triangle of nb x nb tiles is cut into g x g super-tiles
+// (g = kSuper128), taken super-row by super-row, each super-row starting with its
+// diagonal super-tile; inside a super-tile the tiles go row by row. Tiles that are
+// close in this order share their operand panels (columns of X), so a run of them
+// on one XCD reads about 2g panels per k-slice through that XCD's L2 instead of
+// all nb.
+constexpr int64_t kSuper128 = 8;
+constexpr int kXcds = 8;  // workgroup b of a launch is placed on XCD b mod 8
+
+// tile id -> (bi, bj), bi <= bj
 __device__ __forceinline__ void upper_tile(int64_t id, int64_t nb, int64_t& bi, int64_t& bj) {
-    auto start = [nb](int64_t b) { return b * (2 * nb - b + 1) / 2; };
-    const double q = (double)(2 * nb + 1);
-    bi = (int64_t)((q - sqrt(q * q - 8.0 * (double)id)) * 0.5);
-    if (bi < 0) bi = 0;
-    while (bi + 1 < nb && start(bi + 1) <= id) ++bi;
-    while (bi > 0 && start(bi) > id) --bi;
-    bj = bi + (id - start(bi));
+    constexpr int64_t g = kSuper128;
+    int64_t s0 = 0;  // first tile-row of the super-row
+    for (;;) {
+        const int64_t r = min(g, nb - s0);
+        const int64_t tri = r * (r + 1) / 2;
+        const int64_t row = tri + r * (nb - s0 - r);
+        if (id < row || s0 + r >= nb) {
+            if (id < tri) {  // the diagonal super-tile, row by row
+                int64_t i = 0;
+                while (id >= r - i) {
+                    id -= r - i;
+                    ++i;
+                }
+                bi = s0 + i;
+                bj = bi + id;
+            } else {  // an off-diagonal super-tile of r rows and c columns
+                id -= tri;
+                int64_t c0 = s0 + r;
+                for (;;) {
+                    const int64_t c = min(g, nb - c0);
+                    if (id < r * c) {
+                        bi = s0 + id / c;
+                        bj = c0 + id % c;
+                        break;
+                    }
+                    id -= r * c;
+                    c0 += c;
+                }
+            }
+            return;
+        }
+        id -= row;
+        s0 += r;
+    }
+}
+
+// Workgroup b of an n-workgroup launch -> its place in [0, n): XCD x takes the
+// x-th contiguous run of the order, so the workgroups resident on one XCD at a
+// time hold neighbouring tiles.
+__device__ __forceinline__ int64_t xcd_rank(int64_t b, int64_t n) {
+    const int64_t x = b % kXcds;
+    const int64_t q = n / kXcds, rr = n % kXcds;
+    return x * q + min(x, rr) + b / kXcds;
 }
 
 // Thread t loads rows k0 + (t >> 5) + 8 h (h = 0..3), columns 4 (t & 31)..+3
@@ -274,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void k_syrk_full(const float* __restrict_
                                                         int64_t ldh, int64_t nb, int64_t tile_beg) {
     __shared__ SyrkShared sm;
     int64_t bi, bj;
-    upper_tile(tile_beg + blockIdx.x, nb, bi, bj);
+    upper_tile(tile_beg + xcd_rank(blockIdx.x, gridDim.x), nb, bi, bj);
     const int R = (int)min<int64_t>(kT128, d - bi * kT128);
     const int Cn = (int)min<int64_t>(kT128, d - bj * kT128);
     f32x16 acc[2][2];
@@ -351,25 +396,285 @@ __global__ __launch_bounds__(kThreads) void k_syrk_reduce(int64_t d, float alpha
     }
 }
 
-namespace {
-int resident_slots() {
-    static int slots = 0;
-    if (slots == 0) {
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
-        slots = 2 * cus;  // two 64 KB-LDS workgroups per CU
+// ---------------------------------------------------------------------------
+// The three-piece bf16 path.
+//
+// The gfx950 matrix cores multiply bf16 pairs at sixteen times their fp32 rate.
+// Each x of X is cut into three bf16 pieces, h = bf16(x), m = bf16(x - h) and
+// l = bf16(x - h - m), rounding to nearest even; both differences are exact in
+// fp32, and |x - (h + m + l)| <= 2^-24 |x|, so the pieces hold x to fp32
+// precision. A product x y is taken as hh' + hm' + mh' + hl' + lh' + mm'; the
+// terms left out (ml' + lm' + ll') are below 2^-23 |x y|. The bf16 products are
+// exact in fp32 and add into fp32 accumulators, so the sum carries errors of
+// the order of the fp32 product's, for six matrix-core passes at a sixteenth of
+// the cost each.
+//
+// A pre-pass writes the pieces in the order the MFMA reads them: for each group
+// g of 8 consecutive tokens and each column c, the 8 bf16 values of that column
+// (16 bytes), piece planes apart: Xs[piece][g][c][0..7]. The tokens are padded
+// with zeros to a whole number of stages and the columns to whole 128-wide
+// tiles, so every tile streams whole 2 KB rows of Xs straight into LDS.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+#ifndef BK_S3_KB
+#define BK_S3_KB 1
+#endif
+#ifndef BK_S3_NS
+#define BK_S3_NS 3
+#endif
+constexpr int kS3KB = BK_S3_KB;  // 16-token blocks per stage
+constexpr int kS3NS = BK_S3_NS;  // stages in the ring: loads run kS3NS - 1 stages ahead
+constexpr int64_t kS3Pad = 32;   // tokens are padded to a multiple of this (a multiple of 16 kS3KB)
+static_assert(kS3Pad % (16 * kS3KB) == 0, "whole stages");
+
+struct Split3Shape {
+    int64_t ng;  // groups of 8 tokens (padded)
+    int64_t dp;  // columns (padded to whole tiles)
+    int64_t nstage;
+    size_t bytes;
+};
+inline Split3Shape split3_shape(int64_t T, int64_t d) {
+    Split3Shape s;
+    const int64_t Tp = (T + kS3Pad - 1) / kS3Pad * kS3Pad;
+    s.ng = Tp / 8;
+    s.dp = (d + kT128 - 1) / kT128 * kT128;
+    s.nstage = Tp / (16 * kS3KB);
+    s.bytes = align256((size_t)3 * (size_t)Tp * (size_t)s.dp * 2);
+    return s;
+}
+
+// bf16 bits of x, rounded to nearest even; infinities stay, NaNs stay NaN
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7f800000u) == 0x7f800000u) return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_value(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Thread (c, g): column c of tokens 8 g .. 8 g + 7 into the three planes.
+__global__ __launch_bounds__(kThreads) void k_split3(const float* __restrict__ X, int64_t T,
+                                                     int64_t d, int64_t ldx, int64_t ng,
+                                                     int64_t dp, uint4* __restrict__ Xs) {
+    const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (c >= dp) return;
+    for (int64_t g = blockIdx.y; g < ng; g += gridDim.y) {
+        uint32_t pk[3][4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            uint32_t b[3][2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int64_t k = 8 * g + e + q;
+                const float x = (k < T && c < d) ? X[k * ldx + c] : 0.0f;
+                b[0][q] = bf16_bits(x);
+                const float r1 = x - bf16_value(b[0][q]);
+                b[1][q] = bf16_bits(r1);
+                b[2][q] = bf16_bits(r1 - bf16_value(b[1][q]));
+            }
+#pragma unroll
+            for (int p = 0; p < 3; ++p) pk[p][e >> 1] = (b[p][0] & 0xffffu) | (b[p][1] << 16);
+        }
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+            Xs[((int64_t)p * ng + g) * dp + c] = uint4{pk[p][0], pk[p][1], pk[p][2], pk[p][3]};
     }
-    return slots;
+}
+
+// One ring stage of both operands: [piece][16-token block][token half][column].
+struct Split3Stage {
+    bf16x8 v[3][kS3KB][2][kT128];
+};
+struct Split3Ring {
+    Split3Stage a[kS3NS];
+    Split3Stage b[kS3NS];
+};
+
+// The 24 MFMAs of one 16-token block, per wave quadrant (rows wr.., columns wc..):
+// six piece products for each of the four 32 x 32 blocks, the four blocks
+// interleaved so that no MFMA waits on the one before it.
+__device__ __forceinline__ void split3_block(const bf16x8 (&fa)[3][2], const bf16x8 (&fb)[3][2],
+                                             f32x16 (&acc)[2][2]) {
+    constexpr int kPa[6] = {1, 0, 2, 0, 1, 0};
+    constexpr int kPb[6] = {1, 2, 0, 1, 0, 0};
+#pragma unroll
+    for (int t = 0; t < 6; ++t)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+                acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kPa[t]][rb], fb[kPb[t]][cb],
+                                                                      acc[rb][cb], 0, 0, 0);
+}
+
+// The MFMAs of one stage; the operands of block kb + 1 are read from LDS before
+// the MFMAs of block kb issue.
+template <typename F>
+__device__ __forceinline__ void split3_stage(const Split3Stage& a, const Split3Stage& b, int wr,
+                                             int wc, int lane, f32x16 (&acc)[2][2], F&& after_reads) {
+    const int kh = lane >> 5, l31 = lane & 31;
+    bf16x8 fa[2][3][2], fb[2][3][2];
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            fa[0][p][h] = a.v[p][0][kh][wr + 32 * h + l31];
+            fb[0][p][h] = b.v[p][0][kh][wc + 32 * h + l31];
+        }
+    after_reads();  // the next stage's loads go out behind this stage's first reads
+#pragma unroll
+    for (int kb = 0; kb < kS3KB; ++kb) {
+        const int cur = kb & 1;
+        if (kb + 1 < kS3KB) {
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    fa[cur ^ 1][p][h] = a.v[p][kb + 1][kh][wr + 32 * h + l31];
+                    fb[cur ^ 1][p][h] = b.v[p][kb + 1][kh][wc + 32 * h + l31];
+                }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of this block's MFMAs
+        split3_block(fa[cur], fb[cur], acc);
+    }
+}
+
+// Stages [s_beg, s_end) of tile columns (ca.., cb..): stage s goes to ring slot
+// s mod kS3NS; at the top of stage s the loads of stage s + kS3NS - 1 go out into
+// the slot every wave finished reading in stage s - 1 (as in syrk_tile_ring).
+__device__ __forceinline__ void split3_tile(const uint4* __restrict__ Xs, int64_t ng, int64_t dp,
+                                            int64_t ca, int64_t cb, int64_t s_beg, int64_t s_end,
+                                            f32x16 (&acc)[2][2], Split3Ring& sm) {
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = (w >> 1) * 64, wc = (w & 1) * 64;
+    constexpr int kRows = 3 * kS3KB * 2 * 2;  // 1 KB rows per operand per stage
+    constexpr int kPerWave = kRows / 4;
+    constexpr int kLoads = 2 * kPerWave;      // direct loads per wave per stage
+    const int64_t ns = s_end - s_beg;
+    auto issue = [&](int64_t s) {
+        const int slot = (int)(s % kS3NS);
+        const int64_t kb0 = (s_beg + s) * kS3KB;
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i) {
+            const int q = w + 4 * i;
+            const int half = q & 1, th = (q >> 1) & 1, kbl = (q >> 2) % kS3KB, p = (q >> 2) / kS3KB;
+            const int64_t g = 2 * (kb0 + kbl) + th;
+            const uint4* row = Xs + ((int64_t)p * ng + g) * dp + 64 * half + lane;
+            __builtin_amdgcn_global_load_lds(row + ca, &sm.a[slot].v[p][kbl][th][64 * half], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(row + cb, &sm.b[slot].v[p][kbl][th][64 * half], 16, 0, 0);
+        }
+    };
+    for (int s = 0; s < kS3NS - 1; ++s)
+        if (s < ns) issue(s);
+    for (int64_t it = 0; it < ns; ++it) {
+        if (it + kS3NS - 2 < ns) vm_wait_barrier<(kS3NS - 2) * kLoads>();
+        else vm_wait_barrier<0>();
+        const int slot = (int)(it % kS3NS);
+        split3_stage(sm.a[slot], sm.b[slot], wr, wc, lane, acc, [&] {
+            if (it + kS3NS - 1 < ns) issue(it + kS3NS - 1);
+        });
+    }
+}
+
+// Whole tiles [tile_beg, tile_beg + gridDim.x) over all stages.
+__global__ __launch_bounds__(kThreads) void k_syrk3_full(const uint4* __restrict__ Xs, int64_t ng,
+                                                         int64_t dp, int64_t nstage, int64_t d,
+                                                         float alpha, float beta, float* __restrict__ H,
+                                                         int64_t ldh, int64_t nb, int64_t tile_beg) {
+    __shared__ Split3Ring sm;
+    int64_t bi, bj;
+    upper_tile(tile_beg + xcd_rank(blockIdx.x, gridDim.x), nb, bi, bj);
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+    split3_tile(Xs, ng, dp, bi * kT128, bj * kT128, 0, nstage, acc, sm);
+    syrk_write(H, ldh, d, bi, bj, alpha, beta, acc);
+}
+
+// Tiles [tile_beg, tile_beg + ntiles), each split into nsplit stage ranges; block
+// (tile u, split s) writes its raw 128x128 partial to part[(u * nsplit + s)].
+__global__ __launch_bounds__(kThreads) void k_syrk3_split(const uint4* __restrict__ Xs, int64_t ng,
+                                                          int64_t dp, int64_t nstage, int64_t nb,
+                                                          int64_t tile_beg, int nsplit,
+                                                          float* __restrict__ part) {
+    __shared__ Split3Ring sm;
+    const int u = blockIdx.x / nsplit, sp = blockIdx.x % nsplit;
+    int64_t bi, bj;
+    upper_tile(tile_beg + u, nb, bi, bj);
+    const int64_t per = (nstage + nsplit - 1) / nsplit;
+    const int64_t sb = std::min<int64_t>(nstage, (int64_t)sp * per);
+    const int64_t se = std::min<int64_t>(nstage, sb + per);
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+    split3_tile(Xs, ng, dp, bi * kT128, bj * kT128, sb, se, acc, sm);
+    float* out = part + (size_t)blockIdx.x * kT128 * kT128;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            const int c = syrk_col(cb);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) out[syrk_row(rb, v) * kT128 + c] = acc[rb][cb][v];
+        }
+}
+
+namespace {
+// workgroups resident at once: LDS-limited per CU (160 KB)
+int resident_slots(size_t lds_bytes) {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cus = n;
+    }
+    return cus * std::max<int>(1, (int)((160 * 1024) / lds_bytes));
+}
+
+// Whole rounds of P tiles over the full K; a short last round is split over K
+// into at most P workgroups (at least 8 K-units each), if the partials fit in
+// `room` bytes; otherwise it runs whole.
+struct SyrkPlan {
+    int64_t full, rem;
+    int nsplit;
+};
+SyrkPlan plan_tiles(int64_t tiles, int64_t P, int64_t kunits, size_t room) {
+    SyrkPlan pl;
+    pl.full = (tiles / P) * P;
+    pl.rem = tiles - pl.full;
+    pl.nsplit = 1;
+    if (pl.rem > P / 2) {  // a well-filled last round: run it whole too
+        pl.full = tiles;
+        pl.rem = 0;
+    }
+    if (pl.rem > 0) {
+        pl.nsplit = (int)std::min<int64_t>(P / pl.rem, kunits / 8);
+        const size_t need = sizeof(float) * (size_t)pl.rem * (size_t)std::max(pl.nsplit, 1) * kT128 * kT128;
+        if (pl.nsplit < 2 || room < need) {  // no split possible
+            pl.full = tiles;
+            pl.rem = 0;
+            pl.nsplit = 1;
+        }
+    }
+    return pl;
 }
 }  // namespace
 
 size_t hessian_workspace_bytes(int64_t T, int64_t d) {
-    (void)T;
-    (void)d;
-    return sizeof(float) * (size_t)resident_slots() * kT128 * kT128;
+    const size_t part = sizeof(float) * kT128 * kT128 *
+                        (size_t)std::max(resident_slots(sizeof(SyrkShared)), resident_slots(sizeof(Split3Ring)));
+    return split3_shape(T, d).bytes + part;
 }
 
 int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, float alpha,
@@ -378,30 +683,43 @@ int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, floa
     const int64_t nb = (d + kT128 - 1) / kT128;
     const int64_t tiles = nb * (nb + 1) / 2;
     if (tiles > 0x7fffffff) return BAKRON_E_INVALID_ARG;
-    const int64_t P = resident_slots();
-    int64_t full = (tiles / P) * P;  // whole rounds over the full K
-    int64_t rem = tiles - full;
-    if (rem > P / 2) {  // a well-filled last round: run it whole too
-        full = tiles;
-        rem = 0;
+    const Split3Shape sh = split3_shape(T, d);
+    if (ws != nullptr && ws_bytes >= sh.bytes) {
+        // the three-piece bf16 path
+        uint4* Xs = (uint4*)ws;
+        if (sh.ng > 0) {
+            const unsigned gy = (unsigned)std::min<int64_t>(sh.ng, 65535);
+            hipLaunchKernelGGL(k_split3, dim3((unsigned)(sh.dp / kThreads + (sh.dp % kThreads != 0)), gy),
+                               dim3(kThreads), 0, stream, X, T, d, ldx, sh.ng, sh.dp, Xs);
+        }
+        const SyrkPlan pl = plan_tiles(tiles, resident_slots(sizeof(Split3Ring)), sh.nstage,
+                                       ws_bytes - sh.bytes);
+        if (pl.full > 0)
+            hipLaunchKernelGGL(k_syrk3_full, dim3((unsigned)pl.full), dim3(kThreads), 0, stream, Xs,
+                               sh.ng, sh.dp, sh.nstage, d, alpha, beta, H, ldh, nb, (int64_t)0);
+        if (pl.rem > 0) {
+            float* part = (float*)((char*)ws + sh.bytes);
+            hipLaunchKernelGGL(k_syrk3_split, dim3((unsigned)(pl.rem * pl.nsplit)), dim3(kThreads), 0,
+                               stream, Xs, sh.ng, sh.dp, sh.nstage, nb, pl.full, pl.nsplit, part);
+            hipLaunchKernelGGL(k_syrk_reduce, dim3((unsigned)pl.rem, kT128 / 8), dim3(kThreads), 0, stream,
+                               d, alpha, beta, H, ldh, nb, pl.full, pl.nsplit, (const float*)part);
+        }
+        return hipGetLastError() == hipSuccess ? BAKRON_OK : BAKRON_E_DEVICE;
     }
+    // the fp32-MFMA path (no room for the pieces)
     const int64_t nsl = (T + kSyKT - 1) / kSyKT;
-    int nsplit = rem > 0 ? (int)std::min<int64_t>(P / rem, nsl / 8) : 1;
-    const size_t need = sizeof(float) * (size_t)rem * (size_t)std::max(nsplit, 1) * kT128 * kT128;
-    if (rem > 0 && (nsplit < 2 || ws == nullptr || ws_bytes < need)) {  // no split possible
-        full = tiles;
-        rem = 0;
-    }
-    if (full > 0) {
-        hipLaunchKernelGGL(k_syrk_full, dim3((unsigned)full), dim3(kThreads), 0, stream, X, T, d,
+    const SyrkPlan pl = plan_tiles(tiles, resident_slots(sizeof(SyrkShared)), nsl,
+                                   ws != nullptr ? ws_bytes : 0);
+    if (pl.full > 0) {
+        hipLaunchKernelGGL(k_syrk_full, dim3((unsigned)pl.full), dim3(kThreads), 0, stream, X, T, d,
                            ldx, alpha, beta, H, ldh, nb, (int64_t)0);
     }
-    if (rem > 0) {
+    if (pl.rem > 0) {
         float* part = (float*)ws;
-        hipLaunchKernelGGL(k_syrk_split, dim3((unsigned)(rem * nsplit)), dim3(kThreads), 0, stream,
-                           X, T, d, ldx, nb, full, nsplit, part);
-        hipLaunchKernelGGL(k_syrk_reduce, dim3((unsigned)rem, kT128 / 8), dim3(kThreads), 0, stream, d, alpha,
-                           beta, H, ldh, nb, full, nsplit, (const float*)part);
+        hipLaunchKernelGGL(k_syrk_split, dim3((unsigned)(pl.rem * pl.nsplit)), dim3(kThreads), 0, stream,
+                           X, T, d, ldx, nb, pl.full, pl.nsplit, part);
+        hipLaunchKernelGGL(k_syrk_reduce, dim3((unsigned)pl.rem, kT128 / 8), dim3(kThreads), 0, stream, d, alpha,
+                           beta, H, ldh, nb, pl.full, pl.nsplit, (const float*)part);
     }
     return hipGetLastError() == hipSuccess ? BAKRON_OK : BAKRON_E_DEVICE;
 }

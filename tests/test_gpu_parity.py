@@ -109,17 +109,23 @@ def check_solve(bk, w, LO, LI, DO, DI, bits, rounding="nearest", seed=0, row_sca
 # ----------------------------------------------------------------------------
 # Hessian factor accumulation
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("T,d", [(1024, 64), (333, 100), (8192, 512), (1, 5), (2000, 129), (0, 7)])
-def test_hessian_accum_matches_oracle(bk, T, d):
-    note("hessian T=%d d=%d" % (T, d))
+# pieces=True: three bf16 pieces per element on the bf16 matrix cores (the default);
+# pieces=False: the fp32 matrix-core path. Both are held to the same fp32 bound.
+@pytest.mark.parametrize("pieces", [True, False])
+@pytest.mark.parametrize("T,d", [(1024, 64), (333, 100), (8192, 512), (1, 5), (2000, 129), (0, 7),
+                                 (4000, 2907)])
+def test_hessian_accum_matches_oracle(bk, T, d, pieces):
+    # (4000, 2907): 276 output tiles of 128, so the last short round is split over
+    # the tokens into partials; ragged in both T and d
+    note("hessian T=%d d=%d pieces=%s" % (T, d, pieces))
     x = workloads.make_x(max(T, 1), d, 99 + d, "gauss", 2 if d > 2 else 0)[:T]
     X = torch.from_numpy(np.ascontiguousarray(x)).to(dev())
     if T == 0:
         H = torch.full((d, d), 3.0, device=dev())
-        bk.hessian_accum(X, H, alpha=1.0, beta=0.5)
+        bk.hessian_accum(X, H, alpha=1.0, beta=0.5, pieces=pieces)
         assert torch.all(H.cpu() == 1.5)
         return
-    H = bk.hessian_accum(X).cpu().numpy()
+    H = bk.hessian_accum(X, pieces=pieces).cpu().numpy()
     assert np.array_equal(H, H.T)
     ref = oracle.hessian(x)
     ax = np.abs(x.astype(np.float64))
@@ -127,34 +133,36 @@ def test_hessian_accum_matches_oracle(bk, T, d):
     assert np.all(np.abs(H - ref) <= bound), np.max(np.abs(H - ref) / bound)
 
 
-def test_hessian_accum_chunks_and_strides(bk):
-    note("hessian chunked + strided")
+@pytest.mark.parametrize("pieces", [True, False])
+def test_hessian_accum_chunks_and_strides(bk, pieces):
+    note("hessian chunked + strided pieces=%s" % pieces)
     x = workloads.make_x(3000, 96, 5, "gauss", 2)
     big = np.zeros((3000, 128), dtype=np.float32)
     big[:, :96] = x
     Xb = torch.from_numpy(big).to(dev())
     Xv = Xb[:, :96]  # leading dimension 128
     H = torch.empty((96, 96), device=dev())
-    bk.hessian_accum(Xv[:1000], H, alpha=1.0 / 3000, beta=0.0)
-    bk.hessian_accum(Xv[1000:], H, alpha=1.0 / 3000, beta=1.0)
+    bk.hessian_accum(Xv[:1000], H, alpha=1.0 / 3000, beta=0.0, pieces=pieces)
+    bk.hessian_accum(Xv[1000:], H, alpha=1.0 / 3000, beta=1.0, pieces=pieces)
     ref = oracle.hessian(x)
     ax = np.abs(x.astype(np.float64))
     bound = 8 * U32 * np.sqrt(3000) * (ax.T @ ax) / 3000
     assert np.all(np.abs(H.cpu().numpy() - ref) <= bound)
 
 
+@pytest.mark.parametrize("pieces", [True, False])
 @pytest.mark.parametrize("off", [4, 1])
-def test_hessian_accum_strided_whole_tiles(bk, off):
-    # a 256-column view of a wider buffer: at a 16-byte offset the whole 128x128 tiles
-    # stream their k-slices straight into LDS; at a 4-byte offset they take the
-    # register path. T is odd, so the last k-slice is partial either way.
-    note("hessian strided whole tiles, column offset %d" % off)
+def test_hessian_accum_strided_whole_tiles(bk, off, pieces):
+    # a 256-column view of a wider buffer. On the fp32 path, at a 16-byte offset the
+    # whole 128x128 tiles stream their k-slices straight into LDS; at a 4-byte offset
+    # they take the register path. T is odd, so the last k-slice is partial either way.
+    note("hessian strided whole tiles, column offset %d pieces=%s" % (off, pieces))
     T, d = 4133, 256
     x = workloads.make_x(T, d, 17 + off, "gauss", 2)
     big = np.zeros((T, d + 8), dtype=np.float32)
     big[:, off:off + d] = x
     Xb = torch.from_numpy(big).to(dev())
-    H = bk.hessian_accum(Xb[:, off:off + d]).cpu().numpy()
+    H = bk.hessian_accum(Xb[:, off:off + d], pieces=pieces).cpu().numpy()
     assert np.array_equal(H, H.T)
     ref = oracle.hessian(x)
     ax = np.abs(x.astype(np.float64))
