@@ -452,32 +452,68 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
 }
 __device__ __forceinline__ float bf16_value(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Thread (c, g): column c of tokens 8 g .. 8 g + 7 into the three planes.
+// the three pieces of x, as bf16 bits
+__device__ __forceinline__ void split3_value(float x, uint32_t& h, uint32_t& m, uint32_t& l) {
+    h = bf16_bits(x);
+    const float r1 = x - bf16_value(h);
+    m = bf16_bits(r1);
+    l = bf16_bits(r1 - bf16_value(m));
+}
+
+// Block (x, g): columns 1024 x .. 1024 x + 1023 of tokens 8 g .. 8 g + 7 into the
+// three planes, through LDS. Each row is read as 16-byte vectors where four
+// columns lie inside [0, d) and X allows it (kVec), element by element
+// otherwise; thread t then splits columns t, t + 256, t + 512, t + 768, so each
+// store instruction writes 1 KB of consecutive 16-byte units of a plane.
+constexpr int kSplitCols = 4 * kThreads;
+template <bool kVec>
 __global__ __launch_bounds__(kThreads) void k_split3(const float* __restrict__ X, int64_t T,
                                                      int64_t d, int64_t ldx, int64_t ng,
                                                      int64_t dp, uint4* __restrict__ Xs) {
-    const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (c >= dp) return;
+    __shared__ float tile[8][kSplitCols];
+    const int t = threadIdx.x;
+    const int64_t cb = (int64_t)blockIdx.x * kSplitCols;
+    const int64_t c4 = cb + 4 * t;  // this thread's four columns on the read side
+    const bool vec = kVec && c4 + 4 <= d;
     for (int64_t g = blockIdx.y; g < ng; g += gridDim.y) {
-        uint32_t pk[3][4];
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-            uint32_t b[3][2];
+        for (int e = 0; e < 8; ++e) {
+            const int64_t k = 8 * g + e;
+            const float* row = X + k * ldx + c4;
+            f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (k < T) {
+                if (vec) {
+                    v = *reinterpret_cast<const f32x4*>(row);
+                } else {
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int64_t k = 8 * g + e + q;
-                const float x = (k < T && c < d) ? X[k * ldx + c] : 0.0f;
-                b[0][q] = bf16_bits(x);
-                const float r1 = x - bf16_value(b[0][q]);
-                b[1][q] = bf16_bits(r1);
-                b[2][q] = bf16_bits(r1 - bf16_value(b[1][q]));
+                    for (int j = 0; j < 4; ++j)
+                        if (c4 + j < d) v[j] = row[j];
+                }
             }
-#pragma unroll
-            for (int p = 0; p < 3; ++p) pk[p][e >> 1] = (b[p][0] & 0xffffu) | (b[p][1] << 16);
+            *reinterpret_cast<f32x4*>(&tile[e][4 * t]) = v;
         }
+        __syncthreads();
 #pragma unroll
-        for (int p = 0; p < 3; ++p)
-            Xs[((int64_t)p * ng + g) * dp + c] = uint4{pk[p][0], pk[p][1], pk[p][2], pk[p][3]};
+        for (int q = 0; q < 4; ++q) {
+            const int cl = t + kThreads * q;
+            const int64_t c = cb + cl;
+            uint32_t pk[3][4];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                uint32_t h0, m0, l0, h1, m1, l1;
+                split3_value(tile[e][cl], h0, m0, l0);
+                split3_value(tile[e + 1][cl], h1, m1, l1);
+                pk[0][e >> 1] = (h0 & 0xffffu) | (h1 << 16);
+                pk[1][e >> 1] = (m0 & 0xffffu) | (m1 << 16);
+                pk[2][e >> 1] = (l0 & 0xffffu) | (l1 << 16);
+            }
+            if (c < dp) {
+#pragma unroll
+                for (int p = 0; p < 3; ++p)
+                    Xs[((int64_t)p * ng + g) * dp + c] = uint4{pk[p][0], pk[p][1], pk[p][2], pk[p][3]};
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -689,8 +725,12 @@ int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, floa
         uint4* Xs = (uint4*)ws;
         if (sh.ng > 0) {
             const unsigned gy = (unsigned)std::min<int64_t>(sh.ng, 65535);
-            hipLaunchKernelGGL(k_split3, dim3((unsigned)(sh.dp / kThreads + (sh.dp % kThreads != 0)), gy),
-                               dim3(kThreads), 0, stream, X, T, d, ldx, sh.ng, sh.dp, Xs);
+            const dim3 grid((unsigned)((sh.dp + kSplitCols - 1) / kSplitCols), gy);
+            const bool vec = (ldx & 3) == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0;
+            if (vec)
+                hipLaunchKernelGGL(k_split3<true>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, sh.ng, sh.dp, Xs);
+            else
+                hipLaunchKernelGGL(k_split3<false>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, sh.ng, sh.dp, Xs);
         }
         const SyrkPlan pl = plan_tiles(tiles, resident_slots(sizeof(Split3Ring)), sh.nstage,
                                        ws_bytes - sh.bytes);
