@@ -4,7 +4,7 @@ The computation runs in libbakron (HIP kernels for gfx950, C ABI in
 include/bakron.h); this package is a thin ctypes binding that takes PyTorch
 tensors for device memory and uses the current stream.
 
-  hessian_accum(X)            H <- beta H + alpha X^T X            (fp32 MFMA)
+  hessian_accum(X)            H <- beta H + alpha X^T X            (bf16 pieces, fp32 accuracy)
   ldl(H, damp_rel)            H + lambda I = (L + I) D (L + I)^T   (fp64, L strictly upper)
   ldl_pair(HA, HB, damp_rel)  two independent factorisations side by side on two streams
   solve(W, L_O, L_I, bits)    BaKron rounding: codes, scales, error, proxy loss

@@ -1,4 +1,4 @@
-// bk_accum.hip -- Hessian factor accumulation H <- beta H + alpha X^T X (fp32 MFMA).
+// bk_accum.hip -- Hessian factor accumulation H <- beta H + alpha X^T X.
 //
 // The Kronecker factors are second moments over tokens: H_I = E[x^T x] of the
 // layer inputs and H_O = E[g^T g] of the output gradients (YAQA article,
@@ -9,15 +9,21 @@
 // tile, and a diagonal tile writes its upper half and mirrors it, so H is
 // exactly symmetric.
 //
-// Work balance: with P workgroups resident at once (two per CU), whole rounds
-// of P tiles run over the full K; the tiles left over after the last whole
-// round (or all tiles, when there are fewer than P) are split over K into
-// partials that a second kernel adds in a fixed order, so the result does not
-// depend on scheduling.
+// Two arithmetic paths, picked by the workspace the caller passes:
+//  * three bf16 pieces per element on the bf16 matrix cores (the piece path,
+//    below k_syrk_reduce), when the workspace holds the pieces;
+//  * fp32 MFMA otherwise.
+// Both keep the product to fp32 accuracy.
 //
-// Whole 128x128 tiles stream their 32-deep k-slices straight from global memory
-// into LDS (direct-to-LDS loads, one slice ahead); ragged tiles go through
-// registers with zero fill.
+// Work balance (both paths): with P workgroups resident at once (two per CU),
+// whole rounds of P tiles run over the full K; the tiles left over after the
+// last whole round (or all tiles, when there are fewer than P) are split over
+// K into partials that a second kernel adds in a fixed order, so the result
+// does not depend on scheduling.
+//
+// fp32 path: whole 128x128 tiles stream their 32-deep k-slices straight from
+// global memory into LDS (direct-to-LDS loads, one slice ahead); ragged tiles
+// go through registers with zero fill.
 #include <algorithm>
 
 #include "bk_common.hpp"
