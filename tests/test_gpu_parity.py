@@ -170,6 +170,29 @@ def test_hessian_accum_strided_whole_tiles(bk, off, pieces):
     assert np.all(np.abs(H - ref) <= bound), np.max(np.abs(H - ref) / bound)
 
 
+@pytest.mark.parametrize("pieces", [True, False])
+def test_hessian_accum_nonfinite_inputs_stay_in_their_rows(bk, pieces):
+    # An Inf and a NaN in X make every entry of their columns' rows and columns of H
+    # non-finite (NaN or Inf: the three-piece split of an Inf is Inf, NaN, NaN); every
+    # other entry keeps the usual fp32 bound.
+    note("hessian non-finite inputs pieces=%s" % pieces)
+    T, d = 700, 150
+    x = workloads.make_x(T, d, 31, "gauss", 2)
+    bad = [17, 140]
+    xb = x.copy()
+    xb[5, bad[0]] = np.inf
+    xb[600, bad[1]] = np.nan
+    H = bk.hessian_accum(torch.from_numpy(xb).to(dev()), pieces=pieces).cpu().numpy()
+    for c in bad:
+        assert not np.any(np.isfinite(H[c, :])) and not np.any(np.isfinite(H[:, c]))
+    keep = np.setdiff1d(np.arange(d), bad)
+    Hk = H[np.ix_(keep, keep)]
+    ref = oracle.hessian(x)[np.ix_(keep, keep)]
+    ax = np.abs(x[:, keep].astype(np.float64))
+    bound = 4 * U32 * np.sqrt(T) * (ax.T @ ax) / T
+    assert np.all(np.abs(Hk - ref) <= bound)
+
+
 # ----------------------------------------------------------------------------
 # damped LDL
 # ----------------------------------------------------------------------------
