@@ -21,6 +21,10 @@ Sources (cited by page title and section):
             divide-and-conquer), modular in the base quantiser.
   [KFAC-5]  K-FAC tutorial (www.mlqm.cn/news/1313094), section 5: the factor
             estimate A = X^T X / N plus a small multiple of the identity.
+  [KronQ]   "KronQ: Kronecker-factored Hessian LLM quantization" (ai-feeds.com),
+            method, "bidirectional incoherence processing": the random
+            rotation of the input side is extended to the output side,
+            W' = R_O W R_I^T.
 
 Readings where the pages are silent or garbled (each is listed in the design doc):
   * L is strictly UPPER and H = (L + I) D (L + I)^T (one paragraph says unit
@@ -32,6 +36,10 @@ Readings where the pages are silent or garbled (each is listed in the design doc):
     floor(y + 1/2), stochastic floor(y + u) with u from SplitMix64; both
     clamped to [0, Lq]; y = t / s_i + Lq / 2.
   * Damping adds 0.01 * mean(diag H) * I (mean over the undamped diagonal).
+  * The incoherence rotation (the pages name random rotations, not their
+    construction): for n = 2^k r with r odd, U_n = (I_r (x) H_{2^k} / sqrt(2^k))
+    diag(s), H the Sylvester Hadamard matrix, s_i = -1 if the top bit of
+    SplitMix64 output i of the seed is set, else +1.
 """
 from __future__ import annotations
 
@@ -45,7 +53,8 @@ from . import build as _build
 __all__ = [
     "hessian", "hessian_entries", "damp", "udu", "udu_lapack", "row_scales", "sweep",
     "replay", "replay_rows", "proxy_loss", "loss_identity", "bound_terms", "splitmix64",
-    "uniform_matrix", "pipeline",
+    "uniform_matrix", "pipeline", "rht_signs", "rht_block", "sylvester", "rht_matrix",
+    "rotate_layer",
 ]
 
 _lib = None
@@ -93,14 +102,20 @@ _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
 
-def uniform_matrix(seed: int, m: int, n: int) -> np.ndarray:
-    """u_ij = (splitmix64(seed, i*n + j) >> 40) * 2^-24 as an fp64 m x n array."""
+def _splitmix_outputs(seed: int, count: int) -> np.ndarray:
+    """SplitMix64 outputs 1 .. count of the stream seeded with `seed` (uint64)."""
     with np.errstate(over="ignore"):
-        idx = np.arange(1, m * n + 1, dtype=np.uint64)
+        idx = np.arange(1, count + 1, dtype=np.uint64)
         z = np.uint64(seed & (2**64 - 1)) + idx * _GAMMA
         z = (z ^ (z >> np.uint64(30))) * _M1
         z = (z ^ (z >> np.uint64(27))) * _M2
         z = z ^ (z >> np.uint64(31))
+    return z
+
+
+def uniform_matrix(seed: int, m: int, n: int) -> np.ndarray:
+    """u_ij = (splitmix64(seed, i*n + j) >> 40) * 2^-24 as an fp64 m x n array."""
+    z = _splitmix_outputs(seed, m * n)
     return ((z >> np.uint64(40)).astype(np.float64) * 2.0**-24).reshape(m, n)
 
 
@@ -387,3 +402,50 @@ def pipeline(W, X, G, bits, rounding="nearest", seed=0, damp_rel=0.01, method="a
     res = sweep(W, LO, LI, s, bits, rounding, seed, method=method)
     res.update(HI=HI, HO=HO, LI=LI, LO=LO, DI=DI, DO=DO, scales=s)
     return res
+
+
+# --------------------------------------------------------------------------
+# Two-sided incoherence processing. [YAQA-4]: the error bound tightens as H_O
+# and H_I become more incoherent, so, as for LDLQ, both Hessians are to be made
+# incoherent before rounding. [KronQ] (bidirectional incoherence processing):
+# the input-side random rotation is extended to the output side,
+# W' = R_O W R_I^T. The construction of the rotation is a reading (see the
+# module docstring): a randomised Hadamard transform, block-diagonal where n is
+# not a power of two.
+# --------------------------------------------------------------------------
+def rht_signs(n: int, seed: int) -> np.ndarray:
+    """s_i = -1 where the top bit of SplitMix64 output i of `seed` is set, else +1 (fp64)."""
+    z = _splitmix_outputs(seed, n)
+    return np.where((z >> np.uint64(63)) == np.uint64(1), -1.0, 1.0)
+
+
+def rht_block(n: int) -> int:
+    """2^k, the largest power of two dividing n."""
+    return n & -n
+
+
+def sylvester(b: int) -> np.ndarray:
+    """The Sylvester Hadamard matrix of order b (a power of two), by doubling."""
+    H = np.ones((1, 1))
+    while H.shape[0] < b:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def rht_matrix(n: int, seed: int) -> np.ndarray:
+    """U_n = (I_r (x) H_b / sqrt(b)) diag(s), b = rht_block(n), r = n / b, as a dense fp64 matrix."""
+    b = rht_block(n)
+    Hb = sylvester(b) / np.sqrt(b)
+    B = np.kron(np.eye(n // b), Hb)
+    return B * rht_signs(n, seed)[None, :]
+
+
+def rotate_layer(W, HI, HO, seed_O: int, seed_I: int):
+    """(U_O W U_I^T, U_I H_I U_I^T, U_O H_O U_O^T) in fp64; HO may be None (H_O = I stays I)."""
+    m, n = W.shape
+    UO = rht_matrix(m, seed_O)
+    UI = rht_matrix(n, seed_I)
+    W2 = UO @ np.asarray(W, np.float64) @ UI.T
+    HI2 = UI @ np.asarray(HI, np.float64) @ UI.T
+    HO2 = None if HO is None else UO @ np.asarray(HO, np.float64) @ UO.T
+    return W2, HI2, HO2

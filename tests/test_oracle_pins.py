@@ -12,6 +12,8 @@ section:
       anti-diagonal parallelism and divide-and-conquer; modular in the quantiser.
   K-FAC tutorial (www.mlqm.cn/news/1313094), sections 2 and 5: Kronecker-product
       identities and the X^T X / N factor estimate.
+  KronQ page (ai-feeds.com), method, bidirectional incoherence processing: the
+      weight is rotated on both sides, W' = R_O W R_I^T, before quantisation.
 """
 import itertools
 import os
@@ -582,3 +584,75 @@ def test_pins_catch_mutated_rules(mutation):
             D[i, j] = float(w[i, j]) - float(s[i]) * (c - 1.5)
     ref = ldlq_vectorised(w, HO, HI, s, 2)
     assert not np.array_equal(codes, ref)
+
+
+# ----------------------------------------------------------------------------
+# incoherence rotation (KronQ, bidirectional incoherence processing; YAQA
+# article, section 4: incoherence processing of both Hessians before rounding)
+# ----------------------------------------------------------------------------
+def test_rht_signs_follow_the_published_splitmix64_outputs():
+    # the top bits of the golden seed-0 outputs e220..., 6e78..., 06c4...
+    rows = [ln.split() for ln in open(os.path.join(GOLDEN, "splitmix64_seed0.txt"))
+            if ln.strip() and not ln.startswith("#")]
+    want = [-1.0 if int(val, 16) >> 63 else 1.0 for _, val in rows]
+    assert list(oracle.rht_signs(len(want), 0)) == want
+
+
+@pytest.mark.parametrize("b", [1, 2, 4, 64, 512])
+def test_sylvester_matches_scipy_hadamard(b):
+    import scipy.linalg
+    assert np.array_equal(oracle.sylvester(b), scipy.linalg.hadamard(b).astype(np.float64))
+
+
+@pytest.mark.parametrize("n,seed", [(1, 3), (2, 3), (12, 7), (64, 0), (100, 11), (448, 5), (3, 9)])
+def test_rht_matrix_is_orthogonal_and_block_hadamard(n, seed):
+    import scipy.linalg
+    U = oracle.rht_matrix(n, seed)
+    assert np.abs(U.T @ U - np.eye(n)).max() < 1e-12
+    # block structure: the largest power of two dividing n, written out here
+    b = 1
+    while n % (2 * b) == 0:
+        b *= 2
+    assert oracle.rht_block(n) == b
+    s = oracle.rht_signs(n, seed)
+    Hb = scipy.linalg.hadamard(b) / np.sqrt(b)
+    for r in range(n // b):
+        blk = slice(r * b, (r + 1) * b)
+        assert np.allclose(U[blk, blk], Hb * s[None, blk], atol=1e-15)
+        off = np.ones(n, bool)
+        off[blk] = False
+        assert np.all(U[blk][:, off] == 0.0)
+
+
+def test_rotation_keeps_the_proxy_loss_and_the_spectrum():
+    # tr(D H_I D^T H_O) is unchanged when D, H_I and H_O are rotated together, and
+    # each Hessian keeps its eigenvalues
+    rng = np.random.default_rng(4)
+    m, n = 24, 40
+    D = rng.standard_normal((m, n))
+    HI, HO = spd(n, 1), spd(m, 2)
+    D2, HI2, HO2 = oracle.rotate_layer(D, HI, HO, 31, 32)
+    l1 = np.trace(D @ HI @ D.T @ HO)
+    l2 = np.trace(D2 @ HI2 @ D2.T @ HO2)
+    assert abs(l1 - l2) <= 1e-10 * abs(l1)
+    assert np.allclose(np.linalg.eigvalsh(HI2), np.linalg.eigvalsh(HI), rtol=1e-10)
+    assert np.allclose(np.linalg.eigvalsh(HO2), np.linalg.eigvalsh(HO), rtol=1e-10)
+    # the weight is rotated on the left by U_O and on the right by U_I^T, not transposed
+    UO, UI = oracle.rht_matrix(m, 31), oracle.rht_matrix(n, 32)
+    assert np.allclose(UO.T @ D2 @ UI, D, atol=1e-12)
+
+
+def test_rotated_rounding_keeps_the_loss_identity():
+    # rounding the rotated problem is ordinary BaKron rounding: the loss identity
+    # (sum D_O D_I eta^2 = tr(Delta H_I Delta^T H_O)) holds on the rotated factors
+    w = workloads.make_w(32, 48, 3)
+    HI = oracle.damp(spd(48, 5))
+    HO = oracle.damp(spd(32, 6))
+    W2, HI2, HO2 = oracle.rotate_layer(w, HI, HO, 1, 2)
+    LI, DI = oracle.udu(HI2)
+    LO, DO = oracle.udu(HO2)
+    s = oracle.row_scales(W2.astype(np.float32), 3)
+    res = oracle.sweep(W2.astype(np.float32), LO, LI, s, 3)
+    lhs = oracle.loss_identity(res["eta"], DO, DI)
+    rhs = oracle.proxy_loss(res["delta"], HO2, HI2)
+    assert abs(lhs - rhs) <= 1e-9 * abs(rhs)
