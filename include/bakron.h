@@ -186,6 +186,29 @@ int bakron_solve(const float* W, int64_t m, int64_t n, int64_t ldw, const float*
                  const float* D_I, double* loss_out, int64_t* clamped_out, int32_t* info,
                  void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Randomised Hadamard rotation, for two-sided incoherence processing before
+ * the LDL and the solve (YAQA article, section 4: both Hessians are made
+ * incoherent before rounding, as for LDLQ; KronQ page, method, bidirectional
+ * incoherence processing: W' = R_O W R_I^T). In place on a rows x cols fp32
+ * matrix A (device, row-major, lda >= cols):
+ *   axis 0: A <- U_rows A      (every column is rotated; U of order rows)
+ *   axis 1: A <- A U_cols^T    (every row is rotated; U of order cols)
+ *   transpose != 0 applies U^T instead of U (the inverse rotation).
+ * U_n = (I_r (x) H_b / sqrt(b)) diag(s): b is the largest power of two dividing
+ * n, r = n / b, H_b the Sylvester Hadamard matrix (entry (i, j) =
+ * (-1)^popcount(i & j)), and s_i = -1 where bit 63 of SplitMix64 output i of
+ * `seed` (the generator of the stochastic rounding) is set, else +1.
+ * A layer is rotated as W' = U_O W U_I^T (axis 0 with seed_O, then axis 1 with
+ * seed_I), H_I' = U_I H_I U_I^T and H_O' = U_O H_O U_O^T (both axes, one seed);
+ * the proxy loss of any rounding is unchanged, and the rounded W' maps back as
+ * U_O^T W' U_I. Computed in fp32: every pass reads and writes A once.
+ * Errors: INVALID_ARG for NULL A, rows or cols <= 0, lda < cols, axis other
+ * than 0 or 1, or (axis 1) b > 16384.
+ */
+int bakron_rht(float* A, int64_t rows, int64_t cols, int64_t lda, int axis, uint64_t seed, int transpose,
+               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -8,10 +8,11 @@ tensors for device memory and uses the current stream.
   ldl(H, damp_rel)            H + lambda I = (L + I) D (L + I)^T   (fp64, L strictly upper)
   ldl_pair(HA, HB, damp_rel)  two independent factorisations side by side on two streams
   solve(W, L_O, L_I, bits)    BaKron rounding: codes, scales, error, proxy loss
+  rotate_layer(W, HI, HO, sO, sI) two-sided randomised Hadamard rotation (incoherence processing)
   quantize_layer(W, X, G, b)  the whole per-layer path
 """
 from ._binding import (  # noqa: F401
     BAKRON_E_DEVICE, BAKRON_E_INVALID_ARG, BAKRON_E_NOT_SPD, BAKRON_E_WORKSPACE, BAKRON_OK,
     EXPORTS, LIB, LIB_PATH, BakronError, SolveResult, abi_version, hessian_accum, ldl, ldl_pair,
-    quantize_layer, release_workspace, solve,
+    quantize_layer, release_workspace, rht, rotate_layer, solve,
 )

@@ -58,6 +58,8 @@ def _load() -> ctypes.CDLL:
     lib.bakron_ldl.argtypes = [vp, i64, i64, ctypes.c_double, vp, ctypes.POINTER(i64), vp, sz, vp]
     lib.bakron_ldl_async.restype = ctypes.c_int
     lib.bakron_ldl_async.argtypes = [vp, i64, i64, ctypes.c_double, vp, vp, vp, sz, vp]
+    lib.bakron_rht.restype = ctypes.c_int
+    lib.bakron_rht.argtypes = [vp, i64, i64, i64, ctypes.c_int, ctypes.c_uint64, ctypes.c_int, vp]
     lib.bakron_solve_workspace_bytes.restype = sz
     lib.bakron_solve_workspace_bytes.argtypes = [i64, i64]
     lib.bakron_solve.restype = ctypes.c_int
@@ -70,7 +72,7 @@ LIB = _load()
 
 EXPORTS = ("bakron_abi_version", "bakron_status_str", "bakron_hessian_accum_workspace_bytes",
            "bakron_hessian_accum", "bakron_ldl_workspace_bytes", "bakron_ldl", "bakron_ldl_async",
-           "bakron_solve_workspace_bytes", "bakron_solve")
+           "bakron_solve_workspace_bytes", "bakron_solve", "bakron_rht")
 
 
 def abi_version() -> int:
@@ -289,6 +291,32 @@ def solve(W: torch.Tensor, L_O: Optional[torch.Tensor], L_I: Optional[torch.Tens
                           _ptr(out.clamped), _ptr(out.info), _ptr(ws), nb, _stream())
     _check("bakron_solve", st)
     return out
+
+
+def rht(A: torch.Tensor, axis: int, seed: int, transpose: bool = False) -> torch.Tensor:
+    """In place: axis 0: A <- U A (U of order rows); axis 1: A <- A U^T (U of order cols).
+
+    U = (I_r (x) H_b / sqrt(b)) diag(s) with random signs from `seed`;
+    transpose=True applies U^T, the inverse.
+    """
+    lda = _mat(A, "A")
+    rows, cols = A.shape
+    _check("bakron_rht", LIB.bakron_rht(_ptr(A), rows, cols, lda, int(axis), int(seed) & (2**64 - 1),
+                                        1 if transpose else 0, _stream()))
+    return A
+
+
+def rotate_layer(W: torch.Tensor, HI: Optional[torch.Tensor], HO: Optional[torch.Tensor], seed_O: int,
+                 seed_I: int, transpose: bool = False):
+    """Two-sided incoherence processing, in place: W <- U_O W U_I^T, H_I <- U_I H_I U_I^T,
+    H_O <- U_O H_O U_O^T (H_I and H_O may be None). transpose=True undoes it."""
+    rht(W, 0, seed_O, transpose)
+    rht(W, 1, seed_I, transpose)
+    for H, seed in ((HI, seed_I), (HO, seed_O)):
+        if H is not None:
+            rht(H, 0, seed, transpose)
+            rht(H, 1, seed, transpose)
+    return W, HI, HO
 
 
 def quantize_layer(W: torch.Tensor, X: torch.Tensor, G: Optional[torch.Tensor], bits: int,

@@ -107,4 +107,12 @@ int bakron_solve(const float* W, int64_t m, int64_t n, int64_t ldw, const float*
     return bk::run_solve(a, ws, (hipStream_t)stream);
 }
 
+int bakron_rht(float* A, int64_t rows, int64_t cols, int64_t lda, int axis, uint64_t seed, int transpose,
+               void* stream) {
+    if (!A || rows <= 0 || cols <= 0 || bad_ld(lda, cols) || (axis != 0 && axis != 1))
+        return BAKRON_E_INVALID_ARG;
+    if (axis == 1 && (cols & -cols) > 16384) return BAKRON_E_INVALID_ARG;
+    return bk::launch_rht(A, rows, cols, lda, axis, seed, transpose, (hipStream_t)stream);
+}
+
 }  // extern "C"

@@ -9,7 +9,7 @@
 //    A workgroup of 256 threads (4 waves) owns one 64x64 tile; wave w owns the
 //    32x32 quadrant (w/2, w%2). Operand k-slices are staged in LDS, double
 //    buffered, with the next slice fetched into registers during the MFMAs.
-//  * the base quantiser and the counter-based uniform draw.
+//  * the base quantiser and the counter-based draws (SplitMix64).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -278,15 +278,19 @@ __device__ __forceinline__ int acc64_col(int bj) {
 }
 
 // ---------------------------------------------------------------------------
-// Counter-based uniform draw: SplitMix64 (Steele, Lea, Flood 2014) output
-// number idx+1 of a stream seeded with `seed`; the top 24 bits as u in [0, 1).
+// Counter-based draws: SplitMix64 (Steele, Lea, Flood 2014) output number
+// idx+1 of a stream seeded with `seed`. uniform24 takes its top 24 bits as u in
+// [0, 1) (stochastic rounding); the incoherence rotation takes its top bit as a
+// sign.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float uniform24(uint64_t seed, uint64_t idx) {
+__device__ __forceinline__ uint64_t splitmix64_out(uint64_t seed, uint64_t idx) {
     uint64_t z = seed + (idx + 1ull) * 0x9E3779B97F4A7C15ull;
     z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
     z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-    z ^= z >> 31;
-    return (float)(uint32_t)(z >> 40) * (1.0f / 16777216.0f);
+    return z ^ (z >> 31);
+}
+__device__ __forceinline__ float uniform24(uint64_t seed, uint64_t idx) {
+    return (float)(uint32_t)(splitmix64_out(seed, idx) >> 40) * (1.0f / 16777216.0f);
 }
 
 // Sum over the 4 lanes of a quad (lanes 4k..4k+3), result in every lane.

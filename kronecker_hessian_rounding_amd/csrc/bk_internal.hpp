@@ -27,6 +27,10 @@ int enqueue_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, voi
 int run_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, int64_t* bad_pivot,
             void* ws, hipStream_t stream);
 
+// --- incoherence rotation (bk_rotate.hip) ---
+int launch_rht(float* A, int64_t rows, int64_t cols, int64_t lda, int axis, uint64_t seed, int transpose,
+               hipStream_t stream);
+
 // --- rounding solve (bk_solve.hip) ---
 struct SolveArgs {
     const float* W;

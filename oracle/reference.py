@@ -54,7 +54,7 @@ __all__ = [
     "hessian", "hessian_entries", "damp", "udu", "udu_lapack", "row_scales", "sweep",
     "replay", "replay_rows", "proxy_loss", "loss_identity", "bound_terms", "splitmix64",
     "uniform_matrix", "pipeline", "rht_signs", "rht_block", "sylvester", "rht_matrix",
-    "rotate_layer",
+    "rht_apply", "rotate_layer",
 ]
 
 _lib = None
@@ -438,6 +438,26 @@ def rht_matrix(n: int, seed: int) -> np.ndarray:
     Hb = sylvester(b) / np.sqrt(b)
     B = np.kron(np.eye(n // b), Hb)
     return B * rht_signs(n, seed)[None, :]
+
+
+def rht_apply(A, axis: int, seed: int, transpose: bool = False) -> np.ndarray:
+    """axis 0: U A (U of order rows); axis 1: A U^T (U of order cols); U^T for transpose.
+
+    The same U_n as rht_matrix, applied block by block (H_b is symmetric, so
+    U^T = diag(s) (I_r (x) H_b / sqrt(b))); for orders too large for a dense U.
+    """
+    A = np.asarray(A, np.float64)
+    X = A if axis == 0 else A.T  # the vectors to rotate are the columns of X
+    n = X.shape[0]
+    b = rht_block(n)
+    Hb = sylvester(b) / np.sqrt(b)
+    s = rht_signs(n, seed)[:, None]
+    if not transpose:
+        X = s * X
+    Y = np.matmul(Hb, X.reshape(n // b, b, -1)).reshape(n, -1)
+    if transpose:
+        Y = s * Y
+    return Y if axis == 0 else Y.T
 
 
 def rotate_layer(W, HI, HO, seed_O: int, seed_I: int):

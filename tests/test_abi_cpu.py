@@ -122,3 +122,19 @@ def test_solve_rejects_bad_arguments(lib):
     assert call(ws=None) == 3
     assert call(nb=need - 1) == 3
     assert lib.bakron_solve_workspace_bytes(0, 5) == 0
+
+
+def test_rht_rejects_invalid_arguments(lib):
+    # host-side checks only: every call below returns before any launch
+    f = lib.bakron_rht
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                  ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    INVALID = 1
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: the arguments fail first
+    assert f(None, 4, 4, 4, 0, 1, 0, None) == INVALID
+    assert f(fake, 0, 4, 4, 0, 1, 0, None) == INVALID
+    assert f(fake, 4, 0, 4, 1, 1, 0, None) == INVALID
+    assert f(fake, 4, 8, 7, 0, 1, 0, None) == INVALID  # lda < cols
+    assert f(fake, 4, 8, 8, 2, 1, 0, None) == INVALID  # no such axis
+    assert f(fake, 4, 32768, 32768, 1, 1, 0, None) == INVALID  # row blocks above 16384

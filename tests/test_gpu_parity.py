@@ -418,3 +418,101 @@ def test_solve_is_deterministic(bk):
     b = bk.solve(T(w), T(LO), T(LI), 2, D_O=T(DO), D_I=T(DI), want_loss=True, want_delta=True)
     assert torch.equal(a_codes, b.codes) and torch.equal(a_delta, b.delta)
     assert torch.equal(a_loss, b.loss)
+
+
+# ----------------------------------------------------------------------------
+# two-sided incoherence processing: randomised Hadamard rotation
+# ----------------------------------------------------------------------------
+def rht_tol(a, axis):
+    """4 (k + 2) u_fp32 ||x||_2 for every rotated vector x (the columns for axis 0,
+    the rows for axis 1): k butterfly stages, the scale and the signs, each one
+    fp32 rounding of quantities bounded by ||x||_2."""
+    n = a.shape[axis]
+    k = (n & -n).bit_length() - 1
+    return 4 * (k + 2) * U32 * np.linalg.norm(a.astype(np.float64), axis=axis, keepdims=True)
+
+
+@pytest.mark.parametrize("transpose", [False, True])
+@pytest.mark.parametrize("rows,cols,axis", [
+    (64, 64, 0), (64, 64, 1), (100, 48, 0), (100, 48, 1), (512, 300, 0), (300, 512, 1),
+    (4096, 96, 0),   # 12 index bits: two column passes of 6
+    (8192, 40, 0),   # 13 bits: passes of 5, 4 and 4
+    (7, 5, 0), (7, 5, 1),  # odd orders: signs only
+    (40, 20480, 1),  # 4096-blocks, 16384-float chunks: one of four blocks, one of one
+    (3, 28672, 1),   # 7 blocks of 4096: chunks of 4 and 3 blocks
+])
+def test_rht_matches_oracle(bk, rows, cols, axis, transpose):
+    note("rht %dx%d axis %d transpose %d" % (rows, cols, axis, transpose))
+    rng = np.random.default_rng(rows * 7 + cols)
+    a = rng.standard_normal((rows, cols)).astype(np.float32)
+    seed = 1000 + rows + cols
+    A = torch.from_numpy(a).to(dev())
+    bk.rht(A, axis, seed, transpose)
+    got = A.cpu().numpy().astype(np.float64)
+    ref = oracle.rht_apply(a, axis, seed, transpose)
+    assert np.all(np.abs(got - ref) <= rht_tol(a, axis)), np.max(np.abs(got - ref) / rht_tol(a, axis))
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+def test_rht_strided_view_leaves_the_rest(bk, axis):
+    note("rht strided view axis %d" % axis)
+    rng = np.random.default_rng(3)
+    big = rng.standard_normal((96, 133)).astype(np.float32)
+    B = torch.from_numpy(big).to(dev())
+    view = B[:, 5:5 + 64]  # leading dimension 133, 64 columns
+    a = big[:, 5:5 + 64].copy()
+    bk.rht(view, axis, 21)
+    got = B.cpu().numpy()
+    ref = oracle.rht_apply(a, axis, 21)
+    assert np.all(np.abs(got[:, 5:69] - ref) <= rht_tol(a, axis))
+    assert np.array_equal(got[:, :5], big[:, :5]) and np.array_equal(got[:, 69:], big[:, 69:])
+
+
+@pytest.mark.parametrize("rows,cols", [(4096, 4096), (16, 16384)])
+def test_rht_round_trip_keeps_norms(bk, rows, cols):
+    # at the attention shape both axes, against the oracle; at a 16384-long row block
+    # (too large for a dense oracle H_b) the properties that hold at any size:
+    # U^T U = I and ||U x|| = ||x||
+    note("rht round trip %dx%d" % (rows, cols))
+    rng = np.random.default_rng(rows + cols)
+    a = rng.standard_normal((rows, cols)).astype(np.float32)
+    A = torch.from_numpy(a).to(dev())
+    bk.rht(A, 0, 5)
+    bk.rht(A, 1, 6)
+    once = A.cpu().numpy().astype(np.float64)
+    kb = (rows & -rows).bit_length() + (cols & -cols).bit_length()
+    fro = np.linalg.norm(a.astype(np.float64))
+    assert abs(np.linalg.norm(once) - fro) <= 4 * (kb + 4) * U32 * fro
+    if rows * cols <= 4096 * 4096 and max(rows & -rows, cols & -cols) <= 4096:
+        ref = oracle.rht_apply(oracle.rht_apply(a, 0, 5), 1, 6)
+        assert np.linalg.norm(once - ref) <= 4 * (kb + 4) * U32 * fro
+    bk.rht(A, 1, 6, transpose=True)
+    bk.rht(A, 0, 5, transpose=True)
+    back = A.cpu().numpy().astype(np.float64)
+    assert np.linalg.norm(back - a) <= 8 * (kb + 4) * U32 * fro
+
+
+def test_rotated_layer_through_ldl_and_solve(bk):
+    # two-sided incoherence processing between the Hessians and the LDL, all on the
+    # device; the rotation against the oracle's, then the solve on the rotated layer
+    # against the oracle's replay with the device's own factors
+    m, n, T = 96, 128, 1024
+    w, x, g = workloads.make_inputs("tiny", m=m, n=n, T=T)
+    note("rotated layer m=%d n=%d" % (m, n))
+    d = dev()
+    W = torch.from_numpy(np.ascontiguousarray(w)).to(d)
+    HI = bk.hessian_accum(torch.from_numpy(x).to(d))
+    HO = bk.hessian_accum(torch.from_numpy(g).to(d))
+    hi0, ho0 = HI.cpu().numpy(), HO.cpu().numpy()
+    bk.rotate_layer(W, HI, HO, 11, 12)
+    rw, rhi, rho = oracle.rotate_layer(w, hi0, ho0, 11, 12)
+    km, kn = (m & -m).bit_length(), (n & -n).bit_length()
+    for got, ref, src in ((W, rw, w), (HI, rhi, hi0), (HO, rho, ho0)):
+        err = np.linalg.norm(got.cpu().numpy().astype(np.float64) - ref)
+        assert err <= 4 * (km + kn + 4) * U32 * np.linalg.norm(src.astype(np.float64))
+    w2 = W.cpu().numpy()
+    Hi, Di = bk.ldl(HI, 0.01)
+    Ho, Do = bk.ldl(HO, 0.01)
+    LI = np.triu(Hi.cpu().numpy(), 1)
+    LO = np.triu(Ho.cpu().numpy(), 1)
+    check_solve(bk, w2, LO, LI, Do.cpu().numpy(), Di.cpu().numpy(), 3, label="rotated")

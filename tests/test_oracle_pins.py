@@ -656,3 +656,16 @@ def test_rotated_rounding_keeps_the_loss_identity():
     lhs = oracle.loss_identity(res["eta"], DO, DI)
     rhs = oracle.proxy_loss(res["delta"], HO2, HI2)
     assert abs(lhs - rhs) <= 1e-9 * abs(rhs)
+
+
+@pytest.mark.parametrize("shape", [(12, 20), (7, 64), (96, 5)])
+@pytest.mark.parametrize("axis", [0, 1])
+@pytest.mark.parametrize("transpose", [False, True])
+def test_rht_apply_is_the_dense_rotation(shape, axis, transpose):
+    rng = np.random.default_rng(8)
+    A = rng.standard_normal(shape)
+    U = oracle.rht_matrix(shape[axis], 77)
+    if transpose:
+        U = U.T
+    want = U @ A if axis == 0 else A @ U.T
+    assert np.allclose(oracle.rht_apply(A, axis, 77, transpose), want, atol=1e-12)
