@@ -74,6 +74,9 @@ def parse():
     ap.add_argument("--rounding", default="nearest", choices=["nearest", "stochastic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the CPU sweep sample")
+    ap.add_argument("--rotate", action="store_true",
+                    help="two-sided incoherence rotation of W, H_I and H_O before the LDL "
+                         "(W is rotated in place every step)")
     return ap.parse_args()
 
 
@@ -167,7 +170,7 @@ def main():
     cal_out.copy_(cal)
     torch.cuda.synchronize()
     del cal, cal_out
-    phases = ("hess_I", "hess_O", "ldl", "solve")
+    phases = ("hess_I", "hess_O") + (("rotate",) if args.rotate else ()) + ("ldl", "solve")
     ev = {k: [] for k in phases}
 
     def step(timed=False):
@@ -187,6 +190,9 @@ def main():
         mark()
         bk.hessian_accum(G, HO)
         mark()
+        if args.rotate:
+            bk.rotate_layer(W, HI, HO, seed + 1, seed + 2)
+            mark()
         # the two factorisations are independent and each a chain of small launches:
         # they run side by side on two streams
         bk.ldl_pair(HI, HO, 0.01, DI, DO)
@@ -259,7 +265,7 @@ def main():
         "config": {"workload": "%s, %d-bit %s" % (WORKLOAD_LABEL[args.workload], args.bits,
                                                   args.rounding),
                    "m": m, "n": n, "tokens": T, "bits": args.bits, "rounding": args.rounding,
-                   "damp_rel": 0.01, "leaf": 64},
+                   "damp_rel": 0.01, "leaf": 64, "rotate": bool(args.rotate)},
         "phases_ms": ph,
         "dominant_phase": dominant,
         "solve_ms": ph["solve"],
@@ -271,6 +277,18 @@ def main():
         "clamped": clamped,
         "info": info,
     }
+    if args.rotate:
+        # algorithmic HBM bytes of the rotation: every pass reads and writes its
+        # matrix once; a column rotation of order d takes ceil(k / 6) passes
+        # (k = the power of two in d), a row rotation one
+        def col_passes(dim):
+            k = (dim & -dim).bit_length() - 1
+            return max(1, (k + 5) // 6)
+        rot_bytes = 8.0 * (m * n * (col_passes(m) + 1) + n * n * (col_passes(n) + 1)
+                           + m * m * (col_passes(m) + 1))
+        res["rotate_ms"] = ph["rotate"]
+        res["rotate_hbm_gbs"] = rot_bytes / (ph["rotate"] * 1e-3) / 1e9
+        res["rotate_bytes"] = rot_bytes
     if not args.no_cpu_baseline:
         LI = np.triu(HI.cpu().numpy(), 1).astype(np.float64)
         LO = HO.cpu().numpy()

@@ -19,7 +19,8 @@
 //  * Along each column (the index is the row): passes over up to 6 index bits.
 //    Each lane of a wave owns one column and holds the 2^bits values of its
 //    group in registers, so every load and store of a wave is 64 consecutive
-//    floats of one row.
+//    floats of one row; the group's signs are drawn one per lane and shared by
+//    a ballot.
 #include <cmath>
 
 #include "bk_common.hpp"
@@ -70,12 +71,13 @@ __global__ __launch_bounds__(kThreads) void k_rht_rows(float* __restrict__ A, in
 
 // One pass over index bits [b0, b0 + NB) of the row index, for every column.
 // A group is the 2^NB rows of a 2^kbits-block that differ only in those bits;
-// group g = (block, bits above, bits below). The first pass of U applies the
-// signs, the last applies the scale (and, for U^T, the signs).
-template <int NB>
+// group g = (block, bits above, bits below). The last pass applies the scale.
+// kSgn: 0, no signs in this pass; 1, signs on the loaded values (the first pass
+// of U); 2, signs on the stored values (the last pass of U^T).
+template <int NB, int kSgn>
 __global__ __launch_bounds__(kThreads) void k_rht_cols(float* __restrict__ A, int64_t rows, int64_t cols,
                                                        int64_t lda, int kbits, int b0, uint64_t seed,
-                                                       float scale, int first, int last, int transpose) {
+                                                       float scale, int last) {
     constexpr int kN = 1 << NB;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t c = ((int64_t)blockIdx.x * (kThreads / 64) + w) * 64 + lane;
@@ -88,13 +90,24 @@ __global__ __launch_bounds__(kThreads) void k_rht_cols(float* __restrict__ A, in
         const int64_t hi = rest & (((int64_t)1 << hib) - 1);
         const int64_t blk = rest >> hib;
         const int64_t r0 = (blk << kbits) + (hi << (b0 + NB)) + lo;
+        // the group's signs: lane j draws the sign of row j of the group, and the
+        // ballot hands all of them to every lane
+        uint64_t neg = 0;
+        if (kSgn != 0)
+            neg = __ballot((splitmix64_out(seed, (uint64_t)(r0 + ((int64_t)(lane & (kN - 1)) << b0))) >> 63) != 0);
+        auto flip = [&](float x, int j) {
+            return __uint_as_float(__float_as_uint(x) ^ ((uint32_t)(neg >> j) << 31));
+        };
         float v[kN];
 #pragma unroll
         for (int j = 0; j < kN; ++j) {
             const int64_t r = r0 + ((int64_t)j << b0);
-            float x = in ? A[r * lda + c] : 0.0f;
-            if (first && !transpose) x *= rht_sign(seed, r);
-            v[j] = x;
+            v[j] = in ? A[r * lda + c] : 0.0f;
+        }
+        if (kSgn == 1) {
+            __builtin_amdgcn_sched_barrier(0);  // every load is in flight before the first sign waits on one
+#pragma unroll
+            for (int j = 0; j < kN; ++j) v[j] = flip(v[j], j);
         }
 #pragma unroll
         for (int s = 0; s < NB; ++s)
@@ -108,11 +121,8 @@ __global__ __launch_bounds__(kThreads) void k_rht_cols(float* __restrict__ A, in
 #pragma unroll
         for (int j = 0; j < kN; ++j) {
             const int64_t r = r0 + ((int64_t)j << b0);
-            float x = v[j];
-            if (last) {
-                x *= scale;
-                if (transpose) x *= rht_sign(seed, r);
-            }
+            float x = last ? v[j] * scale : v[j];
+            if (kSgn == 2) x = flip(x, j);
             if (in) A[r * lda + c] = x;
         }
     }
@@ -124,8 +134,16 @@ void col_pass(float* A, int64_t rows, int64_t cols, int64_t lda, int kbits, int 
               int first, int last, int transpose, hipStream_t stream) {
     const int64_t G = rows >> NB;
     const dim3 grid((unsigned)((cols + kThreads - 1) / kThreads), (unsigned)std::min<int64_t>(G, 65535));
-    hipLaunchKernelGGL(k_rht_cols<NB>, grid, dim3(kThreads), 0, stream, A, rows, cols, lda, kbits, b0, seed,
-                       scale, first, last, transpose);
+    const int sgn = (first && !transpose) ? 1 : (last && transpose) ? 2 : 0;
+    if (sgn == 1)
+        hipLaunchKernelGGL((k_rht_cols<NB, 1>), grid, dim3(kThreads), 0, stream, A, rows, cols, lda, kbits, b0,
+                           seed, scale, last);
+    else if (sgn == 2)
+        hipLaunchKernelGGL((k_rht_cols<NB, 2>), grid, dim3(kThreads), 0, stream, A, rows, cols, lda, kbits, b0,
+                           seed, scale, last);
+    else
+        hipLaunchKernelGGL((k_rht_cols<NB, 0>), grid, dim3(kThreads), 0, stream, A, rows, cols, lda, kbits, b0,
+                           seed, scale, last);
 }
 }  // namespace
 
