@@ -9,7 +9,9 @@ Sources (cited by page title and section):
             Hessian is approximated by a Kronecker product H_O (m x m) (x)
             H_I (n x n) of the vectorised weight.
   [YAQA-3]  same article, section 3: H_I = E[x^T x] over tokens (the
-            initialisation H_1 of Sketch A).
+            initialisation H_1 of Sketch A); Sketch B, one round of power
+            iteration from H_I = H_O = I: H_I = E_s[G_s^T G_s] / m and
+            H_O = E_s[G_s G_s^T] / n over per-sequence weight gradients G_s.
   [YAQA-4]  same article, section 4: the rounding rule
             W_ij = Q(W*_ij + a_i^T D[:i,:j] b_j + a_i^T D[:i,j] + D[i,:j] b_j),
             a_i / b_j columns of the strictly upper L_O / L_I, Q nearest or
@@ -54,7 +56,7 @@ __all__ = [
     "hessian", "hessian_entries", "damp", "udu", "udu_lapack", "row_scales", "sweep",
     "replay", "replay_rows", "proxy_loss", "loss_identity", "bound_terms", "splitmix64",
     "uniform_matrix", "pipeline", "rht_signs", "rht_block", "sylvester", "rht_matrix",
-    "rht_apply", "rotate_layer",
+    "rht_apply", "rotate_layer", "sketch_b",
 ]
 
 _lib = None
@@ -469,3 +471,24 @@ def rotate_layer(W, HI, HO, seed_O: int, seed_I: int):
     HI2 = UI @ np.asarray(HI, np.float64) @ UI.T
     HO2 = None if HO is None else UO @ np.asarray(HO, np.float64) @ UO.T
     return W2, HI2, HO2
+
+
+# --------------------------------------------------------------------------
+# Sketch B [YAQA-3]: one round of power iteration on the Hessian from the
+# identity. With (H_I)_0 = (H_O)_0 = I the update
+#   (H_I)_1 = E_s[G_s^T (H_O)_0 G_s] / ||(H_O)_0||_F^2,
+#   (H_O)_1 = E_s[G_s (H_I)_0 G_s^T] / ||(H_I)_0||_F^2
+# reduces to E_s[G_s^T G_s] / m and E_s[G_s G_s^T] / n, G_s the m x n weight
+# gradient of sequence s.
+# --------------------------------------------------------------------------
+def sketch_b(grads):
+    """(H_I, H_O) in fp64 from per-sequence gradients grads[s] (m x n each)."""
+    G = [np.asarray(g, np.float64) for g in grads]
+    S = len(G)
+    m, n = G[0].shape
+    HI = np.zeros((n, n))
+    HO = np.zeros((m, m))
+    for g in G:
+        HI += g.T @ g
+        HO += g @ g.T
+    return HI / (S * m), HO / (S * n)

@@ -669,3 +669,44 @@ def test_rht_apply_is_the_dense_rotation(shape, axis, transpose):
         U = U.T
     want = U @ A if axis == 0 else A @ U.T
     assert np.allclose(oracle.rht_apply(A, axis, 77, transpose), want, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# Sketch B (YAQA article, section 3): H_I = E_s[G_s^T G_s] / m, H_O = E_s[G_s G_s^T] / n
+# ----------------------------------------------------------------------------
+def test_sketch_b_traces_are_the_mean_squared_gradient_norm():
+    rng = np.random.default_rng(12)
+    grads = [rng.standard_normal((6, 9)) * rng.lognormal(0, 1, size=9) for _ in range(5)]
+    HI, HO = oracle.sketch_b(grads)
+    fro2 = np.mean([np.sum(g * g) for g in grads])
+    assert abs(6 * np.trace(HI) - fro2) <= 1e-12 * fro2
+    assert abs(9 * np.trace(HO) - fro2) <= 1e-12 * fro2
+    for H in (HI, HO):
+        assert np.array_equal(H, H.T) or np.abs(H - H.T).max() <= 1e-14 * np.abs(H).max()
+        assert np.linalg.eigvalsh(H).min() >= -1e-12 * np.abs(H).max()
+
+
+def test_sketch_b_rank_one_gradients():
+    # G_s = u_s v_s^T: G^T G = |u|^2 v v^T and G G^T = |v|^2 u u^T
+    rng = np.random.default_rng(13)
+    us = [rng.standard_normal(7) for _ in range(3)]
+    vs = [rng.standard_normal(4) for _ in range(3)]
+    HI, HO = oracle.sketch_b([np.outer(u, v) for u, v in zip(us, vs)])
+    HI_want = sum(np.dot(u, u) * np.outer(v, v) for u, v in zip(us, vs)) / (3 * 7)
+    HO_want = sum(np.dot(v, v) * np.outer(u, u) for u, v in zip(us, vs)) / (3 * 4)
+    assert np.allclose(HI, HI_want, rtol=1e-13, atol=1e-15)
+    assert np.allclose(HO, HO_want, rtol=1e-13, atol=1e-15)
+
+
+def test_sketch_b_brute_force():
+    rng = np.random.default_rng(14)
+    grads = [rng.standard_normal((3, 4)) for _ in range(2)]
+    HI, HO = oracle.sketch_b(grads)
+    for i in range(4):
+        for j in range(4):
+            want = sum(g[a][i] * g[a][j] for g in grads for a in range(3)) / (2 * 3)
+            assert abs(HI[i, j] - want) <= 1e-13
+    for i in range(3):
+        for j in range(3):
+            want = sum(g[i][b] * g[j][b] for g in grads for b in range(4)) / (2 * 4)
+            assert abs(HO[i, j] - want) <= 1e-13
