@@ -115,6 +115,22 @@ int bakron_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, floa
                          void* stream);
 
 /*
+ * The same accumulation with X stored d x T (one row per output index, the
+ * contraction along the rows): H <- beta * H + alpha * X X^T. With X the m x n
+ * weight gradient G_s of one sequence this gives the output-side term of
+ * Sketch B (YAQA article, section 3: H_O = E_s[G_s G_s^T] / n, alpha = 1/(S n));
+ * the input-side term E_s[G_s^T G_s] / m is bakron_hessian_accum with T = m.
+ *   X: d x T fp32, ldx >= T. H: d x d fp32, ldh >= d, both triangles written.
+ *   ws: at least bakron_hessian_accum_workspace_bytes(T, d) bytes (this form
+ *       runs on the three-piece path only).
+ * Errors: INVALID_ARG as for bakron_hessian_accum (with ldx >= T);
+ * WORKSPACE if ws is NULL or too small.
+ */
+int bakron_hessian_accum_t(const float* X, int64_t T, int64_t d, int64_t ldx, float alpha,
+                           float beta, float* H, int64_t ldh, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/*
  * Damped LDL factorisation (YAQA section 4): with lambda = damp_rel * mean(diag H)
  * (the mean of the undamped diagonal, in fp64), factor
  *     H + lambda I = (L + I) diag(D) (L + I)^T,  L strictly UPPER triangular,

@@ -52,6 +52,8 @@ def _load() -> ctypes.CDLL:
     lib.bakron_hessian_accum_workspace_bytes.argtypes = [i64, i64]
     lib.bakron_hessian_accum.restype = ctypes.c_int
     lib.bakron_hessian_accum.argtypes = [vp, i64, i64, i64, f32, f32, vp, i64, vp, sz, vp]
+    lib.bakron_hessian_accum_t.restype = ctypes.c_int
+    lib.bakron_hessian_accum_t.argtypes = [vp, i64, i64, i64, f32, f32, vp, i64, vp, sz, vp]
     lib.bakron_ldl_workspace_bytes.restype = sz
     lib.bakron_ldl_workspace_bytes.argtypes = [i64]
     lib.bakron_ldl.restype = ctypes.c_int
@@ -71,7 +73,7 @@ def _load() -> ctypes.CDLL:
 LIB = _load()
 
 EXPORTS = ("bakron_abi_version", "bakron_status_str", "bakron_hessian_accum_workspace_bytes",
-           "bakron_hessian_accum", "bakron_ldl_workspace_bytes", "bakron_ldl", "bakron_ldl_async",
+           "bakron_hessian_accum", "bakron_hessian_accum_t", "bakron_ldl_workspace_bytes", "bakron_ldl", "bakron_ldl_async",
            "bakron_solve_workspace_bytes", "bakron_solve", "bakron_rht")
 
 
@@ -144,15 +146,21 @@ def _aux_stream(device) -> torch.cuda.Stream:
 
 # --------------------------------------------------------------------------
 def hessian_accum(X: torch.Tensor, H: Optional[torch.Tensor] = None, alpha: Optional[float] = None,
-                  beta: float = 0.0, pieces: bool = True) -> torch.Tensor:
+                  beta: float = 0.0, pieces: bool = True, transposed: bool = False) -> torch.Tensor:
     """H <- beta H + alpha X^T X (default alpha = 1/T) on the device.
 
     pieces=True passes the full workspace: each fp32 product is formed from three
     bf16 pieces per operand on the bf16 matrix cores. pieces=False passes none,
-    which selects the fp32 matrix-core path.
+    which selects the fp32 matrix-core path. transposed=True takes X as d x T and
+    forms alpha X X^T (three-piece path only).
     """
     ldx = _mat(X, "X")
-    T, d = X.shape
+    if transposed:
+        if not pieces:
+            raise ValueError("the transposed form runs on the three-piece path only")
+        d, T = X.shape
+    else:
+        T, d = X.shape
     if H is None:
         H = torch.empty((d, d), dtype=torch.float32, device=X.device)
     ldh = _mat(H, "H")
@@ -162,10 +170,22 @@ def hessian_accum(X: torch.Tensor, H: Optional[torch.Tensor] = None, alpha: Opti
         alpha = 1.0 / max(T, 1)
     nb = LIB.bakron_hessian_accum_workspace_bytes(T, d) if pieces else 0
     ws = _workspace(nb, X.device)
-    _check("bakron_hessian_accum",
-           LIB.bakron_hessian_accum(_ptr(X), T, d, ldx, alpha, beta, _ptr(H), ldh, _ptr(ws), nb,
-                                    _stream()))
+    fn = LIB.bakron_hessian_accum_t if transposed else LIB.bakron_hessian_accum
+    _check("bakron_hessian_accum_t" if transposed else "bakron_hessian_accum",
+           fn(_ptr(X), T, d, ldx, alpha, beta, _ptr(H), ldh, _ptr(ws), nb, _stream()))
     return H
+
+
+def sketch_b(grads, HI: Optional[torch.Tensor] = None, HO: Optional[torch.Tensor] = None):
+    """Sketch B factors from per-sequence weight gradients (S x m x n, or a sequence of m x n):
+    H_I = E_s[G_s^T G_s] / m and H_O = E_s[G_s G_s^T] / n. Returns (H_I, H_O)."""
+    S = len(grads)
+    m, n = grads[0].shape
+    for s in range(S):
+        beta = 0.0 if s == 0 else 1.0
+        HI = hessian_accum(grads[s], HI, alpha=1.0 / (S * m), beta=beta)
+        HO = hessian_accum(grads[s], HO, alpha=1.0 / (S * n), beta=beta, transposed=True)
+    return HI, HO
 
 
 def ldl(H: torch.Tensor, damp_rel: float = 0.01, D: Optional[torch.Tensor] = None):

@@ -523,6 +523,51 @@ __global__ __launch_bounds__(kThreads) void k_split3(const float* __restrict__ X
     }
 }
 
+// The same planes from X stored d x T (one row per output column, the tokens
+// along the row), for H = X X^T: thread (c, q) splits tokens 32 q .. 32 q + 31 of
+// row c, one whole 128-byte line, into four groups of 8; a wave writes 1 KB of
+// consecutive 16-byte units of each plane per group.
+template <bool kVec>
+__global__ __launch_bounds__(kThreads) void k_split3_t(const float* __restrict__ X, int64_t T,
+                                                       int64_t d, int64_t ldx, int64_t ng,
+                                                       int64_t dp, uint4* __restrict__ Xs) {
+    const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (c >= dp) return;
+    for (int64_t q = blockIdx.y; q < ng / 4; q += gridDim.y) {
+        const int64_t k0 = 32 * q;
+        const float* row = X + c * ldx + k0;
+        float v[32];
+        if (kVec && c < d && k0 + 32 <= T) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const f32x4 t = *reinterpret_cast<const f32x4*>(row + 4 * e);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[4 * e + j] = t[j];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 32; ++e) v[e] = (c < d && k0 + e < T) ? row[e] : 0.0f;
+        }
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+            uint32_t pk[3][4];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                uint32_t h0, m0, l0, h1, m1, l1;
+                split3_value(v[8 * gi + e], h0, m0, l0);
+                split3_value(v[8 * gi + e + 1], h1, m1, l1);
+                pk[0][e >> 1] = (h0 & 0xffffu) | (h1 << 16);
+                pk[1][e >> 1] = (m0 & 0xffffu) | (m1 << 16);
+                pk[2][e >> 1] = (l0 & 0xffffu) | (l1 << 16);
+            }
+            const int64_t g = 4 * q + gi;
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+                Xs[((int64_t)p * ng + g) * dp + c] = uint4{pk[p][0], pk[p][1], pk[p][2], pk[p][3]};
+        }
+    }
+}
+
 // One ring stage of both operands: [piece][16-token block][token half][column].
 struct Split3Stage {
     bf16x8 v[3][kS3KB][2][kT128];
@@ -721,7 +766,7 @@ size_t hessian_workspace_bytes(int64_t T, int64_t d) {
 
 int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, float alpha,
                          float beta, float* H, int64_t ldh, void* ws, size_t ws_bytes,
-                         hipStream_t stream) {
+                         hipStream_t stream, bool trans) {
     const int64_t nb = (d + kT128 - 1) / kT128;
     const int64_t tiles = nb * (nb + 1) / 2;
     if (tiles > 0x7fffffff) return BAKRON_E_INVALID_ARG;
@@ -729,7 +774,15 @@ int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, floa
     if (ws != nullptr && ws_bytes >= sh.bytes) {
         // the three-piece bf16 path
         uint4* Xs = (uint4*)ws;
-        if (sh.ng > 0) {
+        if (sh.ng > 0 && trans) {
+            const unsigned gy = (unsigned)std::min<int64_t>(sh.ng / 4, 65535);
+            const dim3 grid((unsigned)((sh.dp + kThreads - 1) / kThreads), gy);
+            const bool vec = (ldx & 3) == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0;
+            if (vec)
+                hipLaunchKernelGGL(k_split3_t<true>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, sh.ng, sh.dp, Xs);
+            else
+                hipLaunchKernelGGL(k_split3_t<false>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, sh.ng, sh.dp, Xs);
+        } else if (sh.ng > 0) {
             const unsigned gy = (unsigned)std::min<int64_t>(sh.ng, 65535);
             const dim3 grid((unsigned)((sh.dp + kSplitCols - 1) / kSplitCols), gy);
             const bool vec = (ldx & 3) == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0;
@@ -752,7 +805,8 @@ int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, floa
         }
         return hipGetLastError() == hipSuccess ? BAKRON_OK : BAKRON_E_DEVICE;
     }
-    // the fp32-MFMA path (no room for the pieces)
+    // the fp32-MFMA path (no room for the pieces); it reads X as T x d only
+    if (trans) return BAKRON_E_WORKSPACE;
     const int64_t nsl = (T + kSyKT - 1) / kSyKT;
     const SyrkPlan pl = plan_tiles(tiles, resident_slots(sizeof(SyrkShared)), nsl,
                                    ws != nullptr ? ws_bytes : 0);

@@ -38,6 +38,16 @@ int bakron_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, floa
                                     (hipStream_t)stream);
 }
 
+int bakron_hessian_accum_t(const float* X, int64_t T, int64_t d, int64_t ldx, float alpha,
+                           float beta, float* H, int64_t ldh, void* ws, size_t ws_bytes,
+                           void* stream) {
+    if (!H || d <= 0 || T < 0 || bad_ld(ldh, d)) return BAKRON_E_INVALID_ARG;
+    if (T > 0 && (!X || bad_ld(ldx, T))) return BAKRON_E_INVALID_ARG;
+    if (!ws || ws_bytes < bk::hessian_workspace_bytes(T, d)) return BAKRON_E_WORKSPACE;
+    return bk::launch_hessian_accum(X, T, d, ldx, alpha, beta, H, ldh, ws, ws_bytes,
+                                    (hipStream_t)stream, true);
+}
+
 size_t bakron_ldl_workspace_bytes(int64_t d) {
     if (d <= 0) return 0;
     return bk::ldl_workspace_bytes(d);

@@ -14,9 +14,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // --- Hessian factor accumulation (bk_accum.hip) ---
 size_t hessian_workspace_bytes(int64_t T, int64_t d);
+// trans: X is stored d x T (H = X X^T); needs the workspace of the piece path
 int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, float alpha,
                          float beta, float* H, int64_t ldh, void* ws, size_t ws_bytes,
-                         hipStream_t stream);
+                         hipStream_t stream, bool trans = false);
 
 // --- LDL factorisation (bk_ldl.hip) ---
 size_t ldl_workspace_bytes(int64_t d);

@@ -138,3 +138,17 @@ def test_rht_rejects_invalid_arguments(lib):
     assert f(fake, 4, 8, 7, 0, 1, 0, None) == INVALID  # lda < cols
     assert f(fake, 4, 8, 8, 2, 1, 0, None) == INVALID  # no such axis
     assert f(fake, 4, 32768, 32768, 1, 1, 0, None) == INVALID  # row blocks above 16384
+
+
+def test_hessian_accum_t_rejects_invalid_arguments(lib):
+    f = lib.bakron_hessian_accum_t
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                  ctypes.c_float, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t,
+                  ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    INVALID, WORKSPACE = 1, 3
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: the arguments fail first
+    assert f(fake, 16, 8, 15, 1.0, 0.0, fake, 8, fake, 1 << 30, None) == INVALID  # ldx < T
+    assert f(fake, 16, 0, 16, 1.0, 0.0, fake, 8, fake, 1 << 30, None) == INVALID  # d <= 0
+    assert f(None, 16, 8, 16, 1.0, 0.0, fake, 8, fake, 1 << 30, None) == INVALID  # X missing
+    assert f(fake, 16, 8, 16, 1.0, 0.0, fake, 8, None, 0, None) == WORKSPACE      # no workspace

@@ -11,6 +11,7 @@ Acceptance (from the method's definition; see the oracle's replay()):
   * LDL: fp64 on the device, so L^ and D^ agree with the fp64 oracle to a
     couple of fp32 ulps; backward error ||H - (L^+I)D^(L^+I)^T|| / ||H|| <= 1e-6.
 """
+import ctypes
 import sys
 
 import numpy as np
@@ -516,3 +517,61 @@ def test_rotated_layer_through_ldl_and_solve(bk):
     LI = np.triu(Hi.cpu().numpy(), 1)
     LO = np.triu(Ho.cpu().numpy(), 1)
     check_solve(bk, w2, LO, LI, Do.cpu().numpy(), Di.cpu().numpy(), 3, label="rotated")
+
+
+# ----------------------------------------------------------------------------
+# Sketch B: H_I = E_s[G_s^T G_s] / m, H_O = E_s[G_s G_s^T] / n (YAQA article, section 3)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("d,T", [(64, 1024), (100, 333), (129, 2000), (5, 1), (300, 77)])
+def test_hessian_accum_transposed_matches_oracle(bk, d, T):
+    # X stored d x T: H = X X^T / T
+    note("hessian transposed d=%d T=%d" % (d, T))
+    x = workloads.make_x(T, d, 41 + d, "gauss", 2 if d > 2 else 0)  # T x d
+    xt = np.ascontiguousarray(x.T)
+    H = bk.hessian_accum(torch.from_numpy(xt).to(dev()), transposed=True).cpu().numpy()
+    assert np.array_equal(H, H.T)
+    ref = oracle.hessian(x)
+    ax = np.abs(x.astype(np.float64))
+    bound = 4 * U32 * np.sqrt(max(T, 64)) * (ax.T @ ax) / T + 1e-30
+    assert np.all(np.abs(H - ref) <= bound), np.max(np.abs(H - ref) / bound)
+
+
+def test_hessian_accum_transposed_strided_view(bk):
+    note("hessian transposed strided view")
+    T, d = 333, 70
+    x = workloads.make_x(T, d, 44, "gauss", 2)
+    big = np.zeros((d, T + 11), dtype=np.float32)
+    big[:, 3:3 + T] = x.T
+    view = torch.from_numpy(big).to(dev())[:, 3:3 + T]  # leading dimension T + 11, 4-byte offset
+    H = bk.hessian_accum(view, transposed=True).cpu().numpy()
+    ref = oracle.hessian(x)
+    ax = np.abs(x.astype(np.float64))
+    assert np.all(np.abs(H - ref) <= 4 * U32 * np.sqrt(T) * (ax.T @ ax) / T)
+
+
+def test_hessian_accum_transposed_needs_the_piece_workspace(bk):
+    note("hessian transposed without workspace")
+    X = torch.zeros((8, 16), device=dev())
+    with pytest.raises(ValueError):
+        bk.hessian_accum(X, transposed=True, pieces=False)
+    H = torch.empty((8, 8), device=dev())
+    st = bk.LIB.bakron_hessian_accum_t(ctypes.c_void_p(X.data_ptr()), 16, 8, 16, 1.0, 0.0,
+                                       ctypes.c_void_p(H.data_ptr()), 8, None, 0, None)
+    assert st == bk.BAKRON_E_WORKSPACE
+
+
+@pytest.mark.parametrize("S,m,n", [(3, 96, 130), (1, 64, 64), (4, 33, 257)])
+def test_sketch_b_matches_oracle(bk, S, m, n):
+    note("sketch B S=%d m=%d n=%d" % (S, m, n))
+    g = workloads.make_grads(S, m, n, 50 + m)
+    HI, HO = bk.sketch_b(torch.from_numpy(g).to(dev()))
+    HI, HO = HI.cpu().numpy(), HO.cpu().numpy()
+    ri, ro = oracle.sketch_b(list(g))
+    ag = np.abs(g.astype(np.float64))
+    # S accumulations of K-long sums, each within the fp32 bound, plus the S - 1
+    # fp32 additions into H: 8 u sqrt(S K) of the mean |G|-product
+    bi = 8 * U32 * np.sqrt(S * m) * sum(a.T @ a for a in ag) / (S * m) + 1e-30
+    bo = 8 * U32 * np.sqrt(S * n) * sum(a @ a.T for a in ag) / (S * n) + 1e-30
+    assert np.all(np.abs(HI - ri) <= bi), np.max(np.abs(HI - ri) / bi)
+    assert np.all(np.abs(HO - ro) <= bo), np.max(np.abs(HO - ro) / bo)
+    assert np.array_equal(HI, HI.T) and np.array_equal(HO, HO.T)

@@ -24,6 +24,9 @@ Recipe (all fp32, numpy PCG64 streams):
   G   T x m : N(0, 1) times a per-column lognormal(0, 0.5) factor.
 Seeds: W 1000+k, X 2000+k, G 3000+k, stochastic rounding 4000+k for
 workload k = 0..4.
+Sketch B (YAQA article, section 3) takes per-sequence weight gradients instead
+of X and G: make_grads draws S x m x n with the G row scales and the X column
+scales and outliers (seed 5000+k in bench.py).
 """
 from __future__ import annotations
 
@@ -121,3 +124,22 @@ def make_inputs(name: str, m: int | None = None, n: int | None = None, T: int | 
     g = make_g(T, m, wl.seed_g)
     return w, x, g
 
+
+
+def make_grads(S: int, m: int, n: int, seed: int, outliers: int = 8, mult: float = 20.0) -> np.ndarray:
+    """S per-sequence weight gradients (S x m x n fp32) for the Sketch B estimate.
+
+    G_s = N(0, 1) scaled per output row by lognormal(0, 0.5) (the output-gradient
+    recipe) and per input column by lognormal(0, 1) with `outliers` columns
+    multiplied by `mult` (the input recipe): a weight gradient is a sum of
+    outer products of output gradients and inputs, so it carries both scales.
+    """
+    rng = np.random.default_rng(seed)
+    row = rng.lognormal(0.0, 0.5, size=m).astype(np.float32)
+    col = rng.lognormal(0.0, 1.0, size=n).astype(np.float32)
+    idx = rng.choice(n, size=min(outliers, n), replace=False) if outliers > 0 else np.zeros(0, int)
+    col[idx] *= np.float32(mult)
+    g = rng.standard_normal((S, m, n), dtype=np.float32)
+    g *= row[None, :, None]
+    g *= col[None, None, :]
+    return g
