@@ -74,6 +74,10 @@ def parse():
     ap.add_argument("--rounding", default="nearest", choices=["nearest", "stochastic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the CPU sweep sample")
+    ap.add_argument("--hessian", default="tokens", choices=["tokens", "sketch_b"],
+                    help="factor estimate: X^T X / T and G^T G / T over tokens, or Sketch B from "
+                         "per-sequence weight gradients")
+    ap.add_argument("--sequences", type=int, default=8, help="gradients per step for Sketch B")
     ap.add_argument("--rotate", action="store_true",
                     help="two-sided incoherence rotation of W, H_I and H_O before the LDL "
                          "(W is rotated in place every step)")
@@ -170,7 +174,11 @@ def main():
     cal_out.copy_(cal)
     torch.cuda.synchronize()
     del cal, cal_out
-    phases = ("hess_I", "hess_O") + (("rotate",) if args.rotate else ()) + ("ldl", "solve")
+    sketch = args.hessian == "sketch_b"
+    if sketch:
+        grads = torch.from_numpy(workloads.make_grads(args.sequences, m, n, 5000 + wl.key)).to(dev)
+    hess_phases = ("hess_sketch_b",) if sketch else ("hess_I", "hess_O")
+    phases = hess_phases + (("rotate",) if args.rotate else ()) + ("ldl", "solve")
     ev = {k: [] for k in phases}
 
     def step(timed=False):
@@ -186,10 +194,14 @@ def main():
                 e.record()
                 marks.append(e)
 
-        bk.hessian_accum(X, HI)
-        mark()
-        bk.hessian_accum(G, HO)
-        mark()
+        if sketch:
+            bk.sketch_b(grads, HI, HO)
+            mark()
+        else:
+            bk.hessian_accum(X, HI)
+            mark()
+            bk.hessian_accum(G, HO)
+            mark()
         if args.rotate:
             bk.rotate_layer(W, HI, HO, seed + 1, seed + 2)
             mark()
@@ -225,11 +237,17 @@ def main():
     # kernels run on); one call is the k_split3 pre-pass, k_syrk3_full and, when
     # the tile count is not a whole number of rounds, the split-K pair
     # k_syrk3_split + k_syrk_reduce for the leftover tiles.
-    syrk_ms = float(np.mean(ev["hess_I"] + ev["hess_O"]))
-    # algorithmic fp32 flops per call, averaged over the two calls: T d^2 per
-    # factor (the upper half, T d^2 / 2 FMAs at 2 flops each); the matrix cores
-    # run six bf16 piece products for each
-    syrk_flops = float(T) * (n * n + m * m) / 2.0
+    if sketch:
+        # one "call" is the whole Sketch B phase: S sequences, each an m n^2 (H_I)
+        # and an n m^2 (H_O) accumulation
+        syrk_ms = float(np.mean(ev["hess_sketch_b"]))
+        syrk_flops = float(args.sequences) * (m * n * n + n * m * m)
+    else:
+        syrk_ms = float(np.mean(ev["hess_I"] + ev["hess_O"]))
+        # algorithmic fp32 flops per call, averaged over the two calls: T d^2 per
+        # factor (the upper half, T d^2 / 2 FMAs at 2 flops each); the matrix cores
+        # run six bf16 piece products for each
+        syrk_flops = float(T) * (n * n + m * m) / 2.0
     solve_flops = float(m) * n * (m + n)            # far-field feedback, minimal
     dominant = max(ph, key=ph.get)
     fp32_equiv = syrk_flops / (syrk_ms * 1e-3) / 1e12
@@ -240,7 +258,7 @@ def main():
         "achieved": PIECE_PRODUCTS * fp32_equiv,
         "peak": PEAK_BF16_MFMA_TFLOPS,
         "unit": "TFLOP/s",
-        "traffic": syrk_traffic_bytes(args.workload),
+        "traffic": None if sketch else syrk_traffic_bytes(args.workload),
         "flops_per_call": PIECE_PRODUCTS * syrk_flops,
         "fp32_equiv_tflops": fp32_equiv,
         "fp32_equiv_frac_of_fp32_peak": fp32_equiv / PEAK_FP32_MFMA_TFLOPS,
@@ -265,7 +283,8 @@ def main():
         "config": {"workload": "%s, %d-bit %s" % (WORKLOAD_LABEL[args.workload], args.bits,
                                                   args.rounding),
                    "m": m, "n": n, "tokens": T, "bits": args.bits, "rounding": args.rounding,
-                   "damp_rel": 0.01, "leaf": 64, "rotate": bool(args.rotate)},
+                   "damp_rel": 0.01, "leaf": 64, "rotate": bool(args.rotate),
+                   "hessian": args.hessian + (" x %d sequences" % args.sequences if sketch else "")},
         "phases_ms": ph,
         "dominant_phase": dominant,
         "solve_ms": ph["solve"],

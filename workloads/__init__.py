@@ -34,7 +34,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "get", "make_w", "make_x", "make_g", "make_inputs"]
+__all__ = ["Workload", "WORKLOADS", "get", "make_w", "make_x", "make_g", "make_grads", "make_inputs"]
 
 
 @dataclass(frozen=True)
