@@ -308,6 +308,10 @@ def main():
         res["rotate_ms"] = ph["rotate"]
         res["rotate_hbm_gbs"] = rot_bytes / (ph["rotate"] * 1e-3) / 1e9
         res["rotate_bytes"] = rot_bytes
+    # the layer's bound terms from the last step's factors and scales (untimed;
+    # the traces of H are not kept past the LDL, so they are left out)
+    rep = bk.layer_report(DO, DI, out.scales)
+    res["bound"] = {k: rep[k] for k in ("tr_DO", "tr_DI", "bound_sharp", "bound_page")}
     if not args.no_cpu_baseline:
         LI = np.triu(HI.cpu().numpy(), 1).astype(np.float64)
         LO = HO.cpu().numpy()

@@ -225,6 +225,24 @@ int bakron_solve(const float* W, int64_t m, int64_t n, int64_t ldw, const float*
 int bakron_rht(float* A, int64_t rows, int64_t cols, int64_t lda, int axis, uint64_t seed, int transpose,
                void* stream);
 
+/*
+ * Per-layer bound and sensitivity report, written to out (device, 7 doubles)
+ * by one workgroup summing in fp64:
+ *   out[0] = tr(D_O), out[1] = tr(D_I)   (the LDL pivots; D_O NULL means H_O = I: m)
+ *   out[2] = sum_i D_O,i s_i^2 / 4 * tr(D_I)
+ *            (YAQA article, section 4: the loss bound with |eta_ij| <= s_i / 2,
+ *            which holds for nearest rounding when no code was clamped)
+ *   out[3] = tr(D_I) tr(D_O) max_i s_i^2 / 4   (the bound in the page's form)
+ *   out[4] = tr(H_I), out[5] = tr(H_O)   (NaN where H_I / H_O is NULL). Pass the
+ *            factors before bakron_ldl, which writes D over their diagonal.
+ *   out[6] = out[4] * out[5], the KronQ page's layer sensitivity tr(A) tr(G).
+ *   scales: [m] the row scales the solve used (scales_out).
+ * Errors: INVALID_ARG for m or n <= 0, NULL D_I, scales or out, bad ld.
+ */
+int bakron_layer_report(int64_t m, int64_t n, const float* D_O, const float* D_I, const float* scales,
+                        const float* H_I, int64_t ldhi, const float* H_O, int64_t ldho, double* out,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

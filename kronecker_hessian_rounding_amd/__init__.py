@@ -15,5 +15,5 @@ tensors for device memory and uses the current stream.
 from ._binding import (  # noqa: F401
     BAKRON_E_DEVICE, BAKRON_E_INVALID_ARG, BAKRON_E_NOT_SPD, BAKRON_E_WORKSPACE, BAKRON_OK,
     EXPORTS, LIB, LIB_PATH, BakronError, SolveResult, abi_version, hessian_accum, ldl, ldl_pair,
-    quantize_layer, release_workspace, rht, rotate_layer, sketch_b, solve,
+    layer_report, quantize_layer, release_workspace, rht, rotate_layer, sketch_b, solve,
 )

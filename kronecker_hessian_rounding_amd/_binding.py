@@ -60,6 +60,8 @@ def _load() -> ctypes.CDLL:
     lib.bakron_ldl.argtypes = [vp, i64, i64, ctypes.c_double, vp, ctypes.POINTER(i64), vp, sz, vp]
     lib.bakron_ldl_async.restype = ctypes.c_int
     lib.bakron_ldl_async.argtypes = [vp, i64, i64, ctypes.c_double, vp, vp, vp, sz, vp]
+    lib.bakron_layer_report.restype = ctypes.c_int
+    lib.bakron_layer_report.argtypes = [i64, i64, vp, vp, vp, vp, i64, vp, i64, vp, vp]
     lib.bakron_rht.restype = ctypes.c_int
     lib.bakron_rht.argtypes = [vp, i64, i64, i64, ctypes.c_int, ctypes.c_uint64, ctypes.c_int, vp]
     lib.bakron_solve_workspace_bytes.restype = sz
@@ -74,7 +76,8 @@ LIB = _load()
 
 EXPORTS = ("bakron_abi_version", "bakron_status_str", "bakron_hessian_accum_workspace_bytes",
            "bakron_hessian_accum", "bakron_hessian_accum_t", "bakron_ldl_workspace_bytes", "bakron_ldl", "bakron_ldl_async",
-           "bakron_solve_workspace_bytes", "bakron_solve", "bakron_rht")
+           "bakron_solve_workspace_bytes", "bakron_solve", "bakron_rht",
+           "bakron_layer_report")
 
 
 def abi_version() -> int:
@@ -311,6 +314,27 @@ def solve(W: torch.Tensor, L_O: Optional[torch.Tensor], L_I: Optional[torch.Tens
                           _ptr(out.clamped), _ptr(out.info), _ptr(ws), nb, _stream())
     _check("bakron_solve", st)
     return out
+
+
+def layer_report(D_O: Optional[torch.Tensor], D_I: torch.Tensor, scales: torch.Tensor,
+                 H_I: Optional[torch.Tensor] = None, H_O: Optional[torch.Tensor] = None) -> dict:
+    """Bound and sensitivity terms of a rounded layer (fp64 sums on the device).
+
+    Keys: tr_DO, tr_DI, bound_sharp, bound_page, tr_HI, tr_HO (NaN when not given;
+    pass the factors before ldl, which writes D over their diagonal), sensitivity
+    = tr_HI * tr_HO.
+    """
+    n = int(D_I.shape[0])
+    m = int(scales.shape[0])
+    ldhi = _mat(H_I, "H_I") if H_I is not None else 0
+    ldho = _mat(H_O, "H_O") if H_O is not None else 0
+    out = torch.empty(7, dtype=torch.float64, device=D_I.device)
+    _check("bakron_layer_report", LIB.bakron_layer_report(m, n, _ptr(D_O), _ptr(D_I), _ptr(scales),
+                                                          _ptr(H_I), ldhi, _ptr(H_O), ldho, _ptr(out),
+                                                          _stream()))
+    v = out.cpu().tolist()
+    keys = ("tr_DO", "tr_DI", "bound_sharp", "bound_page", "tr_HI", "tr_HO", "sensitivity")
+    return dict(zip(keys, v))
 
 
 def rht(A: torch.Tensor, axis: int, seed: int, transpose: bool = False) -> torch.Tensor:

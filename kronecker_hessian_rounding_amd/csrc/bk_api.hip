@@ -117,6 +117,14 @@ int bakron_solve(const float* W, int64_t m, int64_t n, int64_t ldw, const float*
     return bk::run_solve(a, ws, (hipStream_t)stream);
 }
 
+int bakron_layer_report(int64_t m, int64_t n, const float* D_O, const float* D_I, const float* scales,
+                        const float* H_I, int64_t ldhi, const float* H_O, int64_t ldho, double* out,
+                        void* stream) {
+    if (m <= 0 || n <= 0 || !D_I || !scales || !out) return BAKRON_E_INVALID_ARG;
+    if ((H_I && bad_ld(ldhi, n)) || (H_O && bad_ld(ldho, m))) return BAKRON_E_INVALID_ARG;
+    return bk::launch_layer_report(m, n, D_O, D_I, scales, H_I, ldhi, H_O, ldho, out, (hipStream_t)stream);
+}
+
 int bakron_rht(float* A, int64_t rows, int64_t cols, int64_t lda, int axis, uint64_t seed, int transpose,
                void* stream) {
     if (!A || rows <= 0 || cols <= 0 || bad_ld(lda, cols) || (axis != 0 && axis != 1))

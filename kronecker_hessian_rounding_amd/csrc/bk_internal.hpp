@@ -32,6 +32,11 @@ int run_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, int64_t
 int launch_rht(float* A, int64_t rows, int64_t cols, int64_t lda, int axis, uint64_t seed, int transpose,
                hipStream_t stream);
 
+// --- bound and sensitivity report (bk_report.hip) ---
+int launch_layer_report(int64_t m, int64_t n, const float* DO, const float* DI, const float* scales,
+                        const float* HI, int64_t ldhi, const float* HO, int64_t ldho, double* out,
+                        hipStream_t stream);
+
 // --- rounding solve (bk_solve.hip) ---
 struct SolveArgs {
     const float* W;

@@ -152,3 +152,18 @@ def test_hessian_accum_t_rejects_invalid_arguments(lib):
     assert f(fake, 16, 0, 16, 1.0, 0.0, fake, 8, fake, 1 << 30, None) == INVALID  # d <= 0
     assert f(None, 16, 8, 16, 1.0, 0.0, fake, 8, fake, 1 << 30, None) == INVALID  # X missing
     assert f(fake, 16, 8, 16, 1.0, 0.0, fake, 8, None, 0, None) == WORKSPACE      # no workspace
+
+
+def test_layer_report_rejects_invalid_arguments(lib):
+    f = lib.bakron_layer_report
+    f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    INVALID = 1
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: the arguments fail first
+    assert f(0, 4, fake, fake, fake, None, 0, None, 0, fake, None) == INVALID
+    assert f(4, 4, fake, None, fake, None, 0, None, 0, fake, None) == INVALID   # no D_I
+    assert f(4, 4, fake, fake, None, None, 0, None, 0, fake, None) == INVALID   # no scales
+    assert f(4, 4, fake, fake, fake, None, 0, None, 0, None, None) == INVALID   # no out
+    assert f(4, 8, fake, fake, fake, fake, 7, None, 0, fake, None) == INVALID   # ld(H_I) < n

@@ -575,3 +575,32 @@ def test_sketch_b_matches_oracle(bk, S, m, n):
     assert np.all(np.abs(HI - ri) <= bi), np.max(np.abs(HI - ri) / bi)
     assert np.all(np.abs(HO - ro) <= bo), np.max(np.abs(HO - ro) / bo)
     assert np.array_equal(HI, HI.T) and np.array_equal(HO, HO.T)
+
+
+# ----------------------------------------------------------------------------
+# per-layer bound and sensitivity report (YAQA article, section 4; KronQ page)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("m,n,one_sided", [(64, 48, False), (300, 257, False), (40, 3000, True)])
+def test_layer_report_matches_oracle(bk, m, n, one_sided):
+    note("layer report m=%d n=%d one_sided=%d" % (m, n, one_sided))
+    rng = np.random.default_rng(m + n)
+    DO = None if one_sided else rng.lognormal(0.0, 1.0, m).astype(np.float32)
+    DI = rng.lognormal(0.0, 1.0, n).astype(np.float32)
+    s = rng.lognormal(-4.0, 0.5, m).astype(np.float32)
+    HO = rng.standard_normal((m, m)).astype(np.float32)
+    T = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+    HIt = torch.from_numpy(rng.standard_normal((n, n + 3)).astype(np.float32)).to(dev())
+    HIv = HIt[:, :n]  # a view with leading dimension n + 3
+    hi = HIv.cpu().numpy()
+    r = bk.layer_report(T(DO), T(DI), T(s), H_I=HIv, H_O=T(HO))
+    do = np.ones(m) if DO is None else DO
+    sharp, page = oracle.bound_terms(s, do, DI)
+    want = dict(tr_DO=float(np.sum(do, dtype=np.float64)), tr_DI=float(np.sum(DI, dtype=np.float64)),
+                bound_sharp=sharp, bound_page=page, tr_HI=float(np.trace(hi.astype(np.float64))),
+                tr_HO=float(np.trace(HO.astype(np.float64))))
+    want["sensitivity"] = want["tr_HI"] * want["tr_HO"]
+    for k, v in want.items():
+        assert abs(r[k] - v) <= 1e-12 * max(1.0, abs(v)), (k, r[k], v)
+    r2 = bk.layer_report(T(DO), T(DI), T(s))
+    assert np.isnan(r2["tr_HI"]) and np.isnan(r2["tr_HO"]) and np.isnan(r2["sensitivity"])
+    assert r2["bound_sharp"] == r["bound_sharp"]
