@@ -9,7 +9,8 @@ Sources (cited by page title and section):
             Hessian is approximated by a Kronecker product H_O (m x m) (x)
             H_I (n x n) of the vectorised weight.
   [YAQA-3]  same article, section 3: H_I = E[x^T x] over tokens (the
-            initialisation H_1 of Sketch A); Sketch B, one round of power
+            initialisation H_1 of Sketch A); Sketch A, the alternating
+            estimator with per-token weights <H, y^T y> / ||H||_F^2; Sketch B, one round of power
             iteration from H_I = H_O = I: H_I = E_s[G_s^T G_s] / m and
             H_O = E_s[G_s G_s^T] / n over per-sequence weight gradients G_s.
   [YAQA-4]  same article, section 4: the rounding rule
@@ -56,7 +57,7 @@ __all__ = [
     "hessian", "hessian_entries", "damp", "udu", "udu_lapack", "row_scales", "sweep",
     "replay", "replay_rows", "proxy_loss", "loss_identity", "bound_terms", "splitmix64",
     "uniform_matrix", "pipeline", "rht_signs", "rht_block", "sylvester", "rht_matrix",
-    "rht_apply", "rotate_layer", "sketch_b",
+    "rht_apply", "rotate_layer", "sketch_b", "token_weights", "sketch_a",
 ]
 
 _lib = None
@@ -492,3 +493,34 @@ def sketch_b(grads):
         HI += g.T @ g
         HO += g @ g.T
     return HI / (S * m), HO / (S * n)
+
+
+# --------------------------------------------------------------------------
+# Sketch A [YAQA-3]: tokens are taken as independent, and the factors are
+# updated in turn, each token weighted by the other factor's quadratic form:
+#   (H_I)_i = E_t[x_t^T x_t <(H_O)_{i-1}, g_t^T g_t>] / ||(H_O)_{i-1}||_F^2
+#   (H_O)_i = E_t[g_t^T g_t <(H_I)_{i-1}, x_t^T x_t>] / ||(H_I)_{i-1}||_F^2
+# from (H_I)_0 = E[x^T x] and (H_O)_0 = I; <H, y^T y> = y H y^T. Both updates of
+# an iteration use the previous iterates.
+# --------------------------------------------------------------------------
+def token_weights(Y, H=None) -> np.ndarray:
+    """w_t = y_t H y_t^T / ||H||_F^2 for the rows y_t of Y (fp64); H None means the identity."""
+    Y = np.asarray(Y, np.float64)
+    if H is None:
+        return np.sum(Y * Y, axis=1) / Y.shape[1]
+    H = np.asarray(H, np.float64)
+    return np.einsum("tk,kc,tc->t", Y, H, Y, optimize=True) / np.sum(H * H)
+
+
+def sketch_a(X, G, iters: int = 3):
+    """(H_I, H_O) after `iters` Sketch A iterations (fp64)."""
+    X = np.asarray(X, np.float64)
+    G = np.asarray(G, np.float64)
+    T = X.shape[0]
+    HI = X.T @ X / T
+    HO = None
+    for _ in range(iters):
+        w = token_weights(G, HO)
+        v = token_weights(X, HI)
+        HI, HO = (X * w[:, None]).T @ X / T, (G * v[:, None]).T @ G / T
+    return HI, HO

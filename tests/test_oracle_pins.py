@@ -710,3 +710,54 @@ def test_sketch_b_brute_force():
         for j in range(3):
             want = sum(g[i][b] * g[j][b] for g in grads for b in range(4)) / (2 * 4)
             assert abs(HO[i, j] - want) <= 1e-13
+
+
+# ----------------------------------------------------------------------------
+# Sketch A (YAQA article, section 3): alternating factor estimates with
+# per-token weights <H, y^T y> / ||H||_F^2, from H_I = E[x^T x] and H_O = I
+# ----------------------------------------------------------------------------
+def test_sketch_a_first_step_with_equal_gradient_norms():
+    # with ||g_t|| the same for every token the first H_I is E[x^T x] scaled by ||g||^2 / m
+    rng = np.random.default_rng(21)
+    T, n, m = 200, 6, 5
+    X = rng.standard_normal((T, n))
+    G = rng.standard_normal((T, m))
+    G *= 3.0 / np.linalg.norm(G, axis=1, keepdims=True)
+    HI, _ = oracle.sketch_a(X, G, 1)
+    assert np.allclose(HI, (9.0 / m) * (X.T @ X / T), rtol=1e-12)
+
+
+def test_sketch_a_brute_force_two_iterations():
+    rng = np.random.default_rng(22)
+    T, n, m = 7, 3, 4
+    X = rng.standard_normal((T, n))
+    G = rng.standard_normal((T, m))
+
+    def quad(y, H):
+        return sum(y[a] * H[a][b] * y[b] for a in range(len(y)) for b in range(len(y)))
+
+    def fro2(H):
+        return sum(H[a][b] ** 2 for a in range(len(H)) for b in range(len(H)))
+
+    HI = [[sum(X[t][a] * X[t][b] for t in range(T)) / T for b in range(n)] for a in range(n)]
+    HO = [[1.0 if a == b else 0.0 for b in range(m)] for a in range(m)]
+    for _ in range(2):
+        w = [quad(G[t], HO) / fro2(HO) for t in range(T)]
+        v = [quad(X[t], HI) / fro2(HI) for t in range(T)]
+        HI, HO = ([[sum(w[t] * X[t][a] * X[t][b] for t in range(T)) / T for b in range(n)] for a in range(n)],
+                  [[sum(v[t] * G[t][a] * G[t][b] for t in range(T)) / T for b in range(m)] for a in range(m)])
+    hi, ho = oracle.sketch_a(X, G, 2)
+    assert np.allclose(hi, np.array(HI), rtol=1e-12, atol=1e-15)
+    assert np.allclose(ho, np.array(HO), rtol=1e-12, atol=1e-15)
+
+
+def test_token_weights_identity_and_scale():
+    rng = np.random.default_rng(23)
+    Y = rng.standard_normal((9, 5))
+    assert np.allclose(oracle.token_weights(Y), np.sum(Y * Y, axis=1) / 5, rtol=1e-14)
+    H = spd(5, 3)
+    # <aH, y^T y> / ||aH||_F^2 = (1/a) <H, y^T y> / ||H||_F^2
+    assert np.allclose(oracle.token_weights(Y, 7.0 * H), oracle.token_weights(Y, H) / 7.0, rtol=1e-13)
+    # and against the quadratic form written out
+    want = np.array([sum(y[a] * H[a, b] * y[b] for a in range(5) for b in range(5)) for y in Y]) / np.sum(H * H)
+    assert np.allclose(oracle.token_weights(Y, H), want, rtol=1e-12)
