@@ -131,6 +131,29 @@ int bakron_hessian_accum_t(const float* X, int64_t T, int64_t d, int64_t ldx, fl
                            void* stream);
 
 /*
+ * Sketch A (YAQA article, section 3) alternates the two factors, each token
+ * weighted by the other factor's quadratic form:
+ *   (H_I)_i = E_t[x_t^T x_t w_t], w_t = g_t (H_O)_{i-1} g_t^T / ||(H_O)_{i-1}||_F^2,
+ * and likewise (H_O)_i with v_t = x_t (H_I)_{i-1} x_t^T / ||(H_I)_{i-1}||_F^2.
+ *
+ * bakron_token_weights: w[t] = y_t H y_t^T / ||H||_F^2 for the rows y_t of Y
+ *   (T x d, ldy >= d), H d x d symmetric (ldh >= d); H == NULL means H = I,
+ *   w[t] = ||y_t||^2 / d. The quadratic forms run as fp32 MFMA tile GEMMs and
+ *   are summed in a fixed order; ||H||_F^2 in fp64. ws: with H given, at least
+ *   bakron_token_weights_workspace_bytes(T, d) (Y transposed, d T floats).
+ * bakron_hessian_accum_w: H <- beta H + alpha sum_t w[t] x_t^T x_t for w >= 0
+ *   (negative weights count as 0), X as in bakron_hessian_accum, on the
+ *   three-piece path (ws at least bakron_hessian_accum_workspace_bytes(T, d)).
+ * Errors: INVALID_ARG for NULL pointers, d <= 0, T < 0, bad ld; WORKSPACE for a
+ * missing or short workspace.
+ */
+size_t bakron_token_weights_workspace_bytes(int64_t T, int64_t d);
+int bakron_token_weights(const float* Y, int64_t T, int64_t d, int64_t ldy, const float* H, int64_t ldh,
+                         float* w, void* ws, size_t ws_bytes, void* stream);
+int bakron_hessian_accum_w(const float* X, int64_t T, int64_t d, int64_t ldx, const float* w, float alpha,
+                           float beta, float* H, int64_t ldh, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Damped LDL factorisation (YAQA section 4): with lambda = damp_rel * mean(diag H)
  * (the mean of the undamped diagonal, in fp64), factor
  *     H + lambda I = (L + I) diag(D) (L + I)^T,  L strictly UPPER triangular,

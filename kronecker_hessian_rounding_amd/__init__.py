@@ -6,6 +6,7 @@ tensors for device memory and uses the current stream.
 
   hessian_accum(X)            H <- beta H + alpha X^T X            (bf16 pieces, fp32 accuracy)
   sketch_b(grads)             H_I = E[G^T G]/m, H_O = E[G G^T]/n from per-sequence gradients
+  sketch_a(X, G, iters)       alternating factor estimate with per-token weights
   ldl(H, damp_rel)            H + lambda I = (L + I) D (L + I)^T   (fp64, L strictly upper)
   ldl_pair(HA, HB, damp_rel)  two independent factorisations side by side on two streams
   solve(W, L_O, L_I, bits)    BaKron rounding: codes, scales, error, proxy loss
@@ -15,5 +16,6 @@ tensors for device memory and uses the current stream.
 from ._binding import (  # noqa: F401
     BAKRON_E_DEVICE, BAKRON_E_INVALID_ARG, BAKRON_E_NOT_SPD, BAKRON_E_WORKSPACE, BAKRON_OK,
     EXPORTS, LIB, LIB_PATH, BakronError, SolveResult, abi_version, hessian_accum, ldl, ldl_pair,
-    layer_report, quantize_layer, release_workspace, rht, rotate_layer, sketch_b, solve,
+    layer_report, quantize_layer, release_workspace, rht, rotate_layer, sketch_a, sketch_b, solve,
+    token_weights,
 )

@@ -54,6 +54,12 @@ def _load() -> ctypes.CDLL:
     lib.bakron_hessian_accum.argtypes = [vp, i64, i64, i64, f32, f32, vp, i64, vp, sz, vp]
     lib.bakron_hessian_accum_t.restype = ctypes.c_int
     lib.bakron_hessian_accum_t.argtypes = [vp, i64, i64, i64, f32, f32, vp, i64, vp, sz, vp]
+    lib.bakron_hessian_accum_w.restype = ctypes.c_int
+    lib.bakron_hessian_accum_w.argtypes = [vp, i64, i64, i64, vp, f32, f32, vp, i64, vp, sz, vp]
+    lib.bakron_token_weights_workspace_bytes.restype = sz
+    lib.bakron_token_weights_workspace_bytes.argtypes = [i64, i64]
+    lib.bakron_token_weights.restype = ctypes.c_int
+    lib.bakron_token_weights.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, sz, vp]
     lib.bakron_ldl_workspace_bytes.restype = sz
     lib.bakron_ldl_workspace_bytes.argtypes = [i64]
     lib.bakron_ldl.restype = ctypes.c_int
@@ -75,7 +81,8 @@ def _load() -> ctypes.CDLL:
 LIB = _load()
 
 EXPORTS = ("bakron_abi_version", "bakron_status_str", "bakron_hessian_accum_workspace_bytes",
-           "bakron_hessian_accum", "bakron_hessian_accum_t", "bakron_ldl_workspace_bytes", "bakron_ldl", "bakron_ldl_async",
+           "bakron_hessian_accum", "bakron_hessian_accum_t", "bakron_hessian_accum_w",
+           "bakron_token_weights_workspace_bytes", "bakron_token_weights", "bakron_ldl_workspace_bytes", "bakron_ldl", "bakron_ldl_async",
            "bakron_solve_workspace_bytes", "bakron_solve", "bakron_rht",
            "bakron_layer_report")
 
@@ -149,13 +156,15 @@ def _aux_stream(device) -> torch.cuda.Stream:
 
 # --------------------------------------------------------------------------
 def hessian_accum(X: torch.Tensor, H: Optional[torch.Tensor] = None, alpha: Optional[float] = None,
-                  beta: float = 0.0, pieces: bool = True, transposed: bool = False) -> torch.Tensor:
+                  beta: float = 0.0, pieces: bool = True, transposed: bool = False,
+                  weights: Optional[torch.Tensor] = None) -> torch.Tensor:
     """H <- beta H + alpha X^T X (default alpha = 1/T) on the device.
 
     pieces=True passes the full workspace: each fp32 product is formed from three
     bf16 pieces per operand on the bf16 matrix cores. pieces=False passes none,
     which selects the fp32 matrix-core path. transposed=True takes X as d x T and
-    forms alpha X X^T (three-piece path only).
+    forms alpha X X^T (three-piece path only). weights (T,) forms
+    alpha sum_t w_t x_t^T x_t (three-piece path only).
     """
     ldx = _mat(X, "X")
     if transposed:
@@ -173,10 +182,52 @@ def hessian_accum(X: torch.Tensor, H: Optional[torch.Tensor] = None, alpha: Opti
         alpha = 1.0 / max(T, 1)
     nb = LIB.bakron_hessian_accum_workspace_bytes(T, d) if pieces else 0
     ws = _workspace(nb, X.device)
+    if weights is not None:
+        if transposed or not pieces:
+            raise ValueError("token weights take the untransposed three-piece path")
+        wv = _vec(weights, "weights", T)
+        _check("bakron_hessian_accum_w",
+               LIB.bakron_hessian_accum_w(_ptr(X), T, d, ldx, _ptr(wv), alpha, beta, _ptr(H), ldh, _ptr(ws),
+                                          nb, _stream()))
+        return H
     fn = LIB.bakron_hessian_accum_t if transposed else LIB.bakron_hessian_accum
     _check("bakron_hessian_accum_t" if transposed else "bakron_hessian_accum",
            fn(_ptr(X), T, d, ldx, alpha, beta, _ptr(H), ldh, _ptr(ws), nb, _stream()))
     return H
+
+
+def token_weights(Y: torch.Tensor, H: Optional[torch.Tensor] = None,
+                  w: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """w_t = y_t H y_t^T / ||H||_F^2 for the rows of Y (T x d); H None means the identity."""
+    ldy = _mat(Y, "Y")
+    T, d = Y.shape
+    ldh = 0
+    if H is not None:
+        ldh = _mat(H, "H")
+        if tuple(H.shape) != (d, d):
+            raise ValueError("H must be %d x %d" % (d, d))
+    if w is None:
+        w = torch.empty(T, dtype=torch.float32, device=Y.device)
+    nb = LIB.bakron_token_weights_workspace_bytes(T, d) if H is not None else 0
+    ws = _workspace(nb, Y.device, slot=1)
+    _check("bakron_token_weights", LIB.bakron_token_weights(_ptr(Y), T, d, ldy, _ptr(H), ldh, _ptr(w),
+                                                            _ptr(ws), nb, _stream()))
+    return w
+
+
+def sketch_a(X: torch.Tensor, G: torch.Tensor, iters: int = 3):
+    """Sketch A factors (YAQA article, section 3) from token inputs X (T x n) and output
+    gradients G (T x m): `iters` alternating updates from E[x^T x] and I. Returns (H_I, H_O)."""
+    T = X.shape[0]
+    HI = hessian_accum(X)
+    HO = None
+    for _ in range(iters):
+        w = token_weights(G, HO)
+        v = token_weights(X, HI)
+        HI_new = hessian_accum(X, alpha=1.0 / T, weights=w)
+        HO = hessian_accum(G, HO, alpha=1.0 / T, weights=v)
+        HI = HI_new
+    return HI, HO
 
 
 def sketch_b(grads, HI: Optional[torch.Tensor] = None, HO: Optional[torch.Tensor] = None):

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "libbakron.so")
-SOURCES = ["bk_api.hip", "bk_accum.hip", "bk_ldl.hip", "bk_solve.hip", "bk_rotate.hip", "bk_report.hip"]
+SOURCES = ["bk_api.hip", "bk_accum.hip", "bk_ldl.hip", "bk_solve.hip", "bk_rotate.hip", "bk_report.hip", "bk_sketch.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -472,10 +472,13 @@ __device__ __forceinline__ void split3_value(float x, uint32_t& h, uint32_t& m, 
 // otherwise; thread t then splits columns t, t + 256, t + 512, t + 768, so each
 // store instruction writes 1 KB of consecutive 16-byte units of a plane.
 constexpr int kSplitCols = 4 * kThreads;
+// wt (optional): token weights; row k is scaled by sqrt(max(wt[k], 0)) before the
+// split, which turns the SYRK into sum_k wt[k] x_k^T x_k.
 template <bool kVec>
 __global__ __launch_bounds__(kThreads) void k_split3(const float* __restrict__ X, int64_t T,
                                                      int64_t d, int64_t ldx, int64_t ng,
-                                                     int64_t dp, uint4* __restrict__ Xs) {
+                                                     int64_t dp, uint4* __restrict__ Xs,
+                                                     const float* __restrict__ wt) {
     __shared__ float tile[8][kSplitCols];
     const int t = threadIdx.x;
     const int64_t cb = (int64_t)blockIdx.x * kSplitCols;
@@ -496,6 +499,7 @@ __global__ __launch_bounds__(kThreads) void k_split3(const float* __restrict__ X
                         if (c4 + j < d) v[j] = row[j];
                 }
             }
+            if (wt && k < T) v *= sqrtf(fmaxf(wt[k], 0.0f));
             *reinterpret_cast<f32x4*>(&tile[e][4 * t]) = v;
         }
         __syncthreads();
@@ -766,7 +770,7 @@ size_t hessian_workspace_bytes(int64_t T, int64_t d) {
 
 int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, float alpha,
                          float beta, float* H, int64_t ldh, void* ws, size_t ws_bytes,
-                         hipStream_t stream, bool trans) {
+                         hipStream_t stream, bool trans, const float* wt) {
     const int64_t nb = (d + kT128 - 1) / kT128;
     const int64_t tiles = nb * (nb + 1) / 2;
     if (tiles > 0x7fffffff) return BAKRON_E_INVALID_ARG;
@@ -787,9 +791,11 @@ int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, floa
             const dim3 grid((unsigned)((sh.dp + kSplitCols - 1) / kSplitCols), gy);
             const bool vec = (ldx & 3) == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0;
             if (vec)
-                hipLaunchKernelGGL(k_split3<true>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, sh.ng, sh.dp, Xs);
+                hipLaunchKernelGGL(k_split3<true>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, sh.ng, sh.dp, Xs,
+                                   wt);
             else
-                hipLaunchKernelGGL(k_split3<false>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, sh.ng, sh.dp, Xs);
+                hipLaunchKernelGGL(k_split3<false>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, sh.ng, sh.dp, Xs,
+                                   wt);
         }
         const SyrkPlan pl = plan_tiles(tiles, resident_slots(sizeof(Split3Ring)), sh.nstage,
                                        ws_bytes - sh.bytes);
@@ -806,7 +812,7 @@ int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, floa
         return hipGetLastError() == hipSuccess ? BAKRON_OK : BAKRON_E_DEVICE;
     }
     // the fp32-MFMA path (no room for the pieces); it reads X as T x d only
-    if (trans) return BAKRON_E_WORKSPACE;
+    if (trans || wt) return BAKRON_E_WORKSPACE;
     const int64_t nsl = (T + kSyKT - 1) / kSyKT;
     const SyrkPlan pl = plan_tiles(tiles, resident_slots(sizeof(SyrkShared)), nsl,
                                    ws != nullptr ? ws_bytes : 0);

@@ -48,6 +48,27 @@ int bakron_hessian_accum_t(const float* X, int64_t T, int64_t d, int64_t ldx, fl
                                     (hipStream_t)stream, true);
 }
 
+int bakron_hessian_accum_w(const float* X, int64_t T, int64_t d, int64_t ldx, const float* w, float alpha,
+                           float beta, float* H, int64_t ldh, void* ws, size_t ws_bytes, void* stream) {
+    if (!H || d <= 0 || T < 0 || bad_ld(ldh, d)) return BAKRON_E_INVALID_ARG;
+    if (T > 0 && (!X || !w || bad_ld(ldx, d))) return BAKRON_E_INVALID_ARG;
+    if (!ws || ws_bytes < bk::hessian_workspace_bytes(T, d)) return BAKRON_E_WORKSPACE;
+    return bk::launch_hessian_accum(X, T, d, ldx, alpha, beta, H, ldh, ws, ws_bytes, (hipStream_t)stream,
+                                    false, w);
+}
+
+size_t bakron_token_weights_workspace_bytes(int64_t T, int64_t d) {
+    if (d <= 0 || T < 0) return 0;
+    return bk::token_weights_workspace_bytes(T, d);
+}
+
+int bakron_token_weights(const float* Y, int64_t T, int64_t d, int64_t ldy, const float* H, int64_t ldh,
+                         float* w, void* ws, size_t ws_bytes, void* stream) {
+    if (d <= 0 || T < 0 || (T > 0 && (!Y || !w || bad_ld(ldy, d))) || (H && bad_ld(ldh, d)))
+        return BAKRON_E_INVALID_ARG;
+    return bk::launch_token_weights(Y, T, d, ldy, H, ldh, w, ws, ws_bytes, (hipStream_t)stream);
+}
+
 size_t bakron_ldl_workspace_bytes(int64_t d) {
     if (d <= 0) return 0;
     return bk::ldl_workspace_bytes(d);

@@ -14,10 +14,16 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // --- Hessian factor accumulation (bk_accum.hip) ---
 size_t hessian_workspace_bytes(int64_t T, int64_t d);
-// trans: X is stored d x T (H = X X^T); needs the workspace of the piece path
+// trans: X is stored d x T (H = X X^T); wt: per-token weights (H = sum_k wt_k
+// x_k^T x_k); both need the workspace of the piece path
 int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, float alpha,
                          float beta, float* H, int64_t ldh, void* ws, size_t ws_bytes,
-                         hipStream_t stream, bool trans = false);
+                         hipStream_t stream, bool trans = false, const float* wt = nullptr);
+
+// --- Sketch A token weights (bk_sketch.hip) ---
+size_t token_weights_workspace_bytes(int64_t T, int64_t d);
+int launch_token_weights(const float* Y, int64_t T, int64_t d, int64_t ldy, const float* H, int64_t ldh,
+                         float* w, void* ws, size_t ws_bytes, hipStream_t stream);
 
 // --- LDL factorisation (bk_ldl.hip) ---
 size_t ldl_workspace_bytes(int64_t d);

@@ -167,3 +167,24 @@ def test_layer_report_rejects_invalid_arguments(lib):
     assert f(4, 4, fake, fake, None, None, 0, None, 0, fake, None) == INVALID   # no scales
     assert f(4, 4, fake, fake, fake, None, 0, None, 0, None, None) == INVALID   # no out
     assert f(4, 8, fake, fake, fake, fake, 7, None, 0, fake, None) == INVALID   # ld(H_I) < n
+
+
+def test_sketch_a_entry_points_reject_invalid_arguments(lib):
+    fw = lib.bakron_token_weights
+    fw.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    fw.restype = ctypes.c_int
+    fa = lib.bakron_hessian_accum_w
+    fa.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                   ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                   ctypes.c_size_t, ctypes.c_void_p]
+    fa.restype = ctypes.c_int
+    INVALID, WORKSPACE = 1, 3
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: the arguments fail first
+    assert fw(fake, 10, 0, 4, None, 0, fake, None, 0, None) == INVALID       # d <= 0
+    assert fw(fake, 10, 4, 3, None, 0, fake, None, 0, None) == INVALID       # ldy < d
+    assert fw(fake, 10, 4, 4, fake, 3, fake, None, 0, None) == INVALID       # ldh < d
+    assert fw(fake, 10, 4, 4, fake, 4, fake, None, 0, None) == WORKSPACE     # H given, no workspace
+    assert fa(fake, 10, 4, 4, None, 1.0, 0.0, fake, 4, fake, 1 << 30, None) == INVALID  # no weights
+    assert fa(fake, 10, 4, 4, fake, 1.0, 0.0, fake, 4, None, 0, None) == WORKSPACE
+    assert lib.bakron_token_weights_workspace_bytes(10, 0) == 0

@@ -604,3 +604,71 @@ def test_layer_report_matches_oracle(bk, m, n, one_sided):
     r2 = bk.layer_report(T(DO), T(DI), T(s))
     assert np.isnan(r2["tr_HI"]) and np.isnan(r2["tr_HO"]) and np.isnan(r2["sensitivity"])
     assert r2["bound_sharp"] == r["bound_sharp"]
+
+
+# ----------------------------------------------------------------------------
+# Sketch A: token weights and the weighted accumulation (YAQA article, section 3)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("T,d,identity", [(100, 64, False), (333, 129, False), (64, 5, False),
+                                          (1000, 300, False), (77, 40, True)])
+def test_token_weights_match_oracle(bk, T, d, identity):
+    note("token weights T=%d d=%d identity=%d" % (T, d, identity))
+    y = workloads.make_x(T, d, 60 + d, "gauss", 2 if d > 2 else 0)
+    H = None if identity else oracle.hessian(workloads.make_x(4 * d, d, 61 + d, "gauss", 0)).astype(np.float32)
+    Ht = None if H is None else torch.from_numpy(H).to(dev())
+    w = bk.token_weights(torch.from_numpy(y).to(dev()), Ht).cpu().numpy().astype(np.float64)
+    ref = oracle.token_weights(y, None if H is None else H.astype(np.float64))
+    if identity:
+        assert np.all(np.abs(w - ref) <= 2 * U32 * ref)
+    else:
+        ay = np.abs(y.astype(np.float64))
+        h64 = H.astype(np.float64)
+        mag = np.einsum("tk,kc,tc->t", ay, np.abs(h64), ay) / np.sum(h64 * h64)
+        assert np.all(np.abs(w - ref) <= 4 * U32 * np.sqrt(d) * mag + 2 * U32 * np.abs(ref))
+
+
+@pytest.mark.parametrize("T,d", [(1024, 64), (2000, 129), (333, 100)])
+def test_hessian_accum_weighted_matches_oracle(bk, T, d):
+    note("hessian weighted T=%d d=%d" % (T, d))
+    x = workloads.make_x(T, d, 70 + d, "gauss", 2)
+    wt = np.random.default_rng(d).lognormal(0.0, 1.0, T).astype(np.float32)
+    wt[::7] = 0.0
+    H = bk.hessian_accum(torch.from_numpy(x).to(dev()), alpha=1.0 / T,
+                         weights=torch.from_numpy(wt).to(dev())).cpu().numpy()
+    x64, w64 = x.astype(np.float64), wt.astype(np.float64)
+    ref = (x64 * w64[:, None]).T @ x64 / T
+    ax = np.abs(x64)
+    # the fp32 sqrt(w) scaling (2 u relative on each product) on top of the fp32 SYRK bound
+    bound = (4 * np.sqrt(T) + 4) * U32 * (ax * w64[:, None]).T @ ax / T + 1e-30
+    assert np.all(np.abs(H - ref) <= bound), np.max(np.abs(H - ref) / bound)
+    assert np.array_equal(H, H.T)
+
+
+def test_sketch_a_matches_oracle(bk):
+    # each device iteration against the oracle's step from the device's previous
+    # iterates (so that errors do not compound), then three iterations end to end
+    T, n, m = 2048, 96, 80
+    w_, x, g = workloads.make_inputs("tiny", m=m, n=n, T=T)
+    note("sketch A T=%d n=%d m=%d" % (T, n, m))
+    X, G = torch.from_numpy(x).to(dev()), torch.from_numpy(g).to(dev())
+    HI, HO = bk.hessian_accum(X), None
+    x64, g64 = x.astype(np.float64), g.astype(np.float64)
+    for it in range(3):
+        hi_prev = HI.cpu().numpy().astype(np.float64)
+        ho_prev = None if HO is None else HO.cpu().numpy().astype(np.float64)
+        w = bk.token_weights(G, HO)
+        v = bk.token_weights(X, HI)
+        HI_new = bk.hessian_accum(X, alpha=1.0 / T, weights=w)
+        HO = bk.hessian_accum(G, HO, alpha=1.0 / T, weights=v)
+        HI = HI_new
+        wr = oracle.token_weights(g64, ho_prev)
+        vr = oracle.token_weights(x64, hi_prev)
+        hi_ref = (x64 * wr[:, None]).T @ x64 / T
+        ho_ref = (g64 * vr[:, None]).T @ g64 / T
+        for got, ref in ((HI, hi_ref), (HO, ho_ref)):
+            rel = np.linalg.norm(got.cpu().numpy() - ref) / np.linalg.norm(ref)
+            assert rel < 1e-5, (it, rel)
+    hi3, ho3 = bk.sketch_a(X, G, 3)
+    ri, ro = oracle.sketch_a(x64, g64, 3)
+    assert np.linalg.norm(hi3.cpu().numpy() - ri) / np.linalg.norm(ri) < 1e-5
+    assert np.linalg.norm(ho3.cpu().numpy() - ro) / np.linalg.norm(ro) < 1e-5
