@@ -74,9 +74,11 @@ def parse():
     ap.add_argument("--rounding", default="nearest", choices=["nearest", "stochastic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the CPU sweep sample")
-    ap.add_argument("--hessian", default="tokens", choices=["tokens", "sketch_b"],
-                    help="factor estimate: X^T X / T and G^T G / T over tokens, or Sketch B from "
-                         "per-sequence weight gradients")
+    ap.add_argument("--hessian", default="tokens", choices=["tokens", "sketch_a", "sketch_b"],
+                    help="factor estimate: X^T X / T and G^T G / T over tokens, Sketch A (alternating, "
+                         "per-token weights) on the same X and G, or Sketch B from per-sequence weight "
+                         "gradients")
+    ap.add_argument("--iters", type=int, default=3, help="Sketch A iterations")
     ap.add_argument("--sequences", type=int, default=8, help="gradients per step for Sketch B")
     ap.add_argument("--rotate", action="store_true",
                     help="two-sided incoherence rotation of W, H_I and H_O before the LDL "
@@ -177,7 +179,8 @@ def main():
     sketch = args.hessian == "sketch_b"
     if sketch:
         grads = torch.from_numpy(workloads.make_grads(args.sequences, m, n, 5000 + wl.key)).to(dev)
-    hess_phases = ("hess_sketch_b",) if sketch else ("hess_I", "hess_O")
+    hess_phases = {"tokens": ("hess_I", "hess_O"), "sketch_b": ("hess_sketch_b",),
+                   "sketch_a": ("hess_sketch_a",)}[args.hessian]
     phases = hess_phases + (("rotate",) if args.rotate else ()) + ("ldl", "solve")
     ev = {k: [] for k in phases}
 
@@ -196,6 +199,11 @@ def main():
 
         if sketch:
             bk.sketch_b(grads, HI, HO)
+            mark()
+        elif args.hessian == "sketch_a":
+            hi, ho = bk.sketch_a(X, G, args.iters)
+            HI.copy_(hi)
+            HO.copy_(ho)
             mark()
         else:
             bk.hessian_accum(X, HI)
@@ -242,6 +250,13 @@ def main():
         # and an n m^2 (H_O) accumulation
         syrk_ms = float(np.mean(ev["hess_sketch_b"]))
         syrk_flops = float(args.sequences) * (m * n * n + n * m * m)
+    elif args.hessian == "sketch_a":
+        # the whole phase in fp32-equivalent flops: the SYRKs (the initial X^T X,
+        # then two per iteration, T d^2 each) and the token weights' quadratic
+        # forms (2 T d^2 per factor and iteration, fp32 MFMA)
+        syrk_ms = float(np.mean(ev["hess_sketch_a"]))
+        syrk_flops = float(T) * (n * n * (1 + args.iters) + m * m * args.iters
+                                 + 2.0 * args.iters * (n * n + m * m))
     else:
         syrk_ms = float(np.mean(ev["hess_I"] + ev["hess_O"]))
         # algorithmic fp32 flops per call, averaged over the two calls: T d^2 per
@@ -258,11 +273,15 @@ def main():
         "achieved": PIECE_PRODUCTS * fp32_equiv,
         "peak": PEAK_BF16_MFMA_TFLOPS,
         "unit": "TFLOP/s",
-        "traffic": None if sketch else syrk_traffic_bytes(args.workload),
+        "traffic": None if args.hessian != "tokens" else syrk_traffic_bytes(args.workload),
         "flops_per_call": PIECE_PRODUCTS * syrk_flops,
         "fp32_equiv_tflops": fp32_equiv,
         "fp32_equiv_frac_of_fp32_peak": fp32_equiv / PEAK_FP32_MFMA_TFLOPS,
     }
+    if args.hessian == "sketch_a":
+        roof.update(kernel="sketch_a phase: token-weight tile GEMMs (fp32 MFMA) and weighted SYRKs "
+                           "(bf16 pieces), in fp32-equivalent flops",
+                    achieved=fp32_equiv, peak=PEAK_FP32_MFMA_TFLOPS, flops_per_call=syrk_flops)
     roof["frac"] = roof["achieved"] / roof["peak"]
 
     res = {
@@ -284,7 +303,8 @@ def main():
                                                   args.rounding),
                    "m": m, "n": n, "tokens": T, "bits": args.bits, "rounding": args.rounding,
                    "damp_rel": 0.01, "leaf": 64, "rotate": bool(args.rotate),
-                   "hessian": args.hessian + (" x %d sequences" % args.sequences if sketch else "")},
+                   "hessian": args.hessian + (" x %d sequences" % args.sequences if sketch else "")
+                   + (" x %d iterations" % args.iters if args.hessian == "sketch_a" else "")},
         "phases_ms": ph,
         "dominant_phase": dominant,
         "solve_ms": ph["solve"],
