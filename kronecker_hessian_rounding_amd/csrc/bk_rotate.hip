@@ -38,15 +38,18 @@ __device__ __forceinline__ float rht_sign(uint64_t seed, int64_t i) {
 // Workgroup (row, chunk): columns [chunk * cs, chunk * cs + len) of one row, a
 // whole number of 2^kbits-blocks. U: signs, butterflies, scale; U^T: butterflies,
 // scale, signs.
-__global__ __launch_bounds__(kThreads) void k_rht_rows(float* __restrict__ A, int64_t cols, int64_t lda,
-                                                       int64_t nchunk, int64_t cs, int kbits, uint64_t seed,
-                                                       float scale, int transpose) {
+// kRowThreads grows with the chunk (one thread per 16 floats, 256 to 1024), so
+// each butterfly stage between two barriers stays short.
+template <int kRowThreads>
+__global__ __launch_bounds__(kRowThreads) void k_rht_rows(float* __restrict__ A, int64_t cols, int64_t lda,
+                                                          int64_t nchunk, int64_t cs, int kbits, uint64_t seed,
+                                                          float scale, int transpose) {
     extern __shared__ float buf[];
     const int64_t row = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
     const int64_t c0 = chunk * cs;
     const int len = (int)min<int64_t>(cs, cols - c0);
     float* p = A + row * lda + c0;
-    for (int i = threadIdx.x; i < len; i += kThreads) {
+    for (int i = threadIdx.x; i < len; i += kRowThreads) {
         float v = p[i];
         if (!transpose) v *= rht_sign(seed, c0 + i);
         buf[i] = v;
@@ -54,7 +57,7 @@ __global__ __launch_bounds__(kThreads) void k_rht_rows(float* __restrict__ A, in
     __syncthreads();
     for (int s = 0; s < kbits; ++s) {
         const int h = 1 << s;
-        for (int q = threadIdx.x; q < len / 2; q += kThreads) {
+        for (int q = threadIdx.x; q < len / 2; q += kRowThreads) {
             const int lo = ((q >> s) << (s + 1)) | (q & (h - 1));
             const float a = buf[lo], b = buf[lo + h];
             buf[lo] = a + b;
@@ -62,7 +65,7 @@ __global__ __launch_bounds__(kThreads) void k_rht_rows(float* __restrict__ A, in
         }
         __syncthreads();
     }
-    for (int i = threadIdx.x; i < len; i += kThreads) {
+    for (int i = threadIdx.x; i < len; i += kRowThreads) {
         float v = buf[i] * scale;
         if (transpose) v *= rht_sign(seed, c0 + i);
         p[i] = v;
@@ -159,8 +162,17 @@ int launch_rht(float* A, int64_t rows, int64_t cols, int64_t lda, int axis, uint
         const int64_t cs = b * (kRowMaxFloats / b < cols / b ? kRowMaxFloats / b : cols / b);
         const int64_t nchunk = (cols + cs - 1) / cs;
         if (rows * nchunk > 0x7fffffff) return BAKRON_E_INVALID_ARG;
-        hipLaunchKernelGGL(k_rht_rows, dim3((unsigned)(rows * nchunk)), dim3(kThreads), sizeof(float) * cs,
-                           stream, A, cols, lda, nchunk, cs, kbits, seed, scale, transpose);
+        const dim3 grid((unsigned)(rows * nchunk));
+        const size_t lds = sizeof(float) * cs;
+        if (cs > 8192)
+            hipLaunchKernelGGL(k_rht_rows<1024>, grid, dim3(1024), lds, stream, A, cols, lda, nchunk, cs, kbits,
+                               seed, scale, transpose);
+        else if (cs > 4096)
+            hipLaunchKernelGGL(k_rht_rows<512>, grid, dim3(512), lds, stream, A, cols, lda, nchunk, cs, kbits,
+                               seed, scale, transpose);
+        else
+            hipLaunchKernelGGL(k_rht_rows<256>, grid, dim3(256), lds, stream, A, cols, lda, nchunk, cs, kbits,
+                               seed, scale, transpose);
     } else {
         // passes of at most 6 bits, as even as possible
         const int npass = kbits == 0 ? 1 : (kbits + kColPassBits - 1) / kColPassBits;
