@@ -235,9 +235,15 @@ def sketch_b(grads, HI: Optional[torch.Tensor] = None, HO: Optional[torch.Tensor
     H_I = E_s[G_s^T G_s] / m and H_O = E_s[G_s G_s^T] / n. Returns (H_I, H_O)."""
     S = len(grads)
     m, n = grads[0].shape
+    # sum_s G_s^T G_s is X^T X of the gradients stacked vertically: for one contiguous
+    # S x m x n tensor H_I is a single accumulation over S m tokens
+    stacked = isinstance(grads, torch.Tensor) and grads.dim() == 3 and grads.is_contiguous()
+    if stacked:
+        HI = hessian_accum(grads.reshape(S * m, n), HI, alpha=1.0 / (S * m), beta=0.0)
     for s in range(S):
         beta = 0.0 if s == 0 else 1.0
-        HI = hessian_accum(grads[s], HI, alpha=1.0 / (S * m), beta=beta)
+        if not stacked:
+            HI = hessian_accum(grads[s], HI, alpha=1.0 / (S * m), beta=beta)
         HO = hessian_accum(grads[s], HO, alpha=1.0 / (S * n), beta=beta, transposed=True)
     return HI, HO
 

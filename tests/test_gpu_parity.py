@@ -564,17 +564,23 @@ def test_hessian_accum_transposed_needs_the_piece_workspace(bk):
 def test_sketch_b_matches_oracle(bk, S, m, n):
     note("sketch B S=%d m=%d n=%d" % (S, m, n))
     g = workloads.make_grads(S, m, n, 50 + m)
-    HI, HO = bk.sketch_b(torch.from_numpy(g).to(dev()))
+    Gt = torch.from_numpy(g).to(dev())
+    HI, HO = bk.sketch_b(Gt)  # one stacked accumulation for H_I
     HI, HO = HI.cpu().numpy(), HO.cpu().numpy()
+    HI2, HO2 = bk.sketch_b([Gt[s] for s in range(S)])  # one call per sequence
+    HI2, HO2 = HI2.cpu().numpy(), HO2.cpu().numpy()
+    assert np.array_equal(HO, HO2)
     ri, ro = oracle.sketch_b(list(g))
     ag = np.abs(g.astype(np.float64))
     # S accumulations of K-long sums, each within the fp32 bound, plus the S - 1
     # fp32 additions into H: 8 u sqrt(S K) of the mean |G|-product
     bi = 8 * U32 * np.sqrt(S * m) * sum(a.T @ a for a in ag) / (S * m) + 1e-30
     bo = 8 * U32 * np.sqrt(S * n) * sum(a @ a.T for a in ag) / (S * n) + 1e-30
-    assert np.all(np.abs(HI - ri) <= bi), np.max(np.abs(HI - ri) / bi)
+    for hi in (HI, HI2):
+        assert np.all(np.abs(hi - ri) <= bi), np.max(np.abs(hi - ri) / bi)
+        assert np.array_equal(hi, hi.T)
     assert np.all(np.abs(HO - ro) <= bo), np.max(np.abs(HO - ro) / bo)
-    assert np.array_equal(HI, HI.T) and np.array_equal(HO, HO.T)
+    assert np.array_equal(HO, HO.T)
 
 
 # ----------------------------------------------------------------------------
