@@ -15,7 +15,11 @@
  *       with a_i, b_j columns of the strictly upper L_O, L_I and D = W* - W;
  *       the factorisation H = (L + I) D (L + I)^T; the error bound.
  *   YAQA article, section 3, and the K-FAC tutorial (www.mlqm.cn), section 5:
- *       the factor estimates H_I = E[x^T x], H_O = E[g^T g] and damping.
+ *       the factor estimates H_I = E[x^T x], H_O = E[g^T g] and damping; the
+ *       YAQA article's Sketch A and Sketch B estimators (section 3).
+ *   "KronQ: Kronecker-factored Hessian LLM quantization" (ai-feeds.com),
+ *       method: bidirectional incoherence processing, W' = R_O W R_I^T, and
+ *       the layer sensitivity tr(A) tr(G).
  *
  * Conventions for every entry point:
  *   - All matrix and vector pointers are DEVICE pointers (memory of the
