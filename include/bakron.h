@@ -151,6 +151,19 @@ int bakron_hessian_accum_t(const float* X, int64_t T, int64_t d, int64_t ldx, fl
  * Errors: INVALID_ARG for NULL pointers, d <= 0, T < 0, bad ld; WORKSPACE for a
  * missing or short workspace.
  */
+/*
+ * The transposed form over a batch: H <- beta H + alpha sum_s X_s X_s^T for S
+ * matrices X_s (d x tin, ldx >= tin) at X + s * bs (bs >= d * ldx when S > 1),
+ * accumulated as one call with T = S tin tokens. With X_s the gradients G_s of
+ * S sequences (an S x m x n tensor: d = m, tin = n, bs = m n) this is the whole
+ * output-side term of Sketch B. ws: bakron_hessian_accum_workspace_bytes(S tin, d).
+ * Errors: INVALID_ARG for NULL pointers, d <= 0, S or tin < 0, bad ld or
+ * overlapping batch stride; WORKSPACE for a missing or short workspace.
+ */
+int bakron_hessian_accum_tb(const float* X, int64_t S, int64_t d, int64_t tin, int64_t ldx, int64_t bs,
+                            float alpha, float beta, float* H, int64_t ldh, void* ws, size_t ws_bytes,
+                            void* stream);
+
 size_t bakron_token_weights_workspace_bytes(int64_t T, int64_t d);
 int bakron_token_weights(const float* Y, int64_t T, int64_t d, int64_t ldy, const float* H, int64_t ldh,
                          float* w, void* ws, size_t ws_bytes, void* stream);

@@ -54,6 +54,8 @@ def _load() -> ctypes.CDLL:
     lib.bakron_hessian_accum.argtypes = [vp, i64, i64, i64, f32, f32, vp, i64, vp, sz, vp]
     lib.bakron_hessian_accum_t.restype = ctypes.c_int
     lib.bakron_hessian_accum_t.argtypes = [vp, i64, i64, i64, f32, f32, vp, i64, vp, sz, vp]
+    lib.bakron_hessian_accum_tb.restype = ctypes.c_int
+    lib.bakron_hessian_accum_tb.argtypes = [vp, i64, i64, i64, i64, i64, f32, f32, vp, i64, vp, sz, vp]
     lib.bakron_hessian_accum_w.restype = ctypes.c_int
     lib.bakron_hessian_accum_w.argtypes = [vp, i64, i64, i64, vp, f32, f32, vp, i64, vp, sz, vp]
     lib.bakron_token_weights_workspace_bytes.restype = sz
@@ -81,7 +83,8 @@ def _load() -> ctypes.CDLL:
 LIB = _load()
 
 EXPORTS = ("bakron_abi_version", "bakron_status_str", "bakron_hessian_accum_workspace_bytes",
-           "bakron_hessian_accum", "bakron_hessian_accum_t", "bakron_hessian_accum_w",
+           "bakron_hessian_accum", "bakron_hessian_accum_t", "bakron_hessian_accum_tb",
+           "bakron_hessian_accum_w",
            "bakron_token_weights_workspace_bytes", "bakron_token_weights", "bakron_ldl_workspace_bytes", "bakron_ldl", "bakron_ldl_async",
            "bakron_solve_workspace_bytes", "bakron_solve", "bakron_rht",
            "bakron_layer_report")
@@ -237,13 +240,24 @@ def sketch_b(grads, HI: Optional[torch.Tensor] = None, HO: Optional[torch.Tensor
     m, n = grads[0].shape
     # sum_s G_s^T G_s is X^T X of the gradients stacked vertically: for one contiguous
     # S x m x n tensor H_I is a single accumulation over S m tokens
+    # and sum_s G_s G_s^T is one transposed accumulation over the batch (S n tokens)
     stacked = isinstance(grads, torch.Tensor) and grads.dim() == 3 and grads.is_contiguous()
     if stacked:
         HI = hessian_accum(grads.reshape(S * m, n), HI, alpha=1.0 / (S * m), beta=0.0)
+        if grads.dtype != torch.float32 or not grads.is_cuda:
+            raise ValueError("grads must be a CUDA float32 tensor")
+        if HO is None:
+            HO = torch.empty((m, m), dtype=torch.float32, device=grads.device)
+        ldho = _mat(HO, "H_O")
+        nb = LIB.bakron_hessian_accum_workspace_bytes(S * n, m)
+        ws = _workspace(nb, grads.device)
+        _check("bakron_hessian_accum_tb",
+               LIB.bakron_hessian_accum_tb(_ptr(grads), S, m, n, n, m * n, 1.0 / (S * n), 0.0, _ptr(HO), ldho,
+                                           _ptr(ws), nb, _stream()))
+        return HI, HO
     for s in range(S):
         beta = 0.0 if s == 0 else 1.0
-        if not stacked:
-            HI = hessian_accum(grads[s], HI, alpha=1.0 / (S * m), beta=beta)
+        HI = hessian_accum(grads[s], HI, alpha=1.0 / (S * m), beta=beta)
         HO = hessian_accum(grads[s], HO, alpha=1.0 / (S * n), beta=beta, transposed=True)
     return HI, HO
 

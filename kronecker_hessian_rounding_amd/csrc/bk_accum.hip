@@ -530,18 +530,21 @@ __global__ __launch_bounds__(kThreads) void k_split3(const float* __restrict__ X
 // The same planes from X stored d x T (one row per output column, the tokens
 // along the row), for H = X X^T: thread (c, q) splits tokens 32 q .. 32 q + 31 of
 // row c, one whole 128-byte line, into four groups of 8; a wave writes 1 KB of
-// consecutive 16-byte units of each plane per group.
+// consecutive 16-byte units of each plane per group. A batch of S such matrices
+// of tin tokens each, bs floats apart, reads as one with T = S tin: token k of
+// row c is X[(k / tin) bs + c ldx + k % tin].
 template <bool kVec>
 __global__ __launch_bounds__(kThreads) void k_split3_t(const float* __restrict__ X, int64_t T,
-                                                       int64_t d, int64_t ldx, int64_t ng,
-                                                       int64_t dp, uint4* __restrict__ Xs) {
+                                                       int64_t d, int64_t ldx, int64_t tin, int64_t bs,
+                                                       int64_t ng, int64_t dp, uint4* __restrict__ Xs) {
     const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (c >= dp) return;
     for (int64_t q = blockIdx.y; q < ng / 4; q += gridDim.y) {
         const int64_t k0 = 32 * q;
-        const float* row = X + c * ldx + k0;
+        const int64_t j0 = k0 % tin;
+        const float* row = X + (k0 / tin) * bs + c * ldx + j0;
         float v[32];
-        if (kVec && c < d && k0 + 32 <= T) {
+        if (kVec && c < d && k0 + 32 <= T && j0 + 32 <= tin) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const f32x4 t = *reinterpret_cast<const f32x4*>(row + 4 * e);
@@ -550,7 +553,10 @@ __global__ __launch_bounds__(kThreads) void k_split3_t(const float* __restrict__
             }
         } else {
 #pragma unroll
-            for (int e = 0; e < 32; ++e) v[e] = (c < d && k0 + e < T) ? row[e] : 0.0f;
+            for (int e = 0; e < 32; ++e) {
+                const int64_t k = k0 + e;
+                v[e] = (c < d && k < T) ? X[(k / tin) * bs + c * ldx + k % tin] : 0.0f;
+            }
         }
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
@@ -770,7 +776,7 @@ size_t hessian_workspace_bytes(int64_t T, int64_t d) {
 
 int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, float alpha,
                          float beta, float* H, int64_t ldh, void* ws, size_t ws_bytes,
-                         hipStream_t stream, bool trans, const float* wt) {
+                         hipStream_t stream, bool trans, const float* wt, int64_t tin, int64_t bs) {
     const int64_t nb = (d + kT128 - 1) / kT128;
     const int64_t tiles = nb * (nb + 1) / 2;
     if (tiles > 0x7fffffff) return BAKRON_E_INVALID_ARG;
@@ -781,11 +787,15 @@ int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, floa
         if (sh.ng > 0 && trans) {
             const unsigned gy = (unsigned)std::min<int64_t>(sh.ng / 4, 65535);
             const dim3 grid((unsigned)((sh.dp + kThreads - 1) / kThreads), gy);
-            const bool vec = (ldx & 3) == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0;
+            if (tin <= 0) tin = T;  // one matrix
+            const bool vec = (ldx & 3) == 0 && (tin & 3) == 0 && (bs & 3) == 0 &&
+                             (reinterpret_cast<uintptr_t>(X) & 15) == 0;
             if (vec)
-                hipLaunchKernelGGL(k_split3_t<true>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, sh.ng, sh.dp, Xs);
+                hipLaunchKernelGGL(k_split3_t<true>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, tin, bs, sh.ng,
+                                   sh.dp, Xs);
             else
-                hipLaunchKernelGGL(k_split3_t<false>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, sh.ng, sh.dp, Xs);
+                hipLaunchKernelGGL(k_split3_t<false>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, tin, bs, sh.ng,
+                                   sh.dp, Xs);
         } else if (sh.ng > 0) {
             const unsigned gy = (unsigned)std::min<int64_t>(sh.ng, 65535);
             const dim3 grid((unsigned)((sh.dp + kSplitCols - 1) / kSplitCols), gy);

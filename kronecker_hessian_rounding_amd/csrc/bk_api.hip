@@ -48,6 +48,17 @@ int bakron_hessian_accum_t(const float* X, int64_t T, int64_t d, int64_t ldx, fl
                                     (hipStream_t)stream, true);
 }
 
+int bakron_hessian_accum_tb(const float* X, int64_t S, int64_t d, int64_t tin, int64_t ldx, int64_t bs,
+                            float alpha, float beta, float* H, int64_t ldh, void* ws, size_t ws_bytes,
+                            void* stream) {
+    if (!H || d <= 0 || S < 0 || tin < 0 || bad_ld(ldh, d)) return BAKRON_E_INVALID_ARG;
+    const int64_t T = S * tin;
+    if (T > 0 && (!X || bad_ld(ldx, tin) || (S > 1 && bs < d * ldx))) return BAKRON_E_INVALID_ARG;
+    if (!ws || ws_bytes < bk::hessian_workspace_bytes(T, d)) return BAKRON_E_WORKSPACE;
+    return bk::launch_hessian_accum(X, T, d, ldx, alpha, beta, H, ldh, ws, ws_bytes, (hipStream_t)stream,
+                                    true, nullptr, tin, bs);
+}
+
 int bakron_hessian_accum_w(const float* X, int64_t T, int64_t d, int64_t ldx, const float* w, float alpha,
                            float beta, float* H, int64_t ldh, void* ws, size_t ws_bytes, void* stream) {
     if (!H || d <= 0 || T < 0 || bad_ld(ldh, d)) return BAKRON_E_INVALID_ARG;

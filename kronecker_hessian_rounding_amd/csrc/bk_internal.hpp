@@ -18,7 +18,8 @@ size_t hessian_workspace_bytes(int64_t T, int64_t d);
 // x_k^T x_k); both need the workspace of the piece path
 int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, float alpha,
                          float beta, float* H, int64_t ldh, void* ws, size_t ws_bytes,
-                         hipStream_t stream, bool trans = false, const float* wt = nullptr);
+                         hipStream_t stream, bool trans = false, const float* wt = nullptr,
+                         int64_t tin = 0, int64_t bs = 0);
 
 // --- Sketch A token weights (bk_sketch.hip) ---
 size_t token_weights_workspace_bytes(int64_t T, int64_t d);

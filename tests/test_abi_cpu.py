@@ -188,3 +188,20 @@ def test_sketch_a_entry_points_reject_invalid_arguments(lib):
     assert fa(fake, 10, 4, 4, None, 1.0, 0.0, fake, 4, fake, 1 << 30, None) == INVALID  # no weights
     assert fa(fake, 10, 4, 4, fake, 1.0, 0.0, fake, 4, None, 0, None) == WORKSPACE
     assert lib.bakron_token_weights_workspace_bytes(10, 0) == 0
+
+
+def test_hessian_accum_tb_rejects_invalid_arguments(lib):
+    f = lib.bakron_hessian_accum_tb
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                  ctypes.c_int64, ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    INVALID, WORKSPACE = 1, 3
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: the arguments fail first
+    assert f(fake, 2, 8, 16, 15, 128, 1.0, 0.0, fake, 8, fake, 1 << 30, None) == INVALID  # ldx < tin
+    assert f(fake, 2, 8, 16, 16, 127, 1.0, 0.0, fake, 8, fake, 1 << 30, None) == INVALID  # batches overlap
+    assert f(fake, 2, 0, 16, 16, 128, 1.0, 0.0, fake, 8, fake, 1 << 30, None) == INVALID  # d <= 0
+    assert f(fake, -1, 8, 16, 16, 128, 1.0, 0.0, fake, 8, fake, 1 << 30, None) == INVALID  # S < 0
+    assert f(None, 2, 8, 16, 16, 128, 1.0, 0.0, fake, 8, fake, 1 << 30, None) == INVALID  # X missing
+    assert f(fake, 2, 8, 16, 16, 128, 1.0, 0.0, fake, 7, fake, 1 << 30, None) == INVALID  # ldh < d
+    assert f(fake, 2, 8, 16, 16, 128, 1.0, 0.0, fake, 8, None, 0, None) == WORKSPACE      # no workspace
