@@ -57,7 +57,7 @@ __all__ = [
     "hessian", "hessian_entries", "damp", "udu", "udu_lapack", "row_scales", "sweep",
     "replay", "replay_rows", "proxy_loss", "loss_identity", "bound_terms", "splitmix64",
     "uniform_matrix", "pipeline", "rht_signs", "rht_block", "sylvester", "rht_matrix",
-    "rht_apply", "rotate_layer", "sketch_b", "token_weights", "sketch_a",
+    "rht_apply", "rotate_layer", "sketch_b", "token_weights", "weighted_hessian", "sketch_a",
 ]
 
 _lib = None
@@ -279,11 +279,14 @@ def replay(W, LO, LI, scales, bits, codes, rounding="nearest", seed=0, u=None, b
     return _classify(y, Lq, uu, c_hat, band, t, q, s, DO, DI)
 
 
-def replay_rows(W, LO, LI, scales, bits, codes, rows, rounding="nearest", seed=0, band=1e-4):
+def replay_rows(W, LO, LI, scales, bits, codes, rows, rounding="nearest", seed=0, band=1e-4,
+                batch=256):
     """replay() restricted to selected full rows (cheap at very large sizes).
 
     For row i: t^_i = W*_i + (a_i^T D^[:i+1]) A_I - D^_i with a_i column i of A_O
     restricted to rows 0..i, evaluated with the candidate's committed error D^.
+    Rows are taken `batch` at a time: the a_i of a batch form one matrix, so the two
+    products are matrix products (the same sums as the definition).
     """
     w = np.asarray(W, dtype=np.float32)
     m, n = w.shape
@@ -298,33 +301,33 @@ def replay_rows(W, LO, LI, scales, bits, codes, rows, rounding="nearest", seed=0
         dh[r0:r1] = w[r0:r1].astype(np.float64) - s_all[r0:r1, None] * (
             np.asarray(codes[r0:r1]).astype(np.float64) - Lq / 2.0)
     li = None if LI is None else np.asarray(LI)
-    out_y, out_t, out_q = [], [], []
-    for i in rows:
-        a = np.zeros(i + 1)
-        a[i] = 1.0
-        if LO is not None:
-            a[:i] = np.asarray(LO[:i, i], dtype=np.float64)
-        v = a @ dh[: i + 1]                          # (A_O^T D^)_{i,:}
+    E = np.empty((len(rows), n), dtype=np.float64)
+    for b0 in range(0, len(rows), batch):
+        rb = rows[b0:b0 + batch]
+        # A[r, k] = L_O[k, i_r] for k < i_r, 1 at k = i_r, 0 beyond
+        A = np.zeros((len(rb), top), dtype=np.float64)
+        for r, i in enumerate(rb):
+            if LO is not None and i > 0:
+                A[r, :i] = np.asarray(LO[:i, i], dtype=np.float64)
+            A[r, i] = 1.0
+        V = A @ dh                                    # rows of A_O^T D^
         if li is not None:
-            # v A_I = v + v L_I, evaluated without forming an n x n fp64 copy
-            vl = np.zeros(n)
+            # V A_I = V + V L_I, with L_I taken 2048 columns at a time in fp64
+            VL = np.empty_like(V)
             for j0 in range(0, n, 2048):
                 blk = np.triu(np.asarray(li[:, j0:j0 + 2048], dtype=np.float64), 1 - j0)
-                vl[j0:j0 + 2048] = v @ blk
-            e = v + vl
-        else:
-            e = v
-        q = w[i].astype(np.float64) - dh[i]
-        t = w[i].astype(np.float64) + (e - dh[i])
-        out_t.append(t)
-        out_q.append(q)
-        out_y.append(t / s_all[i] + Lq / 2.0)
-    y = np.array(out_y)
+                VL[:, j0:j0 + 2048] = V @ blk
+            V += VL
+        E[b0:b0 + len(rb)] = V
+    dr = dh[rows]
+    q = w[rows].astype(np.float64) - dr
+    t = w[rows].astype(np.float64) + (E - dr)
+    y = t / s_all[rows][:, None] + Lq / 2.0
     uu = None
     if rounding == "stochastic":
         uu = np.stack([_uniform_row(seed, i, n) for i in rows])
     return _classify(y, Lq, uu, np.asarray(codes)[rows].astype(np.int64), band,
-                     np.array(out_t), np.array(out_q), s_all[rows][:, None], None, None)
+                     t, q, s_all[rows][:, None], None, None)
 
 
 def _uniform_row(seed, i, n):
@@ -391,7 +394,12 @@ def bound_terms(scales, DO, DI):
 # --------------------------------------------------------------------------
 def pipeline(W, X, G, bits, rounding="nearest", seed=0, damp_rel=0.01, method="accum",
              one_sided=False):
-    """Factors from X / G, damping, LDL, fp32 scales and the free-run sweep."""
+    """Factors from X / G, damping, LDL, fp32 scales and the free-run sweep.
+
+    one_sided=True takes H_O = I. Damping applies to both factors, so that
+    factor is (1 + damp_rel) I: L_O = 0 and D_O = 1 + damp_rel (the codes are
+    those of H_O = I; the proxy loss carries the factor 1 + damp_rel).
+    """
     HI = damp(hessian(X), damp_rel)
     LI, DI = udu(HI) if HI.shape[0] <= 2048 else udu_lapack(HI)
     if one_sided:
@@ -512,6 +520,14 @@ def token_weights(Y, H=None) -> np.ndarray:
     return np.einsum("tk,kc,tc->t", Y, H, Y, optimize=True) / np.sum(H * H)
 
 
+def weighted_hessian(X, w) -> np.ndarray:
+    """sum_t w_t x_t^T x_t / T in fp64: one Sketch A update of a factor, the token
+    weights w (T,) taken as given."""
+    X = np.asarray(X, np.float64)
+    w = np.asarray(w, np.float64)
+    return (X * w[:, None]).T @ X / X.shape[0]
+
+
 def sketch_a(X, G, iters: int = 3):
     """(H_I, H_O) after `iters` Sketch A iterations (fp64)."""
     X = np.asarray(X, np.float64)
@@ -522,5 +538,5 @@ def sketch_a(X, G, iters: int = 3):
     for _ in range(iters):
         w = token_weights(G, HO)
         v = token_weights(X, HI)
-        HI, HO = (X * w[:, None]).T @ X / T, (G * v[:, None]).T @ G / T
+        HI, HO = weighted_hessian(X, w), weighted_hessian(G, v)
     return HI, HO

@@ -761,3 +761,113 @@ def test_token_weights_identity_and_scale():
     # and against the quadratic form written out
     want = np.array([sum(y[a] * H[a, b] * y[b] for a in range(5) for b in range(5)) for y in Y]) / np.sum(H * H)
     assert np.allclose(oracle.token_weights(Y, H), want, rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# bound terms (YAQA article, section 4, error bound): closed forms
+# ----------------------------------------------------------------------------
+def test_bound_terms_closed_form():
+    # written out by hand: D_O = (1, 2, 3), D_I = (4, 5), s = (1/2, 1, 2)
+    #   sharp = (1 * 1/16 + 2 * 1/4 + 3 * 1) * (4 + 5) = 3.5625 * 9 = 32.0625
+    #   page  = (4 + 5) * (1 + 2 + 3) * 2^2 / 4     = 54
+    sharp, page = oracle.bound_terms(np.array([0.5, 1.0, 2.0], np.float32), [1.0, 2.0, 3.0], [4.0, 5.0])
+    assert sharp == 32.0625 and page == 54.0
+    # equal scales: both forms are tr(D_O) tr(D_I) s^2 / 4
+    sharp, page = oracle.bound_terms(np.full(3, 0.5, np.float32), [1.0, 2.0, 3.0], [4.0, 5.0])
+    assert sharp == page == 6.0 * 9.0 * 0.25 / 4.0
+
+
+def test_bound_is_attained_with_every_residual_at_half_a_step():
+    # Diagonal factors (L = 0: round to nearest, no feedback) and every W*_ij a whole
+    # multiple of s_i, so that y = W*/s + 3/2 (2 bits) sits exactly halfway between
+    # two codes: |eta_ij| = s_i / 2 for every entry and nothing clamps. The loss
+    # sum_ij D_O,i D_I,j eta_ij^2 then equals the sharp bound exactly.
+    rng = np.random.default_rng(31)
+    m, n = 5, 7
+    s = np.float32(2.0) ** rng.integers(-8, -3, size=m).astype(np.float32)
+    w = (s[:, None] * rng.integers(-1, 2, size=(m, n))).astype(np.float32)
+    DO = rng.lognormal(0.0, 1.0, m)
+    DI = rng.lognormal(0.0, 1.0, n)
+    r = oracle.sweep(w, np.zeros((m, m)), np.zeros((n, n)), s, 2)
+    assert r["clamped"] == 0
+    assert np.all(np.abs(r["eta"]) == s[:, None].astype(np.float64) / 2)
+    loss = oracle.proxy_loss(r["delta"], np.diag(DO), np.diag(DI))
+    sharp, page = oracle.bound_terms(s, DO, DI)
+    assert abs(loss - sharp) <= 1e-13 * sharp
+    assert page >= sharp
+
+
+@pytest.mark.parametrize("mutation", ["no_quarter", "page_for_sharp", "sum_not_max", "swapped"])
+def test_bound_pins_catch_mutated_terms(mutation):
+    # plausible slips in writing the bound; the closed-form and attained-bound pins
+    # above must reject every one of them
+    def mutated(scales, DO, DI):
+        s = np.asarray(scales, np.float64)
+        do, di = np.asarray(DO, np.float64), np.asarray(DI, np.float64)
+        if mutation == "no_quarter":
+            return float(np.sum(do * s * s) * np.sum(di)), float(np.sum(di) * np.sum(do) * np.max(s) ** 2)
+        if mutation == "page_for_sharp":
+            v = float(np.sum(di) * np.sum(do) * np.max(s) ** 2 / 4.0)
+            return v, v
+        if mutation == "sum_not_max":
+            return (float(np.sum(do * s * s / 4.0) * np.sum(di)),
+                    float(np.sum(di) * np.sum(do) * np.sum(s * s) / 4.0))
+        return float(np.sum(di * s[: len(di)] ** 2 / 4.0) * np.sum(do)), float(
+            np.sum(di) * np.sum(do) * np.max(s) ** 2 / 4.0)
+
+    sharp, page = mutated(np.array([0.5, 1.0, 2.0]), [1.0, 2.0, 3.0], [4.0, 5.0])
+    assert (sharp, page) != (32.0625, 54.0)
+
+
+# ----------------------------------------------------------------------------
+# the whole CPU chain: pipeline() against an independent chain written here
+# (numpy X^T X / T, damping, vectorised LDLQ on H_O (x) H_I; GPTQ when H_O = I)
+# ----------------------------------------------------------------------------
+def test_pipeline_matches_an_independent_chain():
+    w, x, g = workloads.make_inputs("tiny", m=14, n=12, T=96)
+    r = oracle.pipeline(w, x, g, 2)
+    x64, g64 = x.astype(np.float64), g.astype(np.float64)
+    HI = x64.T @ x64 / 96
+    HI += 0.01 * np.trace(HI) / 12 * np.eye(12)
+    HO = g64.T @ g64 / 96
+    HO += 0.01 * np.trace(HO) / 14 * np.eye(14)
+    assert np.allclose(r["HI"], HI, rtol=1e-13) and np.allclose(r["HO"], HO, rtol=1e-13)
+    s = (np.float32(2.0) * np.max(np.abs(w), axis=1)) / np.float32(3.0)
+    assert np.array_equal(r["scales"], s)
+    codes_equal_or_tie(r["codes"], ldlq_vectorised(w, HO, HI, s, 2), r["margin"], tol=1e-8)
+    A_O, A_I = np.triu(r["LO"], 1) + np.eye(14), np.triu(r["LI"], 1) + np.eye(12)
+    assert np.allclose(A_O @ np.diag(r["DO"]) @ A_O.T, HO, rtol=1e-12, atol=1e-14 * np.abs(HO).max())
+    assert np.allclose(A_I @ np.diag(r["DI"]) @ A_I.T, HI, rtol=1e-12, atol=1e-14 * np.abs(HI).max())
+
+
+def test_pipeline_one_sided_damps_the_identity():
+    # H_O = I, damped like every factor: (1 + 0.01) I, so L_O = 0 and D_O = 1.01;
+    # the codes are GPTQ's on H_I and the loss is 1.01 tr(D H_I D^T)
+    w, x, _ = workloads.make_inputs("tiny", m=20, n=24, T=128)
+    r = oracle.pipeline(w, x, None, 3, one_sided=True)
+    assert r["LO"] is None and np.all(r["DO"] == 1.01)
+    x64 = x.astype(np.float64)
+    HI = x64.T @ x64 / 128
+    HI += 0.01 * np.trace(HI) / 24 * np.eye(24)
+    codes_equal_or_tie(r["codes"], gptq(w, HI, r["scales"], 3), r["margin"], tol=1e-8)
+    loss = oracle.loss_identity(r["eta"], r["DO"], r["DI"])
+    want = 1.01 * np.sum((r["delta"] @ HI) * r["delta"])
+    assert abs(loss - want) <= 1e-10 * want
+
+
+# ----------------------------------------------------------------------------
+# weighted accumulation (one Sketch A update with the weights given)
+# ----------------------------------------------------------------------------
+def test_weighted_hessian_brute_force():
+    rng = np.random.default_rng(24)
+    T, d = 9, 4
+    X = rng.standard_normal((T, d))
+    w = rng.lognormal(0.0, 1.0, T)
+    w[3] = 0.0
+    H = oracle.weighted_hessian(X, w)
+    for a in range(d):
+        for b in range(d):
+            want = sum(w[t] * X[t][a] * X[t][b] for t in range(T)) / T
+            assert abs(H[a, b] - want) <= 1e-13 * max(1.0, abs(want))
+    # unit weights give X^T X / T
+    assert np.allclose(oracle.weighted_hessian(X, np.ones(T)), X.T @ X / T, rtol=1e-14)
