@@ -30,30 +30,49 @@ PIECE_PRODUCTS = 6  # bf16 piece products per fp32 product in the Hessian
 PEAK_FP64_MFMA_TFLOPS = 78.6
 CAL_BYTES = 256 << 20
 
-# HBM traffic of one hessian_accum call at the attn workload, from two
+# HBM traffic per launch of the kernels the roofline objects price, from two
 # rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per
-# dispatch, summed over the call's k_split3, k_syrk3_full, k_syrk3_split and
-# k_syrk_reduce). The counters are scaled by what they read for the
-# calibration copy above: FETCH_SIZE 131089.0 KiB and WRITE_SIZE 262144.0 KiB
-# for 262144 KiB moved each way. Valid only for the kernel source it was
-# measured on (hash of bk_accum.hip, which holds the SYRK kernels); otherwise
-# reported null.
-SYRK_COUNTERS = {
-    ("attn", "7e36cee6be0cd9f7"): {"fetch_kib": 2270509.1, "write_kib": 887728.2},
-}
+# dispatch). The counters are scaled by what they read for the calibration copy
+# above (CAL_* below: KiB read by FETCH_SIZE and WRITE_SIZE for 262144 KiB moved
+# each way). A reading is valid only for the kernel source it was taken on: the
+# key is a hash of the listed source files with comments and blank space
+# removed, so edits to comments keep it and any code change drops it (null).
 CAL_FETCH_KIB, CAL_WRITE_KIB = 131089.0, 262144.0
+COUNTERS = {
+    # one hessian_accum call at attn: k_split3 + k_syrk3_full (+ split-K pair)
+    ("hessian", "attn", "5bc2996ba9af1e89"): {"fetch_kib": 2270509.1, "write_kib": 887728.2},
+    # one solve at attn, 2-bit nearest: k_solve_run
+    ("solve", "attn", "ba6389e41bb2d18e"): {"fetch_kib": 4472228.2, "write_kib": 643941.2},
+}
+COUNTER_SOURCES = {
+    "hessian": ("bk_accum.hip", "bk_common.hpp"),
+    "solve": ("bk_solve.hip", "bk_common.hpp"),
+}
 
 
-def syrk_traffic_bytes(workload):
-    """Calibrated HBM bytes per hessian_accum call, or None if not measured for this source."""
+def source_key(kind):
+    """Hash of the kernel sources behind `kind`, comments and blank space removed."""
     import hashlib
+    import re
+
     csrc = os.path.join(ROOT, "kronecker_hessian_rounding_amd", "csrc")
-    key = (workload, hashlib.sha256(open(os.path.join(csrc, "bk_accum.hip"), "rb").read()).hexdigest()[:16])
-    c = SYRK_COUNTERS.get(key)
+    h = hashlib.sha256()
+    for f in COUNTER_SOURCES[kind]:
+        text = open(os.path.join(csrc, f)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()[:16]
+
+
+def traffic_bytes(kind, workload):
+    """Calibrated HBM bytes per launch (call), or None if not measured for this source."""
+    c = COUNTERS.get((kind, workload, source_key(kind)))
     if c is None:
         return None
     cal_kib = CAL_BYTES / 1024.0
     return 1024.0 * (c["fetch_kib"] * cal_kib / CAL_FETCH_KIB + c["write_kib"] * cal_kib / CAL_WRITE_KIB)
+
 
 WORKLOAD_LABEL = {
     "tiny": "tiny 64x64, T=1024",
@@ -74,6 +93,9 @@ def parse():
     ap.add_argument("--rounding", default="nearest", choices=["nearest", "stochastic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the CPU sweep sample")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="time the whole oracle chain on the whole layer instead of a bounded sample "
+                         "(minutes at the attention shape)")
     ap.add_argument("--hessian", default="tokens", choices=["tokens", "sketch_a", "sketch_b"],
                     help="factor estimate: X^T X / T and G^T G / T over tokens, Sketch A (alternating, "
                          "per-token weights) on the same X and G, or Sketch B from per-sequence weight "
@@ -86,14 +108,18 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(w, LO, LI, x, bits, rounding, seed, rows):
-    """The oracle as it stands, on a bounded sample of the same layer, extrapolated.
+def cpu_baseline(w, LO, LI, x, bits, rounding, seed, rows, g=None, full=False):
+    """The oracle as it stands, timed on the host cores.
 
-    Phases: fp64 X^T X on 8192 tokens (scaled by T/8192, twice: H_I and H_O of
-    the same size class), the plain O(d^3) LDL at d=2048 (scaled by (d/2048)^3
-    per factor) and the row-major accumulator sweep on the first `rows` rows
-    with the device's factors (scaled by the sweep's cost model
-    (m^2 n + m n^2) / (r^2 n + r n^2)).
+    Default: a bounded sample of the same layer, extrapolated. Phases: fp64 X^T X
+    on 8192 tokens (scaled by T/8192, for H_I (T n^2) and H_O (T m^2)), the plain
+    O(d^3) LDL at d=2048 (scaled by (d/2048)^3 per factor) and the row-major
+    accumulator sweep on the first `rows` rows with the device's factors (scaled
+    by the sweep's cost model (m^2 n + m n^2) / (r^2 n + r n^2)).
+
+    full=True: the whole oracle chain on the whole layer, every phase measured
+    (fp64 X^T X / T and G^T G / T, damping, the LDL of both factors as the oracle's
+    pipeline takes it, the fp32 scales and the whole accumulator sweep).
     """
     import numpy as np
 
@@ -102,6 +128,33 @@ def cpu_baseline(w, LO, LI, x, bits, rounding, seed, rows):
     m, n = w.shape
     T = x.shape[0]
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    if full:
+        t = {}
+        t0 = time.perf_counter()
+        HI = oracle.damp(oracle.hessian(x))
+        HO = oracle.damp(oracle.hessian(g))
+        t["hessians"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        li, di = oracle.udu(HI) if n <= 2048 else oracle.udu_lapack(HI)
+        lo, do = oracle.udu(HO) if m <= 2048 else oracle.udu_lapack(HO)
+        t["ldl"] = time.perf_counter() - t0
+        del HI, HO
+        t0 = time.perf_counter()
+        s = oracle.row_scales(w, bits)
+        oracle.sweep(w, lo, li, s, bits, rounding, seed)
+        t["sweep"] = time.perf_counter() - t0
+        total = sum(t.values())
+        return {
+            "value": m * n / total,
+            "unit": "weights/s",
+            "cores": cores,
+            "kind": "oracle",
+            "sample": ("fp64 oracle, the whole %dx%d layer measured: Hessians %.1fs, LDL of both %.1fs, "
+                       "scales and accumulator sweep %.1fs; %.1fs in all" % (m, n, t["hessians"], t["ldl"],
+                                                                              t["sweep"], total)),
+            "solve_only_value": m * n / t["sweep"],
+            "phases_s": t,
+        }
     ts = min(T, 8192)
     t0 = time.perf_counter()
     oracle.hessian(x[:ts])
@@ -157,7 +210,8 @@ def main():
     W = torch.from_numpy(w).to(dev)
     X = torch.from_numpy(x).to(dev)
     G = torch.from_numpy(g).to(dev)
-    del g
+    if not args.cpu_full:
+        del g
     HI = torch.empty((n, n), dtype=torch.float32, device=dev)
     HO = torch.empty((m, m), dtype=torch.float32, device=dev)
     DI = torch.empty(n, dtype=torch.float32, device=dev)
@@ -273,7 +327,7 @@ def main():
         "achieved": PIECE_PRODUCTS * fp32_equiv,
         "peak": PEAK_BF16_MFMA_TFLOPS,
         "unit": "TFLOP/s",
-        "traffic": None if args.hessian != "tokens" else syrk_traffic_bytes(args.workload),
+        "traffic": None if args.hessian != "tokens" else traffic_bytes("hessian", args.workload),
         "flops_per_call": PIECE_PRODUCTS * syrk_flops,
         "fp32_equiv_tflops": fp32_equiv,
         "fp32_equiv_frac_of_fp32_peak": fp32_equiv / PEAK_FP32_MFMA_TFLOPS,
@@ -283,6 +337,34 @@ def main():
                            "(bf16 pieces), in fp32-equivalent flops",
                     achieved=fp32_equiv, peak=PEAK_FP32_MFMA_TFLOPS, flops_per_call=syrk_flops)
     roof["frac"] = roof["achieved"] / roof["peak"]
+
+    # The solve (one persistent launch, k_solve_run, plus three small kernels), priced
+    # three ways: its far-field GEMMs against the fp32 MFMA peak (the minimum
+    # mn(m+n) flops of the two triangular long-K products), its base case against
+    # HBM (the accumulator form's algorithmic traffic, 25 B per weight: W* 4, the
+    # two far-field offsets 8, D 4, C 4, the code 1, the diagonal factor blocks
+    # about 4), and its time per step of the dependent chain the schedule runs
+    # (64 x 64 leaves, a leaf-diagonal lag of 94 steps: (M + N - 2) 94 + 127 steps)
+    # next to the chain of the rule itself (m + n - 1 anti-diagonals).
+    solve_s = ph["solve"] * 1e-3
+    M, N = (m + 63) // 64, (n + 63) // 64
+    chain = (M + N - 2) * 94 + 127
+    base_bytes = 25.0 * m * n
+    roof_solve = {
+        "kernel": "k_solve_run (+ k_solve_init, k_scales, k_solve_finish)",
+        "time_ms": ph["solve"],
+        "far_field": {"bound": "mfma", "flops": solve_flops, "achieved": solve_flops / solve_s / 1e12,
+                      "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                      "frac": solve_flops / solve_s / 1e12 / PEAK_FP32_MFMA_TFLOPS},
+        "base_case": {"bound": "hbm", "bytes": base_bytes, "achieved": base_bytes / solve_s / 1e9,
+                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": base_bytes / solve_s / 1e9 / PEAK_HBM_GBS,
+                      "traffic": traffic_bytes("solve", args.workload)},
+        "chain": {"steps": chain, "ns_per_step": solve_s * 1e9 / chain, "rule_steps": m + n - 1,
+                  "ns_per_rule_step": solve_s * 1e9 / (m + n - 1)},
+    }
+    tr = roof_solve["base_case"]["traffic"]
+    if tr is not None:
+        roof_solve["base_case"]["counter_gbs"] = tr / solve_s / 1e9
 
     res = {
         "metric": "BaKron ms/layer + weights/s at 4096x4096 2-bit; % of MFMA / HBM roofline",
@@ -312,6 +394,7 @@ def main():
         "solve_gemm_tflops": solve_flops / (ph["solve"] * 1e-3) / 1e12,
         "ldl_fp64_tflops": (m ** 3 + n ** 3) / 3.0 / (ph["ldl"] * 1e-3) / 1e12,
         "roofline": roof,
+        "roofline_solve": roof_solve,
         "proxy_loss": loss,
         "clamped": clamped,
         "info": info,
@@ -336,7 +419,7 @@ def main():
         LI = np.triu(HI.cpu().numpy(), 1).astype(np.float64)
         LO = HO.cpu().numpy()
         res["cpu_baseline"] = cpu_baseline(w, LO, LI, x, args.bits, args.rounding, seed,
-                                           args.cpu_rows)
+                                           args.cpu_rows, g if args.cpu_full else None, args.cpu_full)
     print(json.dumps(res), flush=True)
 
 

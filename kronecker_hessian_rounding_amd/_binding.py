@@ -237,18 +237,30 @@ def sketch_b(grads, HI: Optional[torch.Tensor] = None, HO: Optional[torch.Tensor
     """Sketch B factors from per-sequence weight gradients (S x m x n, or a sequence of m x n):
     H_I = E_s[G_s^T G_s] / m and H_O = E_s[G_s G_s^T] / n. Returns (H_I, H_O)."""
     S = len(grads)
+    if S == 0:
+        raise ValueError("sketch_b needs at least one gradient")
     m, n = grads[0].shape
+    # every argument is checked before the first launch
+    dev = grads[0].device
+    for g in grads:
+        if not isinstance(g, torch.Tensor) or not g.is_cuda or g.dtype != torch.float32:
+            raise ValueError("grads must be CUDA float32 tensors")
+        if tuple(g.shape) != (m, n) or g.device != dev:
+            raise ValueError("every gradient must be %d x %d on %s" % (m, n, dev))
+    for H, d, name in ((HI, n, "H_I"), (HO, m, "H_O")):
+        if H is not None:
+            _mat(H, name)
+            if tuple(H.shape) != (d, d) or H.device != dev:
+                raise ValueError("%s must be %d x %d on %s" % (name, d, d, dev))
     # sum_s G_s^T G_s is X^T X of the gradients stacked vertically: for one contiguous
     # S x m x n tensor H_I is a single accumulation over S m tokens
     # and sum_s G_s G_s^T is one transposed accumulation over the batch (S n tokens)
     stacked = isinstance(grads, torch.Tensor) and grads.dim() == 3 and grads.is_contiguous()
     if stacked:
-        HI = hessian_accum(grads.reshape(S * m, n), HI, alpha=1.0 / (S * m), beta=0.0)
-        if grads.dtype != torch.float32 or not grads.is_cuda:
-            raise ValueError("grads must be a CUDA float32 tensor")
         if HO is None:
-            HO = torch.empty((m, m), dtype=torch.float32, device=grads.device)
+            HO = torch.empty((m, m), dtype=torch.float32, device=dev)
         ldho = _mat(HO, "H_O")
+        HI = hessian_accum(grads.reshape(S * m, n), HI, alpha=1.0 / (S * m), beta=0.0)
         nb = LIB.bakron_hessian_accum_workspace_bytes(S * n, m)
         ws = _workspace(nb, grads.device)
         _check("bakron_hessian_accum_tb",
@@ -438,7 +450,8 @@ def quantize_layer(W: torch.Tensor, X: torch.Tensor, G: Optional[torch.Tensor], 
                    rounding: str = "nearest", seed: int = 0, damp_rel: float = 0.01,
                    want_delta: bool = False, want_loss: bool = True, workspace=None):
     """The whole per-layer path on the device: H_I from X, H_O from G (or H_O = I when
-    G is None), damping + LDL of both, scales, and the BaKron solve."""
+    G is None, damped to (1 + damp_rel) I), damping + LDL of both, scales, and the
+    BaKron solve."""
     m, n = W.shape
     if workspace is None:
         workspace = {}
@@ -450,7 +463,13 @@ def quantize_layer(W: torch.Tensor, X: torch.Tensor, G: Optional[torch.Tensor], 
         LO = HO
     else:
         HI, DI = ldl(HI, damp_rel, workspace.get("DI"))
-        LO, DO = None, None
+        # H_O = I is damped like any factor: (1 + damp_rel) I, so L_O = 0 (the codes of
+        # H_O = I) and D_O = 1 + damp_rel, which enters the proxy loss
+        LO = None
+        DO = workspace.get("DO")
+        if DO is None:
+            DO = torch.empty(m, dtype=torch.float32, device=W.device)
+        DO.fill_(1.0 + damp_rel)
     res = solve(W, LO, HI, bits, rounding, seed, D_O=DO, D_I=DI, want_delta=want_delta,
                 want_loss=want_loss, out=workspace.get("out"))
     return res, (LO, DO, HI, DI)

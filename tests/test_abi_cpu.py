@@ -205,3 +205,24 @@ def test_hessian_accum_tb_rejects_invalid_arguments(lib):
     assert f(None, 2, 8, 16, 16, 128, 1.0, 0.0, fake, 8, fake, 1 << 30, None) == INVALID  # X missing
     assert f(fake, 2, 8, 16, 16, 128, 1.0, 0.0, fake, 7, fake, 1 << 30, None) == INVALID  # ldh < d
     assert f(fake, 2, 8, 16, 16, 128, 1.0, 0.0, fake, 8, None, 0, None) == WORKSPACE      # no workspace
+
+
+def test_sketch_b_checks_arguments_before_any_launch(monkeypatch):
+    # invalid gradients (host tensors here) are rejected before the library is called
+    import torch
+
+    import kronecker_hessian_rounding_amd as bk
+
+    calls = []
+
+    class Spy:
+        def __getattr__(self, name):
+            calls.append(name)
+            raise AssertionError("library called: " + name)
+
+    monkeypatch.setattr(bk._binding, "LIB", Spy())
+    with pytest.raises(ValueError):
+        bk.sketch_b(torch.zeros((2, 8, 16)))
+    with pytest.raises(ValueError):
+        bk.sketch_b([])
+    assert calls == []

@@ -7,10 +7,11 @@ any size:
     against fp64 dot products over all tokens;
   * LDL: sampled entries of (L+I) D (L+I)^T against the damped fp32 factor the
     device was given (backward error), with D > 0 and L strictly upper;
-  * solve: sampled FULL rows replayed by the oracle with the device's factors
-    and the device's own committed error (every code exact or a counted flip
-    inside the 1e-4 band); the device's proxy loss against the oracle's
-    tr(D H_I D^T H_O) where the CPU can afford the two products.
+  * solve: one FULL row from every 64-row block of leaves (plus the first and
+    last rows) replayed by the oracle with the device's factors and the device's
+    own committed error (every code exact or a counted flip inside the 1e-4
+    band); the device's proxy loss against the oracle's tr(D H_I D^T H_O) with
+    the damped factors, evaluated in fp64 row block by row block.
 """
 import sys
 
@@ -20,6 +21,7 @@ import torch
 
 import oracle
 import workloads
+from conftest import record_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -109,9 +111,9 @@ def run_chain(bk, name, rng):
     HId = torch.diagonal(HI).cpu().numpy().astype(np.float64)
     HOd = torch.diagonal(HO).cpu().numpy().astype(np.float64)
     lam_i, lam_o = 0.01 * HId.mean(), 0.01 * HOd.mean()
-    keep = name != "up70b"  # dense copies for the loss check where the CPU can afford it
-    HIc = HI.cpu().numpy() if keep else None
-    HOc = HO.cpu().numpy() if keep else None
+    # the undamped factors, for the proxy-loss check (up70b: 3.3 GB for H_O)
+    HIc = HI.cpu().numpy()
+    HOc = HO.cpu().numpy()
     note("%s: LDL" % name)
     HI, DI = bk.ldl(HI, 0.01)
     HO, DO = bk.ldl(HO, 0.01)
@@ -120,36 +122,55 @@ def run_chain(bk, name, rng):
     return w, W, HI, DI, HO, DO, HIc, HOc, lam_i, lam_o
 
 
-def check_solve(bk, name, w, W, HI, DI, HO, DO, bits, rounding, seed, rng, HIc=None, HOc=None,
-                lam_i=0.0, lam_o=0.0):
+def loss_blockwise(dl, HIc, lam_i, HOc, lam_o, rows=2048):
+    """tr(D H_I D^T H_O) in fp64 with the damped factors, H_O taken a row block at a time."""
+    hi = HIc.astype(np.float64)
+    hi[np.diag_indices_from(hi)] += lam_i
+    DH = dl @ hi                                    # D H_I
+    del hi
+    total = 0.0
+    for r0 in range(0, dl.shape[0], rows):
+        r1 = min(dl.shape[0], r0 + rows)
+        ho = HOc[r0:r1].astype(np.float64)
+        ho[:, r0:r1][np.diag_indices(r1 - r0)] += lam_o
+        total += float(np.sum((ho @ dl) * DH[r0:r1]))  # rows r0..r1 of H_O D, against D H_I
+    return total
+
+
+def check_solve(bk, name, w, W, HI, DI, HO, DO, bits, rounding, seed, rng, HIc, HOc, lam_i, lam_o):
     m, n = w.shape
     note("%s: solve %d-bit %s" % (name, bits, rounding))
-    res = bk.solve(W, HO, HI, bits, rounding, seed, D_O=DO, D_I=DI, want_loss=True,
-                   want_delta=HIc is not None)
+    res = bk.solve(W, HO, HI, bits, rounding, seed, D_O=DO, D_I=DI, want_loss=True)
     torch.cuda.synchronize()
     assert int(res.info.item()) == 0
     codes = res.codes.cpu().numpy()
     scales = res.scales.cpu().numpy()
     assert np.array_equal(scales, oracle.row_scales(w, bits))
-    LO = np.triu(HO.cpu().numpy(), 1)
-    LI = np.triu(HI.cpu().numpy(), 1)
-    rows = sorted(set([0, 1, m // 3, m - 1] + list(rng.integers(0, m, 2))))
+    LO = HO.cpu().numpy()  # L_O above the diagonal (replay reads only the strict upper triangle)
+    LI = HI.cpu().numpy()
+    # one row from every 64-row block of leaves, plus the first and the last row
+    blocks = (m + 63) // 64
+    rows = sorted(set([0, m - 1] + [min(m - 1, 64 * b + int(rng.integers(0, 64))) for b in range(blocks)]))
+    note("  replaying %d rows" % len(rows))
     rp = oracle.replay_rows(w, LO, LI, scales, bits, codes, rows, rounding, seed)
-    note("  replayed rows %s: mismatches %d, flips %d, bad %d, max flip margin %.2e" % (
-        rows, rp["mismatches"], rp["flips"], rp["bad"], rp["max_flip_margin"]))
-    assert rp["bad"] == 0
+    note("  replayed %d rows: mismatches %d, flips %d, bad %d, max flip margin %.2e" % (
+        len(rows), rp["mismatches"], rp["flips"], rp["bad"], rp["max_flip_margin"]))
     loss = float(res.loss.item())
-    if HIc is not None:
-        # tr(D H_I D^T H_O) with the damped factors, D = W* - s (c - Lq/2) exactly
-        Lq = 2**bits - 1
-        dl = w.astype(np.float64) - scales[:, None].astype(np.float64) * (codes - Lq / 2.0)
-        hi = HIc.astype(np.float64)
-        hi[np.diag_indices_from(hi)] += lam_i
-        ho = HOc.astype(np.float64)
-        ho[np.diag_indices_from(ho)] += lam_o
-        ref = oracle.proxy_loss(dl, ho, hi)
-        note("  proxy loss device %.10g  oracle %.10g  rel %.2e" % (loss, ref, abs(loss - ref) / ref))
-        assert abs(loss - ref) <= 1e-4 * abs(ref)
+    Lq = 2**bits - 1
+    note("  proxy loss in fp64 (row blocks)")
+    dl = w.astype(np.float64) - scales[:, None].astype(np.float64) * (codes - Lq / 2.0)
+    del codes
+    ref = loss_blockwise(dl, HIc, lam_i, HOc, lam_o)
+    del dl
+    rel = abs(loss - ref) / ref
+    note("  proxy loss device %.10g  oracle %.10g  rel %.2e  clamped %d" % (loss, ref, rel, int(res.clamped.item())))
+    record_parity("full-" + name, m=m, n=n, bits=bits, rounding=rounding, one_sided=False, entries=m * n,
+                  replayed=len(rows) * n, rows_replayed=len(rows), flips=rp["flips"],
+                  max_flip_margin=rp["max_flip_margin"], replay_mismatches=rp["mismatches"], bad=rp["bad"],
+                  clamped=int(res.clamped.item()), loss=loss, loss_ref=ref, loss_rel=rel)
+    assert rp["bad"] == 0
+    assert rp["max_flip_margin"] < 1e-4
+    assert rel <= 1e-4
     return res
 
 
@@ -169,8 +190,8 @@ def test_mlp_down_full_size(bk):
     check_solve(bk, "mlp_down", w, W, HI, DI, HO, DO, 2, "nearest", 4003, rng, HIc, HOc, li, lo)
 
 
-@pytest.mark.timeout(900)
+@pytest.mark.timeout(1100)
 def test_up70b_full_size(bk):
     rng = np.random.default_rng(13)
-    w, W, HI, DI, HO, DO, _, _, _, _ = run_chain(bk, "up70b", rng)
-    check_solve(bk, "up70b", w, W, HI, DI, HO, DO, 2, "nearest", 4004, rng)
+    w, W, HI, DI, HO, DO, HIc, HOc, li, lo = run_chain(bk, "up70b", rng)
+    check_solve(bk, "up70b", w, W, HI, DI, HO, DO, 2, "nearest", 4004, rng, HIc, HOc, li, lo)
