@@ -28,7 +28,9 @@
  *     columns. No alignment is required.
  *   - The caller owns every buffer, including the workspace; the library
  *     never allocates, frees or retains memory and keeps no state between
- *     calls. Calls on different streams may run concurrently.
+ *     calls. Calls on different streams may run concurrently. The one
+ *     exception is bakron_solve_noalloc, which works in a fixed scratch array
+ *     that the library holds on each device (see there).
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream). Only bakron_ldl waits for its work to finish (bakron_ldl_async
  *     does not).
@@ -241,6 +243,34 @@ int bakron_solve(const float* W, int64_t m, int64_t n, int64_t ldw, const float*
                  int64_t ldc, float* scales_out, float* delta_out, int64_t ldd, const float* D_O,
                  const float* D_I, double* loss_out, int64_t* clamped_out, int32_t* info,
                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * solve as bakron_solve, with the same arguments, outputs and errors, but its
+ * workspace is a scratch array of BAKRON_NOALLOC_SCRATCH_BYTES that the
+ * library holds in device memory (one per device, from the moment the library
+ * is loaded on it until the process ends) instead of a caller's buffer. The
+ * call allocates nothing: no hipMalloc, no hipFree, no allocating library
+ * routine.
+ *   Sizes: bakron_solve_workspace_bytes(m, n) must not exceed
+ *      BAKRON_NOALLOC_SCRATCH_BYTES (for example m = n = 2048, or
+ *      m = 1024 with n up to 4096); larger shapes return BAKRON_E_WORKSPACE
+ *      before anything is enqueued.
+ *   Sharing: every call on a device uses that device's one array, which keeps
+ *      the last call's contents (the solve clears what must start at zero).
+ *      Calls that overlap on one device -- on two streams, or from two host
+ *      threads -- race on it; calls in one stream are ordered and safe.
+ *   Errors: those of bakron_solve (INVALID_ARG, WORKSPACE as above), and
+ *      BAKRON_E_DEVICE if the scratch array's address cannot be obtained on
+ *      the current device.
+ */
+#define BAKRON_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int bakron_solve_noalloc(const float* W, int64_t m, int64_t n, int64_t ldw, const float* L_O, int64_t ldlo,
+                         const float* L_I, int64_t ldli, const bakron_quantizer* q, uint8_t* codes,
+                         int64_t ldc, float* scales_out, float* delta_out, int64_t ldd, const float* D_O,
+                         const float* D_I, double* loss_out, int64_t* clamped_out, int32_t* info,
+                         void* stream);
 
 /*
  * Randomised Hadamard rotation, for two-sided incoherence processing before

@@ -77,16 +77,22 @@ def _load() -> ctypes.CDLL:
     lib.bakron_solve.restype = ctypes.c_int
     lib.bakron_solve.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, ctypes.POINTER(_Quantizer),
                                  vp, i64, vp, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.bakron_solve_noalloc.restype = ctypes.c_int
+    lib.bakron_solve_noalloc.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, ctypes.POINTER(_Quantizer),
+                                         vp, i64, vp, vp, i64, vp, vp, vp, vp, vp, vp]
     return lib
 
 
 LIB = _load()
 
+# bytes of the device scratch array that bakron_solve_noalloc works in
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
 EXPORTS = ("bakron_abi_version", "bakron_status_str", "bakron_hessian_accum_workspace_bytes",
            "bakron_hessian_accum", "bakron_hessian_accum_t", "bakron_hessian_accum_tb",
            "bakron_hessian_accum_w",
            "bakron_token_weights_workspace_bytes", "bakron_token_weights", "bakron_ldl_workspace_bytes", "bakron_ldl", "bakron_ldl_async",
-           "bakron_solve_workspace_bytes", "bakron_solve", "bakron_rht",
+           "bakron_solve_workspace_bytes", "bakron_solve", "bakron_solve_noalloc", "bakron_rht",
            "bakron_layer_report")
 
 
@@ -396,6 +402,45 @@ def solve(W: torch.Tensor, L_O: Optional[torch.Tensor], L_I: Optional[torch.Tens
                           _ptr(out.delta), ldd, _ptr(D_O), _ptr(D_I), _ptr(out.loss),
                           _ptr(out.clamped), _ptr(out.info), _ptr(ws), nb, _stream())
     _check("bakron_solve", st)
+    return out
+
+
+def solve_noalloc(W: torch.Tensor, L_O: Optional[torch.Tensor], L_I: Optional[torch.Tensor], bits: int,
+                  out: SolveResult, rounding: str = "nearest", seed: int = 0,
+                  row_scale: Optional[torch.Tensor] = None, D_O: Optional[torch.Tensor] = None,
+                  D_I: Optional[torch.Tensor] = None) -> SolveResult:
+    """solve() through bakron_solve_noalloc: the caller passes every output in `out`
+    (codes, scales, info, and optionally delta, loss, clamped) and nothing is
+    allocated, by this function or by the library, which works in its own device
+    scratch array (shapes up to NOALLOC_SCRATCH_BYTES of workspace). For callers that
+    cannot allocate, e.g. under HIP graph capture. Calls that overlap on one device
+    share the array and race."""
+    ldw = _mat(W, "W")
+    m, n = W.shape
+    ldlo = ldli = 0
+    if L_O is not None:
+        ldlo = _mat(L_O, "L_O")
+        if tuple(L_O.shape) != (m, m):
+            raise ValueError("L_O must be %d x %d" % (m, m))
+    if L_I is not None:
+        ldli = _mat(L_I, "L_I")
+        if tuple(L_I.shape) != (n, n):
+            raise ValueError("L_I must be %d x %d" % (n, n))
+    _vec(row_scale, "row_scale", m)
+    _vec(D_O, "D_O", m)
+    _vec(D_I, "D_I", n)
+    if tuple(out.codes.shape) != (m, n) or out.scales.numel() != m:
+        raise ValueError("out.codes must be %d x %d and out.scales [%d]" % (m, n, m))
+    if out.delta is not None and tuple(out.delta.shape) != (m, n):
+        raise ValueError("out.delta must be %d x %d" % (m, n))
+    q = _Quantizer(int(bits), ROUNDING[rounding], int(seed) & (2**64 - 1),
+                   None if row_scale is None else row_scale.data_ptr())
+    ldd = n if out.delta is None else _mat(out.delta, "delta")
+    st = LIB.bakron_solve_noalloc(_ptr(W), m, n, ldw, _ptr(L_O), ldlo, _ptr(L_I), ldli, ctypes.byref(q),
+                                  _ptr(out.codes), _mat(out.codes, "codes", torch.uint8), _ptr(out.scales),
+                                  _ptr(out.delta), ldd, _ptr(D_O), _ptr(D_I), _ptr(out.loss),
+                                  _ptr(out.clamped), _ptr(out.info), _stream())
+    _check("bakron_solve_noalloc", st)
     return out
 
 

@@ -1,11 +1,84 @@
 // bk_api.hip -- the extern "C" entry points of libbakron: argument validation on
 // the host, workspace checks, then dispatch to the kernel drivers. Every check
 // happens before anything is enqueued, so an invalid call enqueues no work.
+#include <mutex>
+
 #include "bk_internal.hpp"
 
 namespace {
 
 bool bad_ld(int64_t ld, int64_t cols) { return ld < cols || ld <= 0; }
+
+// The solve's workspace for callers that cannot allocate (bakron_solve_noalloc):
+// one array per device, held from the moment the library is loaded on it. In
+// host code `scratch` is only a stand-in for the symbol; its device address is
+// taken once per device with hipGetSymbolAddress and used from then on.
+__device__ __align__(256) unsigned char scratch[BAKRON_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// The device address of `scratch` on the current device, or nullptr.
+void* scratch_address() {
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
+// Host-side checks of the solve's arguments (shared by both solve entry points).
+int check_solve_args(const float* W, int64_t m, int64_t n, int64_t ldw, const float* L_O, int64_t ldlo,
+                     const float* L_I, int64_t ldli, const bakron_quantizer* q, const uint8_t* codes,
+                     int64_t ldc, const float* scales_out, const float* delta_out, int64_t ldd,
+                     const float* D_O, const float* D_I, const double* loss_out) {
+    if (!W || !q || !codes || !scales_out) return BAKRON_E_INVALID_ARG;
+    if (m <= 0 || n <= 0 || bad_ld(ldw, n) || bad_ld(ldc, n)) return BAKRON_E_INVALID_ARG;
+    if (m > (int64_t)1 << 30 || n > (int64_t)1 << 30) return BAKRON_E_INVALID_ARG;
+    if (L_O && bad_ld(ldlo, m)) return BAKRON_E_INVALID_ARG;
+    if (L_I && bad_ld(ldli, n)) return BAKRON_E_INVALID_ARG;
+    if (delta_out && bad_ld(ldd, n)) return BAKRON_E_INVALID_ARG;
+    if (q->bits < 1 || q->bits > 8) return BAKRON_E_INVALID_ARG;
+    if (q->rounding != BAKRON_ROUND_NEAREST && q->rounding != BAKRON_ROUND_STOCHASTIC)
+        return BAKRON_E_INVALID_ARG;
+    if (loss_out && (!D_I || (!D_O && L_O))) return BAKRON_E_INVALID_ARG;
+    return BAKRON_OK;
+}
+
+bk::SolveArgs solve_args(const float* W, int64_t m, int64_t n, int64_t ldw, const float* L_O, int64_t ldlo,
+                         const float* L_I, int64_t ldli, const bakron_quantizer* q, uint8_t* codes,
+                         int64_t ldc, float* scales_out, float* delta_out, int64_t ldd, const float* D_O,
+                         const float* D_I, double* loss_out, int64_t* clamped_out, int32_t* info) {
+    bk::SolveArgs a;
+    a.W = W;
+    a.m = m;
+    a.n = n;
+    a.ldw = ldw;
+    a.LO = L_O;
+    a.ldlo = ldlo;
+    a.LI = L_I;
+    a.ldli = ldli;
+    a.bits = q->bits;
+    a.stochastic = q->rounding == BAKRON_ROUND_STOCHASTIC;
+    a.seed = q->seed;
+    a.row_scale = q->row_scale;
+    a.codes = codes;
+    a.ldc = ldc;
+    a.scales = scales_out;
+    a.delta = delta_out;
+    a.ldd = ldd;
+    a.DO = D_O;
+    a.DI = D_I;
+    a.loss = loss_out;
+    a.clamped = clamped_out;
+    a.info = info;
+    return a;
+}
 
 }  // namespace
 
@@ -112,41 +185,29 @@ int bakron_solve(const float* W, int64_t m, int64_t n, int64_t ldw, const float*
                  int64_t ldc, float* scales_out, float* delta_out, int64_t ldd, const float* D_O,
                  const float* D_I, double* loss_out, int64_t* clamped_out, int32_t* info,
                  void* ws, size_t ws_bytes, void* stream) {
-    if (!W || !q || !codes || !scales_out) return BAKRON_E_INVALID_ARG;
-    if (m <= 0 || n <= 0 || bad_ld(ldw, n) || bad_ld(ldc, n)) return BAKRON_E_INVALID_ARG;
-    if (m > (int64_t)1 << 30 || n > (int64_t)1 << 30) return BAKRON_E_INVALID_ARG;
-    if (L_O && bad_ld(ldlo, m)) return BAKRON_E_INVALID_ARG;
-    if (L_I && bad_ld(ldli, n)) return BAKRON_E_INVALID_ARG;
-    if (delta_out && bad_ld(ldd, n)) return BAKRON_E_INVALID_ARG;
-    if (q->bits < 1 || q->bits > 8) return BAKRON_E_INVALID_ARG;
-    if (q->rounding != BAKRON_ROUND_NEAREST && q->rounding != BAKRON_ROUND_STOCHASTIC)
-        return BAKRON_E_INVALID_ARG;
-    if (loss_out && (!D_I || (!D_O && L_O))) return BAKRON_E_INVALID_ARG;
+    const int st = check_solve_args(W, m, n, ldw, L_O, ldlo, L_I, ldli, q, codes, ldc, scales_out, delta_out,
+                                    ldd, D_O, D_I, loss_out);
+    if (st != BAKRON_OK) return st;
     if (!ws || ws_bytes < bk::solve_workspace_bytes(m, n)) return BAKRON_E_WORKSPACE;
-    bk::SolveArgs a;
-    a.W = W;
-    a.m = m;
-    a.n = n;
-    a.ldw = ldw;
-    a.LO = L_O;
-    a.ldlo = ldlo;
-    a.LI = L_I;
-    a.ldli = ldli;
-    a.bits = q->bits;
-    a.stochastic = q->rounding == BAKRON_ROUND_STOCHASTIC;
-    a.seed = q->seed;
-    a.row_scale = q->row_scale;
-    a.codes = codes;
-    a.ldc = ldc;
-    a.scales = scales_out;
-    a.delta = delta_out;
-    a.ldd = ldd;
-    a.DO = D_O;
-    a.DI = D_I;
-    a.loss = loss_out;
-    a.clamped = clamped_out;
-    a.info = info;
-    return bk::run_solve(a, ws, (hipStream_t)stream);
+    return bk::run_solve(solve_args(W, m, n, ldw, L_O, ldlo, L_I, ldli, q, codes, ldc, scales_out, delta_out, ldd,
+                                    D_O, D_I, loss_out, clamped_out, info),
+                         ws, (hipStream_t)stream);
+}
+
+int bakron_solve_noalloc(const float* W, int64_t m, int64_t n, int64_t ldw, const float* L_O, int64_t ldlo,
+                         const float* L_I, int64_t ldli, const bakron_quantizer* q, uint8_t* codes,
+                         int64_t ldc, float* scales_out, float* delta_out, int64_t ldd, const float* D_O,
+                         const float* D_I, double* loss_out, int64_t* clamped_out, int32_t* info,
+                         void* stream) {
+    const int st = check_solve_args(W, m, n, ldw, L_O, ldlo, L_I, ldli, q, codes, ldc, scales_out, delta_out,
+                                    ldd, D_O, D_I, loss_out);
+    if (st != BAKRON_OK) return st;
+    if (bk::solve_workspace_bytes(m, n) > BAKRON_NOALLOC_SCRATCH_BYTES) return BAKRON_E_WORKSPACE;
+    void* ws = scratch_address();
+    if (ws == nullptr) return BAKRON_E_DEVICE;
+    return bk::run_solve(solve_args(W, m, n, ldw, L_O, ldlo, L_I, ldli, q, codes, ldc, scales_out, delta_out, ldd,
+                                    D_O, D_I, loss_out, clamped_out, info),
+                         ws, (hipStream_t)stream);
 }
 
 int bakron_layer_report(int64_t m, int64_t n, const float* D_O, const float* D_I, const float* scales,

@@ -226,3 +226,23 @@ def test_sketch_b_checks_arguments_before_any_launch(monkeypatch):
     with pytest.raises(ValueError):
         bk.sketch_b([])
     assert calls == []
+
+
+def test_solve_noalloc_rejects_bad_arguments_and_oversize_shapes(lib):
+    # validated on the host before the library's scratch array is touched: the same
+    # argument errors as bakron_solve, and BAKRON_E_WORKSPACE for shapes whose
+    # workspace exceeds the scratch array
+    import kronecker_hessian_rounding_amd as bk
+
+    q = bk._binding._Quantizer(2, 0, 0, None)
+    f = lib.bakron_solve_noalloc
+    args = lambda m, n, qq: (FAKE, m, n, n, FAKE, m, FAKE, n, qq, FAKE, n, FAKE, None, n, None, None, None,
+                             None, None, None)
+    assert f(*args(0, 64, ctypes.byref(q))) == 1
+    assert f(*args(64, 64, None)) == 1
+    bad = bk._binding._Quantizer(9, 0, 0, None)
+    assert f(*args(64, 64, ctypes.byref(bad))) == 1
+    assert lib.bakron_solve_workspace_bytes(4096, 4096) > bk.NOALLOC_SCRATCH_BYTES
+    assert f(*args(4096, 4096, ctypes.byref(q))) == 3
+    assert lib.bakron_solve_workspace_bytes(2048, 2048) <= bk.NOALLOC_SCRATCH_BYTES
+    assert lib.bakron_solve_workspace_bytes(1024, 4096) <= bk.NOALLOC_SCRATCH_BYTES
