@@ -1,8 +1,9 @@
 """Benchmark of the BaKron per-layer hot path on one MI355X.
 
 One step = the whole path for one layer on synthetic inputs already resident
-in HBM: H_I = X^T X / T and H_O = G^T G / T (fp32 products formed from three
-bf16 pieces per operand on the bf16 matrix cores), damping + LDL of
+in HBM: H_I = X^T X / T and H_O = G^T G / T (fp32 products formed from two
+fp16 pieces per operand of power-of-two-scaled columns on the fp16 matrix
+cores), damping + LDL of
 both (fp64), fp32 per-row scales, and the BaKron rounding solve with its proxy
 loss. Default workload: the attention-projection shape, W* 4096 x 4096,
 T = 32768 tokens, 2-bit nearest rounding.
@@ -25,8 +26,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 PEAK_FP32_MFMA_TFLOPS = 157.3
-PEAK_BF16_MFMA_TFLOPS = 2500.0
-PIECE_PRODUCTS = 6  # bf16 piece products per fp32 product in the Hessian
+PEAK_F16_MFMA_TFLOPS = 2500.0
+PIECE_PRODUCTS = 3  # fp16 piece products per fp32 product in the Hessian
 PEAK_FP64_MFMA_TFLOPS = 78.6
 CAL_BYTES = 256 << 20
 
@@ -39,8 +40,6 @@ CAL_BYTES = 256 << 20
 # removed, so edits to comments keep it and any code change drops it (null).
 CAL_FETCH_KIB, CAL_WRITE_KIB = 131089.0, 262144.0
 COUNTERS = {
-    # one hessian_accum call at attn: k_split3 + k_syrk3_full (+ split-K pair)
-    ("hessian", "attn", "5bc2996ba9af1e89"): {"fetch_kib": 2270509.1, "write_kib": 887728.2},
     # one solve at attn, 2-bit nearest: k_solve_run
     ("solve", "attn", "ba6389e41bb2d18e"): {"fetch_kib": 4472228.2, "write_kib": 643941.2},
 }
@@ -315,17 +314,17 @@ def main():
         syrk_ms = float(np.mean(ev["hess_I"] + ev["hess_O"]))
         # algorithmic fp32 flops per call, averaged over the two calls: T d^2 per
         # factor (the upper half, T d^2 / 2 FMAs at 2 flops each); the matrix cores
-        # run six bf16 piece products for each
+        # run three fp16 piece products for each
         syrk_flops = float(T) * (n * n + m * m) / 2.0
     solve_flops = float(m) * n * (m + n)            # far-field feedback, minimal
     dominant = max(ph, key=ph.get)
     fp32_equiv = syrk_flops / (syrk_ms * 1e-3) / 1e12
     roof = {
-        "kernel": "hessian_accum: k_split3 + k_syrk3_full (+ k_syrk3_split, k_syrk_reduce), "
-                  "bf16 MFMA, six piece products per fp32 product",
+        "kernel": "hessian_accum: k_colmax + k_colexp + k_split2 + k_syrk2_full (+ k_syrk2_split, "
+                  "k_syrk_reduce), fp16 MFMA, three piece products per fp32 product",
         "bound": "mfma",
         "achieved": PIECE_PRODUCTS * fp32_equiv,
-        "peak": PEAK_BF16_MFMA_TFLOPS,
+        "peak": PEAK_F16_MFMA_TFLOPS,
         "unit": "TFLOP/s",
         "traffic": None if args.hessian != "tokens" else traffic_bytes("hessian", args.workload),
         "flops_per_call": PIECE_PRODUCTS * syrk_flops,
@@ -334,7 +333,7 @@ def main():
     }
     if args.hessian == "sketch_a":
         roof.update(kernel="sketch_a phase: token-weight tile GEMMs (fp32 MFMA) and weighted SYRKs "
-                           "(bf16 pieces), in fp32-equivalent flops",
+                           "(fp16 pieces), in fp32-equivalent flops",
                     achieved=fp32_equiv, peak=PEAK_FP32_MFMA_TFLOPS, flops_per_call=syrk_flops)
     roof["frac"] = roof["achieved"] / roof["peak"]
 
@@ -378,8 +377,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "dtype_detail": "Hessian: fp32 products as six bf16 piece products, fp32 accumulate; "
-                        "LDL: fp64; solve: fp32",
+        "dtype_detail": "Hessian: fp32 products as three fp16 piece products of power-of-two-scaled "
+                        "columns, fp32 accumulate; LDL: fp64; solve: fp32",
         "data": "synthetic",
         "config": {"workload": "%s, %d-bit %s" % (WORKLOAD_LABEL[args.workload], args.bits,
                                                   args.rounding),

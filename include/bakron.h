@@ -97,17 +97,21 @@ const char* bakron_status_str(int status);
  *   T == 0 scales H by beta.
  *   ws: optional device workspace; its size picks the arithmetic.
  *      - At least bakron_hessian_accum_workspace_bytes(T, d) bytes: the
- *        product runs on the bf16 matrix cores. X is first cut into three
- *        bf16 pieces per element (x = h + m + l to within 2^-24 |x|), stored
- *        in ws: 6 bytes per element of X, with T padded to a multiple of 32
- *        and d to a multiple of 128. Each product is then the sum of six
- *        piece products (hh, hm, mh, hl, lh, mm), accumulated in fp32. The
- *        terms left out are below 2^-23 |x y|, so the error is of the order
- *        of an fp32 product's. The remainder of ws (after the pieces,
- *        256-byte aligned) holds the split-K partials of a short last round
- *        of output tiles.
- *      - NULL or smaller: the product runs on the fp32 matrix cores (1.6x
- *        slower at T = 32768, d = 4096, 2.2x with no workspace at all). A
+ *        product runs on the fp16 matrix cores. Each column c of X is scaled
+ *        by a power of two 2^e_c that puts its largest magnitude in
+ *        [2^14, 2^15), and each scaled element is cut into two fp16 pieces
+ *        (x' = h + l to within 2^-22 |x'| for |x'| >= 2^-3, i.e. within 2^17
+ *        of the column's largest magnitude; an absolute 2^-25 below that),
+ *        stored in ws: 4 bytes per element of X, with T padded to a multiple
+ *        of 32 and d to a multiple of 128, then the exponents and the
+ *        column-maximum partials. Each product is the sum of three piece
+ *        products (hh, hl, lh), exact in fp32 and accumulated in fp32, then
+ *        scaled back by 2^-(e_i + e_j). The term left out is below
+ *        2^-22 |x y|, so the error is of the order of an fp32 product's.
+ *        The remainder of ws (after the pieces, 256-byte aligned) holds the
+ *        split-K partials of a short last round of output tiles.
+ *      - NULL or smaller: the product runs on the fp32 matrix cores (2.3x
+ *        slower at T = 32768, d = 4096, 3.2x with no workspace at all). A
  *        workspace too small for the pieces is still used for those split-K
  *        partials if it is large enough.
  *      Both paths are within fp32 rounding of X^T X, but their results are
@@ -128,7 +132,7 @@ int bakron_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, floa
  * the input-side term E_s[G_s^T G_s] / m is bakron_hessian_accum with T = m.
  *   X: d x T fp32, ldx >= T. H: d x d fp32, ldh >= d, both triangles written.
  *   ws: at least bakron_hessian_accum_workspace_bytes(T, d) bytes (this form
- *       runs on the three-piece path only).
+ *       runs on the fp16 piece path only).
  * Errors: INVALID_ARG as for bakron_hessian_accum (with ldx >= T);
  * WORKSPACE if ws is NULL or too small.
  */
@@ -149,7 +153,7 @@ int bakron_hessian_accum_t(const float* X, int64_t T, int64_t d, int64_t ldx, fl
  *   bakron_token_weights_workspace_bytes(T, d) (Y transposed, d T floats).
  * bakron_hessian_accum_w: H <- beta H + alpha sum_t w[t] x_t^T x_t for w >= 0
  *   (negative weights count as 0), X as in bakron_hessian_accum, on the
- *   three-piece path (ws at least bakron_hessian_accum_workspace_bytes(T, d)).
+ *   fp16 piece path (ws at least bakron_hessian_accum_workspace_bytes(T, d)).
  * Errors: INVALID_ARG for NULL pointers, d <= 0, T < 0, bad ld; WORKSPACE for a
  * missing or short workspace.
  */

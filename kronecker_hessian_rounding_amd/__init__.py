@@ -4,7 +4,7 @@ The computation runs in libbakron (HIP kernels for gfx950, C ABI in
 include/bakron.h); this package is a thin ctypes binding that takes PyTorch
 tensors for device memory and uses the current stream.
 
-  hessian_accum(X)            H <- beta H + alpha X^T X            (bf16 pieces, fp32 accuracy)
+  hessian_accum(X)            H <- beta H + alpha X^T X            (fp16 pieces, fp32 accuracy)
   sketch_b(grads)             H_I = E[G^T G]/m, H_O = E[G G^T]/n from per-sequence gradients
   sketch_a(X, G, iters)       alternating factor estimate with per-token weights
   ldl(H, damp_rel)            H + lambda I = (L + I) D (L + I)^T   (fp64, L strictly upper)

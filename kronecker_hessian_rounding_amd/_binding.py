@@ -169,16 +169,17 @@ def hessian_accum(X: torch.Tensor, H: Optional[torch.Tensor] = None, alpha: Opti
                   weights: Optional[torch.Tensor] = None) -> torch.Tensor:
     """H <- beta H + alpha X^T X (default alpha = 1/T) on the device.
 
-    pieces=True passes the full workspace: each fp32 product is formed from three
-    bf16 pieces per operand on the bf16 matrix cores. pieces=False passes none,
+    pieces=True passes the full workspace: each fp32 product is formed from two
+    fp16 pieces per operand (of power-of-two-scaled columns) on the fp16 matrix
+    cores. pieces=False passes none,
     which selects the fp32 matrix-core path. transposed=True takes X as d x T and
-    forms alpha X X^T (three-piece path only). weights (T,) forms
-    alpha sum_t w_t x_t^T x_t (three-piece path only).
+    forms alpha X X^T (piece path only). weights (T,) forms
+    alpha sum_t w_t x_t^T x_t (piece path only).
     """
     ldx = _mat(X, "X")
     if transposed:
         if not pieces:
-            raise ValueError("the transposed form runs on the three-piece path only")
+            raise ValueError("the transposed form runs on the fp16 piece path only")
         d, T = X.shape
     else:
         T, d = X.shape
@@ -193,7 +194,7 @@ def hessian_accum(X: torch.Tensor, H: Optional[torch.Tensor] = None, alpha: Opti
     ws = _workspace(nb, X.device)
     if weights is not None:
         if transposed or not pieces:
-            raise ValueError("token weights take the untransposed three-piece path")
+            raise ValueError("token weights take the untransposed fp16 piece path")
         wv = _vec(weights, "weights", T)
         _check("bakron_hessian_accum_w",
                LIB.bakron_hessian_accum_w(_ptr(X), T, d, ldx, _ptr(wv), alpha, beta, _ptr(H), ldh, _ptr(ws),

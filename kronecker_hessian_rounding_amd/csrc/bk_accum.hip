@@ -10,8 +10,9 @@
 // exactly symmetric.
 //
 // Two arithmetic paths, picked by the workspace the caller passes:
-//  * three bf16 pieces per element on the bf16 matrix cores (the piece path,
-//    below k_syrk_reduce), when the workspace holds the pieces;
+//  * two fp16 pieces per element, of columns scaled by powers of two, on the
+//    fp16 matrix cores (the piece path, below k_syrk_reduce), when the
+//    workspace holds the pieces;
 //  * fp32 MFMA otherwise.
 // Both keep the product to fp32 accuracy.
 //
@@ -294,23 +295,27 @@ __device__ __forceinline__ int syrk_col(int cb) {
     return (w & 1) * 64 + 32 * cb + (lane & 31);
 }
 
-// Write alpha * acc (+ beta H) into tile (bi, bj) of H and its mirror.
+// Write alpha * acc (+ beta H) into tile (bi, bj) of H and its mirror. With exps
+// (the piece path's column exponents), acc holds the product of the scaled columns
+// and is first scaled back by 2^-(e_i + e_j), exactly.
 __device__ __forceinline__ void syrk_write(float* __restrict__ H, int64_t ldh, int64_t d,
                                            int64_t bi, int64_t bj, float alpha, float beta,
-                                           const f32x16 (&acc)[2][2]) {
+                                           const f32x16 (&acc)[2][2], const int* __restrict__ exps) {
     const int64_t r0 = bi * kT128, c0 = bj * kT128;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
             const int c = syrk_col(cb);
+            const int ec = exps ? exps[c0 + c] : 0;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int r = syrk_row(rb, v);
                 const int64_t gi = r0 + r, gj = c0 + c;
                 if (gi >= d || gj >= d) continue;
                 if (bi == bj && r > c) continue;
-                float val = alpha * acc[rb][cb][v];
+                const float a = exps ? ldexpf(acc[rb][cb][v], -(exps[gi] + ec)) : acc[rb][cb][v];
+                float val = alpha * a;
                 if (beta != 0.0f) val = fmaf(beta, H[gi * ldh + gj], val);
                 H[gi * ldh + gj] = val;
                 if (gi != gj) H[gj * ldh + gi] = val;
@@ -336,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void k_syrk_full(const float* __restrict_
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
     syrk_tile(X, ldx, bi * kT128, R, bj * kT128, Cn, 0, T, acc, sm);
-    syrk_write(H, ldh, d, bi, bj, alpha, beta, acc);
+    syrk_write(H, ldh, d, bi, bj, alpha, beta, acc, nullptr);
 }
 
 // Tiles [tile_beg, tile_beg + ntiles), each split into nsplit K-ranges; block
@@ -380,7 +385,8 @@ __global__ __launch_bounds__(kThreads) void k_syrk_split(const float* __restrict
 __global__ __launch_bounds__(kThreads) void k_syrk_reduce(int64_t d, float alpha, float beta,
                                                           float* __restrict__ H, int64_t ldh,
                                                           int64_t nb, int64_t tile_beg, int nsplit,
-                                                          const float* __restrict__ part) {
+                                                          const float* __restrict__ part,
+                                                          const int* __restrict__ exps) {
     const int u = blockIdx.x;
     int64_t bi, bj;
     upper_tile(tile_beg + u, nb, bi, bj);
@@ -395,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void k_syrk_reduce(int64_t d, float alpha
         const int64_t gi = bi * kT128 + r, gj = bj * kT128 + c;
         if (gi >= d || gj >= d) continue;
         if (bi == bj && r > c) continue;
-        float val = alpha * s[k];
+        float val = alpha * (exps ? ldexpf(s[k], -(exps[gi] + exps[gj])) : s[k]);
         if (beta != 0.0f) val = fmaf(beta, H[gi * ldh + gj], val);
         H[gi * ldh + gj] = val;
         if (gi != gj) H[gj * ldh + gi] = val;
@@ -403,71 +409,161 @@ __global__ __launch_bounds__(kThreads) void k_syrk_reduce(int64_t d, float alpha
 }
 
 // ---------------------------------------------------------------------------
-// The three-piece bf16 path.
+// The two-piece fp16 path.
 //
-// The gfx950 matrix cores multiply bf16 pairs at sixteen times their fp32 rate.
-// Each x of X is cut into three bf16 pieces, h = bf16(x), m = bf16(x - h) and
-// l = bf16(x - h - m), rounding to nearest even; both differences are exact in
-// fp32, and |x - (h + m + l)| <= 2^-24 |x|, so the pieces hold x to fp32
-// precision. A product x y is taken as hh' + hm' + mh' + hl' + lh' + mm'; the
-// terms left out (ml' + lm' + ll') are below 2^-23 |x y|. The bf16 products are
-// exact in fp32 and add into fp32 accumulators, so the sum carries errors of
-// the order of the fp32 product's, for six matrix-core passes at a sixteenth of
-// the cost each.
+// The gfx950 matrix cores multiply fp16 pairs at sixteen times their fp32
+// rate. Column c of X is first scaled by a power of two, x' = x 2^e_c, chosen
+// so that the column's largest magnitude lies in [2^14, 2^15) (well inside the
+// fp16 range; e_c = 0 for a zero or non-finite column). Each x' is cut into two
+// fp16 pieces, h = fp16(x') and l = fp16(x' - h), rounding to nearest even;
+// x' - h is exact in fp32, |x' - h| <= 2^-11 |x'| and |x' - h - l| <= 2^-22 |x'|
+// while l is a normal fp16, i.e. for |x'| >= 2^-3, within 2^17 of the column's
+// largest magnitude; below that l carries an absolute error of at most 2^-25
+// (half the smallest fp16 step), 2^-39 of the column's largest magnitude. A
+// product x'y' is taken as hh' + hl' + lh'; the term left out (ll') is below
+// 2^-22 |x'y'|. The fp16 products are exact in fp32 and add into fp32
+// accumulators, so a 128 x 128 tile of H costs three matrix-core passes at a
+// sixteenth of the fp32 cost each, and the pieces take 4 bytes per element.
+// The tile's result is scaled back by 2^-(e_i + e_j), which is exact.
 //
-// A pre-pass writes the pieces in the order the MFMA reads them: for each group
-// g of 8 consecutive tokens and each column c, the 8 bf16 values of that column
-// (16 bytes), piece planes apart: Xs[piece][g][c][0..7]. The tokens are padded
-// with zeros to a whole number of stages and the columns to whole 128-wide
-// tiles, so every tile streams whole 2 KB rows of Xs straight into LDS.
+// The pre-pass: per-column maxima over chunks of tokens (k_colmax /
+// k_colmax_t), their reduction to the exponents (k_colexp), then the split
+// (k_split2 / k_split2_t), which writes the pieces in the order the MFMA reads
+// them: for each group g of 8 consecutive tokens and each column c, the 8 fp16
+// values of that column (16 bytes), piece planes apart: Xs[piece][g][c][0..7].
+// The tokens are padded with zeros to a whole number of stages and the columns
+// to whole 128-wide tiles, so every tile streams whole 2 KB rows of Xs straight
+// into LDS.
 // ---------------------------------------------------------------------------
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-#ifndef BK_S3_KB
-#define BK_S3_KB 1
+#ifndef BK_S2_NS
+#define BK_S2_NS 4
 #endif
-#ifndef BK_S3_NS
-#define BK_S3_NS 3
+#ifndef BK_S2_KB
+#define BK_S2_KB 1
 #endif
-constexpr int kS3KB = BK_S3_KB;  // 16-token blocks per stage
-constexpr int kS3NS = BK_S3_NS;  // stages in the ring: loads run kS3NS - 1 stages ahead
-constexpr int64_t kS3Pad = 32;   // tokens are padded to a multiple of this (a multiple of 16 kS3KB)
-static_assert(kS3Pad % (16 * kS3KB) == 0, "whole stages");
+constexpr int kNP = 2;           // fp16 pieces per element
+constexpr int kS2NS = BK_S2_NS;  // stages in the ring: loads run kS2NS - 1 stages ahead
+constexpr int kS2KB = BK_S2_KB;  // 16-token blocks per stage
+constexpr int64_t kS2Pad = 32;   // tokens are padded to a multiple of this (whole stages)
+static_assert(kS2Pad % (16 * kS2KB) == 0, "whole stages");
+constexpr int kMaxChunks = 256;  // token chunks of the column-maximum pass
 
-struct Split3Shape {
+struct Split2Shape {
     int64_t ng;  // groups of 8 tokens (padded)
     int64_t dp;  // columns (padded to whole tiles)
     int64_t nstage;
+    int nchunk;       // token chunks of the column-maximum pass
+    size_t exps_off;  // int32 [dp] column exponents
+    size_t cmax_off;  // fp32 [nchunk][dp] partial column maxima
     size_t bytes;
 };
-inline Split3Shape split3_shape(int64_t T, int64_t d) {
-    Split3Shape s;
-    const int64_t Tp = (T + kS3Pad - 1) / kS3Pad * kS3Pad;
+inline Split2Shape split2_shape(int64_t T, int64_t d) {
+    Split2Shape s;
+    const int64_t Tp = (T + kS2Pad - 1) / kS2Pad * kS2Pad;
     s.ng = Tp / 8;
     s.dp = (d + kT128 - 1) / kT128 * kT128;
-    s.nstage = Tp / (16 * kS3KB);
-    s.bytes = align256((size_t)3 * (size_t)Tp * (size_t)s.dp * 2);
+    s.nstage = Tp / (16 * kS2KB);
+    s.nchunk = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxChunks, (T + 127) / 128));
+    size_t o = align256((size_t)kNP * (size_t)Tp * (size_t)s.dp * 2);
+    s.exps_off = o;
+    o += align256(sizeof(int) * (size_t)s.dp);
+    s.cmax_off = o;
+    o += align256(sizeof(float) * (size_t)s.nchunk * (size_t)s.dp);
+    s.bytes = o;
     return s;
 }
 
-// bf16 bits of x, rounded to nearest even; infinities stay, NaNs stay NaN
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-    const uint32_t u = __float_as_uint(x);
-    if ((u & 0x7f800000u) == 0x7f800000u) return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-__device__ __forceinline__ float bf16_value(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ float nan_max(float m, float a) { return (a > m || a != a) ? a : m; }
 
-// the three pieces of x, as bf16 bits
-__device__ __forceinline__ void split3_value(float x, uint32_t& h, uint32_t& m, uint32_t& l) {
-    h = bf16_bits(x);
-    const float r1 = x - bf16_value(h);
-    m = bf16_bits(r1);
-    l = bf16_bits(r1 - bf16_value(m));
+// Partial maxima of |x| (|x sqrt(w)| with token weights) for columns 4 t .. 4 t + 3 of
+// block x over the tokens of chunk blockIdx.y; columns in [d, dp) get 0.
+template <bool kVec>
+__global__ __launch_bounds__(kThreads) void k_colmax(const float* __restrict__ X, int64_t T, int64_t d,
+                                                     int64_t ldx, int64_t dp, int nchunk,
+                                                     const float* __restrict__ wt, float* __restrict__ part) {
+    const int64_t c4 = (int64_t)blockIdx.x * (4 * kThreads) + 4 * threadIdx.x;
+    if (c4 >= dp) return;
+    const int64_t per = (T + nchunk - 1) / nchunk;
+    const int64_t k0 = std::min<int64_t>(T, (int64_t)blockIdx.y * per), k1 = std::min<int64_t>(T, k0 + per);
+    f32x4 m = {0.0f, 0.0f, 0.0f, 0.0f};
+    const bool vec = kVec && c4 + 4 <= d;
+    constexpr int kU = 4;  // rows in flight per thread
+    for (int64_t kb = k0; kb < k1; kb += kU) {
+        f32x4 v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t k = kb + u;
+            const float* row = X + k * ldx + c4;
+            v[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (k < k1) {
+                if (vec) {
+                    v[u] = *reinterpret_cast<const f32x4*>(row);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (c4 + j < d) v[u][j] = row[j];
+                }
+                if (wt) v[u] *= sqrtf(fmaxf(wt[k], 0.0f));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) m[j] = nan_max(m[j], fabsf(v[u][j]));
+    }
+    float* out = part + (size_t)blockIdx.y * dp + c4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = m[j];
+}
+
+// The same for X stored d x T (one row per column of the product; a batch of S
+// matrices of tin tokens, bs floats apart): wave w of block x takes row 4 x + w.
+__global__ __launch_bounds__(kThreads) void k_colmax_t(const float* __restrict__ X, int64_t T, int64_t d,
+                                                       int64_t ldx, int64_t tin, int64_t bs, int64_t dp,
+                                                       int nchunk, float* __restrict__ part) {
+    const int lane = threadIdx.x & 63;
+    const int64_t c = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (c >= dp) return;
+    const int64_t per = (T + nchunk - 1) / nchunk;
+    const int64_t k0 = std::min<int64_t>(T, (int64_t)blockIdx.y * per), k1 = std::min<int64_t>(T, k0 + per);
+    float m = 0.0f;
+    if (c < d)
+        for (int64_t k = k0 + lane; k < k1; k += 64) m = nan_max(m, fabsf(X[(k / tin) * bs + c * ldx + k % tin]));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = nan_max(m, __shfl_xor(m, o));
+    if (lane == 0) part[(size_t)blockIdx.y * dp + c] = m;
+}
+
+// e_c = 15 - E for a column maximum f 2^E (f in [1/2, 1)), so the scaled column's
+// largest magnitude lies in [2^14, 2^15); 0 for a zero or non-finite maximum.
+__global__ __launch_bounds__(kThreads) void k_colexp(const float* __restrict__ part, int64_t dp, int nchunk,
+                                                     int* __restrict__ exps) {
+    const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (c >= dp) return;
+    float m = 0.0f;
+    for (int q = 0; q < nchunk; ++q) m = nan_max(m, part[(size_t)q * dp + c]);
+    int e = 0;
+    if (m > 0.0f && m < INFINITY) {
+        int E;
+        frexpf(m, &E);
+        e = 15 - E;
+    }
+    exps[c] = e;
+}
+
+// the two pieces of x' = x 2^e, as fp16 bits
+__device__ __forceinline__ void split2_value(float x, int e, uint32_t& h, uint32_t& l) {
+    const float xs = ldexpf(x, e);
+    const _Float16 hv = (_Float16)xs;
+    const _Float16 lv = (_Float16)(xs - (float)hv);
+    h = (uint32_t)__builtin_bit_cast(uint16_t, hv);
+    l = (uint32_t)__builtin_bit_cast(uint16_t, lv);
 }
 
 // Block (x, g): columns 1024 x .. 1024 x + 1023 of tokens 8 g .. 8 g + 7 into the
-// three planes, through LDS. Each row is read as 16-byte vectors where four
+// two planes, through LDS. Each row is read as 16-byte vectors where four
 // columns lie inside [0, d) and X allows it (kVec), element by element
 // otherwise; thread t then splits columns t, t + 256, t + 512, t + 768, so each
 // store instruction writes 1 KB of consecutive 16-byte units of a plane.
@@ -475,15 +571,18 @@ constexpr int kSplitCols = 4 * kThreads;
 // wt (optional): token weights; row k is scaled by sqrt(max(wt[k], 0)) before the
 // split, which turns the SYRK into sum_k wt[k] x_k^T x_k.
 template <bool kVec>
-__global__ __launch_bounds__(kThreads) void k_split3(const float* __restrict__ X, int64_t T,
+__global__ __launch_bounds__(kThreads) void k_split2(const float* __restrict__ X, int64_t T,
                                                      int64_t d, int64_t ldx, int64_t ng,
                                                      int64_t dp, uint4* __restrict__ Xs,
-                                                     const float* __restrict__ wt) {
+                                                     const float* __restrict__ wt, const int* __restrict__ exps) {
     __shared__ float tile[8][kSplitCols];
     const int t = threadIdx.x;
     const int64_t cb = (int64_t)blockIdx.x * kSplitCols;
     const int64_t c4 = cb + 4 * t;  // this thread's four columns on the read side
     const bool vec = kVec && c4 + 4 <= d;
+    int ex[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ex[q] = cb + t + kThreads * q < dp ? exps[cb + t + kThreads * q] : 0;
     for (int64_t g = blockIdx.y; g < ng; g += gridDim.y) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -507,19 +606,18 @@ __global__ __launch_bounds__(kThreads) void k_split3(const float* __restrict__ X
         for (int q = 0; q < 4; ++q) {
             const int cl = t + kThreads * q;
             const int64_t c = cb + cl;
-            uint32_t pk[3][4];
+            uint32_t pk[kNP][4];
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                uint32_t h0, m0, l0, h1, m1, l1;
-                split3_value(tile[e][cl], h0, m0, l0);
-                split3_value(tile[e + 1][cl], h1, m1, l1);
-                pk[0][e >> 1] = (h0 & 0xffffu) | (h1 << 16);
-                pk[1][e >> 1] = (m0 & 0xffffu) | (m1 << 16);
-                pk[2][e >> 1] = (l0 & 0xffffu) | (l1 << 16);
+                uint32_t h0, l0, h1, l1;
+                split2_value(tile[e][cl], ex[q], h0, l0);
+                split2_value(tile[e + 1][cl], ex[q], h1, l1);
+                pk[0][e >> 1] = h0 | (h1 << 16);
+                pk[1][e >> 1] = l0 | (l1 << 16);
             }
             if (c < dp) {
 #pragma unroll
-                for (int p = 0; p < 3; ++p)
+                for (int p = 0; p < kNP; ++p)
                     Xs[((int64_t)p * ng + g) * dp + c] = uint4{pk[p][0], pk[p][1], pk[p][2], pk[p][3]};
             }
         }
@@ -534,11 +632,13 @@ __global__ __launch_bounds__(kThreads) void k_split3(const float* __restrict__ X
 // of tin tokens each, bs floats apart, reads as one with T = S tin: token k of
 // row c is X[(k / tin) bs + c ldx + k % tin].
 template <bool kVec>
-__global__ __launch_bounds__(kThreads) void k_split3_t(const float* __restrict__ X, int64_t T,
+__global__ __launch_bounds__(kThreads) void k_split2_t(const float* __restrict__ X, int64_t T,
                                                        int64_t d, int64_t ldx, int64_t tin, int64_t bs,
-                                                       int64_t ng, int64_t dp, uint4* __restrict__ Xs) {
+                                                       int64_t ng, int64_t dp, uint4* __restrict__ Xs,
+                                                       const int* __restrict__ exps) {
     const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (c >= dp) return;
+    const int ec = exps[c];
     for (int64_t q = blockIdx.y; q < ng / 4; q += gridDim.y) {
         const int64_t k0 = 32 * q;
         const int64_t j0 = k0 % tin;
@@ -560,71 +660,68 @@ __global__ __launch_bounds__(kThreads) void k_split3_t(const float* __restrict__
         }
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
-            uint32_t pk[3][4];
+            uint32_t pk[kNP][4];
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                uint32_t h0, m0, l0, h1, m1, l1;
-                split3_value(v[8 * gi + e], h0, m0, l0);
-                split3_value(v[8 * gi + e + 1], h1, m1, l1);
-                pk[0][e >> 1] = (h0 & 0xffffu) | (h1 << 16);
-                pk[1][e >> 1] = (m0 & 0xffffu) | (m1 << 16);
-                pk[2][e >> 1] = (l0 & 0xffffu) | (l1 << 16);
+                uint32_t h0, l0, h1, l1;
+                split2_value(v[8 * gi + e], ec, h0, l0);
+                split2_value(v[8 * gi + e + 1], ec, h1, l1);
+                pk[0][e >> 1] = h0 | (h1 << 16);
+                pk[1][e >> 1] = l0 | (l1 << 16);
             }
             const int64_t g = 4 * q + gi;
 #pragma unroll
-            for (int p = 0; p < 3; ++p)
+            for (int p = 0; p < kNP; ++p)
                 Xs[((int64_t)p * ng + g) * dp + c] = uint4{pk[p][0], pk[p][1], pk[p][2], pk[p][3]};
         }
     }
 }
 
 // One ring stage of both operands: [piece][16-token block][token half][column].
-struct Split3Stage {
-    bf16x8 v[3][kS3KB][2][kT128];
+struct Split2Stage {
+    f16x8 v[kNP][kS2KB][2][kT128];
 };
-struct Split3Ring {
-    Split3Stage a[kS3NS];
-    Split3Stage b[kS3NS];
+struct Split2Ring {
+    Split2Stage a[kS2NS];
+    Split2Stage b[kS2NS];
 };
 
-// The 24 MFMAs of one 16-token block, per wave quadrant (rows wr.., columns wc..):
-// six piece products for each of the four 32 x 32 blocks, the four blocks
-// interleaved so that no MFMA waits on the one before it.
-__device__ __forceinline__ void split3_block(const bf16x8 (&fa)[3][2], const bf16x8 (&fb)[3][2],
+// The 12 MFMAs of one 16-token block, per wave quadrant: the three piece products
+// of each of the four 32 x 32 blocks, smallest first, the four blocks interleaved
+// so that no MFMA waits on the one before it.
+__device__ __forceinline__ void split2_block(const f16x8 (&fa)[kNP][2], const f16x8 (&fb)[kNP][2],
                                              f32x16 (&acc)[2][2]) {
-    constexpr int kPa[6] = {1, 0, 2, 0, 1, 0};
-    constexpr int kPb[6] = {1, 2, 0, 1, 0, 0};
+    constexpr int kPa[3] = {0, 1, 0};
+    constexpr int kPb[3] = {1, 0, 0};
 #pragma unroll
-    for (int t = 0; t < 6; ++t)
+    for (int t = 0; t < 3; ++t)
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
-                acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kPa[t]][rb], fb[kPb[t]][cb],
-                                                                      acc[rb][cb], 0, 0, 0);
+                acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[kPa[t]][rb], fb[kPb[t]][cb], acc[rb][cb],
+                                                                     0, 0, 0);
 }
 
-// The MFMAs of one stage; the operands of block kb + 1 are read from LDS before
-// the MFMAs of block kb issue.
-template <typename F>
-__device__ __forceinline__ void split3_stage(const Split3Stage& a, const Split3Stage& b, int wr,
-                                             int wc, int lane, f32x16 (&acc)[2][2], F&& after_reads) {
+// The MFMAs of one stage (rows wr.., columns wc.. of the tile); the operands of
+// block kb + 1 are read from LDS before the MFMAs of block kb issue.
+__device__ __forceinline__ void split2_stage(const Split2Stage& a, const Split2Stage& b, int wr, int wc,
+                                             int lane, f32x16 (&acc)[2][2]) {
     const int kh = lane >> 5, l31 = lane & 31;
-    bf16x8 fa[2][3][2], fb[2][3][2];
+    f16x8 fa[2][kNP][2], fb[2][kNP][2];
 #pragma unroll
-    for (int p = 0; p < 3; ++p)
+    for (int p = 0; p < kNP; ++p)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             fa[0][p][h] = a.v[p][0][kh][wr + 32 * h + l31];
             fb[0][p][h] = b.v[p][0][kh][wc + 32 * h + l31];
         }
-    after_reads();  // the next stage's loads go out behind this stage's first reads
 #pragma unroll
-    for (int kb = 0; kb < kS3KB; ++kb) {
+    for (int kb = 0; kb < kS2KB; ++kb) {
         const int cur = kb & 1;
-        if (kb + 1 < kS3KB) {
+        if (kb + 1 < kS2KB) {
 #pragma unroll
-            for (int p = 0; p < 3; ++p)
+            for (int p = 0; p < kNP; ++p)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     fa[cur ^ 1][p][h] = a.v[p][kb + 1][kh][wr + 32 * h + l31];
@@ -632,54 +729,54 @@ __device__ __forceinline__ void split3_stage(const Split3Stage& a, const Split3S
                 }
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of this block's MFMAs
-        split3_block(fa[cur], fb[cur], acc);
+        split2_block(fa[cur], fb[cur], acc);
     }
 }
 
 // Stages [s_beg, s_end) of tile columns (ca.., cb..): stage s goes to ring slot
-// s mod kS3NS; at the top of stage s the loads of stage s + kS3NS - 1 go out into
+// s mod kS2NS; at the top of stage s the loads of stage s + kS2NS - 1 go out into
 // the slot every wave finished reading in stage s - 1 (as in syrk_tile_ring).
-__device__ __forceinline__ void split3_tile(const uint4* __restrict__ Xs, int64_t ng, int64_t dp,
+__device__ __forceinline__ void split2_tile(const uint4* __restrict__ Xs, int64_t ng, int64_t dp,
                                             int64_t ca, int64_t cb, int64_t s_beg, int64_t s_end,
-                                            f32x16 (&acc)[2][2], Split3Ring& sm) {
+                                            f32x16 (&acc)[2][2], Split2Ring& sm) {
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = (w >> 1) * 64, wc = (w & 1) * 64;
-    constexpr int kRows = 3 * kS3KB * 2 * 2;  // 1 KB rows per operand per stage
+    constexpr int kRows = kNP * kS2KB * 2 * 2;  // 1 KB rows per operand per stage
     constexpr int kPerWave = kRows / 4;
-    constexpr int kLoads = 2 * kPerWave;      // direct loads per wave per stage
+    constexpr int kLoads = 2 * kPerWave;        // direct loads per wave per stage
     const int64_t ns = s_end - s_beg;
     auto issue = [&](int64_t s) {
-        const int slot = (int)(s % kS3NS);
-        const int64_t kb0 = (s_beg + s) * kS3KB;
+        const int slot = (int)(s % kS2NS);
+        const int64_t kb0 = (s_beg + s) * kS2KB;
 #pragma unroll
         for (int i = 0; i < kPerWave; ++i) {
             const int q = w + 4 * i;
-            const int half = q & 1, th = (q >> 1) & 1, kbl = (q >> 2) % kS3KB, p = (q >> 2) / kS3KB;
+            const int half = q & 1, th = (q >> 1) & 1, kbl = (q >> 2) % kS2KB, p = (q >> 2) / kS2KB;
             const int64_t g = 2 * (kb0 + kbl) + th;
             const uint4* row = Xs + ((int64_t)p * ng + g) * dp + 64 * half + lane;
             __builtin_amdgcn_global_load_lds(row + ca, &sm.a[slot].v[p][kbl][th][64 * half], 16, 0, 0);
             __builtin_amdgcn_global_load_lds(row + cb, &sm.b[slot].v[p][kbl][th][64 * half], 16, 0, 0);
         }
     };
-    for (int s = 0; s < kS3NS - 1; ++s)
+    for (int s = 0; s < kS2NS - 1; ++s)
         if (s < ns) issue(s);
     for (int64_t it = 0; it < ns; ++it) {
-        if (it + kS3NS - 2 < ns) vm_wait_barrier<(kS3NS - 2) * kLoads>();
+        if (it + kS2NS - 2 < ns) vm_wait_barrier<(kS2NS - 2) * kLoads>();
         else vm_wait_barrier<0>();
-        const int slot = (int)(it % kS3NS);
-        split3_stage(sm.a[slot], sm.b[slot], wr, wc, lane, acc, [&] {
-            if (it + kS3NS - 1 < ns) issue(it + kS3NS - 1);
-        });
+        const int slot = (int)(it % kS2NS);
+        if (it + kS2NS - 1 < ns) issue(it + kS2NS - 1);
+        split2_stage(sm.a[slot], sm.b[slot], wr, wc, lane, acc);
     }
 }
 
 // Whole tiles [tile_beg, tile_beg + gridDim.x) over all stages.
-__global__ __launch_bounds__(kThreads) void k_syrk3_full(const uint4* __restrict__ Xs, int64_t ng,
+__global__ __launch_bounds__(kThreads) void k_syrk2_full(const uint4* __restrict__ Xs, int64_t ng,
                                                          int64_t dp, int64_t nstage, int64_t d,
                                                          float alpha, float beta, float* __restrict__ H,
-                                                         int64_t ldh, int64_t nb, int64_t tile_beg) {
-    __shared__ Split3Ring sm;
+                                                         int64_t ldh, int64_t nb, int64_t tile_beg,
+                                                         const int* __restrict__ exps) {
+    __shared__ Split2Ring sm;
     int64_t bi, bj;
     upper_tile(tile_beg + xcd_rank(blockIdx.x, gridDim.x), nb, bi, bj);
     f32x16 acc[2][2];
@@ -689,17 +786,17 @@ __global__ __launch_bounds__(kThreads) void k_syrk3_full(const uint4* __restrict
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
-    split3_tile(Xs, ng, dp, bi * kT128, bj * kT128, 0, nstage, acc, sm);
-    syrk_write(H, ldh, d, bi, bj, alpha, beta, acc);
+    split2_tile(Xs, ng, dp, bi * kT128, bj * kT128, 0, nstage, acc, sm);
+    syrk_write(H, ldh, d, bi, bj, alpha, beta, acc, exps);
 }
 
 // Tiles [tile_beg, tile_beg + ntiles), each split into nsplit stage ranges; block
 // (tile u, split s) writes its raw 128x128 partial to part[(u * nsplit + s)].
-__global__ __launch_bounds__(kThreads) void k_syrk3_split(const uint4* __restrict__ Xs, int64_t ng,
+__global__ __launch_bounds__(kThreads) void k_syrk2_split(const uint4* __restrict__ Xs, int64_t ng,
                                                           int64_t dp, int64_t nstage, int64_t nb,
                                                           int64_t tile_beg, int nsplit,
                                                           float* __restrict__ part) {
-    __shared__ Split3Ring sm;
+    __shared__ Split2Ring sm;
     const int u = blockIdx.x / nsplit, sp = blockIdx.x % nsplit;
     int64_t bi, bj;
     upper_tile(tile_beg + u, nb, bi, bj);
@@ -713,7 +810,7 @@ __global__ __launch_bounds__(kThreads) void k_syrk3_split(const uint4* __restric
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
-    split3_tile(Xs, ng, dp, bi * kT128, bj * kT128, sb, se, acc, sm);
+    split2_tile(Xs, ng, dp, bi * kT128, bj * kT128, sb, se, acc, sm);
     float* out = part + (size_t)blockIdx.x * kT128 * kT128;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
@@ -770,8 +867,8 @@ SyrkPlan plan_tiles(int64_t tiles, int64_t P, int64_t kunits, size_t room) {
 
 size_t hessian_workspace_bytes(int64_t T, int64_t d) {
     const size_t part = sizeof(float) * kT128 * kT128 *
-                        (size_t)std::max(resident_slots(sizeof(SyrkShared)), resident_slots(sizeof(Split3Ring)));
-    return split3_shape(T, d).bytes + part;
+                        (size_t)std::max(resident_slots(sizeof(SyrkShared)), resident_slots(sizeof(Split2Ring)));
+    return split2_shape(T, d).bytes + part;
 }
 
 int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, float alpha,
@@ -780,44 +877,62 @@ int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, floa
     const int64_t nb = (d + kT128 - 1) / kT128;
     const int64_t tiles = nb * (nb + 1) / 2;
     if (tiles > 0x7fffffff) return BAKRON_E_INVALID_ARG;
-    const Split3Shape sh = split3_shape(T, d);
+    const Split2Shape sh = split2_shape(T, d);
     if (ws != nullptr && ws_bytes >= sh.bytes) {
-        // the three-piece bf16 path
+        // the two-piece fp16 path: column exponents, then the pieces
         uint4* Xs = (uint4*)ws;
+        int* exps = (int*)((char*)ws + sh.exps_off);
+        float* cmax = (float*)((char*)ws + sh.cmax_off);
+        if (tin <= 0) tin = T;  // one matrix
+        if (trans) {
+            const dim3 grid((unsigned)((sh.dp + kThreads / 64 - 1) / (kThreads / 64)), (unsigned)sh.nchunk);
+            hipLaunchKernelGGL(k_colmax_t, grid, dim3(kThreads), 0, stream, X, T, d, ldx, tin, bs, sh.dp, sh.nchunk,
+                               cmax);
+        } else {
+            const dim3 grid((unsigned)((sh.dp + 4 * kThreads - 1) / (4 * kThreads)), (unsigned)sh.nchunk);
+            const bool vec = (ldx & 3) == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0;
+            if (vec)
+                hipLaunchKernelGGL(k_colmax<true>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, sh.dp, sh.nchunk,
+                                   wt, cmax);
+            else
+                hipLaunchKernelGGL(k_colmax<false>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, sh.dp, sh.nchunk,
+                                   wt, cmax);
+        }
+        hipLaunchKernelGGL(k_colexp, dim3((unsigned)((sh.dp + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
+                           (const float*)cmax, sh.dp, sh.nchunk, exps);
         if (sh.ng > 0 && trans) {
             const unsigned gy = (unsigned)std::min<int64_t>(sh.ng / 4, 65535);
             const dim3 grid((unsigned)((sh.dp + kThreads - 1) / kThreads), gy);
-            if (tin <= 0) tin = T;  // one matrix
             const bool vec = (ldx & 3) == 0 && (tin & 3) == 0 && (bs & 3) == 0 &&
                              (reinterpret_cast<uintptr_t>(X) & 15) == 0;
             if (vec)
-                hipLaunchKernelGGL(k_split3_t<true>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, tin, bs, sh.ng,
-                                   sh.dp, Xs);
+                hipLaunchKernelGGL(k_split2_t<true>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, tin, bs, sh.ng,
+                                   sh.dp, Xs, (const int*)exps);
             else
-                hipLaunchKernelGGL(k_split3_t<false>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, tin, bs, sh.ng,
-                                   sh.dp, Xs);
+                hipLaunchKernelGGL(k_split2_t<false>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, tin, bs, sh.ng,
+                                   sh.dp, Xs, (const int*)exps);
         } else if (sh.ng > 0) {
             const unsigned gy = (unsigned)std::min<int64_t>(sh.ng, 65535);
             const dim3 grid((unsigned)((sh.dp + kSplitCols - 1) / kSplitCols), gy);
             const bool vec = (ldx & 3) == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0;
             if (vec)
-                hipLaunchKernelGGL(k_split3<true>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, sh.ng, sh.dp, Xs,
-                                   wt);
+                hipLaunchKernelGGL(k_split2<true>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, sh.ng, sh.dp, Xs,
+                                   wt, (const int*)exps);
             else
-                hipLaunchKernelGGL(k_split3<false>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, sh.ng, sh.dp, Xs,
-                                   wt);
+                hipLaunchKernelGGL(k_split2<false>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, sh.ng, sh.dp, Xs,
+                                   wt, (const int*)exps);
         }
-        const SyrkPlan pl = plan_tiles(tiles, resident_slots(sizeof(Split3Ring)), sh.nstage,
+        const SyrkPlan pl = plan_tiles(tiles, resident_slots(sizeof(Split2Ring)), sh.nstage,
                                        ws_bytes - sh.bytes);
         if (pl.full > 0)
-            hipLaunchKernelGGL(k_syrk3_full, dim3((unsigned)pl.full), dim3(kThreads), 0, stream, Xs,
-                               sh.ng, sh.dp, sh.nstage, d, alpha, beta, H, ldh, nb, (int64_t)0);
+            hipLaunchKernelGGL(k_syrk2_full, dim3((unsigned)pl.full), dim3(kThreads), 0, stream, Xs,
+                               sh.ng, sh.dp, sh.nstage, d, alpha, beta, H, ldh, nb, (int64_t)0, (const int*)exps);
         if (pl.rem > 0) {
             float* part = (float*)((char*)ws + sh.bytes);
-            hipLaunchKernelGGL(k_syrk3_split, dim3((unsigned)(pl.rem * pl.nsplit)), dim3(kThreads), 0,
+            hipLaunchKernelGGL(k_syrk2_split, dim3((unsigned)(pl.rem * pl.nsplit)), dim3(kThreads), 0,
                                stream, Xs, sh.ng, sh.dp, sh.nstage, nb, pl.full, pl.nsplit, part);
             hipLaunchKernelGGL(k_syrk_reduce, dim3((unsigned)pl.rem, kT128 / 8), dim3(kThreads), 0, stream,
-                               d, alpha, beta, H, ldh, nb, pl.full, pl.nsplit, (const float*)part);
+                               d, alpha, beta, H, ldh, nb, pl.full, pl.nsplit, (const float*)part, (const int*)exps);
         }
         return hipGetLastError() == hipSuccess ? BAKRON_OK : BAKRON_E_DEVICE;
     }
@@ -835,7 +950,7 @@ int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, floa
         hipLaunchKernelGGL(k_syrk_split, dim3((unsigned)(pl.rem * pl.nsplit)), dim3(kThreads), 0, stream,
                            X, T, d, ldx, nb, pl.full, pl.nsplit, part);
         hipLaunchKernelGGL(k_syrk_reduce, dim3((unsigned)pl.rem, kT128 / 8), dim3(kThreads), 0, stream, d, alpha,
-                           beta, H, ldh, nb, pl.full, pl.nsplit, (const float*)part);
+                           beta, H, ldh, nb, pl.full, pl.nsplit, (const float*)part, (const int*)nullptr);
     }
     return hipGetLastError() == hipSuccess ? BAKRON_OK : BAKRON_E_DEVICE;
 }

@@ -121,7 +121,8 @@ def check_solve(bk, w, LO, LI, DO, DI, bits, rounding="nearest", seed=0, row_sca
 # ----------------------------------------------------------------------------
 # Hessian factor accumulation
 # ----------------------------------------------------------------------------
-# pieces=True: three bf16 pieces per element on the bf16 matrix cores (the default);
+# pieces=True: two fp16 pieces per element of power-of-two-scaled columns on the fp16
+# matrix cores (the default);
 # pieces=False: the fp32 matrix-core path. Both are held to the same fp32 bound.
 @pytest.mark.parametrize("pieces", [True, False])
 @pytest.mark.parametrize("T,d", [(1024, 64), (333, 100), (8192, 512), (1, 5), (2000, 129), (0, 7),
@@ -185,7 +186,8 @@ def test_hessian_accum_strided_whole_tiles(bk, off, pieces):
 @pytest.mark.parametrize("pieces", [True, False])
 def test_hessian_accum_nonfinite_inputs_stay_in_their_rows(bk, pieces):
     # An Inf and a NaN in X make every entry of their columns' rows and columns of H
-    # non-finite (NaN or Inf: the three-piece split of an Inf is Inf, NaN, NaN); every
+    # non-finite (NaN or Inf: the piece split of an Inf is Inf, NaN, and its column keeps
+    # the exponent 0); every
     # other entry keeps the usual fp32 bound.
     note("hessian non-finite inputs pieces=%s" % pieces)
     T, d = 700, 150
