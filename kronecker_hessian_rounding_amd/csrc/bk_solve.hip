@@ -45,7 +45,6 @@ constexpr int kNch = 4;          // maximum K-chunks per far-field product
 constexpr int kRing = 4;         // diagonals whose far-field partials are held at once
 constexpr int kTargetWg = 1024;  // far-field tasks aimed for per diagonal
 constexpr int kFarKT = 64;       // k-slice depth of the far-field GEMMs
-constexpr int kSweep = 2 * kB - 1;  // steps of one leaf's wavefront
 constexpr int kStrip = 16;       // columns (rows) per hand-over
 constexpr int kStrips = kB / kStrip;
 
@@ -398,22 +397,30 @@ __device__ __forceinline__ void far_task(const SolveParams& p, int d, int task, 
 // Entry (i, j) is finalised at step i + j. Its in-leaf sums
 //   pn = sum_{k<i} L_O[k][i] D[k][j],   rn = sum_{l<j} g[i][l] L_I[l][j]
 // (g = C, the column feedback plus error of the row) are split into a bulk,
-// which only uses entries finalised three or more steps earlier, and the two
-// newest terms of each (k = i-1, i-2 and l = j-1, j-2). Four bulk waves compute
-// the bulk of step st + 2 while the finaliser wave finalises step st, so the dependent chain
-// of a step holds no LDS read: the finaliser takes D[i-1][j] and D[i-2][j]
-// from the lanes above by DPP, g[i][j-1] and g[i][j-2] from its own previous
-// steps, and the bulk sums and static inputs were read one step ahead.
+// which only uses entries finalised four or more steps earlier, and the three
+// newest terms of each (k = i-1, i-2, i-3 and l = j-1, j-2, j-3). Three bulk
+// waves compute the bulk of step st + 2 while the finaliser wave finalises step
+// st. Every entry the bulk of step st + 2 reads was final by step st - 2, so
+// its reads go out in the step before and stay in flight across the barrier:
+// no step of a bulk wave starts with an LDS read. The dependent chain of the
+// finaliser holds no LDS read either: it takes D[i-1][j], D[i-2][j] and
+// D[i-3][j] from the lanes above by DPP, g[i][j-1], g[i][j-2] and g[i][j-3]
+// from its own previous steps, and the bulk sums and static inputs were read
+// one step ahead.
 //
-// Bulk lanes are (a, quarter q) with lane = 4 a + q; quarter q owns the k / l
-// range [16q, 16q + 16). Lane a sums P along row a of L_O^T and R along column
-// a of L_I, both held in registers, against 16-float chunks of D and g read as
-// four adjacent 16-byte words (68-float rows spread a row group over the
-// banks); the factors are zero beyond the bulk's range, so no term needs a
-// per-step mask.
+// Bulk work comes in units (a, quarter q): quarter q owns the k / l range
+// [16q, 16q + 16), and unit (a, q) exists only where that range meets the
+// bulk's range k, l <= a - 4 (144 units: one quarter for a = 4..19, up to four
+// for a >= 52). The units are packed onto the lanes of three waves, one per
+// SIMD, in order of a, so a lane with only zero factors does no work on a
+// wave that has any. Unit (a, q) sums P along row a of L_O^T and R along
+// column a of L_I, both held in registers, against 16-float chunks of D and g
+// read as four adjacent 16-byte words (68-float rows spread a row group over
+// the banks), and stores its two partials; the finaliser adds the four
+// quarters of its entry.
 //
-// Waves 5 and 6 do the hand-overs, column-wise (5: D to the leaf below, and
-// L_O[above, this]^T D[above, strip] into p) and row-wise (6: C to the leaf on
+// Waves 4 and 5 do the hand-overs, column-wise (4: D to the leaf below, and
+// L_O[above, this]^T D[above, strip] into p) and row-wise (5: C to the leaf on
 // the right, and C[strip, left] L_I[left, this] into o). Strip c (columns or
 // rows 16c..16c+15) of this leaf is final after step 78 + 16c; it is stored a
 // step later (storing each column as it became final, 64 scattered rows a
@@ -426,16 +433,25 @@ __device__ __forceinline__ void far_task(const SolveParams& p, int d, int task, 
 // to p (o) before the finaliser reads columns (rows) 16c.., at the end of step
 // 16c - 1. Strip 0 is taken before the sweep.
 // ---------------------------------------------------------------------------
-constexpr int kLeafWaves = 7;
+constexpr int kLeafWaves = 6;
 constexpr int kLeafThreads = kLeafWaves * 64;
 // Roles in the sweep by wave index. Waves are spread over the four SIMDs by
 // index (SIMD w mod 4): the finaliser, whose chain sets the pace, has SIMD 3 to
 // itself (sharing it with a bulk wave cost a fifth of the sweep's speed); bulk
-// waves 0, 1, 2 and 4 and hand-over waves 5 and 6 fill SIMDs 0-2. Putting both
-// hand-over waves on one SIMD measured slower.
+// waves 0, 1 and 2 have one SIMD each, and hand-over waves 4 and 5 share SIMDs
+// 0 and 1 with them (putting both hand-over waves on one SIMD measured slower).
 constexpr int kFinWave = 3;
-constexpr int kColWave = 5;  // hand-over of columns of D (to the leaf below)
-constexpr int kRowWave = 6;  // hand-over of rows of C (to the leaf on the right)
+constexpr int kColWave = 4;  // hand-over of columns of D (to the leaf below)
+constexpr int kRowWave = 5;  // hand-over of rows of C (to the leaf on the right)
+constexpr int kNew = 5;          // newest terms of each in-leaf sum that the finaliser adds
+constexpr int kBulkUnits = 136;  // (a, q) with 16 q <= a - 1 - kNew
+constexpr int bulk_units() {
+    int n = 0;
+    for (int a = kNew + 1; a < kB; ++a) n += (a - 1 - kNew) / 16 + 1;
+    return n;
+}
+static_assert(bulk_units() == kBulkUnits && kBulkUnits <= 3 * 64, "the bulk units fill three waves");
+constexpr int kSuper = kB;       // super-steps of the sweep: two steps (anti-diagonals) each
 constexpr int kTs = 68;  // row stride of the 64x64 tiles: 16-byte aligned rows, 4 banks apart
 constexpr int kPs = 66;  // row stride of the per-entry inputs: anti-diagonal walks hit distinct banks
 
@@ -445,10 +461,9 @@ struct LeafSmem {
     float bt[kB][kTs];     // W* + o, transposed: bt[j][i] for entry (i, j)
     float pt[kB][kTs];     // p, transposed: pt[j][i]
     float wst[kB][kPs];    // W*, overwritten by eta = t - q once the entry is final
-    float pnb[3][kB];      // bulk sums, by step modulo 3 (written two steps ahead)
-    float rnb[3][kB];
-    float li1[kB];         // L_I[j-1][j], L_I[j-2][j]: the finaliser's terms
-    float li2[kB];
+    float pnb[4][kB][4];   // bulk partials by diagonal modulo 4, entry and quarter
+    float rnb[4][kB][4];
+    float li[kNew][kB];    // li[e][j] = L_I[j-1-e][j]: the finaliser's terms
     uint8_t code[kB][kB + 4];
     float DI[kB];
     double red[kLeafWaves];
@@ -483,6 +498,11 @@ __device__ __forceinline__ float lane_above(float x) {
 }
 
 __device__ __forceinline__ f32x4 lds4(const float* q) { return *reinterpret_cast<const f32x4*>(q); }
+
+// wave_shr:1 with bound_ctrl: lane i receives lane i-1's value, lane 0 receives 0
+__device__ __forceinline__ float lane_above0(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x138, 0xF, 0xF, true));
+}
 
 // ---- hand-overs (waves 5 and 6). Operand kk of lane l is row 4 kk + l / 16,
 // column l % 16 of the neighbour's strip: D[i0-64+k][j0+16c+x] (column-wise) or
@@ -595,14 +615,12 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
     const bool far_p = p.LO && I > 2, far_o = p.LI && J > 2;  // far-field partials (blocks <= I-3, J-3)
     const bool two_p = p.LO && I > 1, two_o = p.LI && J > 1;  // the blocks two back
     const bool adj_p = p.LO && I > 0, adj_o = p.LI && J > 0;  // the adjacent blocks (handed over)
-    if (t < 2) {  // no L_I[j-d][j] for j < d
-        sm.li2[t] = 0.0f;
-        if (t < 1) sm.li1[t] = 0.0f;
-    }
+    for (int e = t; e < kNew * kB; e += kLeafThreads) sm.li[e / kB][e % kB] = 0.0f;  // no L_I[j-1-e][j] for j <= e
+    __syncthreads();
     constexpr int kPer = (kB * kB + kLeafThreads - 1) / kLeafThreads;
     // ---- A: static inputs, every load of the thread in flight at once
     //   DT  <- L_O[i0-128+k][i0+c]  pt <- L_I[j0-128+k][j0+c]    (blocks two back: staging)
-    //   wst <- W*[i0+k][j0+c]       li1, li2 <- the first two superdiagonals of L_I
+    //   wst <- W*[i0+k][j0+c]       li <- the first kNew superdiagonals of L_I
     {
         float v1[kPer], v3[kPer], v5[kPer], v6[kPer];
 #pragma unroll
@@ -613,7 +631,7 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
             v1[u] = (in && two_p && c < R) ? p.LO[(i0 - 2 * kB + k) * p.ldlo + i0 + c] : 0.0f;
             v3[u] = (in && two_o && c < Cc) ? p.LI[(j0 - 2 * kB + k) * p.ldli + j0 + c] : 0.0f;
             v5[u] = (in && k < R && c < Cc) ? p.W[(i0 + k) * p.ldw + j0 + c] : 0.0f;
-            v6[u] = (in && p.LI && (c - k == 1 || c - k == 2) && c < Cc) ? p.LI[(j0 + k) * p.ldli + j0 + c] : 0.0f;
+            v6[u] = (in && p.LI && c - k >= 1 && c - k <= kNew && c < Cc) ? p.LI[(j0 + k) * p.ldli + j0 + c] : 0.0f;
         }
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
@@ -623,8 +641,7 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
                 sm.DT[k][c] = v1[u];
                 sm.pt[k][c] = v3[u];
                 sm.wst[k][c] = v5[u];
-                if (c - k == 1) sm.li1[c] = v6[u];
-                if (c - k == 2) sm.li2[c] = v6[u];
+                if (c - k >= 1 && c - k <= kNew) sm.li[c - k - 1][c] = v6[u];
             }
         }
     }
@@ -758,10 +775,11 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
         const int j = e / kB, i = e % kB;
         sm.bt[j][i] += sm.wst[i][j];
     }
-    if (t < kB) {
-        sm.DI[t] = (p.want_loss && t < Cc) ? p.DI[j0 + t] : 0.0f;
-        sm.pnb[0][t] = sm.pnb[1][t] = sm.pnb[2][t] = 0.0f;
-        sm.rnb[0][t] = sm.rnb[1][t] = sm.rnb[2][t] = 0.0f;
+    if (t < kB) sm.DI[t] = (p.want_loss && t < Cc) ? p.DI[j0 + t] : 0.0f;
+    // the partials of units that do not exist stay zero
+    for (int e = t; e < 4 * kB * 4; e += kLeafThreads) {
+        (&sm.pnb[0][0][0])[e] = 0.0f;
+        (&sm.rnb[0][0][0])[e] = 0.0f;
     }
     __syncthreads();
     // ---- D: the neighbours' first strips are taken before the sweep
@@ -784,206 +802,254 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
     const bool bulk = w != kFinWave && w != kColWave && w != kRowWave;
     if (bulk) {
         // ---------------- bulk waves ----------------
-        // Lane (a, quarter q) sums the k / l range [16q, 16q + 16) of two bulk sums of
-        // the entries finalised two steps later (x = st + 2 - a):
-        //   P of entry (a, x): sum_k L_O[k][a] D[k][x],  k <= a - 3 (row a)
-        //   R of entry (x, a): sum_l g[x][l] L_I[l][a],  l <= a - 3 (column a)
+        // Unit (a, quarter q) sums the k / l range [16q, 16q + 16) of two bulk sums of
+        // the entries of diagonal d (x = d - a):
+        //   P of entry (a, x): sum_k L_O[k][a] D[k][x],  k <= a - 1 - kNew (row a)
+        //   R of entry (x, a): sum_l g[x][l] L_I[l][a],  l <= a - 1 - kNew (column a)
         // so both triangular factors stay in registers (row a of L_O^T, column a of
-        // L_I) and a step reads two 16-float chunks per lane: column x of D and row x
-        // of g. The newest terms (k, l = a - 3, final in the previous step) are read
-        // on their own at the start of the step; the chunks (entries final a step
-        // earlier) were read at the end of the previous step, so their LDS latency
-        // overlaps the barrier and the finaliser's work.
-        const int bt = (w == 4 ? kFinWave : w) * 64 + lane;  // bulk thread 0..255 (waves 0, 1, 2, 4)
-        const int a = bt >> 2;
-        const int q = bt & 3;
+        // L_I) and a diagonal takes two 16-float chunks per lane: column x of D and
+        // row x of g. Super-step S forms diagonals 2S + 2 and 2S + 3. Every entry they
+        // read with a nonzero factor was final by step 2S - 3, i.e. before the barrier
+        // that opened super-step S - 1, so the chunks are read at the end of
+        // super-step S - 1 and stay in flight across its barrier; an entry written
+        // while they are read meets a zero factor.
+        // Units are packed in order of a: bulk thread bt < kBulkUnits takes unit
+        // (a, q) with bt = sum_{a' < a} n(a') + q, n(a) = (a - 1 - kNew) / 16 + 1.
+        const int bt = w * 64 + lane;  // bulk thread 0..191 (waves 0, 1, 2)
+        int a = 0, q = 0;
+        bool unit = false;
+        {
+            int first = 0;
+#pragma unroll 1
+            for (int aa = kNew + 1; aa < kB; ++aa) {
+                const int nq = ((aa - 1 - kNew) >> 4) + 1;
+                if (bt >= first && bt < first + nq) {
+                    a = aa;
+                    q = bt - first;
+                    unit = true;
+                }
+                first += nq;
+            }
+        }
         const int k0 = 16 * q;
-        float lo[16];  // L_O[i0 + k][i0 + a] for k <= a - 4, else 0
-        float li[16];  // L_I[j0 + l][j0 + a] for l <= a - 4, else 0
+        float lo[16];  // L_O[i0 + k][i0 + a] for k <= a - 1 - kNew, else 0
+        float li[16];  // L_I[j0 + l][j0 + a] for l <= a - 1 - kNew, else 0
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            lo[e] = (p.LO && k0 + e <= a - 4 && a < R) ? p.LO[(i0 + k0 + e) * p.ldlo + i0 + a] : 0.0f;
-            li[e] = (p.LI && k0 + e <= a - 4 && a < Cc) ? p.LI[(j0 + k0 + e) * p.ldli + j0 + a] : 0.0f;
+            const bool nz = unit && k0 + e <= a - 1 - kNew;
+            lo[e] = (nz && p.LO && a < R) ? p.LO[(i0 + k0 + e) * p.ldlo + i0 + a] : 0.0f;
+            li[e] = (nz && p.LI && a < Cc) ? p.LI[(j0 + k0 + e) * p.ldli + j0 + a] : 0.0f;
         }
-        // L_O[a-3][a] and L_I[a-3][a], added by quarter 0 with the newest D and g
-        const float lo3 = (p.LO && q == 0 && a >= 3 && a < R) ? p.LO[(i0 + a - 3) * p.ldlo + i0 + a] : 0.0f;
-        const float li3 = (p.LI && q == 0 && a >= 3 && a < Cc) ? p.LI[(j0 + a - 3) * p.ldli + j0 + a] : 0.0f;
-        // An entry written in the step the chunk is read meets a zero factor: L_O and
-        // L_I are zero beyond a - 4.
-        auto fetch = [&](int st, f32x4 (&c)[8]) {
-            const int xc = min(max(st + 2 - a, 0), kB - 1);
-            const float* dp = &sm.DT[xc][k0];
-            const float* gp = &sm.Gs[xc][k0];
+        // lanes with no live unit on a diagonal read nothing (their results are not stored)
+        auto fetch = [&](int S, f32x4 (&c)[2][8]) {
 #pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                c[h] = lds4(dp + 4 * h);
-                c[4 + h] = lds4(gp + 4 * h);
+            for (int e = 0; e < 2; ++e) {
+                const int x = 2 * S + 2 + e - a;
+                if (unit && x >= 0 && x < kB) {
+                    const float* dp = &sm.DT[x][k0];
+                    const float* gp = &sm.Gs[x][k0];
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        c[e][h] = lds4(dp + 4 * h);
+                        c[e][4 + h] = lds4(gp + 4 * h);
+                    }
+                }
             }
         };
-        int slot3 = 2;  // (st + 2) mod 3
-        auto step = [&](int st, const f32x4 (&cur)[8], f32x4 (&nxt)[8]) {
-            const int x = st + 2 - a;
-            const bool live = x >= 0 && x < kB;
-            const int xc = min(max(x, 0), kB - 1);
-            // the newest terms, read behind the chunks fetched in the previous step
-            const int a3 = max(a - 3, 0);
-            const float dnew = sm.DT[xc][a3];  // D[a-3][x]
-            const float gnew = sm.Gs[xc][a3];  // g[x][a-3]
-            float p0 = lo3 * dnew, p1 = 0.0f, r0 = li3 * gnew, r1 = 0.0f;
+        auto super = [&](int S, const f32x4 (&c)[2][8], f32x4 (&cn)[2][8]) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                p0 = fmaf(lo[e], cur[0][e], p0);
-                p1 = fmaf(lo[4 + e], cur[1][e], p1);
-                r0 = fmaf(li[e], cur[4][e], r0);
-                r1 = fmaf(li[4 + e], cur[5][e], r1);
-            }
+            for (int e = 0; e < 2; ++e) {
+                const int dg = 2 * S + 2 + e;
+                const int x = dg - a;
+                float p0 = 0.0f, p1 = 0.0f, r0 = 0.0f, r1 = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                p0 = fmaf(lo[8 + e], cur[2][e], p0);
-                p1 = fmaf(lo[12 + e], cur[3][e], p1);
-                r0 = fmaf(li[8 + e], cur[6][e], r0);
-                r1 = fmaf(li[12 + e], cur[7][e], r1);
+                for (int v = 0; v < 4; ++v) {
+                    p0 = fmaf(lo[v], c[e][0][v], p0);
+                    p1 = fmaf(lo[4 + v], c[e][1][v], p1);
+                    r0 = fmaf(li[v], c[e][4][v], r0);
+                    r1 = fmaf(li[4 + v], c[e][5][v], r1);
+                }
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    p0 = fmaf(lo[8 + v], c[e][2][v], p0);
+                    p1 = fmaf(lo[12 + v], c[e][3][v], p1);
+                    r0 = fmaf(li[8 + v], c[e][6][v], r0);
+                    r1 = fmaf(li[12 + v], c[e][7][v], r1);
+                }
+                if (unit && x >= 0 && x < kB) {
+                    sm.pnb[dg & 3][a][q] = p0 + p1;  // entry (a, x)
+                    sm.rnb[dg & 3][x][q] = r0 + r1;  // entry (x, a)
+                }
             }
-            float pn = live ? p0 + p1 : 0.0f;
-            float rn = live ? r0 + r1 : 0.0f;
-            pn = quad_sum(pn);
-            rn = quad_sum(rn);
-            if (q == 0 && live) {
-                sm.pnb[slot3][a] = pn;  // entry (a, x)
-                sm.rnb[slot3][x] = rn;  // entry (x, a)
-            }
-            slot3 = slot3 == 2 ? 0 : slot3 + 1;
-            // the next step's chunks go out after the stores and stay in flight across
-            // the barrier: every entry they read with a nonzero factor was final a step
-            // earlier, so later writes into the chunks meet a zero factor
             lds_wait_all();
             __builtin_amdgcn_sched_barrier(0);
-            fetch(st + 1, nxt);
+            fetch(S + 1, cn);  // the next super-step's chunks, in flight across the barrier
             __builtin_amdgcn_sched_barrier(0);
             barrier_no_wait();
         };
-        f32x4 ca[8], cb[8];
+        f32x4 ca[2][8], cb[2][8];
         __syncthreads();
-        fetch(0, ca);
-        int st = 0;
-        for (; st + 1 < 2 * kB - 1; st += 2) {
-            step(st, ca, cb);
-            step(st + 1, cb, ca);
+        fetch(0, ca);  // diagonals 2 and 3: nothing final is needed yet (a nonzero factor needs a >= 6)
+#pragma nounroll
+        for (int S = 0; S < kSuper; S += 2) {
+            super(S, ca, cb);
+            super(S + 1, cb, ca);
         }
-        step(st, ca, cb);  // 127 steps: the last one
     } else if (w == kFinWave) {
         // ---------------- finaliser wave: lane i owns row i ----------------
-        // adds the two newest terms of each sum: D[i-1][j], D[i-2][j] (from the
-        // lanes above, by DPP) and g[i][j-1], g[i][j-2] (its own previous results);
-        // eta = t - q goes into W*'s slot (consumed one step earlier) for the loss
+        // Super-step S finalises steps 2S and 2S + 1 with no barrier between them.
+        // Each entry adds the bulk's four quarters and the kNew newest terms of each
+        // sum: D[i-1][j] .. D[i-kNew][j] (from the lanes above, by DPP: the lane
+        // above's value of the previous step, passed down one lane per step) and
+        // g[i][j-1] .. g[i][j-kNew] (its own previous results); eta = t - q goes into
+        // W*'s slot (consumed by then) for the loss. The arithmetic runs on every
+        // lane; only the stores and the carried values depend on whether the entry
+        // exists.
         const int i = t & 63;
-        const float lo1 = (p.LO && i >= 1 && i < R) ? p.LO[(i0 + i - 1) * p.ldlo + i0 + i] : 0.0f;
-        const float lo2 = (p.LO && i >= 2 && i < R) ? p.LO[(i0 + i - 2) * p.ldlo + i0 + i] : 0.0f;
+        float lon[kNew];  // L_O[i-1-e][i]
+#pragma unroll
+        for (int e = 0; e < kNew; ++e)
+            lon[e] = (p.LO && i >= e + 1 && i < R) ? p.LO[(i0 + i - 1 - e) * p.ldlo + i0 + i] : 0.0f;
         const int Lq = (1 << p.bits) - 1;
         const float half = 0.5f * (float)Lq;
+        const float fLq = (float)Lq;
         const float s = (i < R) ? p.scales[i0 + i] : 1.0f;
         const float rs = 1.0f / s;
-        float d_last = 0.0f;   // D of this row's previous entry (read by the lane below)
-        float dp1_last = 0.0f; // D[i-1][j] of the previous step (read by the lane below)
-        float g_last = 0.0f, g_last2 = 0.0f;  // g of this row's previous two entries
-        __syncthreads();
-        // inputs of the next entry, read one step ahead: bulk sums and static data
-        float n_pb = sm.pnb[0][i], n_rb = sm.rnb[0][i];
-        float n_pin = 0.f, n_base = 0.f, n_w = 0.f, n_l1 = 0.f, n_l2 = 0.f;
-        if (i == 0) {
-            n_pin = sm.pt[0][0];
-            n_base = sm.bt[0][0];
-            n_w = sm.wst[0][0];
-        }
-        int slot3n = 1;  // (st + 1) mod 3
-        for (int st = 0; st < 2 * kB - 1; ++st) {
+        const bool row = i < R;
+        float dcar[kNew];  // dcar[e]: D[i-e][j-1] of the previous step (e = 0: this row's own)
+        float gcar[kNew];  // gcar[e]: g[i][j-1-e]
+#pragma unroll
+        for (int e = 0; e < kNew; ++e) dcar[e] = gcar[e] = 0.0f;
+        // the per-entry inputs of a step: the far-field offsets (pt, bt), W* and the
+        // kNew superdiagonals of L_I at column j
+        struct In {
+            float pin, base, w, l[kNew];
+        };
+        auto load_in = [&](int st, In& v) {
+            const int jc = min(max(st - i, 0), kB - 1);
+            v.pin = sm.pt[jc][i];
+            v.base = sm.bt[jc][i];
+            v.w = sm.wst[i][jc];
+#pragma unroll
+            for (int e = 0; e < kNew; ++e) v.l[e] = sm.li[e][jc];
+        };
+        auto entry = [&](int st, const In& v, const f32x4& pq, const f32x4& rq) {
             const int j = st - i;
-            const float dprev1 = lane_above(d_last);    // D[i-1][j]
-            const float dprev2 = lane_above(dp1_last);  // D[i-2][j]
-            const float pb = n_pb, rb = n_rb;
-            const float x_pin = n_pin, x_base = n_base, x_w = n_w, x_l1 = n_l1, x_l2 = n_l2;
-            if (j >= 0 && j < Cc && i < R) {
-                float u = 0.5f;
-                if (p.stochastic)
-                    u = uniform24(p.seed, (uint64_t)(i0 + i) * (uint64_t)p.n + (uint64_t)(j0 + j));
-                const float P = x_pin + ((pb + lo2 * dprev2) + lo1 * dprev1);
-                const float Rr = (rb + g_last2 * x_l2) + g_last * x_l1;
-                const float tv = x_base + P + Rr;
-                const float y = fmaf(tv, rs, half);
-                float cf = floorf(y + u);
-                nclamp += (cf < 0.0f || cf > (float)Lq) ? 1 : 0;
-                cf = fminf(fmaxf(cf, 0.0f), (float)Lq);
-                const float dl = fmaf(-s, cf - half, x_w);  // D = W* - s (c - Lq/2)
-                const float g = P + dl;
+            const bool live = row && j >= 0 && j < Cc;
+            float dn[kNew];  // D[i-1-e][j], from the lane above's carried values
+#pragma unroll
+            for (int e = 0; e < kNew; ++e) dn[e] = lane_above0(dcar[e]);
+            float u = 0.5f;
+            if (p.stochastic) u = uniform24(p.seed, (uint64_t)(i0 + i) * (uint64_t)p.n + (uint64_t)(j0 + j));
+            float pb = (pq[0] + pq[1]) + (pq[2] + pq[3]);
+            float rb = (rq[0] + rq[1]) + (rq[2] + rq[3]);
+#pragma unroll
+            for (int e = kNew - 1; e >= 0; --e) {
+                pb = fmaf(lon[e], dn[e], pb);
+                rb = fmaf(gcar[e], v.l[e], rb);
+            }
+            const float P = v.pin + pb;
+            const float tv = v.base + P + rb;
+            const float y = fmaf(tv, rs, half);
+            const float cu = floorf(y + u);
+            const float cf = fminf(fmaxf(cu, 0.0f), fLq);
+            const float dl = fmaf(-s, cf - half, v.w);  // D = W* - s (c - Lq/2)
+            const float g = P + dl;
+            if (live) {
+                nclamp += (cu < 0.0f || cu > fLq) ? 1 : 0;
                 sm.DT[j][i] = dl;
                 sm.Gs[i][j] = g;
                 sm.code[i][j] = (uint8_t)cf;
                 sm.wst[i][j] = fmaf(-s, cf - half, tv);  // eta
-                d_last = dl;
-                g_last2 = g_last;
-                g_last = g;
             }
-            dp1_last = dprev1;
-            // inputs of the next entry (the bulk sums written in the previous step, static
-            // data, this lane's own W* slot), read after the stores and left in flight
-            // across the barrier; nothing writes them in the next step
+            // carried values: a row's own D and g only where the entry exists
+#pragma unroll
+            for (int e = kNew - 1; e >= 1; --e) {
+                dcar[e] = dn[e - 1];
+                gcar[e] = live ? gcar[e - 1] : gcar[e];
+            }
+            dcar[0] = live ? dl : dcar[0];
+            gcar[0] = live ? g : gcar[0];
+        };
+        auto super = [&](int S, const In& c0, const In& c1, In& n0, In& n1) {
+            // the bulk partials of diagonals 2S and 2S + 1 (written in super-step S - 1)
+            const f32x4 pq0 = lds4(&sm.pnb[(2 * S) & 3][i][0]);
+            const f32x4 rq0 = lds4(&sm.rnb[(2 * S) & 3][i][0]);
+            const f32x4 pq1 = lds4(&sm.pnb[(2 * S + 1) & 3][i][0]);
+            const f32x4 rq1 = lds4(&sm.rnb[(2 * S + 1) & 3][i][0]);
+            // the inputs of the next super-step: the strip hand-overs that feed them
+            // were added by super-step S - 1, and nothing writes them in this one
+            load_in(2 * S + 2, n0);
+            load_in(2 * S + 3, n1);
+            entry(2 * S, c0, pq0, rq0);
+            entry(2 * S + 1, c1, pq1, rq1);
             lds_wait_all();
-            __builtin_amdgcn_sched_barrier(0);
-            const int jn = min(max(j + 1, 0), kB - 1);
-            n_pb = sm.pnb[slot3n][i];
-            n_rb = sm.rnb[slot3n][i];
-            n_pin = sm.pt[jn][i];
-            n_base = sm.bt[jn][i];
-            n_w = sm.wst[i][jn];
-            n_l1 = sm.li1[jn];
-            n_l2 = sm.li2[jn];
-            slot3n = slot3n == 2 ? 0 : slot3n + 1;
-            __builtin_amdgcn_sched_barrier(0);
             barrier_no_wait();
+        };
+        __syncthreads();
+        In a0, a1, b0, b1;
+        load_in(0, a0);
+        load_in(1, a1);
+#pragma nounroll
+        for (int S = 0; S < kSuper; S += 2) {
+            super(S, a0, a1, b0, b1);
+            super(S + 1, b0, b1, a0, a1);
         }
     } else {
         // ---------------- hand-over waves (column-wise, row-wise) ----------------
-        int seen = 0;  // neighbour's counter, read three steps before it is looked at
-        __syncthreads();
-#pragma nounroll
-        for (int st = 0; st < kSweep; ++st) {
-            // the lane index, opaque per step, so that the address arithmetic of the
-            // loads and stores below is not hoisted out of the sweep and held across it
-            int ln = lane;
-            asm volatile("" : "+v"(ln));
-            // the neighbour's strip c >= 1: window st = 16c - 12 .. 16c - 2
-            const int cw = (st + 12) >> 4, ph = (st + 12) & 15;
-            if (hown && cw >= 1 && cw < kStrips) {
-                if (ph == 0) {
-                    seen = ld_flag(hflag);
-                } else if (ph == 2) {
-                    if (seen < cw + 1) wait_flag(p, hflag, cw + 1);
-                    compiler_fence();
-                    handover_load(p, hcol, cw, i0, j0, R, Cc, h, ln);
-                } else if (ph == 5) {
-                    handover_mma<0, 3>(hcol, h);
-                } else if (ph == 6) {
-                    handover_mma<3, 6>(hcol, h);
-                } else if (ph == 7) {
-                    handover_mma<6, 9>(hcol, h);
-                } else if (ph == 8) {
-                    handover_mma<9, 12>(hcol, h);
-                } else if (ph == 9) {
-                    handover_mma<12, 16>(hcol, h);
-                } else if (ph == 10) {
-                    handover_add(sm, hcol, cw, h, ln);
-                }
-            }
-            // this leaf's strip c <= 2: stored at st = 79 + 16c, counter raised 3 steps later
-            if (st >= kB + kStrip - 1) {
-                const int cp = (st - (kB + kStrip - 1)) >> 4, pp = (st - (kB + kStrip - 1)) & 15;
-                if (cp < kStrips - 1) {
-                    if (pp == 0) handover_publish(p, sm, hcol, cp, i0, j0, R, Cc, ln);
-                    else if (pp == 3) handover_flag(p, hcol, leaf, cp + 1, ln);
-                }
-            }
+        // Super-steps 0-23 are the three windows of the neighbour's strips 1-3 (strip
+        // c: super-steps 8c - 8 .. 8c - 1), written out super-step by super-step, so
+        // that each window is straight-line code: the counter read at 8c - 8 is waited
+        // for only where it is checked, a super-step later, and the strip loads of
+        // 8c - 7 only at the first multiply, two super-steps later. The product is
+        // added at 8c - 2, before the finaliser reads the inputs of step 16c (at the
+        // start of super-step 8c - 1). Super-steps 24-63 publish this leaf's strips 0-2.
+        auto sync_step = [&]() {
             lds_wait_all();
             barrier_no_wait();
+        };
+        __syncthreads();
+#pragma nounroll
+        for (int cw = 1; cw < kStrips; ++cw) {
+            int seen = 0;
+            if (hown) seen = ld_flag(hflag);  // super-step 8c - 8
+            sync_step();
+            if (hown) {  // 8c - 7
+                // keeps the check (and the wait for the counter's load) from moving up
+                // to the super-step of the load
+                asm volatile("" : "+v"(seen));
+                if (seen < cw + 1) wait_flag(p, hflag, cw + 1);
+                compiler_fence();
+                handover_load(p, hcol, cw, i0, j0, R, Cc, h, lane);
+            }
+            sync_step();
+            sync_step();                            // 8c - 6
+            if (hown) handover_mma<0, 5>(hcol, h);  // 8c - 5 .. 8c - 3
+            sync_step();
+            if (hown) handover_mma<5, 10>(hcol, h);
+            sync_step();
+            if (hown) handover_mma<10, 16>(hcol, h);
+            sync_step();
+            if (hown) handover_add(sm, hcol, cw, h, lane);  // 8c - 2
+            sync_step();
+            sync_step();                                    // 8c - 1
+        }
+        // this leaf's strip c <= 2 (final after step 78 + 16c, in super-step 39 + 8c):
+        // stored in super-step 40 + 8c, counter raised two super-steps later
+#pragma nounroll
+        for (int S = 8 * (kStrips - 1); S < kSuper; ++S) {
+            // the lane index, opaque per super-step, so that the address arithmetic of the
+            // stores below is not hoisted out of the sweep and held across it
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            if (S >= 40) {
+                const int cp = (S - 40) >> 3, pp = (S - 40) & 7;
+                if (cp < kStrips - 1) {
+                    if (pp == 0) handover_publish(p, sm, hcol, cp, i0, j0, R, Cc, ln);
+                    else if (pp == 2) handover_flag(p, hcol, leaf, cp + 1, ln);
+                }
+            }
+            sync_step();
         }
     }
     // the last strips
