@@ -258,8 +258,8 @@ int bakron_solve(const float* W, int64_t m, int64_t n, int64_t ldw, const float*
  * call allocates nothing: no hipMalloc, no hipFree, no allocating library
  * routine.
  *   Sizes: bakron_solve_workspace_bytes(m, n) must not exceed
- *      BAKRON_NOALLOC_SCRATCH_BYTES (for example m = n = 2048, or
- *      m = 1024 with n up to 4096); larger shapes return BAKRON_E_WORKSPACE
+ *      BAKRON_NOALLOC_SCRATCH_BYTES, 128 MiB (for example m = n = 2048, or
+ *      m = 1024 with n up to 3072); larger shapes return BAKRON_E_WORKSPACE
  *      before anything is enqueued.
  *   Sharing: every call on a device uses that device's one array, which keeps
  *      the last call's contents (the solve clears what must start at zero).
@@ -269,7 +269,7 @@ int bakron_solve(const float* W, int64_t m, int64_t n, int64_t ldw, const float*
  *      BAKRON_E_DEVICE if the scratch array's address cannot be obtained on
  *      the current device.
  */
-#define BAKRON_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+#define BAKRON_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 int bakron_solve_noalloc(const float* W, int64_t m, int64_t n, int64_t ldw, const float* L_O, int64_t ldlo,
                          const float* L_I, int64_t ldli, const bakron_quantizer* q, uint8_t* codes,
                          int64_t ldc, float* scales_out, float* delta_out, int64_t ldd, const float* D_O,

@@ -86,7 +86,7 @@ def _load() -> ctypes.CDLL:
 LIB = _load()
 
 # bytes of the device scratch array that bakron_solve_noalloc works in
-NOALLOC_SCRATCH_BYTES = 64 << 20
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 EXPORTS = ("bakron_abi_version", "bakron_status_str", "bakron_hessian_accum_workspace_bytes",
            "bakron_hessian_accum", "bakron_hessian_accum_t", "bakron_hessian_accum_tb",

@@ -435,7 +435,6 @@ __global__ __launch_bounds__(kThreads) void k_syrk_reduce(int64_t d, float alpha
 // to whole 128-wide tiles, so every tile streams whole 2 KB rows of Xs straight
 // into LDS.
 // ---------------------------------------------------------------------------
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 #ifndef BK_S2_NS
 #define BK_S2_NS 4
@@ -475,7 +474,6 @@ inline Split2Shape split2_shape(int64_t T, int64_t d) {
     return s;
 }
 
-__device__ __forceinline__ float nan_max(float m, float a) { return (a > m || a != a) ? a : m; }
 
 // Partial maxima of |x| (|x sqrt(w)| with token weights) for columns 4 t .. 4 t + 3 of
 // block x over the tokens of chunk blockIdx.y; columns in [d, dp) get 0.
@@ -553,14 +551,6 @@ __global__ __launch_bounds__(kThreads) void k_colexp(const float* __restrict__ p
     exps[c] = e;
 }
 
-// the two pieces of x' = x 2^e, as fp16 bits
-__device__ __forceinline__ void split2_value(float x, int e, uint32_t& h, uint32_t& l) {
-    const float xs = ldexpf(x, e);
-    const _Float16 hv = (_Float16)xs;
-    const _Float16 lv = (_Float16)(xs - (float)hv);
-    h = (uint32_t)__builtin_bit_cast(uint16_t, hv);
-    l = (uint32_t)__builtin_bit_cast(uint16_t, lv);
-}
 
 // Block (x, g): columns 1024 x .. 1024 x + 1023 of tokens 8 g .. 8 g + 7 into the
 // two planes, through LDS. Each row is read as 16-byte vectors where four

@@ -21,6 +21,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef double f64x2 __attribute__((ext_vector_type(2)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kTile = 64;      // output tile edge (also the rounding leaf edge)
 constexpr int kThreads = 256;  // threads per workgroup for tile kernels
@@ -301,6 +302,20 @@ __device__ __forceinline__ float quad_sum(float x) {
     x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E,
                                                                 0xF, 0xF, false));
     return x;
+}
+
+// max that lets a NaN through
+__device__ __forceinline__ float nan_max(float m, float a) { return (a > m || a != a) ? a : m; }
+
+// The two fp16 pieces of x' = x 2^e (hi = fp16(x'), lo = fp16(x' - hi)), as fp16
+// bits: with |x'| < 2^15 the pair holds x' to about 22 bits, and hi lo' + lo hi' +
+// hi hi' gives a product to about fp32 accuracy.
+__device__ __forceinline__ void split2_value(float x, int e, uint32_t& h, uint32_t& l) {
+    const float xs = ldexpf(x, e);
+    const _Float16 hv = (_Float16)xs;
+    const _Float16 lv = (_Float16)(xs - (float)hv);
+    h = (uint32_t)__builtin_bit_cast(uint16_t, hv);
+    l = (uint32_t)__builtin_bit_cast(uint16_t, lv);
 }
 
 }  // namespace bk

@@ -43,8 +43,8 @@ namespace bk {
 constexpr int kB = kTile;        // leaf edge
 constexpr int kNch = 4;          // maximum K-chunks per far-field product
 constexpr int kRing = 4;         // diagonals whose far-field partials are held at once
-constexpr int kTargetWg = 1024;  // far-field tasks aimed for per diagonal
-constexpr int kFarKT = 64;       // k-slice depth of the far-field GEMMs
+constexpr int kTargetWg = 512;   // far-field tasks aimed for per diagonal
+constexpr int kFarMin = 4;       // first diagonal with a far field (blocks four or more back)
 constexpr int kStrip = 16;       // columns (rows) per hand-over
 constexpr int kStrips = kB / kStrip;
 
@@ -80,11 +80,22 @@ struct SolveParams {
     int* prog_c;     // per leaf: strips of C published (0..4)
     int* setup;      // per leaf: 1 once its far-field partials are consumed
     int* fardone;    // per leaf: far-field tasks finished
+    int* pdone;      // per leaf: 1 once its D and C pieces, and those of the leaves above and to its left, are written
     int* seg;        // first task of each group k (ND + 1 entries)
     int* nchd;       // K-chunks of the far-field products, per diagonal
     int ND;          // leaf-diagonals
     int ntask;
     uint64_t spin_limit;  // wall-clock ticks a single wait may take
+    // far-field operands as fp16 piece planes (see the far-field section)
+    int64_t Mp, Np;  // rows, columns padded to whole leaves
+    const f16x8* lop;  // L_O: [2][Mp / 8][Mp]
+    const f16x8* lip;  // L_I: [2][Np / 8][Np]
+    f16x8* dpl;        // D:   [2][Mp / 8][Np]
+    f16x8* cpl;        // C:   [2][Np / 8][Mp]
+    const int* exd;    // eD per row of W (Mp)
+    const int* exc;    // eC per row of W (Mp)
+    const int* fexo;   // fO per column of L_O (Mp)
+    const int* fexi;   // fI per column of L_I (Np)
 };
 
 __host__ __device__ __forceinline__ int diag_lo(int N, int d) { return d - (N - 1) > 0 ? d - (N - 1) : 0; }
@@ -92,26 +103,40 @@ __host__ __device__ __forceinline__ int diag_hi(int M, int d) { return d < M - 1
 __host__ __device__ __forceinline__ int diag_leaves(int M, int N, int d) {
     return diag_hi(M, d) - diag_lo(N, d) + 1;
 }
-// K-chunks per far-field product on diagonal d: enough tasks to fill the chip,
-// chunks of at least 4 blocks
+// even indices in [lo, hi]
+__host__ __device__ __forceinline__ int count_even(int lo, int hi) { return (hi >> 1) - ((lo + 1) >> 1) + 1; }
+// K-chunks per far-field product on diagonal d: about kTargetWg tasks (one pair task
+// per leaf on average), chunks of at least 4 blocks
 __host__ __device__ __forceinline__ int diag_nch(int M, int N, int d) {
     const int lo = diag_lo(N, d), hi = diag_hi(M, d), nl = hi - lo + 1;
-    const int kmax = (hi > d - lo ? hi : d - lo) - 2;  // blocks three or more back
-    int nch = (kTargetWg + 2 * nl - 1) / (2 * nl);
+    const int kmax = (hi > d - lo ? hi : d - lo) - 3;  // blocks four or more back
+    int nch = (kTargetWg + nl - 1) / nl;
     const int cap = kmax / 4 > 1 ? kmax / 4 : 1;
     nch = nch < cap ? nch : cap;
     nch = nch < kNch ? nch : kNch;
     return nch > 1 ? nch : 1;
 }
-// tasks of group k: the leaves of diagonal k, then the far fields of diagonal k + 1
-// (those exist from diagonal 3 on: they need blocks three or more back). A far
-// task reads leaves two or more groups back, so it rarely waits; the leaves of
-// its diagonal come right after it in the order.
-__host__ __device__ __forceinline__ int group_far(int ND, int k) { return (k + 1 >= 3 && k + 1 < ND) ? k + 1 : -1; }
+// The far fields come in pairs that share a factor panel: the column far field p of
+// leaves (I, J) and (I, J + 1) for even J (one L_O panel, two adjacent D panels), and
+// the row far field o of leaves (I, J) and (I + 1, J) for even I (one L_I panel, two
+// adjacent C^T panels). A pair is computed with the first leaf's diagonal; the second
+// leaf lies on the next one. On an odd diagonal every leaf starts one pair (p where I
+// is odd, o where I is even); on an even diagonal the leaves with even I start both.
+__host__ __device__ __forceinline__ int far_tasks(int M, int N, int d, int nch) {
+    const int lo = diag_lo(N, d), hi = diag_hi(M, d);
+    return (d & 1) ? (hi - lo + 1) * nch : count_even(lo, hi) * 2 * nch;
+}
+// tasks of group k: the leaves of diagonal k, then the far-field pairs of diagonal
+// k + 1 (those exist from diagonal kFarMin on). A pair task reads leaves three or
+// more groups back, so it rarely waits; the leaves of its diagonal come right after
+// it in the order.
+__host__ __device__ __forceinline__ int group_far(int ND, int k) {
+    return (k + 1 >= kFarMin && k + 1 < ND) ? k + 1 : -1;
+}
 __host__ __device__ __forceinline__ int group_tasks(int M, int N, int ND, int k) {
     int s = diag_leaves(M, N, k);
     const int df = group_far(ND, k);
-    if (df >= 0) s += diag_leaves(M, N, df) * 2 * diag_nch(M, N, df);
+    if (df >= 0) s += far_tasks(M, N, df, diag_nch(M, N, df));
     return s;
 }
 
@@ -141,6 +166,13 @@ __device__ __forceinline__ void st_flag(int* f, int v) {
 __device__ __forceinline__ void st_coherent(float* q, float v) {
     __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16 bytes as two device-coherent 8-byte stores
+__device__ __forceinline__ void st_coherent16(f16x8* q, const uint32_t (&v)[4]) {
+    uint64_t* q64 = reinterpret_cast<uint64_t*>(q);
+    __hip_atomic_store(q64, (uint64_t)v[0] | ((uint64_t)v[1] << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q64 + 1, (uint64_t)v[2] | ((uint64_t)v[3] << 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 // keeps the compiler from moving the data loads above the counter check
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
@@ -163,42 +195,136 @@ __device__ __forceinline__ bool wait_flag(const SolveParams& p, const int* f, in
 }
 
 // ---------------------------------------------------------------------------
-// scales: s_i = fp32(2 max_j |W*_ij|) / fp32(Lq), or the caller's scale
+// scales: s_i = fp32(2 max_j |W*_ij|) / fp32(Lq), or the caller's scale; also the
+// bound b_i = max_j |W*_ij| + s_i Lq / 2 on row i of D and its exponent eD_i
 // ---------------------------------------------------------------------------
+// 2^e b below 2^14 (in [2^13, 2^14)); 0 for a zero or non-finite b
+__device__ __forceinline__ int bound_exp(float b) {
+    if (!(b > 0.0f) || !(b < INFINITY)) return 0;
+    int E;
+    frexpf(b, &E);
+    return min(100, max(-100, 14 - E));
+}
+// 2^e m in [2^14, 2^15) for the largest magnitude m; 0 for a zero or non-finite m
+__device__ __forceinline__ int max_exp(float m) {
+    if (!(m > 0.0f) || !(m < INFINITY)) return 0;
+    int E;
+    frexpf(m, &E);
+    return min(100, max(-100, 15 - E));
+}
+
 __global__ __launch_bounds__(kThreads) void k_scales(const float* __restrict__ W, int64_t n,
                                                      int64_t ldw, int bits,
                                                      const float* __restrict__ row_scale,
-                                                     float* __restrict__ scales, int* info) {
+                                                     float* __restrict__ scales, float* __restrict__ bd,
+                                                     int* __restrict__ ed, int* info) {
     const int64_t i = blockIdx.x;
-    float s;
-    if (row_scale) {
-        s = row_scale[i];
-    } else {
-        __shared__ float red[kThreads];
-        float a = 0.0f;
-        const float* w = W + i * ldw;
-        for (int64_t j = threadIdx.x; j < n; j += kThreads) {
-            const float v = fabsf(w[j]);
-            a = (v > a || v != v) ? v : a;  // NaN propagates
-        }
-        red[threadIdx.x] = a;
+    __shared__ float red[kThreads];
+    float a = 0.0f;
+    const float* w = W + i * ldw;
+    for (int64_t j = threadIdx.x; j < n; j += kThreads) a = nan_max(a, fabsf(w[j]));
+    red[threadIdx.x] = a;
+    __syncthreads();
+    for (int o = kThreads / 2; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) red[threadIdx.x] = nan_max(red[threadIdx.x], red[threadIdx.x + o]);
         __syncthreads();
-        for (int o = kThreads / 2; o > 0; o >>= 1) {
-            if ((int)threadIdx.x < o) {
-                const float b = red[threadIdx.x + o];
-                const float c = red[threadIdx.x];
-                red[threadIdx.x] = (b > c || b != b) ? b : c;
-            }
-            __syncthreads();
-        }
-        s = (2.0f * red[0]) / (float)((1 << bits) - 1);
     }
+    const float Lq = (float)((1 << bits) - 1);
+    const float s = row_scale ? row_scale[i] : (2.0f * red[0]) / Lq;
     if (threadIdx.x == 0) {
         scales[i] = s;
         if (!(s > 0.0f) || !(s < INFINITY)) atomicMin(info, (int)min<int64_t>(i + 1, INT_MAX - 1));
+        const float b = red[0] + s * (0.5f * Lq);
+        bd[i] = b;
+        ed[i] = bound_exp(b);
     }
 }
 
+// ---------------------------------------------------------------------------
+// pre-pass: the piece planes of L_O and L_I, and the exponents of the planes of C
+// ---------------------------------------------------------------------------
+constexpr int kPrepRows = 256;  // rows of a factor per pre-pass workgroup
+
+// Column statistics of the strictly upper factor L (d x d) over rows 256 y .. 256 y + 255,
+// for the 64 columns of block x:
+//   mx[y][c] = max |L[k][c]| 2^-re_k over the far-field rows k < 64 (x - 3)   (re: none = 0)
+//   sb[y][c] = sum |L[k][c]| rb_k over k < c                               (when rb is given)
+__global__ __launch_bounds__(kThreads) void k_lstats(const float* __restrict__ L, int64_t ld, int64_t d,
+                                                     const int* __restrict__ re, const float* __restrict__ rb,
+                                                     int64_t dp, float* __restrict__ mx, float* __restrict__ sb) {
+    __shared__ float rm[4][kB], rs[4][kB];
+    const int t = threadIdx.x, c = t & 63, rq = t >> 6;
+    const int64_t x = blockIdx.x, col = x * kB + c;
+    const int64_t k0 = (int64_t)blockIdx.y * kPrepRows;
+    const int64_t kf = max<int64_t>(0, (x - 3) * kB);
+    const int64_t k1 = min<int64_t>(k0 + kPrepRows, min<int64_t>(d, col));
+    float m = 0.0f, sum = 0.0f;
+    if (col < d) {
+        for (int64_t k = k0 + rq; k < k1; k += 4) {
+            const float v = fabsf(L[k * ld + col]);
+            if (k < kf) m = nan_max(m, re ? ldexpf(v, -re[k]) : v);
+            if (rb) sum += v * rb[k];
+        }
+    }
+    rm[rq][c] = m;
+    rs[rq][c] = sum;
+    __syncthreads();
+    if (rq == 0) {
+        const size_t o = (size_t)blockIdx.y * dp + col;
+        mx[o] = nan_max(nan_max(rm[0][c], rm[1][c]), nan_max(rm[2][c], rm[3][c]));
+        if (sb) sb[o] = (rs[0][c] + rs[1][c]) + (rs[2][c] + rs[3][c]);
+    }
+}
+
+// Per column c < dp: fex[c] from the maxima (mx given), and cex[c] = the exponent of
+// the bound rb_c + sum_y sb[y][c] (cex given; rows c >= d have bound 0).
+__global__ __launch_bounds__(kThreads) void k_lexp(const float* __restrict__ mx, const float* __restrict__ sb,
+                                                   int nchunk, int64_t dp, int64_t d,
+                                                   const float* __restrict__ rb, int* __restrict__ fex,
+                                                   int* __restrict__ cex) {
+    const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (c >= dp) return;
+    float m = 0.0f, sum = 0.0f;
+    for (int y = 0; y < nchunk; ++y) {
+        if (mx) m = nan_max(m, mx[(size_t)y * dp + c]);
+        if (sb) sum += sb[(size_t)y * dp + c];
+    }
+    if (fex) fex[c] = max_exp(m);
+    if (cex) cex[c] = c < d ? bound_exp(rb[c] + sum) : 0;
+}
+
+// The far-field rows of column block x (groups g < 8 (x - 3)) of L, 32 groups per
+// workgroup (y), into the planes P[piece][g][c]: element (k, c) scaled by
+// 2^(fex_c - re_k). Thread (c, q) writes the units of column c for groups q, q + 4, ..
+// (a wave stores 1 KB of consecutive units per plane).
+__global__ __launch_bounds__(kThreads) void k_lsplit(const float* __restrict__ L, int64_t ld, int64_t d,
+                                                     const int* __restrict__ re, const int* __restrict__ fex,
+                                                     int64_t dp, int64_t ng, f16x8* __restrict__ P) {
+    const int t = threadIdx.x, c = t & 63, gq = t >> 6;
+    const int64_t x = blockIdx.x, col = x * kB + c;
+    const int64_t gf = max<int64_t>(0, 8 * (x - 3));
+    const int64_t gb = (int64_t)blockIdx.y * (kPrepRows / 8);
+    const int64_t ge = min<int64_t>(gb + kPrepRows / 8, gf);
+    const int fc = fex[col];
+    for (int64_t g = gb + gq; g < ge; g += 4) {
+        uint32_t pk[2][4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const int64_t k = 8 * g + e;  // < 64 (x - 3) <= d - 64
+            const float v0 = col < d ? L[k * ld + col] : 0.0f;
+            const float v1 = col < d ? L[(k + 1) * ld + col] : 0.0f;
+            uint32_t h0, l0, h1, l1;
+            split2_value(v0, fc - (re ? re[k] : 0), h0, l0);
+            split2_value(v1, fc - (re ? re[k + 1] : 0), h1, l1);
+            pk[0][e >> 1] = h0 | (h1 << 16);
+            pk[1][e >> 1] = l0 | (l1 << 16);
+        }
+#pragma unroll
+        for (int pc = 0; pc < 2; ++pc)
+            *reinterpret_cast<uint4*>(&P[((int64_t)pc * ng + g) * dp + col]) =
+                uint4{pk[pc][0], pk[pc][1], pk[pc][2], pk[pc][3]};
+    }
+}
 
 // Clears the schedule state and builds the task table: workgroup 0 scans the
 // per-group task counts 256 diagonals at a time; the counters are cleared by the
@@ -210,6 +336,7 @@ __global__ __launch_bounds__(kThreads) void k_solve_init(SolveParams p) {
         p.prog_c[e] = 0;
         p.setup[e] = 0;
         p.fardone[e] = 0;
+        p.pdone[e] = 0;
     }
     if (blockIdx.x != 0) return;
     __shared__ int sc[kThreads];
@@ -243,12 +370,25 @@ __global__ __launch_bounds__(kThreads) void k_solve_init(SolveParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// far field of diagonal d: chunk c (of nch) of p (kind 0) or o^T (kind 1) of
-// one leaf, over the blocks three or more above (p) or to the left (o) of the
-// leaf. It starts once the last leaf of its K range has published all of its
-// D (C); the leaves before it in that column (row) finished earlier, since
-// each waited on its predecessor. Each chunk writes its own 64x64 partial (an
-// empty chunk writes zeros); the leaf adds them in chunk order.
+// far field of diagonal d: chunk c (of nch) of a pair of p (kind 0) or o^T
+// (kind 1) tiles, over the blocks four or more above (p) or to the left (o) of
+// the pair's leaves. The products run on fp16 MFMAs over two-piece operands
+// (hi = fp16(x'), lo = fp16(x' - hi) of a power-of-two-scaled x'): three piece
+// products per fp32 product, accumulated in fp32. The operands are piece
+// planes, P[piece][k / 8][column] with the 8 fp16 values of k = 8g .. 8g + 7 in
+// one 16-byte unit, laid out so that a 16-byte unit is an MFMA operand:
+//   A of p:   L_O, row k scaled by 2^-eD_k and column i by 2^fO_i (pre-pass)
+//   B of p:   D,   row k scaled by 2^eD_k                  (written by leaf (k/64, j/64))
+//   A of o^T: L_I, column j scaled by 2^fI_j              (pre-pass)
+//   B of o^T: C,   row i scaled by 2^eC_i (contracted over its columns l)
+// so that p_ij = 2^-fO_i (A^T B)_ij and o^T_ji = 2^-(fI_j + eC_i) (A^T B)_ji. eD_k
+// and eC_i come from bounds known before the sweep: |D_kl| <= max_l |W*_kl| +
+// s_k Lq / 2 =: b_k (the code is clamped to [0, Lq]) and |C_il| <= b_i + sum_{k<i}
+// |L_O[k,i]| b_k, each scaled to below 2^14; fO and fI from the column maxima
+// (scaled to [2^14, 2^15)). A task starts once the last leaves of its K range
+// have written their pieces (each leaf marks its pieces written only after the
+// leaves above and to its left did, so those finished earlier). Each chunk
+// writes its own fp32 64x64 partial per leaf; the leaf adds them in chunk order.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void chunk_range(int kblk, int nch, int c, int& b0, int& b1) {
     const int len = (kblk + nch - 1) / nch;
@@ -256,138 +396,196 @@ __device__ __forceinline__ void chunk_range(int kblk, int nch, int c, int& b0, i
     b1 = min(b0 + len, kblk);
 }
 
-// Whole 64x64 far-field tiles with 16-byte aligned rows: k-slices of kFarRingKT
-// rows fill a ring of kFarRingNS slots in LDS by direct global-to-LDS loads
-// (global_load_lds_dwordx4: one instruction of a wave fills four 64-float rows),
-// kFarRingNS - 1 slices ahead of the MFMAs, so several slices of loads are in
-// flight while the tile is computed. Waves 0-3 load and compute (32x32 quadrant
-// each); the others only join the barriers.
-constexpr int kFarRingKT = 32;
-constexpr int kFarRingNS = 4;
-struct FarRing {
-    float a[kFarRingNS][kFarRingKT][kB];
-    float b[kFarRingNS][kFarRingKT][kB];
-};
-
 // Wait until at most N of this wave's vector-memory operations are outstanding, then
 // meet the other waves. Direct-to-LDS loads complete in issue order, so with N = the
-// loads issued after slice s, slice s is in LDS once every wave has passed; the later
+// loads issued after stage s, stage s is in LDS once every wave has passed; the later
 // loads stay in flight across the barrier.
 template <int N>
 __device__ __forceinline__ void vm_wait_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// acc += A^T B over K (a multiple of kFarRingKT) for a whole 64x64 tile: A (k, r) at
-// A[k*lda + r], B (k, c) at B[k*ldb + c]; every thread of the workgroup calls it.
-__device__ __forceinline__ void far_gemm_ring(const float* __restrict__ A, int64_t lda,
-                                              const float* __restrict__ B, int64_t ldb, int64_t K,
-                                              f32x16& acc, FarRing& sm, int tid) {
+// One ring stage: 32 k (four 8-k groups) of both pieces of A (64 columns) and B (up
+// to 128 columns: the pair's two targets side by side).
+#ifndef BK_PIECE_NS
+#define BK_PIECE_NS 4
+#endif
+constexpr int kPieceNS = BK_PIECE_NS;  // stages in the ring: loads run kPieceNS - 1 stages ahead
+struct PieceStage {
+    f16x8 a[2][4][kB];
+    f16x8 b[2][4][2 * kB];
+};
+struct PieceRing {
+    PieceStage s[kPieceNS];
+    int fr[kB];      // exponent of each output row (A column)
+    int fc[2 * kB];  // exponent of each output column (B column)
+};
+
+// acc[t] += A^T B over groups [g0, g1) (whole stages) for NT targets: A columns
+// ca .. ca + 63 of plane A (ngA groups, ncA columns), B columns cb .. cb + 64 NT - 1
+// of plane B. Waves 0-3 load and compute (wave w: output rows 32 (w >> 1) .., target
+// w & 1 for a pair, or columns 32 (w & 1) .. of the lone target); the others only
+// join the barriers. Every thread of the workgroup calls it.
+template <int NT>
+__device__ __forceinline__ void far_pieces(const f16x8* __restrict__ A, int64_t ngA, int64_t ncA, int64_t ca,
+                                           const f16x8* __restrict__ B, int64_t ngB, int64_t ncB, int64_t cb,
+                                           int64_t g0, int64_t g1, f32x16 (&acc)[2], PieceRing& sm, int tid) {
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool active = w < 4;
-    const int ra = (w >> 1) * 32 + (lane & 31);
-    const int rb = (w & 1) * 32 + (lane & 31);
-    const int kh = lane >> 5;
-    const int c4 = (lane & 15) << 2;
-    constexpr int kLoads = 2 * (kFarRingKT / 16);  // direct loads per active wave per slice
-    const int64_t ns = K / kFarRingKT;
+    const int kh = lane >> 5, l31 = lane & 31;
+    const int ar = (w >> 1) * 32 + l31;
+    const int bc = (w & 1) * 32 * NT + l31;
+    constexpr int kLoads = (8 + 8 * NT) / 4;  // direct loads per active wave per stage
+    const int64_t ns = (g1 - g0) / 4;
     auto issue = [&](int64_t s) {
-        const int slot = (int)(s % kFarRingNS);
-        const int64_t k0 = s * kFarRingKT;
+        PieceStage& st = sm.s[s % kPieceNS];
+        const int64_t gs = g0 + 4 * s;
 #pragma unroll
-        for (int h = 0; h < kFarRingKT / 16; ++h) {
-            const int r = 4 * (2 * w + h);  // rows r .. r+3 of the slice
-            const int64_t k = k0 + r + (lane >> 4);
-            __builtin_amdgcn_global_load_lds(A + k * lda + c4, &sm.a[slot][r][0], 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(B + k * ldb + c4, &sm.b[slot][r][0], 16, 0, 0);
+        for (int h = 0; h < kLoads; ++h) {
+            const int q = w + 4 * h;
+            if (q < 8) {  // A: one 1 KB row (64 units) per load
+                const int pc = q >> 2, gl = q & 3;
+                __builtin_amdgcn_global_load_lds(A + (pc * ngA + gs + gl) * ncA + ca + lane, &st.a[pc][gl][0],
+                                                 16, 0, 0);
+            } else {
+                const int q2 = q - 8;
+                const int pc = q2 / (4 * NT), gl = (q2 / NT) & 3, hf = q2 % NT;
+                __builtin_amdgcn_global_load_lds(B + (pc * ngB + gs + gl) * ncB + cb + kB * hf + lane,
+                                                 &st.b[pc][gl][kB * hf], 16, 0, 0);
+            }
         }
     };
     if (active)
-        for (int s = 0; s < kFarRingNS - 1; ++s)
+        for (int s = 0; s < kPieceNS - 1; ++s)
             if (s < ns) issue(s);
+    // the three piece products (lo hi', hi lo', hi hi'), smallest first
+    constexpr int kPa[3] = {1, 0, 0};
+    constexpr int kPb[3] = {0, 1, 0};
     for (int64_t it = 0; it < ns; ++it) {
-        if (it + kFarRingNS - 2 < ns) vm_wait_barrier<(kFarRingNS - 2) * kLoads>();
+        if (it + kPieceNS - 2 < ns) vm_wait_barrier<(kPieceNS - 2) * kLoads>();
         else vm_wait_barrier<0>();
         if (!active) continue;
-        if (it + kFarRingNS - 1 < ns) issue(it + kFarRingNS - 1);
-        const int slot = (int)(it % kFarRingNS);
-        float fa[3], fb[3];
-        fa[0] = sm.a[slot][kh][ra];
-        fb[0] = sm.b[slot][kh][rb];
-        fa[1] = sm.a[slot][2 + kh][ra];
-        fb[1] = sm.b[slot][2 + kh][rb];
+        if (it + kPieceNS - 1 < ns) issue(it + kPieceNS - 1);
+        const PieceStage& st = sm.s[it % kPieceNS];
+        f16x8 fa[2][2], fb[2][2][NT];
 #pragma unroll
-        for (int s = 0; s < kFarRingKT / 2; ++s) {
-            if (s + 2 < kFarRingKT / 2) {
-                fa[(s + 2) % 3] = sm.a[slot][2 * (s + 2) + kh][ra];
-                fb[(s + 2) % 3] = sm.b[slot][2 * (s + 2) + kh][rb];
+        for (int pc = 0; pc < 2; ++pc) {
+            fa[0][pc] = st.a[pc][kh][ar];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) fb[0][pc][t] = st.b[pc][kh][bc + 32 * t];
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {  // two 16-k steps
+            if (s2 == 0) {
+#pragma unroll
+                for (int pc = 0; pc < 2; ++pc) {
+                    fa[1][pc] = st.a[pc][2 + kh][ar];
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) fb[1][pc][t] = st.b[pc][2 + kh][bc + 32 * t];
+                }
             }
-            __builtin_amdgcn_sched_barrier(0);  // keep the reads two steps ahead of the MFMAs
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[s % 3], fb[s % 3], acc, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);  // the next step's reads go out before these MFMAs
+#pragma unroll
+            for (int u = 0; u < 3; ++u)
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[s2][kPa[u]], fb[s2][kPb[u]][t], acc[t], 0, 0,
+                                                                    0);
         }
     }
 }
 
 union FarSmem {
-    GemmSmemF32<kFarKT> staged;  // ragged tiles
-    FarRing ring;
+    PieceRing pc;
 };
 
 __device__ __forceinline__ void far_task(const SolveParams& p, int d, int task, FarSmem& sm, int tid) {
     const int nch = p.nchd[d];
-    const int slot = task / (2 * nch);
-    const int kind = (task / nch) & 1;
-    const int c = task % nch;
-    const int I = leaf_lo(p, d) + slot;
+    const int lo = leaf_lo(p, d);
+    int I, kind, c;
+    if (d & 1) {  // every leaf starts one pair: p where I is odd (J even), o where I is even
+        c = task % nch;
+        I = lo + task / nch;
+        kind = (I & 1) ? 0 : 1;
+    } else {  // the leaves with even I (and J) start both
+        c = task % nch;
+        kind = (task / nch) & 1;
+        I = lo + (lo & 1) + 2 * (task / (2 * nch));
+    }
     const int J = d - I;
-    const bool has = kind == 0 ? (p.LO != nullptr && I > 2) : (p.LI != nullptr && J > 2);
+    // the pair's second leaf, on diagonal d + 1
+    const int I2 = kind == 0 ? I : I + 1, J2 = kind == 0 ? J + 1 : J;
+    const bool two = I2 < p.M && J2 < p.N;
+    const int slot = I - lo, slot2 = two ? I2 - leaf_lo(p, d + 1) : 0;
+    const int kblk = (kind == 0 ? I : J) - 3;  // blocks 0 .. kblk - 1: four or more back
+    const bool has = (kind == 0 ? p.LO != nullptr : p.LI != nullptr) && kblk > 0;
     if (has) {
         int kb0, kb1;
-        chunk_range((kind == 0 ? I : J) - 2, nch, c, kb0, kb1);
+        chunk_range(kblk, nch, c, kb0, kb1);
+        const int64_t i0 = (int64_t)I * kB, j0 = (int64_t)J * kB;
         if (tid == 0) {
+            // the last leaf of the K range next to the pair's second (or only) target:
+            // its pieces, and so those of every leaf above and to the left of it
             if (kb1 > kb0) {
-                if (kind == 0) wait_flag(p, &p.prog_d[(int64_t)(kb1 - 1) * p.N + J], kStrips);
-                else wait_flag(p, &p.prog_c[(int64_t)I * p.N + kb1 - 1], kStrips);
+                if (kind == 0) wait_flag(p, &p.pdone[(int64_t)(kb1 - 1) * p.N + (two ? J2 : J)], 1);
+                else wait_flag(p, &p.pdone[(int64_t)(two ? I2 : I) * p.N + kb1 - 1], 1);
             }
-            if (d >= kRing) {  // the leaf that last used this ring slot has read it
+            // the leaves that last used these ring slots (kRing diagonals back) have read them
+            if (d >= kRing) {
                 const int dp = d - kRing;
                 if (slot < diag_leaves(p.M, p.N, dp)) {
                     const int Ip = leaf_lo(p, dp) + slot;
                     wait_flag(p, &p.setup[(int64_t)Ip * p.N + (dp - Ip)], 1);
                 }
             }
+            if (two && d + 1 >= kRing) {
+                const int dp = d + 1 - kRing;
+                if (slot2 < diag_leaves(p.M, p.N, dp)) {
+                    const int Ip = leaf_lo(p, dp) + slot2;
+                    wait_flag(p, &p.setup[(int64_t)Ip * p.N + (dp - Ip)], 1);
+                }
+            }
             acquire_agent();
             vm_wait_all();
         }
+        // output exponents: rows (A columns) and, for o^T, columns (rows of C)
+        const int64_t ca = kind == 0 ? i0 : j0, cb = kind == 0 ? j0 : i0;
+        if (tid < kB) sm.pc.fr[tid] = (kind == 0 ? p.fexo : p.fexi)[ca + tid];
+        else if (tid < 3 * kB) sm.pc.fc[tid - kB] = kind == 0 ? 0 : p.exc[min<int64_t>(cb + tid - kB, p.Mp - 1)];
         __syncthreads();
-        const int64_t i0 = (int64_t)I * kB, j0 = (int64_t)J * kB;
-        const int R = (int)min<int64_t>(kB, p.m - i0), Cc = (int)min<int64_t>(kB, p.n - j0);
-        const int64_t k0 = (int64_t)kb0 * kB, K = (int64_t)(kb1 - kb0) * kB;
-        f32x16 acc;
+        f32x16 acc[2];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-        const bool active = tid < kThreads;  // the other waves only join the barriers
-        // p[ii][jj] = sum_k L_O[k][i0+ii] D[k][j0+jj];  o^T[jj][ii] = sum_l L_I[l][j0+jj] C^T[l][i0+ii]
-        const float* A = kind == 0 ? p.LO + k0 * p.ldlo + i0 : p.LI + k0 * p.ldli + j0;
-        const float* Bm = kind == 0 ? p.delta + k0 * p.ldd + j0 : p.ct + k0 * p.m + i0;
-        const int64_t lda = kind == 0 ? p.ldlo : p.ldli, ldb = kind == 0 ? p.ldd : p.m;
-        const int ra_lim = kind == 0 ? R : Cc, cb_lim = kind == 0 ? Cc : R;
-        const bool whole = R == kB && Cc == kB && ((lda | ldb) & 3) == 0 &&
-                           ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(Bm)) & 15) == 0;
-        if (whole) far_gemm_ring(A, lda, Bm, ldb, K, acc, sm.ring, tid);
-        else tile_gemm_f32<kFarKT>(A, lda, ra_lim, Bm, ldb, cb_lim, K, acc, sm.staged, active, tid);
-        if (active) {
-            float* part = part_ptr(p, d, slot, kind, c);
-            const int cc = acc32_col(tid);
+        for (int v = 0; v < 16; ++v) acc[0][v] = acc[1][v] = 0.0f;
+        const f16x8* A = kind == 0 ? p.lop : p.lip;
+        const f16x8* Bp = kind == 0 ? p.dpl : p.cpl;
+        const int64_t ngA = (kind == 0 ? p.Mp : p.Np) / 8, ncA = kind == 0 ? p.Mp : p.Np;
+        const int64_t ngB = ngA, ncB = kind == 0 ? p.Np : p.Mp;
+        if (two) far_pieces<2>(A, ngA, ncA, ca, Bp, ngB, ncB, cb, 8 * kb0, 8 * kb1, acc, sm.pc, tid);
+        else far_pieces<1>(A, ngA, ncA, ca, Bp, ngB, ncB, cb, 8 * kb0, 8 * kb1, acc, sm.pc, tid);
+        if (tid < kThreads) {
+            const int w = tid >> 6, lane = tid & 63;
+            const int tgt = two ? (w & 1) : 0;
+            float* part = part_ptr(p, tgt ? d + 1 : d, tgt ? slot2 : slot, kind, c);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) st_coherent(&part[acc32_row(v, tid) * kB + cc], acc[v]);
+            for (int b = 0; b < (two ? 2 : 1); ++b) {
+                const int col = two ? 32 * b + (lane & 31) : 32 * (w & 1) + (lane & 31);
+                const int ec = sm.pc.fc[kB * tgt + col];
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = (w >> 1) * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    st_coherent(&part[row * kB + col], ldexpf(acc[b][v], -(sm.pc.fr[row] + ec)));
+                }
+            }
         }
         vm_wait_all();  // every wave's device-coherent partial stores have completed
         __syncthreads();
     }
     if (tid == 0) {
         __hip_atomic_fetch_add(&p.fardone[(int64_t)I * p.N + J], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (two)
+            __hip_atomic_fetch_add(&p.fardone[(int64_t)I2 * p.N + J2], 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -466,6 +664,8 @@ struct LeafSmem {
     float li[kNew][kB];    // li[e][j] = L_I[j-1-e][j]: the finaliser's terms
     uint8_t code[kB][kB + 4];
     float DI[kB];
+    int exr[kB];  // eD of the leaf's rows
+    int exq[kB];  // eC of the leaf's rows
     double red[kLeafWaves];
     int red_i[kLeafWaves];
 };
@@ -611,25 +811,27 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
     const int lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int64_t leaf = (int64_t)I * p.N + J;
-    const int nch = p.nchd[d];
-    const bool far_p = p.LO && I > 2, far_o = p.LI && J > 2;  // far-field partials (blocks <= I-3, J-3)
-    const bool two_p = p.LO && I > 1, two_o = p.LI && J > 1;  // the blocks two back
+    // this leaf's far fields come from the pair that starts at (I, J) or at the leaf before
+    // it in its row (p) or column (o), on this diagonal or the one before
+    const int dp_src = (J & 1) ? d - 1 : d, do_src = (I & 1) ? d - 1 : d;
+    const int nch_p = dp_src >= kFarMin ? p.nchd[dp_src] : 0;
+    const int nch_o = do_src >= kFarMin ? p.nchd[do_src] : 0;
+    const bool far_p = p.LO && I > 3, far_o = p.LI && J > 3;  // far-field partials (blocks <= I-4, J-4)
+    const bool b2_p = p.LO && I > 1, b2_o = p.LI && J > 1;    // the blocks two back
+    const bool b3_p = p.LO && I > 2, b3_o = p.LI && J > 2;    // the blocks three back
     const bool adj_p = p.LO && I > 0, adj_o = p.LI && J > 0;  // the adjacent blocks (handed over)
     for (int e = t; e < kNew * kB; e += kLeafThreads) sm.li[e / kB][e % kB] = 0.0f;  // no L_I[j-1-e][j] for j <= e
     __syncthreads();
     constexpr int kPer = (kB * kB + kLeafThreads - 1) / kLeafThreads;
     // ---- A: static inputs, every load of the thread in flight at once
-    //   DT  <- L_O[i0-128+k][i0+c]  pt <- L_I[j0-128+k][j0+c]    (blocks two back: staging)
     //   wst <- W*[i0+k][j0+c]       li <- the first kNew superdiagonals of L_I
     {
-        float v1[kPer], v3[kPer], v5[kPer], v6[kPer];
+        float v5[kPer], v6[kPer];
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
             const int e = t + u * kLeafThreads;
             const int k = e >> 6, c = e & 63;
             const bool in = e < kB * kB;
-            v1[u] = (in && two_p && c < R) ? p.LO[(i0 - 2 * kB + k) * p.ldlo + i0 + c] : 0.0f;
-            v3[u] = (in && two_o && c < Cc) ? p.LI[(j0 - 2 * kB + k) * p.ldli + j0 + c] : 0.0f;
             v5[u] = (in && k < R && c < Cc) ? p.W[(i0 + k) * p.ldw + j0 + c] : 0.0f;
             v6[u] = (in && p.LI && c - k >= 1 && c - k <= kNew && c < Cc) ? p.LI[(j0 + k) * p.ldli + j0 + c] : 0.0f;
         }
@@ -638,18 +840,16 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
             const int e = t + u * kLeafThreads;
             if (e < kB * kB) {
                 const int k = e >> 6, c = e & 63;
-                sm.DT[k][c] = v1[u];
-                sm.pt[k][c] = v3[u];
                 sm.wst[k][c] = v5[u];
                 if (c - k >= 1 && c - k <= kNew) sm.li[c - k - 1][c] = v6[u];
             }
         }
     }
-    // ---- B: far fields from three or more blocks back: once their tasks are done,
+    // ---- B: far fields from four or more blocks back: once their tasks are done,
     // the K-chunk partials are summed in chunk order into registers (every load
     // issued first; absent chunks read a valid address and are replaced by zero)
     if (t == 0) {
-        if (d >= 3) wait_flag(p, &p.fardone[leaf], 2 * nch);
+        if (nch_p + nch_o > 0) wait_flag(p, &p.fardone[leaf], nch_p + nch_o);
         acquire_agent();
         vm_wait_all();
     }
@@ -659,6 +859,7 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
     f32x4 pvs[kG], ovs[kG];  // p and o^T, four consecutive entries per group
     {
         const bool any = far_p || far_o;
+        const int lp = nch_p > 0 ? nch_p - 1 : 0, lo_ = nch_o > 0 ? nch_o - 1 : 0;
         f32x4 xp[kG][kNch], xo[kG][kNch];
         if (any) {
 #pragma unroll
@@ -666,9 +867,8 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
                 const int g = min(t + u * kLeafThreads, kB * kB / 4 - 1);
 #pragma unroll
                 for (int c = 0; c < kNch; ++c) {
-                    const int cc = min(c, nch - 1);
-                    xp[u][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, d, slot, 0, cc) + 4 * g);
-                    xo[u][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, d, slot, 1, cc) + 4 * g);
+                    xp[u][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, d, slot, 0, min(c, lp)) + 4 * g);
+                    xo[u][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, d, slot, 1, min(c, lo_)) + 4 * g);
                 }
             }
         }
@@ -680,9 +880,8 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
                     const int gg = min(t + uu * kLeafThreads, kB * kB / 4 - 1);
 #pragma unroll
                     for (int c = 0; c < kNch; ++c) {
-                        const int cc = min(c, nch - 1);
-                        xp[uu][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, d, slot, 0, cc) + 4 * gg);
-                        xo[uu][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, d, slot, 1, cc) + 4 * gg);
+                        xp[uu][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, d, slot, 0, min(c, lp)) + 4 * gg);
+                        xo[uu][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, d, slot, 1, min(c, lo_)) + 4 * gg);
                     }
                 }
             }
@@ -690,7 +889,7 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
             if (any) {
 #pragma unroll
                 for (int c = 0; c < kNch; ++c) {
-                    const bool up = far_p && c < nch, uo = far_o && c < nch;
+                    const bool up = far_p && c < nch_p, uo = far_o && c < nch_o;
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         pv[k] += up ? xp[u][c][k] : 0.0f;
@@ -705,45 +904,54 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
     // the partials are read (their ring slot may be reused)
     __syncthreads();
     if (t == 0) st_flag(&p.setup[leaf], 1);
-    // ---- the leaves two blocks up and to the left: once they are done, their
-    // blocks are multiplied (K = 64)
+    // ---- the leaves two and three blocks up and to the left: once the ones two back
+    // are done (the ones three back finished before them), their blocks are multiplied
+    // (K = 64 each): p += L_O[back, this]^T D[back, J], o^T += L_I[back, this]^T C^T[back, I]
     if (t == 0) {
-        if (two_p) wait_flag(p, &p.prog_d[leaf - 2 * (int64_t)p.N], kStrips);
-        if (two_o) wait_flag(p, &p.prog_c[leaf - 2], kStrips);
+        if (b2_p) wait_flag(p, &p.prog_d[leaf - 2 * (int64_t)p.N], kStrips);
+        if (b2_o) wait_flag(p, &p.prog_c[leaf - 2], kStrips);
         acquire_agent();
         vm_wait_all();
     }
     __syncthreads();
-    //   Gs <- D[i0-128+k][j0+c]     bt <- C^T[j0-128+k][i0+c]     (staging)
-    {
-        float v2[kPer], v4[kPer];
+    f32x16 ap, ao;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) ap[v] = ao[v] = 0.0f;
+#pragma unroll 1
+    for (int back = 2; back <= 3; ++back) {
+        const bool bp = back == 2 ? b2_p : b3_p, bo = back == 2 ? b2_o : b3_o;
+        //   DT <- L_O[i0-64b+k][i0+c]   Gs <- D[i0-64b+k][j0+c]
+        //   pt <- L_I[j0-64b+k][j0+c]   bt <- C^T[j0-64b+k][i0+c]     (staging)
+        float v1[kPer], v2[kPer], v3[kPer], v4[kPer];
+        const int64_t ib = i0 - back * kB, jb = j0 - back * kB;
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
             const int e = t + u * kLeafThreads;
             const int k = e >> 6, c = e & 63;
             const bool in = e < kB * kB;
-            v2[u] = (in && two_p && c < Cc) ? p.delta[(i0 - 2 * kB + k) * p.ldd + j0 + c] : 0.0f;
-            v4[u] = (in && two_o && c < R) ? p.ct[(j0 - 2 * kB + k) * p.m + i0 + c] : 0.0f;
+            v1[u] = (in && bp && c < R) ? p.LO[(ib + k) * p.ldlo + i0 + c] : 0.0f;
+            v2[u] = (in && bp && c < Cc) ? p.delta[(ib + k) * p.ldd + j0 + c] : 0.0f;
+            v3[u] = (in && bo && c < Cc) ? p.LI[(jb + k) * p.ldli + j0 + c] : 0.0f;
+            v4[u] = (in && bo && c < R) ? p.ct[(jb + k) * p.m + i0 + c] : 0.0f;
         }
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
             const int e = t + u * kLeafThreads;
             if (e < kB * kB) {
                 const int k = e >> 6, c = e & 63;
+                sm.DT[k][c] = v1[u];
                 sm.Gs[k][c] = v2[u];
+                sm.pt[k][c] = v3[u];
                 sm.bt[k][c] = v4[u];
             }
         }
+        __syncthreads();
+        if (w < 4) {
+            if (bp) adj_gemm(&sm.DT[0][0], kTs, &sm.Gs[0][0], kTs, ap, t);
+            if (bo) adj_gemm(&sm.pt[0][0], kTs, &sm.bt[0][0], kTs, ao, t);
+        }
+        __syncthreads();
     }
-    __syncthreads();
-    f32x16 ap, ao;  // products with the blocks two back: p += L_O^T D, o^T += L_I^T C^T
-#pragma unroll
-    for (int v = 0; v < 16; ++v) ap[v] = ao[v] = 0.0f;
-    if (w < 4) {
-        if (two_p) adj_gemm(&sm.DT[0][0], kTs, &sm.Gs[0][0], kTs, ap, t);
-        if (two_o) adj_gemm(&sm.pt[0][0], kTs, &sm.bt[0][0], kTs, ao, t);
-    }
-    __syncthreads();
     // ---- C: p = partials + ap, o = partials + ao, then W* added to o; D, g and
     // the codes cleared (the staging is consumed)
 #pragma unroll
@@ -1057,6 +1265,60 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
         handover_publish(p, sm, hcol, kStrips - 1, i0, j0, R, Cc, lane);
         handover_flag(p, hcol, leaf, kStrips, lane);
     }
+    // ---- the pieces of D (for the column far fields of the leaves four or more below)
+    // and of C (for the row far fields of the leaves four or more to the right); the
+    // entries outside the matrix are zero
+    {
+        const bool wd = p.LO && I + 4 < p.M, wc = p.LI && J + 4 < p.N;
+        if (wd || wc) {
+            if (t < kB) {
+                sm.exr[t] = i0 + t < p.m ? p.exd[i0 + t] : 0;
+                sm.exq[t] = p.exc[i0 + t];
+            }
+            __syncthreads();
+            for (int e = t; e < 8 * kB; e += kLeafThreads) {
+                const int gl = e >> 6, x = e & 63;  // 8-entry group gl along the contraction, column x
+                if (wd) {  // D[i0 + 8 gl + q][j0 + x] = DT[x][8 gl + q], row q scaled by 2^eD
+                    const f32x4 v0 = lds4(&sm.DT[x][8 * gl]), v1 = lds4(&sm.DT[x][8 * gl + 4]);
+                    uint32_t pk[2][4];
+#pragma unroll
+                    for (int q = 0; q < 8; q += 2) {
+                        uint32_t h0, l0, h1, l1;
+                        split2_value(q < 4 ? v0[q] : v1[q - 4], sm.exr[8 * gl + q], h0, l0);
+                        split2_value(q < 4 ? v0[q + 1] : v1[q - 3], sm.exr[8 * gl + q + 1], h1, l1);
+                        pk[0][q >> 1] = h0 | (h1 << 16);
+                        pk[1][q >> 1] = l0 | (l1 << 16);
+                    }
+#pragma unroll
+                    for (int pc = 0; pc < 2; ++pc)
+                        st_coherent16(&p.dpl[((int64_t)pc * (p.Mp / 8) + 8 * I + gl) * p.Np + j0 + x], pk[pc]);
+                }
+                if (wc) {  // C[i0 + x][j0 + 8 gl + q] = Gs[x][8 gl + q], scaled by 2^eC of row x
+                    const f32x4 v0 = lds4(&sm.Gs[x][8 * gl]), v1 = lds4(&sm.Gs[x][8 * gl + 4]);
+                    const int ex = sm.exq[x];
+                    uint32_t pk[2][4];
+#pragma unroll
+                    for (int q = 0; q < 8; q += 2) {
+                        uint32_t h0, l0, h1, l1;
+                        split2_value(q < 4 ? v0[q] : v1[q - 4], ex, h0, l0);
+                        split2_value(q < 4 ? v0[q + 1] : v1[q - 3], ex, h1, l1);
+                        pk[0][q >> 1] = h0 | (h1 << 16);
+                        pk[1][q >> 1] = l0 | (l1 << 16);
+                    }
+#pragma unroll
+                    for (int pc = 0; pc < 2; ++pc)
+                        st_coherent16(&p.cpl[((int64_t)pc * (p.Np / 8) + 8 * J + gl) * p.Mp + i0 + x], pk[pc]);
+                }
+            }
+            vm_wait_all();  // this wave's piece stores have completed
+        }
+        __syncthreads();
+        if (t == 0) {
+            if (I > 0) wait_flag(p, &p.pdone[leaf - p.N], 1);
+            if (J > 0) wait_flag(p, &p.pdone[leaf - 1], 1);
+            st_flag(&p.pdone[leaf], 1);
+        }
+    }
     // loss partial: sum of D_O,i D_I,j eta_ij^2 over the leaf, in fp64
     if (p.want_loss) {
         for (int e = t; e < kB * kB; e += kLeafThreads) {
@@ -1182,7 +1444,10 @@ __global__ __launch_bounds__(kThreads) void k_solve_finish(const double* leaf_lo
 namespace {
 struct Layout {
     int M, N, maxleaf, ND;
-    size_t ct, delta, parts, leaf_loss, leaf_clamp, info, sched, flags, seg, nchd, total;
+    int64_t Mp, Np;
+    int nkcO, nkcI;  // pre-pass row chunks of L_O, L_I
+    size_t ct, delta, parts, leaf_loss, leaf_clamp, info, sched, flags, seg, nchd;
+    size_t lop, lip, dpl, cpl, bd, exd, exc, fexo, fexi, mxO, sbO, mxI, total;
 };
 
 Layout layout(int64_t m, int64_t n) {
@@ -1191,7 +1456,12 @@ Layout layout(int64_t m, int64_t n) {
     L.N = (int)((n + kB - 1) / kB);
     L.maxleaf = std::min(L.M, L.N);
     L.ND = L.M + L.N - 1;
+    L.Mp = (int64_t)L.M * kB;
+    L.Np = (int64_t)L.N * kB;
+    L.nkcO = (int)((m + kPrepRows - 1) / kPrepRows);
+    L.nkcI = (int)((n + kPrepRows - 1) / kPrepRows);
     const size_t nl = (size_t)L.M * L.N;
+    const size_t Mp = (size_t)L.Mp, Np = (size_t)L.Np;
     size_t o = 0;
     L.ct = o;
     o += align256(sizeof(float) * (size_t)m * (size_t)n);
@@ -1207,12 +1477,37 @@ Layout layout(int64_t m, int64_t n) {
     o += 256;
     L.sched = o;  // ticket, abort
     o += 256;
-    L.flags = o;  // prog_d, prog_c, setup, fardone
-    o += align256(sizeof(int) * 4 * nl);
+    L.flags = o;  // prog_d, prog_c, setup, fardone, pdone
+    o += align256(sizeof(int) * 5 * nl);
     L.seg = o;
     o += align256(sizeof(int) * ((size_t)L.ND + 1));
     L.nchd = o;
     o += align256(sizeof(int) * (size_t)L.ND);
+    // piece planes: two fp16 values (4 bytes) per element
+    L.lop = o;
+    o += align256(4 * Mp * Mp);
+    L.lip = o;
+    o += align256(4 * Np * Np);
+    L.dpl = o;
+    o += align256(4 * Mp * Np);
+    L.cpl = o;
+    o += align256(4 * Mp * Np);
+    L.bd = o;
+    o += align256(sizeof(float) * Mp);
+    L.exd = o;
+    o += align256(sizeof(int) * Mp);
+    L.exc = o;
+    o += align256(sizeof(int) * Mp);
+    L.fexo = o;
+    o += align256(sizeof(int) * Mp);
+    L.fexi = o;
+    o += align256(sizeof(int) * Np);
+    L.mxO = o;
+    o += align256(sizeof(float) * (size_t)L.nkcO * Mp);
+    L.sbO = o;
+    o += align256(sizeof(float) * (size_t)L.nkcO * Mp);
+    L.mxI = o;
+    o += align256(sizeof(float) * (size_t)L.nkcI * Np);
     L.total = o;
     return L;
 }
@@ -1284,6 +1579,7 @@ int run_solve(const SolveArgs& a, void* ws, hipStream_t stream) {
     p.prog_c = p.prog_d + nl;
     p.setup = p.prog_c + nl;
     p.fardone = p.setup + nl;
+    p.pdone = p.fardone + nl;
     p.seg = (int*)(base + L.seg);
     p.nchd = (int*)(base + L.nchd);
     p.ND = L.ND;
@@ -1295,11 +1591,50 @@ int run_solve(const SolveArgs& a, void* ws, hipStream_t stream) {
         if (v > 0) limit_us = (uint64_t)v;
     }
     p.spin_limit = (uint64_t)di.clock_khz * limit_us / 1000ull;
+    p.Mp = L.Mp;
+    p.Np = L.Np;
+    p.lop = (const f16x8*)(base + L.lop);
+    p.lip = (const f16x8*)(base + L.lip);
+    p.dpl = (f16x8*)(base + L.dpl);
+    p.cpl = (f16x8*)(base + L.cpl);
+    float* bd = (float*)(base + L.bd);
+    int* exd = (int*)(base + L.exd);
+    int* exc = (int*)(base + L.exc);
+    int* fexo = (int*)(base + L.fexo);
+    int* fexi = (int*)(base + L.fexi);
+    p.exd = exd;
+    p.exc = exc;
+    p.fexo = fexo;
+    p.fexi = fexi;
 
     const int init_blocks = (int)std::min<size_t>(1024, std::max<size_t>(1, (nl + kThreads - 1) / kThreads));
     hipLaunchKernelGGL(k_solve_init, dim3((unsigned)init_blocks), dim3(kThreads), 0, stream, p);
     hipLaunchKernelGGL(k_scales, dim3((unsigned)a.m), dim3(kThreads), 0, stream, a.W, a.n, a.ldw,
-                       a.bits, a.row_scale, a.scales, p.info);
+                       a.bits, a.row_scale, a.scales, bd, exd, p.info);
+    // the piece planes of the factors and the exponents of C's rows
+    float* mxO = (float*)(base + L.mxO);
+    float* sbO = (float*)(base + L.sbO);
+    float* mxI = (float*)(base + L.mxI);
+    const unsigned eg_o = (unsigned)((L.Mp + kThreads - 1) / kThreads), eg_i = (unsigned)((L.Np + kThreads - 1) / kThreads);
+    if (a.LO) {
+        hipLaunchKernelGGL(k_lstats, dim3((unsigned)L.M, (unsigned)L.nkcO), dim3(kThreads), 0, stream, a.LO,
+                           a.ldlo, a.m, exd, bd, L.Mp, mxO, sbO);
+        hipLaunchKernelGGL(k_lexp, dim3(eg_o), dim3(kThreads), 0, stream, mxO, sbO, L.nkcO, L.Mp, a.m, bd, fexo,
+                           exc);
+        hipLaunchKernelGGL(k_lsplit, dim3((unsigned)L.M, (unsigned)L.nkcO), dim3(kThreads), 0, stream, a.LO,
+                           a.ldlo, a.m, exd, fexo, L.Mp, L.Mp / 8, (f16x8*)(base + L.lop));
+    } else {  // C = D
+        hipLaunchKernelGGL(k_lexp, dim3(eg_o), dim3(kThreads), 0, stream, nullptr, nullptr, 0, L.Mp, a.m, bd,
+                           nullptr, exc);
+    }
+    if (a.LI) {
+        hipLaunchKernelGGL(k_lstats, dim3((unsigned)L.N, (unsigned)L.nkcI), dim3(kThreads), 0, stream, a.LI,
+                           a.ldli, a.n, nullptr, nullptr, L.Np, mxI, nullptr);
+        hipLaunchKernelGGL(k_lexp, dim3(eg_i), dim3(kThreads), 0, stream, mxI, nullptr, L.nkcI, L.Np, a.n, nullptr,
+                           fexi, nullptr);
+        hipLaunchKernelGGL(k_lsplit, dim3((unsigned)L.N, (unsigned)L.nkcI), dim3(kThreads), 0, stream, a.LI,
+                           a.ldli, a.n, nullptr, fexi, L.Np, L.Np / 8, (f16x8*)(base + L.lip));
+    }
     const int grid = (int)std::min<int64_t>(di.cus, ntask);
     hipLaunchKernelGGL(k_solve_run, dim3((unsigned)grid), dim3(kLeafThreads), 0, stream, p);
     hipLaunchKernelGGL(k_solve_finish, dim3(1), dim3(kThreads), 0, stream, p.leaf_loss,

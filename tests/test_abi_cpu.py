@@ -245,4 +245,5 @@ def test_solve_noalloc_rejects_bad_arguments_and_oversize_shapes(lib):
     assert lib.bakron_solve_workspace_bytes(4096, 4096) > bk.NOALLOC_SCRATCH_BYTES
     assert f(*args(4096, 4096, ctypes.byref(q))) == 3
     assert lib.bakron_solve_workspace_bytes(2048, 2048) <= bk.NOALLOC_SCRATCH_BYTES
-    assert lib.bakron_solve_workspace_bytes(1024, 4096) <= bk.NOALLOC_SCRATCH_BYTES
+    assert lib.bakron_solve_workspace_bytes(1024, 3072) <= bk.NOALLOC_SCRATCH_BYTES
+    assert lib.bakron_solve_workspace_bytes(1024, 4096) > bk.NOALLOC_SCRATCH_BYTES
