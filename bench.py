@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_F16_MFMA_TFLOPS = 2500.0
-PIECE_PRODUCTS = 3  # fp16 piece products per fp32 product in the Hessian
+PIECE_PRODUCTS = 3  # fp16 piece products per fp32 product (Hessian, solve far field)
 PEAK_FP64_MFMA_TFLOPS = 78.6
 CAL_BYTES = 256 << 20
 
@@ -337,24 +337,27 @@ def main():
                     achieved=fp32_equiv, peak=PEAK_FP32_MFMA_TFLOPS, flops_per_call=syrk_flops)
     roof["frac"] = roof["achieved"] / roof["peak"]
 
-    # The solve (one persistent launch, k_solve_run, plus three small kernels), priced
-    # three ways: its far-field GEMMs against the fp32 MFMA peak (the minimum
-    # mn(m+n) flops of the two triangular long-K products), its base case against
-    # HBM (the accumulator form's algorithmic traffic, 25 B per weight: W* 4, the
-    # two far-field offsets 8, D 4, C 4, the code 1, the diagonal factor blocks
+    # The solve (one persistent launch, k_solve_run, plus small kernels), priced
+    # three ways: its far-field GEMMs against the fp16 MFMA peak (the minimum
+    # mn(m+n) flops of the two triangular long-K products, each fp32 product done
+    # as three fp16 piece products), its base case against HBM (the accumulator
+    # form's algorithmic traffic, 33 B per weight: W* 4, the two far-field offsets 8,
+    # D 4, C 4, the pieces of D and C 8, the code 1, the diagonal factor blocks
     # about 4), and its time per step of the dependent chain the schedule runs
     # (64 x 64 leaves, a leaf-diagonal lag of 94 steps: (M + N - 2) 94 + 127 steps)
     # next to the chain of the rule itself (m + n - 1 anti-diagonals).
     solve_s = ph["solve"] * 1e-3
     M, N = (m + 63) // 64, (n + 63) // 64
     chain = (M + N - 2) * 94 + 127
-    base_bytes = 25.0 * m * n
+    base_bytes = 33.0 * m * n
     roof_solve = {
         "kernel": "k_solve_run (+ k_solve_init, k_scales, k_solve_finish)",
         "time_ms": ph["solve"],
-        "far_field": {"bound": "mfma", "flops": solve_flops, "achieved": solve_flops / solve_s / 1e12,
-                      "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                      "frac": solve_flops / solve_s / 1e12 / PEAK_FP32_MFMA_TFLOPS},
+        "far_field": {"bound": "mfma", "flops": PIECE_PRODUCTS * solve_flops,
+                      "achieved": PIECE_PRODUCTS * solve_flops / solve_s / 1e12,
+                      "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                      "frac": PIECE_PRODUCTS * solve_flops / solve_s / 1e12 / PEAK_F16_MFMA_TFLOPS,
+                      "fp32_equiv_tflops": solve_flops / solve_s / 1e12},
         "base_case": {"bound": "hbm", "bytes": base_bytes, "achieved": base_bytes / solve_s / 1e9,
                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": base_bytes / solve_s / 1e9 / PEAK_HBM_GBS,
                       "traffic": traffic_bytes("solve", args.workload)},
@@ -378,7 +381,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "dtype_detail": "Hessian: fp32 products as three fp16 piece products of power-of-two-scaled "
-                        "columns, fp32 accumulate; LDL: fp64; solve: fp32",
+                        "columns, fp32 accumulate; LDL: fp64; solve: fp32 (far field: three fp16 piece products "
+                        "per fp32 product, fp32 accumulate)",
         "data": "synthetic",
         "config": {"workload": "%s, %d-bit %s" % (WORKLOAD_LABEL[args.workload], args.bits,
                                                   args.rounding),

@@ -13,10 +13,12 @@
 //   p = sum_{I'<I} L_O[R_I', R_I]^T D[R_I', S_J]   (column far field)
 //   o = sum_{J'<J} C[R_I, S_J'] L_I[S_J', S_J]      (row far field)
 // is split by how far back the source block lies:
-//  * three or more blocks back: MFMA GEMMs over K, split into partials, run by
-//    other workgroups once those leaves are done (O(mn(m+n)) flops in all, the
+//  * four or more blocks back: MFMA GEMMs over K (fp16 piece products), split
+//    into partials, run by other workgroups once those leaves are done, two
+//    leaves that share a factor panel at a time (O(mn(m+n)) flops in all, the
 //    bound of the BaKron Abstract);
-//  * two blocks back: multiplied by the leaf's own workgroup before its sweep;
+//  * two and three blocks back: multiplied by the leaf's own workgroup before
+//    its sweep (fp32 MFMA);
 //  * the adjacent block: handed over 16 columns (rows) at a time while the
 //    neighbour is still sweeping, and multiplied as it arrives.
 // The leaf then runs its in-leaf sums as a 127-step anti-diagonal wavefront.
