@@ -423,6 +423,57 @@ struct PieceRing {
     int fc[2 * kB];  // exponent of each output column (B column)
 };
 
+__device__ __forceinline__ uint32_t lds_addr(const void* q) {
+    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)q);
+}
+
+// The MFMA operands of one stage, read in one block that also waits for them. Left
+// to the compiler, these reads of the ring, whose other slots direct-to-LDS loads
+// are still filling, were preceded by a wait for every load in flight (vmcnt(0)),
+// which undid the prefetch; the waits for the stage's own loads are the barrier's.
+// a: the lane's A unit of group kh (fa[s][pc]: group 2 s + kh, piece pc); b: its B
+// unit (fb[s][pc][t]: group 2 s + kh, piece pc, target t at +32 t columns).
+template <int NT>
+__device__ __forceinline__ void stage_reads(uint32_t a, uint32_t b, f16x8 (&fa)[2][2], f16x8 (&fb)[2][2][2]) {
+    // offsets: a[pc][g][c] at 4096 pc + 1024 g + 16 c; b[pc][g][c] at 8192 pc + 2048 g + 16 c
+    if constexpr (NT == 2) {
+        asm volatile(
+            "ds_read_b128 %0, %12\n\t"
+            "ds_read_b128 %1, %12 offset:4096\n\t"
+            "ds_read_b128 %2, %12 offset:2048\n\t"
+            "ds_read_b128 %3, %12 offset:6144\n\t"
+            "ds_read_b128 %4, %13\n\t"
+            "ds_read_b128 %5, %13 offset:512\n\t"
+            "ds_read_b128 %6, %13 offset:8192\n\t"
+            "ds_read_b128 %7, %13 offset:8704\n\t"
+            "ds_read_b128 %8, %13 offset:4096\n\t"
+            "ds_read_b128 %9, %13 offset:4608\n\t"
+            "ds_read_b128 %10, %13 offset:12288\n\t"
+            "ds_read_b128 %11, %13 offset:12800\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(fa[0][0]), "=&v"(fa[0][1]), "=&v"(fa[1][0]), "=&v"(fa[1][1]), "=&v"(fb[0][0][0]),
+              "=&v"(fb[0][0][1]), "=&v"(fb[0][1][0]), "=&v"(fb[0][1][1]), "=&v"(fb[1][0][0]), "=&v"(fb[1][0][1]),
+              "=&v"(fb[1][1][0]), "=&v"(fb[1][1][1])
+            : "v"(a), "v"(b)
+            : "memory");
+    } else {
+        asm volatile(
+            "ds_read_b128 %0, %8\n\t"
+            "ds_read_b128 %1, %8 offset:4096\n\t"
+            "ds_read_b128 %2, %8 offset:2048\n\t"
+            "ds_read_b128 %3, %8 offset:6144\n\t"
+            "ds_read_b128 %4, %9\n\t"
+            "ds_read_b128 %5, %9 offset:8192\n\t"
+            "ds_read_b128 %6, %9 offset:4096\n\t"
+            "ds_read_b128 %7, %9 offset:12288\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(fa[0][0]), "=&v"(fa[0][1]), "=&v"(fa[1][0]), "=&v"(fa[1][1]), "=&v"(fb[0][0][0]),
+              "=&v"(fb[0][1][0]), "=&v"(fb[1][0][0]), "=&v"(fb[1][1][0])
+            : "v"(a), "v"(b)
+            : "memory");
+    }
+}
+
 // acc[t] += A^T B over groups [g0, g1) (whole stages) for NT targets: A columns
 // ca .. ca + 63 of plane A (ngA groups, ncA columns), B columns cb .. cb + 64 NT - 1
 // of plane B. Waves 0-3 load and compute (wave w: output rows 32 (w >> 1) .., target
@@ -470,31 +521,16 @@ __device__ __forceinline__ void far_pieces(const f16x8* __restrict__ A, int64_t 
         if (!active) continue;
         if (it + kPieceNS - 1 < ns) issue(it + kPieceNS - 1);
         const PieceStage& st = sm.s[it % kPieceNS];
-        f16x8 fa[2][2], fb[2][2][NT];
+        f16x8 fa[2][2], fb[2][2][2];  // [16-k step][piece](, [target])
+        stage_reads<NT>(lds_addr(&st.a[0][kh][ar]), lds_addr(&st.b[0][kh][bc]), fa, fb);
 #pragma unroll
-        for (int pc = 0; pc < 2; ++pc) {
-            fa[0][pc] = st.a[pc][kh][ar];
-#pragma unroll
-            for (int t = 0; t < NT; ++t) fb[0][pc][t] = st.b[pc][kh][bc + 32 * t];
-        }
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {  // two 16-k steps
-            if (s2 == 0) {
-#pragma unroll
-                for (int pc = 0; pc < 2; ++pc) {
-                    fa[1][pc] = st.a[pc][2 + kh][ar];
-#pragma unroll
-                    for (int t = 0; t < NT; ++t) fb[1][pc][t] = st.b[pc][2 + kh][bc + 32 * t];
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);  // the next step's reads go out before these MFMAs
+        for (int s2 = 0; s2 < 2; ++s2)  // two 16-k steps
 #pragma unroll
             for (int u = 0; u < 3; ++u)
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
                     acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[s2][kPa[u]], fb[s2][kPb[u]][t], acc[t], 0, 0,
                                                                     0);
-        }
     }
 }
 
