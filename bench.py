@@ -306,10 +306,12 @@ def main():
     elif args.hessian == "sketch_a":
         # the whole phase in fp32-equivalent flops: the SYRKs (the initial X^T X,
         # then two per iteration, T d^2 each) and the token weights' quadratic
-        # forms (2 T d^2 per factor and iteration, fp32 MFMA)
+        # forms (T d^2 each with the symmetry of H, fp32 MFMA): one over H_I per
+        # iteration, one over H_O from the second on (the first weights the
+        # gradients with H_O = I)
         syrk_ms = float(np.mean(ev["hess_sketch_a"]))
         syrk_flops = float(T) * (n * n * (1 + args.iters) + m * m * args.iters
-                                 + 2.0 * args.iters * (n * n + m * m))
+                                 + args.iters * n * n + (args.iters - 1) * m * m)
     else:
         syrk_ms = float(np.mean(ev["hess_I"] + ev["hess_O"]))
         # algorithmic fp32 flops per call, averaged over the two calls: T d^2 per

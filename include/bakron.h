@@ -148,8 +148,10 @@ int bakron_hessian_accum_t(const float* X, int64_t T, int64_t d, int64_t ldx, fl
  *
  * bakron_token_weights: w[t] = y_t H y_t^T / ||H||_F^2 for the rows y_t of Y
  *   (T x d, ldy >= d), H d x d symmetric (ldh >= d); H == NULL means H = I,
- *   w[t] = ||y_t||^2 / d. The quadratic forms run as fp32 MFMA tile GEMMs and
- *   are summed in a fixed order; ||H||_F^2 in fp64. ws: with H given, at least
+ *   w[t] = ||y_t||^2 / d. The quadratic forms read H's lower triangle and
+ *   diagonal only (y H y^T = sum of the diagonal blocks' forms plus twice those
+ *   of the blocks below them), as fp32 MFMA tile GEMMs summed in a fixed order;
+ *   ||H||_F^2 reads all of H, in fp64. ws: with H given, at least
  *   bakron_token_weights_workspace_bytes(T, d) (Y transposed, d T floats).
  * bakron_hessian_accum_w: H <- beta H + alpha sum_t w[t] x_t^T x_t for w >= 0
  *   (negative weights count as 0), X as in bakron_hessian_accum, on the

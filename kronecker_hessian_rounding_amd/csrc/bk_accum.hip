@@ -536,12 +536,31 @@ __global__ __launch_bounds__(kThreads) void k_colmax_t(const float* __restrict__
 
 // e_c = 15 - E for a column maximum f 2^E (f in [1/2, 1)), so the scaled column's
 // largest magnitude lies in [2^14, 2^15); 0 for a zero or non-finite maximum.
+// Workgroup x reduces columns 16 x .. 16 x + 15: thread (c, r) takes chunks r, r + 16,
+// .. of column c (every load in flight at once), then the 16 partial maxima of a
+// column are combined through LDS.
+constexpr int kExpCols = 16;
 __global__ __launch_bounds__(kThreads) void k_colexp(const float* __restrict__ part, int64_t dp, int nchunk,
                                                      int* __restrict__ exps) {
-    const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (c >= dp) return;
+    constexpr int kRowsPer = kThreads / kExpCols;  // 16 chunk groups
+    constexpr int kU = kMaxChunks / kRowsPer;      // chunks per thread at most
+    __shared__ float red[kRowsPer][kExpCols];
+    const int cl = threadIdx.x % kExpCols, rg = threadIdx.x / kExpCols;
+    const int64_t c = (int64_t)blockIdx.x * kExpCols + cl;
+    float v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const int q = rg + kRowsPer * u;
+        v[u] = (c < dp && q < nchunk) ? part[(size_t)q * dp + c] : 0.0f;
+    }
     float m = 0.0f;
-    for (int q = 0; q < nchunk; ++q) m = nan_max(m, part[(size_t)q * dp + c]);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) m = nan_max(m, v[u]);
+    red[rg][cl] = m;
+    __syncthreads();
+    if (rg != 0 || c >= dp) return;
+#pragma unroll
+    for (int r = 1; r < kRowsPer; ++r) m = nan_max(m, red[r][cl]);
     int e = 0;
     if (m > 0.0f && m < INFINITY) {
         int E;
@@ -888,7 +907,7 @@ int launch_hessian_accum(const float* X, int64_t T, int64_t d, int64_t ldx, floa
                 hipLaunchKernelGGL(k_colmax<false>, grid, dim3(kThreads), 0, stream, X, T, d, ldx, sh.dp, sh.nchunk,
                                    wt, cmax);
         }
-        hipLaunchKernelGGL(k_colexp, dim3((unsigned)((sh.dp + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
+        hipLaunchKernelGGL(k_colexp, dim3((unsigned)((sh.dp + kExpCols - 1) / kExpCols)), dim3(kThreads), 0, stream,
                            (const float*)cmax, sh.dp, sh.nchunk, exps);
         if (sh.ng > 0 && trans) {
             const unsigned gy = (unsigned)std::min<int64_t>(sh.ng / 4, 65535);

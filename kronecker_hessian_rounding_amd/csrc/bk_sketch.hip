@@ -9,13 +9,17 @@
 // weighted accumulation itself is the Hessian SYRK with every token scaled by
 // sqrt(w_t) in its pre-pass (bk_accum.hip).
 //
-// The quadratic forms are the row sums of (Y H) o Y. H is symmetric, so
-// (Y H)^T = H Y^T is a TN product of H and Y^T (both K-major): Y is first
-// transposed into the workspace, then each 64 x 64 tile (c, t) of H Y^T is one
-// fp32 MFMA tile GEMM over K = d whose epilogue multiplies by Y^T and sums
-// its 64 rows c, giving one partial per token and column tile. A last kernel
-// adds the partials in tile order (deterministic) and divides by ||H||_F^2,
-// itself summed in fp64 in a fixed order.
+// The quadratic forms are the row sums of (Y H) o Y. H is symmetric, so with
+// 64-wide index blocks C, C' the form is
+//   y H y^T = sum_C y_C (H_CC y_C^T + 2 sum_{C' > C} H_CC' y_C'^T),
+// half the products of the dense form. H_CC' for C' > C is read as the rows
+// C' of column block C (H_C'C, the lower triangle), so every product is a TN
+// product of H and Y^T (both K-major): Y is first transposed into the
+// workspace, then tile (C, t) is two fp32 MFMA tile GEMMs, over K = C (the
+// diagonal block) and over K = the blocks below it, whose epilogue multiplies
+// by Y^T and sums the tile's 64 rows, giving one partial per token and column
+// tile. A last kernel adds the partials in tile order (deterministic) and
+// divides by ||H||_F^2, itself summed in fp64 in a fixed order.
 #include "bk_common.hpp"
 #include "bk_internal.hpp"
 
@@ -74,7 +78,9 @@ __global__ __launch_bounds__(kThreads) void k_tw_fro(const float* __restrict__ H
     }
 }
 
-// Tile (t-tile, c-tile) = (blockIdx.x, blockIdx.y): part[ct][t] = sum_{c in tile} (H Y^T)[c][t] * Y^T[c][t].
+// Tile (t-tile, c-tile) = (blockIdx.x, blockIdx.y):
+//   part[ct][t] = sum_{c in tile} Y^T[c][t] ((H_CC Y_C^T)[c][t] + 2 sum_{C' > C} (H_CC' Y_C'^T)[c][t]).
+// Column tiles are blockIdx.y, so the tiles with the longest K (C = 0) start first.
 __global__ __launch_bounds__(kThreads) void k_tw_qform(const float* __restrict__ H, int64_t ldh,
                                                        const float* __restrict__ Yt, int64_t T, int64_t d,
                                                        float* __restrict__ part) {
@@ -83,17 +89,23 @@ __global__ __launch_bounds__(kThreads) void k_tw_qform(const float* __restrict__
     const int tid = threadIdx.x;
     const int64_t t0 = (int64_t)blockIdx.x * kTile, c0 = (int64_t)blockIdx.y * kTile;
     const int R = (int)min<int64_t>(kTile, d - c0), Cn = (int)min<int64_t>(kTile, T - t0);
-    f32x16 acc;
+    f32x16 accd, acco;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-    // C[r][c] = sum_k A[k][r] B[k][c] with A = H (column block c0) and B = Y^T (token block t0)
-    tile_gemm_f32<kQKT>(H + c0, ldh, R, Yt + t0, T, Cn, d, acc, sm, true, tid);
+    for (int v = 0; v < 16; ++v) accd[v] = acco[v] = 0.0f;
+    // C[r][c] = sum_k A[k][r] B[k][c] with A = rows k of H's column block c0 and B = rows k
+    // of Y^T (token block t0): k in the diagonal block, then k below it
+    tile_gemm_f32<kQKT>(H + c0 * ldh + c0, ldh, R, Yt + c0 * T + t0, T, Cn, R, accd, sm, true, tid);
+    const int64_t kb = c0 + kTile;
+    if (kb < d) {
+        __syncthreads();  // the shared memory is reused
+        tile_gemm_f32<kQKT>(H + kb * ldh + c0, ldh, R, Yt + kb * T + t0, T, Cn, d - kb, acco, sm, true, tid);
+    }
     const int col = acc32_col(tid);
     float s = 0.0f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
         const int row = acc32_row(v, tid);
-        if (row < R && col < Cn) s = fmaf(acc[v], Yt[(c0 + row) * T + t0 + col], s);
+        if (row < R && col < Cn) s = fmaf(fmaf(2.0f, acco[v], accd[v]), Yt[(c0 + row) * T + t0 + col], s);
     }
     const int w = tid >> 6, lane = tid & 63;
     red[w >> 1][lane >> 5][col] = s;
