@@ -43,10 +43,11 @@
 namespace bk {
 
 constexpr int kB = kTile;        // leaf edge
-constexpr int kNch = 4;          // maximum K-chunks per far-field product
-constexpr int kRing = 4;         // diagonals whose far-field partials are held at once
+constexpr int kNch = 4;          // far-field partials per leaf and kind: up to three K-chunks and a fringe
+constexpr int kFringe = kNch - 1;  // the partial slot of the fringe (see far_tasks)
+constexpr int kRing = 6;         // diagonals whose far-field partials are held at once
 constexpr int kTargetWg = 512;   // far-field tasks aimed for per diagonal
-constexpr int kFarMin = 4;       // first diagonal with a far field (blocks four or more back)
+constexpr int kFarMin = 3;       // first diagonal with far-field tasks (blocks four or more back)
 constexpr int kStrip = 16;       // columns (rows) per hand-over
 constexpr int kStrips = kB / kStrip;
 
@@ -89,11 +90,12 @@ struct SolveParams {
     int ntask;
     uint64_t spin_limit;  // wall-clock ticks a single wait may take
     // far-field operands as fp16 piece planes (see the far-field section)
-    int64_t Mp, Np;  // rows, columns padded to whole leaves
+    int64_t Mp, Np;  // rows, columns padded to whole quads (an even number of leaves)
+    int64_t Mc;      // columns of the C plane: a leaf of padding, the rows, whole quads
     const f16x8* lop;  // L_O: [2][Mp / 8][Mp]
     const f16x8* lip;  // L_I: [2][Np / 8][Np]
     f16x8* dpl;        // D:   [2][Mp / 8][Np]
-    f16x8* cpl;        // C:   [2][Np / 8][Mp]
+    f16x8* cpl;        // C:   [2][Np / 8][Mc], row i at column i + 64
     const int* exd;    // eD per row of W (Mp)
     const int* exc;    // eC per row of W (Mp)
     const int* fexo;   // fO per column of L_O (Mp)
@@ -115,23 +117,43 @@ __host__ __device__ __forceinline__ int diag_nch(int M, int N, int d) {
     int nch = (kTargetWg + nl - 1) / nl;
     const int cap = kmax / 4 > 1 ? kmax / 4 : 1;
     nch = nch < cap ? nch : cap;
-    nch = nch < kNch ? nch : kNch;
+    nch = nch < kFringe ? nch : kFringe;
     return nch > 1 ? nch : 1;
 }
-// The far fields come in pairs that share a factor panel: the column far field p of
-// leaves (I, J) and (I, J + 1) for even J (one L_O panel, two adjacent D panels), and
-// the row far field o of leaves (I, J) and (I + 1, J) for even I (one L_I panel, two
-// adjacent C^T panels). A pair is computed with the first leaf's diagonal; the second
-// leaf lies on the next one. On an odd diagonal every leaf starts one pair (p where I
-// is odd, o where I is even); on an even diagonal the leaves with even I start both.
-__host__ __device__ __forceinline__ int far_tasks(int M, int N, int d, int nch) {
-    const int lo = diag_lo(N, d), hi = diag_hi(M, d);
-    return (d & 1) ? (hi - lo + 1) * nch : count_even(lo, hi) * 2 * nch;
+// The far fields come in quads: the 2 x 2 leaves (I, J), (I, J + 1), (I + 1, J),
+// (I + 1, J + 1) share two factor panels in each direction (the column far fields p:
+// L_O panels I, I + 1 and D panels J, J + 1; the row far fields o: L_I panels J, J + 1
+// and C panels I, I + 1), so one 128 x 128 tile gives all four. A quad covers the
+// blocks four or more above (p) or left of (o) its first row (column): the second
+// row's (column's) leaves take one more block during set-up. A quad is computed with
+// its first leaf's diagonal d; its other leaves lie on d + 1 and d + 2. Column quads
+// start at even I and J (even d), row quads at odd I (from -1: the first has row 0
+// only) and even J (odd d), so every diagonal has quads of one kind.
+__host__ __device__ __forceinline__ int quad_lo(int N, int d) {  // first row of a quad origin on d
+    int lo = d - (N - 1) > -1 ? d - (N - 1) : -1;
+    if ((d & 1) == 0) lo = lo < 0 ? 0 : lo;
+    const int par = d & 1;  // origins have I of the parity of d (J is even)
+    return ((lo & 1) == par) ? lo : lo + 1;
 }
-// tasks of group k: the leaves of diagonal k, then the far-field pairs of diagonal
-// k + 1 (those exist from diagonal kFarMin on). A pair task reads leaves three or
-// more groups back, so it rarely waits; the leaves of its diagonal come right after
-// it in the order.
+__host__ __device__ __forceinline__ int quad_count(int M, int N, int d) {
+    const int lo = quad_lo(N, d), hi = d < M - 1 ? d : M - 1;
+    return hi < lo ? 0 : (hi - lo) / 2 + 1;
+}
+__host__ __device__ __forceinline__ int far_tasks(int M, int N, int d, int nch) {
+    return quad_count(M, N, d) * nch;
+}
+// The second row (column) of a quad needs one block more than the quad covers: its
+// fringe, a 64 x 128 tile over that one block (K = 64) for the second row's two
+// leaves, is one task per quad, run after the leaves of the quad's own diagonal; it
+// writes partial slot kFringe. So every leaf multiplies the same two blocks during
+// set-up.
+__host__ __device__ __forceinline__ int fringe_tasks(int M, int N, int d) {
+    return d >= kFarMin ? quad_count(M, N, d) : 0;
+}
+// tasks of group k: the leaves of diagonal k, then the far-field quads of diagonal
+// k + 1 (those exist from diagonal kFarMin on), then the fringes of diagonal k. A quad
+// task reads leaves three or more groups back and a fringe two, so they rarely wait;
+// the leaves that take them come after them in the order.
 __host__ __device__ __forceinline__ int group_far(int ND, int k) {
     return (k + 1 >= kFarMin && k + 1 < ND) ? k + 1 : -1;
 }
@@ -139,7 +161,7 @@ __host__ __device__ __forceinline__ int group_tasks(int M, int N, int ND, int k)
     int s = diag_leaves(M, N, k);
     const int df = group_far(ND, k);
     if (df >= 0) s += far_tasks(M, N, df, diag_nch(M, N, df));
-    return s;
+    return s + fringe_tasks(M, N, k);
 }
 
 __device__ __forceinline__ int leaf_lo(const SolveParams& p, int d) { return diag_lo(p.N, d); }
@@ -407,19 +429,19 @@ __device__ __forceinline__ void vm_wait_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// One ring stage: 32 k (four 8-k groups) of both pieces of A (64 columns) and B (up
-// to 128 columns: the pair's two targets side by side).
+// One ring stage: 32 k (four 8-k groups) of both pieces of A and B, 128 columns each
+// (the quad's two rows and two columns of leaves).
 #ifndef BK_PIECE_NS
 #define BK_PIECE_NS 4
 #endif
 constexpr int kPieceNS = BK_PIECE_NS;  // stages in the ring: loads run kPieceNS - 1 stages ahead
 struct PieceStage {
-    f16x8 a[2][4][kB];
+    f16x8 a[2][4][2 * kB];
     f16x8 b[2][4][2 * kB];
 };
 struct PieceRing {
     PieceStage s[kPieceNS];
-    int fr[kB];      // exponent of each output row (A column)
+    int fr[2 * kB];  // exponent of each output row (A column)
     int fc[2 * kB];  // exponent of each output column (B column)
 };
 
@@ -431,82 +453,67 @@ __device__ __forceinline__ uint32_t lds_addr(const void* q) {
 // to the compiler, these reads of the ring, whose other slots direct-to-LDS loads
 // are still filling, were preceded by a wait for every load in flight (vmcnt(0)),
 // which undid the prefetch; the waits for the stage's own loads are the barrier's.
-// a: the lane's A unit of group kh (fa[s][pc]: group 2 s + kh, piece pc); b: its B
-// unit (fb[s][pc][t]: group 2 s + kh, piece pc, target t at +32 t columns).
-template <int NT>
-__device__ __forceinline__ void stage_reads(uint32_t a, uint32_t b, f16x8 (&fa)[2][2], f16x8 (&fb)[2][2][2]) {
-    // offsets: a[pc][g][c] at 4096 pc + 1024 g + 16 c; b[pc][g][c] at 8192 pc + 2048 g + 16 c
-    if constexpr (NT == 2) {
-        asm volatile(
-            "ds_read_b128 %0, %12\n\t"
-            "ds_read_b128 %1, %12 offset:4096\n\t"
-            "ds_read_b128 %2, %12 offset:2048\n\t"
-            "ds_read_b128 %3, %12 offset:6144\n\t"
-            "ds_read_b128 %4, %13\n\t"
-            "ds_read_b128 %5, %13 offset:512\n\t"
-            "ds_read_b128 %6, %13 offset:8192\n\t"
-            "ds_read_b128 %7, %13 offset:8704\n\t"
-            "ds_read_b128 %8, %13 offset:4096\n\t"
-            "ds_read_b128 %9, %13 offset:4608\n\t"
-            "ds_read_b128 %10, %13 offset:12288\n\t"
-            "ds_read_b128 %11, %13 offset:12800\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(fa[0][0]), "=&v"(fa[0][1]), "=&v"(fa[1][0]), "=&v"(fa[1][1]), "=&v"(fb[0][0][0]),
-              "=&v"(fb[0][0][1]), "=&v"(fb[0][1][0]), "=&v"(fb[0][1][1]), "=&v"(fb[1][0][0]), "=&v"(fb[1][0][1]),
-              "=&v"(fb[1][1][0]), "=&v"(fb[1][1][1])
-            : "v"(a), "v"(b)
-            : "memory");
-    } else {
-        asm volatile(
-            "ds_read_b128 %0, %8\n\t"
-            "ds_read_b128 %1, %8 offset:4096\n\t"
-            "ds_read_b128 %2, %8 offset:2048\n\t"
-            "ds_read_b128 %3, %8 offset:6144\n\t"
-            "ds_read_b128 %4, %9\n\t"
-            "ds_read_b128 %5, %9 offset:8192\n\t"
-            "ds_read_b128 %6, %9 offset:4096\n\t"
-            "ds_read_b128 %7, %9 offset:12288\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(fa[0][0]), "=&v"(fa[0][1]), "=&v"(fa[1][0]), "=&v"(fa[1][1]), "=&v"(fb[0][0][0]),
-              "=&v"(fb[0][1][0]), "=&v"(fb[1][0][0]), "=&v"(fb[1][1][0])
-            : "v"(a), "v"(b)
-            : "memory");
-    }
+// a: the lane's A unit of group kh in the wave's first 32 columns; b: likewise for B.
+// fa[s][pc][h]: group 2 s + kh, piece pc, columns +32 h; fb likewise.
+__device__ __forceinline__ void stage_reads(uint32_t a, uint32_t b, f16x8 (&fa)[2][2][2], f16x8 (&fb)[2][2][2]) {
+    // offsets: x[pc][g][c] at 8192 pc + 2048 g + 16 c, for both operands
+    asm volatile(
+        "ds_read_b128 %0, %16\n\t"
+        "ds_read_b128 %1, %16 offset:512\n\t"
+        "ds_read_b128 %2, %16 offset:8192\n\t"
+        "ds_read_b128 %3, %16 offset:8704\n\t"
+        "ds_read_b128 %4, %16 offset:4096\n\t"
+        "ds_read_b128 %5, %16 offset:4608\n\t"
+        "ds_read_b128 %6, %16 offset:12288\n\t"
+        "ds_read_b128 %7, %16 offset:12800\n\t"
+        "ds_read_b128 %8, %17\n\t"
+        "ds_read_b128 %9, %17 offset:512\n\t"
+        "ds_read_b128 %10, %17 offset:8192\n\t"
+        "ds_read_b128 %11, %17 offset:8704\n\t"
+        "ds_read_b128 %12, %17 offset:4096\n\t"
+        "ds_read_b128 %13, %17 offset:4608\n\t"
+        "ds_read_b128 %14, %17 offset:12288\n\t"
+        "ds_read_b128 %15, %17 offset:12800\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(fa[0][0][0]), "=&v"(fa[0][0][1]), "=&v"(fa[0][1][0]), "=&v"(fa[0][1][1]), "=&v"(fa[1][0][0]),
+          "=&v"(fa[1][0][1]), "=&v"(fa[1][1][0]), "=&v"(fa[1][1][1]), "=&v"(fb[0][0][0]), "=&v"(fb[0][0][1]),
+          "=&v"(fb[0][1][0]), "=&v"(fb[0][1][1]), "=&v"(fb[1][0][0]), "=&v"(fb[1][0][1]), "=&v"(fb[1][1][0]),
+          "=&v"(fb[1][1][1])
+        : "v"(a), "v"(b)
+        : "memory");
 }
 
-// acc[t] += A^T B over groups [g0, g1) (whole stages) for NT targets: A columns
-// ca .. ca + 63 of plane A (ngA groups, ncA columns), B columns cb .. cb + 64 NT - 1
-// of plane B. Waves 0-3 load and compute (wave w: output rows 32 (w >> 1) .., target
-// w & 1 for a pair, or columns 32 (w & 1) .. of the lone target); the others only
-// join the barriers. Every thread of the workgroup calls it.
-template <int NT>
-__device__ __forceinline__ void far_pieces(const f16x8* __restrict__ A, int64_t ngA, int64_t ncA, int64_t ca,
-                                           const f16x8* __restrict__ B, int64_t ngB, int64_t ncB, int64_t cb,
-                                           int64_t g0, int64_t g1, f32x16 (&acc)[2], PieceRing& sm, int tid) {
+// acc[h][t] += A^T B over groups [g0, g1) (whole stages) for a 128 x 128 tile: A columns
+// ca .. ca + 127 of plane A (ngA groups, ncA columns), B columns cb .. cb + 127 of plane
+// B. Waves 0-3 load and compute: wave w owns output rows 64 (w >> 1) .. (the quad's
+// row of leaves w >> 1) and columns 64 (w & 1) .. (its column w & 1), as 2 x 2 blocks
+// of 32 x 32 (h: rows +32 h, t: columns +32 t); the others only join the barriers.
+// Every thread of the workgroup calls it.
+__device__ __forceinline__ void far_quad(const f16x8* __restrict__ A, int64_t ngA, int64_t ncA, int64_t ca,
+                                         const f16x8* __restrict__ B, int64_t ngB, int64_t ncB, int64_t cb,
+                                         int64_t g0, int64_t g1, f32x16 (&acc)[2][2], PieceRing& sm, int tid) {
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool active = w < 4;
     const int kh = lane >> 5, l31 = lane & 31;
-    const int ar = (w >> 1) * 32 + l31;
-    const int bc = (w & 1) * 32 * NT + l31;
-    constexpr int kLoads = (8 + 8 * NT) / 4;  // direct loads per active wave per stage
+    const int ar = (w >> 1) * kB + l31;
+    const int bc = (w & 1) * kB + l31;
+    constexpr int kLoads = 8;  // direct loads per active wave per stage: 16 rows of 2 KB per operand
     const int64_t ns = (g1 - g0) / 4;
     auto issue = [&](int64_t s) {
         PieceStage& st = sm.s[s % kPieceNS];
         const int64_t gs = g0 + 4 * s;
 #pragma unroll
         for (int h = 0; h < kLoads; ++h) {
-            const int q = w + 4 * h;
-            if (q < 8) {  // A: one 1 KB row (64 units) per load
-                const int pc = q >> 2, gl = q & 3;
-                __builtin_amdgcn_global_load_lds(A + (pc * ngA + gs + gl) * ncA + ca + lane, &st.a[pc][gl][0],
-                                                 16, 0, 0);
-            } else {
-                const int q2 = q - 8;
-                const int pc = q2 / (4 * NT), gl = (q2 / NT) & 3, hf = q2 % NT;
+            const int q = w + 4 * h;  // 0..31: operand q >> 4, piece, group, half row
+            const int o = q & 15;
+            const int pc = o >> 3, gl = (o >> 1) & 3, hf = o & 1;
+            if (q < 16)
+                __builtin_amdgcn_global_load_lds(A + (pc * ngA + gs + gl) * ncA + ca + kB * hf + lane,
+                                                 &st.a[pc][gl][kB * hf], 16, 0, 0);
+            else
                 __builtin_amdgcn_global_load_lds(B + (pc * ngB + gs + gl) * ncB + cb + kB * hf + lane,
                                                  &st.b[pc][gl][kB * hf], 16, 0, 0);
-            }
         }
     };
     if (active)
@@ -521,16 +528,18 @@ __device__ __forceinline__ void far_pieces(const f16x8* __restrict__ A, int64_t 
         if (!active) continue;
         if (it + kPieceNS - 1 < ns) issue(it + kPieceNS - 1);
         const PieceStage& st = sm.s[it % kPieceNS];
-        f16x8 fa[2][2], fb[2][2][2];  // [16-k step][piece](, [target])
-        stage_reads<NT>(lds_addr(&st.a[0][kh][ar]), lds_addr(&st.b[0][kh][bc]), fa, fb);
+        f16x8 fa[2][2][2], fb[2][2][2];  // [16-k step][piece][32-column half]
+        stage_reads(lds_addr(&st.a[0][kh][ar]), lds_addr(&st.b[0][kh][bc]), fa, fb);
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)  // two 16-k steps
 #pragma unroll
             for (int u = 0; u < 3; ++u)
 #pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[s2][kPa[u]], fb[s2][kPb[u]][t], acc[t], 0, 0,
-                                                                    0);
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        acc[h][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[s2][kPa[u]][h], fb[s2][kPb[u]][t],
+                                                                           acc[h][t], 0, 0, 0);
     }
 }
 
@@ -538,92 +547,112 @@ union FarSmem {
     PieceRing pc;
 };
 
-__device__ __forceinline__ void far_task(const SolveParams& p, int d, int task, FarSmem& sm, int tid) {
-    const int nch = p.nchd[d];
-    const int lo = leaf_lo(p, d);
-    int I, kind, c;
-    if (d & 1) {  // every leaf starts one pair: p where I is odd (J even), o where I is even
-        c = task % nch;
-        I = lo + task / nch;
-        kind = (I & 1) ? 0 : 1;
-    } else {  // the leaves with even I (and J) start both
-        c = task % nch;
-        kind = (task / nch) & 1;
-        I = lo + (lo & 1) + 2 * (task / (2 * nch));
+// waits until the leaf that last used ring slot `slot` of diagonal dt (kRing diagonals
+// back) has taken its partials
+__device__ __forceinline__ void wait_ring(const SolveParams& p, int dt, int slot) {
+    if (dt < kRing) return;
+    const int dp = dt - kRing;
+    if (slot < diag_leaves(p.M, p.N, dp)) {
+        const int Ip = leaf_lo(p, dp) + slot;
+        wait_flag(p, &p.setup[(int64_t)Ip * p.N + (dp - Ip)], 1);
     }
+}
+
+// Task `task` of diagonal d: a quad (chunk c of its K range) or, with fringe, the fringe
+// of quad `task` (the one block after the quad's K range, for the second row or column).
+__device__ __forceinline__ void far_task(const SolveParams& p, int d, int task, bool fringe, FarSmem& sm,
+                                         int tid) {
+    const int nch = p.nchd[d];
+    const int c = fringe ? kFringe : task % nch, kind = d & 1;
+    const int I = quad_lo(p.N, d) + 2 * (fringe ? task : task / nch);  // the quad's first leaf (I may be -1)
     const int J = d - I;
-    // the pair's second leaf, on diagonal d + 1
-    const int I2 = kind == 0 ? I : I + 1, J2 = kind == 0 ? J + 1 : J;
-    const bool two = I2 < p.M && J2 < p.N;
-    const int slot = I - lo, slot2 = two ? I2 - leaf_lo(p, d + 1) : 0;
-    const int kblk = (kind == 0 ? I : J) - 3;  // blocks 0 .. kblk - 1: four or more back
-    const bool has = (kind == 0 ? p.LO != nullptr : p.LI != nullptr) && kblk > 0;
+    const int kfirst = (kind == 0 ? I : J) - 3;  // the quad: blocks 0 .. kfirst - 1; the fringe: block kfirst
+    const bool fac = kind == 0 ? p.LO != nullptr : p.LI != nullptr;
+    int kb0 = 0, kb1 = 0;
+    if (fringe) {
+        kb0 = kfirst;
+        kb1 = kfirst + 1;
+    } else if (kfirst > 0) {
+        chunk_range(kfirst, nch, c, kb0, kb1);
+    }
+    // a quad's empty chunk still writes its (zero) partial: the leaf adds every chunk
+    const bool has = fac && (fringe ? kfirst >= 0 : kfirst > 0);
+    // target (h, t): the leaf of A half h and B half t; a fringe has only h = 1
+    auto tgt_i = [&](int h, int t) { return kind == 0 ? I + h : I + t; };
+    auto tgt_j = [&](int h, int t) { return kind == 0 ? J + t : J + h; };
+    auto exists = [&](int h, int t) {
+        return (!fringe || h == 1) && tgt_i(h, t) >= 0 && tgt_i(h, t) < p.M && tgt_j(h, t) < p.N;
+    };
     if (has) {
-        int kb0, kb1;
-        chunk_range(kblk, nch, c, kb0, kb1);
         const int64_t i0 = (int64_t)I * kB, j0 = (int64_t)J * kB;
         if (tid == 0) {
-            // the last leaf of the K range next to the pair's second (or only) target:
-            // its pieces, and so those of every leaf above and to the left of it
+            // the last leaf of the K range next to the quad's farthest column (row): its
+            // pieces, and so those of every leaf above and to the left of it
             if (kb1 > kb0) {
-                if (kind == 0) wait_flag(p, &p.pdone[(int64_t)(kb1 - 1) * p.N + (two ? J2 : J)], 1);
-                else wait_flag(p, &p.pdone[(int64_t)(two ? I2 : I) * p.N + kb1 - 1], 1);
+                if (kind == 0) wait_flag(p, &p.pdone[(int64_t)(kb1 - 1) * p.N + min(J + 1, p.N - 1)], 1);
+                else wait_flag(p, &p.pdone[(int64_t)min(I + 1, p.M - 1) * p.N + kb1 - 1], 1);
             }
-            // the leaves that last used these ring slots (kRing diagonals back) have read them
-            if (d >= kRing) {
-                const int dp = d - kRing;
-                if (slot < diag_leaves(p.M, p.N, dp)) {
-                    const int Ip = leaf_lo(p, dp) + slot;
-                    wait_flag(p, &p.setup[(int64_t)Ip * p.N + (dp - Ip)], 1);
-                }
-            }
-            if (two && d + 1 >= kRing) {
-                const int dp = d + 1 - kRing;
-                if (slot2 < diag_leaves(p.M, p.N, dp)) {
-                    const int Ip = leaf_lo(p, dp) + slot2;
-                    wait_flag(p, &p.setup[(int64_t)Ip * p.N + (dp - Ip)], 1);
-                }
-            }
+            // the leaves that last used these ring slots have read them
+            for (int h = 0; h < 2; ++h)
+                for (int t = 0; t < 2; ++t)
+                    if (exists(h, t)) {
+                        const int it = tgt_i(h, t), dt = it + tgt_j(h, t);
+                        wait_ring(p, dt, it - leaf_lo(p, dt));
+                    }
             acquire_agent();
             vm_wait_all();
         }
         // output exponents: rows (A columns) and, for o^T, columns (rows of C)
         const int64_t ca = kind == 0 ? i0 : j0, cb = kind == 0 ? j0 : i0;
-        if (tid < kB) sm.pc.fr[tid] = (kind == 0 ? p.fexo : p.fexi)[ca + tid];
-        else if (tid < 3 * kB) sm.pc.fc[tid - kB] = kind == 0 ? 0 : p.exc[min<int64_t>(cb + tid - kB, p.Mp - 1)];
+        if (tid < 2 * kB) {
+            sm.pc.fr[tid] = (kind == 0 ? p.fexo : p.fexi)[ca + tid];
+        } else if (tid < 4 * kB) {
+            const int64_t r = cb + tid - 2 * kB;
+            sm.pc.fc[tid - 2 * kB] = (kind == 0 || r < 0 || r >= p.Mp) ? 0 : p.exc[r];
+        }
         __syncthreads();
-        f32x16 acc[2];
+        f32x16 acc[2][2];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[0][v] = acc[1][v] = 0.0f;
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[h][t][v] = 0.0f;
         const f16x8* A = kind == 0 ? p.lop : p.lip;
         const f16x8* Bp = kind == 0 ? p.dpl : p.cpl;
         const int64_t ngA = (kind == 0 ? p.Mp : p.Np) / 8, ncA = kind == 0 ? p.Mp : p.Np;
-        const int64_t ngB = ngA, ncB = kind == 0 ? p.Np : p.Mp;
-        if (two) far_pieces<2>(A, ngA, ncA, ca, Bp, ngB, ncB, cb, 8 * kb0, 8 * kb1, acc, sm.pc, tid);
-        else far_pieces<1>(A, ngA, ncA, ca, Bp, ngB, ncB, cb, 8 * kb0, 8 * kb1, acc, sm.pc, tid);
+        const int64_t ngB = ngA, ncB = kind == 0 ? p.Np : p.Mc;
+        // the C plane's columns start one leaf early (row -64 .. -1: the first row quad)
+        far_quad(A, ngA, ncA, ca, Bp, ngB, ncB, kind == 0 ? cb : cb + kB, 8 * kb0, 8 * kb1, acc, sm.pc, tid);
         if (tid < kThreads) {
             const int w = tid >> 6, lane = tid & 63;
-            const int tgt = two ? (w & 1) : 0;
-            float* part = part_ptr(p, tgt ? d + 1 : d, tgt ? slot2 : slot, kind, c);
+            const int h = w >> 1, t = w & 1;
+            if (exists(h, t)) {
+                const int it = tgt_i(h, t), dt = it + tgt_j(h, t);
+                float* part = part_ptr(p, dt, it - leaf_lo(p, dt), kind, c);
 #pragma unroll
-            for (int b = 0; b < (two ? 2 : 1); ++b) {
-                const int col = two ? 32 * b + (lane & 31) : 32 * (w & 1) + (lane & 31);
-                const int ec = sm.pc.fc[kB * tgt + col];
+                for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = (w >> 1) * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                    st_coherent(&part[row * kB + col], ldexpf(acc[b][v], -(sm.pc.fr[row] + ec)));
-                }
+                    for (int tt = 0; tt < 2; ++tt) {
+                        const int col = 32 * tt + (lane & 31);
+                        const int ec = sm.pc.fc[kB * t + col];
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const int row = 32 * hh + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                            st_coherent(&part[row * kB + col], ldexpf(acc[hh][tt][v], -(sm.pc.fr[kB * h + row] + ec)));
+                        }
+                    }
             }
         }
         vm_wait_all();  // every wave's device-coherent partial stores have completed
         __syncthreads();
     }
     if (tid == 0) {
-        __hip_atomic_fetch_add(&p.fardone[(int64_t)I * p.N + J], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (two)
-            __hip_atomic_fetch_add(&p.fardone[(int64_t)I2 * p.N + J2], 1, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+        for (int h = 0; h < 2; ++h)
+            for (int t = 0; t < 2; ++t)
+                if (exists(h, t))
+                    __hip_atomic_fetch_add(&p.fardone[(int64_t)tgt_i(h, t) * p.N + tgt_j(h, t)], 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -849,15 +878,23 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
     const int lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int64_t leaf = (int64_t)I * p.N + J;
-    // this leaf's far fields come from the pair that starts at (I, J) or at the leaf before
-    // it in its row (p) or column (o), on this diagonal or the one before
-    const int dp_src = (J & 1) ? d - 1 : d, do_src = (I & 1) ? d - 1 : d;
-    const int nch_p = dp_src >= kFarMin ? p.nchd[dp_src] : 0;
-    const int nch_o = do_src >= kFarMin ? p.nchd[do_src] : 0;
-    const bool far_p = p.LO && I > 3, far_o = p.LI && J > 3;  // far-field partials (blocks <= I-4, J-4)
-    const bool b2_p = p.LO && I > 1, b2_o = p.LI && J > 1;    // the blocks two back
-    const bool b3_p = p.LO && I > 2, b3_o = p.LI && J > 2;    // the blocks three back
-    const bool adj_p = p.LO && I > 0, adj_o = p.LI && J > 0;  // the adjacent blocks (handed over)
+    // this leaf's far fields come from two quads, on this diagonal or up to two before:
+    // the column quad whose first leaf is (I, J) rounded down to even indices, and the
+    // row quad that starts at the odd row at or above I and the even column at or left
+    // of J. They cover the blocks below fI - 3 (p) and fJ - 3 (o); in an odd row
+    // (column) the quad's fringe adds block fI - 3 (fJ - 3). The set-up multiplies the
+    // two blocks from there to two back.
+    const int fI = I & ~1, fJ = J & ~1;
+    const int dsrc_p = fI + fJ, dsrc_o = ((I & 1) ? I : I - 1) + fJ;
+    const int nch_p = dsrc_p >= kFarMin ? p.nchd[dsrc_p] : 0;
+    const int nch_o = dsrc_o >= kFarMin ? p.nchd[dsrc_o] : 0;
+    // far-field tasks that report to this leaf: the chunks of its quads, and their
+    // fringes in an odd row (column)
+    const int nfar = nch_p + nch_o + ((I & 1) && dsrc_p >= kFarMin) + ((J & 1) && dsrc_o >= kFarMin);
+    const bool far_p = p.LO && fI > 3, far_o = p.LI && fJ > 3;  // quad partials
+    const bool fr_p = p.LO && (I & 1) && I >= 5, fr_o = p.LI && (J & 1) && J >= 5;  // fringe partials
+    const int s0_p = max(0, I - 3), s0_o = max(0, J - 3);       // first block of the set-up
+    const bool adj_p = p.LO && I > 0, adj_o = p.LI && J > 0;    // the adjacent blocks (handed over)
     for (int e = t; e < kNew * kB; e += kLeafThreads) sm.li[e / kB][e % kB] = 0.0f;  // no L_I[j-1-e][j] for j <= e
     __syncthreads();
     constexpr int kPer = (kB * kB + kLeafThreads - 1) / kLeafThreads;
@@ -887,7 +924,7 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
     // the K-chunk partials are summed in chunk order into registers (every load
     // issued first; absent chunks read a valid address and are replaced by zero)
     if (t == 0) {
-        if (nch_p + nch_o > 0) wait_flag(p, &p.fardone[leaf], nch_p + nch_o);
+        if (nfar > 0) wait_flag(p, &p.fardone[leaf], nfar);
         acquire_agent();
         vm_wait_all();
     }
@@ -896,8 +933,11 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
     const f32x4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
     f32x4 pvs[kG], ovs[kG];  // p and o^T, four consecutive entries per group
     {
-        const bool any = far_p || far_o;
-        const int lp = nch_p > 0 ? nch_p - 1 : 0, lo_ = nch_o > 0 ? nch_o - 1 : 0;
+        const bool any = far_p || far_o || fr_p || fr_o;
+        // slots read: the quad chunks and the fringe's (slot kFringe); the others read
+        // slot 0 (a valid address) and are replaced by zero
+        auto sp = [&](int c) { return c < nch_p ? c : (c == kFringe && fr_p ? kFringe : 0); };
+        auto so = [&](int c) { return c < nch_o ? c : (c == kFringe && fr_o ? kFringe : 0); };
         f32x4 xp[kG][kNch], xo[kG][kNch];
         if (any) {
 #pragma unroll
@@ -905,8 +945,8 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
                 const int g = min(t + u * kLeafThreads, kB * kB / 4 - 1);
 #pragma unroll
                 for (int c = 0; c < kNch; ++c) {
-                    xp[u][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, d, slot, 0, min(c, lp)) + 4 * g);
-                    xo[u][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, d, slot, 1, min(c, lo_)) + 4 * g);
+                    xp[u][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, d, slot, 0, sp(c)) + 4 * g);
+                    xo[u][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, d, slot, 1, so(c)) + 4 * g);
                 }
             }
         }
@@ -918,8 +958,8 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
                     const int gg = min(t + uu * kLeafThreads, kB * kB / 4 - 1);
 #pragma unroll
                     for (int c = 0; c < kNch; ++c) {
-                        xp[uu][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, d, slot, 0, min(c, lp)) + 4 * gg);
-                        xo[uu][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, d, slot, 1, min(c, lo_)) + 4 * gg);
+                        xp[uu][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, d, slot, 0, sp(c)) + 4 * gg);
+                        xo[uu][c] = *reinterpret_cast<const f32x4*>(part_ptr(p, d, slot, 1, so(c)) + 4 * gg);
                     }
                 }
             }
@@ -927,7 +967,8 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
             if (any) {
 #pragma unroll
                 for (int c = 0; c < kNch; ++c) {
-                    const bool up = far_p && c < nch_p, uo = far_o && c < nch_o;
+                    const bool up = (far_p && c < nch_p) || (fr_p && c == kFringe);
+                    const bool uo = (far_o && c < nch_o) || (fr_o && c == kFringe);
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         pv[k] += up ? xp[u][c][k] : 0.0f;
@@ -942,12 +983,13 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
     // the partials are read (their ring slot may be reused)
     __syncthreads();
     if (t == 0) st_flag(&p.setup[leaf], 1);
-    // ---- the leaves two and three blocks up and to the left: once the ones two back
-    // are done (the ones three back finished before them), their blocks are multiplied
-    // (K = 64 each): p += L_O[back, this]^T D[back, J], o^T += L_I[back, this]^T C^T[back, I]
+    // ---- the leaves two to four blocks up and to the left, down to the set-up's first
+    // block: once the ones two back are done (those further back finished before them),
+    // their blocks are multiplied (K = 64 each): p += L_O[back, this]^T D[back, J],
+    // o^T += L_I[back, this]^T C^T[back, I]
     if (t == 0) {
-        if (b2_p) wait_flag(p, &p.prog_d[leaf - 2 * (int64_t)p.N], kStrips);
-        if (b2_o) wait_flag(p, &p.prog_c[leaf - 2], kStrips);
+        if (p.LO && I - 2 >= s0_p) wait_flag(p, &p.prog_d[leaf - 2 * (int64_t)p.N], kStrips);
+        if (p.LI && J - 2 >= s0_o) wait_flag(p, &p.prog_c[leaf - 2], kStrips);
         acquire_agent();
         vm_wait_all();
     }
@@ -956,8 +998,9 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
 #pragma unroll
     for (int v = 0; v < 16; ++v) ap[v] = ao[v] = 0.0f;
 #pragma unroll 1
-    for (int back = 2; back <= 3; ++back) {
-        const bool bp = back == 2 ? b2_p : b3_p, bo = back == 2 ? b2_o : b3_o;
+    for (int back = 2; back <= 4; ++back) {
+        const bool bp = p.LO && I - back >= s0_p, bo = p.LI && J - back >= s0_o;
+        if (!bp && !bo) break;  // uniform: the blocks further back are in the far field
         //   DT <- L_O[i0-64b+k][i0+c]   Gs <- D[i0-64b+k][j0+c]
         //   pt <- L_I[j0-64b+k][j0+c]   bt <- C^T[j0-64b+k][i0+c]     (staging)
         float v1[kPer], v2[kPer], v3[kPer], v4[kPer];
@@ -1345,7 +1388,7 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
                     }
 #pragma unroll
                     for (int pc = 0; pc < 2; ++pc)
-                        st_coherent16(&p.cpl[((int64_t)pc * (p.Np / 8) + 8 * J + gl) * p.Mp + i0 + x], pk[pc]);
+                        st_coherent16(&p.cpl[((int64_t)pc * (p.Np / 8) + 8 * J + gl) * p.Mc + kB + i0 + x], pk[pc]);
                 }
             }
             vm_wait_all();  // this wave's piece stores have completed
@@ -1439,8 +1482,14 @@ __global__ __launch_bounds__(kLeafThreads, 1) void k_solve_run(SolveParams p) {
         }
         const int r = tk - p.seg[lo];
         const int nl = diag_leaves(p.M, p.N, lo);
-        if (r < nl) leaf_task(p, lo, r, sm.leaf, tid);
-        else far_task(p, lo + 1, r - nl, sm.far, tid);
+        if (r < nl) {
+            leaf_task(p, lo, r, sm.leaf, tid);
+        } else {
+            const int df = group_far(p.ND, lo);
+            const int nf = df >= 0 ? far_tasks(p.M, p.N, df, p.nchd[df]) : 0;
+            if (r < nl + nf) far_task(p, df, r - nl, false, sm.far, tid);
+            else far_task(p, lo, r - nl - nf, true, sm.far, tid);
+        }
         __syncthreads();  // the next task reuses the shared memory
     }
 }
@@ -1485,6 +1534,7 @@ struct Layout {
     int64_t Mp, Np;
     int nkcO, nkcI;  // pre-pass row chunks of L_O, L_I
     size_t ct, delta, parts, leaf_loss, leaf_clamp, info, sched, flags, seg, nchd;
+    int64_t Mc;
     size_t lop, lip, dpl, cpl, bd, exd, exc, fexo, fexi, mxO, sbO, mxI, total;
 };
 
@@ -1494,8 +1544,10 @@ Layout layout(int64_t m, int64_t n) {
     L.N = (int)((n + kB - 1) / kB);
     L.maxleaf = std::min(L.M, L.N);
     L.ND = L.M + L.N - 1;
-    L.Mp = (int64_t)L.M * kB;
-    L.Np = (int64_t)L.N * kB;
+    // the planes hold whole quads: rows and columns padded to an even number of leaves
+    L.Mp = (int64_t)((L.M + 1) & ~1) * kB;
+    L.Np = (int64_t)((L.N + 1) & ~1) * kB;
+    L.Mc = (int64_t)((L.M + 2) & ~1) * kB;
     L.nkcO = (int)((m + kPrepRows - 1) / kPrepRows);
     L.nkcI = (int)((n + kPrepRows - 1) / kPrepRows);
     const size_t nl = (size_t)L.M * L.N;
@@ -1529,7 +1581,7 @@ Layout layout(int64_t m, int64_t n) {
     L.dpl = o;
     o += align256(4 * Mp * Np);
     L.cpl = o;
-    o += align256(4 * Mp * Np);
+    o += align256(4 * (size_t)L.Mc * Np);
     L.bd = o;
     o += align256(sizeof(float) * Mp);
     L.exd = o;
@@ -1631,6 +1683,7 @@ int run_solve(const SolveArgs& a, void* ws, hipStream_t stream) {
     p.spin_limit = (uint64_t)di.clock_khz * limit_us / 1000ull;
     p.Mp = L.Mp;
     p.Np = L.Np;
+    p.Mc = L.Mc;
     p.lop = (const f16x8*)(base + L.lop);
     p.lip = (const f16x8*)(base + L.lip);
     p.dpl = (f16x8*)(base + L.dpl);
@@ -1655,22 +1708,22 @@ int run_solve(const SolveArgs& a, void* ws, hipStream_t stream) {
     float* mxI = (float*)(base + L.mxI);
     const unsigned eg_o = (unsigned)((L.Mp + kThreads - 1) / kThreads), eg_i = (unsigned)((L.Np + kThreads - 1) / kThreads);
     if (a.LO) {
-        hipLaunchKernelGGL(k_lstats, dim3((unsigned)L.M, (unsigned)L.nkcO), dim3(kThreads), 0, stream, a.LO,
+        hipLaunchKernelGGL(k_lstats, dim3((unsigned)(L.Mp / kB), (unsigned)L.nkcO), dim3(kThreads), 0, stream, a.LO,
                            a.ldlo, a.m, exd, bd, L.Mp, mxO, sbO);
         hipLaunchKernelGGL(k_lexp, dim3(eg_o), dim3(kThreads), 0, stream, mxO, sbO, L.nkcO, L.Mp, a.m, bd, fexo,
                            exc);
-        hipLaunchKernelGGL(k_lsplit, dim3((unsigned)L.M, (unsigned)L.nkcO), dim3(kThreads), 0, stream, a.LO,
+        hipLaunchKernelGGL(k_lsplit, dim3((unsigned)(L.Mp / kB), (unsigned)L.nkcO), dim3(kThreads), 0, stream, a.LO,
                            a.ldlo, a.m, exd, fexo, L.Mp, L.Mp / 8, (f16x8*)(base + L.lop));
     } else {  // C = D
         hipLaunchKernelGGL(k_lexp, dim3(eg_o), dim3(kThreads), 0, stream, nullptr, nullptr, 0, L.Mp, a.m, bd,
                            nullptr, exc);
     }
     if (a.LI) {
-        hipLaunchKernelGGL(k_lstats, dim3((unsigned)L.N, (unsigned)L.nkcI), dim3(kThreads), 0, stream, a.LI,
+        hipLaunchKernelGGL(k_lstats, dim3((unsigned)(L.Np / kB), (unsigned)L.nkcI), dim3(kThreads), 0, stream, a.LI,
                            a.ldli, a.n, nullptr, nullptr, L.Np, mxI, nullptr);
         hipLaunchKernelGGL(k_lexp, dim3(eg_i), dim3(kThreads), 0, stream, mxI, nullptr, L.nkcI, L.Np, a.n, nullptr,
                            fexi, nullptr);
-        hipLaunchKernelGGL(k_lsplit, dim3((unsigned)L.N, (unsigned)L.nkcI), dim3(kThreads), 0, stream, a.LI,
+        hipLaunchKernelGGL(k_lsplit, dim3((unsigned)(L.Np / kB), (unsigned)L.nkcI), dim3(kThreads), 0, stream, a.LI,
                            a.ldli, a.n, nullptr, fexi, L.Np, L.Np / 8, (f16x8*)(base + L.lip));
     }
     const int grid = (int)std::min<int64_t>(di.cus, ntask);
