@@ -96,8 +96,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the CPU sweep sample")
     ap.add_argument("--cpu-full", action="store_true",
-                    help="time the whole oracle chain on the whole layer instead of a bounded sample "
-                         "(minutes at the attention shape)")
+                    help="time the whole oracle chain on the whole layer (the default where its work, "
+                         "m n (m + n), is at most the attention shape's: about 26 s on 16 cores there)")
+    ap.add_argument("--cpu-sample", action="store_true",
+                    help="time a bounded sample of the oracle and extrapolate, whatever the shape")
     ap.add_argument("--hessian", default="tokens", choices=["tokens", "sketch_a", "sketch_b"],
                     help="factor estimate: X^T X / T and G^T G / T over tokens, Sketch A (alternating, "
                          "per-token weights) on the same X and G, or Sketch B from per-sequence weight "
@@ -208,6 +210,8 @@ def main():
     torch.cuda.set_device(dev)
     wl = workloads.get(args.workload)
     m, n, T = wl.m, wl.n, wl.T
+    # the whole oracle where it finishes in about half a minute on the host, else a sample
+    args.cpu_full = not args.cpu_sample and (args.cpu_full or m * n * (m + n) <= 4096 * 4096 * 8192)
     w, x, g = workloads.make_inputs(args.workload)
     W = torch.from_numpy(w).to(dev)
     X = torch.from_numpy(x).to(dev)
