@@ -353,11 +353,11 @@ def main():
     # form's algorithmic traffic, 33 B per weight: W* 4, the two far-field offsets 8,
     # D 4, C 4, the pieces of D and C 8, the code 1, the diagonal factor blocks
     # about 4), and its time per step of the dependent chain the schedule runs
-    # (64 x 64 leaves, a leaf-diagonal lag of 94 steps: (M + N - 2) 94 + 127 steps)
+    # (64 x 64 leaves, a leaf-diagonal lag of 96 steps: (M + N - 2) 96 + 127 steps)
     # next to the chain of the rule itself (m + n - 1 anti-diagonals).
     solve_s = ph["solve"] * 1e-3
     M, N = (m + 63) // 64, (n + 63) // 64
-    chain = (M + N - 2) * 94 + 127
+    chain = (M + N - 2) * 96 + 127
     base_bytes = 33.0 * m * n
     roof_solve = {
         "kernel": "k_solve_run (+ k_solve_init, k_scales, k_solve_finish)",
