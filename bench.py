@@ -53,9 +53,12 @@ COUNTER_SOURCES = {
 
 
 def source_key(kind):
-    """Hash of the kernel sources behind `kind`, comments and blank space removed."""
+    """Hash of the kernel sources behind `kind`, comments and blank space removed, and
+    of the compiler flags they are built with."""
     import hashlib
     import re
+
+    from kronecker_hessian_rounding_amd import build as hip_build
 
     csrc = os.path.join(ROOT, "kronecker_hessian_rounding_amd", "csrc")
     h = hashlib.sha256()
@@ -64,6 +67,7 @@ def source_key(kind):
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
+        h.update(" ".join(hip_build.CFLAGS[:-2] + hip_build.FILE_FLAGS.get(f, [])).encode())
     return h.hexdigest()[:16]
 
 
@@ -273,8 +277,8 @@ def main():
         if args.rotate:
             bk.rotate_layer(W, HI, HO, seed + 1, seed + 2)
             mark()
-        # the two factorisations are independent and each a chain of small launches:
-        # they run side by side on two streams
+        # the two factorisations are independent: one persistent launch serves both
+        # (orders up to 8192), else two chains of launches run side by side
         bk.ldl_pair(HI, HO, 0.01, DI, DO)
         mark()
         bk.solve(W, HO, HI, args.bits, args.rounding, seed, D_O=DO, D_I=DI, want_loss=True,

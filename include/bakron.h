@@ -194,6 +194,13 @@ int bakron_hessian_accum_w(const float* X, int64_t T, int64_t d, int64_t ldx, co
  *      not positive and finite. H is then unspecified.
  *   ws: device workspace of at least bakron_ldl_workspace_bytes(d) bytes.
  * This call waits for the stream so that NOT_SPD can be reported.
+ * Orders up to 8192 are factored by one persistent launch whose workgroups wait
+ * on each other's progress, each wait bounded (10 s of wall clock; the
+ * environment variable BAKRON_LDL_WAIT_LIMIT_US, read at each call, lowers it so
+ * that tests can reach this path): a wait that runs past it stops the launch,
+ * and the call returns BAKRON_E_DEVICE with *bad_pivot = -2. BAKRON_LDL_PATH =
+ * "launch", read at each call, makes such orders take the chain of launches that
+ * larger orders take (for tests).
  */
 size_t bakron_ldl_workspace_bytes(int64_t d);
 int bakron_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, int64_t* bad_pivot,
@@ -206,13 +213,32 @@ int bakron_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, int6
  * small launches that leaves most of the GPU idle.
  *   bad_pivot_dev: DEVICE int64 (required); when the stream reaches it, it holds
  *      -1, or the index of the first pivot that was not positive and finite (H is
- *      then unspecified). The return value reports only argument, workspace and
+ *      then unspecified), or -2 if a wait between workgroups ran past its limit
+ *      (see bakron_ldl). The return value reports only argument, workspace and
  *      launch errors.
  *   ws: as for bakron_ldl; it and H, D stay in use until the stream has passed
  *      the call.
  */
 int bakron_ldl_async(float* H, int64_t d, int64_t ldh, double damp_rel, float* D,
                      int64_t* bad_pivot_dev, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Two independent damped LDL factorisations (YAQA section 4, as above: H_I and
+ * H_O of one layer) enqueued without waiting. When both orders are at most 8192
+ * (and BAKRON_LDL_PATH is not "launch") they share one persistent launch on
+ * stream_a, whose workgroups serve both chains of diagonal blocks alike, and
+ * nothing is enqueued on stream_b. Otherwise A is factored on stream_a and B on
+ * stream_b, side by side, both by the chain of launches (a persistent launch for
+ * the smaller one would hold a slot on every compute unit that the larger one's
+ * updates need). The caller orders stream_b after earlier work and stream_a after
+ * stream_b as it needs; stream_b may equal stream_a. Each other argument is as
+ * for bakron_ldl_async, per matrix; damp_rel applies to both. A failure of one
+ * (bad pivot, or -2) leaves the other's result intact.
+ */
+int bakron_ldl_pair_async(float* HA, int64_t dA, int64_t ldha, float* DA, int64_t* bad_pivot_dev_A,
+                          void* wsA, size_t wsA_bytes, float* HB, int64_t dB, int64_t ldhb, float* DB,
+                          int64_t* bad_pivot_dev_B, void* wsB, size_t wsB_bytes, double damp_rel,
+                          void* stream_a, void* stream_b);
 
 /*
  * BaKron solve: round W* (m x n) under H_O (x) H_I given the strict upper LDL

@@ -68,6 +68,9 @@ def _load() -> ctypes.CDLL:
     lib.bakron_ldl.argtypes = [vp, i64, i64, ctypes.c_double, vp, ctypes.POINTER(i64), vp, sz, vp]
     lib.bakron_ldl_async.restype = ctypes.c_int
     lib.bakron_ldl_async.argtypes = [vp, i64, i64, ctypes.c_double, vp, vp, vp, sz, vp]
+    lib.bakron_ldl_pair_async.restype = ctypes.c_int
+    lib.bakron_ldl_pair_async.argtypes = [vp, i64, i64, vp, vp, vp, sz, vp, i64, i64, vp, vp, vp, sz,
+                                          ctypes.c_double, vp, vp]
     lib.bakron_layer_report.restype = ctypes.c_int
     lib.bakron_layer_report.argtypes = [i64, i64, vp, vp, vp, vp, i64, vp, i64, vp, vp]
     lib.bakron_rht.restype = ctypes.c_int
@@ -92,6 +95,7 @@ EXPORTS = ("bakron_abi_version", "bakron_status_str", "bakron_hessian_accum_work
            "bakron_hessian_accum", "bakron_hessian_accum_t", "bakron_hessian_accum_tb",
            "bakron_hessian_accum_w",
            "bakron_token_weights_workspace_bytes", "bakron_token_weights", "bakron_ldl_workspace_bytes", "bakron_ldl", "bakron_ldl_async",
+           "bakron_ldl_pair_async",
            "bakron_solve_workspace_bytes", "bakron_solve", "bakron_solve_noalloc", "bakron_rht",
            "bakron_layer_report")
 
@@ -285,7 +289,8 @@ def ldl(H: torch.Tensor, damp_rel: float = 0.01, D: Optional[torch.Tensor] = Non
     """In place: H + damp_rel*mean(diag H)*I = (L + I) diag(D) (L + I)^T, L strictly upper.
 
     Returns (H, D): H holds L above its diagonal, D on it and zeros below.
-    Raises BakronError(status=BAKRON_E_NOT_SPD) with .bad_pivot on failure.
+    Raises BakronError(status=BAKRON_E_NOT_SPD) with .bad_pivot on failure, or
+    (status=BAKRON_E_DEVICE, .bad_pivot = -2) if a wait between workgroups timed out.
     """
     ldh = _mat(H, "H")
     d = H.shape[0]
@@ -310,10 +315,12 @@ def ldl_pair(HA: torch.Tensor, HB: torch.Tensor, damp_rel: float = 0.01,
              DA: Optional[torch.Tensor] = None, DB: Optional[torch.Tensor] = None):
     """Two independent damped LDL factorisations at once (H_I and H_O of one layer).
 
-    HA is factored on the current stream and HB on a second stream that starts after
-    the current stream's earlier work; the current stream then waits for it, and the
+    bakron_ldl_pair_async with the current stream and a second one that starts after
+    the current stream's earlier work; the current stream then waits for it. The
     call waits for both to report their pivots. Returns ((HA, DA), (HB, DB)); raises
-    BakronError(status=BAKRON_E_NOT_SPD) with .bad_pivot and .which (0 for HA, 1 for HB).
+    BakronError(status=BAKRON_E_NOT_SPD) with .bad_pivot and .which (0 for HA, 1 for
+    HB), or (status=BAKRON_E_DEVICE, .bad_pivot = -2) if a wait between workgroups
+    timed out.
     """
     mats = []
     for H, D, name in ((HA, DA, "HA"), (HB, DB, "HB")):
@@ -329,25 +336,25 @@ def ldl_pair(HA: torch.Tensor, HB: torch.Tensor, damp_rel: float = 0.01,
     cur = torch.cuda.current_stream(dev)
     aux = _aux_stream(dev)
     info = torch.full((2,), -1, dtype=torch.int64, device=dev)
+    ws = [_workspace(LIB.bakron_ldl_workspace_bytes(m[2]), dev, slot=k) for k, m in enumerate(mats)]
     start = torch.cuda.Event()
     start.record(cur)
     aux.wait_event(start)
-    status = []
-    for k, ((H, D, d, ldh), s) in enumerate(zip(mats, (cur, aux))):
-        nb = LIB.bakron_ldl_workspace_bytes(d)
-        ws = _workspace(nb, dev, slot=k)
-        status.append(LIB.bakron_ldl_async(_ptr(H), d, ldh, damp_rel, _ptr(D),
-                                           ctypes.c_void_p(info.data_ptr() + 8 * k), _ptr(ws), nb,
-                                           ctypes.c_void_p(s.cuda_stream)))
+    (HA_, DA_, dA, lda), (HB_, DB_, dB, ldb) = mats
+    st = LIB.bakron_ldl_pair_async(_ptr(HA_), dA, lda, _ptr(DA_), ctypes.c_void_p(info.data_ptr()),
+                                   _ptr(ws[0]), ws[0].numel(), _ptr(HB_), dB, ldb, _ptr(DB_),
+                                   ctypes.c_void_p(info.data_ptr() + 8), _ptr(ws[1]), ws[1].numel(),
+                                   damp_rel, ctypes.c_void_p(cur.cuda_stream), ctypes.c_void_p(aux.cuda_stream))
+    status = [st, st]
     done = torch.cuda.Event()
     done.record(aux)
     cur.wait_event(done)
     bad = info.cpu().tolist()  # waits for both factorisations
     for k in range(2):
         _check("bakron_ldl_async", status[k])
-        if bad[k] >= 0:
-            err = BakronError("bakron_ldl_async", BAKRON_E_NOT_SPD,
-                              LIB.bakron_status_str(BAKRON_E_NOT_SPD).decode())
+        if bad[k] >= 0 or bad[k] == -2:
+            st = BAKRON_E_NOT_SPD if bad[k] >= 0 else BAKRON_E_DEVICE
+            err = BakronError("bakron_ldl_async", st, LIB.bakron_status_str(st).decode())
             err.bad_pivot = int(bad[k])
             err.which = k
             raise err

@@ -1,7 +1,11 @@
 """Build libbakron.so (HIP, gfx950) in-tree with hipcc.
 
 The library is written for gfx950 only. Packed fp32 instructions are disabled
-(-packed-fp32-ops) for every device compile.
+(-packed-fp32-ops) for every device compile. In the LDL the fp64 MFMA
+instructions take their accumulators in ordinary VGPRs (-amdgpu-mfma-vgpr-form):
+with accumulation registers the compiler copied every tile's accumulators
+between the two register files on each pass of the k-loop. The Hessian kernels
+measured a few per cent slower with the option, so it is set per file.
 """
 from __future__ import annotations
 
@@ -23,11 +27,12 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(os.path.dirname(HERE), "include"),
 ]
+FILE_FLAGS = {"bk_ldl.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -175,6 +175,19 @@ int bakron_ldl_async(float* H, int64_t d, int64_t ldh, double damp_rel, float* D
     return bk::enqueue_ldl(H, d, ldh, damp_rel, D, ws, (hipStream_t)stream, bad_pivot_dev);
 }
 
+int bakron_ldl_pair_async(float* HA, int64_t dA, int64_t ldha, float* DA, int64_t* bad_pivot_dev_A,
+                          void* wsA, size_t wsA_bytes, float* HB, int64_t dB, int64_t ldhb, float* DB,
+                          int64_t* bad_pivot_dev_B, void* wsB, size_t wsB_bytes, double damp_rel,
+                          void* stream_a, void* stream_b) {
+    if (!HA || !bad_pivot_dev_A || dA <= 0 || bad_ld(ldha, dA)) return BAKRON_E_INVALID_ARG;
+    if (!HB || !bad_pivot_dev_B || dB <= 0 || bad_ld(ldhb, dB)) return BAKRON_E_INVALID_ARG;
+    if (!(damp_rel >= 0.0) || !(damp_rel < INFINITY)) return BAKRON_E_INVALID_ARG;
+    if (!wsA || wsA_bytes < bk::ldl_workspace_bytes(dA)) return BAKRON_E_WORKSPACE;
+    if (!wsB || wsB_bytes < bk::ldl_workspace_bytes(dB)) return BAKRON_E_WORKSPACE;
+    return bk::enqueue_ldl_pair(HA, dA, ldha, DA, wsA, bad_pivot_dev_A, HB, dB, ldhb, DB, wsB, bad_pivot_dev_B,
+                                damp_rel, (hipStream_t)stream_a, (hipStream_t)stream_b);
+}
+
 size_t bakron_solve_workspace_bytes(int64_t m, int64_t n) {
     if (m <= 0 || n <= 0) return 0;
     return bk::solve_workspace_bytes(m, n);

@@ -160,6 +160,15 @@ __device__ __forceinline__ int acc32_col(int tid) {
 // loaded); same structure as the fp32 tile: loads of the next slice in
 // flight during the MFMAs, MFMA operands read one k-step ahead.
 // ---------------------------------------------------------------------------
+// threadIdx.x through an opaque move: what is derived from it is computed where
+// it is used, not hoisted out of a persistent kernel's task loop (where it would
+// hold registers across every task)
+__device__ __forceinline__ int tid_opaque() {
+    int r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"((int)threadIdx.x));
+    return r;
+}
+
 template <int KT>
 struct GemmSmemF64 {
     double a[2][KT][kTile];
@@ -171,8 +180,7 @@ struct GemmSmemF64 {
 // aligned rows (rows past K clamped here, zeroed by the store).
 template <int KT, bool kFast>
 __device__ __forceinline__ void slice_load_f64(const double* __restrict__ A, int64_t lda, int R,
-                                               int64_t K, int64_t k0, f64x2 (&v)[KT / 8]) {
-    const int t = threadIdx.x;
+                                               int64_t K, int64_t k0, f64x2 (&v)[KT / 8], int t) {
     const int c2 = (t & 31) << 1;
 #pragma unroll
     for (int u = 0; u < KT / 8; ++u) {
@@ -189,8 +197,7 @@ __device__ __forceinline__ void slice_load_f64(const double* __restrict__ A, int
 
 template <int KT>
 __device__ __forceinline__ void slice_store_f64(double (&dst)[KT][kTile], const f64x2 (&v)[KT / 8],
-                                                int64_t K, int64_t k0) {
-    const int t = threadIdx.x;
+                                                int64_t K, int64_t k0, int t) {
     const int c2 = (t & 31) << 1;
 #pragma unroll
     for (int u = 0; u < KT / 8; ++u) {
@@ -203,24 +210,25 @@ template <int KT, bool kFast>
 __device__ __forceinline__ void tile_gemm_f64_impl(const double* __restrict__ A, int64_t lda, int R,
                                                    const double* __restrict__ B, int64_t ldb, int Cn,
                                                    int64_t K, f64x4 (&acc)[2][2], GemmSmemF64<KT>& sm) {
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int tid = tid_opaque();
+    const int lane = tid & 63;
+    const int w = tid >> 6;
     const int ra = (w >> 1) * 32 + (lane & 15);
     const int rb = (w & 1) * 32 + (lane & 15);
     const int kq = lane >> 4;
     const int64_t nk = (K + KT - 1) / KT;
     f64x2 va[KT / 8], vb[KT / 8];
-    slice_load_f64<KT, kFast>(A, lda, R, K, 0, va);
-    slice_load_f64<KT, kFast>(B, ldb, Cn, K, 0, vb);
-    slice_store_f64<KT>(sm.a[0], va, K, 0);
-    slice_store_f64<KT>(sm.b[0], vb, K, 0);
+    slice_load_f64<KT, kFast>(A, lda, R, K, 0, va, tid);
+    slice_load_f64<KT, kFast>(B, ldb, Cn, K, 0, vb, tid);
+    slice_store_f64<KT>(sm.a[0], va, K, 0, tid);
+    slice_store_f64<KT>(sm.b[0], vb, K, 0, tid);
     __syncthreads();
     for (int64_t it = 0; it < nk; ++it) {
         const int cur = (int)(it & 1);
         const bool more = it + 1 < nk;
         if (more) {
-            slice_load_f64<KT, kFast>(A, lda, R, K, (it + 1) * KT, va);
-            slice_load_f64<KT, kFast>(B, ldb, Cn, K, (it + 1) * KT, vb);
+            slice_load_f64<KT, kFast>(A, lda, R, K, (it + 1) * KT, va, tid);
+            slice_load_f64<KT, kFast>(B, ldb, Cn, K, (it + 1) * KT, vb, tid);
         }
         double fa[2][2], fb[2][2];
         fa[0][0] = sm.a[cur][kq][ra];
@@ -245,8 +253,8 @@ __device__ __forceinline__ void tile_gemm_f64_impl(const double* __restrict__ A,
                     acc[bi][bj] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[c][bi], fb[c][bj], acc[bi][bj], 0, 0, 0);
         }
         if (more) {
-            slice_store_f64<KT>(sm.a[cur ^ 1], va, K, (it + 1) * KT);
-            slice_store_f64<KT>(sm.b[cur ^ 1], vb, K, (it + 1) * KT);
+            slice_store_f64<KT>(sm.a[cur ^ 1], va, K, (it + 1) * KT, tid);
+            slice_store_f64<KT>(sm.b[cur ^ 1], vb, K, (it + 1) * KT, tid);
         }
         __syncthreads();
     }
@@ -270,11 +278,11 @@ __device__ __forceinline__ void tile_gemm_f64(const double* __restrict__ A, int6
 // (v_mfma_f64_16x16x4_f64 output layout, checked on gfx950: col = lane % 16,
 // row = lane / 16 + 4 r).
 __device__ __forceinline__ int acc64_row(int bi, int r) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int tid = tid_opaque(), lane = tid & 63, w = tid >> 6;
     return (w >> 1) * 32 + bi * 16 + (lane >> 4) + 4 * r;
 }
 __device__ __forceinline__ int acc64_col(int bj) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int tid = tid_opaque(), lane = tid & 63, w = tid >> 6;
     return (w & 1) * 32 + bj * 16 + (lane & 15);
 }
 
@@ -317,5 +325,38 @@ __device__ __forceinline__ void split2_value(float x, int e, uint32_t& h, uint32
     h = (uint32_t)__builtin_bit_cast(uint16_t, hv);
     l = (uint32_t)__builtin_bit_cast(uint16_t, lv);
 }
+
+// ---------------------------------------------------------------------------
+// Hand-over primitives for persistent kernels. Each XCD has its own L2, so
+// data passed between workgroups is written with device-coherent (agent-scope)
+// stores, which go through to memory, and a producer raises its counter (also
+// agent scope) only once those stores have completed (s_waitcnt vmcnt(0)): no
+// cache-wide write-back is needed. A consumer that then reads through the
+// caches first invalidates them (acquire fence at agent scope).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int ld_flag(const int* f) {
+    return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_flag(int* f, int v) {
+    __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent(float* q, float v) {
+    __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent(double* q, double v) {
+    __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16 bytes as two device-coherent 8-byte stores
+__device__ __forceinline__ void st_coherent16(f16x8* q, const uint32_t (&v)[4]) {
+    uint64_t* q64 = reinterpret_cast<uint64_t*>(q);
+    __hip_atomic_store(q64, (uint64_t)v[0] | ((uint64_t)v[1] << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q64 + 1, (uint64_t)v[2] | ((uint64_t)v[3] << 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+// keeps the compiler from moving the data loads above the counter check
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+// the wave's own memory operations, cache maintenance included, have completed
+__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 }  // namespace bk

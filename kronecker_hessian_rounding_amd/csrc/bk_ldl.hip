@@ -17,6 +17,9 @@
 //   outer : after each super-panel, A[0:s0, 0:s0] -= C_S C_S^T with
 //           K = the super-panel width                 (MFMA, lower part)
 #include <algorithm>
+#include <climits>
+#include <cstdlib>
+#include <cstring>
 
 #include "bk_common.hpp"
 #include "bk_internal.hpp"
@@ -29,30 +32,42 @@ constexpr int kLdlKT = 32;   // k-slice depth of the fp64 panel / inner-update G
 
 struct LdlWs {
     double* A;     // d x d working copy, lower triangle used, ld = d
-    double* Wt;    // 64 x 64: Wt[q][p] = (C22^-1)[p][q] of the current diagonal block
+    double* Wt;    // one 64 x 64 slot per block: Wt[q][p] = (C22^-1)[p][q] of that diagonal block
     double* lam;   // damping lambda
-    int64_t* info; // -1, or the first failing pivot index
+    int64_t* info; // -1, the first failing pivot index, or -2 (a wait of the scheduled path timed out)
+    int* cnt;      // scheduled path: one progress counter per 64x64 tile of A (nb x nb)
+    int* ticket;   // scheduled path: next task ticket
+    int* abort;    // scheduled path: nonzero once any workgroup gives up
 };
 
+static int64_t ldl_blocks(int64_t d) { return (d + kTile - 1) / kTile; }
+
 static LdlWs carve(void* ws, int64_t d) {
+    const size_t nb = (size_t)ldl_blocks(d);
     char* p = (char*)ws;
     LdlWs w;
     w.A = (double*)p;
     p += align256(sizeof(double) * (size_t)d * (size_t)d);
     w.Wt = (double*)p;
-    p += align256(sizeof(double) * 64 * 64);
+    p += align256(sizeof(double) * 4096 * nb);
     w.lam = (double*)p;
     p += 256;
     w.info = (int64_t*)p;
+    p += 256;
+    w.ticket = (int*)p;
+    w.abort = w.ticket + 1;
+    p += 256;
+    w.cnt = (int*)p;
     return w;
 }
 
 size_t ldl_workspace_bytes(int64_t d) {
-    return align256(sizeof(double) * (size_t)d * (size_t)d) + align256(sizeof(double) * 4096) +
-           256 + 256;
+    const size_t nb = (size_t)ldl_blocks(d);
+    return align256(sizeof(double) * (size_t)d * (size_t)d) + align256(sizeof(double) * 4096 * nb) +
+           3 * 256 + align256(sizeof(int) * nb * nb);
 }
 
-// lambda = damp_rel * mean(diag H) in fp64; info = -1.
+// lambda = damp_rel * mean(diag H) in fp64; info = -1; the scheduler's ticket and abort flag 0.
 __global__ __launch_bounds__(kThreads) void k_ldl_init(const float* __restrict__ H, int64_t d,
                                                        int64_t ldh, double damp_rel, LdlWs w) {
     __shared__ double red[kThreads];
@@ -67,15 +82,19 @@ __global__ __launch_bounds__(kThreads) void k_ldl_init(const float* __restrict__
     if (threadIdx.x == 0) {
         *w.lam = damp_rel * (red[0] / (double)d);
         *w.info = -1;
+        *w.ticket = 0;
+        *w.abort = 0;
     }
 }
 
 // A[r][c] = H[c][r] (upper triangle of H read, lower triangle of A written),
-// plus lambda on the diagonal; 64x64 tiles transposed through LDS.
+// plus lambda on the diagonal; 64x64 tiles transposed through LDS. Each tile's
+// progress counter starts at 0.
 __global__ __launch_bounds__(kThreads) void k_ldl_load(const float* __restrict__ H, int64_t d,
                                                        int64_t ldh, LdlWs w) {
     const int64_t rt = blockIdx.y, ct = blockIdx.x;  // tile of A: rows rt, cols ct, rt >= ct
     if (ct > rt) return;
+    if (threadIdx.x == 0) w.cnt[rt * gridDim.x + ct] = 0;
     __shared__ float tile[kTile][kTile + 1];
     const int64_t r0 = rt * kTile, c0 = ct * kTile;
     for (int e = threadIdx.x; e < kTile * kTile; e += kThreads) {
@@ -239,69 +258,47 @@ __device__ __forceinline__ void ldl_inv_off(DiagSmem& s, int I, int J, int lane)
     for (int r = 0; r < 4; ++r) s.xs[16 * I + (lane >> 4) + 4 * r][16 * J + (lane & 15)] = -xacc[r];
 }
 
-// With pn, the block first takes the update of the panel block just formed below it:
-// u[i][j] -= sum_{p < np} pn[p d + i] pn[p d + j] (np rows of C12^T, the block's 64 columns).
-__device__ __forceinline__ void diag_body(int64_t d, int64_t k0, int nb, const LdlWs& w, DiagSmem& s,
-                                          const double* pn = nullptr, int np = 0) {
-    const int t = threadIdx.x;
-    const int lane = t & 63;
-    const int wv = t >> 6;
-    {
-        // the block, the panel rows and the status word in flight together
-        constexpr int kPer = 64 * 64 / kThreads;
-        double v[kPer], pv[kPer];
+// u[i][j] -= sum_p xs[p][i] xs[p][j] on and above the diagonal: the update of the
+// block by the 64 rows held in xs (rows of the panel block just formed below it,
+// zero past its last row). 32x32 quadrants, one wave each, K = 64.
+__device__ __forceinline__ void diag_syrk(DiagSmem& s, int wv, int lane) {
+    const int qi = wv >> 1, qj = wv & 1;
+    if (qi > qj) return;
+    const int ra = 32 * qi + (lane & 15), rb = 32 * qj + (lane & 15);
+    const int kq = lane >> 4;
+    f64x4 acc[2][2];
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) {
-            const int e = t + r * kThreads;
-            const int i = e & 63, j = e >> 6;
-            v[r] = (i <= j && j < nb) ? w.A[(k0 + j) * d + k0 + i] : (i == j ? 1.0 : 0.0);
-            pv[r] = (pn && j < np) ? pn[j * d + i] : 0.0;  // row j of the panel, column i
-        }
-        if (*w.info >= 0) return;  // an earlier block failed
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) {
-            const int e = t + r * kThreads;
-            s.u[e & 63][e >> 6] = v[r];
-            s.xs[e >> 6][e & 63] = pv[r];  // xs is free until the inverse
-        }
-    }
-    __syncthreads();
-    if (pn) {
-        // 32x32 quadrants on or above the diagonal, one wave each, K = 64 panel rows
-        const int qi = wv >> 1, qj = wv & 1;
-        if (qi <= qj) {
-            const int ra = 32 * qi + (lane & 15), rb = 32 * qj + (lane & 15);
-            const int kq = lane >> 4;
-            f64x4 acc[2][2];
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+        for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll 4
-            for (int kk = 0; kk < 16; ++kk) {
-                const int p = 4 * kk + kq;
-                const double fa0 = s.xs[p][ra], fa1 = s.xs[p][ra + 16];
-                const double fb0 = s.xs[p][rb], fb1 = s.xs[p][rb + 16];
-                acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa0, fb0, acc[0][0], 0, 0, 0);
-                acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa0, fb1, acc[0][1], 0, 0, 0);
-                acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa1, fb0, acc[1][0], 0, 0, 0);
-                acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa1, fb1, acc[1][1], 0, 0, 0);
-            }
-            // output layout: row = 16 bi + lane / 16 + 4 r, column = 16 bj + lane % 16
-#pragma unroll
-            for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-                for (int bj = 0; bj < 2; ++bj)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int i = 32 * qi + 16 * bi + (lane >> 4) + 4 * r;
-                        const int j = 32 * qj + 16 * bj + (lane & 15);
-                        if (i <= j) s.u[i][j] -= acc[bi][bj][r];
-                    }
-        }
-        __syncthreads();
+    for (int kk = 0; kk < 16; ++kk) {
+        const int p = 4 * kk + kq;
+        const double fa0 = s.xs[p][ra], fa1 = s.xs[p][ra + 16];
+        const double fb0 = s.xs[p][rb], fb1 = s.xs[p][rb + 16];
+        acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa0, fb0, acc[0][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa0, fb1, acc[0][1], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa1, fb0, acc[1][0], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa1, fb1, acc[1][1], 0, 0, 0);
     }
+    // output layout: row = 16 bi + lane / 16 + 4 r, column = 16 bj + lane % 16
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 32 * qi + 16 * bi + (lane >> 4) + 4 * r;
+                const int j = 32 * qj + 16 * bj + (lane & 15);
+                if (i <= j) s.u[i][j] -= acc[bi][bj][r];
+            }
+}
 
+// Factors the block held in s.u (identity past its nb rows) into C22 (left in
+// s.u, upper part) and X = C22^-1 (s.xs, upper part). Returns -1, or the local
+// index of the first failing pivot (uniform across the workgroup; the inverse
+// is then incomplete). Starts and ends with every wave at a barrier.
+__device__ __forceinline__ int diag_factor(DiagSmem& s, int nb, int wv, int lane) {
     // block column 3
     if (wv == 0) ldl_factor_bcol<3>(s, lane);
     __syncthreads();
@@ -337,13 +334,50 @@ __device__ __forceinline__ void diag_body(int64_t d, int64_t k0, int nb, const L
         ldl_inv_off(s, 1, 3, lane);
     }
     __syncthreads();
-    if (s.badj >= 0) {  // uniform after the barrier
-        if (t == 0) *w.info = k0 + s.badj;
-        return;
-    }
+    const int badj = s.badj;
+    if (badj >= 0) return badj;
     // X[0][1], X[0][2], X[0][3]
     if (wv > 0) ldl_inv_off(s, 0, wv, lane);
     __syncthreads();
+    return -1;
+}
+
+// With pn, the block first takes the update of the panel block just formed below it:
+// u[i][j] -= sum_{p < np} pn[p d + i] pn[p d + j] (np rows of C12^T, the block's 64 columns).
+__device__ __forceinline__ void diag_body(int64_t d, int64_t k0, int nb, const LdlWs& w, DiagSmem& s,
+                                          const double* pn = nullptr, int np = 0) {
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wv = t >> 6;
+    {
+        // the block, the panel rows and the status word in flight together
+        constexpr int kPer = 64 * 64 / kThreads;
+        double v[kPer], pv[kPer];
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+            const int e = t + r * kThreads;
+            const int i = e & 63, j = e >> 6;
+            v[r] = (i <= j && j < nb) ? w.A[(k0 + j) * d + k0 + i] : (i == j ? 1.0 : 0.0);
+            pv[r] = (pn && j < np) ? pn[j * d + i] : 0.0;  // row j of the panel, column i
+        }
+        if (*w.info >= 0) return;  // an earlier block failed
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+            const int e = t + r * kThreads;
+            s.u[e & 63][e >> 6] = v[r];
+            s.xs[e >> 6][e & 63] = pv[r];  // xs is free until the inverse
+        }
+    }
+    __syncthreads();
+    if (pn) {
+        diag_syrk(s, wv, lane);
+        __syncthreads();
+    }
+    const int badj = diag_factor(s, nb, wv, lane);
+    if (badj >= 0) {
+        if (t == 0) *w.info = k0 + badj;
+        return;
+    }
 
     // C22 back into A (lower storage: A[k0 + j][k0 + i] = C[i][j]); Wt[j][i] = X[i][j].
     // Every LDS read of the thread first, then the stores.
@@ -462,6 +496,400 @@ __global__ __launch_bounds__(kThreads) void k_ldl_diag_update(int64_t d, int64_t
     update_tile<kLdlKT>(d, r0, r_hi, c0, c_hi, q0, K, w, sm.g);
 }
 
+// ---------------------------------------------------------------------------
+// Scheduled factorisation: the same blocked algorithm in one persistent launch
+// per factor, for orders up to kSchedMaxBlocks blocks, where the launch chain
+// above leaves the GPU mostly idle.
+//
+// Block b (last to first) needs its diagonal tile (b, b) and its panel row
+// (b, C), C < b, updated by every later block: tile (R, C) -= P_b,R^T P_b,C with
+// P_b = C12^T, the panel row of block b. The first workgroup to start runs the
+// chain alone: it factors each diagonal block and forms the panel tile
+// (b, b - 1) in LDS, which is all that the next diagonal block waits for (its
+// update by block b is applied straight from LDS). The other workgroups take
+// tasks in ticket order from a table ordered by "phase" b = nb-1 .. 0:
+//   panel  (b, C), C <= b - 2     C12^T tile = C22^-1 A(b, C)             (K = 64)
+//   near   (R, C) by block b, for the kNear rows R just below b           (K = 64)
+//   far    (R, C) by blocks b .. b + kSeg - 1, for the rows R = b - kNear - 1 - kSeg s
+// so that a row's updates from blocks more than kNear above it come in segments
+// of kSeg blocks, each as soon as its blocks are done and none longer than kSeg
+// blocks (no workgroup is tied up for long while the chain waits on short tasks).
+// Each tile's updates are applied in one fixed order (far segments from the
+// highest, then the near blocks from the highest down) and counted in its
+// progress counter; an update task computes its product first and waits for its
+// turn only to read, subtract and store. The panel of tile (b, C) is marked by
+// raising its counter one past the number of its updates. Every wait is on work
+// earlier in ticket order (the chain counts as running ahead of phase b when it
+// reaches block b), so the tasks cannot deadlock, and every wait is bounded in time.
+// ---------------------------------------------------------------------------
+constexpr int kSchedMaxBlocks = 128;  // orders up to 8192
+constexpr int kNear = 3;              // rows that take a block's update on their own
+constexpr int kSeg = 12;              // blocks per far update
+
+struct SchedArgs {
+    int64_t d;
+    int nb;
+    int ntask;            // tasks in the table; ticket 0 is the chain
+    uint64_t spin_limit;  // wall-clock ticks a single wait may take
+};
+
+// last block whose update row R takes on its own
+__host__ __device__ inline int sched_near_hi(int R, int nb) { return R + kNear < nb - 1 ? R + kNear : nb - 1; }
+// far segments of row R: blocks R + kNear + 1 .. nb - 1 in groups of kSeg
+__host__ __device__ inline int sched_nfar(int R, int nb) {
+    const int lo = R + kNear + 1;
+    return lo < nb ? (nb - lo + kSeg - 1) / kSeg : 0;
+}
+// updates tile (R, C) receives from tasks (the diagonal tile takes block R + 1's in the chain)
+__host__ __device__ inline int sched_expect(int R, int C, int nb) {
+    return sched_nfar(R, nb) + sched_near_hi(R, nb) - R - ((C == R && R + 1 < nb) ? 1 : 0);
+}
+// tasks of phase p, in table order: panels, near rows p-1 .. p-kNear, far rows p-kNear-1-kSeg s
+__host__ __device__ inline int sched_phase_tasks(int p, int nb) {
+    int n = p > 1 ? p - 1 : 0;
+    for (int R = p - 1; R >= 0 && R >= p - kNear; --R) n += (R == p - 1) ? R : R + 1;
+    for (int R = p - kNear - 1; R >= 0; R -= kSeg) n += R + 1;
+    return n;
+}
+
+struct SchedTask {
+    bool panel;
+    int R, C;    // panel: tile (lo, C); update: tile (R, C)
+    int lo, hi;  // blocks [lo, hi) whose panel rows update the tile
+    int ord;     // the update's turn on the tile
+};
+
+// task i of phase p
+__device__ __forceinline__ SchedTask sched_decode(int p, int i, int nb) {
+    SchedTask k;
+    const int npan = p > 1 ? p - 1 : 0;
+    if (i < npan) {
+        k.panel = true;
+        k.lo = p;
+        k.C = p - 2 - i;
+        return k;
+    }
+    i -= npan;
+    k.panel = false;
+    for (int R = p - 1; R >= 0 && R >= p - kNear; --R) {
+        const int top = (R == p - 1) ? R - 1 : R;  // row p - 1 leaves its diagonal tile to the chain
+        if (i <= top) {
+            k.R = R;
+            k.C = top - i;
+            k.lo = p;
+            k.hi = p + 1;
+            k.ord = sched_nfar(R, nb) + sched_near_hi(R, nb) - p;
+            return k;
+        }
+        i -= top + 1;
+    }
+    // far: segment sg of row R = p - kNear - 1 - kSeg sg, blocks p .. p + kSeg - 1
+    k.lo = p;
+    k.hi = min(p + kSeg, nb);
+    int R = p - kNear - 1, sg = 0;
+    while (i > R) {
+        i -= R + 1;
+        R -= kSeg;
+        ++sg;
+    }
+    k.R = R;
+    k.C = R - i;
+    k.ord = sched_nfar(R, nb) - 1 - sg;
+    return k;
+}
+
+// thread 0: waits until *f >= v; false if the factorisation was abandoned or this
+// wait ran past its limit (which abandons it: info = -2 unless already set)
+__device__ __forceinline__ bool sched_wait(const SchedArgs& a, const LdlWs& w, const int* f, int v) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (;;) {
+        if (ld_flag(f) >= v) return true;
+        if (ld_flag(w.abort)) return false;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > a.spin_limit) {
+            atomicCAS((unsigned long long*)w.info, ~0ull, (unsigned long long)-2ll);
+            st_flag(w.abort, 1);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// thread 0's verdict to the whole workgroup, with the caches invalidated on success
+__device__ __forceinline__ bool sched_share(bool ok, int& s_ok) {
+    if (threadIdx.x == 0) {
+        if (ok) acquire_agent();
+        vm_wait_all();
+        s_ok = ok;
+    }
+    __syncthreads();
+    const bool r = s_ok != 0;
+    __syncthreads();
+    return r;
+}
+
+// The chain: every diagonal block in turn, and the panel tile just below-left of it.
+__device__ __forceinline__ void sched_chain(const LdlWs& w, const SchedArgs& a, DiagSmem& s, int& s_ok) {
+    const int64_t d = a.d;
+    const int nb = a.nb;
+    constexpr int kPer = 64 * 64 / kThreads;
+    for (int b = nb - 1; b >= 0; --b) {
+        const int t = tid_opaque(), lane = t & 63, wv = t >> 6;
+        const int64_t k0 = (int64_t)b * kTile;
+        const int nr = (int)min<int64_t>(kTile, d - k0);
+        // (1) the diagonal block, once every update but block b + 1's is in
+        bool ok = true;
+        if (t == 0) ok = sched_wait(a, w, &w.cnt[b * nb + b], sched_expect(b, b, nb));
+        if (!sched_share(ok, s_ok)) return;
+        // 32-bit offsets from per-block bases keep the addresses to one register each;
+        // thread t holds column i = t % 64 of rows j = t / 64 + 4 r
+        const int i = t & 63, j0 = t >> 6;
+        const int di4 = 4 * (int)d;
+        double* const Ab = w.A + k0 * d + k0;
+        {
+            double v[kPer];
+#pragma unroll
+            for (int r = 0; r < kPer; ++r) {
+                const int j = j0 + 4 * r;
+                v[r] = (i <= j && j < nr) ? Ab[j0 * (int)d + i + r * di4] : (i == j ? 1.0 : 0.0);
+            }
+#pragma unroll
+            for (int r = 0; r < kPer; ++r) s.u[i][j0 + 4 * r] = v[r];
+        }
+        __syncthreads();
+        if (b + 1 < nb) {  // s.xs holds the panel tile (b + 1, b) from the step before
+            diag_syrk(s, wv, lane);
+            __syncthreads();
+        }
+        const int badj = diag_factor(s, nr, wv, lane);
+        if (badj >= 0) {
+            if (t == 0) {
+                atomicCAS((unsigned long long*)w.info, ~0ull, (unsigned long long)(k0 + badj));
+                st_flag(w.abort, 1);
+            }
+            return;
+        }
+        // C22 into A (lower storage: A[k0 + j][k0 + i] = C[i][j]), X^T into the block's Wt slot
+        double* const wb = w.Wt + (size_t)b * 4096;
+#pragma unroll 4
+        for (int r = 0; r < kPer; ++r) {
+            const int j = j0 + 4 * r;
+            const double cv = s.u[i][j];
+            const double xv = (i <= j) ? s.xs[i][j] : 0.0;
+            if (i <= j && j < nr) st_coherent(&Ab[j0 * (int)d + i + r * di4], cv);
+            st_coherent(&wb[t + r * kThreads], xv);
+        }
+        vm_wait_all();
+        __syncthreads();
+        if (t == 0) st_flag(&w.cnt[b * nb + b], sched_expect(b, b, nb) + 1);
+        if (b == 0) return;
+
+        // (2) the panel tile (b, b - 1): P = X A(b, b - 1), into A and into s.xs
+        if (t == 0) ok = sched_wait(a, w, &w.cnt[b * nb + b - 1], sched_expect(b, b - 1, nb));
+        if (!sched_share(ok, s_ok)) return;
+        double* const Pb = Ab - kTile;  // rows k0.., columns k0 - 64..
+        {
+            double v[kPer];
+#pragma unroll
+            for (int r = 0; r < kPer; ++r) {
+                const int q = j0 + 4 * r;
+                v[r] = q < nr ? Pb[j0 * (int)d + i + r * di4] : 0.0;
+            }
+#pragma unroll
+            for (int r = 0; r < kPer; ++r) s.u[j0 + 4 * r][i] = v[r];
+        }
+        __syncthreads();
+        // 32x32 quadrant per wave; X is upper triangular, so k starts at the quadrant's first row
+        const int qi = wv >> 1, qj = wv & 1;
+        f64x4 acc[2][2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
+        const int pa = 32 * qi + (lane & 15), pb = pa + 16, rc = 32 * qj + (lane & 15);
+        for (int kk = 8 * qi; kk < 16; ++kk) {
+            const int q = 4 * kk + (lane >> 4);
+            const double fa0 = q >= pa ? s.xs[pa][q] : 0.0;
+            const double fa1 = q >= pb ? s.xs[pb][q] : 0.0;
+            const double fb0 = s.u[q][rc], fb1 = s.u[q][rc + 16];
+            acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa0, fb0, acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa0, fb1, acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa1, fb0, acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa1, fb1, acc[1][1], 0, 0, 0);
+        }
+        __syncthreads();  // every read of X and of the tile is done
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int pr = 32 * qi + 16 * bi + (lane >> 4) + 4 * r;
+                    const int c = 32 * qj + 16 * bj + (lane & 15);
+                    s.xs[pr][c] = acc[bi][bj][r];
+                    if (pr < nr) st_coherent(&Pb[pr * (int)d + c], acc[bi][bj][r]);
+                }
+        vm_wait_all();
+        __syncthreads();
+        if (t == 0) st_flag(&w.cnt[b * nb + b - 1], sched_expect(b, b - 1, nb) + 1);
+    }
+}
+
+// panel tile (b, C): C12^T = C22^-1 A(b, C), in place
+__device__ __forceinline__ void sched_panel(const LdlWs& w, const SchedArgs& a, int b, int C,
+                                            GemmSmemF64<kLdlKT>& sm, int& s_ok) {
+    const int64_t d = a.d;
+    const int nb = a.nb;
+    const int64_t k0 = (int64_t)b * kTile, c0 = (int64_t)C * kTile;
+    const int nr = (int)min<int64_t>(kTile, d - k0);
+    bool ok = true;
+    if (threadIdx.x == 0)
+        ok = sched_wait(a, w, &w.cnt[b * nb + b], sched_expect(b, b, nb) + 1) &&
+             sched_wait(a, w, &w.cnt[b * nb + C], sched_expect(b, C, nb));
+    if (!sched_share(ok, s_ok)) return;
+    f64x4 acc[2][2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
+    tile_gemm_f64<kLdlKT>(w.Wt + (size_t)b * 4096, 64, nr, w.A + k0 * d + c0, d, kTile, nr, acc, sm);
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int pr = acc64_row(bi, r), rc = acc64_col(bj);
+                if (pr < nr) st_coherent(&w.A[(k0 + pr) * d + c0 + rc], acc[bi][bj][r]);
+            }
+    vm_wait_all();
+    __syncthreads();
+    if (threadIdx.x == 0) st_flag(&w.cnt[b * nb + C], sched_expect(b, C, nb) + 1);
+}
+
+// tile (R, C) -= sum over blocks [lo, hi) of P_b,R^T P_b,C, as update number `ord` of the tile
+__device__ __forceinline__ void sched_update(const LdlWs& w, const SchedArgs& a, const SchedTask& k,
+                                             GemmSmemF64<kLdlKT>& sm, int& s_ok) {
+    const int64_t d = a.d;
+    const int nb = a.nb;
+    const int R = k.R, C = k.C;
+    // the panel tiles (b, R) and (b, C) of every block b in [lo, hi): one thread per block
+    bool ok = true;
+    const int t = tid_opaque();
+    if (t < k.hi - k.lo) {
+        const int b = k.lo + t;
+        ok = sched_wait(a, w, &w.cnt[b * nb + R], sched_expect(b, R, nb) + 1);
+        if (ok && C != R) ok = sched_wait(a, w, &w.cnt[b * nb + C], sched_expect(b, C, nb) + 1);
+    }
+    if (t == 0) s_ok = 1;
+    __syncthreads();
+    if (!ok) s_ok = 0;
+    __syncthreads();
+    if (!s_ok) return;
+    if (t == 0) {
+        acquire_agent();
+        vm_wait_all();
+    }
+    __syncthreads();
+    const int64_t q0 = (int64_t)k.lo * kTile;
+    const int64_t K = min<int64_t>((int64_t)k.hi * kTile, d) - q0;
+    const int64_t r0 = (int64_t)R * kTile, c0 = (int64_t)C * kTile;
+    f64x4 acc[2][2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
+    const double* P = w.A + q0 * d;
+    tile_gemm_f64<kLdlKT>(P + r0, d, kTile, P + c0, d, kTile, K, acc, sm);
+    // this tile's turn
+    if (threadIdx.x == 0) ok = sched_wait(a, w, &w.cnt[R * nb + C], k.ord);
+    if (!sched_share(ok, s_ok)) return;
+    double old[2][2][4];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t gi = r0 + acc64_row(bi, r), gj = c0 + acc64_col(bj);
+                old[bi][bj][r] = gj <= gi ? w.A[gi * d + gj] : 0.0;
+            }
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t gi = r0 + acc64_row(bi, r), gj = c0 + acc64_col(bj);
+                if (gj <= gi) st_coherent(&w.A[gi * d + gj], old[bi][bj][r] - acc[bi][bj][r]);
+            }
+    vm_wait_all();
+    __syncthreads();
+    if (threadIdx.x == 0) st_flag(&w.cnt[R * nb + C], k.ord + 1);
+}
+
+// One or two factorisations (nf) in one launch: tickets 0 .. nf-1 are the
+// chains, the rest the two task tables merged phase by phase (factor 0's phase
+// nb-1-j, then factor 1's), so both chains are served alike. Each factor keeps
+// its own counters, abort flag and status; the ticket counter is factor 0's.
+struct SchedLaunch {
+    LdlWs w[2];
+    SchedArgs a[2];
+    int nf;
+};
+
+__global__ __launch_bounds__(kThreads, 2) void k_ldl_sched(SchedLaunch L) {
+    __shared__ union {
+        DiagSmem diag;
+        GemmSmemF64<kLdlKT> g;
+    } sm;
+    __shared__ int s_tk, s_ok;
+    // s_ps[m]: first task of merged slot m = nf j + f, factor f's phase nb_f - 1 - j
+    __shared__ int s_ps[2 * kSchedMaxBlocks + 1];
+    const int nf = L.nf;
+    const int nbmax = nf == 2 ? max(L.a[0].nb, L.a[1].nb) : L.a[0].nb;
+    for (int m = threadIdx.x; m < nf * nbmax; m += kThreads) {
+        const int j = m / nf, nb = (m % nf) ? L.a[1].nb : L.a[0].nb;
+        s_ps[m + 1] = j < nb ? sched_phase_tasks(nb - 1 - j, nb) : 0;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        s_ps[0] = 0;
+        for (int m = 0; m < nf * nbmax; ++m) s_ps[m + 1] += s_ps[m];
+    }
+    __syncthreads();
+    const int ntask = s_ps[nf * nbmax];
+    int m = 0;  // slot cursor: a workgroup's tickets only grow
+    for (;;) {
+        if (threadIdx.x == 0) s_tk = atomicAdd(L.w[0].ticket, 1);
+        __syncthreads();
+        const int tk = s_tk;
+        __syncthreads();
+        if (tk >= nf + ntask) return;
+        // the factor's arguments by selection (an indexed kernel argument would be copied
+        // to scratch memory)
+        int f;
+        if (tk < nf) {
+            f = tk;
+        } else {
+            while (s_ps[m + 1] <= tk - nf) ++m;
+            f = m % nf;
+        }
+        const LdlWs w = f ? L.w[1] : L.w[0];
+        const SchedArgs a = f ? L.a[1] : L.a[0];
+        if (tk < nf) {
+            // the chain's waves issue first on their SIMDs: workgroups of other
+            // work may share its compute unit
+            __builtin_amdgcn_s_setprio(3);
+            sched_chain(w, a, sm.diag, s_ok);
+            __builtin_amdgcn_s_setprio(0);
+            continue;
+        }
+        const SchedTask k = sched_decode(a.nb - 1 - m / nf, tk - nf - s_ps[m], a.nb);
+        if (k.panel) sched_panel(w, a, k.lo, k.C, sm.g, s_ok);
+        else sched_update(w, a, k, sm.g, s_ok);
+    }
+}
+
 // H[i][j] = C[i][j] / C[j][j] (i < j), C[j][j]^2 (i = j), 0 (i > j), with
 // C[i][j] = A[j][i]; D[j] = C[j][j]^2 if requested.
 __global__ __launch_bounds__(kThreads) void k_ldl_store(float* __restrict__ H, int64_t d,
@@ -499,43 +927,91 @@ __global__ __launch_bounds__(kThreads) void k_ldl_store(float* __restrict__ H, i
 // status word out: -1, or the first failing pivot
 __global__ void k_ldl_info_out(LdlWs w, int64_t* out) { *out = *w.info; }
 
+// The scheduled path for orders up to kSchedMaxBlocks blocks, else the launch
+// chain; BAKRON_LDL_PATH = "launch" or "scheduled" (read at each call) picks one
+// where both apply, for tests.
+static bool use_sched(int64_t nbt) {
+    if (nbt > kSchedMaxBlocks) return false;
+    const char* e = std::getenv("BAKRON_LDL_PATH");
+    return !(e && std::strcmp(e, "launch") == 0);
+}
+
+static SchedArgs sched_args(int64_t d, uint64_t spin_limit) {
+    SchedArgs a;
+    a.d = d;
+    a.nb = (int)ldl_blocks(d);
+    a.ntask = 0;
+    for (int p = 0; p < a.nb; ++p) a.ntask += sched_phase_tasks(p, a.nb);
+    a.spin_limit = spin_limit;
+    return a;
+}
+
+// the scheduled factorisation of nf (1 or 2) matrices, already loaded, in one launch
+static void enqueue_sched(int nf, const int64_t* d, const LdlWs* w, hipStream_t stream) {
+    // 10 s, or BAKRON_LDL_WAIT_LIMIT_US (a test hook that makes the waits expire)
+    uint64_t limit_us = 10ull * 1000 * 1000;
+    if (const char* e = std::getenv("BAKRON_LDL_WAIT_LIMIT_US")) {
+        const long long v = std::atoll(e);
+        if (v > 0) limit_us = (uint64_t)v;
+    }
+    const DeviceInfo di = device_info();
+    const uint64_t spin = (uint64_t)di.clock_khz * limit_us / 1000ull;
+    SchedLaunch L;
+    L.nf = nf;
+    int64_t total = 0;
+    for (int f = 0; f < 2; ++f) {
+        const int g = f < nf ? f : 0;
+        L.w[f] = w[g];
+        L.a[f] = sched_args(d[g], spin);
+        if (f < nf) total += L.a[f].ntask + 1;
+    }
+    // one workgroup per compute unit, for one factor or two: more workgroups take
+    // tickets further ahead of the chains and mostly wait (measured slower)
+    const int grid = (int)std::min<int64_t>(di.cus, total);
+    hipLaunchKernelGGL(k_ldl_sched, dim3((unsigned)grid), dim3(kThreads), 0, stream, L);
+}
+
 int enqueue_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, void* ws,
-                hipStream_t stream, int64_t* info_dev) {
+                hipStream_t stream, int64_t* info_dev, bool allow_sched) {
     LdlWs w = carve(ws, d);
-    const int64_t nbt = (d + kTile - 1) / kTile;
+    const int64_t nbt = ldl_blocks(d);
     if (nbt > 65535) return BAKRON_E_INVALID_ARG;
     hipLaunchKernelGGL(k_ldl_init, dim3(1), dim3(kThreads), 0, stream, H, d, ldh, damp_rel, w);
     hipLaunchKernelGGL(k_ldl_load, dim3((unsigned)nbt, (unsigned)nbt), dim3(kThreads), 0, stream,
                        H, d, ldh, w);
-    // Per 64-wide block k0 (last to first) of each 256-wide super-panel [s0, s1):
-    //   panel(k0)
-    //   diag(k0 - 64) + inner(k0)      -- one launch: the next diagonal block takes this
-    //                                     block's update and is factored beside the rest
-    //                                     of this block's inner update
-    // and after the super-panel the outer update, then the next super-panel's first
-    // diagonal block on its own.
-    const int64_t nsuper = (d + kSuper - 1) / kSuper;
-    for (int64_t s = nsuper - 1; s >= 0; --s) {
-        const int64_t s0 = s * kSuper, s1 = std::min<int64_t>(s0 + kSuper, d);
-        const int64_t top = ((s1 - 1) / 64) * 64;
-        hipLaunchKernelGGL(k_ldl_diag, dim3(1), dim3(kThreads), 0, stream, d, top,
-                           (int)std::min<int64_t>(64, d - top), w);
-        for (int64_t k0 = top; k0 >= s0; k0 -= 64) {
-            const int nb = (int)std::min<int64_t>(64, d - k0);
-            if (k0 > 0) {
-                hipLaunchKernelGGL(k_ldl_panel, dim3((unsigned)((k0 + 63) / 64)), dim3(kThreads),
-                                   0, stream, d, k0, nb, w);
+    if (allow_sched && use_sched(nbt)) {
+        enqueue_sched(1, &d, &w, stream);
+    } else {
+        // Per 64-wide block k0 (last to first) of each 256-wide super-panel [s0, s1):
+        //   panel(k0)
+        //   diag(k0 - 64) + inner(k0)      -- one launch: the next diagonal block takes this
+        //                                     block's update and is factored beside the rest
+        //                                     of this block's inner update
+        // and after the super-panel the outer update, then the next super-panel's first
+        // diagonal block on its own.
+        const int64_t nsuper = (d + kSuper - 1) / kSuper;
+        for (int64_t s = nsuper - 1; s >= 0; --s) {
+            const int64_t s0 = s * kSuper, s1 = std::min<int64_t>(s0 + kSuper, d);
+            const int64_t top = ((s1 - 1) / 64) * 64;
+            hipLaunchKernelGGL(k_ldl_diag, dim3(1), dim3(kThreads), 0, stream, d, top,
+                               (int)std::min<int64_t>(64, d - top), w);
+            for (int64_t k0 = top; k0 >= s0; k0 -= 64) {
+                const int nb = (int)std::min<int64_t>(64, d - k0);
+                if (k0 > 0) {
+                    hipLaunchKernelGGL(k_ldl_panel, dim3((unsigned)((k0 + 63) / 64)), dim3(kThreads),
+                                       0, stream, d, k0, nb, w);
+                }
+                if (k0 > s0) {  // rows [s0, k0) of the super-panel, every column < k0
+                    const int64_t rt = (k0 - s0 + kTile - 1) / kTile, ct = (k0 + kTile - 1) / kTile;
+                    hipLaunchKernelGGL(k_ldl_diag_update, dim3((unsigned)(1 + rt * ct)), dim3(kThreads),
+                                       0, stream, d, k0 - 64, s0, k0, k0, k0, (int64_t)nb, (int)ct, w);
+                }
             }
-            if (k0 > s0) {  // rows [s0, k0) of the super-panel, every column < k0
-                const int64_t rt = (k0 - s0 + kTile - 1) / kTile, ct = (k0 + kTile - 1) / kTile;
-                hipLaunchKernelGGL(k_ldl_diag_update, dim3((unsigned)(1 + rt * ct)), dim3(kThreads),
-                                   0, stream, d, k0 - 64, s0, k0, k0, k0, (int64_t)nb, (int)ct, w);
+            if (s0 > 0) {
+                const int64_t tt = (s0 + kTile - 1) / kTile;
+                hipLaunchKernelGGL(k_ldl_update<16>, dim3((unsigned)tt, (unsigned)tt), dim3(kThreads), 0,
+                                   stream, d, (int64_t)0, s0, s0, s0, s1 - s0, w);
             }
-        }
-        if (s0 > 0) {
-            const int64_t tt = (s0 + kTile - 1) / kTile;
-            hipLaunchKernelGGL(k_ldl_update<16>, dim3((unsigned)tt, (unsigned)tt), dim3(kThreads), 0,
-                               stream, d, (int64_t)0, s0, s0, s0, s1 - s0, w);
         }
     }
     hipLaunchKernelGGL(k_ldl_store, dim3((unsigned)nbt, (unsigned)nbt), dim3(kThreads), 0, stream,
@@ -544,9 +1020,43 @@ int enqueue_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, voi
     return hipGetLastError() == hipSuccess ? BAKRON_OK : BAKRON_E_DEVICE;
 }
 
+int enqueue_ldl_pair(float* HA, int64_t dA, int64_t ldha, float* DA, void* wsA, int64_t* infoA,
+                     float* HB, int64_t dB, int64_t ldhb, float* DB, void* wsB, int64_t* infoB,
+                     double damp_rel, hipStream_t stream, hipStream_t stream_b) {
+    const int64_t nbA = ldl_blocks(dA), nbB = ldl_blocks(dB);
+    if (!use_sched(nbA) || !use_sched(nbB)) {
+        // Side by side on the two streams, both by the chain of launches: a persistent
+        // launch for the smaller one would hold a slot on every compute unit for the
+        // whole of its run, which the larger one's wide updates need.
+        const int st = enqueue_ldl(HA, dA, ldha, damp_rel, DA, wsA, stream, infoA, false);
+        if (st != BAKRON_OK) return st;
+        return enqueue_ldl(HB, dB, ldhb, damp_rel, DB, wsB, stream_b, infoB, false);
+    }
+    const LdlWs w[2] = {carve(wsA, dA), carve(wsB, dB)};
+    const int64_t d[2] = {dA, dB};
+    float* H[2] = {HA, HB};
+    float* D[2] = {DA, DB};
+    const int64_t ldh[2] = {ldha, ldhb};
+    int64_t* info[2] = {infoA, infoB};
+    for (int f = 0; f < 2; ++f) {
+        const int64_t nbt = ldl_blocks(d[f]);
+        hipLaunchKernelGGL(k_ldl_init, dim3(1), dim3(kThreads), 0, stream, H[f], d[f], ldh[f], damp_rel, w[f]);
+        hipLaunchKernelGGL(k_ldl_load, dim3((unsigned)nbt, (unsigned)nbt), dim3(kThreads), 0, stream, H[f],
+                           d[f], ldh[f], w[f]);
+    }
+    enqueue_sched(2, d, w, stream);
+    for (int f = 0; f < 2; ++f) {
+        const int64_t nbt = ldl_blocks(d[f]);
+        hipLaunchKernelGGL(k_ldl_store, dim3((unsigned)nbt, (unsigned)nbt), dim3(kThreads), 0, stream, H[f],
+                           d[f], ldh[f], D[f], w[f]);
+        hipLaunchKernelGGL(k_ldl_info_out, dim3(1), dim3(1), 0, stream, w[f], info[f]);
+    }
+    return hipGetLastError() == hipSuccess ? BAKRON_OK : BAKRON_E_DEVICE;
+}
+
 int run_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, int64_t* bad_pivot,
             void* ws, hipStream_t stream) {
-    const int st = enqueue_ldl(H, d, ldh, damp_rel, D, ws, stream, nullptr);
+    const int st = enqueue_ldl(H, d, ldh, damp_rel, D, ws, stream, nullptr, true);
     if (st != BAKRON_OK) return st;
     const LdlWs w = carve(ws, d);
     int64_t info = -1;
@@ -555,6 +1065,7 @@ int run_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, int64_t
         return BAKRON_E_DEVICE;
     if (hipStreamSynchronize(stream) != hipSuccess) return BAKRON_E_DEVICE;
     if (bad_pivot) *bad_pivot = info;
+    if (info == -2) return BAKRON_E_DEVICE;  // a wait between workgroups ran past its limit
     return info >= 0 ? BAKRON_E_NOT_SPD : BAKRON_OK;
 }
 

@@ -171,37 +171,9 @@ __device__ __forceinline__ float* part_ptr(const SolveParams& p, int d, int slot
     return p.parts + ((((size_t)(d % kRing) * p.maxleaf + slot) * 2 + kind) * kNch + c) * (kB * kB);
 }
 
-// ---------------------------------------------------------------------------
-// hand-over primitives. Each XCD has its own L2, so data passed between
-// workgroups is written with device-coherent (agent-scope) stores, which go
-// through to memory, and a producer raises its counter (also agent scope)
-// only once those stores have completed (s_waitcnt vmcnt(0)): no cache-wide
-// write-back is needed. A consumer that then reads through the caches first
-// invalidates them (acquire fence at agent scope); the hand-overs inside a
-// leaf's sweep read with device-coherent loads instead, so the sweep never
-// waits on cache maintenance.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int ld_flag(const int* f) {
-    return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_flag(int* f, int v) {
-    __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_coherent(float* q, float v) {
-    __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// 16 bytes as two device-coherent 8-byte stores
-__device__ __forceinline__ void st_coherent16(f16x8* q, const uint32_t (&v)[4]) {
-    uint64_t* q64 = reinterpret_cast<uint64_t*>(q);
-    __hip_atomic_store(q64, (uint64_t)v[0] | ((uint64_t)v[1] << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(q64 + 1, (uint64_t)v[2] | ((uint64_t)v[3] << 32), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-// keeps the compiler from moving the data loads above the counter check
-__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
-// the wave's own memory operations, cache maintenance included, have completed
-__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Hand-overs between workgroups use the primitives of bk_common.hpp; those
+// inside a leaf's sweep read with device-coherent loads instead, so the sweep
+// never waits on cache maintenance.
 
 // Waits until *f >= v. Returns false if this wait ran past the time limit (it
 // then stops every other wait of the solve) or another one already did.
@@ -1602,27 +1574,6 @@ Layout layout(int64_t m, int64_t n) {
     return L;
 }
 
-struct DeviceInfo {
-    int cus = 0;
-    int clock_khz = 0;  // wall clock of s_memrealtime
-};
-
-DeviceInfo device_info() {
-    static DeviceInfo cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    DeviceInfo& di = cache[dev];
-    if (di.cus == 0) {
-        int cus = 0, khz = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            cus = 256;
-        if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
-            khz = 100000;
-        di.clock_khz = khz;
-        di.cus = cus;
-    }
-    return di;
-}
 }  // namespace
 
 size_t solve_workspace_bytes(int64_t m, int64_t n) { return layout(m, n).total; }

@@ -210,9 +210,16 @@ def test_hessian_accum_nonfinite_inputs_stay_in_their_rows(bk, pieces):
 # ----------------------------------------------------------------------------
 # damped LDL
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("d", [1, 5, 64, 100, 257, 512, 1000])
-def test_ldl_matches_oracle(bk, d):
-    note("ldl d=%d" % d)
+LDL_PATHS = ["scheduled", "launch"]
+
+
+@pytest.mark.parametrize("path", LDL_PATHS)
+@pytest.mark.parametrize("d", [1, 5, 64, 100, 257, 512, 1000, 1500, 2100])
+def test_ldl_matches_oracle(bk, d, path, monkeypatch):
+    # orders up to 128 blocks take the scheduled (persistent) path by default; the
+    # launch chain is forced here for the same sizes
+    monkeypatch.setenv("BAKRON_LDL_PATH", path)
+    note("ldl d=%d %s" % (d, path))
     x = workloads.make_x(max(2 * d, 64), d, 7 + d, "gauss", min(2, d))
     H32 = oracle.hessian(x).astype(np.float32)
     ref_H = oracle.damp(H32.astype(np.float64), 0.01)
@@ -231,8 +238,10 @@ def test_ldl_matches_oracle(bk, d):
     assert np.linalg.norm(rec - ref_H) / np.linalg.norm(ref_H) < 1e-6
 
 
-def test_ldl_reports_first_bad_pivot(bk):
-    note("ldl not-SPD")
+@pytest.mark.parametrize("path", LDL_PATHS)
+def test_ldl_reports_first_bad_pivot(bk, path, monkeypatch):
+    monkeypatch.setenv("BAKRON_LDL_PATH", path)
+    note("ldl not-SPD %s" % path)
     x = workloads.make_x(256, 130, 3, "gauss", 2)
     H = oracle.hessian(x).astype(np.float32)
     H[77, 77] = -5.0
@@ -243,6 +252,44 @@ def test_ldl_reports_first_bad_pivot(bk):
         bk.ldl(torch.from_numpy(H).to(dev()), 0.01)
     assert ei.value.status == bk.BAKRON_E_NOT_SPD
     assert ei.value.bad_pivot == 120
+
+
+@pytest.mark.parametrize("d", [777, 2048, 3000])
+def test_ldl_scheduled_matches_launch_chain(bk, d, monkeypatch):
+    # the same blocked factorisation by the two schedules: they sum the updates of a
+    # tile in different groupings, so the fp64 factors differ by rounding only and
+    # the fp32 results by at most a few units in the last place
+    note("ldl scheduled vs launch d=%d" % d)
+    H = oracle.hessian(workloads.make_x(d + 64, d, 40 + d, "gauss", 2)).astype(np.float32)
+    g = torch.from_numpy(H).to(dev())
+    monkeypatch.setenv("BAKRON_LDL_PATH", "launch")
+    Hl, Dl = bk.ldl(g.clone(), 0.01)
+    monkeypatch.setenv("BAKRON_LDL_PATH", "scheduled")
+    Hs, Ds = bk.ldl(g.clone(), 0.01)
+    Hl, Hs = Hl.cpu().numpy().astype(np.float64), Hs.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(Hs - Hl) <= 4 * U32 * np.abs(Hl) + 1e-9 * np.abs(Hl).max())
+    assert np.all(np.abs(Ds.cpu().numpy() - Dl.cpu().numpy()) <= 4 * U32 * np.abs(Dl.cpu().numpy()))
+    # and again, bit for bit: the scheduled path applies each tile's updates in a fixed order
+    Hs2, Ds2 = bk.ldl(g.clone(), 0.01)
+    assert np.array_equal(Hs2.cpu().numpy().astype(np.float64), Hs) and torch.equal(Ds2, Ds)
+
+
+def test_ldl_expired_wait_is_reported(bk, monkeypatch):
+    # The scheduled LDL's workgroups wait on each other's tile counters, each wait
+    # bounded in time. A 1 us limit, set from the host, makes them expire: the call
+    # must stop (every kernel still ends) and report BAKRON_E_DEVICE with pivot -2;
+    # the next call runs normally.
+    note("ldl with a 1 us wait limit")
+    H = oracle.hessian(workloads.make_x(1200, 1000, 9, "gauss", 2)).astype(np.float32)
+    g = torch.from_numpy(H).to(dev())
+    monkeypatch.setenv("BAKRON_LDL_PATH", "scheduled")
+    monkeypatch.setenv("BAKRON_LDL_WAIT_LIMIT_US", "1")
+    with pytest.raises(bk.BakronError) as ei:
+        bk.ldl(g.clone(), 0.01)
+    assert ei.value.status == bk.BAKRON_E_DEVICE and ei.value.bad_pivot == -2
+    monkeypatch.delenv("BAKRON_LDL_WAIT_LIMIT_US")
+    Hf, Df = bk.ldl(g.clone(), 0.01)
+    assert torch.isfinite(Df).all() and bool((Df > 0).all())
 
 
 def test_ldl_pair_matches_single_calls(bk):
@@ -257,6 +304,49 @@ def test_ldl_pair_matches_single_calls(bk):
     sb, eb = bk.ldl(gb.clone(), 0.01)
     assert torch.equal(pa, sa) and torch.equal(da, ea)
     assert torch.equal(pb, sb) and torch.equal(db, eb)
+
+
+def test_ldl_pair_past_one_launch_matches_single_calls(bk, monkeypatch):
+    # an order above 8192 keeps both factorisations on the chain of launches, on two
+    # streams: each equals its single call on that path bit for bit
+    note("ldl pair d=8256 and d=300 (two streams, launch chain)")
+    g = torch.Generator().manual_seed(31)
+    X = torch.randn(8320, 8256, generator=g).to(dev())
+    HA = bk.hessian_accum(X)
+    HB = torch.from_numpy(oracle.hessian(workloads.make_x(700, 300, 21, "gauss", 2)).astype(np.float32)).to(dev())
+    (pa, da), (pb, db) = bk.ldl_pair(HA.clone(), HB.clone(), 0.01)
+    monkeypatch.setenv("BAKRON_LDL_PATH", "launch")
+    sa, ea = bk.ldl(HA.clone(), 0.01)
+    sb, eb = bk.ldl(HB.clone(), 0.01)
+    assert torch.equal(pa, sa) and torch.equal(da, ea)
+    assert torch.equal(pb, sb) and torch.equal(db, eb)
+
+
+@pytest.mark.parametrize("which", [0, 1])
+def test_ldl_pair_failure_leaves_the_other_intact(bk, which):
+    # one launch factors both matrices; a bad pivot in one stops only that one
+    note("ldl pair, one launch, matrix %d not SPD" % which)
+    good = oracle.hessian(workloads.make_x(900, 700, 5, "gauss", 2)).astype(np.float32)
+    bad = oracle.hessian(workloads.make_x(400, 330, 3, "gauss", 2)).astype(np.float32)
+    bad[200, 200] = -5.0
+    ref, _ = bk.ldl(torch.from_numpy(good).to(dev()), 0.01)
+    mats = [torch.from_numpy(good).to(dev()), torch.from_numpy(bad).to(dev())]
+    if which == 0:
+        mats.reverse()
+    Ds = [torch.empty(m.shape[0], device=dev()) for m in mats]
+    info = torch.full((2,), -1, dtype=torch.int64, device=dev())
+    ws = [torch.empty(bk.LIB.bakron_ldl_workspace_bytes(m.shape[0]), dtype=torch.uint8, device=dev())
+          for m in mats]
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = bk.LIB.bakron_ldl_pair_async(
+        P(mats[0]), mats[0].shape[0], mats[0].shape[0], P(Ds[0]), P(info), P(ws[0]), ws[0].numel(),
+        P(mats[1]), mats[1].shape[0], mats[1].shape[0], P(Ds[1]), ctypes.c_void_p(info.data_ptr() + 8),
+        P(ws[1]), ws[1].numel(), 0.01, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream),
+        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == bk.BAKRON_OK
+    got = info.cpu().tolist()
+    assert got[which] == 200 and got[1 - which] == -1
+    assert torch.equal(mats[1 - which], ref)
 
 
 @pytest.mark.parametrize("which", [0, 1])
