@@ -627,25 +627,44 @@ __device__ __forceinline__ bool sched_share(bool ok, int& s_ok) {
     return r;
 }
 
+// thread 0 looks, without waiting, whether *f >= v; the answer goes to the whole
+// workgroup, with the caches invalidated if so
+__device__ __forceinline__ bool sched_ready(const int* f, int v, int& s_ok) {
+    if (threadIdx.x == 0) {
+        const bool r = ld_flag(f) >= v;
+        if (r) acquire_agent();
+        s_ok = r;
+    }
+    __syncthreads();
+    const bool r = s_ok != 0;
+    __syncthreads();
+    return r;
+}
+
 // The chain: every diagonal block in turn, and the panel tile just below-left of it.
+// Tiles whose updates are already all in are loaded ahead: the panel tile's loads go
+// out with the diagonal block's stores, and the next diagonal tile's before the
+// panel product.
 __device__ __forceinline__ void sched_chain(const LdlWs& w, const SchedArgs& a, DiagSmem& s, int& s_ok) {
     const int64_t d = a.d;
     const int nb = a.nb;
     constexpr int kPer = 64 * 64 / kThreads;
+    bool have_diag = false;  // s.u already holds block b's diagonal tile
     for (int b = nb - 1; b >= 0; --b) {
         const int t = tid_opaque(), lane = t & 63, wv = t >> 6;
         const int64_t k0 = (int64_t)b * kTile;
         const int nr = (int)min<int64_t>(kTile, d - k0);
-        // (1) the diagonal block, once every update but block b + 1's is in
-        bool ok = true;
-        if (t == 0) ok = sched_wait(a, w, &w.cnt[b * nb + b], sched_expect(b, b, nb));
-        if (!sched_share(ok, s_ok)) return;
         // 32-bit offsets from per-block bases keep the addresses to one register each;
         // thread t holds column i = t % 64 of rows j = t / 64 + 4 r
         const int i = t & 63, j0 = t >> 6;
         const int di4 = 4 * (int)d;
         double* const Ab = w.A + k0 * d + k0;
-        {
+        double* const Pb = Ab - kTile;  // the panel tile (b, b - 1): rows k0.., columns k0 - 64..
+        // (1) the diagonal block, once every update but block b + 1's is in
+        if (!have_diag) {
+            bool ok = true;
+            if (t == 0) ok = sched_wait(a, w, &w.cnt[b * nb + b], sched_expect(b, b, nb));
+            if (!sched_share(ok, s_ok)) return;
             double v[kPer];
 #pragma unroll
             for (int r = 0; r < kPer; ++r) {
@@ -654,8 +673,8 @@ __device__ __forceinline__ void sched_chain(const LdlWs& w, const SchedArgs& a, 
             }
 #pragma unroll
             for (int r = 0; r < kPer; ++r) s.u[i][j0 + 4 * r] = v[r];
+            __syncthreads();
         }
-        __syncthreads();
         if (b + 1 < nb) {  // s.xs holds the panel tile (b + 1, b) from the step before
             diag_syrk(s, wv, lane);
             __syncthreads();
@@ -667,6 +686,12 @@ __device__ __forceinline__ void sched_chain(const LdlWs& w, const SchedArgs& a, 
                 st_flag(w.abort, 1);
             }
             return;
+        }
+        const bool pre = b > 0 && sched_ready(&w.cnt[b * nb + b - 1], sched_expect(b, b - 1, nb), s_ok);
+        double v[kPer];
+        if (pre) {
+#pragma unroll
+            for (int r = 0; r < kPer; ++r) v[r] = j0 + 4 * r < nr ? Pb[j0 * (int)d + i + r * di4] : 0.0;
         }
         // C22 into A (lower storage: A[k0 + j][k0 + i] = C[i][j]), X^T into the block's Wt slot
         double* const wb = w.Wt + (size_t)b * 4096;
@@ -684,20 +709,27 @@ __device__ __forceinline__ void sched_chain(const LdlWs& w, const SchedArgs& a, 
         if (b == 0) return;
 
         // (2) the panel tile (b, b - 1): P = X A(b, b - 1), into A and into s.xs
-        if (t == 0) ok = sched_wait(a, w, &w.cnt[b * nb + b - 1], sched_expect(b, b - 1, nb));
-        if (!sched_share(ok, s_ok)) return;
-        double* const Pb = Ab - kTile;  // rows k0.., columns k0 - 64..
-        {
-            double v[kPer];
+        if (!pre) {
+            bool ok = true;
+            if (t == 0) ok = sched_wait(a, w, &w.cnt[b * nb + b - 1], sched_expect(b, b - 1, nb));
+            if (!sched_share(ok, s_ok)) return;
+#pragma unroll
+            for (int r = 0; r < kPer; ++r) v[r] = j0 + 4 * r < nr ? Pb[j0 * (int)d + i + r * di4] : 0.0;
+        }
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) s.u[j0 + 4 * r][i] = v[r];
+        __syncthreads();
+        // the next diagonal tile (block b - 1, never the ragged last block)
+        have_diag = sched_ready(&w.cnt[(b - 1) * nb + b - 1], sched_expect(b - 1, b - 1, nb), s_ok);
+        double vn[kPer];
+        if (have_diag) {
+            const double* An = Ab - kTile * d - kTile;
 #pragma unroll
             for (int r = 0; r < kPer; ++r) {
-                const int q = j0 + 4 * r;
-                v[r] = q < nr ? Pb[j0 * (int)d + i + r * di4] : 0.0;
+                const int j = j0 + 4 * r;
+                vn[r] = i <= j ? An[j0 * (int)d + i + r * di4] : 0.0;
             }
-#pragma unroll
-            for (int r = 0; r < kPer; ++r) s.u[j0 + 4 * r][i] = v[r];
         }
-        __syncthreads();
         // 32x32 quadrant per wave; X is upper triangular, so k starts at the quadrant's first row
         const int qi = wv >> 1, qj = wv & 1;
         f64x4 acc[2][2];
@@ -728,6 +760,13 @@ __device__ __forceinline__ void sched_chain(const LdlWs& w, const SchedArgs& a, 
                     s.xs[pr][c] = acc[bi][bj][r];
                     if (pr < nr) st_coherent(&Pb[pr * (int)d + c], acc[bi][bj][r]);
                 }
+        if (have_diag) {
+#pragma unroll
+            for (int r = 0; r < kPer; ++r) {
+                const int j = j0 + 4 * r;
+                s.u[i][j] = i <= j ? vn[r] : (i == j ? 1.0 : 0.0);
+            }
+        }
         vm_wait_all();
         __syncthreads();
         if (t == 0) st_flag(&w.cnt[b * nb + b - 1], sched_expect(b, b - 1, nb) + 1);
