@@ -456,18 +456,31 @@ __device__ __forceinline__ void update_tile(int64_t d, int64_t r0, int64_t r_hi,
             }
 }
 
-// A[r][c] -= sum_{q < K} A[q0 + q][r] A[q0 + q][c] over rows [r_lo, r_hi),
-// columns [0, c_hi), lower triangle only (c <= r).
-template <int KT>
-__global__ __launch_bounds__(kThreads) void k_ldl_update(int64_t d, int64_t r_lo, int64_t r_hi,
-                                                         int64_t c_hi, int64_t q0, int64_t K,
-                                                         LdlWs w) {
+// The outer update A[r][c] -= sum_{q < K} A[q0 + q][r] A[q0 + q][c] over the lower
+// triangle of [0, n) x [0, n), in 64x64 tiles grouped in kOuterSq x kOuterSq squares.
+// Workgroups are dealt to the XCDs in turn (workgroup u to XCD u % 8), so square q
+// goes to the workgroups of one XCD (those with u % 8 == q % 8): the panel columns
+// that a square's tiles share are fetched into that XCD's L2 and reused there.
+constexpr int kOuterSq = 8;
+constexpr int kXcds = 8;
+
+__global__ __launch_bounds__(kThreads) void k_ldl_outer(int64_t d, int64_t n, int64_t q0, int64_t K,
+                                                        int nsq, LdlWs w) {
     if (*w.info >= 0) return;
-    const int64_t r0 = r_lo + (int64_t)blockIdx.y * kTile;
-    const int64_t c0 = (int64_t)blockIdx.x * kTile;
-    if (c0 > r0 + kTile - 1) return;  // tile entirely above the diagonal
-    __shared__ GemmSmemF64<KT> sm;
-    update_tile<KT>(d, r0, r_hi, c0, c_hi, q0, K, w, sm);
+    const int u = blockIdx.x;
+    const int q = (u / kXcds / (kOuterSq * kOuterSq)) * kXcds + u % kXcds;
+    if (q >= nsq) return;
+    const int loc = (u / kXcds) % (kOuterSq * kOuterSq);
+    // square q = (I, J), J <= I, in row order of the lower triangle of squares
+    int I = (int)((sqrt(8.0 * (double)q + 1.0) - 1.0) * 0.5);
+    while (I * (I + 1) / 2 > q) --I;
+    while ((I + 1) * (I + 2) / 2 <= q) ++I;
+    const int J = q - I * (I + 1) / 2;
+    const int64_t r0 = ((int64_t)I * kOuterSq + loc / kOuterSq) * kTile;
+    const int64_t c0 = ((int64_t)J * kOuterSq + loc % kOuterSq) * kTile;
+    if (r0 >= n || c0 > r0) return;  // past the edge, or above the diagonal
+    __shared__ GemmSmemF64<16> sm;
+    update_tile<16>(d, r0, n, c0, n, q0, K, w, sm);
 }
 
 // Workgroup 0 applies the update of the block just panelled (K rows at q0) to the
@@ -1048,8 +1061,10 @@ int enqueue_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, voi
             }
             if (s0 > 0) {
                 const int64_t tt = (s0 + kTile - 1) / kTile;
-                hipLaunchKernelGGL(k_ldl_update<16>, dim3((unsigned)tt, (unsigned)tt), dim3(kThreads), 0,
-                                   stream, d, (int64_t)0, s0, s0, s0, s1 - s0, w);
+                const int64_t ns = (tt + kOuterSq - 1) / kOuterSq, nsq = ns * (ns + 1) / 2;
+                const int64_t grid = kXcds * ((nsq + kXcds - 1) / kXcds) * kOuterSq * kOuterSq;
+                hipLaunchKernelGGL(k_ldl_outer, dim3((unsigned)grid), dim3(kThreads), 0, stream, d, s0, s0,
+                                   s1 - s0, (int)nsq, w);
             }
         }
     }
