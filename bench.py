@@ -41,10 +41,10 @@ CAL_BYTES = 256 << 20
 CAL_FETCH_KIB, CAL_WRITE_KIB = 131089.0, 262144.0
 COUNTERS = {
     # one solve at attn, 2-bit nearest: k_solve_run
-    ("solve", "attn", "4599874e6362bb1c"): {"fetch_kib": 2694361.8, "write_kib": 822609.8},
+    ("solve", "attn", "9319c76512b64a7b"): {"fetch_kib": 2689600.2, "write_kib": 822600.5},
     # one hessian_accum call at attn (mean of H_I and H_O): k_colmax + k_colexp + k_split2
     # + k_syrk2_full + k_syrk2_split + k_syrk_reduce
-    ("hessian", "attn", "03898ffe81ec0685"): {"fetch_kib": 2033627.8, "write_kib": 630312.5},
+    ("hessian", "attn", "23d9959685c68706"): {"fetch_kib": 2026068.1, "write_kib": 630213.6},
 }
 COUNTER_SOURCES = {
     "hessian": ("bk_accum.hip", "bk_common.hpp"),
