@@ -457,30 +457,128 @@ __device__ __forceinline__ void update_tile(int64_t d, int64_t r0, int64_t r_hi,
 }
 
 // The outer update A[r][c] -= sum_{q < K} A[q0 + q][r] A[q0 + q][c] over the lower
-// triangle of [0, n) x [0, n), in 64x64 tiles grouped in kOuterSq x kOuterSq squares.
+// triangle of [0, n) x [0, n), in 128 x 64 tiles of eight waves (4 x 2, each a 32 x 32
+// quadrant of 2 x 2 MFMA blocks), grouped in squares of 4 x 8 tiles (512 x 512).
 // Workgroups are dealt to the XCDs in turn (workgroup u to XCD u % 8), so square q
 // goes to the workgroups of one XCD (those with u % 8 == q % 8): the panel columns
 // that a square's tiles share are fetched into that XCD's L2 and reused there.
-constexpr int kOuterSq = 8;
+constexpr int kOutM = 128, kOutN = 64, kOutKT = 16, kOutThreads = 512;
+constexpr int kSqR = 4, kSqC = 8;  // tiles per square: rows, columns (512 x 512 elements)
 constexpr int kXcds = 8;
 
-__global__ __launch_bounds__(kThreads) void k_ldl_outer(int64_t d, int64_t n, int64_t q0, int64_t K,
-                                                        int nsq, LdlWs w) {
+struct OuterSmem {
+    double a[2][kOutKT][kOutM];
+    double b[2][kOutKT][kOutN];
+};
+
+// rows k0 .. k0 + kOutKT - 1 of a W-wide panel: thread t loads 16-byte pairs (rows
+// t / (W/2) + (512 / (W/2)) u, columns 2 (t % (W/2)), +1); zeros outside [0, K) x [0, R).
+// kFast: a full width and 16-byte aligned rows (rows past K clamped here, zeroed by the store).
+template <int W, bool kFast>
+__device__ __forceinline__ void outer_load(const double* __restrict__ A, int64_t lda, int R, int64_t K,
+                                           int64_t k0, f64x2 (&v)[kOutKT * W / 2 / kOutThreads], int t) {
+    constexpr int PR = W / 2, RPP = kOutThreads / PR;
+#pragma unroll
+    for (int u = 0; u < kOutKT * W / 2 / kOutThreads; ++u) {
+        const int64_t k = k0 + t / PR + RPP * u;
+        const int c2 = (t % PR) * 2;
+        if (kFast) {
+            v[u] = *reinterpret_cast<const f64x2*>(A + min(k, K - 1) * lda + c2);
+        } else {
+            const double* p = A + k * lda + c2;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) v[u][e] = (k < K && c2 + e < R) ? p[e] : 0.0;
+        }
+    }
+}
+template <int W>
+__device__ __forceinline__ void outer_store(double (&dst)[kOutKT][W], const f64x2 (&v)[kOutKT * W / 2 / kOutThreads],
+                                            int64_t K, int64_t k0, int t) {
+    constexpr int PR = W / 2, RPP = kOutThreads / PR;
+#pragma unroll
+    for (int u = 0; u < kOutKT * W / 2 / kOutThreads; ++u) {
+        const int r = t / PR + RPP * u;
+        *reinterpret_cast<f64x2*>(&dst[r][(t % PR) * 2]) = k0 + r < K ? v[u] : f64x2{0.0, 0.0};
+    }
+}
+
+template <bool kFast>
+__device__ __forceinline__ void outer_gemm(const double* __restrict__ A, int R, const double* __restrict__ B, int Cn,
+                                           int64_t lda, int64_t K, f64x4 (&acc)[2][2], OuterSmem& sm, int t) {
+    const int lane = t & 63, wv = t >> 6;
+    const int ra = (wv >> 1) * 32 + (lane & 15), rb = (wv & 1) * 32 + (lane & 15), kq = lane >> 4;
+    f64x2 va[kOutKT * kOutM / 2 / kOutThreads], vb[kOutKT * kOutN / 2 / kOutThreads];
+    outer_load<kOutM, kFast>(A, lda, R, K, 0, va, t);
+    outer_load<kOutN, kFast>(B, lda, Cn, K, 0, vb, t);
+    outer_store<kOutM>(sm.a[0], va, K, 0, t);
+    outer_store<kOutN>(sm.b[0], vb, K, 0, t);
+    __syncthreads();
+    const int64_t nk = (K + kOutKT - 1) / kOutKT;
+    for (int64_t it = 0; it < nk; ++it) {
+        const int cur = (int)(it & 1);
+        const bool more = it + 1 < nk;
+        if (more) {
+            outer_load<kOutM, kFast>(A, lda, R, K, (it + 1) * kOutKT, va, t);
+            outer_load<kOutN, kFast>(B, lda, Cn, K, (it + 1) * kOutKT, vb, t);
+        }
+#pragma unroll
+        for (int s = 0; s < kOutKT / 4; ++s) {
+            const int kr = 4 * s + kq;
+            const double fa0 = sm.a[cur][kr][ra], fa1 = sm.a[cur][kr][ra + 16];
+            const double fb0 = sm.b[cur][kr][rb], fb1 = sm.b[cur][kr][rb + 16];
+            acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa0, fb0, acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa0, fb1, acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa1, fb0, acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa1, fb1, acc[1][1], 0, 0, 0);
+        }
+        if (more) {
+            outer_store<kOutM>(sm.a[cur ^ 1], va, K, (it + 1) * kOutKT, t);
+            outer_store<kOutN>(sm.b[cur ^ 1], vb, K, (it + 1) * kOutKT, t);
+        }
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(kOutThreads) void k_ldl_outer(int64_t d, int64_t n, int64_t q0, int64_t K, int nsq,
+                                                           LdlWs w) {
     if (*w.info >= 0) return;
     const int u = blockIdx.x;
-    const int q = (u / kXcds / (kOuterSq * kOuterSq)) * kXcds + u % kXcds;
+    constexpr int kPerSq = kSqR * kSqC;
+    const int q = (u / kXcds / kPerSq) * kXcds + u % kXcds;
     if (q >= nsq) return;
-    const int loc = (u / kXcds) % (kOuterSq * kOuterSq);
+    const int loc = (u / kXcds) % kPerSq;
     // square q = (I, J), J <= I, in row order of the lower triangle of squares
     int I = (int)((sqrt(8.0 * (double)q + 1.0) - 1.0) * 0.5);
     while (I * (I + 1) / 2 > q) --I;
     while ((I + 1) * (I + 2) / 2 <= q) ++I;
     const int J = q - I * (I + 1) / 2;
-    const int64_t r0 = ((int64_t)I * kOuterSq + loc / kOuterSq) * kTile;
-    const int64_t c0 = ((int64_t)J * kOuterSq + loc % kOuterSq) * kTile;
-    if (r0 >= n || c0 > r0) return;  // past the edge, or above the diagonal
-    __shared__ GemmSmemF64<16> sm;
-    update_tile<16>(d, r0, n, c0, n, q0, K, w, sm);
+    const int64_t r0 = (int64_t)I * (kSqR * kOutM) + (loc / kSqC) * kOutM;
+    const int64_t c0 = (int64_t)J * (kSqC * kOutN) + (loc % kSqC) * kOutN;
+    if (r0 >= n || c0 >= n || c0 > r0 + kOutM - 1) return;  // past the edge, or above the diagonal
+    const int R = (int)min<int64_t>(kOutM, n - r0), Cn = (int)min<int64_t>(kOutN, n - c0);
+    __shared__ OuterSmem sm;
+    const int t = tid_opaque();
+    f64x4 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+    const double* P = w.A + q0 * d;
+    const bool fast = R == kOutM && Cn == kOutN && (d & 1) == 0 && (reinterpret_cast<uintptr_t>(w.A) & 15) == 0;
+    if (fast) outer_gemm<true>(P + r0, R, P + c0, Cn, d, K, acc, sm, t);
+    else outer_gemm<false>(P + r0, R, P + c0, Cn, d, K, acc, sm, t);
+    const int lane = t & 63, wv = t >> 6;
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int lr = (wv >> 1) * 32 + 16 * bi + (lane >> 4) + 4 * r;
+                const int lc = (wv & 1) * 32 + 16 * bj + (lane & 15);
+                const int64_t gi = r0 + lr, gj = c0 + lc;
+                if (lr < R && lc < Cn && gj <= gi) w.A[gi * d + gj] -= acc[bi][bj][r];
+            }
 }
 
 // Workgroup 0 applies the update of the block just panelled (K rows at q0) to the
@@ -1060,10 +1158,9 @@ int enqueue_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, voi
                 }
             }
             if (s0 > 0) {
-                const int64_t tt = (s0 + kTile - 1) / kTile;
-                const int64_t ns = (tt + kOuterSq - 1) / kOuterSq, nsq = ns * (ns + 1) / 2;
-                const int64_t grid = kXcds * ((nsq + kXcds - 1) / kXcds) * kOuterSq * kOuterSq;
-                hipLaunchKernelGGL(k_ldl_outer, dim3((unsigned)grid), dim3(kThreads), 0, stream, d, s0, s0,
+                const int64_t ns = (s0 + kSqR * kOutM - 1) / (kSqR * kOutM), nsq = ns * (ns + 1) / 2;
+                const int64_t grid = kXcds * ((nsq + kXcds - 1) / kXcds) * kSqR * kSqC;
+                hipLaunchKernelGGL(k_ldl_outer, dim3((unsigned)grid), dim3(kOutThreads), 0, stream, d, s0, s0,
                                    s1 - s0, (int)nsq, w);
             }
         }
