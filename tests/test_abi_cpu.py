@@ -90,6 +90,33 @@ def test_ldl_async_rejects_bad_arguments(lib):
     assert f(FAKE, 100, 100, 0.01, None, FAKE, FAKE, ws_need - 1, None) == 3
 
 
+def test_ldl_pair_async_rejects_bad_arguments(lib):
+    f = lib.bakron_ldl_pair_async
+    na, nb = lib.bakron_ldl_workspace_bytes(100), lib.bakron_ldl_workspace_bytes(60)
+    ok = (FAKE, 100, 100, None, FAKE, FAKE, na, FAKE, 60, 60, None, FAKE, FAKE, nb, 0.01, None, None)
+
+    def call(**kw):
+        a = list(ok)
+        names = ["HA", "dA", "ldha", "DA", "badA", "wsA", "wsA_bytes", "HB", "dB", "ldhb", "DB", "badB", "wsB",
+                 "wsB_bytes", "damp", "sa", "sb"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(badA=None) == 1          # status pointers are required
+    assert call(badB=None) == 1
+    assert call(HA=None) == 1
+    assert call(HB=None) == 1
+    assert call(dA=0) == 1
+    assert call(dB=-3) == 1
+    assert call(ldha=99) == 1            # ldh < d
+    assert call(ldhb=59) == 1
+    assert call(damp=-0.5) == 1
+    assert call(damp=float("inf")) == 1
+    assert call(wsA=None) == 3           # workspace missing or short
+    assert call(wsB_bytes=nb - 1) == 3
+
+
 def test_solve_rejects_bad_arguments(lib):
     import kronecker_hessian_rounding_amd._binding as b
     f = lib.bakron_solve
