@@ -16,6 +16,9 @@
 //           super-panel's rows                        (MFMA, lower part)
 //   outer : after each super-panel, A[0:s0, 0:s0] -= C_S C_S^T with
 //           K = the super-panel width                 (MFMA, lower part)
+// Orders up to 8192 take the same steps in one persistent launch (k_ldl_sched,
+// one factor or a layer's two), scheduled per 64x64 tile; larger orders run them
+// as a chain of launches, one per step.
 #include <algorithm>
 #include <climits>
 #include <cstdlib>
@@ -27,8 +30,8 @@
 namespace bk {
 
 constexpr int kSuper = 256;  // super-panel width (K of the big trailing updates)
-constexpr int kLdlKT = 32;   // k-slice depth of the fp64 panel / inner-update GEMMs (K = 64);
-                             // the wide outer updates use 16 (half the LDS, more workgroups per CU)
+constexpr int kLdlKT = 32;   // k-slice depth of the fp64 panel / inner-update GEMMs (K = 64) and
+                             // of the scheduled path's tile tasks; the wide outer updates use 16
 
 struct LdlWs {
     double* A;     // d x d working copy, lower triangle used, ld = d
