@@ -49,6 +49,7 @@ COUNTERS = {
 COUNTER_SOURCES = {
     "hessian": ("bk_accum.hip", "bk_common.hpp"),
     "solve": ("bk_solve.hip", "bk_common.hpp"),
+    "ldl": ("bk_ldl.hip", "bk_common.hpp"),
 }
 
 
@@ -381,6 +382,21 @@ def main():
     if tr is not None:
         roof_solve["base_case"]["counter_gbs"] = tr / solve_s / 1e9
 
+    # The LDL pair: d^3/3 fp64 flops per factor against the fp64 MFMA peak, and its
+    # chain of 64-wide diagonal blocks (the longer factor's) priced per block
+    ldl_s = ph["ldl"] * 1e-3
+    ldl_flops = (float(m) ** 3 + float(n) ** 3) / 3.0
+    nblk = (max(m, n) + 63) // 64
+    roof_ldl = {
+        "kernel": ("k_ldl_sched (both factors in one persistent launch)" if max(m, n) <= 8192 else
+                   "chains of launches (k_ldl_panel, k_ldl_diag_update, k_ldl_outer) on two streams"),
+        "bound": "mfma", "flops": ldl_flops, "achieved": ldl_flops / ldl_s / 1e12,
+        "peak": PEAK_FP64_MFMA_TFLOPS, "unit": "TFLOP/s",
+        "frac": ldl_flops / ldl_s / 1e12 / PEAK_FP64_MFMA_TFLOPS,
+        "traffic": traffic_bytes("ldl", args.workload),
+        "chain": {"blocks": nblk, "us_per_block": ldl_s * 1e6 / nblk},
+    }
+
     res = {
         "metric": "BaKron ms/layer + weights/s at 4096x4096 2-bit; % of MFMA / HBM roofline",
         "value": m * n / (ms_step * 1e-3),
@@ -411,6 +427,7 @@ def main():
         "ldl_fp64_tflops": (m ** 3 + n ** 3) / 3.0 / (ph["ldl"] * 1e-3) / 1e12,
         "roofline": roof,
         "roofline_solve": roof_solve,
+        "roofline_ldl": roof_ldl,
         "proxy_loss": loss,
         "clamped": clamped,
         "info": info,
