@@ -45,6 +45,8 @@ COUNTERS = {
     # one hessian_accum call at attn (mean of H_I and H_O): k_colmax + k_colexp + k_split2
     # + k_syrk2_full + k_syrk2_split + k_syrk_reduce
     ("hessian", "attn", "23d9959685c68706"): {"fetch_kib": 2026068.1, "write_kib": 630213.6},
+    # one LDL pair at attn (both 4096 factors in one launch): k_ldl_sched
+    ("ldl", "attn", "19780284fbb2bf03"): {"fetch_kib": 1873850.8, "write_kib": 757905.0},
 }
 COUNTER_SOURCES = {
     "hessian": ("bk_accum.hip", "bk_common.hpp"),
