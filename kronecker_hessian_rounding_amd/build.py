@@ -6,6 +6,11 @@ instructions take their accumulators in ordinary VGPRs (-amdgpu-mfma-vgpr-form):
 with accumulation registers the compiler copied every tile's accumulators
 between the two register files on each pass of the k-loop. The Hessian kernels
 measured a few per cent slower with the option, so it is set per file.
+
+The build fails if any kernel spills registers to scratch memory: several kernels
+count their own loads in flight with explicit s_waitcnt vmcnt(N) (the direct-to-LDS
+rings of the Hessian and the solve's far field), and spill loads and stores would
+enter that count and let a wait end before the data it waits for has landed.
 """
 from __future__ import annotations
 
@@ -30,14 +35,34 @@ CFLAGS = [
 FILE_FLAGS = {"bk_ldl.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
+def _scratch_users(remarks: str):
+    """(function, bytes per lane) for every function the resource remarks show with scratch."""
+    out, name = [], None
+    for ln in remarks.splitlines():
+        if "remark:" not in ln:
+            continue
+        if "Function Name:" in ln:
+            name = ln.split("Function Name:")[1].split("[")[0].strip()
+        elif "ScratchSize [bytes/lane]:" in ln and name:
+            n = int(ln.split("ScratchSize [bytes/lane]:")[1].split("[")[0].strip())
+            if n > 0:
+                out.append((name, n))
+    return out
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(src, []), "-Rpass-analysis=kernel-resource-usage", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s%s" % (src, r.stdout, r.stderr))
+    spills = _scratch_users(r.stderr)
+    if spills:
+        raise RuntimeError("%s: kernels spill to scratch memory (%s); the explicit vmcnt waits "
+                           "assume none" % (src, ", ".join("%s %d B/lane" % x for x in spills)))
     warn = [ln for ln in r.stderr.splitlines()
             if "warning" in ln and "packed-fp32-ops" not in ln]
     if verbose and warn:

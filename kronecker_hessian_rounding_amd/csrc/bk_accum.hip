@@ -211,6 +211,9 @@ __device__ __forceinline__ void syrk_tile_staged(const float* __restrict__ A, co
 // other vector loads, so with N = the loads issued after slice s, slice s is in LDS
 // once every wave has passed. No compiler fence is involved: the ring's later loads
 // stay in flight across the barrier.
+// N counts only the ring's own loads, so this holds only while the kernel keeps every
+// value in registers: a spill would add scratch loads and stores to the count (the
+// build rejects any kernel with scratch for that reason).
 template <int N>
 __device__ __forceinline__ void vm_wait_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");

@@ -396,6 +396,9 @@ __device__ __forceinline__ void chunk_range(int kblk, int nch, int c, int& b0, i
 // meet the other waves. Direct-to-LDS loads complete in issue order, so with N = the
 // loads issued after stage s, stage s is in LDS once every wave has passed; the later
 // loads stay in flight across the barrier.
+// N counts only the ring's own loads, so this holds only while the kernel keeps every
+// value in registers: a spill would add scratch loads and stores to the count (the
+// build rejects any kernel with scratch for that reason).
 template <int N>
 __device__ __forceinline__ void vm_wait_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
