@@ -250,6 +250,7 @@ def main():
                    "sketch_a": ("hess_sketch_a",)}[args.hessian]
     phases = hess_phases + (("rotate",) if args.rotate else ()) + ("ldl", "solve")
     ev = {k: [] for k in phases}
+    ldl_status = torch.empty(2, dtype=torch.int64, device=dev)
 
     def step(timed=False):
         marks = []
@@ -281,8 +282,10 @@ def main():
             bk.rotate_layer(W, HI, HO, seed + 1, seed + 2)
             mark()
         # the two factorisations are independent: one persistent launch serves both
-        # (orders up to 8192), else two chains of launches run side by side
-        bk.ldl_pair(HI, HO, 0.01, DI, DO)
+        # (orders up to 8192), else two chains of launches run side by side; their
+        # pivot statuses are checked once the steps have run, so the solve is queued
+        # right behind them
+        bk.ldl_pair(HI, HO, 0.01, DI, DO, status=ldl_status)
         mark()
         bk.solve(W, HO, HI, args.bits, args.rounding, seed, D_O=DO, D_I=DI, want_loss=True,
                  out=out)
@@ -292,12 +295,15 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.warmup:
+        bk.check_ldl_pair(ldl_status)
     all_marks = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
         all_marks.append(step(timed=True))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    bk.check_ldl_pair(ldl_status)  # every step factors the same matrices
     ms_step = (t1 - t0) * 1e3 / args.steps
     for marks in all_marks:
         for k, a, b in zip(phases, marks[:-1], marks[1:]):

@@ -312,15 +312,19 @@ def ldl(H: torch.Tensor, damp_rel: float = 0.01, D: Optional[torch.Tensor] = Non
 
 
 def ldl_pair(HA: torch.Tensor, HB: torch.Tensor, damp_rel: float = 0.01,
-             DA: Optional[torch.Tensor] = None, DB: Optional[torch.Tensor] = None):
+             DA: Optional[torch.Tensor] = None, DB: Optional[torch.Tensor] = None,
+             status: Optional[torch.Tensor] = None):
     """Two independent damped LDL factorisations at once (H_I and H_O of one layer).
 
     bakron_ldl_pair_async with the current stream and a second one that starts after
-    the current stream's earlier work; the current stream then waits for it. The
-    call waits for both to report their pivots. Returns ((HA, DA), (HB, DB)); raises
+    the current stream's earlier work; the current stream then waits for it. Without
+    `status` the call waits for both to report their pivots and raises
     BakronError(status=BAKRON_E_NOT_SPD) with .bad_pivot and .which (0 for HA, 1 for
     HB), or (status=BAKRON_E_DEVICE, .bad_pivot = -2) if a wait between workgroups
-    timed out.
+    timed out. With `status` (a device int64 tensor of 2 entries) nothing waits: the
+    two statuses land there in stream order, work queued after the call runs right
+    behind the factorisations, and check_ldl_pair(status) raises the same errors
+    later. Returns ((HA, DA), (HB, DB)).
     """
     mats = []
     for H, D, name in ((HA, DA, "HA"), (HB, DB, "HB")):
@@ -333,9 +337,15 @@ def ldl_pair(HA: torch.Tensor, HB: torch.Tensor, damp_rel: float = 0.01,
         _vec(D, "D" + name[1], d)
         mats.append((H, D, d, ldh))
     dev = HA.device
+    if status is not None:
+        if (status.device != dev or status.dtype != torch.int64 or status.numel() != 2
+                or not status.is_contiguous()):
+            raise ValueError("status must be a contiguous int64 tensor of 2 entries on %s" % dev)
+        info = status
+    else:
+        info = torch.empty((2,), dtype=torch.int64, device=dev)  # the library writes both
     cur = torch.cuda.current_stream(dev)
     aux = _aux_stream(dev)
-    info = torch.full((2,), -1, dtype=torch.int64, device=dev)
     ws = [_workspace(LIB.bakron_ldl_workspace_bytes(m[2]), dev, slot=k) for k, m in enumerate(mats)]
     start = torch.cuda.Event()
     start.record(cur)
@@ -345,20 +355,25 @@ def ldl_pair(HA: torch.Tensor, HB: torch.Tensor, damp_rel: float = 0.01,
                                    _ptr(ws[0]), ws[0].numel(), _ptr(HB_), dB, ldb, _ptr(DB_),
                                    ctypes.c_void_p(info.data_ptr() + 8), _ptr(ws[1]), ws[1].numel(),
                                    damp_rel, ctypes.c_void_p(cur.cuda_stream), ctypes.c_void_p(aux.cuda_stream))
-    status = [st, st]
     done = torch.cuda.Event()
     done.record(aux)
     cur.wait_event(done)
-    bad = info.cpu().tolist()  # waits for both factorisations
+    _check("bakron_ldl_pair_async", st)
+    if status is None:
+        check_ldl_pair(info)
+    return (mats[0][0], mats[0][1]), (mats[1][0], mats[1][1])
+
+
+def check_ldl_pair(status: torch.Tensor) -> None:
+    """Waits for the statuses that ldl_pair(..., status=status) left and raises as ldl_pair."""
+    bad = status.cpu().tolist()  # waits for both factorisations
     for k in range(2):
-        _check("bakron_ldl_async", status[k])
         if bad[k] >= 0 or bad[k] == -2:
             st = BAKRON_E_NOT_SPD if bad[k] >= 0 else BAKRON_E_DEVICE
-            err = BakronError("bakron_ldl_async", st, LIB.bakron_status_str(st).decode())
+            err = BakronError("bakron_ldl_pair_async", st, LIB.bakron_status_str(st).decode())
             err.bad_pivot = int(bad[k])
             err.which = k
             raise err
-    return (mats[0][0], mats[0][1]), (mats[1][0], mats[1][1])
 
 
 @dataclass
@@ -509,10 +524,14 @@ def quantize_layer(W: torch.Tensor, X: torch.Tensor, G: Optional[torch.Tensor], 
     if workspace is None:
         workspace = {}
     HI = hessian_accum(X, workspace.get("HI"))
+    status = None
     if G is not None:
         HO = hessian_accum(G, workspace.get("HO"))
-        # the two factorisations are independent: run them side by side
-        (HI, DI), (HO, DO) = ldl_pair(HI, HO, damp_rel, workspace.get("DI"), workspace.get("DO"))
+        # the two factorisations are independent: run them side by side; their
+        # statuses are read once the solve is queued behind them
+        status = torch.empty(2, dtype=torch.int64, device=W.device)
+        (HI, DI), (HO, DO) = ldl_pair(HI, HO, damp_rel, workspace.get("DI"), workspace.get("DO"),
+                                      status=status)
         LO = HO
     else:
         HI, DI = ldl(HI, damp_rel, workspace.get("DI"))
@@ -525,4 +544,8 @@ def quantize_layer(W: torch.Tensor, X: torch.Tensor, G: Optional[torch.Tensor], 
         DO.fill_(1.0 + damp_rel)
     res = solve(W, LO, HI, bits, rounding, seed, D_O=DO, D_I=DI, want_delta=want_delta,
                 want_loss=want_loss, out=workspace.get("out"))
+    if status is not None:
+        # the solve has no value-dependent control flow, so it ends normally on the
+        # factors of a failed factorisation; the failure is raised here
+        check_ldl_pair(status)
     return res, (LO, DO, HI, DI)

@@ -365,6 +365,40 @@ def test_ldl_pair_reports_which_failed(bk, which):
     assert ei.value.bad_pivot == 120
 
 
+@pytest.mark.parametrize("which", [None, 0, 1])
+def test_ldl_pair_deferred_status(bk, which):
+    # with a status tensor the call does not wait: work queued after it runs behind
+    # both factorisations, and check_ldl_pair raises what the waiting call raises
+    note("ldl pair, deferred status, not-SPD matrix %s" % which)
+    good = oracle.hessian(workloads.make_x(300, 90, 5, "gauss", 2)).astype(np.float32)
+    other = oracle.hessian(workloads.make_x(400, 130, 3, "gauss", 2)).astype(np.float32)
+    if which is not None:
+        other[120, 120] = -5.0
+    mats = [torch.from_numpy(good).to(dev()), torch.from_numpy(other).to(dev())]
+    if which == 0:
+        mats.reverse()
+    with pytest.raises(ValueError):
+        bk.ldl_pair(mats[0].clone(), mats[1].clone(), 0.01,
+                    status=torch.empty(2, dtype=torch.int32, device=dev()))
+    refs = [bk.ldl(m.clone(), 0.01) for m in mats] if which is None else None
+    status = torch.full((2,), 7, dtype=torch.int64, device=dev())
+    (pa, da), (pb, db) = bk.ldl_pair(mats[0], mats[1], 0.01, status=status)
+    after = (pa.sum(dim=0, dtype=torch.float64), pb.sum(dim=0, dtype=torch.float64))
+    if which is None:
+        bk.check_ldl_pair(status)
+        assert status.cpu().tolist() == [-1, -1]
+        assert torch.equal(pa, refs[0][0]) and torch.equal(da, refs[0][1])
+        assert torch.equal(pb, refs[1][0]) and torch.equal(db, refs[1][1])
+        assert torch.equal(after[0], refs[0][0].sum(dim=0, dtype=torch.float64))
+        assert torch.equal(after[1], refs[1][0].sum(dim=0, dtype=torch.float64))
+    else:
+        with pytest.raises(bk.BakronError) as ei:
+            bk.check_ldl_pair(status)
+        assert ei.value.status == bk.BAKRON_E_NOT_SPD
+        assert ei.value.which == which
+        assert ei.value.bad_pivot == 120
+
+
 # ----------------------------------------------------------------------------
 # the BaKron solve
 # ----------------------------------------------------------------------------
