@@ -1111,16 +1111,25 @@ static void enqueue_sched(int nf, const int64_t* d, const LdlWs* w, hipStream_t 
     const uint64_t spin = (uint64_t)di.clock_khz * limit_us / 1000ull;
     SchedLaunch L;
     L.nf = nf;
-    int64_t total = 0;
+    int64_t total = 0, nbmax = 0, cube = 0;
     for (int f = 0; f < 2; ++f) {
         const int g = f < nf ? f : 0;
         L.w[f] = w[g];
         L.a[f] = sched_args(d[g], spin);
-        if (f < nf) total += L.a[f].ntask + 1;
+        if (f < nf) {
+            total += L.a[f].ntask + 1;
+            nbmax = std::max<int64_t>(nbmax, L.a[f].nb);
+            cube += (int64_t)L.a[f].nb * L.a[f].nb * L.a[f].nb;
+        }
     }
-    // one workgroup per compute unit, for one factor or two: more workgroups take
-    // tickets further ahead of the chains and mostly wait (measured slower)
-    const int grid = (int)std::min<int64_t>(di.cus, total);
+    // One workgroup per compute unit while the chains set the pace: more take tickets
+    // further ahead of them and mostly wait. Two per compute unit (what the kernel's
+    // registers and LDS allow) once the tile updates per diagonal block, sum nb^3 / nb_max
+    // in tile products, reach 14000: measured faster from a pair of order 6144 (18432)
+    // and a single factor of 8192 (16384), slower for a single 7168 (12544), even for a
+    // pair of 5120 (12800).
+    const int per_cu = cube / std::max<int64_t>(nbmax, 1) >= 14000 ? 2 : 1;
+    const int grid = (int)std::min<int64_t>((int64_t)per_cu * di.cus, total);
     hipLaunchKernelGGL(k_ldl_sched, dim3((unsigned)grid), dim3(kThreads), 0, stream, L);
 }
 

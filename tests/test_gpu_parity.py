@@ -322,6 +322,26 @@ def test_ldl_pair_past_one_launch_matches_single_calls(bk, monkeypatch):
     assert torch.equal(pb, sb) and torch.equal(db, eb)
 
 
+def test_ldl_pair_two_workgroups_per_cu_matches_single_calls(bk, monkeypatch):
+    # a pair of order 6144 runs with two workgroups per compute unit, each single call
+    # with one: the scheduled path applies every tile's updates in a fixed order, so the
+    # results agree bit for bit, and with the launch chain to rounding
+    note("ldl pair d=6144 and d=6144 (scheduled, two workgroups per CU)")
+    g = torch.Generator().manual_seed(33)
+    HA = bk.hessian_accum(torch.randn(6208, 6144, generator=g).to(dev()))
+    HB = bk.hessian_accum((torch.randn(6400, 6144, generator=g) * torch.rand(6144, generator=g)).to(dev()))
+    (pa, da), (pb, db) = bk.ldl_pair(HA.clone(), HB.clone(), 0.01)
+    sa, ea = bk.ldl(HA.clone(), 0.01)
+    sb, eb = bk.ldl(HB.clone(), 0.01)
+    assert torch.equal(pa, sa) and torch.equal(da, ea)
+    assert torch.equal(pb, sb) and torch.equal(db, eb)
+    monkeypatch.setenv("BAKRON_LDL_PATH", "launch")
+    la, fa = bk.ldl(HA.clone(), 0.01)
+    la, pa = la.double(), pa.double()
+    assert bool((torch.abs(pa - la) <= 4 * U32 * torch.abs(la) + 1e-9 * torch.abs(la).max()).all())
+    assert bool((torch.abs(da - fa) <= 4 * U32 * torch.abs(fa)).all())
+
+
 @pytest.mark.parametrize("which", [0, 1])
 def test_ldl_pair_failure_leaves_the_other_intact(bk, which):
     # one launch factors both matrices; a bad pivot in one stops only that one
