@@ -12,7 +12,7 @@
 // contraction then has the "TN" form of bk_common.hpp (both operands K-major):
 //   diag  : C22 = reverse Cholesky of the 64x64 diagonal block, and C22^-1
 //   panel : C12^T = C22^-1 A[k0:k1, 0:k0]           (MFMA, in place)
-//   inner : A[s0:k0, 0:k0] -= C12 C12^T restricted to the current 256-wide
+//   inner : A[s0:k0, 0:k0] -= C12 C12^T restricted to the current 512-wide
 //           super-panel's rows                        (MFMA, lower part)
 //   outer : after each super-panel, A[0:s0, 0:s0] -= C_S C_S^T with
 //           K = the super-panel width                 (MFMA, lower part)
@@ -29,7 +29,7 @@
 
 namespace bk {
 
-constexpr int kSuper = 256;  // super-panel width (K of the big trailing updates)
+constexpr int kSuper = 512;  // super-panel width (K of the big trailing updates)
 constexpr int kLdlKT = 32;   // k-slice depth of the fp64 panel / inner-update GEMMs (K = 64) and
                              // of the scheduled path's tile tasks; the wide outer updates use 16
 
@@ -1144,7 +1144,7 @@ int enqueue_ldl(float* H, int64_t d, int64_t ldh, double damp_rel, float* D, voi
     if (allow_sched && use_sched(nbt)) {
         enqueue_sched(1, &d, &w, stream);
     } else {
-        // Per 64-wide block k0 (last to first) of each 256-wide super-panel [s0, s1):
+        // Per 64-wide block k0 (last to first) of each 512-wide super-panel [s0, s1):
         //   panel(k0)
         //   diag(k0 - 64) + inner(k0)      -- one launch: the next diagonal block takes this
         //                                     block's update and is factored beside the rest
