@@ -74,8 +74,21 @@ size_t ldl_workspace_bytes(int64_t d) {
 __global__ __launch_bounds__(kThreads) void k_ldl_init(const float* __restrict__ H, int64_t d,
                                                        int64_t ldh, double damp_rel, LdlWs w) {
     __shared__ double red[kThreads];
+    // thread t sums the diagonal entries t, t + 256, ... in that order, loading a batch
+    // of them at once (each lies on a line of its own)
+    constexpr int kIn = 16;
     double s = 0.0;
-    for (int64_t i = threadIdx.x; i < d; i += kThreads) s += (double)H[i * ldh + i];
+    for (int64_t i0 = threadIdx.x; i0 < d; i0 += (int64_t)kIn * kThreads) {
+        float v[kIn];
+#pragma unroll
+        for (int u = 0; u < kIn; ++u) {
+            const int64_t i = i0 + (int64_t)u * kThreads;
+            v[u] = i < d ? H[i * ldh + i] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kIn; ++u)
+            if (i0 + (int64_t)u * kThreads < d) s += (double)v[u];
+    }
     red[threadIdx.x] = s;
     __syncthreads();
     for (int o = kThreads / 2; o > 0; o >>= 1) {
@@ -92,28 +105,66 @@ __global__ __launch_bounds__(kThreads) void k_ldl_init(const float* __restrict__
 
 // A[r][c] = H[c][r] (upper triangle of H read, lower triangle of A written),
 // plus lambda on the diagonal; 64x64 tiles transposed through LDS. Each tile's
-// progress counter starts at 0.
+// progress counter starts at 0. Whole tiles of an H with 16-byte aligned rows (and
+// an even order, for A's rows) move in 16-byte pieces, every load in flight; the
+// strict upper part of a diagonal tile of A is then written as zeros (A's upper
+// triangle is never read). Other tiles go element by element.
 __global__ __launch_bounds__(kThreads) void k_ldl_load(const float* __restrict__ H, int64_t d,
                                                        int64_t ldh, LdlWs w) {
     const int64_t rt = blockIdx.y, ct = blockIdx.x;  // tile of A: rows rt, cols ct, rt >= ct
     if (ct > rt) return;
-    if (threadIdx.x == 0) w.cnt[rt * gridDim.x + ct] = 0;
+    const int t = threadIdx.x;
+    if (t == 0) w.cnt[rt * gridDim.x + ct] = 0;
     __shared__ float tile[kTile][kTile + 1];
     const int64_t r0 = rt * kTile, c0 = ct * kTile;
-    for (int e = threadIdx.x; e < kTile * kTile; e += kThreads) {
-        const int a = e / kTile, b = e % kTile;  // H row c0 + a, col r0 + b
-        const int64_t hr = c0 + a, hc = r0 + b;
-        tile[a][b] = (hr < d && hc < d && hr <= hc) ? H[hr * ldh + hc] : 0.0f;
+    const bool vec = r0 + kTile <= d && (ldh & 3) == 0 && (d & 1) == 0 &&
+                     (reinterpret_cast<uintptr_t>(H) & 15) == 0;
+    constexpr int kV4 = kTile * kTile / 4 / kThreads, kV2 = kTile * kTile / 2 / kThreads;
+    if (vec) {
+        // H rows c0 + a, columns r0 + b4 .. r0 + b4 + 3 (c0 <= r0: the columns exist too)
+        f32x4 v[kV4];
+#pragma unroll
+        for (int u = 0; u < kV4; ++u) {
+            const int q = t + u * kThreads;
+            v[u] = *reinterpret_cast<const f32x4*>(H + (c0 + (q >> 4)) * ldh + r0 + ((q & 15) << 2));
+        }
+#pragma unroll
+        for (int u = 0; u < kV4; ++u) {
+            const int q = t + u * kThreads;
+            const int a = q >> 4, b4 = (q & 15) << 2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tile[a][b4 + e] = (rt > ct || a <= b4 + e) ? v[u][e] : 0.0f;
+        }
+    } else {
+        for (int e = t; e < kTile * kTile; e += kThreads) {
+            const int a = e / kTile, b = e % kTile;  // H row c0 + a, col r0 + b
+            const int64_t hr = c0 + a, hc = r0 + b;
+            tile[a][b] = (hr < d && hc < d && hr <= hc) ? H[hr * ldh + hc] : 0.0f;
+        }
     }
     __syncthreads();
     const double lam = *w.lam;
-    for (int e = threadIdx.x; e < kTile * kTile; e += kThreads) {
-        const int a = e / kTile, b = e % kTile;  // A row r0 + a, col c0 + b
-        const int64_t r = r0 + a, c = c0 + b;
-        if (r >= d || c > r) continue;
-        double v = (double)tile[b][a];
-        if (r == c) v += lam;
-        w.A[r * d + c] = v;
+    if (vec) {
+#pragma unroll
+        for (int u = 0; u < kV2; ++u) {
+            const int q = t + u * kThreads;
+            const int a = q >> 5, b2 = (q & 31) << 1;  // A row r0 + a, cols c0 + b2, +1
+            f64x2 x = {(double)tile[b2][a], (double)tile[b2 + 1][a]};
+            if (rt == ct) {
+                if (a == b2) x[0] += lam;
+                if (a == b2 + 1) x[1] += lam;
+            }
+            *reinterpret_cast<f64x2*>(w.A + (r0 + a) * d + c0 + b2) = x;
+        }
+    } else {
+        for (int e = t; e < kTile * kTile; e += kThreads) {
+            const int a = e / kTile, b = e % kTile;  // A row r0 + a, col c0 + b
+            const int64_t r = r0 + a, c = c0 + b;
+            if (r >= d || c > r) continue;
+            double v = (double)tile[b][a];
+            if (r == c) v += lam;
+            w.A[r * d + c] = v;
+        }
     }
 }
 
@@ -1044,36 +1095,93 @@ __global__ __launch_bounds__(kThreads, 2) void k_ldl_sched(SchedLaunch L) {
 }
 
 // H[i][j] = C[i][j] / C[j][j] (i < j), C[j][j]^2 (i = j), 0 (i > j), with
-// C[i][j] = A[j][i]; D[j] = C[j][j]^2 if requested.
+// C[i][j] = A[j][i]; D[j] = C[j][j]^2 if requested. Tiles below the diagonal are
+// zeros and read nothing; whole tiles of an H with 16-byte aligned rows (and an
+// even order) move in 16-byte pieces, every load in flight; others go element by
+// element.
 __global__ __launch_bounds__(kThreads) void k_ldl_store(float* __restrict__ H, int64_t d,
                                                         int64_t ldh, float* __restrict__ D,
                                                         LdlWs w) {
     const int64_t rt = blockIdx.y, ct = blockIdx.x;  // tile of H: rows rt, cols ct
+    const int t = threadIdx.x;
     __shared__ float tile[kTile][kTile + 1];
     __shared__ double dj[kTile];
     const int64_t i0 = rt * kTile, j0 = ct * kTile;
-    if (threadIdx.x < kTile) {
-        const int64_t j = j0 + threadIdx.x;
-        dj[threadIdx.x] = (j < d) ? w.A[j * d + j] : 1.0;
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < kTile * kTile; e += kThreads) {
-        const int b = e / kTile, a = e % kTile;  // A row j0 + b, col i0 + a
-        const int64_t j = j0 + b, i = i0 + a;
-        float v = 0.0f;
-        if (i < d && j < d) {
-            if (i < j) v = (float)(w.A[j * d + i] / dj[b]);
-            else if (i == j) v = (float)(dj[b] * dj[b]);
+    const bool vec = i0 + kTile <= d && j0 + kTile <= d && (ldh & 3) == 0 && (d & 1) == 0 &&
+                     (reinterpret_cast<uintptr_t>(H) & 15) == 0;
+    constexpr int kV4 = kTile * kTile / 4 / kThreads, kV2 = kTile * kTile / 2 / kThreads;
+    if (rt > ct) {
+        if (vec) {
+#pragma unroll
+            for (int u = 0; u < kV4; ++u) {
+                const int q = t + u * kThreads;
+                *reinterpret_cast<f32x4*>(H + (i0 + (q >> 4)) * ldh + j0 + ((q & 15) << 2)) =
+                    f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        } else {
+            for (int e = t; e < kTile * kTile; e += kThreads) {
+                const int64_t i = i0 + e / kTile, j = j0 + e % kTile;
+                if (i < d && j < d) H[i * ldh + j] = 0.0f;
+            }
         }
-        tile[a][b] = v;
+        return;
+    }
+    if (t < kTile) {
+        const int64_t j = j0 + t;
+        dj[t] = (j < d) ? w.A[j * d + j] : 1.0;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < kTile * kTile; e += kThreads) {
-        const int a = e / kTile, b = e % kTile;  // H row i0 + a, col j0 + b
-        const int64_t i = i0 + a, j = j0 + b;
-        if (i >= d || j >= d) continue;
-        H[i * ldh + j] = tile[a][b];
-        if (D && i == j) D[j] = tile[a][b];
+    if (vec) {
+        // A rows j0 + b, columns i0 + a2, +1
+        f64x2 x[kV2];
+#pragma unroll
+        for (int u = 0; u < kV2; ++u) {
+            const int q = t + u * kThreads;
+            x[u] = *reinterpret_cast<const f64x2*>(w.A + (j0 + (q >> 5)) * d + i0 + ((q & 31) << 1));
+        }
+#pragma unroll
+        for (int u = 0; u < kV2; ++u) {
+            const int q = t + u * kThreads;
+            const int b = q >> 5, a2 = (q & 31) << 1;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int64_t i = i0 + a2 + e, j = j0 + b;
+                float v = 0.0f;
+                if (i < j) v = (float)(x[u][e] / dj[b]);
+                else if (i == j) v = (float)(dj[b] * dj[b]);
+                tile[a2 + e][b] = v;
+            }
+        }
+    } else {
+        for (int e = t; e < kTile * kTile; e += kThreads) {
+            const int b = e / kTile, a = e % kTile;  // A row j0 + b, col i0 + a
+            const int64_t j = j0 + b, i = i0 + a;
+            float v = 0.0f;
+            if (i < d && j < d) {
+                if (i < j) v = (float)(w.A[j * d + i] / dj[b]);
+                else if (i == j) v = (float)(dj[b] * dj[b]);
+            }
+            tile[a][b] = v;
+        }
+    }
+    __syncthreads();
+    if (vec) {
+#pragma unroll
+        for (int u = 0; u < kV4; ++u) {
+            const int q = t + u * kThreads;
+            const int a = q >> 4, b4 = (q & 15) << 2;
+            const f32x4 v = {tile[a][b4], tile[a][b4 + 1], tile[a][b4 + 2], tile[a][b4 + 3]};
+            *reinterpret_cast<f32x4*>(H + (i0 + a) * ldh + j0 + b4) = v;
+        }
+        if (D && rt == ct && t < kTile) D[j0 + t] = tile[t][t];
+    } else {
+        for (int e = t; e < kTile * kTile; e += kThreads) {
+            const int a = e / kTile, b = e % kTile;  // H row i0 + a, col j0 + b
+            const int64_t i = i0 + a, j = j0 + b;
+            if (i >= d || j >= d) continue;
+            H[i * ldh + j] = tile[a][b];
+            if (D && i == j) D[j] = tile[a][b];
+        }
     }
 }
 

@@ -239,6 +239,24 @@ def test_ldl_matches_oracle(bk, d, path, monkeypatch):
 
 
 @pytest.mark.parametrize("path", LDL_PATHS)
+@pytest.mark.parametrize("d,extra", [(256, 4), (1024, 3), (777, 4), (1100, 12)])
+def test_ldl_strided_view(bk, d, extra, path, monkeypatch):
+    # H as a view of a wider buffer (leading dimension d + extra): 16-byte aligned rows
+    # with whole tiles take the wide loads and stores, others the element-wise ones;
+    # the result equals the contiguous call bit for bit and the rest of the buffer
+    # is untouched
+    monkeypatch.setenv("BAKRON_LDL_PATH", path)
+    note("ldl strided view d=%d ld=%d %s" % (d, d + extra, path))
+    H = oracle.hessian(workloads.make_x(d + 64, d, 60 + d, "gauss", 2)).astype(np.float32)
+    ref, refD = bk.ldl(torch.from_numpy(H).to(dev()), 0.01)
+    big = torch.full((d, d + extra), 7.0, device=dev())
+    big[:, :d] = torch.from_numpy(H).to(dev())
+    got, gotD = bk.ldl(big[:, :d], 0.01)
+    assert torch.equal(got, ref) and torch.equal(gotD, refD)
+    assert bool((big[:, d:] == 7.0).all())
+
+
+@pytest.mark.parametrize("path", LDL_PATHS)
 def test_ldl_reports_first_bad_pivot(bk, path, monkeypatch):
     monkeypatch.setenv("BAKRON_LDL_PATH", path)
     note("ldl not-SPD %s" % path)
