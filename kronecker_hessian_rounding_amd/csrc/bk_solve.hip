@@ -218,7 +218,18 @@ __global__ __launch_bounds__(kThreads) void k_scales(const float* __restrict__ W
     __shared__ float red[kThreads];
     float a = 0.0f;
     const float* w = W + i * ldw;
-    for (int64_t j = threadIdx.x; j < n; j += kThreads) a = nan_max(a, fabsf(w[j]));
+    // a batch of the row's entries in flight at once
+    constexpr int kIn = 16;
+    for (int64_t j0 = threadIdx.x; j0 < n; j0 += (int64_t)kIn * kThreads) {
+        float v[kIn];
+#pragma unroll
+        for (int u = 0; u < kIn; ++u) {
+            const int64_t j = j0 + (int64_t)u * kThreads;
+            v[u] = j < n ? fabsf(w[j]) : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kIn; ++u) a = nan_max(a, v[u]);
+    }
     red[threadIdx.x] = a;
     __syncthreads();
     for (int o = kThreads / 2; o > 0; o >>= 1) {
@@ -256,10 +267,28 @@ __global__ __launch_bounds__(kThreads) void k_lstats(const float* __restrict__ L
     const int64_t k1 = min<int64_t>(k0 + kPrepRows, min<int64_t>(d, col));
     float m = 0.0f, sum = 0.0f;
     if (col < d) {
-        for (int64_t k = k0 + rq; k < k1; k += 4) {
-            const float v = fabsf(L[k * ld + col]);
-            if (k < kf) m = nan_max(m, re ? ldexpf(v, -re[k]) : v);
-            if (rb) sum += v * rb[k];
+        // rows k0 + rq, + 4, ... in that order, a batch of them (and of their
+        // exponents and bounds) loaded at once
+        constexpr int kIn = 16;
+        for (int64_t kb = k0 + rq; kb < k1; kb += 4 * kIn) {
+            float v[kIn], f[kIn];
+            int e[kIn];
+#pragma unroll
+            for (int u = 0; u < kIn; ++u) {
+                const int64_t k = kb + 4 * u;
+                const bool in = k < k1;
+                v[u] = in ? fabsf(L[k * ld + col]) : 0.0f;
+                e[u] = (in && re && k < kf) ? re[k] : 0;
+                f[u] = (in && rb) ? rb[k] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < kIn; ++u) {
+                const int64_t k = kb + 4 * u;
+                if (k < k1) {
+                    if (k < kf) m = nan_max(m, re ? ldexpf(v[u], -e[u]) : v[u]);
+                    if (rb) sum += v[u] * f[u];
+                }
+            }
         }
     }
     rm[rq][c] = m;
