@@ -41,12 +41,12 @@ CAL_BYTES = 256 << 20
 CAL_FETCH_KIB, CAL_WRITE_KIB = 131089.0, 262144.0
 COUNTERS = {
     # one solve at attn, 2-bit nearest: k_solve_run
-    ("solve", "attn", "9319c76512b64a7b"): {"fetch_kib": 2689600.2, "write_kib": 822600.5},
+    ("solve", "attn", "53ecec16397797e6"): {"fetch_kib": 2693204.3, "write_kib": 822614.8},
     # one hessian_accum call at attn (mean of H_I and H_O): k_colmax + k_colexp + k_split2
     # + k_syrk2_full + k_syrk2_split + k_syrk_reduce
-    ("hessian", "attn", "23d9959685c68706"): {"fetch_kib": 2026068.1, "write_kib": 630213.6},
+    ("hessian", "attn", "23d9959685c68706"): {"fetch_kib": 2026493.2, "write_kib": 630644.3},
     # one LDL pair at attn (both 4096 factors in one launch): k_ldl_sched
-    ("ldl", "attn", "19780284fbb2bf03"): {"fetch_kib": 1873850.8, "write_kib": 757905.0},
+    ("ldl", "attn", "d61a493cfa1a054e"): {"fetch_kib": 1864342.7, "write_kib": 757905.0},
 }
 COUNTER_SOURCES = {
     "hessian": ("bk_accum.hip", "bk_common.hpp"),
