@@ -733,6 +733,7 @@ struct LeafSmem {
     float pnb[4][kB][4];   // bulk partials by diagonal modulo 4, entry and quarter
     float rnb[4][kB][4];
     float li[kNew][kB];    // li[e][j] = L_I[j-1-e][j]: the finaliser's terms
+    float un[4][kB];       // stochastic rounding: the draws by diagonal modulo 4, one per row
     uint8_t code[kB][kB + 4];
     float DI[kB];
     int exr[kB];  // eD of the leaf's rows
@@ -1226,14 +1227,13 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
 #pragma unroll
             for (int e = 0; e < kNew; ++e) v.l[e] = sm.li[e][jc];
         };
-        auto entry = [&](int st, const In& v, const f32x4& pq, const f32x4& rq) {
+        auto entry = [&](int st, const In& v, const f32x4& pq, const f32x4& rq, float ud) {
             const int j = st - i;
             const bool live = row && j >= 0 && j < Cc;
             float dn[kNew];  // D[i-1-e][j], from the lane above's carried values
 #pragma unroll
             for (int e = 0; e < kNew; ++e) dn[e] = lane_above0(dcar[e]);
-            float u = 0.5f;
-            if (p.stochastic) u = uniform24(p.seed, (uint64_t)(i0 + i) * (uint64_t)p.n + (uint64_t)(j0 + j));
+            const float u = p.stochastic ? ud : 0.5f;
             float pb = (pq[0] + pq[1]) + (pq[2] + pq[3]);
             float rb = (rq[0] + rq[1]) + (rq[2] + rq[3]);
 #pragma unroll
@@ -1270,12 +1270,16 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
             const f32x4 rq0 = lds4(&sm.rnb[(2 * S) & 3][i][0]);
             const f32x4 pq1 = lds4(&sm.pnb[(2 * S + 1) & 3][i][0]);
             const f32x4 rq1 = lds4(&sm.rnb[(2 * S + 1) & 3][i][0]);
+            // the draws of diagonals 2S and 2S + 1 (written by the hand-over waves in
+            // super-step S - 1)
+            const float ud0 = p.stochastic ? sm.un[(2 * S) & 3][i] : 0.5f;
+            const float ud1 = p.stochastic ? sm.un[(2 * S + 1) & 3][i] : 0.5f;
             // the inputs of the next super-step: the strip hand-overs that feed them
             // were added by super-step S - 1, and nothing writes them in this one
             load_in(2 * S + 2, n0);
             load_in(2 * S + 3, n1);
-            entry(2 * S, c0, pq0, rq0);
-            entry(2 * S + 1, c1, pq1, rq1);
+            entry(2 * S, c0, pq0, rq0, ud0);
+            entry(2 * S + 1, c1, pq1, rq1, ud1);
             lds_wait_all();
             barrier_no_wait();
         };
@@ -1297,10 +1301,25 @@ __device__ __forceinline__ void leaf_task(const SolveParams& p, int d, int slot,
         // 8c - 7 only at the first multiply, two super-steps later. The product is
         // added at 8c - 2, before the finaliser reads the inputs of step 16c (at the
         // start of super-step 8c - 1). Super-steps 24-63 publish this leaf's strips 0-2.
+        // With stochastic rounding they also draw the finaliser's uniforms off its
+        // dependent chain: in super-step S, those of super-step S + 1, the column wave
+        // for diagonal 2S + 2 and the row wave for 2S + 3 (row = lane), into the ring
+        // slot that the finaliser read two super-steps before.
+        auto put_draws = [&](int S) {
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const int dg = 2 * S + (hcol ? 0 : 1);
+            sm.un[dg & 3][ln] =
+                uniform24(p.seed, (uint64_t)(i0 + ln) * (uint64_t)p.n + (uint64_t)(j0 + (dg - ln)));
+        };
+        int sst = 0;  // the super-step that the next sync_step ends
         auto sync_step = [&]() {
+            if (p.stochastic) put_draws(sst + 1);
             lds_wait_all();
             barrier_no_wait();
+            ++sst;
         };
+        if (p.stochastic) put_draws(0);
         __syncthreads();
 #pragma nounroll
         for (int cw = 1; cw < kStrips; ++cw) {
