@@ -41,7 +41,7 @@ CAL_BYTES = 256 << 20
 CAL_FETCH_KIB, CAL_WRITE_KIB = 131089.0, 262144.0
 COUNTERS = {
     # one solve at attn, 2-bit nearest: k_solve_run
-    ("solve", "attn", "53ecec16397797e6"): {"fetch_kib": 2693204.3, "write_kib": 822614.8},
+    ("solve", "attn", "dbf2c268b3a81d14"): {"fetch_kib": 2688065.3, "write_kib": 822587.6},
     # one hessian_accum call at attn (mean of H_I and H_O): k_colmax + k_colexp + k_split2
     # + k_syrk2_full + k_syrk2_split + k_syrk_reduce
     ("hessian", "attn", "23d9959685c68706"): {"fetch_kib": 2026493.2, "write_kib": 630644.3},
