@@ -360,6 +360,23 @@ def test_ldl_pair_two_workgroups_per_cu_matches_single_calls(bk, monkeypatch):
     assert bool((torch.abs(da - fa) <= 4 * U32 * torch.abs(fa)).all())
 
 
+def test_ldl_single_8192_two_workgroups_per_cu(bk, monkeypatch):
+    # a single factor of order 8192 (the largest the persistent launch takes) runs with
+    # two workgroups per compute unit: it agrees with the launch chain to rounding and
+    # repeats bit for bit
+    note("ldl d=8192 scheduled (two workgroups per CU) vs launch chain")
+    g = torch.Generator().manual_seed(35)
+    H = bk.hessian_accum((torch.randn(8256, 8192, generator=g) * torch.rand(8192, generator=g)).to(dev()))
+    s1, e1 = bk.ldl(H.clone(), 0.01)
+    s2, e2 = bk.ldl(H.clone(), 0.01)
+    assert torch.equal(s1, s2) and torch.equal(e1, e2)
+    monkeypatch.setenv("BAKRON_LDL_PATH", "launch")
+    la, fa = bk.ldl(H.clone(), 0.01)
+    la, s1 = la.double(), s1.double()
+    assert bool((torch.abs(s1 - la) <= 4 * U32 * torch.abs(la) + 1e-9 * torch.abs(la).max()).all())
+    assert bool((torch.abs(e1 - fa) <= 4 * U32 * torch.abs(fa)).all())
+
+
 @pytest.mark.parametrize("which", [0, 1])
 def test_ldl_pair_failure_leaves_the_other_intact(bk, which):
     # one launch factors both matrices; a bad pivot in one stops only that one
