@@ -119,7 +119,34 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(w, LO, LI, x, bits, rounding, seed, rows, g=None, full=False):
+def _replay(dev, LO, LI, bits, rounding, seed, rows):
+    """The oracle's replay of the device's codes (all rows, or the first `rows`)."""
+    if dev is None:
+        return None
+    import numpy as np
+
+    import oracle
+
+    t0 = time.perf_counter()
+    w = dev["W"]
+    m, n = w.shape
+    if rows is None:
+        rp = oracle.replay(w, LO, LI, dev["scales"], bits, dev["codes"], rounding, seed,
+                           DO=dev["DO"], DI=dev["DI"])
+        loss_rel = abs(dev["loss"] - rp["loss"]) / abs(rp["loss"]) if rp["loss"] else None
+        what = "every entry"
+    else:
+        rp = oracle.replay_rows(w, LO, LI, dev["scales"], bits, dev["codes"], np.arange(rows),
+                                rounding, seed)
+        loss_rel = None
+        what = "rows 0..%d" % (rows - 1)
+    return {"entries": int(rp["y"].size), "rows": what, "mismatches": rp["mismatches"],
+            "flips": rp["flips"], "max_flip_margin": rp["max_flip_margin"], "bad": rp["bad"],
+            "band": 1e-4, "loss_rel": loss_rel, "seconds": time.perf_counter() - t0,
+            "factors": "the device's L_O, L_I, D_O, D_I and scales"}
+
+
+def cpu_baseline(w, LO, LI, x, bits, rounding, seed, rows, g=None, full=False, dev=None):
     """The oracle as it stands, timed on the host cores.
 
     Default: a bounded sample of the same layer, extrapolated. Phases: fp64 X^T X
@@ -131,6 +158,13 @@ def cpu_baseline(w, LO, LI, x, bits, rounding, seed, rows, g=None, full=False):
     full=True: the whole oracle chain on the whole layer, every phase measured
     (fp64 X^T X / T and G^T G / T, damping, the LDL of both factors as the oracle's
     pipeline takes it, the fp32 scales and the whole accumulator sweep).
+
+    dev (untimed): the device's last step (W as solved, its codes, scales, D_O, D_I
+    and proxy loss; LO / LI are its factors). The oracle replays the device's codes
+    on the device's own factors -- every entry with full=True, the sampled rows
+    otherwise -- and the counts land in the result's "replay" entry: mismatches,
+    boundary flips (within 1e-4 of a grid step of the boundary between adjacent
+    codes), their largest margin, bad entries, and the proxy loss agreement.
     """
     import numpy as np
 
@@ -156,6 +190,7 @@ def cpu_baseline(w, LO, LI, x, bits, rounding, seed, rows, g=None, full=False):
         t["sweep"] = time.perf_counter() - t0
         total = sum(t.values())
         return {
+            "replay": _replay(dev, LO, LI, bits, rounding, seed, None),
             "value": m * n / total,
             "unit": "weights/s",
             "cores": cores,
@@ -185,6 +220,7 @@ def cpu_baseline(w, LO, LI, x, bits, rounding, seed, rows, g=None, full=False):
     t_sweep = t_s * (m * m * n + m * n * n) / (r * r * n + r * n * n)
     t_layer = t_h * (1.0 + (m / n) ** 2) + t_ldl + t_sweep  # H_I (T n^2) and H_O (T m^2)
     return {
+        "replay": _replay(dev, LO, LI, bits, rounding, seed, r),
         "value": m * n / t_layer,
         "unit": "weights/s",
         "cores": cores,
@@ -459,8 +495,12 @@ def main():
     if not args.no_cpu_baseline:
         LI = np.triu(HI.cpu().numpy(), 1).astype(np.float64)
         LO = HO.cpu().numpy()
+        dev_out = {"W": W.cpu().numpy(), "codes": out.codes.cpu().numpy(),
+                   "scales": out.scales.cpu().numpy(), "DO": DO.cpu().numpy().astype(np.float64),
+                   "DI": DI.cpu().numpy().astype(np.float64), "loss": loss}
         res["cpu_baseline"] = cpu_baseline(w, LO, LI, x, args.bits, args.rounding, seed,
-                                           args.cpu_rows, g if args.cpu_full else None, args.cpu_full)
+                                           args.cpu_rows, g if args.cpu_full else None, args.cpu_full,
+                                           dev_out)
     print(json.dumps(res), flush=True)
 
 
