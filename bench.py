@@ -41,13 +41,21 @@ CAL_BYTES = 256 << 20
 CAL_FETCH_KIB, CAL_WRITE_KIB = 131089.0, 262144.0
 COUNTERS = {
     # one solve at attn, 2-bit nearest: k_solve_run
-    ("solve", "attn", "dbf2c268b3a81d14"): {"fetch_kib": 2688065.3, "write_kib": 822587.6},
+    ("solve", "attn", "dbf2c268b3a81d14"): {"fetch_kib": 2688065.3, "write_kib": 822587.6,
+                                            "mfma_busy": 0.066, "clock_ghz": 2.35},
     # one hessian_accum call at attn (mean of H_I and H_O): k_colmax + k_colexp + k_split2
     # + k_syrk2_full + k_syrk2_split + k_syrk_reduce
-    ("hessian", "attn", "23d9959685c68706"): {"fetch_kib": 2026493.2, "write_kib": 630644.3},
+    ("hessian", "attn", "23d9959685c68706"): {"fetch_kib": 2026493.2, "write_kib": 630644.3,
+                                              "mfma_busy": 0.565, "clock_ghz": 1.87},
     # one LDL pair at attn (both 4096 factors in one launch): k_ldl_sched
-    ("ldl", "attn", "d61a493cfa1a054e"): {"fetch_kib": 1864342.7, "write_kib": 757905.0},
+    ("ldl", "attn", "d61a493cfa1a054e"): {"fetch_kib": 1864342.7, "write_kib": 757905.0,
+                                          "mfma_busy": 0.304, "clock_ghz": 2.20},
 }
+# "mfma_busy" and "clock_ghz" come from a third rocprofv3 --pmc run of this script
+# (GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES and the SQ_INSTS_VALU_MFMA_MOPS_* counters):
+# the share of SIMD cycles in which a matrix instruction issued, and the clock the
+# kernel ran at (GRBM_GUI_ACTIVE per XCD over its duration), for the main kernel of
+# each kind (k_syrk2_full, the mean of the two calls; k_ldl_sched; k_solve_run).
 COUNTER_SOURCES = {
     "hessian": ("bk_accum.hip", "bk_common.hpp"),
     "solve": ("bk_solve.hip", "bk_common.hpp"),
@@ -72,6 +80,14 @@ def source_key(kind):
         h.update(" ".join(text.split()).encode())
         h.update(" ".join(hip_build.CFLAGS[:-2] + hip_build.FILE_FLAGS.get(f, [])).encode())
     return h.hexdigest()[:16]
+
+
+def mfma_counters(kind, workload):
+    """MFMA-busy share and clock of the kind's main kernel from the counters, or None."""
+    c = COUNTERS.get((kind, workload, source_key(kind)))
+    if c is None or "mfma_busy" not in c:
+        return None
+    return {"mfma_busy": c["mfma_busy"], "clock_ghz": c["clock_ghz"]}
 
 
 def traffic_bytes(kind, workload):
@@ -388,6 +404,7 @@ def main():
         "flops_per_call": PIECE_PRODUCTS * syrk_flops,
         "fp32_equiv_tflops": fp32_equiv,
         "fp32_equiv_frac_of_fp32_peak": fp32_equiv / PEAK_FP32_MFMA_TFLOPS,
+        "counters": None if args.hessian != "tokens" else mfma_counters("hessian", args.workload),
     }
     if args.hessian == "sketch_a":
         roof.update(kernel="sketch_a phase: token-weight tile GEMMs (fp32 MFMA) and weighted SYRKs "
@@ -421,6 +438,7 @@ def main():
                       "traffic": traffic_bytes("solve", args.workload)},
         "chain": {"steps": chain, "ns_per_step": solve_s * 1e9 / chain, "rule_steps": m + n - 1,
                   "ns_per_rule_step": solve_s * 1e9 / (m + n - 1)},
+        "counters": mfma_counters("solve", args.workload),
     }
     tr = roof_solve["base_case"]["traffic"]
     if tr is not None:
@@ -439,6 +457,7 @@ def main():
         "frac": ldl_flops / ldl_s / 1e12 / PEAK_FP64_MFMA_TFLOPS,
         "traffic": traffic_bytes("ldl", args.workload),
         "chain": {"blocks": nblk, "us_per_block": ldl_s * 1e6 / nblk},
+        "counters": mfma_counters("ldl", args.workload),
     }
 
     res = {
