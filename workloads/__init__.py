@@ -113,15 +113,52 @@ def make_g(T: int, m: int, seed: int) -> np.ndarray:
     return g
 
 
-def make_inputs(name: str, m: int | None = None, n: int | None = None, T: int | None = None):
-    """(W*, X, G) for a named workload; m/n/T may be overridden for scaled-down variants."""
+# Bump when the recipe above changes: cached inputs drawn under another version
+# are then ignored.
+RECIPE_VERSION = 1
+
+
+def _cache_paths(cache_dir: str, wl: Workload, m: int, n: int, T: int):
+    """The three .npy files of one input set, named by workload, shape, seeds and recipe."""
+    import hashlib
+    import os
+
+    key = "%r|%d|%d|%d|%d" % (wl, m, n, T, RECIPE_VERSION)
+    tag = "%s-%dx%d-T%d-s%d-%s" % (wl.name, m, n, T, wl.key, hashlib.sha256(key.encode()).hexdigest()[:12])
+    return [os.path.join(cache_dir, "%s-%s.npy" % (tag, part)) for part in ("w", "x", "g")]
+
+
+def make_inputs(name: str, m: int | None = None, n: int | None = None, T: int | None = None,
+                cache_dir: str | None = None):
+    """(W*, X, G) for a named workload; m/n/T may be overridden for scaled-down variants.
+
+    cache_dir (default: the BAKRON_INPUT_CACHE environment variable, if set): a
+    directory of .npy files keyed by workload, shape, seeds and recipe version. A
+    set found there is loaded instead of drawn (plain arrays, no pickles); one
+    drawn here is written there. The arrays are the same either way.
+    """
+    import os
+
     wl = WORKLOADS[name]
     m = wl.m if m is None else m
     n = wl.n if n is None else n
     T = wl.T if T is None else T
+    if cache_dir is None:
+        cache_dir = os.environ.get("BAKRON_INPUT_CACHE") or None
+    paths = _cache_paths(cache_dir, wl, m, n, T) if cache_dir else None
+    if paths and all(os.path.exists(p) for p in paths):
+        w, x, g = (np.load(p, allow_pickle=False) for p in paths)
+        if w.shape == (m, n) and x.shape == (T, n) and g.shape == (T, m):
+            return w, x, g
     w = make_w(m, n, wl.seed_w)
     x = make_x(T, n, wl.seed_x, wl.x_kind, min(wl.x_outliers, n), wl.x_outlier_mult)
     g = make_g(T, m, wl.seed_g)
+    if paths:
+        os.makedirs(cache_dir, exist_ok=True)
+        for p, a in zip(paths, (w, x, g)):
+            tmp = "%s.tmp%d.npy" % (p[:-4], os.getpid())
+            np.save(tmp, a, allow_pickle=False)
+            os.replace(tmp, p)
     return w, x, g
 
 
