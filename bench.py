@@ -10,8 +10,9 @@ T = 32768 tokens, 2-bit nearest rounding.
 
 Prints ONE JSON line. `value` is layer throughput in weights/s (m*n per step
 time); per-phase times, the solve-only rate, the roofline of the dominant
-kernel (timed with HIP events on the stream it runs on) and the CPU oracle
-baseline (on a bounded sample, extrapolated to the whole layer) ride along.
+kernel (the solve's k_solve_run, timed with HIP events on the stream it runs
+on), the rooflines of the Hessian calls and the LDL pair, and the CPU oracle
+baseline with its replay of the device's codes ride along.
 """
 from __future__ import annotations
 
@@ -365,11 +366,10 @@ def main():
     loss = float(out.loss.item())
     clamped = int(out.clamped.item())
 
-    # Roofline of the kernel with the most time per step, the Hessian SYRK (two
-    # calls per step). Timed per hessian_accum call (events on the stream the
-    # kernels run on); one call is the k_split3 pre-pass, k_syrk3_full and, when
-    # the tile count is not a whole number of rounds, the split-K pair
-    # k_syrk3_split + k_syrk_reduce for the leftover tiles.
+    # The Hessian calls (two per step), priced per hessian_accum call (events on the
+    # stream the kernels run on); one call is the k_colmax / k_colexp / k_split2
+    # pre-pass, k_syrk2_full and, when the tile count is not a whole number of
+    # rounds, the split-K pair k_syrk2_split + k_syrk_reduce for the leftover tiles.
     if sketch:
         # one "call" is the whole Sketch B phase: S sequences, each an m n^2 (H_I)
         # and an n m^2 (H_O) accumulation
@@ -393,7 +393,7 @@ def main():
     solve_flops = float(m) * n * (m + n)            # far-field feedback, minimal
     dominant = max(ph, key=ph.get)
     fp32_equiv = syrk_flops / (syrk_ms * 1e-3) / 1e12
-    roof = {
+    roof_hess = {
         "kernel": "hessian_accum: k_colmax + k_colexp + k_split2 + k_syrk2_full (+ k_syrk2_split, "
                   "k_syrk_reduce), fp16 MFMA, three piece products per fp32 product",
         "bound": "mfma",
@@ -407,42 +407,52 @@ def main():
         "counters": None if args.hessian != "tokens" else mfma_counters("hessian", args.workload),
     }
     if args.hessian == "sketch_a":
-        roof.update(kernel="sketch_a phase: token-weight tile GEMMs (fp32 MFMA) and weighted SYRKs "
-                           "(fp16 pieces), in fp32-equivalent flops",
-                    achieved=fp32_equiv, peak=PEAK_FP32_MFMA_TFLOPS, flops_per_call=syrk_flops)
-    roof["frac"] = roof["achieved"] / roof["peak"]
+        roof_hess.update(kernel="sketch_a phase: token-weight tile GEMMs (fp32 MFMA) and weighted SYRKs "
+                                "(fp16 pieces), in fp32-equivalent flops",
+                         achieved=fp32_equiv, peak=PEAK_FP32_MFMA_TFLOPS, flops_per_call=syrk_flops)
+    roof_hess["frac"] = roof_hess["achieved"] / roof_hess["peak"]
 
-    # The solve (one persistent launch, k_solve_run, plus small kernels), priced
-    # three ways: its far-field GEMMs against the fp16 MFMA peak (the minimum
-    # mn(m+n) flops of the two triangular long-K products, each fp32 product done
-    # as three fp16 piece products), its base case against HBM (the accumulator
-    # form's algorithmic traffic, 33 B per weight: W* 4, the two far-field offsets 8,
-    # D 4, C 4, the pieces of D and C 8, the code 1, the diagonal factor blocks
-    # about 4), and its time per step of the dependent chain the schedule runs
-    # (64 x 64 leaves, a leaf-diagonal lag of 96 steps: (M + N - 2) 96 + 127 steps)
-    # next to the chain of the rule itself (m + n - 1 anti-diagonals).
-    solve_s = ph["solve"] * 1e-3
+    # The solve, the kernel with the most time per step at the attention shape: one
+    # persistent launch, k_solve_run, behind the row scales and the factors' piece
+    # pre-pass, timed per solve call. It runs the far-field GEMMs and the base case
+    # together; its roofline is the one whose ideal time is longer. The far field's
+    # minimum is mn(m+n) fp32 flops (two triangular long-K products), each done as
+    # three fp16 piece products, against the fp16 MFMA peak. The base case's
+    # algorithmic traffic is the accumulator form's 33 B per weight (W* 4, the two
+    # far-field offsets 8, D 4, C 4, the pieces of D and C 8, the code 1, the
+    # diagonal factor blocks about 4), against HBM. The floor of both is the chain
+    # of dependent steps the schedule runs (64 x 64 leaves, a leaf-diagonal lag of 96
+    # steps: (M + N - 2) 96 + 127 steps), reported beside the rule's own chain
+    # (m + n - 1 anti-diagonals).
+    solve_s = float(np.mean(ev["solve"])) * 1e-3  # average per call
     M, N = (m + 63) // 64, (n + 63) // 64
     chain = (M + N - 2) * 96 + 127
     base_bytes = 33.0 * m * n
-    roof_solve = {
-        "kernel": "k_solve_run (+ k_solve_init, k_scales, k_solve_finish)",
-        "time_ms": ph["solve"],
-        "far_field": {"bound": "mfma", "flops": PIECE_PRODUCTS * solve_flops,
-                      "achieved": PIECE_PRODUCTS * solve_flops / solve_s / 1e12,
-                      "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
-                      "frac": PIECE_PRODUCTS * solve_flops / solve_s / 1e12 / PEAK_F16_MFMA_TFLOPS,
-                      "fp32_equiv_tflops": solve_flops / solve_s / 1e12},
-        "base_case": {"bound": "hbm", "bytes": base_bytes, "achieved": base_bytes / solve_s / 1e9,
-                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": base_bytes / solve_s / 1e9 / PEAK_HBM_GBS,
-                      "traffic": traffic_bytes("solve", args.workload)},
+    ff_flops = PIECE_PRODUCTS * solve_flops
+    t_ff = ff_flops / (PEAK_F16_MFMA_TFLOPS * 1e12)
+    t_base = base_bytes / (PEAK_HBM_GBS * 1e9)
+    far_field = {"bound": "mfma", "flops": ff_flops, "achieved": ff_flops / solve_s / 1e12,
+                 "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                 "frac": ff_flops / solve_s / 1e12 / PEAK_F16_MFMA_TFLOPS,
+                 "fp32_equiv_tflops": solve_flops / solve_s / 1e12, "ideal_ms": t_ff * 1e3}
+    base_case = {"bound": "hbm", "bytes": base_bytes, "achieved": base_bytes / solve_s / 1e9,
+                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": base_bytes / solve_s / 1e9 / PEAK_HBM_GBS,
+                 "ideal_ms": t_base * 1e3}
+    main = far_field if t_ff >= t_base else base_case
+    roof = {
+        "kernel": "k_solve_run (timed as the solve call: + k_scales, k_lstats / k_lexp / k_lsplit, "
+                  "k_solve_init, k_solve_finish)",
+        "bound": main["bound"], "achieved": main["achieved"], "peak": main["peak"], "unit": main["unit"],
+        "frac": main["frac"], "traffic": traffic_bytes("solve", args.workload),
+        "time_ms": solve_s * 1e3,
+        "far_field": far_field,
+        "base_case": base_case,
         "chain": {"steps": chain, "ns_per_step": solve_s * 1e9 / chain, "rule_steps": m + n - 1,
                   "ns_per_rule_step": solve_s * 1e9 / (m + n - 1)},
         "counters": mfma_counters("solve", args.workload),
     }
-    tr = roof_solve["base_case"]["traffic"]
-    if tr is not None:
-        roof_solve["base_case"]["counter_gbs"] = tr / solve_s / 1e9
+    if roof["traffic"] is not None:
+        roof["traffic_gbs"] = roof["traffic"] / solve_s / 1e9
 
     # The LDL pair: d^3/3 fp64 flops per factor against the fp64 MFMA peak, and its
     # chain of 64-wide diagonal blocks (the longer factor's) priced per block
@@ -489,7 +499,7 @@ def main():
         "solve_gemm_tflops": solve_flops / (ph["solve"] * 1e-3) / 1e12,
         "ldl_fp64_tflops": (m ** 3 + n ** 3) / 3.0 / (ph["ldl"] * 1e-3) / 1e12,
         "roofline": roof,
-        "roofline_solve": roof_solve,
+        "roofline_hessian": roof_hess,
         "roofline_ldl": roof_ldl,
         "proxy_loss": loss,
         "clamped": clamped,
